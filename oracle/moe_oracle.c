@@ -1,0 +1,298 @@
+/*
+ * moe_oracle.c -- plain, slow, CPU reference of a mixture-of-experts FFN layer forward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may include, link or call this
+ * file; only the test-suite, the smoke check and the benchmark's CPU-baseline leg use it.
+ * It shares no code, header, table or helper with the GPU library.
+ *
+ * What it computes follows the description of the single-GPU ("TP=1, local") MoE kernels in
+ * "CuTeDSL at Perplexity" (Perplexity blog), section "Mixture-of-Experts Dispatch/Combine",
+ * subsection "Local": a router picks experts per token, dispatch counts the tokens of every
+ * expert and gives each token a unique index inside its expert's list, the MoE GEMMs run per
+ * expert, and combine accumulates the expert outputs of every token with its routing weight.
+ * The pages give no formulas; each step states the reading it takes:
+ *
+ *  route    logits l[t,e] = sum_h x[t,h] * Wr[e,h] (+ b[e]) in the CANONICAL fp32 order below
+ *           (the order is part of the routing contract, so that expert indices are bit-exact);
+ *           top-k by (logit descending, expert index ascending); weights = softmax over the k
+ *           selected logits (== the full softmax renormalised over the selection), in fp64.
+ *  permute  counts[e], exclusive offsets[e], and the STABLE counting sort of assignments
+ *           a = t*k + j by expert: sorted_token[pos] = t, inv_perm[a] = pos.
+ *  expert   SwiGLU FFN (SiLU(gate) * up, then down), gate rows first in W13; no biases.
+ *  combine  y[t] = sum_j w[t,j] * y_perm[inv_perm[t*k+j]].
+ *
+ * Floating point: every value is decoded exactly into double (its own bf16 / E2M1 / E4M3
+ * decoders) and every sum after routing is accumulated in double.  Parity pins: see the tests.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_NVFP4 = 2 };
+
+/* ------------------------------------------------------------------------------------ */
+/* decoders                                                                              */
+/* ------------------------------------------------------------------------------------ */
+
+/* bfloat16: the upper half of an IEEE binary32. */
+static float dec_bf16_f(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+/* E2M1 (OCP microscaling formats v1.0, FP4): sign bit 3, exponent bits 2..1 (bias 1),
+ * mantissa bit 0; exponent 0 is subnormal with value mantissa * 2^-1. */
+static double dec_e2m1(uint8_t code) {
+    int s = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+    double mag = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return s ? -mag : mag;
+}
+
+/* E4M3FN (OCP 8-bit floating point, FN variant): sign bit 7, exponent bits 6..3 (bias 7),
+ * mantissa bits 2..0; exponent 0 is subnormal (m/8 * 2^-6); S.1111.111 is NaN; no infinity. */
+static double dec_e4m3(uint8_t code) {
+    int s = (code >> 7) & 1, e = (code >> 3) & 15, m = code & 7;
+    double mag;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) mag = ldexp(m / 8.0, -6);
+    else mag = ldexp(1.0 + m / 8.0, e - 7);
+    return s ? -mag : mag;
+}
+
+static float act_f(const void* p, int dt, int64_t i) {
+    if (dt == ORC_F32) return ((const float*)p)[i];
+    return dec_bf16_f(((const uint16_t*)p)[i]);
+}
+
+void oracle_decode_bf16(const uint16_t* in, double* out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = (double)dec_bf16_f(in[i]);
+}
+void oracle_decode_e2m1(const uint8_t* codes, double* out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = dec_e2m1(codes[i] & 15);
+}
+void oracle_decode_e4m3(const uint8_t* codes, double* out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = dec_e4m3(codes[i]);
+}
+
+/* Element (n, k) of one expert weight matrix with K columns, decoded to double. */
+typedef struct {
+    int dt;                 /* ORC_F32 | ORC_BF16 | ORC_NVFP4 */
+    const void* w;          /* [rows, K] values, or packed nibbles [rows, K/2] */
+    const uint8_t* scale;   /* NVFP4: E4M3 [rows, K/16] */
+    double gscale;          /* NVFP4: per-expert fp32 second-level scale */
+    int64_t K;
+} wmat;
+
+static double wget(const wmat* m, int64_t n, int64_t k) {
+    if (m->dt == ORC_F32) return ((const float*)m->w)[n * m->K + k];
+    if (m->dt == ORC_BF16) return (double)dec_bf16_f(((const uint16_t*)m->w)[n * m->K + k]);
+    {
+        uint8_t byte = ((const uint8_t*)m->w)[n * (m->K / 2) + k / 2];
+        uint8_t code = (k & 1) ? (byte >> 4) : (byte & 15); /* even k in the low nibble */
+        double s = dec_e4m3(m->scale[n * (m->K / 16) + k / 16]);
+        return dec_e2m1(code) * s * m->gscale;
+    }
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* route                                                                                  */
+/* ------------------------------------------------------------------------------------ */
+
+/* Canonical fp32 router logit.  The hidden vector is cut into chunks of 8 consecutive
+ * elements; chunk c belongs to partial sum p = c mod 64.  Each of the 64 partials starts at
+ * +0 and absorbs its chunks in ascending c, element by element, with one correctly rounded
+ * fused multiply-add per element.  The 64 partials are then folded pairwise:
+ * for off = 32,16,8,4,2,1: a[p] = a[p] + a[p+off] for p < off.  The bias, if any, is added
+ * to a[0] last, in fp32.  Requires H % 8 == 0. */
+float oracle_logit(const void* x_row, const void* w_row, int dt, int64_t H, int has_bias, float bias) {
+    float a[64];
+    for (int p = 0; p < 64; ++p) a[p] = 0.0f;
+    for (int64_t c = 0; c < H / 8; ++c) {
+        int p = (int)(c % 64);
+        for (int i = 0; i < 8; ++i) {
+            int64_t h = 8 * c + i;
+            a[p] = fmaf(act_f(x_row, dt, h), act_f(w_row, dt, h), a[p]);
+        }
+    }
+    for (int off = 32; off >= 1; off >>= 1)
+        for (int p = 0; p < off; ++p) a[p] = a[p] + a[p + off];
+    if (has_bias) a[0] = a[0] + bias;
+    return a[0];
+}
+
+void oracle_router_logits(int64_t T, int64_t H, int64_t E, int dt, const void* x, const void* wr,
+                          const float* bias, float* logits) {
+    size_t es = (dt == ORC_F32) ? 4 : 2;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t e = 0; e < E; ++e)
+            logits[t * E + e] = oracle_logit((const char*)x + (size_t)(t * H) * es,
+                                             (const char*)wr + (size_t)(e * H) * es, dt, H,
+                                             bias != NULL, bias ? bias[e] : 0.0f);
+}
+
+/* Top-k of one row of logits: (logit descending, expert ascending); stored in that order.
+ * Weights: softmax over the selected logits (renorm = 1) or the full softmax value of each
+ * selected expert (renorm = 0), in double. */
+void oracle_select(int64_t T, int64_t E, int k, const float* logits, int renorm, int32_t* ids,
+                   double* w) {
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        const float* l = logits + t * E;
+        unsigned char* taken = (unsigned char*)calloc((size_t)E, 1);
+        for (int j = 0; j < k; ++j) {
+            int64_t best = -1;
+            for (int64_t e = 0; e < E; ++e) {
+                if (taken[e]) continue;
+                if (best < 0 || l[e] > l[best]) best = e; /* strict: the lower index keeps ties */
+            }
+            taken[best] = 1;
+            ids[t * k + j] = (int32_t)best;
+        }
+        free(taken);
+        double top = (double)l[ids[t * k]];
+        double z = 0.0;
+        if (renorm) {
+            for (int j = 0; j < k; ++j) z += exp((double)l[ids[t * k + j]] - top);
+        } else {
+            for (int64_t e = 0; e < E; ++e) z += exp((double)l[e] - top);
+        }
+        for (int j = 0; j < k; ++j) w[t * k + j] = exp((double)l[ids[t * k + j]] - top) / z;
+    }
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* permute                                                                                */
+/* ------------------------------------------------------------------------------------ */
+
+void oracle_permute(int64_t T, int k, int64_t E, const int32_t* ids, int32_t* counts,
+                    int32_t* offsets, int32_t* sorted_token, int32_t* inv_perm) {
+    int64_t A = T * k;
+    for (int64_t e = 0; e < E; ++e) counts[e] = 0;
+    for (int64_t a = 0; a < A; ++a) counts[ids[a]] += 1;
+    offsets[0] = 0;
+    for (int64_t e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+    int32_t* next = (int32_t*)malloc(sizeof(int32_t) * (size_t)(E > 0 ? E : 1));
+    for (int64_t e = 0; e < E; ++e) next[e] = offsets[e];
+    for (int64_t a = 0; a < A; ++a) { /* row-major (t, j) order: stable */
+        int32_t pos = next[ids[a]]++;
+        sorted_token[pos] = (int32_t)(a / k);
+        inv_perm[a] = pos;
+    }
+    free(next);
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* expert FFN                                                                             */
+/* ------------------------------------------------------------------------------------ */
+
+typedef struct {
+    int64_t H, F;
+    int wdt;
+    const void *w13, *w2;                 /* per-expert base pointers are computed below */
+    const uint8_t *w13_scale, *w2_scale;
+    const float *w13_gscale, *w2_gscale;  /* nullable: 1.0 */
+} experts_t;
+
+static void expert_mats(const experts_t* ex, int64_t e, wmat* g13, wmat* g2) {
+    int64_t H = ex->H, F = ex->F;
+    g13->dt = g2->dt = ex->wdt;
+    g13->K = H;
+    g2->K = F;
+    if (ex->wdt == ORC_NVFP4) {
+        g13->w = (const uint8_t*)ex->w13 + e * (2 * F) * (H / 2);
+        g2->w = (const uint8_t*)ex->w2 + e * H * (F / 2);
+        g13->scale = ex->w13_scale + e * (2 * F) * (H / 16);
+        g2->scale = ex->w2_scale + e * H * (F / 16);
+        g13->gscale = ex->w13_gscale ? ex->w13_gscale[e] : 1.0;
+        g2->gscale = ex->w2_gscale ? ex->w2_gscale[e] : 1.0;
+    } else {
+        size_t es = ex->wdt == ORC_F32 ? 4 : 2;
+        g13->w = (const char*)ex->w13 + (size_t)(e * 2 * F * H) * es;
+        g2->w = (const char*)ex->w2 + (size_t)(e * H * F) * es;
+        g13->scale = g2->scale = NULL;
+        g13->gscale = g2->gscale = 1.0;
+    }
+}
+
+/* y[0:H] = W2[e] . ( silu(W13[e][0:F] . x) * (W13[e][F:2F] . x) ), all in double. */
+static void expert_row(const experts_t* ex, int64_t e, const double* x, double* hid, double* y) {
+    wmat g13, g2;
+    expert_mats(ex, e, &g13, &g2);
+    int64_t H = ex->H, F = ex->F;
+    for (int64_t f = 0; f < F; ++f) {
+        double g = 0.0, u = 0.0;
+        for (int64_t h = 0; h < H; ++h) {
+            g += wget(&g13, f, h) * x[h];
+            u += wget(&g13, F + f, h) * x[h];
+        }
+        hid[f] = g / (1.0 + exp(-g)) * u;
+    }
+    for (int64_t h = 0; h < H; ++h) {
+        double s = 0.0;
+        for (int64_t f = 0; f < F; ++f) s += wget(&g2, h, f) * hid[f];
+        y[h] = s;
+    }
+}
+
+/* Expert FFN of a list of assignment rows: row r runs expert row_expert[r] on token
+ * row_token[r]; out[r, 0:H] (double).  hid_out[r, 0:F] optional (NULL to skip). */
+void oracle_expert_rows(int64_t H, int64_t F, int act_dt, int wdt, const void* x, const void* w13,
+                        const void* w2, const uint8_t* w13_scale, const uint8_t* w2_scale,
+                        const float* w13_gscale, const float* w2_gscale, int64_t nrows,
+                        const int32_t* row_token, const int32_t* row_expert, double* out,
+                        double* hid_out) {
+    experts_t ex = {H, F, wdt, w13, w2, w13_scale, w2_scale, w13_gscale, w2_gscale};
+#pragma omp parallel
+    {
+        double* xr = (double*)malloc(sizeof(double) * (size_t)H);
+        double* hid = (double*)malloc(sizeof(double) * (size_t)F);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t r = 0; r < nrows; ++r) {
+            int64_t t = row_token[r];
+            for (int64_t h = 0; h < H; ++h) xr[h] = (double)act_f(x, act_dt, t * H + h);
+            expert_row(&ex, row_expert[r], xr, hid, out + r * H);
+            if (hid_out) memcpy(hid_out + r * F, hid, sizeof(double) * (size_t)F);
+        }
+        free(xr);
+        free(hid);
+    }
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* combine                                                                                */
+/* ------------------------------------------------------------------------------------ */
+
+void oracle_combine(int64_t T, int k, int64_t H, const double* y_perm, const int32_t* inv_perm,
+                    const double* w, double* y) {
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t h = 0; h < H; ++h) {
+            double s = 0.0;
+            for (int j = 0; j < k; ++j) s += w[t * k + j] * y_perm[(int64_t)inv_perm[t * k + j] * H + h];
+            y[t * H + h] = s;
+        }
+}
+
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
