@@ -1,0 +1,154 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) mixture-of-experts FFN layer, forward pass, one GPU.
+ *
+ * The layer is the single-GPU ("TP=1, local") MoE path described in "CuTeDSL at Perplexity"
+ * (Perplexity blog), section "Mixture-of-Experts Dispatch/Combine", subsection "Local":
+ *   route    router logits, top-k expert selection per token and its weights;
+ *   dispatch count the tokens of each expert and give every (token, slot) a unique index in
+ *            its expert's list, so the expert GEMMs see contiguous rows;
+ *   GEMMs    per expert: gate/up projection with SwiGLU, then the down projection ("MoE GEMM",
+ *            "Hosting Qwen on Blackwell", section MoE GEMM; SwiGLU as a stage of the layer in
+ *            the Muse Spark Open megakernel article, section Megakernel implementation);
+ *   combine  the weighted sum of each token's expert outputs, back in token order.
+ *
+ * Notation: T tokens, H hidden, E experts, k experts per token, F expert FFN width,
+ * A = T*k assignments.  All matrices are dense row-major.  Expert weights are stored
+ * [out, in] (y = x W^T): w13 is [E, 2F, H] with gate rows 0..F-1 and up rows F..2F-1;
+ * w2 is [E, H, F].
+ *
+ * Conventions shared by every entry point
+ *  - Pointers are DEVICE memory owned by the caller, 16-byte aligned.  The library never
+ *    allocates, frees or retains device memory; scratch comes from the caller's workspace
+ *    (size from moe_workspace_size).  No global mutable state: calls on different streams
+ *    with different workspaces may run concurrently.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only enqueues work
+ *    on it; nothing synchronises and no device data is read on the host.  Results are valid
+ *    once the caller has synchronised the stream.
+ *  - Errors are return codes; nothing is thrown and nothing aborts.  All arguments are
+ *    validated on the host before any HIP call: MOE_ERR_INVALID_ARGUMENT for a null required
+ *    pointer, a misaligned pointer, negative sizes, k < 1, k > E, k > 16 or E > 512;
+ *    MOE_ERR_UNSUPPORTED for shapes with no compiled kernel (H % 64, F % 64 != 0, bf16
+ *    activations with fp32 weights or the reverse, NVFP4 with fp32 activations);
+ *    MOE_ERR_WORKSPACE_TOO_SMALL; MOE_ERR_DEVICE when a launch reports an error.
+ *  - T = 0 is a successful no-op (token-sized buffers and the workspace may then be NULL;
+ *    moe_permute and moe_forward still set counts/offsets, when given, to zero).
+ *  - Determinism: identical inputs give bitwise identical outputs (no floating-point atomics).
+ *  - Non-finite inputs give unspecified (but memory-safe) results.
+ *
+ * Routing contract (bit-exact):
+ *  - logits l[t,e] are fp32 in a canonical order: H is cut into chunks of 8 consecutive
+ *    elements, chunk c feeds partial sum p = c mod 64; each partial starts at +0 and takes its
+ *    chunks in ascending order, one correctly rounded fused multiply-add per element; the 64
+ *    partials fold as a[p] += a[p+off] for off = 32,16,8,4,2,1; the bias is added last.
+ *  - selection: the k largest logits, ties to the lower expert index, stored in that order.
+ *  - weights (fp32): softmax over the k selected logits (renormalize = 1), or the full
+ *    softmax probability of each selected expert (renormalize = 0).
+ *  - dispatch order: assignments a = t*k + j sorted stably by expert, so rows of one expert
+ *    appear in ascending (t, j) order; offsets are the exclusive prefix sum of the counts.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARGUMENT = 1,
+    MOE_ERR_UNSUPPORTED = 2,
+    MOE_ERR_WORKSPACE_TOO_SMALL = 3,
+    MOE_ERR_DEVICE = 4
+} moe_status;
+
+/* Storage formats.  MOE_NVFP4 (weights only): 4-bit E2M1 values, two per byte with the even
+ * element in the low nibble, one E4M3 (FN) scale per 16 consecutive elements along the input
+ * dimension, and an optional fp32 scale per expert and matrix: w = e2m1 * e4m3 * gscale. */
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_NVFP4 = 2 } moe_dtype;
+
+typedef enum { MOE_GEMM_GATE_UP_SWIGLU = 0, MOE_GEMM_DOWN = 1 } moe_gemm_kind;
+
+/* Kernel family.  AUTO picks DECODE when there are fewer than 16 assignments per expert on
+ * average (weight streaming with small row tiles) and PREFILL otherwise (large MFMA tiles).
+ * Both families give bit-identical routing and dispatch. */
+typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_PREFILL = 1, MOE_PATH_DECODE = 2 } moe_path;
+
+typedef struct {
+    int32_t num_tokens;   /* T >= 0 */
+    int32_t hidden;       /* H, multiple of 64 */
+    int32_t num_experts;  /* E, 1..512 */
+    int32_t top_k;        /* k, 1..min(E,16) */
+    int32_t ffn;          /* F, multiple of 64 */
+    int32_t act_dtype;    /* MOE_F32 | MOE_BF16: x, router weight, hid, y_perm, y */
+    int32_t w_dtype;      /* MOE_F32 (with F32 acts) | MOE_BF16 | MOE_NVFP4 (with BF16 acts) */
+    int32_t renormalize;  /* 1: softmax over the selected k (default); 0: full softmax */
+    int32_t path;         /* moe_path */
+} moe_problem;
+
+typedef struct {
+    const void* w13;              /* [E,2F,H] act-width values, or NVFP4 bytes [E,2F,H/2] */
+    const void* w2;               /* [E,H,F], or NVFP4 bytes [E,H,F/2] */
+    const uint8_t* w13_scale;     /* NVFP4 only: E4M3 [E,2F,H/16] */
+    const uint8_t* w2_scale;      /* NVFP4 only: E4M3 [E,H,F/16] */
+    const float* w13_gscale;      /* NVFP4 only, nullable (=> 1.0): fp32 [E] */
+    const float* w2_gscale;       /* NVFP4 only, nullable (=> 1.0): fp32 [E] */
+} moe_expert_weights;
+
+/* Text of a status code (static storage). */
+const char* moe_status_string(moe_status s);
+
+/* Bytes of workspace every entry point below needs for problem `p` (an upper bound valid
+ * for all of them).  Host only; touches no device.  Returns MOE_ERR_INVALID_ARGUMENT /
+ * MOE_ERR_UNSUPPORTED for problems the entry points would reject. */
+moe_status moe_workspace_size(const moe_problem* p, size_t* bytes);
+
+/* Route.  x [T,H] and w_router [E,H] in act_dtype; router_bias fp32 [E] or NULL.
+ * Writes topk_ids int32 [T,k] and topk_w fp32 [T,k] (routing contract above). */
+moe_status moe_route(const moe_problem* p, const void* x, const void* w_router,
+                     const float* router_bias, int32_t* topk_ids, float* topk_w,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Dispatch.  From topk_ids [T,k] (values in [0,E)) writes counts int32 [E], offsets int32
+ * [E+1], sorted_token int32 [A] (token of each dispatched row) and inv_perm int32 [A]
+ * (dispatched row of assignment t*k+j).  If x and x_perm are both non-NULL it also copies
+ * the token rows into x_perm [A,H] (act_dtype) in dispatch order. */
+moe_status moe_permute(const moe_problem* p, const int32_t* topk_ids, int32_t* counts,
+                       int32_t* offsets, int32_t* sorted_token, int32_t* inv_perm,
+                       const void* x, void* x_perm, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/* Grouped expert GEMM over dispatched rows; expert e owns rows offsets[e]..offsets[e+1]-1.
+ *  GATE_UP_SWIGLU: row r of the input is a[a_rows[r]] ([T,H], a_rows = sorted_token) or
+ *                  a[r] ([A,H], a_rows = NULL); out[r] = silu(g) * u with g / u the gate / up
+ *                  projections by w13[e]: out is hid [A,F] in act_dtype.
+ *  DOWN:           input a = hid [A,F] (a_rows must be NULL); out = y_perm [A,H] =
+ *                  hid W2[e]^T, in act_dtype.
+ * fp32 accumulation; NVFP4 weights are decoded exactly to bf16 inside the kernel.
+ * `offsets` [E+1] is read on the device; values are clamped to [0, A] so that a malformed
+ * table cannot make the kernel reach past the A rows of `a`/`out`. */
+moe_status moe_grouped_gemm(const moe_problem* p, moe_gemm_kind kind, const void* a,
+                            const int32_t* a_rows, const int32_t* offsets,
+                            const moe_expert_weights* w, void* out, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/* Combine.  y[t] = sum_j topk_w[t,j] * y_perm[inv_perm[t*k+j]] accumulated in fp32 in
+ * ascending j and rounded once to act_dtype.  y_perm [A,H], y [T,H] in act_dtype. */
+moe_status moe_combine(const moe_problem* p, const void* y_perm, const int32_t* inv_perm,
+                       const float* topk_w, void* y, void* stream);
+
+/* The whole layer: route -> dispatch -> gate/up GEMM + SwiGLU -> down GEMM -> combine.
+ * y [T,H] in act_dtype.  The routing/dispatch outputs are optional (NULL = keep them in the
+ * workspace); when given they receive the same values the stage entry points produce. */
+moe_status moe_forward(const moe_problem* p, const void* x, const void* w_router,
+                       const float* router_bias, const moe_expert_weights* w, void* y,
+                       int32_t* topk_ids, float* topk_w, int32_t* counts, int32_t* offsets,
+                       int32_t* sorted_token, int32_t* inv_perm, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

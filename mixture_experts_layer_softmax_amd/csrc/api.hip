@@ -1,0 +1,303 @@
+// api.hip -- the C ABI of include/moe.h: validation, workspace layout, kernel policy.
+//
+// Host-side launcher in the spirit of the pages' dispatch() host code ("CuTeDSL at
+// Perplexity", sections Prefill and decode specialization and Grid synchronization): the
+// problem size picks the kernel family (few rows per expert -> weight-streaming decode tiles,
+// many -> large MFMA tiles), and every data-dependent decision after routing stays on the
+// device (tile lists), so nothing is read back and no call synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/moe.h"
+#include "launch.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Layout {
+    size_t logits, ids, w, hist, base, counts, offsets, sorted, inv, tiles1, tiles2, tcount, hid,
+        yperm, total;
+    int family, bm, max_tiles;
+};
+
+int act_bytes(const moe_problem& p) { return p.act_dtype == MOE_F32 ? 4 : 2; }
+
+int family_of(const moe_problem& p) {
+    if (p.act_dtype == MOE_F32) return kFamSimtF32;
+    int path = p.path;
+    if (path == MOE_PATH_AUTO) {
+        const long A = long(p.num_tokens) * p.top_k;
+        path = (A < 16L * p.num_experts) ? MOE_PATH_DECODE : MOE_PATH_PREFILL;
+    }
+    return path == MOE_PATH_DECODE ? kFamDecode : kFamPrefill;
+}
+
+moe_status check_problem(const moe_problem* p) {
+    if (!p) return MOE_ERR_INVALID_ARGUMENT;
+    if (p->num_tokens < 0 || p->hidden <= 0 || p->ffn <= 0 || p->num_experts < 1 ||
+        p->num_experts > kMaxExperts || p->top_k < 1 || p->top_k > kMaxTopK ||
+        p->top_k > p->num_experts || (p->renormalize != 0 && p->renormalize != 1) ||
+        p->path < MOE_PATH_AUTO || p->path > MOE_PATH_DECODE)
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (p->act_dtype != MOE_F32 && p->act_dtype != MOE_BF16) return MOE_ERR_INVALID_ARGUMENT;
+    if (p->w_dtype != MOE_F32 && p->w_dtype != MOE_BF16 && p->w_dtype != MOE_NVFP4)
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (p->hidden % 64 || p->ffn % 64) return MOE_ERR_UNSUPPORTED;
+    if (p->act_dtype == MOE_F32 && p->w_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
+    if (p->act_dtype == MOE_BF16 && p->w_dtype == MOE_F32) return MOE_ERR_UNSUPPORTED;
+    if (long(p->num_tokens) * p->top_k > (1L << 30) || long(p->num_tokens) * p->hidden > (1L << 40))
+        return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+Layout layout(const moe_problem& p) {
+    Layout L{};
+    const size_t T = p.num_tokens, E = p.num_experts, k = p.top_k, H = p.hidden, F = p.ffn;
+    const size_t A = T * k;
+    const size_t nch = (T + kChunkTokens - 1) / kChunkTokens;
+    L.family = family_of(p);
+    L.bm = gemm_tile_rows(L.family);
+    L.max_tiles = int((A + L.bm - 1) / L.bm + (A < E ? A : E) + 1);
+    size_t o = 0;
+    auto take = [&](size_t bytes) { size_t r = o; o += up(bytes > 0 ? bytes : 1); return r; };
+    L.logits = take(T * E * 4);
+    L.ids = take(A * 4);
+    L.w = take(A * 4);
+    L.hist = take(nch * E * 4);
+    L.base = take(nch * E * 4);
+    L.counts = take(E * 4);
+    L.offsets = take((E + 1) * 4);
+    L.sorted = take(A * 4);
+    L.inv = take(A * 4);
+    L.tiles1 = take(size_t(L.max_tiles) * sizeof(Tile));
+    L.tiles2 = take(size_t(L.max_tiles) * sizeof(Tile));
+    L.tcount = take(4 * sizeof(int));
+    L.hid = take(A * F * act_bytes(p));
+    L.yperm = take(A * H * act_bytes(p));
+    L.total = o;
+    return L;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+    return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+moe_status check_ws(const moe_problem& p, void* ws, size_t bytes) {
+    if (!ws || !aligned(ws)) return MOE_ERR_INVALID_ARGUMENT;
+    if (bytes < layout(p).total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    return MOE_OK;
+}
+
+moe_status check_weights(const moe_problem& p, const moe_expert_weights* w) {
+    if (!w || !w->w13 || !w->w2 || !aligned(w->w13) || !aligned(w->w2)) return MOE_ERR_INVALID_ARGUMENT;
+    if (p.w_dtype == MOE_NVFP4) {
+        if (!w->w13_scale || !w->w2_scale) return MOE_ERR_INVALID_ARGUMENT;
+        // scale rows are H/16 or F/16 bytes: 2-byte loads need even offsets
+        if ((reinterpret_cast<uintptr_t>(w->w13_scale) & 1u) || (reinterpret_cast<uintptr_t>(w->w2_scale) & 1u))
+            return MOE_ERR_INVALID_ARGUMENT;
+        if ((reinterpret_cast<uintptr_t>(w->w13_gscale) & 3u) || (reinterpret_cast<uintptr_t>(w->w2_gscale) & 3u))
+            return MOE_ERR_INVALID_ARGUMENT;
+    }
+    return MOE_OK;
+}
+
+moe_status dev(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_DEVICE; }
+
+#define MOE_TRY(x)                           \
+    do {                                     \
+        moe_status _s = (x);                 \
+        if (_s != MOE_OK) return _s;         \
+    } while (0)
+
+moe_status run_route(const moe_problem& p, const void* x, const void* wr, const float* bias,
+                     int32_t* ids, float* w, const Layout& L, void* ws, hipStream_t s) {
+    RouteArgs r{x, wr, bias, at<float>(ws, L.logits), p.num_tokens, p.hidden, p.num_experts,
+                p.act_dtype == MOE_BF16};
+    MOE_TRY(dev(launch_router_logits(r, s)));
+    return dev(launch_topk(r.logits, p.num_tokens, p.num_experts, p.top_k, p.renormalize, ids, w, s));
+}
+
+GemmArgs gemm_args(const moe_problem& p, int kind, const void* a, const int32_t* a_rows,
+                   const Tile* tiles, const int* tcount, const moe_expert_weights& w, void* out) {
+    GemmArgs g{};
+    g.a = a;
+    g.a_rows = a_rows;
+    g.tiles = tiles;
+    g.tile_count = tcount;
+    g.out = out;
+    g.F = p.ffn;
+    g.kind = kind;
+    g.wfmt = p.w_dtype == MOE_F32 ? kWF32 : p.w_dtype == MOE_BF16 ? kWBF16 : kWNVFP4;
+    const int A = p.num_tokens * p.top_k;
+    if (kind == kGateUp) {
+        g.K = p.hidden;
+        g.N = p.ffn;
+        g.w = w.w13;
+        g.wscale = w.w13_scale;
+        g.gscale = w.w13_gscale;
+        g.a_rows_limit = a_rows ? p.num_tokens : A;
+    } else {
+        g.K = p.ffn;
+        g.N = p.hidden;
+        g.w = w.w2;
+        g.wscale = w.w2_scale;
+        g.gscale = w.w2_gscale;
+        g.a_rows_limit = A;
+    }
+    return g;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+    switch (s) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case MOE_ERR_UNSUPPORTED: return "unsupported shape or dtype combination";
+        case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case MOE_ERR_DEVICE: return "device error";
+    }
+    return "unknown status";
+}
+
+moe_status moe_workspace_size(const moe_problem* p, size_t* bytes) {
+    MOE_TRY(check_problem(p));
+    if (!bytes) return MOE_ERR_INVALID_ARGUMENT;
+    *bytes = layout(*p).total;
+    return MOE_OK;
+}
+
+moe_status moe_route(const moe_problem* p, const void* x, const void* w_router,
+                     const float* router_bias, int32_t* topk_ids, float* topk_w, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+    MOE_TRY(check_problem(p));
+    if (p->num_tokens == 0) return MOE_OK;
+    if (!x || !w_router || !topk_ids || !topk_w || !aligned(x) || !aligned(w_router) ||
+        !aligned(topk_ids) || !aligned(topk_w) || (router_bias && !aligned(router_bias)))
+        return MOE_ERR_INVALID_ARGUMENT;
+    MOE_TRY(check_ws(*p, workspace, workspace_bytes));
+    const Layout L = layout(*p);
+    return run_route(*p, x, w_router, router_bias, topk_ids, topk_w, L, workspace,
+                     static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_permute(const moe_problem* p, const int32_t* topk_ids, int32_t* counts,
+                       int32_t* offsets, int32_t* sorted_token, int32_t* inv_perm, const void* x,
+                       void* x_perm, void* workspace, size_t workspace_bytes, void* stream) {
+    MOE_TRY(check_problem(p));
+    if (!counts || !offsets || !aligned(counts) || !aligned(offsets)) return MOE_ERR_INVALID_ARGUMENT;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (p->num_tokens == 0) {  // counts and offsets are still defined: all zero
+        MOE_TRY(dev(launch_fill_i32(counts, p->num_experts, 0, s)));
+        return dev(launch_fill_i32(offsets, p->num_experts + 1, 0, s));
+    }
+    if (!topk_ids || !sorted_token || !inv_perm || !aligned(topk_ids) || !aligned(sorted_token) ||
+        !aligned(inv_perm))
+        return MOE_ERR_INVALID_ARGUMENT;
+    if ((x == nullptr) != (x_perm == nullptr) || (x && (!aligned(x) || !aligned(x_perm))))
+        return MOE_ERR_INVALID_ARGUMENT;
+    MOE_TRY(check_ws(*p, workspace, workspace_bytes));
+    const Layout L = layout(*p);
+    DispatchArgs d{topk_ids, p->num_tokens, p->top_k, p->num_experts, at<int32_t>(workspace, L.hist),
+                   at<int32_t>(workspace, L.base), counts, offsets, sorted_token, inv_perm,
+                   nullptr, nullptr, 0, nullptr, nullptr, 0, L.max_tiles};
+    MOE_TRY(dev(launch_dispatch(d, s)));
+    if (x)
+        MOE_TRY(dev(launch_gather_rows(x, sorted_token, x_perm, p->num_tokens * p->top_k,
+                                       p->num_tokens, p->hidden * act_bytes(*p), s)));
+    return MOE_OK;
+}
+
+moe_status moe_grouped_gemm(const moe_problem* p, moe_gemm_kind kind, const void* a,
+                            const int32_t* a_rows, const int32_t* offsets,
+                            const moe_expert_weights* w, void* out, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+    MOE_TRY(check_problem(p));
+    if (kind != MOE_GEMM_GATE_UP_SWIGLU && kind != MOE_GEMM_DOWN) return MOE_ERR_INVALID_ARGUMENT;
+    if (p->num_tokens == 0) return MOE_OK;
+    if (!a || !offsets || !out || !aligned(a) || !aligned(offsets) || !aligned(out) ||
+        (a_rows && !aligned(a_rows)))
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (kind == MOE_GEMM_DOWN && a_rows) return MOE_ERR_INVALID_ARGUMENT;
+    MOE_TRY(check_weights(*p, w));
+    MOE_TRY(check_ws(*p, workspace, workspace_bytes));
+    const Layout L = layout(*p);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    Tile* tiles = at<Tile>(workspace, L.tiles1);
+    int* tcount = at<int>(workspace, L.tcount);
+    MOE_TRY(dev(launch_tiles_from_offsets(offsets, p->num_experts, p->num_tokens * p->top_k, L.bm,
+                                          tiles, tcount, L.max_tiles, s)));
+    GemmArgs g = gemm_args(*p, kind == MOE_GEMM_GATE_UP_SWIGLU ? kGateUp : kDown, a, a_rows, tiles,
+                           tcount, *w, out);
+    return dev(launch_gemm(g, L.family, L.max_tiles, s));
+}
+
+moe_status moe_combine(const moe_problem* p, const void* y_perm, const int32_t* inv_perm,
+                       const float* topk_w, void* y, void* stream) {
+    MOE_TRY(check_problem(p));
+    if (p->num_tokens == 0) return MOE_OK;
+    if (!y_perm || !inv_perm || !topk_w || !y || !aligned(y_perm) || !aligned(inv_perm) ||
+        !aligned(topk_w) || !aligned(y))
+        return MOE_ERR_INVALID_ARGUMENT;
+    return dev(launch_combine(y_perm, inv_perm, topk_w, y, p->num_tokens, p->top_k, p->hidden,
+                              p->num_tokens * p->top_k, p->act_dtype == MOE_BF16,
+                              static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_forward(const moe_problem* p, const void* x, const void* w_router,
+                       const float* router_bias, const moe_expert_weights* w, void* y,
+                       int32_t* topk_ids, float* topk_w, int32_t* counts, int32_t* offsets,
+                       int32_t* sorted_token, int32_t* inv_perm, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    MOE_TRY(check_problem(p));
+    for (const void* q : {(const void*)topk_ids, (const void*)topk_w, (const void*)counts,
+                          (const void*)offsets, (const void*)sorted_token, (const void*)inv_perm})
+        if (q && !aligned(q)) return MOE_ERR_INVALID_ARGUMENT;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (p->num_tokens == 0) {  // no rows: x, y and the workspace may be empty (NULL)
+        if (counts) MOE_TRY(dev(launch_fill_i32(counts, p->num_experts, 0, s)));
+        if (offsets) MOE_TRY(dev(launch_fill_i32(offsets, p->num_experts + 1, 0, s)));
+        return MOE_OK;
+    }
+    if (!x || !w_router || !y || !aligned(x) || !aligned(w_router) || !aligned(y) ||
+        (router_bias && !aligned(router_bias)))
+        return MOE_ERR_INVALID_ARGUMENT;
+    MOE_TRY(check_weights(*p, w));
+    MOE_TRY(check_ws(*p, workspace, workspace_bytes));
+    const Layout L = layout(*p);
+    int32_t* ids = topk_ids ? topk_ids : at<int32_t>(workspace, L.ids);
+    float* tw = topk_w ? topk_w : at<float>(workspace, L.w);
+    int32_t* off = offsets ? offsets : at<int32_t>(workspace, L.offsets);
+    int32_t* st = sorted_token ? sorted_token : at<int32_t>(workspace, L.sorted);
+    int32_t* ip = inv_perm ? inv_perm : at<int32_t>(workspace, L.inv);
+    int* tcount = at<int>(workspace, L.tcount);
+    Tile* tiles = at<Tile>(workspace, L.tiles1);
+
+    MOE_TRY(run_route(*p, x, w_router, router_bias, ids, tw, L, workspace, s));
+    DispatchArgs d{ids, p->num_tokens, p->top_k, p->num_experts, at<int32_t>(workspace, L.hist),
+                   at<int32_t>(workspace, L.base), counts, off, st, ip, tiles, tcount, L.bm,
+                   nullptr, nullptr, 0, L.max_tiles};
+    MOE_TRY(dev(launch_dispatch(d, s)));
+    void* hid = at<void>(workspace, L.hid);
+    void* yperm = at<void>(workspace, L.yperm);
+    GemmArgs g1 = gemm_args(*p, kGateUp, x, st, tiles, tcount, *w, hid);
+    MOE_TRY(dev(launch_gemm(g1, L.family, L.max_tiles, s)));
+    GemmArgs g2 = gemm_args(*p, kDown, hid, nullptr, tiles, tcount, *w, yperm);
+    MOE_TRY(dev(launch_gemm(g2, L.family, L.max_tiles, s)));
+    return dev(launch_combine(yperm, ip, tw, y, p->num_tokens, p->top_k, p->hidden,
+                              p->num_tokens * p->top_k, p->act_dtype == MOE_BF16, s));
+}
+
+}  // extern "C"

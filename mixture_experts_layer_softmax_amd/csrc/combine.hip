@@ -1,0 +1,81 @@
+// combine.hip -- weighted accumulation of each token's expert outputs back in token order.
+//
+// "CuTeDSL at Perplexity", section Mixture-of-Experts Dispatch/Combine, Local: the combine
+// kernel uses the positions dispatch assigned to gather a token's expert rows and accumulates
+// them in registers with vectorised accesses, then writes the final token.  Here: one block
+// per token, 16-byte loads of y_perm rows, fp32 accumulation in ascending slot order, one
+// rounding to the output type.
+#include "device.h"
+#include "launch.h"
+
+namespace moe {
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y_perm,
+                                                      const int32_t* __restrict__ inv_perm,
+                                                      const float* __restrict__ w,
+                                                      void* __restrict__ y, int k, int H, int A) {
+    const int t = blockIdx.x;
+    int rows[kMaxTopK];
+    float ws[kMaxTopK];
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+        if (j < k) {
+            int r = inv_perm[size_t(t) * k + j];
+            rows[j] = r < 0 ? 0 : (r >= A ? A - 1 : r);
+            ws[j] = w[size_t(t) * k + j];
+        } else {
+            rows[j] = 0;
+            ws[j] = 0.0f;
+        }
+    }
+    if (BF16) {
+        const uint4* src = static_cast<const uint4*>(y_perm);
+        uint4* dst = static_cast<uint4*>(y);
+        const int nv = H / 8;
+        for (int v = threadIdx.x; v < nv; v += blockDim.x) {
+            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < k; ++j) {
+                const uint4 q = src[size_t(rows[j]) * nv + v];
+                const uint32_t u[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    acc[2 * p] = __builtin_fmaf(ws[j], bf16_lo(u[p]), acc[2 * p]);
+                    acc[2 * p + 1] = __builtin_fmaf(ws[j], bf16_hi(u[p]), acc[2 * p + 1]);
+                }
+            }
+            dst[size_t(t) * nv + v] = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                                                 pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
+        }
+    } else {
+        const float4* src = static_cast<const float4*>(y_perm);
+        float4* dst = static_cast<float4*>(y);
+        const int nv = H / 4;
+        for (int v = threadIdx.x; v < nv; v += blockDim.x) {
+            float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int j = 0; j < k; ++j) {
+                const float4 q = src[size_t(rows[j]) * nv + v];
+                acc.x = __builtin_fmaf(ws[j], q.x, acc.x);
+                acc.y = __builtin_fmaf(ws[j], q.y, acc.y);
+                acc.z = __builtin_fmaf(ws[j], q.z, acc.z);
+                acc.w = __builtin_fmaf(ws[j], q.w, acc.w);
+            }
+            dst[size_t(t) * nv + v] = acc;
+        }
+    }
+}
+
+hipError_t launch_combine(const void* y_perm, const int32_t* inv_perm, const float* w, void* y,
+                          int T, int k, int H, int A, bool bf16, hipStream_t s) {
+    const int nv = bf16 ? H / 8 : H / 4;
+    const int threads = nv >= 256 ? 256 : ((nv + 63) / 64) * 64;
+    if (bf16)
+        hipLaunchKernelGGL((combine_kernel<true>), dim3(T), dim3(threads), 0, s, y_perm, inv_perm, w,
+                           y, k, H, A);
+    else
+        hipLaunchKernelGGL((combine_kernel<false>), dim3(T), dim3(threads), 0, s, y_perm, inv_perm,
+                           w, y, k, H, A);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,71 @@
+// launch.h -- internal launchers of the MoE kernels (host side, not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device.h"
+
+namespace moe {
+
+struct RouteArgs {
+    const void* x;      // [T,H] fp32 or bf16
+    const void* wr;     // [E,H]
+    const float* bias;  // [E] or null
+    float* logits;      // [T,E]
+    int T, H, E;
+    bool bf16;
+};
+
+struct DispatchArgs {
+    const int32_t* ids;  // [T,k]
+    int T, k, E;
+    int32_t* hist;       // [nchunks,E]
+    int32_t* base;       // [nchunks,E]
+    int32_t* counts;     // [E] or null
+    int32_t* offsets;    // [E+1]
+    int32_t* sorted_token;
+    int32_t* inv_perm;
+    Tile* tiles1;        // tile list for GEMM1 (or null)
+    int* tile_count1;
+    int bm1;
+    Tile* tiles2;
+    int* tile_count2;
+    int bm2;
+    int tile_cap;        // capacity of each tile list
+};
+
+enum GemmKind { kGateUp = 0, kDown = 1 };
+enum WeightFmt { kWF32 = 0, kWBF16 = 1, kWNVFP4 = 2 };
+enum GemmFamily { kFamSimtF32 = 0, kFamPrefill = 1, kFamDecode = 2 };
+
+struct GemmArgs {
+    const void* a;          // activations: bf16 or fp32, row length K
+    const int32_t* a_rows;  // gather map (dispatched row -> row of a) or null
+    int a_rows_limit;       // rows in a (gathered indices are clamped below it)
+    const Tile* tiles;
+    const int* tile_count;
+    const void* w;          // [E, Nw, K] values or [E, Nw, K/2] packed nibbles
+    const uint8_t* wscale;  // [E, Nw, K/16] (NVFP4)
+    const float* gscale;    // [E] or null (NVFP4)
+    void* out;              // [A, N]
+    int K, N, F;            // reduction length, output columns, gate/up split
+    int kind;               // GemmKind
+    int wfmt;               // WeightFmt
+};
+
+int gemm_tile_rows(int family);
+hipError_t launch_router_logits(const RouteArgs& a, hipStream_t s);
+hipError_t launch_topk(const float* logits, int T, int E, int k, int renorm, int32_t* ids,
+                       float* w, hipStream_t s);
+hipError_t launch_dispatch(const DispatchArgs& d, hipStream_t s);
+hipError_t launch_fill_i32(int32_t* p, int n, int value, hipStream_t s);
+hipError_t launch_tiles_from_offsets(const int32_t* offsets, int E, int A, int bm, Tile* tiles,
+                                     int* tile_count, int cap, hipStream_t s);
+hipError_t launch_gather_rows(const void* x, const int32_t* sorted_token, void* x_perm, int A,
+                              int T, int row_bytes, hipStream_t s);
+hipError_t launch_gemm(const GemmArgs& g, int family, int max_tiles, hipStream_t s);
+hipError_t launch_combine(const void* y_perm, const int32_t* inv_perm, const float* w, void* y,
+                          int T, int k, int H, int A, bool bf16, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,198 @@
+// permute.hip -- dispatch: per-expert counts, offsets and the stable permutation.
+//
+// Follows the local dispatch of "CuTeDSL at Perplexity" (section Mixture-of-Experts
+// Dispatch/Combine, Local): count the tokens routed to every expert, give each (token, slot)
+// a unique index inside its expert's list, and lay the rows out per expert for the MoE GEMMs.
+// The pages assign those indices with shared-memory atomics, first locally per block and then
+// aggregated across blocks in global memory; here the same two-level structure is kept
+// (per-chunk histograms -> one scan -> per-chunk scatter) but each index is a deterministic
+// rank, so rows of one expert appear in ascending (token, slot) order and the permutation is
+// unique.  A chunk is 64 tokens (64*k assignments); a batch of up to 64 tokens is a single
+// chunk, i.e. one block, which is the pages' decode case.
+#include "device.h"
+#include "launch.h"
+
+namespace moe {
+
+// hist[c, e] = number of assignments of chunk c routed to expert e (integer atomics on LDS:
+// the counts do not depend on their order).
+__global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ ids, int T, int k,
+                                                   int E, int32_t* __restrict__ hist) {
+    __shared__ int cnt[kMaxExperts];
+    const int c = blockIdx.x;
+    for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
+    __syncthreads();
+    const int a0 = c * kChunkTokens * k;
+    const int a1 = min(T, (c + 1) * kChunkTokens) * k;
+    for (int a = a0 + threadIdx.x; a < a1; a += blockDim.x)
+        atomicAdd(&cnt[clamp_expert(ids[a], E)], 1);
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x) hist[size_t(c) * E + e] = cnt[e];
+}
+
+// Write the tile list of one grouped GEMM with row-tile height bm from per-expert counts
+// (thread e handles expert e; `start` = exclusive row offset of expert e).
+// At most `cap` tiles are written (a bound that valid counts never reach).
+__device__ void emit_tiles(int e, int E, int count, int start, int bm, Tile* tiles,
+                           int* tile_count, int cap) {
+    const int nt = (e < E) ? (count + bm - 1) / bm : 0;
+    int total;
+    const int first = block_exclusive_scan<kMaxExperts>(nt, &total);
+    for (int i = 0; i < nt && first + i < cap; ++i) {
+        Tile t;
+        t.expert = e;
+        t.row0 = start + i * bm;
+        t.row1 = min(start + count, start + (i + 1) * bm);
+        t.pad = 0;
+        tiles[first + i] = t;
+    }
+    if (threadIdx.x == 0) *tile_count = min(total, cap);
+}
+
+// One block of kMaxExperts threads: counts, offsets, per-chunk bases, GEMM tile lists.
+__global__ __launch_bounds__(kMaxExperts) void scan_kernel(const int32_t* __restrict__ hist,
+                                                           int nchunks, int E,
+                                                           int32_t* __restrict__ base,
+                                                           int32_t* __restrict__ counts,
+                                                           int32_t* __restrict__ offsets,
+                                                           Tile* tiles1, int* tile_count1, int bm1,
+                                                           Tile* tiles2, int* tile_count2,
+                                                           int bm2, int cap) {
+    const int e = threadIdx.x;
+    int run = 0;
+    if (e < E) {
+        for (int c = 0; c < nchunks; ++c) {
+            const int h = hist[size_t(c) * E + e];
+            base[size_t(c) * E + e] = run;
+            run += h;
+        }
+    }
+    int total;
+    const int start = block_exclusive_scan<kMaxExperts>(e < E ? run : 0, &total);
+    if (e < E) {
+        if (counts) counts[e] = run;
+        offsets[e] = start;
+        for (int c = 0; c < nchunks; ++c) base[size_t(c) * E + e] += start;
+    }
+    if (e == 0) offsets[E] = total;
+    if (tiles1) emit_tiles(e, E, run, start, bm1, tiles1, tile_count1, cap);
+    if (tiles2) emit_tiles(e, E, run, start, bm2, tiles2, tile_count2, cap);
+}
+
+// Tile list straight from caller-supplied offsets (stand-alone grouped GEMM entry point).
+// Offsets are clamped to [0, A] so that no tile reaches past the A dispatched rows.
+__global__ __launch_bounds__(kMaxExperts) void tiles_from_offsets_kernel(
+    const int32_t* __restrict__ offsets, int E, int A, int bm, Tile* tiles, int* tile_count,
+    int cap) {
+    const int e = threadIdx.x;
+    int start = 0, count = 0;
+    if (e < E) {
+        start = min(max(offsets[e], 0), A);
+        const int end = min(max(offsets[e + 1], start), A);
+        count = end - start;
+    }
+    emit_tiles(e, E, count, start, bm, tiles, tile_count, cap);
+}
+
+// Stable scatter of one chunk.  Assignments are taken 256 at a time in (t, j) order; within a
+// wave, lanes holding the same expert find each other with one ballot per id bit, and wave
+// totals are prefix-summed across the 4 waves through LDS.
+__global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict__ ids, int T, int k,
+                                                      int E, const int32_t* __restrict__ base,
+                                                      int32_t* __restrict__ sorted_token,
+                                                      int32_t* __restrict__ inv_perm) {
+    __shared__ int cnt[kMaxExperts];
+    __shared__ int wc[4][kMaxExperts];
+    const int c = blockIdx.x;
+    const int lane = lane_id(), w = threadIdx.x / kWave;
+    for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
+    const int a0 = c * kChunkTokens * k;
+    const int a1 = min(T, (c + 1) * kChunkTokens) * k;
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
+    for (int r0 = a0; r0 < a1; r0 += 256) {
+        for (int i = threadIdx.x; i < 4 * kMaxExperts; i += blockDim.x) (&wc[0][0])[i] = 0;
+        __syncthreads();
+        const int a = r0 + threadIdx.x;
+        const bool valid = a < a1;
+        const int id = valid ? clamp_expert(ids[a], E) : 0;
+        uint64_t peers = __ballot(valid);
+        for (int b = 0; b < nbits; ++b) {
+            const bool bit = (id >> b) & 1;
+            const uint64_t m = __ballot(valid && bit);
+            peers &= bit ? m : ~m;
+        }
+        const int rank = __popcll(peers & lanemask_lt());
+        if (valid && rank == 0) wc[w][id] = __popcll(peers);
+        __syncthreads();
+        if (valid) {
+            int prefix = 0;
+            for (int ww = 0; ww < w; ++ww) prefix += wc[ww][id];
+            const int pos = base[size_t(c) * E + id] + cnt[id] + prefix + rank;
+            sorted_token[pos] = a / k;
+            inv_perm[a] = pos;
+        }
+        __syncthreads();
+        for (int e = threadIdx.x; e < E; e += blockDim.x)
+            cnt[e] += wc[0][e] + wc[1][e] + wc[2][e] + wc[3][e];
+        __syncthreads();
+    }
+}
+
+// x_perm[r] = x[sorted_token[r]]; 16-byte copies.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint4* __restrict__ x,
+                                                          const int32_t* __restrict__ sorted_token,
+                                                          uint4* __restrict__ x_perm, int A, int T,
+                                                          int row_vec) {
+    const long n = long(A) * row_vec;
+    for (long i = long(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += long(gridDim.x) * blockDim.x) {
+        const long r = i / row_vec, v = i % row_vec;
+        int t = sorted_token[r];
+        t = t < 0 ? 0 : (t >= T ? T - 1 : t);
+        x_perm[i] = x[long(t) * row_vec + v];
+    }
+}
+
+__global__ void fill_i32_kernel(int32_t* __restrict__ p, int n, int value) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = value;
+}
+
+// ---------------------------------------------------------------------------------------
+
+hipError_t launch_fill_i32(int32_t* p, int n, int value, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(fill_i32_kernel, dim3((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024), dim3(256),
+                       0, s, p, n, value);
+    return hipGetLastError();
+}
+
+hipError_t launch_dispatch(const DispatchArgs& d, hipStream_t s) {
+    const int nch = (d.T + kChunkTokens - 1) / kChunkTokens;
+    hipLaunchKernelGGL(hist_kernel, dim3(nch), dim3(256), 0, s, d.ids, d.T, d.k, d.E, d.hist);
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kMaxExperts), 0, s, d.hist, nch, d.E, d.base,
+                       d.counts, d.offsets, d.tiles1, d.tile_count1, d.bm1, d.tiles2,
+                       d.tile_count2, d.bm2, d.tile_cap);
+    hipLaunchKernelGGL(scatter_kernel, dim3(nch), dim3(256), 0, s, d.ids, d.T, d.k, d.E, d.base,
+                       d.sorted_token, d.inv_perm);
+    return hipGetLastError();
+}
+
+hipError_t launch_tiles_from_offsets(const int32_t* offsets, int E, int A, int bm, Tile* tiles,
+                                     int* tile_count, int cap, hipStream_t s) {
+    hipLaunchKernelGGL(tiles_from_offsets_kernel, dim3(1), dim3(kMaxExperts), 0, s, offsets, E, A,
+                       bm, tiles, tile_count, cap);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const void* x, const int32_t* sorted_token, void* x_perm, int A,
+                              int T, int row_bytes, hipStream_t s) {
+    const int row_vec = row_bytes / 16;
+    const long n = long(A) * row_vec;
+    const int blocks = int(n / 256 + 1 < 65536 ? n / 256 + 1 : 65536);
+    hipLaunchKernelGGL(gather_rows_kernel, dim3(blocks), dim3(256), 0, s,
+                       static_cast<const uint4*>(x), sorted_token, static_cast<uint4*>(x_perm), A, T,
+                       row_vec);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,147 @@
+"""Thin Python binding of the C ABI in ``include/moe.h`` (argument marshalling only).
+
+Every entry point here calls the same-named C function of ``libmoe_mi355x.so`` with device
+pointers taken from torch tensors and the hipStream_t of torch's current stream.  No step
+of the layer runs in Python; if the library is missing this module raises at import time
+of the first call instead of falling back to anything.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import threading
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmoe_mi355x.so")
+
+MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_DEVICE = range(5)
+MOE_F32, MOE_BF16, MOE_NVFP4 = 0, 1, 2
+GATE_UP_SWIGLU, DOWN = 0, 1
+PATH_AUTO, PATH_PREFILL, PATH_DECODE = 0, 1, 2
+DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "nvfp4": MOE_NVFP4}
+PATHS = {"auto": PATH_AUTO, "prefill": PATH_PREFILL, "decode": PATH_DECODE}
+
+#: every symbol the header declares
+EXPORTS = ("moe_status_string", "moe_workspace_size", "moe_route", "moe_permute",
+           "moe_grouped_gemm", "moe_combine", "moe_forward")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)" % (what, status_string(status), status))
+
+
+class Problem(C.Structure):
+    _fields_ = [("num_tokens", C.c_int32), ("hidden", C.c_int32), ("num_experts", C.c_int32),
+                ("top_k", C.c_int32), ("ffn", C.c_int32), ("act_dtype", C.c_int32),
+                ("w_dtype", C.c_int32), ("renormalize", C.c_int32), ("path", C.c_int32)]
+
+
+class ExpertWeights(C.Structure):
+    _fields_ = [("w13", C.c_void_p), ("w2", C.c_void_p), ("w13_scale", C.c_void_p),
+                ("w2_scale", C.c_void_p), ("w13_gscale", C.c_void_p), ("w2_gscale", C.c_void_p)]
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load() -> C.CDLL:
+    """Load the HIP library; raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError("libmoe_mi355x.so is not built (run "
+                                   "`python -m mixture_experts_layer_softmax_amd.build`)")
+            L = C.CDLL(LIB_PATH)
+            vp, sz, i32 = C.c_void_p, C.c_size_t, C.c_int
+            P = C.POINTER(Problem)
+            L.moe_status_string.restype = C.c_char_p
+            L.moe_status_string.argtypes = [i32]
+            L.moe_workspace_size.restype = i32
+            L.moe_workspace_size.argtypes = [P, C.POINTER(C.c_size_t)]
+            L.moe_route.restype = i32
+            L.moe_route.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
+            L.moe_permute.restype = i32
+            L.moe_permute.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+            L.moe_grouped_gemm.restype = i32
+            L.moe_grouped_gemm.argtypes = [P, i32, vp, vp, vp, C.POINTER(ExpertWeights), vp, vp, sz, vp]
+            L.moe_combine.restype = i32
+            L.moe_combine.argtypes = [P, vp, vp, vp, vp, vp]
+            L.moe_forward.restype = i32
+            L.moe_forward.argtypes = [P, vp, vp, vp, C.POINTER(ExpertWeights), vp, vp, vp, vp, vp,
+                                      vp, vp, vp, sz, vp]
+            _lib = L
+    return _lib
+
+
+def status_string(s: int) -> str:
+    return load().moe_status_string(int(s)).decode()
+
+
+def problem(tokens, hidden, experts, top_k, ffn, act="bf16", wdt="bf16", renormalize=True,
+            path="auto") -> Problem:
+    return Problem(int(tokens), int(hidden), int(experts), int(top_k), int(ffn), DTYPES[act],
+                   DTYPES[wdt], int(bool(renormalize)), PATHS[path])
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is not None:
+        return C.c_void_p(int(stream))
+    import torch
+
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(status, what):
+    if status != MOE_OK:
+        raise MoeError(status, what)
+
+
+def workspace_size(p: Problem) -> int:
+    n = C.c_size_t(0)
+    _check(load().moe_workspace_size(C.byref(p), C.byref(n)), "moe_workspace_size")
+    return n.value
+
+
+def weights(w13, w2, w13_scale=None, w2_scale=None, w13_gscale=None, w2_gscale=None) -> ExpertWeights:
+    return ExpertWeights(*[t.data_ptr() if t is not None else None
+                           for t in (w13, w2, w13_scale, w2_scale, w13_gscale, w2_gscale)])
+
+
+def route(p, x, w_router, bias, topk_ids, topk_w, ws, stream=None):
+    _check(load().moe_route(C.byref(p), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(topk_ids),
+                            _ptr(topk_w), _ptr(ws), ws.numel() * ws.element_size(),
+                            _stream(stream)), "moe_route")
+
+
+def permute(p, topk_ids, counts, offsets, sorted_token, inv_perm, ws, x=None, x_perm=None,
+            stream=None):
+    _check(load().moe_permute(C.byref(p), _ptr(topk_ids), _ptr(counts), _ptr(offsets),
+                              _ptr(sorted_token), _ptr(inv_perm), _ptr(x), _ptr(x_perm), _ptr(ws),
+                              ws.numel() * ws.element_size(), _stream(stream)), "moe_permute")
+
+
+def grouped_gemm(p, kind, a, a_rows, offsets, w: ExpertWeights, out, ws, stream=None):
+    _check(load().moe_grouped_gemm(C.byref(p), int(kind), _ptr(a), _ptr(a_rows), _ptr(offsets),
+                                   C.byref(w), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
+                                   _stream(stream)), "moe_grouped_gemm")
+
+
+def combine(p, y_perm, inv_perm, topk_w, y, stream=None):
+    _check(load().moe_combine(C.byref(p), _ptr(y_perm), _ptr(inv_perm), _ptr(topk_w), _ptr(y),
+                              _stream(stream)), "moe_combine")
+
+
+def forward(p, x, w_router, bias, w: ExpertWeights, y, ws, topk_ids=None, topk_w=None,
+            counts=None, offsets=None, sorted_token=None, inv_perm=None, stream=None):
+    _check(load().moe_forward(C.byref(p), _ptr(x), _ptr(w_router), _ptr(bias), C.byref(w), _ptr(y),
+                              _ptr(topk_ids), _ptr(topk_w), _ptr(counts), _ptr(offsets),
+                              _ptr(sorted_token), _ptr(inv_perm), _ptr(ws),
+                              ws.numel() * ws.element_size(), _stream(stream)), "moe_forward")

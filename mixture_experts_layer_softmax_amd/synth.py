@@ -99,18 +99,20 @@ def to_bf16_bits(a: np.ndarray) -> np.ndarray:
     return r.astype(np.uint16)
 
 
-# E2M1 magnitudes in code order 0..7 and the round-to-nearest decision points between them.
+# E2M1 magnitudes in code order 0..7.  Round to nearest: the decision points are the
+# midpoints 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5; a value exactly on one goes to the even code
+# (strict '>' where the lower neighbour's code is even, '>=' where the upper one's is).
 _E2M1_MAG = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float32)
-_E2M1_MID = (_E2M1_MAG[:-1] + _E2M1_MAG[1:]) / 2
+_E2M1_STEPS = ((0.25, False), (0.75, True), (1.25, False), (1.75, True), (2.5, False),
+               (3.5, True), (5.0, False))
 
 
 def _e2m1_codes(v: np.ndarray) -> np.ndarray:
     """Nearest E2M1 code (ties to the even code), saturating at 6; sign in bit 3."""
-    a = np.minimum(np.abs(v), np.float32(6.0))
-    lo = np.searchsorted(_E2M1_MID, a, side="left")
-    hi = np.searchsorted(_E2M1_MID, a, side="right")
-    tie = lo != hi
-    idx = np.where(tie & (lo % 2 == 1), lo + 1, lo).astype(np.uint8)
+    a = np.abs(v)
+    idx = np.zeros(a.shape, dtype=np.uint8)
+    for t, inclusive in _E2M1_STEPS:
+        idx += (a >= np.float32(t)) if inclusive else (a > np.float32(t))
     sign = ((v < 0) & (idx != 0)).astype(np.uint8) << 3
     return idx | sign
 
@@ -230,8 +232,15 @@ def gen_experts(wl: Workload, experts=None) -> dict:
             w2[i], s2[i], g2[i] = quantize_nvfp4(_expert_matrix(wl, T_W2, e, (H, F)))
 
         out.update(w13=w13, w2=w2, w13_scale=s13, w2_scale=s2, w13_gscale=g13, w2_gscale=g2)
-    with _cf.ThreadPoolExecutor(_threads()) as ex:
-        list(ex.map(job, range(n)))
+    import torch
+
+    torch_threads = torch.get_num_threads()
+    torch.set_num_threads(1)  # the pool below is the parallelism; avoid oversubscription
+    try:
+        with _cf.ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(job, range(n)))
+    finally:
+        torch.set_num_threads(torch_threads)
     return out
 
 

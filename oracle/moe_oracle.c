@@ -66,6 +66,17 @@ static double dec_e4m3(uint8_t code) {
     return s ? -mag : mag;
 }
 
+/* Decoded values of every E2M1 and E4M3 code, filled once from the decoders above. */
+static double g_e2m1[16], g_e4m3[256];
+static int g_tables_ready = 0;
+
+static void init_tables(void) {
+    if (g_tables_ready) return;
+    for (int c = 0; c < 16; ++c) g_e2m1[c] = dec_e2m1((uint8_t)c);
+    for (int c = 0; c < 256; ++c) g_e4m3[c] = dec_e4m3((uint8_t)c);
+    g_tables_ready = 1;
+}
+
 static float act_f(const void* p, int dt, int64_t i) {
     if (dt == ORC_F32) return ((const float*)p)[i];
     return dec_bf16_f(((const uint16_t*)p)[i]);
@@ -96,8 +107,8 @@ static double wget(const wmat* m, int64_t n, int64_t k) {
     {
         uint8_t byte = ((const uint8_t*)m->w)[n * (m->K / 2) + k / 2];
         uint8_t code = (k & 1) ? (byte >> 4) : (byte & 15); /* even k in the low nibble */
-        double s = dec_e4m3(m->scale[n * (m->K / 16) + k / 16]);
-        return dec_e2m1(code) * s * m->gscale;
+        double s = g_e4m3[m->scale[n * (m->K / 16) + k / 16]];
+        return g_e2m1[code] * s * m->gscale;
     }
 }
 
@@ -206,24 +217,25 @@ static void expert_mats(const experts_t* ex, int64_t e, wmat* g13, wmat* g2) {
     g13->dt = g2->dt = ex->wdt;
     g13->K = H;
     g2->K = F;
+    g13->w = g2->w = NULL;
+    g13->scale = g2->scale = NULL;
+    g13->gscale = g2->gscale = 1.0;
     if (ex->wdt == ORC_NVFP4) {
-        g13->w = (const uint8_t*)ex->w13 + e * (2 * F) * (H / 2);
+        if (ex->w13) g13->w = (const uint8_t*)ex->w13 + e * (2 * F) * (H / 2);
         g2->w = (const uint8_t*)ex->w2 + e * H * (F / 2);
-        g13->scale = ex->w13_scale + e * (2 * F) * (H / 16);
+        if (ex->w13_scale) g13->scale = ex->w13_scale + e * (2 * F) * (H / 16);
         g2->scale = ex->w2_scale + e * H * (F / 16);
         g13->gscale = ex->w13_gscale ? ex->w13_gscale[e] : 1.0;
         g2->gscale = ex->w2_gscale ? ex->w2_gscale[e] : 1.0;
     } else {
         size_t es = ex->wdt == ORC_F32 ? 4 : 2;
-        g13->w = (const char*)ex->w13 + (size_t)(e * 2 * F * H) * es;
+        if (ex->w13) g13->w = (const char*)ex->w13 + (size_t)(e * 2 * F * H) * es;
         g2->w = (const char*)ex->w2 + (size_t)(e * H * F) * es;
-        g13->scale = g2->scale = NULL;
-        g13->gscale = g2->gscale = 1.0;
     }
 }
 
-/* y[0:H] = W2[e] . ( silu(W13[e][0:F] . x) * (W13[e][F:2F] . x) ), all in double. */
-static void expert_row(const experts_t* ex, int64_t e, const double* x, double* hid, double* y) {
+/* hid[0:F] = silu(W13[e][0:F] . x) * (W13[e][F:2F] . x), silu(g) = g / (1 + e^-g), in double. */
+static void gate_up_row(const experts_t* ex, int64_t e, const double* x, double* hid) {
     wmat g13, g2;
     expert_mats(ex, e, &g13, &g2);
     int64_t H = ex->H, F = ex->F;
@@ -235,6 +247,13 @@ static void expert_row(const experts_t* ex, int64_t e, const double* x, double* 
         }
         hid[f] = g / (1.0 + exp(-g)) * u;
     }
+}
+
+/* y[0:H] = W2[e] . hid, in double. */
+static void down_row(const experts_t* ex, int64_t e, const double* hid, double* y) {
+    wmat g13, g2;
+    expert_mats(ex, e, &g13, &g2);
+    int64_t H = ex->H, F = ex->F;
     for (int64_t h = 0; h < H; ++h) {
         double s = 0.0;
         for (int64_t f = 0; f < F; ++f) s += wget(&g2, h, f) * hid[f];
@@ -250,6 +269,7 @@ void oracle_expert_rows(int64_t H, int64_t F, int act_dt, int wdt, const void* x
                         const int32_t* row_token, const int32_t* row_expert, double* out,
                         double* hid_out) {
     experts_t ex = {H, F, wdt, w13, w2, w13_scale, w2_scale, w13_gscale, w2_gscale};
+    init_tables();
 #pragma omp parallel
     {
         double* xr = (double*)malloc(sizeof(double) * (size_t)H);
@@ -258,12 +278,23 @@ void oracle_expert_rows(int64_t H, int64_t F, int act_dt, int wdt, const void* x
         for (int64_t r = 0; r < nrows; ++r) {
             int64_t t = row_token[r];
             for (int64_t h = 0; h < H; ++h) xr[h] = (double)act_f(x, act_dt, t * H + h);
-            expert_row(&ex, row_expert[r], xr, hid, out + r * H);
+            gate_up_row(&ex, row_expert[r], xr, hid);
+            if (out) down_row(&ex, row_expert[r], hid, out + r * H);
             if (hid_out) memcpy(hid_out + r * F, hid, sizeof(double) * (size_t)F);
         }
         free(xr);
         free(hid);
     }
+}
+
+/* The down projection alone: out[r, 0:H] = W2[row_expert[r]] . hid[r, 0:F] (hid in double). */
+void oracle_down_rows(int64_t H, int64_t F, int wdt, const void* w2, const uint8_t* w2_scale,
+                      const float* w2_gscale, int64_t nrows, const int32_t* row_expert,
+                      const double* hid, double* out) {
+    experts_t ex = {H, F, wdt, NULL, w2, NULL, w2_scale, NULL, w2_gscale};
+    init_tables();
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; ++r) down_row(&ex, row_expert[r], hid + r * F, out + r * H);
 }
 
 /* ------------------------------------------------------------------------------------ */

@@ -57,6 +57,7 @@ def lib() -> C.CDLL:
             L.oracle_permute.argtypes = [i64, i32, i64, vp, vp, vp, vp, vp]
             L.oracle_expert_rows.argtypes = [i64, i64, i32, i32, vp, vp, vp, vp, vp, vp, vp, i64,
                                              vp, vp, vp, vp]
+            L.oracle_down_rows.argtypes = [i64, i64, i32, vp, vp, vp, i64, vp, vp, vp]
             L.oracle_combine.argtypes = [i64, i32, i64, vp, vp, vp, vp]
             for n in ("oracle_decode_bf16", "oracle_decode_e2m1", "oracle_decode_e4m3"):
                 getattr(L, n).argtypes = [vp, vp, i64]
@@ -164,6 +165,30 @@ def expert_rows(inputs: dict, wdt: str, ffn: int, row_token, row_expert, want_hi
     lib().oracle_expert_rows(H, ffn, _act_dt(x), _DT[wdt], _P(x), _P(w13), _P(w2), _P(s13), _P(s2),
                              _P(g13), _P(g2), n, _P(rt), _P(re), _P(out), _P(hid))
     return (out, hid) if want_hid else out
+
+
+def gate_up_rows(inputs: dict, wdt: str, ffn: int, row_token, row_expert):
+    """hid[n, F] = silu(gate) * up of the given (token, expert) rows, in double."""
+    x = np.ascontiguousarray(inputs["x"])
+    rt = np.ascontiguousarray(row_token, dtype=np.int32)
+    re = np.ascontiguousarray(row_expert, dtype=np.int32)
+    hid = np.empty((rt.size, ffn), dtype=np.float64)
+    g = lambda k: None if inputs.get(k) is None else np.ascontiguousarray(inputs[k])
+    lib().oracle_expert_rows(x.shape[1], ffn, _act_dt(x), _DT[wdt], _P(x), _P(g("w13")), _P(g("w2")),
+                             _P(g("w13_scale")), _P(g("w2_scale")), _P(g("w13_gscale")),
+                             _P(g("w2_gscale")), rt.size, _P(rt), _P(re), None, _P(hid))
+    return hid
+
+
+def down_rows(inputs: dict, wdt: str, hidden: int, hid: np.ndarray, row_expert):
+    """out[n, H] = W2[e] . hid[n] for the given rows (hid given as double)."""
+    h = np.ascontiguousarray(hid, dtype=np.float64)
+    re = np.ascontiguousarray(row_expert, dtype=np.int32)
+    out = np.empty((re.size, hidden), dtype=np.float64)
+    g = lambda k: None if inputs.get(k) is None else np.ascontiguousarray(inputs[k])
+    lib().oracle_down_rows(hidden, h.shape[1], _DT[wdt], _P(g("w2")), _P(g("w2_scale")),
+                           _P(g("w2_gscale")), re.size, _P(re), _P(h), _P(out))
+    return out
 
 
 def combine(y_perm: np.ndarray, inv_perm: np.ndarray, w: np.ndarray) -> np.ndarray:

@@ -1,0 +1,106 @@
+"""The C-ABI library on the host (no GPU): it loads, exports every symbol ``include/moe.h``
+declares, and rejects bad arguments before touching the device."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from mixture_experts_layer_softmax_amd import lib, synth
+
+HEADER = os.path.join(os.path.dirname(__file__), "..", "include", "moe.h")
+
+
+def declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(moe_\w+)\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(lib.LIB_PATH):
+        from mixture_experts_layer_softmax_amd import build
+
+        build.build()
+    return lib.load()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared()
+    assert set(names) == set(lib.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    assert lib.status_string(lib.MOE_OK) == "ok"
+    assert "workspace" in lib.status_string(lib.MOE_ERR_WORKSPACE_TOO_SMALL)
+    assert lib.status_string(99) == "unknown status"
+
+
+@pytest.mark.parametrize("name", sorted(synth.WORKLOADS))
+def test_workspace_size_of_every_workload(L, name):
+    wl = synth.WORKLOADS[name]
+    p = lib.problem(wl.tokens, wl.hidden, wl.experts, wl.top_k, wl.ffn, wl.act, wl.wdt)
+    n = lib.workspace_size(p)
+    A = wl.assignments
+    # the intermediates dominate: hid [A,F] and y_perm [A,H]
+    act = 4 if wl.act == "f32" else 2
+    assert n >= A * (wl.ffn + wl.hidden) * act
+    assert n < A * (wl.ffn + wl.hidden) * act + 64 * 2 ** 20
+
+
+FAKE = 1 << 20  # an aligned address that is never dereferenced: validation fails first
+
+
+def _call_route(L, p, x=FAKE, wr=FAKE, ids=FAKE, w=FAKE, ws=FAKE, nbytes=1 << 40):
+    V = C.c_void_p
+    return L.moe_route(C.byref(p), V(x) if x else None, V(wr) if wr else None, None,
+                       V(ids) if ids else None, V(w) if w else None, V(ws) if ws else None,
+                       nbytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(tokens=-1), lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(top_k=0), lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(top_k=9, experts=8), lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(top_k=17, experts=64), lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(experts=513), lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(hidden=100), lib.MOE_ERR_UNSUPPORTED),
+    (dict(ffn=96), lib.MOE_ERR_UNSUPPORTED),
+    (dict(act="f32", wdt="bf16"), lib.MOE_ERR_UNSUPPORTED),
+    (dict(act="bf16", wdt="f32"), lib.MOE_ERR_UNSUPPORTED),
+    (dict(act="f32", wdt="nvfp4"), lib.MOE_ERR_UNSUPPORTED),
+])
+def test_problem_validation(L, kw, status):
+    base = dict(tokens=16, hidden=256, experts=8, top_k=2, ffn=128, act="bf16", wdt="bf16")
+    base.update(kw)
+    p = lib.problem(**base)
+    assert _call_route(L, p) == status
+    n = C.c_size_t()
+    assert L.moe_workspace_size(C.byref(p), C.byref(n)) == status
+
+
+def test_pointer_validation(L):
+    p = lib.problem(16, 256, 8, 2, 128)
+    assert _call_route(L, p, x=0) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert _call_route(L, p, ids=0) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert _call_route(L, p, x=FAKE + 2) == lib.MOE_ERR_INVALID_ARGUMENT  # misaligned
+    assert _call_route(L, p, ws=0) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert _call_route(L, p, nbytes=100) == lib.MOE_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_gemm_and_forward_validation(L):
+    V = C.c_void_p
+    p = lib.problem(16, 256, 8, 2, 128, wdt="nvfp4")
+    w = lib.ExpertWeights(FAKE, FAKE, None, None, None, None)  # NVFP4 without scales
+    assert L.moe_grouped_gemm(C.byref(p), 0, V(FAKE), None, V(FAKE), C.byref(w), V(FAKE), V(FAKE),
+                              1 << 40, None) == lib.MOE_ERR_INVALID_ARGUMENT
+    w = lib.ExpertWeights(FAKE, FAKE, FAKE, FAKE, None, None)
+    assert L.moe_grouped_gemm(C.byref(p), 7, V(FAKE), None, V(FAKE), C.byref(w), V(FAKE), V(FAKE),
+                              1 << 40, None) == lib.MOE_ERR_INVALID_ARGUMENT  # bad kind
+    assert L.moe_grouped_gemm(C.byref(p), 1, V(FAKE), V(FAKE), V(FAKE), C.byref(w), V(FAKE),
+                              V(FAKE), 1 << 40, None) == lib.MOE_ERR_INVALID_ARGUMENT  # down + gather
+    assert L.moe_forward(C.byref(p), V(FAKE), V(FAKE), None, C.byref(w), V(FAKE), None, None, None,
+                         None, None, None, V(FAKE), 10, None) == lib.MOE_ERR_WORKSPACE_TOO_SMALL
+    assert L.moe_combine(C.byref(p), None, V(FAKE), V(FAKE), V(FAKE), None) == lib.MOE_ERR_INVALID_ARGUMENT

@@ -1,0 +1,400 @@
+"""GPU parity: every C-ABI entry point against the CPU oracle on seeded inputs.
+
+Bar: expert ids, counts, offsets, sorted_token and inv_perm bit-exact; routing weights within
+1e-5 relative; layer outputs within 2e-2 max relative error (max|y - ref| / max|ref|).
+Small shapes run the oracle on everything; the full-size workloads check routing and dispatch
+on every token and the layer output on a sample of tokens.
+"""
+import numpy as np
+import pytest
+import torch
+
+from mixture_experts_layer_softmax_amd import lib, synth
+from mixture_experts_layer_softmax_amd.layer import MoELayer, bf16_bits_to_f64, to_device, to_host
+from oracle import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+W_RTOL = 1e-5
+W = synth.Workload
+
+# small shapes spanning several row tiles with ragged tails and skewed expert loads
+SMALL = {
+    "small_bf16": W("small_bf16", 512, 512, 8, 2, 256, "bf16", "bf16", 11, "normal"),
+    "small_nvfp4": W("small_nvfp4", 384, 512, 16, 4, 256, "bf16", "nvfp4", 12, "normal"),
+    "ragged_bf16": W("ragged_bf16", 77, 192, 5, 3, 320, "bf16", "bf16", 13, "normal"),
+    "ragged_nvfp4": W("ragged_nvfp4", 77, 192, 5, 3, 320, "bf16", "nvfp4", 14, "normal"),
+    "tiny": synth.WORKLOADS["tiny"],
+}
+
+
+def note(msg):
+    print("[gpu] " + msg, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _env():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    lib.load()
+    O.build()
+
+
+_CACHE = {}
+
+
+def inputs_of(wl):
+    key = (wl.name, wl.tokens, wl.x_sub)
+    if key not in _CACHE:
+        _CACHE.clear()
+        _CACHE[key] = synth.generate(wl)
+    return _CACHE[key]
+
+
+def act_f64(a):
+    return a.astype(np.float64) if a.dtype == np.float32 else bf16_bits_to_f64(a)
+
+
+def rel_err(y, ref):
+    return float(np.max(np.abs(y - ref)) / max(float(np.max(np.abs(ref))), 1e-30))
+
+
+def dev_i32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+
+# ---------------------------------------------------------------------------------------
+# route
+# ---------------------------------------------------------------------------------------
+
+ROUTE_CASES = ["tiny", "small_bf16", "small_nvfp4", "ragged_bf16", "decode1", "decode8",
+               "decode64", "nvfp4_decode", "prefill", "nvfp4_prefill"]
+
+
+@pytest.mark.parametrize("name", ROUTE_CASES)
+def test_route_matches_oracle(name):
+    wl = SMALL.get(name) or synth.WORKLOADS[name]
+    inp = synth.generate(wl, with_experts=False)
+    note("route %s T=%d E=%d k=%d" % (name, wl.tokens, wl.experts, wl.top_k))
+    ref = O.route(inp, wl.top_k)
+    p = lib.problem(wl.tokens, wl.hidden, wl.experts, wl.top_k, wl.ffn, wl.act, wl.wdt)
+    ws = torch.empty(lib.workspace_size(p), dtype=torch.uint8, device="cuda")
+    ids = torch.empty(wl.tokens, wl.top_k, dtype=torch.int32, device="cuda")
+    w = torch.empty(wl.tokens, wl.top_k, dtype=torch.float32, device="cuda")
+    kind = "bf16" if wl.act == "bf16" else None
+    lib.route(p, to_device(inp["x"], "cuda", kind), to_device(inp["w_router"], "cuda", kind),
+              to_device(inp["bias"], "cuda"), ids, w, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(ids.cpu().numpy(), ref["topk_ids"])
+    np.testing.assert_allclose(w.cpu().numpy(), ref["topk_w"], rtol=W_RTOL, atol=0)
+
+
+def test_route_small_and_large_batch_kernels_agree():
+    """Batches under 64 tokens use one-token wavefronts, larger ones 8x8 blocks: same logits."""
+    wl = synth.WORKLOADS["decode64"]
+    inp = synth.generate(wl, with_experts=False)
+    p64 = lib.problem(64, wl.hidden, wl.experts, wl.top_k, wl.ffn)
+    p63 = lib.problem(63, wl.hidden, wl.experts, wl.top_k, wl.ffn)
+    ws = torch.empty(lib.workspace_size(p64), dtype=torch.uint8, device="cuda")
+    x = to_device(inp["x"], "cuda", "bf16")
+    wr = to_device(inp["w_router"], "cuda", "bf16")
+    out = []
+    for p, T in ((p64, 64), (p63, 63)):
+        ids = torch.empty(T, wl.top_k, dtype=torch.int32, device="cuda")
+        w = torch.empty(T, wl.top_k, dtype=torch.float32, device="cuda")
+        lib.route(p, x[:T], wr, None, ids, w, ws)
+        out.append((ids.cpu().numpy(), w.cpu().numpy()))
+    assert np.array_equal(out[0][0][:63], out[1][0])
+    assert np.array_equal(out[0][1][:63], out[1][1])
+
+
+# ---------------------------------------------------------------------------------------
+# dispatch
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,E,k", [(1, 8, 2), (63, 128, 8), (64, 128, 8), (65, 256, 8),
+                                   (1000, 128, 8), (300, 512, 16), (5, 4, 4), (4096, 128, 8)])
+def test_permute_matches_oracle(T, E, k):
+    rng = np.random.default_rng(T * 1000 + E + k)
+    # skewed loads: draw experts with unequal probabilities, distinct within a token
+    pr = rng.dirichlet(np.full(E, 0.3))
+    ids = np.array([rng.choice(E, size=k, replace=False, p=pr) for _ in range(T)], dtype=np.int32)
+    H = 64
+    x = synth.to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    note("permute T=%d E=%d k=%d" % (T, E, k))
+    counts, offsets, st, ip = O.permute(ids, E)
+    p = lib.problem(T, H, E, k, 64)
+    ws = torch.empty(lib.workspace_size(p), dtype=torch.uint8, device="cuda")
+    g = dict(counts=torch.empty(E, dtype=torch.int32, device="cuda"),
+             offsets=torch.empty(E + 1, dtype=torch.int32, device="cuda"),
+             sorted_token=torch.empty(T * k, dtype=torch.int32, device="cuda"),
+             inv_perm=torch.empty(T * k, dtype=torch.int32, device="cuda"))
+    xd = to_device(x, "cuda", "bf16")
+    x_perm = torch.empty(T * k, H, dtype=torch.bfloat16, device="cuda")
+    lib.permute(p, dev_i32(ids), g["counts"], g["offsets"], g["sorted_token"], g["inv_perm"], ws,
+                x=xd, x_perm=x_perm)
+    torch.cuda.synchronize()
+    assert np.array_equal(g["counts"].cpu().numpy(), counts)
+    assert np.array_equal(g["offsets"].cpu().numpy(), offsets)
+    assert np.array_equal(g["sorted_token"].cpu().numpy(), st)
+    assert np.array_equal(g["inv_perm"].cpu().numpy(), ip)
+    assert np.array_equal(to_host(x_perm), x[st])
+
+
+# ---------------------------------------------------------------------------------------
+# grouped GEMMs
+# ---------------------------------------------------------------------------------------
+
+def _routed(wl, inp):
+    r = O.route(inp, wl.top_k)
+    expert_of_row = np.repeat(np.arange(wl.experts), r["counts"]).astype(np.int32)
+    return r, expert_of_row
+
+
+@pytest.mark.parametrize("name", ["tiny", "small_bf16", "small_nvfp4", "ragged_bf16", "ragged_nvfp4"])
+@pytest.mark.parametrize("path", ["prefill", "decode"])
+def test_gate_up_matches_oracle(name, path):
+    wl = SMALL[name]
+    inp = inputs_of(wl)
+    note("gate_up %s path=%s" % (name, path))
+    r, eor = _routed(wl, inp)
+    ref = O.gate_up_rows(inp, wl.wdt, wl.ffn, r["sorted_token"], eor)
+    layer = MoELayer.from_workload(wl, inp, path=path)
+    p = layer.problem_for(wl.tokens)
+    ws = layer.workspace(wl.tokens)
+    A = wl.assignments
+    hid = layer.empty_act(A, wl.ffn)
+    x = layer.act_tensor(inp["x"])
+    lib.grouped_gemm(p, lib.GATE_UP_SWIGLU, x, dev_i32(r["sorted_token"]), dev_i32(r["offsets"]),
+                     layer.weights, hid, ws)
+    # the same rows handed over already permuted (a_rows = NULL)
+    x_perm = x[torch.from_numpy(r["sorted_token"].astype(np.int64)).cuda()].contiguous()
+    hid2 = layer.empty_act(A, wl.ffn)
+    lib.grouped_gemm(p, lib.GATE_UP_SWIGLU, x_perm, None, dev_i32(r["offsets"]), layer.weights,
+                     hid2, ws)
+    torch.cuda.synchronize()
+    got = act_f64(to_host(hid))
+    e = rel_err(got, ref)
+    note("  gate_up rel err %.3e" % e)
+    assert e <= TOL
+    assert torch.equal(hid, hid2)
+
+
+@pytest.mark.parametrize("name", ["tiny", "small_bf16", "small_nvfp4", "ragged_bf16", "ragged_nvfp4"])
+@pytest.mark.parametrize("path", ["prefill", "decode"])
+def test_down_matches_oracle(name, path):
+    wl = SMALL[name]
+    inp = inputs_of(wl)
+    note("down %s path=%s" % (name, path))
+    r, eor = _routed(wl, inp)
+    rng = np.random.default_rng(5)
+    A = wl.assignments
+    hid_host = rng.standard_normal((A, wl.ffn)).astype(np.float32) * 0.05
+    if wl.act == "bf16":
+        hid_host = synth.to_bf16_bits(hid_host)
+    ref = O.down_rows(inp, wl.wdt, wl.hidden, act_f64(hid_host), eor)
+    layer = MoELayer.from_workload(wl, inp, path=path)
+    p = layer.problem_for(wl.tokens)
+    ws = layer.workspace(wl.tokens)
+    y_perm = layer.empty_act(A, wl.hidden)
+    lib.grouped_gemm(p, lib.DOWN, layer.act_tensor(hid_host), None, dev_i32(r["offsets"]),
+                     layer.weights, y_perm, ws)
+    torch.cuda.synchronize()
+    e = rel_err(act_f64(to_host(y_perm)), ref)
+    note("  down rel err %.3e" % e)
+    assert e <= TOL
+
+
+@pytest.mark.parametrize("wdt", ["bf16", "nvfp4"])
+@pytest.mark.parametrize("path", ["prefill", "decode"])
+def test_down_with_one_hot_rows_returns_exact_weights(wdt, path):
+    """hid row r = unit vector at f_r: y_perm[r, h] must be W2[e][h, f_r] exactly (the 4-bit
+    value decodes exactly to bf16), which pins the weight decode and the tile index maps."""
+    E, H, F = 3, 192, 128
+    wl = W("onehot", 1, H, E, 1, F, "bf16", wdt, 21, "none")
+    inp = synth.generate(wl)
+    inp.pop("w13_gscale", None)
+    inp.pop("w2_gscale", None)  # per-expert scale 1.0: the product stays exact
+    A = E * F
+    f_of_row = np.tile(np.arange(F), E)
+    e_of_row = np.repeat(np.arange(E), F).astype(np.int32)
+    hid = np.zeros((A, F), np.float32)
+    hid[np.arange(A), f_of_row] = 1.0
+    hid_bits = synth.to_bf16_bits(hid)
+    ref = O.down_rows(inp, wdt, H, act_f64(hid_bits), e_of_row)
+    layer = MoELayer(A, H, E, 1, F, "bf16", wdt, inp, path=path)
+    p = layer.problem_for(A)
+    ws = layer.workspace(A)
+    y_perm = layer.empty_act(A, H)
+    offsets = np.arange(E + 1, dtype=np.int32) * F
+    note("one-hot down wdt=%s path=%s" % (wdt, path))
+    lib.grouped_gemm(p, lib.DOWN, layer.act_tensor(hid_bits), None, dev_i32(offsets), layer.weights,
+                     y_perm, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(act_f64(to_host(y_perm)), ref)
+
+
+# ---------------------------------------------------------------------------------------
+# combine
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+def test_combine_matches_oracle(act):
+    rng = np.random.default_rng(7)
+    T, k, H = 300, 8, 256
+    A = T * k
+    ip = rng.permutation(A).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    yp = rng.standard_normal((A, H)).astype(np.float32)
+    if act == "bf16":
+        yp = synth.to_bf16_bits(yp)
+    ref = O.combine(act_f64(yp), ip, w.astype(np.float64))
+    p = lib.problem(T, H, 16, k, 64, act, act)
+    y = torch.empty(T, H, dtype=torch.float32 if act == "f32" else torch.bfloat16, device="cuda")
+    note("combine act=%s" % act)
+    lib.combine(p, to_device(yp, "cuda"), dev_i32(ip), to_device(w, "cuda"), y)
+    torch.cuda.synchronize()
+    e = rel_err(act_f64(to_host(y)), ref)
+    assert e <= (1e-6 if act == "f32" else 8e-3)
+
+
+# ---------------------------------------------------------------------------------------
+# the whole layer
+# ---------------------------------------------------------------------------------------
+
+def _check_forward(wl, inp, layer, tokens=None, path=None):
+    x = layer.act_tensor(inp["x"])
+    y, dbg = layer.forward(x, debug=True, path=path)
+    torch.cuda.synchronize()
+    ref = O.forward(inp, wl.top_k, wl.wdt, wl.ffn, wl.renormalize, tokens=tokens)
+    for key in ("topk_ids", "counts", "offsets", "sorted_token", "inv_perm"):
+        got = dbg[key].cpu().numpy()
+        assert np.array_equal(got.reshape(ref[key].shape), ref[key]), key
+    np.testing.assert_allclose(dbg["topk_w"].cpu().numpy(), ref["topk_w"], rtol=W_RTOL, atol=0)
+    got = act_f64(to_host(y))[ref["tokens"]]
+    e = rel_err(got, ref["y"])
+    note("  %s y rel err %.3e over %d tokens" % (wl.name, e, len(ref["tokens"])))
+    assert e <= TOL
+    return y
+
+
+FWD_CASES = ["tiny", "small_bf16", "small_nvfp4", "ragged_bf16", "ragged_nvfp4", "decode1",
+             "decode8", "nvfp4_decode"]
+
+
+@pytest.mark.parametrize("name", FWD_CASES)
+def test_forward_matches_oracle(name):
+    wl = SMALL.get(name) or synth.WORKLOADS[name]
+    inp = inputs_of(wl)
+    note("forward %s" % name)
+    layer = MoELayer.from_workload(wl, inp)
+    _check_forward(wl, inp, layer)
+
+
+@pytest.mark.parametrize("name,sample", [("decode64", 16), ("prefill", 12), ("nvfp4_prefill", 12)])
+def test_forward_full_size_sampled(name, sample):
+    wl = synth.WORKLOADS[name]
+    note("forward full size %s: generating inputs" % name)
+    inp = inputs_of(wl)
+    layer = MoELayer.from_workload(wl, inp)
+    rng = np.random.default_rng(99)
+    toks = np.unique(np.concatenate([[0, wl.tokens - 1], rng.choice(wl.tokens, sample - 2, replace=False)]))
+    note("forward full size %s: running" % name)
+    _check_forward(wl, inp, layer, tokens=toks)
+    del layer
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", ["small_bf16", "small_nvfp4"])
+def test_prefill_and_decode_paths_agree(name):
+    wl = SMALL[name]
+    inp = inputs_of(wl)
+    layer = MoELayer.from_workload(wl, inp)
+    x = layer.act_tensor(inp["x"])
+    note("paths %s" % name)
+    ya, da = layer.forward(x, debug=True, path="prefill")
+    ya = ya.clone()
+    yb, db = layer.forward(x, debug=True, path="decode")
+    torch.cuda.synchronize()
+    for key in ("topk_ids", "topk_w", "counts", "offsets", "sorted_token", "inv_perm"):
+        assert torch.equal(da[key], db[key]), key
+    assert rel_err(act_f64(to_host(ya)), act_f64(to_host(yb))) <= TOL
+
+
+def test_forward_is_deterministic_and_scales_exactly():
+    wl = SMALL["small_bf16"]
+    inp = dict(inputs_of(wl))
+    layer = MoELayer.from_workload(wl, inp)
+    x = layer.act_tensor(inp["x"])
+    note("determinism")
+    y1 = layer.forward(x).clone()
+    y2 = layer.forward(x).clone()
+    assert torch.equal(y1, y2)
+    # doubling the down weights (exact in bf16) doubles every output exactly
+    inp2 = dict(inp)
+    inp2["w2"] = synth.to_bf16_bits(bf16_bits_to_f64(inp["w2"]).astype(np.float32) * 2)
+    layer2 = MoELayer.from_workload(wl, inp2)
+    y3 = layer2.forward(x)
+    torch.cuda.synchronize()
+    assert torch.equal(y3.float(), (y1.float() * 2))
+
+
+def test_token_permutation_permutes_outputs():
+    wl = SMALL["small_bf16"]
+    inp = inputs_of(wl)
+    layer = MoELayer.from_workload(wl, inp)
+    perm = np.random.default_rng(3).permutation(wl.tokens)
+    note("token permutation")
+    y = layer.forward(layer.act_tensor(inp["x"])).clone()
+    yp = layer.forward(layer.act_tensor(inp["x"][perm]))
+    torch.cuda.synchronize()
+    assert torch.equal(yp, y[torch.from_numpy(perm).cuda()])
+
+
+# ---------------------------------------------------------------------------------------
+# edge cases
+# ---------------------------------------------------------------------------------------
+
+def test_zero_tokens_is_a_no_op():
+    wl = SMALL["small_bf16"]
+    layer = MoELayer.from_workload(wl, inputs_of(wl))
+    x = layer.empty_act(0, wl.hidden)
+    y, dbg = layer.forward(x, debug=True)
+    torch.cuda.synchronize()
+    assert y.shape == (0, wl.hidden)
+    assert int(dbg["counts"].abs().sum()) == 0 and int(dbg["offsets"].abs().sum()) == 0
+
+
+@pytest.mark.parametrize("wdt", ["bf16", "nvfp4"])
+def test_all_tokens_on_the_same_experts(wdt):
+    wl = W("hot", 200, 256, 8, 2, 128, "bf16", wdt, 31, "normal")
+    inp = synth.generate(wl)
+    inp["bias"] = np.zeros(8, np.float32)
+    inp["bias"][[6, 1]] = 1e4
+    note("all tokens on experts 1, 6 wdt=%s" % wdt)
+    layer = MoELayer.from_workload(wl, inp)
+    _check_forward(wl, inp, layer)
+
+
+@pytest.mark.parametrize("E,k", [(4, 4), (1, 1), (16, 16)])
+def test_k_equals_e(E, k):
+    wl = W("keqe", 40, 128, E, k, 64, "bf16", "bf16", 41 + E, "normal")
+    inp = synth.generate(wl)
+    note("k=E=%d" % E)
+    _check_forward(wl, inp, MoELayer.from_workload(wl, inp))
+
+
+def test_full_softmax_weights_option():
+    wl = W("nr", 50, 128, 8, 3, 64, "bf16", "bf16", 51, "normal", renormalize=False)
+    inp = synth.generate(wl)
+    note("renormalize=0")
+    _check_forward(wl, inp, MoELayer.from_workload(wl, inp))
+
+
+def test_single_token_prefill_path_and_large_batch_decode_path():
+    for T, path in ((1, "prefill"), (600, "decode")):
+        wl = W("force", T, 256, 32, 4, 128, "bf16", "nvfp4", 61, "normal")
+        inp = synth.generate(wl)
+        note("forced path %s T=%d" % (path, T))
+        _check_forward(wl, inp, MoELayer.from_workload(wl, inp, path=path))
