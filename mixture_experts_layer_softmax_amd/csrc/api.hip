@@ -65,7 +65,7 @@ Layout layout(const moe_problem& p) {
     const size_t A = T * k;
     const size_t nch = (T + kChunkTokens - 1) / kChunkTokens;
     L.family = family_of(p);
-    L.bm = gemm_tile_rows(L.family);
+    L.bm = gemm_tile_rows(L.family, p.w_dtype == MOE_F32 ? kWF32 : p.w_dtype == MOE_BF16 ? kWBF16 : kWNVFP4, p.ffn);
     L.max_tiles = int((A + L.bm - 1) / L.bm + (A < E ? A : E) + 1);
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t r = o; o += up(bytes > 0 ? bytes : 1); return r; };

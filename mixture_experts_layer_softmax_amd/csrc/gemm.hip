@@ -18,6 +18,9 @@
 // NVFP4 weights (E2M1 nibbles, E4M3 scale per 16 along K, fp32 per-expert scale) are decoded
 // on the way into LDS: e2m1 * e4m3 has at most 6 significant bits, so it is exact in bf16 and
 // the MFMA sees the exact weight; the per-expert scale multiplies the fp32 accumulator.
+#include <tuple>
+#include <type_traits>
+
 #include "device.h"
 #include "launch.h"
 
@@ -234,6 +237,556 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmArgs g) {
         }
 }
 
+// ---------------------------------------------------------------------------------------
+// Prefill kernel, bf16 weights: 256 x 128 block tile, 4 wavefronts (2 x 2) of 128 x 64,
+// K in 64-wide stages through a 3-slot LDS ring filled by direct global->LDS loads
+// (global_load_lds_dwordx4: each wavefront instruction moves 8 rows x 128 bytes straight into
+// LDS without passing through registers), so two stages are in flight while the third is
+// consumed.  The XOR swizzle is applied on the global side: lane l of an instruction lands at
+// LDS chunk l, so it fetches the source chunk that belongs there.  Each slot is its own LDS
+// object so that the compiler can tell the slots apart and does not wait for in-flight loads
+// before reading the current one; waits on the load counter are explicit.
+//
+// The 16 row-groups of 16 rows are interleaved over the two wavefront rows, and groups past
+// the tile's last row skip their MFMAs, so a ragged expert tail costs MFMA time in proportion
+// to its rows (the tile height adapts to skewed expert loads in steps of 16 rows).
+// ---------------------------------------------------------------------------------------
+
+namespace {
+
+constexpr int vm_wait_lgkm0(int n) { return (n & 15) | (7 << 4) | (0 << 8) | ((n >> 4) << 14); }
+
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+    __builtin_amdgcn_s_waitcnt(vm_wait_lgkm0(N));
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane l writes lds_base + 16*l.
+// Issued through inline asm (setting M0 itself) so that the compiler does not treat the
+// write as pending LDS data and wait for it before unrelated LDS reads; the caller owns the
+// load counter.  M0 has no other use in the kernels that call this.
+__device__ __forceinline__ void dma16(const void* src, const void* lds_base) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+        static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_base)));
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(m0)
+                 : "memory");
+}
+
+}  // namespace
+
+template <int KIND>
+__global__ __launch_bounds__(256, 1) void gemm_prefill_bf16_kernel(GemmArgs g) {
+    constexpr int BM = 256, BN = 128;
+    constexpr int A_DMA = BM / 8 / 4;  // 8-row groups per wavefront per stage
+    constexpr int B_DMA = BN / 8 / 4;
+    constexpr int LOADS = A_DMA + B_DMA;
+    __shared__ uint4 sA0[BM * 8], sA1[BM * 8], sA2[BM * 8];
+    __shared__ uint4 sB0[BN * 8], sB1[BN * 8], sB2[BN * 8];
+
+    // XCD-aware work order.  Workgroups go to the 8 XCDs round-robin by block index, and each
+    // XCD has its own L2.  The (tile, column-tile) items, tile-major, are cut into 8 contiguous
+    // runs and XCD x walks run x, so all column tiles of a row tile run on one XCD at about
+    // the same time and share its gathered activation rows in that XCD's L2.
+    const int ncols = (KIND == kGateUp) ? g.F / 64 : (g.N + BN - 1) / BN;
+    const int items = *g.tile_count * ncols;
+    const int run = (items + 7) >> 3;
+    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+    const int item = xcd * run + j;
+    if (j >= run || item >= items) return;
+    const Tile tile = g.tiles[item / ncols];
+    const int e = tile.expert, r0 = tile.row0, r1 = tile.row1;
+    const int nsub = (r1 - r0 + 15) / 16;
+    const int nt = item % ncols;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
+    const int wr = wave >> 1, wc = wave & 1;
+    const int K = g.K;
+    const int Nw = (KIND == kGateUp) ? 2 * g.F : g.N;
+
+    // per-lane source pointers (bytes) of the chunks this lane moves each stage
+    const char* pa[A_DMA];
+    const char* pb[B_DMA];
+#pragma unroll
+    for (int i = 0; i < A_DMA; ++i) {
+        const int row = (i * 4 + wave) * 8 + (lane >> 3);
+        const int ch = (lane & 7) ^ (row & 7);
+        const int rr = min(r0 + row, r1 - 1);
+        int src = g.a_rows ? g.a_rows[rr] : rr;
+        src = src < 0 ? 0 : (src >= g.a_rows_limit ? g.a_rows_limit - 1 : src);
+        pa[i] = static_cast<const char*>(g.a) + (size_t(src) * K + ch * 8) * 2;
+    }
+#pragma unroll
+    for (int i = 0; i < B_DMA; ++i) {
+        const int row = (i * 4 + wave) * 8 + (lane >> 3);
+        const int ch = (lane & 7) ^ (row & 7);
+        int wrow;
+        if (KIND == kGateUp) {
+            const int q = row & 63;
+            const int f = nt * 64 + (row >> 6) * 32 + (q & 31);
+            wrow = q < 32 ? f : g.F + f;
+        } else {
+            wrow = min(nt * BN + row, g.N - 1);
+        }
+        pb[i] = static_cast<const char*>(g.w) + ((size_t(e) * Nw + wrow) * K + ch * 8) * 2;
+    }
+
+#define MOE_ISSUE(SA, SB, K0)                                                                   \
+    do {                                                                                        \
+        const int k0_ = (K0);                                                                   \
+        _Pragma("unroll") for (int i = 0; i < A_DMA; ++i)                                       \
+            dma16(pa[i] + k0_ * 2, &SA[(i * 4 + wave) * 64]);                                   \
+        _Pragma("unroll") for (int i = 0; i < B_DMA; ++i)                                       \
+            dma16(pb[i] + k0_ * 2, &SB[(i * 4 + wave) * 64]);                                   \
+    } while (0)
+
+    f32x4_t acc[8][4];
+#pragma unroll
+    for (int mi = 0; mi < 8; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+#define MOE_COMPUTE(SA, SB)                                                                     \
+    do {                                                                                        \
+        _Pragma("unroll") for (int ks = 0; ks < 2; ++ks) {                                      \
+            const int ch = ks * 4 + (lane >> 4);                                                \
+            bf16x8_t bf[4];                                                                     \
+            _Pragma("unroll") for (int ni = 0; ni < 4; ++ni) bf[ni] =                           \
+                __builtin_bit_cast(bf16x8_t, SB[lds_slot(wc * 64 + ni * 16 + (lane & 15), ch)]); \
+            _Pragma("unroll") for (int mi = 0; mi < 8; ++mi) {                                  \
+                if (mi * 2 + wr < nsub) {                                                       \
+                    const bf16x8_t af = __builtin_bit_cast(                                     \
+                        bf16x8_t, SA[lds_slot((mi * 2 + wr) * 16 + (lane & 15), ch)]);          \
+                    _Pragma("unroll") for (int ni = 0; ni < 4; ++ni) acc[mi][ni] =              \
+                        __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[ni], acc[mi][ni], 0, 0, 0); \
+                }                                                                               \
+            }                                                                                   \
+        }                                                                                       \
+    } while (0)
+
+    // Every step issues the same number of loads (past the last stage they re-read the last
+    // stage into the free slot), so the load counter always holds exactly one stage after the
+    // current one and a fixed wait count is exact.
+    const int nk = K / BK;
+    const int last = (nk - 1) * BK;
+    MOE_ISSUE(sA0, sB0, 0);
+    MOE_ISSUE(sA1, sB1, min(BK, last));
+    for (int kt = 0;; kt += 3) {
+        wait_vm_lgkm0<LOADS>();  // slot 0 = stage kt
+        block_barrier();
+        MOE_ISSUE(sA2, sB2, min((kt + 2) * BK, last));
+        MOE_COMPUTE(sA0, sB0);
+        if (kt + 1 >= nk) break;
+        wait_vm_lgkm0<LOADS>();  // slot 1 = stage kt+1
+        block_barrier();
+        MOE_ISSUE(sA0, sB0, min((kt + 3) * BK, last));
+        MOE_COMPUTE(sA1, sB1);
+        if (kt + 2 >= nk) break;
+        wait_vm_lgkm0<LOADS>();  // slot 2 = stage kt+2
+        block_barrier();
+        MOE_ISSUE(sA1, sB1, min((kt + 4) * BK, last));
+        MOE_COMPUTE(sA2, sB2);
+        if (kt + 3 >= nk) break;
+    }
+    wait_vm_lgkm0<0>();  // no load may still be writing LDS when the block ends
+#undef MOE_ISSUE
+#undef MOE_COMPUTE
+
+    uint16_t* out = static_cast<uint16_t*>(g.out);
+#pragma unroll
+    for (int mi = 0; mi < 8; ++mi) {
+        if (mi * 2 + wr >= nsub) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = r0 + (mi * 2 + wr) * 16 + 4 * (lane >> 4) + i;
+            if (row >= r1) continue;
+            if (KIND == kGateUp) {
+#pragma unroll
+                for (int ni = 0; ni < 2; ++ni) {
+                    const int col = nt * 64 + wc * 32 + ni * 16 + (lane & 15);
+                    out[size_t(row) * g.F + col] = (uint16_t)bf16_rne(silu_mul(acc[mi][ni][i], acc[mi][ni + 2][i]));
+                }
+            } else {
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni) {
+                    const int col = nt * BN + wc * 64 + ni * 16 + (lane & 15);
+                    if (col < g.N) out[size_t(row) * g.N + col] = (uint16_t)bf16_rne(acc[mi][ni][i]);
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Prefill kernel v2, bf16 weights: 256 x 256 block tile, 4 wavefronts (2 x 2) of 128 x 128
+// (256 fp32 accumulators per lane, held in AGPRs), K in 32-wide stages.  A 4-slot LDS ring
+// (4 x 32 KiB) is filled by direct global->LDS loads, so three stages are in flight while
+// one is consumed, and the operand fragments of the next stage are read from LDS into
+// registers while the 64 MFMAs of the current stage run.  Rows are 64 bytes in LDS; the
+// 16-byte chunk c of row r sits in slot c ^ ((r >> 1) & 3), which keeps the fragment reads
+// (8 consecutive rows, one chunk) on distinct banks.
+// ---------------------------------------------------------------------------------------
+
+namespace {
+__device__ __forceinline__ int lds_slot32(int row, int ch) { return row * 4 + (ch ^ ((row >> 1) & 3)); }
+}  // namespace
+
+template <int KIND>
+__global__ __launch_bounds__(256, 1) void gemm_prefill_bf16_v2_kernel(GemmArgs g) {
+    constexpr int BM = 256, BN = 256, BKS = 32;
+    constexpr int A_DMA = BM / 16 / 4;  // 16-row groups (1 KiB) per wavefront per stage
+    constexpr int B_DMA = BN / 16 / 4;
+    constexpr int LOADS = A_DMA + B_DMA;
+    constexpr int HALF = (KIND == kGateUp) ? BN / 2 : BN;  // output columns per block
+    __shared__ uint4 sA0[BM * 4], sA1[BM * 4], sA2[BM * 4], sA3[BM * 4];
+    __shared__ uint4 sB0[BN * 4], sB1[BN * 4], sB2[BN * 4], sB3[BN * 4];
+
+    const int ncols = (KIND == kGateUp) ? g.F / HALF : (g.N + BN - 1) / BN;
+    const int items = *g.tile_count * ncols;
+    const int run = (items + 7) >> 3;
+    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+    const int item = xcd * run + j;
+    if (j >= run || item >= items) return;
+    const Tile tile = g.tiles[item / ncols];
+    const int e = tile.expert, r0 = tile.row0, r1 = tile.row1;
+    const int nsub = (r1 - r0 + 15) / 16;
+    const int nt = item % ncols;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wr = wave >> 1, wc = wave & 1;
+    const int K = g.K;
+    const int Nw = (KIND == kGateUp) ? 2 * g.F : g.N;
+
+    const char* pa[A_DMA];
+    const char* pb[B_DMA];
+#pragma unroll
+    for (int i = 0; i < A_DMA; ++i) {
+        const int row = (i * 4 + wave) * 16 + (lane >> 2);
+        const int ch = (lane & 3) ^ ((row >> 1) & 3);
+        const int rr = min(r0 + row, r1 - 1);
+        int src = g.a_rows ? g.a_rows[rr] : rr;
+        src = src < 0 ? 0 : (src >= g.a_rows_limit ? g.a_rows_limit - 1 : src);
+        pa[i] = static_cast<const char*>(g.a) + (size_t(src) * K + ch * 8) * 2;
+    }
+#pragma unroll
+    for (int i = 0; i < B_DMA; ++i) {
+        const int row = (i * 4 + wave) * 16 + (lane >> 2);
+        const int ch = (lane & 3) ^ ((row >> 1) & 3);
+        int wrow;
+        if (KIND == kGateUp) {  // per wavefront column: 64 gate rows, then the 64 matching up rows
+            const int q = row & 127;
+            const int f = nt * HALF + (row >> 7) * 64 + (q & 63);
+            wrow = q < 64 ? f : g.F + f;
+        } else {
+            wrow = min(nt * BN + row, g.N - 1);
+        }
+        pb[i] = static_cast<const char*>(g.w) + ((size_t(e) * Nw + wrow) * K + ch * 8) * 2;
+    }
+
+#define MOE_ISSUE2(SA, SB, K0)                                                                  \
+    do {                                                                                        \
+        const int k0_ = (K0);                                                                   \
+        _Pragma("unroll") for (int i = 0; i < A_DMA; ++i)                                       \
+            dma16(pa[i] + k0_ * 2, &SA[(i * 4 + wave) * 64]);                                   \
+        _Pragma("unroll") for (int i = 0; i < B_DMA; ++i)                                       \
+            dma16(pb[i] + k0_ * 2, &SB[(i * 4 + wave) * 64]);                                   \
+    } while (0)
+#define MOE_READ2(SA, SB, AF, BF)                                                               \
+    do {                                                                                        \
+        const int ch_ = lane >> 4;                                                              \
+        _Pragma("unroll") for (int ni = 0; ni < 8; ++ni) BF[ni] =                               \
+            __builtin_bit_cast(bf16x8_t, SB[lds_slot32(wc * 128 + ni * 16 + (lane & 15), ch_)]); \
+        _Pragma("unroll") for (int mi = 0; mi < 8; ++mi) AF[mi] =                               \
+            __builtin_bit_cast(bf16x8_t, SA[lds_slot32((mi * 2 + wr) * 16 + (lane & 15), ch_)]); \
+    } while (0)
+#define MOE_MFMA2(AF, BF)                                                                       \
+    do {                                                                                        \
+        _Pragma("unroll") for (int mi = 0; mi < 8; ++mi) {                                      \
+            if (mi * 2 + wr < nsub) {                                                           \
+                _Pragma("unroll") for (int ni = 0; ni < 8; ++ni) acc[mi][ni] =                  \
+                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(AF[mi], BF[ni], acc[mi][ni], 0, 0, 0); \
+            }                                                                                   \
+        }                                                                                       \
+    } while (0)
+
+    f32x4_t acc[8][8];
+#pragma unroll
+    for (int mi = 0; mi < 8; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 8; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    bf16x8_t a0[8], b0[8], a1[8], b1[8];
+
+    // Stage s lives in slot s % 4.  Iteration s: wait for stage s+1, barrier, read its
+    // fragments, refill the slot of stage s (already in registers) with stage s+4, and run
+    // the MFMAs of stage s.  Loads per iteration are unconditional (clamped to the last stage)
+    // so that the load counter always holds exactly two stages after stage s+1.
+    const int nk = K / BKS;
+    const int last = (nk - 1) * BKS;
+    MOE_ISSUE2(sA0, sB0, 0);
+    MOE_ISSUE2(sA1, sB1, min(1 * BKS, last));
+    MOE_ISSUE2(sA2, sB2, min(2 * BKS, last));
+    wait_vm_lgkm0<2 * LOADS>();
+    block_barrier();
+    MOE_READ2(sA0, sB0, a0, b0);
+    MOE_ISSUE2(sA3, sB3, min(3 * BKS, last));
+    for (int s = 0;; s += 4) {
+        wait_vm_lgkm0<2 * LOADS>();  // stage s+1 landed; stage s fragments in a0/b0
+        block_barrier();
+        MOE_READ2(sA1, sB1, a1, b1);
+        MOE_ISSUE2(sA0, sB0, min((s + 4) * BKS, last));
+        MOE_MFMA2(a0, b0);
+        if (s + 1 >= nk) break;
+        wait_vm_lgkm0<2 * LOADS>();
+        block_barrier();
+        MOE_READ2(sA2, sB2, a0, b0);
+        MOE_ISSUE2(sA1, sB1, min((s + 5) * BKS, last));
+        MOE_MFMA2(a1, b1);
+        if (s + 2 >= nk) break;
+        wait_vm_lgkm0<2 * LOADS>();
+        block_barrier();
+        MOE_READ2(sA3, sB3, a1, b1);
+        MOE_ISSUE2(sA2, sB2, min((s + 6) * BKS, last));
+        MOE_MFMA2(a0, b0);
+        if (s + 3 >= nk) break;
+        wait_vm_lgkm0<2 * LOADS>();
+        block_barrier();
+        MOE_READ2(sA0, sB0, a0, b0);
+        MOE_ISSUE2(sA3, sB3, min((s + 7) * BKS, last));
+        MOE_MFMA2(a1, b1);
+        if (s + 4 >= nk) break;
+    }
+    wait_vm_lgkm0<0>();
+#undef MOE_ISSUE2
+#undef MOE_READ2
+#undef MOE_MFMA2
+
+    uint16_t* out = static_cast<uint16_t*>(g.out);
+#pragma unroll
+    for (int mi = 0; mi < 8; ++mi) {
+        if (mi * 2 + wr >= nsub) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = r0 + (mi * 2 + wr) * 16 + 4 * (lane >> 4) + i;
+            if (row >= r1) continue;
+            if (KIND == kGateUp) {
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni) {
+                    const int col = nt * HALF + wc * 64 + ni * 16 + (lane & 15);
+                    out[size_t(row) * g.F + col] = (uint16_t)bf16_rne(silu_mul(acc[mi][ni][i], acc[mi][ni + 4][i]));
+                }
+            } else {
+#pragma unroll
+                for (int ni = 0; ni < 8; ++ni) {
+                    const int col = nt * BN + wc * 128 + ni * 16 + (lane & 15);
+                    if (col < g.N) out[size_t(row) * g.N + col] = (uint16_t)bf16_rne(acc[mi][ni][i]);
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Prefill kernel v4 (bf16 and NVFP4 weights): 256 x 256 block tile, 4 wavefronts (2 x 2) of
+// 128 x 128 (256 fp32 accumulators per lane in AGPRs), K in 32-wide stages.
+//
+// Operands are staged through registers: plain 16-byte global loads run three stages ahead of
+// the MFMAs, and each stage is written to one of two LDS slots after the MFMAs of the previous
+// stage.  (On gfx950 an LDS read waits for the same wavefront's outstanding global->LDS DMA
+// loads, so a wavefront that both DMAs and reads LDS cannot keep DMA in flight across its
+// reads; ordinary loads into registers do not hold LDS reads back.)  NVFP4 weights are staged
+// packed (16 bytes + 2 scale bytes per row and stage) and decoded to exact bf16 on their way
+// into LDS.  Rows are 64 bytes in LDS, chunk c of row r at slot c ^ ((r >> 1) & 3).
+// ---------------------------------------------------------------------------------------
+
+template <int KIND, int WFMT>
+__global__ __launch_bounds__(256, 1) void gemm_prefill_v4_kernel(GemmArgs g) {
+    constexpr int BM = 256, BN = 256, BKS = 32;
+    constexpr int HALF = (KIND == kGateUp) ? BN / 2 : BN;
+    __shared__ uint4 sA[2][BM * 4];
+    __shared__ uint4 sB[2][BN * 4];
+
+    const int ncols = (KIND == kGateUp) ? g.F / HALF : (g.N + BN - 1) / BN;
+    const int items = *g.tile_count * ncols;
+    const int run = (items + 7) >> 3;
+    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+    const int item = xcd * run + j;
+    if (j >= run || item >= items) return;
+    const Tile tile = g.tiles[item / ncols];
+    const int e = tile.expert, r0 = tile.row0, r1 = tile.row1;
+    const int nsub = (r1 - r0 + 15) / 16;
+    const int nt = item % ncols;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wr = wave >> 1, wc = wave & 1;
+    const int K = g.K;
+    const int Nw = (KIND == kGateUp) ? 2 * g.F : g.N;
+
+    auto wrow_of = [&](int row) -> int {
+        if (KIND == kGateUp) {  // per wavefront column: 64 gate rows, then the matching up rows
+            const int q = row & 127;
+            const int f = nt * HALF + (row >> 7) * 64 + (q & 63);
+            return q < 64 ? f : g.F + f;
+        }
+        return min(nt * BN + row, g.N - 1);
+    };
+
+    // A: thread loads rows (tid >> 2) + 64 i, chunk tid & 3 (i = 0..3)
+    auto a_ptr = [&](int i) -> const uint16_t* {
+        const int row = (tid >> 2) + 64 * i;
+        const int rr = min(r0 + row, r1 - 1);
+        int src = g.a_rows ? g.a_rows[rr] : rr;
+        src = src < 0 ? 0 : (src >= g.a_rows_limit ? g.a_rows_limit - 1 : src);
+        return static_cast<const uint16_t*>(g.a) + size_t(src) * K + (tid & 3) * 8;
+    };
+    const uint16_t* const pa0 = a_ptr(0);
+    const uint16_t* const pa1 = a_ptr(1);
+    const uint16_t* const pa2 = a_ptr(2);
+    const uint16_t* const pa3 = a_ptr(3);
+    // B bf16: the same map as A; B NVFP4: thread tid owns weight row tid (16 packed bytes and
+    // 2 scale bytes per stage)
+    auto b_ptr = [&](int i) -> const uint16_t* {
+        return static_cast<const uint16_t*>(g.w) + (size_t(e) * Nw + wrow_of((tid >> 2) + 64 * i)) * K + (tid & 3) * 8;
+    };
+    const uint16_t* pb0 = nullptr;
+    const uint16_t* pb1 = nullptr;
+    const uint16_t* pb2 = nullptr;
+    const uint16_t* pb3 = nullptr;
+    const uint8_t* pq = nullptr;
+    const uint8_t* ps = nullptr;
+    if constexpr (WFMT == kWBF16) {
+        pb0 = b_ptr(0);
+        pb1 = b_ptr(1);
+        pb2 = b_ptr(2);
+        pb3 = b_ptr(3);
+    } else {
+        const size_t wr_ = size_t(e) * Nw + wrow_of(tid);
+        pq = static_cast<const uint8_t*>(g.w) + wr_ * (K / 2);
+        ps = g.wscale + wr_ * (K / 16);
+    }
+
+    // three register stages with named fields (no arrays) so that they stay in VGPRs
+    struct Stage {
+        uint4 a0, a1, a2, a3, b0, b1, b2, b3;
+        uint32_t sc;
+    };
+    Stage st0{}, st1{}, st2{};
+    auto ld16 = [](const void* p) __attribute__((always_inline)) { return *reinterpret_cast<const uint4*>(p); };
+    auto gload = [&](Stage& r, int k0) __attribute__((always_inline)) {
+        r.a0 = ld16(pa0 + k0);
+        r.a1 = ld16(pa1 + k0);
+        r.a2 = ld16(pa2 + k0);
+        r.a3 = ld16(pa3 + k0);
+        if constexpr (WFMT == kWBF16) {
+            r.b0 = ld16(pb0 + k0);
+            r.b1 = ld16(pb1 + k0);
+            r.b2 = ld16(pb2 + k0);
+            r.b3 = ld16(pb3 + k0);
+        } else {
+            r.b0 = ld16(pq + k0 / 2);
+            r.sc = *reinterpret_cast<const uint16_t*>(ps + k0 / 16);
+        }
+    };
+    const int arow = tid >> 2, ach = tid & 3;
+    auto swrite = [&](const Stage& r, int slot) __attribute__((always_inline)) {
+        sA[slot][lds_slot32(arow, ach)] = r.a0;
+        sA[slot][lds_slot32(arow + 64, ach)] = r.a1;
+        sA[slot][lds_slot32(arow + 128, ach)] = r.a2;
+        sA[slot][lds_slot32(arow + 192, ach)] = r.a3;
+        if constexpr (WFMT == kWBF16) {
+            sB[slot][lds_slot32(arow, ach)] = r.b0;
+            sB[slot][lds_slot32(arow + 64, ach)] = r.b1;
+            sB[slot][lds_slot32(arow + 128, ach)] = r.b2;
+            sB[slot][lds_slot32(arow + 192, ach)] = r.b3;
+        } else {
+            const float s0 = e4m3_times_2p14(r.sc & 0xffu);
+            const float s1 = e4m3_times_2p14((r.sc >> 8) & 0xffu);
+            sB[slot][lds_slot32(tid, 0)] = dequant8(r.b0.x, s0);
+            sB[slot][lds_slot32(tid, 1)] = dequant8(r.b0.y, s0);
+            sB[slot][lds_slot32(tid, 2)] = dequant8(r.b0.z, s1);
+            sB[slot][lds_slot32(tid, 3)] = dequant8(r.b0.w, s1);
+        }
+    };
+
+    f32x4_t acc[8][8];
+#pragma unroll
+    for (int mi = 0; mi < 8; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 8; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    auto step = [&](int slot) __attribute__((always_inline)) {
+        const int ch = lane >> 4;
+        bf16x8_t bf[8];
+#pragma unroll
+        for (int ni = 0; ni < 8; ++ni)
+            bf[ni] = __builtin_bit_cast(bf16x8_t, sB[slot][lds_slot32(wc * 128 + ni * 16 + (lane & 15), ch)]);
+#pragma unroll
+        for (int mi = 0; mi < 8; ++mi) {
+            if (mi * 2 + wr < nsub) {
+                const bf16x8_t af =
+                    __builtin_bit_cast(bf16x8_t, sA[slot][lds_slot32((mi * 2 + wr) * 16 + (lane & 15), ch)]);
+#pragma unroll
+                for (int ni = 0; ni < 8; ++ni)
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[ni], acc[mi][ni], 0, 0, 0);
+            }
+        }
+    };
+
+    // iteration s: barrier; MFMAs of stage s from slot s%2 (its fragments read first); loads of
+    // stage s+3 into register set s%3; then stage s+1 (register set (s+1)%3) into slot (s+1)%2.
+    const int nk = K / BKS;
+    const int last = (nk - 1) * BKS;
+    gload(st0, 0);
+    gload(st1, min(BKS, last));
+    gload(st2, min(2 * BKS, last));
+    swrite(st0, 0);
+    for (int s = 0;; s += 6) {
+#define MOE_V4_ITER(S, RS, RN, SLOT)                                             \
+        __builtin_amdgcn_s_waitcnt(vm_wait_lgkm0(63));                          \
+        block_barrier();                                                        \
+        step(SLOT);                                                             \
+        gload(st##RS, min((s + S + 3) * BKS, last));                            \
+        if (s + S + 1 >= nk) break;                                             \
+        swrite(st##RN, (SLOT) ^ 1);
+        MOE_V4_ITER(0, 0, 1, 0)
+        MOE_V4_ITER(1, 1, 2, 1)
+        MOE_V4_ITER(2, 2, 0, 0)
+        MOE_V4_ITER(3, 0, 1, 1)
+        MOE_V4_ITER(4, 1, 2, 0)
+        MOE_V4_ITER(5, 2, 0, 1)
+#undef MOE_V4_ITER
+    }
+    __builtin_amdgcn_s_waitcnt(vm_wait_lgkm0(0));  // drain the clamped tail loads
+
+    const float gs = (WFMT == kWNVFP4 && g.gscale) ? g.gscale[e] : 1.0f;
+    uint16_t* out = static_cast<uint16_t*>(g.out);
+#pragma unroll
+    for (int mi = 0; mi < 8; ++mi) {
+        if (mi * 2 + wr >= nsub) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = r0 + (mi * 2 + wr) * 16 + 4 * (lane >> 4) + i;
+            if (row >= r1) continue;
+            if (KIND == kGateUp) {
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni) {
+                    const int col = nt * HALF + wc * 64 + ni * 16 + (lane & 15);
+                    out[size_t(row) * g.F + col] =
+                        (uint16_t)bf16_rne(silu_mul(acc[mi][ni][i] * gs, acc[mi][ni + 4][i] * gs));
+                }
+            } else {
+#pragma unroll
+                for (int ni = 0; ni < 8; ++ni) {
+                    const int col = nt * BN + wc * 128 + ni * 16 + (lane & 15);
+                    if (col < g.N) out[size_t(row) * g.N + col] = (uint16_t)bf16_rne(acc[mi][ni][i] * gs);
+                }
+            }
+        }
+    }
+}
+
 // fp32 activations and weights: a plain 64 x 64 SIMT tile, 4 x 4 outputs per thread.  For the
 // gate/up kind, B columns 0..31 are gate rows and 32..63 the matching up rows (32 hid columns).
 template <int KIND>
@@ -308,12 +861,14 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
 namespace {
 // prefill: 128 x 128 tiles, 2 x 2 wavefronts of 64 x 64; decode: 16 x 64 tiles, 1 x 2
 // wavefronts of 16 x 32 (weight streaming, many blocks for few rows).
-constexpr int PF_BM = 128, PF_BN = 128, PF_WM = 2, PF_WN = 2;
+constexpr int PF_BM = 128, PF_BN = 128, PF_WM = 2, PF_WN = 2;   // NVFP4 prefill
 constexpr int DC_BM = 16, DC_BN = 64, DC_WM = 1, DC_WN = 2;
 }  // namespace
 
-int gemm_tile_rows(int family) {
-    return family == kFamSimtF32 ? 64 : family == kFamPrefill ? PF_BM : DC_BM;
+int gemm_tile_rows(int family, int wfmt, int ffn) {
+    if (family == kFamSimtF32) return 64;
+    if (family == kFamPrefill) return (wfmt == kWBF16 || ffn % 128 == 0) ? 256 : PF_BM;
+    return DC_BM;
 }
 
 template <int BM, int BN, int WM, int WN>
@@ -333,15 +888,41 @@ static void launch_mfma(const GemmArgs& g, int max_tiles, hipStream_t s) {
     }
 }
 
+// Work items of the prefill kernels: (row tile, column tile) pairs, a multiple of 8 blocks so
+// that every XCD walks the same number of slots.
+static dim3 prefill_grid(const GemmArgs& g, int max_tiles, int bn) {
+    const int ncols = g.kind == kGateUp ? g.F / (bn / 2) : (g.N + bn - 1) / bn;
+    return dim3(((max_tiles * ncols + 7) / 8) * 8);
+}
+
 hipError_t launch_gemm(const GemmArgs& g, int family, int max_tiles, hipStream_t s) {
     if (max_tiles <= 0) return hipSuccess;
+    const bool up = g.kind == kGateUp;
     if (family == kFamSimtF32) {
-        const int ncols = g.kind == kGateUp ? g.F / 32 : (g.N + 63) / 64;
+        const int ncols = up ? g.F / 32 : (g.N + 63) / 64;
         dim3 grid(max_tiles, ncols), block(256);
-        if (g.kind == kGateUp)
+        if (up)
             hipLaunchKernelGGL((gemm_f32_kernel<kGateUp>), grid, block, 0, s, g);
         else
             hipLaunchKernelGGL((gemm_f32_kernel<kDown>), grid, block, 0, s, g);
+    } else if (family == kFamPrefill && g.wfmt == kWBF16 && g.F % 128 == 0) {
+        const dim3 grid = prefill_grid(g, max_tiles, 256);
+        if (up)
+            hipLaunchKernelGGL((gemm_prefill_bf16_v2_kernel<kGateUp>), grid, dim3(256), 0, s, g);
+        else
+            hipLaunchKernelGGL((gemm_prefill_bf16_v2_kernel<kDown>), grid, dim3(256), 0, s, g);
+    } else if (family == kFamPrefill && g.wfmt == kWBF16) {
+        const dim3 grid = prefill_grid(g, max_tiles, 128);
+        if (up)
+            hipLaunchKernelGGL((gemm_prefill_bf16_kernel<kGateUp>), grid, dim3(256), 0, s, g);
+        else
+            hipLaunchKernelGGL((gemm_prefill_bf16_kernel<kDown>), grid, dim3(256), 0, s, g);
+    } else if (family == kFamPrefill && g.F % 128 == 0) {
+        const dim3 grid = prefill_grid(g, max_tiles, 256);
+        if (up)
+            hipLaunchKernelGGL((gemm_prefill_v4_kernel<kGateUp, kWNVFP4>), grid, dim3(256), 0, s, g);
+        else
+            hipLaunchKernelGGL((gemm_prefill_v4_kernel<kDown, kWNVFP4>), grid, dim3(256), 0, s, g);
     } else if (family == kFamPrefill) {
         launch_mfma<PF_BM, PF_BN, PF_WM, PF_WN>(g, max_tiles, s);
     } else {

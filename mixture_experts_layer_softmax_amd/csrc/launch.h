@@ -54,7 +54,7 @@ struct GemmArgs {
     int wfmt;               // WeightFmt
 };
 
-int gemm_tile_rows(int family);
+int gemm_tile_rows(int family, int wfmt, int ffn);
 hipError_t launch_router_logits(const RouteArgs& a, hipStream_t s);
 hipError_t launch_topk(const float* logits, int T, int E, int k, int renorm, int32_t* ids,
                        float* w, hipStream_t s);
