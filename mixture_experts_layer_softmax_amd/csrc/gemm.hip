@@ -32,33 +32,33 @@ constexpr int BK = 64;  // K elements per LDS stage (8 chunks of 16 bytes in bf1
 
 __device__ __forceinline__ int lds_slot(int row, int ch) { return row * 8 + (ch ^ (row & 7)); }
 
-// E4M3 (FN) byte -> its value times 2^14, in fp32 (integer decode; subnormals included).
-__device__ __forceinline__ float e4m3_times_2p14(uint32_t c) {
+// E4M3 (FN) byte -> its value in fp32 (integer decode; subnormals included).
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
     const uint32_t e = (c >> 3) & 15, m = c & 7;
     float v;
     if (e == 0)
         v = float(m) * 0x1p-9f;
     else
         v = __uint_as_float(((e + 120u) << 23) | (m << 20));
-    v = (c & 0x80) ? -v : v;
-    return v * 0x1p14f;
+    return (c & 0x80) ? -v : v;
 }
 
-// One E2M1 nibble -> fp32 value times 2^-14: the nibble's exponent/mantissa bits placed in an
-// IEEE half (sign to bit 15) read 2^-14 * e2m1 exactly, including the subnormal code 0.5.
-__device__ __forceinline__ float e2m1_times_2m14(uint32_t n) {
-    const unsigned short h = (unsigned short)(((n & 7u) << 9) | ((n & 8u) << 12));
-    return float(__builtin_bit_cast(_Float16, h));
-}
-
-// 8 nibbles (elements 0..7, even element in the low nibble) with their block scale -> 8 bf16.
-__device__ __forceinline__ uint4 dequant8(uint32_t word, float s14) {
+// 8 nibbles (elements 0..7, even element in the low nibble) times their block scale -> 8 bf16.
+// v_cvt_scalef32_pk_f32_fp4 with scale 1.0 gives the two E2M1 values of one byte exactly in
+// fp32 (the instruction applies only the exponent of its scale, so the E4M3 scale, which has
+// a mantissa, is multiplied separately).  e2m1 * e4m3 has at most 6 significant bits, so the
+// product is exact in fp32 and its upper half is the exact bf16; v_perm_b32 packs two of them.
+__device__ __forceinline__ uint4 dequant8(uint32_t word, float s) {
+    typedef __attribute__((ext_vector_type(2))) float f32x2_t;
     uint32_t o[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-        const float f0 = e2m1_times_2m14((word >> (8 * p)) & 15u) * s14;
-        const float f1 = e2m1_times_2m14((word >> (8 * p + 4)) & 15u) * s14;
-        o[p] = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xffff0000u);  // exact
+        f32x2_t v;
+        if (p == 0) v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 0);
+        else if (p == 1) v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 1);
+        else if (p == 2) v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 2);
+        else v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 3);
+        o[p] = __builtin_amdgcn_perm(__float_as_uint(v.y * s), __float_as_uint(v.x * s), 0x07060302u);
     }
     return make_uint4(o[0], o[1], o[2], o[3]);
 }
@@ -169,8 +169,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
             for (int it = 0; it < Q_IT; ++it) {
                 const int idx = tid + it * NT, row = idx >> 1, hf = idx & 1;
-                const float s0 = e4m3_times_2p14(rs[it] & 0xffu);
-                const float s1 = e4m3_times_2p14(rs[it] >> 8);
+                const float s0 = e4m3_value(rs[it] & 0xffu);
+                const float s1 = e4m3_value(rs[it] >> 8);
                 sB[buf][lds_slot(row, hf * 4 + 0)] = dequant8(rb[it].x, s0);
                 sB[buf][lds_slot(row, hf * 4 + 1)] = dequant8(rb[it].y, s0);
                 sB[buf][lds_slot(row, hf * 4 + 2)] = dequant8(rb[it].z, s1);
@@ -701,8 +701,8 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_v4_kernel(GemmArgs g) {
             sB[slot][lds_slot32(arow + 128, ach)] = r.b2;
             sB[slot][lds_slot32(arow + 192, ach)] = r.b3;
         } else {
-            const float s0 = e4m3_times_2p14(r.sc & 0xffu);
-            const float s1 = e4m3_times_2p14((r.sc >> 8) & 0xffu);
+            const float s0 = e4m3_value(r.sc & 0xffu);
+            const float s1 = e4m3_value((r.sc >> 8) & 0xffu);
             sB[slot][lds_slot32(tid, 0)] = dequant8(r.b0.x, s0);
             sB[slot][lds_slot32(tid, 1)] = dequant8(r.b0.y, s0);
             sB[slot][lds_slot32(tid, 2)] = dequant8(r.b0.z, s1);
@@ -783,6 +783,178 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_v4_kernel(GemmArgs g) {
                     if (col < g.N) out[size_t(row) * g.N + col] = (uint16_t)bf16_rne(acc[mi][ni][i] * gs);
                 }
             }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Decode kernel: few rows per expert, so the layer streams the selected experts' weights once
+// from HBM ("Hosting Qwen on Blackwell", section Decoders: decode matmuls are bound by weight
+// loads).  One wavefront owns 16 weight rows (gate/up: 16 gate rows and the 16 matching up
+// rows) and up to 16 dispatched rows of one expert; weights go from global memory straight
+// into MFMA operand registers (no LDS), several 128-wide K blocks in flight per lane.
+//
+// Within each 128-wide K block the reduction index is permuted so that one lane's operand
+// elements are contiguous: MFMA i (0..3) of the block takes, in k-group q = lane / 16,
+// elements 128 j + 32 q + 8 i .. +7 for both operands (any common permutation of K leaves the
+// dot products unchanged).  A lane then fetches 64 contiguous bytes of bf16 weights, or 16
+// bytes of packed NVFP4 nibbles plus their two scales, per block.
+//
+// SPLITK wavefronts of a block share 16 columns and split K; their partial sums meet in LDS
+// and are added in a fixed order (deterministic).
+// ---------------------------------------------------------------------------------------
+
+template <int KIND, int WFMT, int SPLITK>
+__global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
+    constexpr int CG = 4 / SPLITK;              // column groups per block
+    constexpr int NB = (KIND == kGateUp) ? 2 : 1;  // weight row sets per column group
+    __shared__ f32x4_t red[4][NB][64];
+
+    const int ncg = (KIND == kGateUp) ? g.F / 16 : (g.N + 15) / 16;
+    const int per_tile = (ncg + CG - 1) / CG;
+    const int item = blockIdx.x;
+    if (item >= *g.tile_count * per_tile) return;
+    const Tile tile = g.tiles[item / per_tile];
+    const int e = tile.expert, r0 = tile.row0, r1 = tile.row1;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int cg = (item % per_tile) * CG + wave / SPLITK;
+    const int kp = wave % SPLITK;
+    const bool live = cg < ncg;                 // uniform per wavefront
+    const int K = g.K;
+    const int Nw = (KIND == kGateUp) ? 2 * g.F : g.N;
+    const int n = lane & 15, q = lane >> 4;
+
+    // this lane's activation row and weight rows
+    const int rr = min(r0 + n, r1 - 1);
+    int src = g.a_rows ? g.a_rows[rr] : rr;
+    src = src < 0 ? 0 : (src >= g.a_rows_limit ? g.a_rows_limit - 1 : src);
+    const uint16_t* pa = static_cast<const uint16_t*>(g.a) + size_t(src) * K + 32 * q;
+    const int col = min(cg, ncg - 1) * 16 + n;
+    int wrow0, wrow1 = 0;
+    if (KIND == kGateUp) {
+        wrow0 = col;
+        wrow1 = g.F + col;
+    } else {
+        wrow0 = min(col, g.N - 1);
+    }
+    const size_t w0 = size_t(e) * Nw + wrow0, w1 = size_t(e) * Nw + wrow1;
+
+    f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    const int nblk = K / 128 / SPLITK;
+    const int j0 = kp * nblk, jend = j0 + nblk;
+
+    // One 128-wide K block of operands, in named registers.  Two blocks are kept in flight:
+    // the loads of block j+1 are outstanding while the MFMAs of block j run.
+    struct Blk {
+        uint4 a0, a1, a2, a3;      // activations, MFMA i = 0..3
+        uint4 g0, g1, g2, g3;      // bf16 weight rows (gate / down)
+        uint4 u0, u1, u2, u3;      // bf16 up rows
+        uint4 pg, pu;              // NVFP4 packed nibbles (gate / down, up)
+        uint32_t sg, su;           // NVFP4 scale pairs
+    };
+    auto ld16 = [](const void* p) __attribute__((always_inline)) { return *reinterpret_cast<const uint4*>(p); };
+    const uint16_t* pw0 = static_cast<const uint16_t*>(g.w) + w0 * K + 32 * q;
+    const uint16_t* pw1 = static_cast<const uint16_t*>(g.w) + w1 * K + 32 * q;
+    const uint8_t* pq0 = static_cast<const uint8_t*>(g.w) + w0 * (K / 2) + 16 * q;
+    const uint8_t* pq1 = static_cast<const uint8_t*>(g.w) + w1 * (K / 2) + 16 * q;
+    const uint8_t* ps0 = g.wscale + w0 * (K / 16) + 2 * q;
+    const uint8_t* ps1 = g.wscale + w1 * (K / 16) + 2 * q;
+    auto load = [&](Blk& b, int j) __attribute__((always_inline)) {
+        const int k = 128 * j;
+        b.a0 = ld16(pa + k);
+        b.a1 = ld16(pa + k + 8);
+        b.a2 = ld16(pa + k + 16);
+        b.a3 = ld16(pa + k + 24);
+        if constexpr (WFMT == kWBF16) {
+            b.g0 = ld16(pw0 + k);
+            b.g1 = ld16(pw0 + k + 8);
+            b.g2 = ld16(pw0 + k + 16);
+            b.g3 = ld16(pw0 + k + 24);
+            if constexpr (KIND == kGateUp) {
+                b.u0 = ld16(pw1 + k);
+                b.u1 = ld16(pw1 + k + 8);
+                b.u2 = ld16(pw1 + k + 16);
+                b.u3 = ld16(pw1 + k + 24);
+            }
+        } else {
+            b.pg = ld16(pq0 + 64 * j);
+            b.sg = *reinterpret_cast<const uint16_t*>(ps0 + 8 * j);
+            if constexpr (KIND == kGateUp) {
+                b.pu = ld16(pq1 + 64 * j);
+                b.su = *reinterpret_cast<const uint16_t*>(ps1 + 8 * j);
+            }
+        }
+    };
+    auto mma = [&](f32x4_t& acc, const uint4& x, const uint4& w) __attribute__((always_inline)) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, x), __builtin_bit_cast(bf16x8_t, w), acc, 0, 0, 0);
+    };
+    auto compute = [&](const Blk& b) __attribute__((always_inline)) {
+        if constexpr (WFMT == kWBF16) {
+            mma(acc0, b.a0, b.g0);
+            mma(acc0, b.a1, b.g1);
+            mma(acc0, b.a2, b.g2);
+            mma(acc0, b.a3, b.g3);
+            if constexpr (KIND == kGateUp) {
+                mma(acc1, b.a0, b.u0);
+                mma(acc1, b.a1, b.u1);
+                mma(acc1, b.a2, b.u2);
+                mma(acc1, b.a3, b.u3);
+            }
+        } else {
+            const float fa = e4m3_value(b.sg & 0xffu), fb = e4m3_value(b.sg >> 8);
+            mma(acc0, b.a0, dequant8(b.pg.x, fa));
+            mma(acc0, b.a1, dequant8(b.pg.y, fa));
+            mma(acc0, b.a2, dequant8(b.pg.z, fb));
+            mma(acc0, b.a3, dequant8(b.pg.w, fb));
+            if constexpr (KIND == kGateUp) {
+                const float ua = e4m3_value(b.su & 0xffu), ub = e4m3_value(b.su >> 8);
+                mma(acc1, b.a0, dequant8(b.pu.x, ua));
+                mma(acc1, b.a1, dequant8(b.pu.y, ua));
+                mma(acc1, b.a2, dequant8(b.pu.z, ub));
+                mma(acc1, b.a3, dequant8(b.pu.w, ub));
+            }
+        }
+    };
+    if (live && nblk > 0) {
+        Blk x0{}, x1{};
+        load(x0, j0);
+        load(x1, min(j0 + 1, jend - 1));  // past the end: a harmless re-read of the last block
+        for (int j = j0;; j += 2) {
+            compute(x0);
+            if (j + 1 >= jend) break;
+            load(x0, min(j + 2, jend - 1));
+            compute(x1);
+            if (j + 2 >= jend) break;
+            load(x1, min(j + 3, jend - 1));
+        }
+    }
+
+    if constexpr (SPLITK > 1) {
+        red[wave][0][lane] = acc0;
+        if (KIND == kGateUp) red[wave][NB - 1][lane] = acc1;
+        __syncthreads();
+        if (kp != 0) return;
+        acc0 = red[wave][0][lane];
+        if (KIND == kGateUp) acc1 = red[wave][NB - 1][lane];
+#pragma unroll
+        for (int p = 1; p < SPLITK; ++p) {
+            acc0 += red[wave + p][0][lane];
+            if (KIND == kGateUp) acc1 += red[wave + p][NB - 1][lane];
+        }
+    }
+    if (!live) return;
+
+    const float gs = (WFMT == kWNVFP4 && g.gscale) ? g.gscale[e] : 1.0f;
+    uint16_t* out = static_cast<uint16_t*>(g.out);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = r0 + 4 * q + i;
+        if (row >= r1) continue;
+        if (KIND == kGateUp) {
+            out[size_t(row) * g.F + col] = (uint16_t)bf16_rne(silu_mul(acc0[i] * gs, acc1[i] * gs));
+        } else if (col < g.N) {
+            out[size_t(row) * g.N + col] = (uint16_t)bf16_rne(acc0[i] * gs);
         }
     }
 }
@@ -925,6 +1097,22 @@ hipError_t launch_gemm(const GemmArgs& g, int family, int max_tiles, hipStream_t
             hipLaunchKernelGGL((gemm_prefill_v4_kernel<kDown, kWNVFP4>), grid, dim3(256), 0, s, g);
     } else if (family == kFamPrefill) {
         launch_mfma<PF_BM, PF_BN, PF_WM, PF_WN>(g, max_tiles, s);
+    } else if (g.K % 128 == 0) {
+        // split K until there are about 4 wavefronts per SIMD (4096) for the worst-case tile count
+        const int ncg = up ? g.F / 16 : (g.N + 15) / 16;
+        int split = 1;
+        while (split < 4 && long(max_tiles) * ncg * split < 4096 && g.K % (128 * split * 2) == 0) split *= 2;
+        const int cgb = 4 / split;
+        dim3 grid(max_tiles * ((ncg + cgb - 1) / cgb)), block(256);
+#define MOE_DEC(KD, WF, SK) hipLaunchKernelGGL((gemm_decode_kernel<KD, WF, SK>), grid, block, 0, s, g)
+        if (g.wfmt == kWBF16) {
+            if (up) { if (split == 1) MOE_DEC(kGateUp, kWBF16, 1); else if (split == 2) MOE_DEC(kGateUp, kWBF16, 2); else MOE_DEC(kGateUp, kWBF16, 4); }
+            else    { if (split == 1) MOE_DEC(kDown, kWBF16, 1);   else if (split == 2) MOE_DEC(kDown, kWBF16, 2);   else MOE_DEC(kDown, kWBF16, 4); }
+        } else {
+            if (up) { if (split == 1) MOE_DEC(kGateUp, kWNVFP4, 1); else if (split == 2) MOE_DEC(kGateUp, kWNVFP4, 2); else MOE_DEC(kGateUp, kWNVFP4, 4); }
+            else    { if (split == 1) MOE_DEC(kDown, kWNVFP4, 1);   else if (split == 2) MOE_DEC(kDown, kWNVFP4, 2);   else MOE_DEC(kDown, kWNVFP4, 4); }
+        }
+#undef MOE_DEC
     } else {
         launch_mfma<DC_BM, DC_BN, DC_WM, DC_WN>(g, max_tiles, s);
     }
