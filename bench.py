@@ -5,16 +5,25 @@
 A step is one ``moe_forward`` call (router -> dispatch -> gate/up GEMM + SwiGLU -> down GEMM
 -> combine) over one batch of seeded synthetic inputs already resident in HBM.  The default
 workload is the prefill-shaped layer (4096 tokens, hidden 4096, 128 experts, top-8, expert FFN
-1536, bf16, router bias N(0,1)).  Prints one JSON line.
+1536, bf16, router bias N(0,1)); ``--workload`` selects another one (tiny, decode1, decode8,
+decode64, nvfp4_decode, nvfp4_prefill).  Prints one JSON line.
 
-Besides the step time it measures, with events on the launch stream, the average duration of
+Timing: W untimed steps, then K steps between two events on the launch stream.  Decode-shaped
+workloads (whose selected weights fit in the 256 MiB Infinity Cache) overwrite a 1 GiB buffer
+before every timed step and time each step with its own event pair, so that weights come from
+HBM; the flush is outside the timed intervals.
+
+Besides the step time it measures, with events on the same stream, the average duration of
 the dominant kernel (the gate/up grouped GEMM, launched alone through ``moe_grouped_gemm`` on
-the same routing) and reports it against the MI355X roofline, and it times the CPU oracle on a
-bounded sub-batch of the same workload as a reported baseline.
+the same routing) and reports it against the MI355X roofline.  ``traffic`` (HBM bytes per
+launch of that kernel) comes from the counter summary under profiles/ when it was taken on the
+current kernel source, else null.  The CPU oracle is timed on a bounded sub-batch of the same
+workload as a reported baseline.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -26,6 +35,8 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_FLOPS = 2.5e15   # MI355X dense bf16 MFMA
 PEAK_HBM_BYTES = 8.0e12    # MI355X HBM3E
 METRIC = "MoE layer tokens/s at 1 GPU; % MFMA peak (prefill) / % HBM BW (decode)"
+GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_softmax_amd", "csrc", "gemm.hip")
+TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def describe(wl) -> str:
@@ -38,7 +49,9 @@ def bytes_per_weight(wdt: str) -> float:
 
 
 def layer_work(wl, active: int):
-    """Algorithmic FLOPs and HBM bytes of one layer call (intermediates excluded)."""
+    """Algorithmic FLOPs and HBM bytes of one layer call: router + expert FFN FLOPs; the
+    active experts' weights once, the router weight, tokens in and out (intermediates
+    excluded: the method need not send them to HBM)."""
     act = 4 if wl.act == "f32" else 2
     flops = 2.0 * wl.tokens * wl.hidden * wl.experts + 6.0 * wl.hidden * wl.ffn * wl.assignments
     nbytes = (active * 3.0 * wl.hidden * wl.ffn * bytes_per_weight(wl.wdt)
@@ -47,8 +60,8 @@ def layer_work(wl, active: int):
 
 
 def gate_up_work(wl, active: int):
-    """Algorithmic FLOPs and bytes of one gate/up grouped-GEMM launch: weights of the active
-    experts once, each token row once, the hid output once."""
+    """Algorithmic FLOPs and bytes of one gate/up grouped-GEMM launch: the active experts'
+    gate/up weights once, each token row once, the hid output once."""
     act = 4 if wl.act == "f32" else 2
     flops = 4.0 * wl.hidden * wl.ffn * wl.assignments
     nbytes = (active * 2.0 * wl.ffn * wl.hidden * bytes_per_weight(wl.wdt)
@@ -56,16 +69,29 @@ def gate_up_work(wl, active: int):
     return flops, nbytes
 
 
+def source_hash() -> str:
+    return hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per gate/up launch from the committed counter summary, if it is current."""
+    try:
+        d = json.load(open(TRAFFIC))
+    except (OSError, ValueError):
+        return None
+    e = d.get(workload)
+    if not e or e.get("gemm_source_sha256_16") != source_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
 def cpu_baseline(wl, inputs, budget_s: float):
     """The oracle (as it stands) on a sub-batch of the same workload's tokens."""
-    import numpy as np
-
     from oracle import oracle as O
 
     O.build()
     sub = dict(inputs)
-    n = 8
-    spent = 0.0
+    n = min(8, wl.tokens)
     while True:
         sub["x"] = inputs["x"][:n]
         t0 = time.perf_counter()
@@ -85,8 +111,11 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="prefill")
+    ap.add_argument("--flush", choices=("auto", "on", "off"), default="auto")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="also run one 512 MiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this layer is built and measured on a single "
@@ -94,7 +123,6 @@ def main() -> int:
               file=sys.stderr)
         return 2
 
-    import numpy as np
     import torch
 
     from mixture_experts_layer_softmax_amd import lib, synth
@@ -113,37 +141,56 @@ def main() -> int:
     torch.cuda.synchronize()
     counts = dbg["counts"].cpu().numpy()
     active = int((counts > 0).sum())
+    w_bytes = active * 3.0 * wl.hidden * wl.ffn * bytes_per_weight(wl.wdt)
+    flush = args.flush == "on" or (args.flush == "auto" and w_bytes < 1.5 * 2 ** 30)
+    scratch = torch.empty(2 ** 30, dtype=torch.uint8, device="cuda:0") if flush else None
 
-    print("[bench] warmup %d, timed %d steps" % (args.warmup, args.steps), file=sys.stderr, flush=True)
+    def timed(fn, steps):
+        """Mean ms per call of fn over `steps` calls on the current stream."""
+        if not flush:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / steps
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for a, b in evs:
+            scratch.fill_(1)  # evict L2 and the Infinity Cache
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in evs) / steps
+
+    print("[bench] warmup %d, timed %d steps%s" % (args.warmup, args.steps, " (flushed)" if flush else ""),
+          file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         layer.forward(x, y=y)
     torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record()
-    for _ in range(args.steps):
-        layer.forward(x, y=y)
-    ev1.record()
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms_per_step = timed(lambda: layer.forward(x, y=y), args.steps)
     wall = time.perf_counter() - t0
-    ms_per_step = ev0.elapsed_time(ev1) / args.steps
 
     # the dominant kernel alone: gate/up grouped GEMM on the same routing, same stream
     p = layer.problem_for(wl.tokens)
     ws = layer.workspace(wl.tokens)
     hid = layer.empty_act(wl.assignments, wl.ffn)
+    gemm1 = lambda: lib.grouped_gemm(p, lib.GATE_UP_SWIGLU, x, dbg["sorted_token"], dbg["offsets"],
+                                     layer.weights, hid, ws)
     for _ in range(2):
-        lib.grouped_gemm(p, lib.GATE_UP_SWIGLU, x, dbg["sorted_token"], dbg["offsets"],
-                         layer.weights, hid, ws)
+        gemm1()
     torch.cuda.synchronize()
-    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    g0.record()
-    for _ in range(args.steps):
-        lib.grouped_gemm(p, lib.GATE_UP_SWIGLU, x, dbg["sorted_token"], dbg["offsets"],
-                         layer.weights, hid, ws)
-    g1.record()
-    torch.cuda.synchronize()
-    gemm1_ms = g0.elapsed_time(g1) / args.steps  # includes the tiny tile-list kernel
+    gemm1_ms = timed(gemm1, args.steps)  # includes the ~5 us tile-list kernel it launches first
+
+    if args.calibration_copy:
+        a = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device="cuda:0")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
 
     flops, nbytes = layer_work(wl, active)
     gflops, gbytes = gate_up_work(wl, active)
@@ -155,9 +202,11 @@ def main() -> int:
         roof = dict(bound="mfma", achieved=gflops / (gemm1_ms * 1e-3) / 1e12,
                     peak=PEAK_BF16_FLOPS / 1e12, unit="TFLOP/s")
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
-    roof["kernel"] = "gemm_bf16_kernel gate/up + SwiGLU (%s weights)" % wl.wdt
+    roof["traffic"] = measured_traffic(wl.name)
+    roof["kernel"] = "grouped gate/up GEMM + SwiGLU (%s weights)" % wl.wdt
     roof["kernel_ms"] = gemm1_ms
+    roof["algorithmic_bytes"] = gbytes
+    roof["algorithmic_flops"] = gflops
 
     tok_s = wl.tokens / (ms_per_step * 1e-3)
     out = dict(metric=METRIC, value=tok_s, unit="tokens/s", n_gpus=1, steps=args.steps,
@@ -165,7 +214,8 @@ def main() -> int:
                scaling="weak", vs_baseline=None, dtype=wl.act, data="synthetic (seeded)",
                config=dict(workload=describe(wl), tokens=wl.tokens, hidden=wl.hidden,
                            experts=wl.experts, top_k=wl.top_k, ffn=wl.ffn, weights=wl.wdt,
-                           active_experts=active, max_expert_rows=int(counts.max())),
+                           active_experts=active, max_expert_rows=int(counts.max()),
+                           cache_flushed=bool(flush)),
                layer_tflops=flops / (ms_per_step * 1e-3) / 1e12,
                layer_mfma_frac=flops / (ms_per_step * 1e-3) / PEAK_BF16_FLOPS,
                layer_hbm_frac=nbytes / (ms_per_step * 1e-3) / PEAK_HBM_BYTES,
