@@ -27,8 +27,10 @@
  *  - Errors are return codes; nothing is thrown and nothing aborts.  All arguments are
  *    validated on the host before any HIP call: MOE_ERR_INVALID_ARGUMENT for a null required
  *    pointer, a misaligned pointer, negative sizes, k < 1, k > E, k > 16 or E > 512;
- *    MOE_ERR_UNSUPPORTED for shapes with no compiled kernel (H % 64, F % 64 != 0, bf16
- *    activations with fp32 weights or the reverse, NVFP4 with fp32 activations);
+ *    MOE_ERR_UNSUPPORTED for shapes with no compiled kernel (H % 64, F % 64 != 0; bf16
+ *    weights with H % 256 or F % 128 != 0; bf16 activations with fp32 weights or the
+ *    reverse; NVFP4 with fp32 activations), and MOE_ERR_INVALID_ARGUMENT for weights not in
+ *    the layout their dtype requires (moe_layout);
  *    MOE_ERR_WORKSPACE_TOO_SMALL; MOE_ERR_DEVICE when a launch reports an error.
  *  - T = 0 is a successful no-op (token-sized buffers and the workspace may then be NULL;
  *    moe_permute and moe_forward still set counts/offsets, when given, to zero).
@@ -88,13 +90,29 @@ typedef struct {
     int32_t path;         /* moe_path */
 } moe_problem;
 
+/* Weight layouts.  bf16 expert weights are consumed in the PACKED layout written by
+ * moe_pack_weights; fp32 and NVFP4 expert weights in the ROW_MAJOR layout described below.
+ *
+ * PACKED (bf16 only; needs H % 256 == 0 and F % 128 == 0; same byte size as row-major):
+ * weights are cut into tiles of 256 weight rows and stages of 32 consecutive input elements;
+ * each (expert, tile, stage) block is 16 KiB = 256 rows x 4 chunks of 8 bf16, and chunk c of
+ * tile row r is stored in slot c ^ ((r >> 1) & 3) of that row.  Blocks are ordered
+ * [expert][tile][stage].
+ *   w13: F/128 tiles of H/32 stages; tile row r of tile t is the gate row
+ *        f = 128 t + 64 (r / 128) + (r % 64) when r % 128 < 64, else the up row F + f.
+ *   w2:  H/256 tiles of F/32 stages; tile row r of tile t is weight row 256 t + r.
+ * One stage of one tile is then one contiguous 16 KiB read that lands in LDS unchanged, and
+ * 16 consecutive rows of one stage are one contiguous 1 KiB. */
+typedef enum { MOE_LAYOUT_ROW_MAJOR = 0, MOE_LAYOUT_PACKED = 1 } moe_layout;
+
 typedef struct {
-    const void* w13;              /* [E,2F,H] act-width values, or NVFP4 bytes [E,2F,H/2] */
-    const void* w2;               /* [E,H,F], or NVFP4 bytes [E,H,F/2] */
+    const void* w13;              /* [E,2F,H] fp32 or packed bf16, or NVFP4 bytes [E,2F,H/2] */
+    const void* w2;               /* [E,H,F] fp32 or packed bf16, or NVFP4 bytes [E,H,F/2] */
     const uint8_t* w13_scale;     /* NVFP4 only: E4M3 [E,2F,H/16] */
     const uint8_t* w2_scale;      /* NVFP4 only: E4M3 [E,H,F/16] */
     const float* w13_gscale;      /* NVFP4 only, nullable (=> 1.0): fp32 [E] */
     const float* w2_gscale;       /* NVFP4 only, nullable (=> 1.0): fp32 [E] */
+    int32_t layout;               /* moe_layout: PACKED for bf16, ROW_MAJOR otherwise */
 } moe_expert_weights;
 
 /* Text of a status code (static storage). */
@@ -104,6 +122,15 @@ const char* moe_status_string(moe_status s);
  * for all of them).  Host only; touches no device.  Returns MOE_ERR_INVALID_ARGUMENT /
  * MOE_ERR_UNSUPPORTED for problems the entry points would reject. */
 moe_status moe_workspace_size(const moe_problem* p, size_t* bytes);
+
+/* Bytes of the packed w13 and w2 of problem `p` (bf16 weights only).  Host only. */
+moe_status moe_packed_weights_size(const moe_problem* p, size_t* w13_bytes, size_t* w2_bytes);
+
+/* Rewrite row-major bf16 expert weights w13 [E,2F,H] and w2 [E,H,F] into the PACKED layout
+ * (see moe_layout).  A one-time transform of static weights; the outputs must not alias the
+ * inputs.  Either pair (w13 -> w13_packed, w2 -> w2_packed) may be NULL to skip it. */
+moe_status moe_pack_weights(const moe_problem* p, const void* w13, const void* w2,
+                            void* w13_packed, void* w2_packed, void* stream);
 
 /* Route.  x [T,H] and w_router [E,H] in act_dtype; router_bias fp32 [E] or NULL.
  * Writes topk_ids int32 [T,k] and topk_w fp32 [T,k] (routing contract above). */

@@ -52,6 +52,7 @@ moe_status check_problem(const moe_problem* p) {
     if (p->w_dtype != MOE_F32 && p->w_dtype != MOE_BF16 && p->w_dtype != MOE_NVFP4)
         return MOE_ERR_INVALID_ARGUMENT;
     if (p->hidden % 64 || p->ffn % 64) return MOE_ERR_UNSUPPORTED;
+    if (p->w_dtype == MOE_BF16 && (p->hidden % 256 || p->ffn % 128)) return MOE_ERR_UNSUPPORTED;
     if (p->act_dtype == MOE_F32 && p->w_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
     if (p->act_dtype == MOE_BF16 && p->w_dtype == MOE_F32) return MOE_ERR_UNSUPPORTED;
     if (long(p->num_tokens) * p->top_k > (1L << 30) || long(p->num_tokens) * p->hidden > (1L << 40))
@@ -100,6 +101,8 @@ moe_status check_ws(const moe_problem& p, void* ws, size_t bytes) {
 
 moe_status check_weights(const moe_problem& p, const moe_expert_weights* w) {
     if (!w || !w->w13 || !w->w2 || !aligned(w->w13) || !aligned(w->w2)) return MOE_ERR_INVALID_ARGUMENT;
+    if (w->layout != (p.w_dtype == MOE_BF16 ? MOE_LAYOUT_PACKED : MOE_LAYOUT_ROW_MAJOR))
+        return MOE_ERR_INVALID_ARGUMENT;
     if (p.w_dtype == MOE_NVFP4) {
         if (!w->w13_scale || !w->w2_scale) return MOE_ERR_INVALID_ARGUMENT;
         // scale rows are H/16 or F/16 bytes: 2-byte loads need even offsets
@@ -176,6 +179,30 @@ moe_status moe_workspace_size(const moe_problem* p, size_t* bytes) {
     MOE_TRY(check_problem(p));
     if (!bytes) return MOE_ERR_INVALID_ARGUMENT;
     *bytes = layout(*p).total;
+    return MOE_OK;
+}
+
+moe_status moe_packed_weights_size(const moe_problem* p, size_t* w13_bytes, size_t* w2_bytes) {
+    MOE_TRY(check_problem(p));
+    if (p->w_dtype != MOE_BF16 || !w13_bytes || !w2_bytes) return MOE_ERR_INVALID_ARGUMENT;
+    const size_t E = p->num_experts, H = p->hidden, F = p->ffn;
+    *w13_bytes = E * 2 * F * H * 2;
+    *w2_bytes = E * H * F * 2;
+    return MOE_OK;
+}
+
+moe_status moe_pack_weights(const moe_problem* p, const void* w13, const void* w2, void* w13_packed,
+                            void* w2_packed, void* stream) {
+    MOE_TRY(check_problem(p));
+    if (p->w_dtype != MOE_BF16) return MOE_ERR_INVALID_ARGUMENT;
+    if ((w13 == nullptr) != (w13_packed == nullptr) || (w2 == nullptr) != (w2_packed == nullptr))
+        return MOE_ERR_INVALID_ARGUMENT;
+    for (const void* q : {w13, w2, (const void*)w13_packed, (const void*)w2_packed})
+        if (q && !aligned(q)) return MOE_ERR_INVALID_ARGUMENT;
+    if ((w13 && w13 == w13_packed) || (w2 && w2 == w2_packed)) return MOE_ERR_INVALID_ARGUMENT;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (w13) MOE_TRY(dev(launch_pack_bf16(w13, w13_packed, 0, p->num_experts, p->ffn, p->hidden, s)));
+    if (w2) MOE_TRY(dev(launch_pack_bf16(w2, w2_packed, 1, p->num_experts, p->ffn, p->hidden, s)));
     return MOE_OK;
 }
 

@@ -278,156 +278,15 @@ __device__ __forceinline__ void dma16(const void* src, const void* lds_base) {
 
 }  // namespace
 
-template <int KIND>
-__global__ __launch_bounds__(256, 1) void gemm_prefill_bf16_kernel(GemmArgs g) {
-    constexpr int BM = 256, BN = 128;
-    constexpr int A_DMA = BM / 8 / 4;  // 8-row groups per wavefront per stage
-    constexpr int B_DMA = BN / 8 / 4;
-    constexpr int LOADS = A_DMA + B_DMA;
-    __shared__ uint4 sA0[BM * 8], sA1[BM * 8], sA2[BM * 8];
-    __shared__ uint4 sB0[BN * 8], sB1[BN * 8], sB2[BN * 8];
-
-    // XCD-aware work order.  Workgroups go to the 8 XCDs round-robin by block index, and each
-    // XCD has its own L2.  The (tile, column-tile) items, tile-major, are cut into 8 contiguous
-    // runs and XCD x walks run x, so all column tiles of a row tile run on one XCD at about
-    // the same time and share its gathered activation rows in that XCD's L2.
-    const int ncols = (KIND == kGateUp) ? g.F / 64 : (g.N + BN - 1) / BN;
-    const int items = *g.tile_count * ncols;
-    const int run = (items + 7) >> 3;
-    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
-    const int item = xcd * run + j;
-    if (j >= run || item >= items) return;
-    const Tile tile = g.tiles[item / ncols];
-    const int e = tile.expert, r0 = tile.row0, r1 = tile.row1;
-    const int nsub = (r1 - r0 + 15) / 16;
-    const int nt = item % ncols;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
-    const int wr = wave >> 1, wc = wave & 1;
-    const int K = g.K;
-    const int Nw = (KIND == kGateUp) ? 2 * g.F : g.N;
-
-    // per-lane source pointers (bytes) of the chunks this lane moves each stage
-    const char* pa[A_DMA];
-    const char* pb[B_DMA];
-#pragma unroll
-    for (int i = 0; i < A_DMA; ++i) {
-        const int row = (i * 4 + wave) * 8 + (lane >> 3);
-        const int ch = (lane & 7) ^ (row & 7);
-        const int rr = min(r0 + row, r1 - 1);
-        int src = g.a_rows ? g.a_rows[rr] : rr;
-        src = src < 0 ? 0 : (src >= g.a_rows_limit ? g.a_rows_limit - 1 : src);
-        pa[i] = static_cast<const char*>(g.a) + (size_t(src) * K + ch * 8) * 2;
-    }
-#pragma unroll
-    for (int i = 0; i < B_DMA; ++i) {
-        const int row = (i * 4 + wave) * 8 + (lane >> 3);
-        const int ch = (lane & 7) ^ (row & 7);
-        int wrow;
-        if (KIND == kGateUp) {
-            const int q = row & 63;
-            const int f = nt * 64 + (row >> 6) * 32 + (q & 31);
-            wrow = q < 32 ? f : g.F + f;
-        } else {
-            wrow = min(nt * BN + row, g.N - 1);
-        }
-        pb[i] = static_cast<const char*>(g.w) + ((size_t(e) * Nw + wrow) * K + ch * 8) * 2;
-    }
-
-#define MOE_ISSUE(SA, SB, K0)                                                                   \
-    do {                                                                                        \
-        const int k0_ = (K0);                                                                   \
-        _Pragma("unroll") for (int i = 0; i < A_DMA; ++i)                                       \
-            dma16(pa[i] + k0_ * 2, &SA[(i * 4 + wave) * 64]);                                   \
-        _Pragma("unroll") for (int i = 0; i < B_DMA; ++i)                                       \
-            dma16(pb[i] + k0_ * 2, &SB[(i * 4 + wave) * 64]);                                   \
-    } while (0)
-
-    f32x4_t acc[8][4];
-#pragma unroll
-    for (int mi = 0; mi < 8; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-#define MOE_COMPUTE(SA, SB)                                                                     \
-    do {                                                                                        \
-        _Pragma("unroll") for (int ks = 0; ks < 2; ++ks) {                                      \
-            const int ch = ks * 4 + (lane >> 4);                                                \
-            bf16x8_t bf[4];                                                                     \
-            _Pragma("unroll") for (int ni = 0; ni < 4; ++ni) bf[ni] =                           \
-                __builtin_bit_cast(bf16x8_t, SB[lds_slot(wc * 64 + ni * 16 + (lane & 15), ch)]); \
-            _Pragma("unroll") for (int mi = 0; mi < 8; ++mi) {                                  \
-                if (mi * 2 + wr < nsub) {                                                       \
-                    const bf16x8_t af = __builtin_bit_cast(                                     \
-                        bf16x8_t, SA[lds_slot((mi * 2 + wr) * 16 + (lane & 15), ch)]);          \
-                    _Pragma("unroll") for (int ni = 0; ni < 4; ++ni) acc[mi][ni] =              \
-                        __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[ni], acc[mi][ni], 0, 0, 0); \
-                }                                                                               \
-            }                                                                                   \
-        }                                                                                       \
-    } while (0)
-
-    // Every step issues the same number of loads (past the last stage they re-read the last
-    // stage into the free slot), so the load counter always holds exactly one stage after the
-    // current one and a fixed wait count is exact.
-    const int nk = K / BK;
-    const int last = (nk - 1) * BK;
-    MOE_ISSUE(sA0, sB0, 0);
-    MOE_ISSUE(sA1, sB1, min(BK, last));
-    for (int kt = 0;; kt += 3) {
-        wait_vm_lgkm0<LOADS>();  // slot 0 = stage kt
-        block_barrier();
-        MOE_ISSUE(sA2, sB2, min((kt + 2) * BK, last));
-        MOE_COMPUTE(sA0, sB0);
-        if (kt + 1 >= nk) break;
-        wait_vm_lgkm0<LOADS>();  // slot 1 = stage kt+1
-        block_barrier();
-        MOE_ISSUE(sA0, sB0, min((kt + 3) * BK, last));
-        MOE_COMPUTE(sA1, sB1);
-        if (kt + 2 >= nk) break;
-        wait_vm_lgkm0<LOADS>();  // slot 2 = stage kt+2
-        block_barrier();
-        MOE_ISSUE(sA1, sB1, min((kt + 4) * BK, last));
-        MOE_COMPUTE(sA2, sB2);
-        if (kt + 3 >= nk) break;
-    }
-    wait_vm_lgkm0<0>();  // no load may still be writing LDS when the block ends
-#undef MOE_ISSUE
-#undef MOE_COMPUTE
-
-    uint16_t* out = static_cast<uint16_t*>(g.out);
-#pragma unroll
-    for (int mi = 0; mi < 8; ++mi) {
-        if (mi * 2 + wr >= nsub) continue;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = r0 + (mi * 2 + wr) * 16 + 4 * (lane >> 4) + i;
-            if (row >= r1) continue;
-            if (KIND == kGateUp) {
-#pragma unroll
-                for (int ni = 0; ni < 2; ++ni) {
-                    const int col = nt * 64 + wc * 32 + ni * 16 + (lane & 15);
-                    out[size_t(row) * g.F + col] = (uint16_t)bf16_rne(silu_mul(acc[mi][ni][i], acc[mi][ni + 2][i]));
-                }
-            } else {
-#pragma unroll
-                for (int ni = 0; ni < 4; ++ni) {
-                    const int col = nt * BN + wc * 64 + ni * 16 + (lane & 15);
-                    if (col < g.N) out[size_t(row) * g.N + col] = (uint16_t)bf16_rne(acc[mi][ni][i]);
-                }
-            }
-        }
-    }
-}
-
 // ---------------------------------------------------------------------------------------
-// Prefill kernel v2, bf16 weights: 256 x 256 block tile, 4 wavefronts (2 x 2) of 128 x 128
+// Prefill kernel, bf16 weights: 256 x 256 block tile, 4 wavefronts (2 x 2) of 128 x 128
 // (256 fp32 accumulators per lane, held in AGPRs), K in 32-wide stages.  A 4-slot LDS ring
-// (4 x 32 KiB) is filled by direct global->LDS loads, so three stages are in flight while
-// one is consumed, and the operand fragments of the next stage are read from LDS into
-// registers while the 64 MFMAs of the current stage run.  Rows are 64 bytes in LDS; the
-// 16-byte chunk c of row r sits in slot c ^ ((r >> 1) & 3), which keeps the fragment reads
-// (8 consecutive rows, one chunk) on distinct banks.
+// (4 x 32 KiB) is filled by direct global->LDS loads and the operand fragments of the next
+// stage are read from LDS into registers while the 64 MFMAs of the current stage run.  Rows
+// are 64 bytes in LDS; the 16-byte chunk c of row r sits in slot c ^ ((r >> 1) & 3), which
+// keeps the fragment reads (8 consecutive rows, one chunk) on distinct banks.  Activation
+// rows are gathered through the dispatch map; weights come in the packed layout, where every
+// stage of a 256-row tile is already this LDS image (one contiguous 16 KiB read).
 // ---------------------------------------------------------------------------------------
 
 namespace {
@@ -435,7 +294,7 @@ __device__ __forceinline__ int lds_slot32(int row, int ch) { return row * 4 + (c
 }  // namespace
 
 template <int KIND>
-__global__ __launch_bounds__(256, 1) void gemm_prefill_bf16_v2_kernel(GemmArgs g) {
+__global__ __launch_bounds__(256, 1) void gemm_prefill_bf16_kernel(GemmArgs g) {
     constexpr int BM = 256, BN = 256, BKS = 32;
     constexpr int A_DMA = BM / 16 / 4;  // 16-row groups (1 KiB) per wavefront per stage
     constexpr int B_DMA = BN / 16 / 4;
@@ -471,20 +330,12 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_bf16_v2_kernel(GemmArgs g
         src = src < 0 ? 0 : (src >= g.a_rows_limit ? g.a_rows_limit - 1 : src);
         pa[i] = static_cast<const char*>(g.a) + (size_t(src) * K + ch * 8) * 2;
     }
+    // packed weights: block (e, nt, stage) is the 16 KiB image of the LDS slot; wavefront
+    // instruction i moves its bytes [1 KiB (i * 4 + wave), +1 KiB) (ncols equals the packed
+    // tile count: F/128 gate/up tiles, H/256 down tiles)
+    const char* const wblk = static_cast<const char*>(g.w) + (size_t(e) * ncols + nt) * size_t(K / BKS) * 16384;
 #pragma unroll
-    for (int i = 0; i < B_DMA; ++i) {
-        const int row = (i * 4 + wave) * 16 + (lane >> 2);
-        const int ch = (lane & 3) ^ ((row >> 1) & 3);
-        int wrow;
-        if (KIND == kGateUp) {  // per wavefront column: 64 gate rows, then the 64 matching up rows
-            const int q = row & 127;
-            const int f = nt * HALF + (row >> 7) * 64 + (q & 63);
-            wrow = q < 64 ? f : g.F + f;
-        } else {
-            wrow = min(nt * BN + row, g.N - 1);
-        }
-        pb[i] = static_cast<const char*>(g.w) + ((size_t(e) * Nw + wrow) * K + ch * 8) * 2;
-    }
+    for (int i = 0; i < B_DMA; ++i) pb[i] = wblk + (i * 4 + wave) * 1024 + lane * 16;
 
 #define MOE_ISSUE2(SA, SB, K0)                                                                  \
     do {                                                                                        \
@@ -492,7 +343,7 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_bf16_v2_kernel(GemmArgs g
         _Pragma("unroll") for (int i = 0; i < A_DMA; ++i)                                       \
             dma16(pa[i] + k0_ * 2, &SA[(i * 4 + wave) * 64]);                                   \
         _Pragma("unroll") for (int i = 0; i < B_DMA; ++i)                                       \
-            dma16(pb[i] + k0_ * 2, &SB[(i * 4 + wave) * 64]);                                   \
+            dma16(pb[i] + k0_ * 512, &SB[(i * 4 + wave) * 64]);                                 \
     } while (0)
 #define MOE_READ2(SA, SB, AF, BF)                                                               \
     do {                                                                                        \
@@ -792,13 +643,14 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_v4_kernel(GemmArgs g) {
 // from HBM ("Hosting Qwen on Blackwell", section Decoders: decode matmuls are bound by weight
 // loads).  One wavefront owns 16 weight rows (gate/up: 16 gate rows and the 16 matching up
 // rows) and up to 16 dispatched rows of one expert; weights go from global memory straight
-// into MFMA operand registers (no LDS), several 128-wide K blocks in flight per lane.
+// into MFMA operand registers (no LDS), two 128-wide K blocks in flight per lane.
 //
-// Within each 128-wide K block the reduction index is permuted so that one lane's operand
-// elements are contiguous: MFMA i (0..3) of the block takes, in k-group q = lane / 16,
-// elements 128 j + 32 q + 8 i .. +7 for both operands (any common permutation of K leaves the
-// dot products unchanged).  A lane then fetches 64 contiguous bytes of bf16 weights, or 16
-// bytes of packed NVFP4 nibbles plus their two scales, per block.
+// bf16 weights come packed: MFMA i of K block j is stage 4 j + i, and lane (row n, k-group q)
+// reads logical chunk q of its row in that stage (16 rows x 64 bytes of a stage are one
+// contiguous KiB).  NVFP4 weights are row-major; there the reduction index is permuted inside
+// each 128-wide block so that one lane's 32 nibbles are contiguous: MFMA i takes, in k-group
+// q, elements 128 j + 32 q + 8 i .. +7 of both operands (a common permutation of K leaves the
+// dot products unchanged).
 //
 // SPLITK wavefronts of a block share 16 columns and split K; their partial sums meet in LDS
 // and are added in a fixed order (deterministic).
@@ -829,7 +681,7 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
     const int rr = min(r0 + n, r1 - 1);
     int src = g.a_rows ? g.a_rows[rr] : rr;
     src = src < 0 ? 0 : (src >= g.a_rows_limit ? g.a_rows_limit - 1 : src);
-    const uint16_t* pa = static_cast<const uint16_t*>(g.a) + size_t(src) * K + 32 * q;
+    const uint16_t* pa = static_cast<const uint16_t*>(g.a) + size_t(src) * K + (WFMT == kWBF16 ? 8 : 32) * q;
     const int col = min(cg, ncg - 1) * 16 + n;
     int wrow0, wrow1 = 0;
     if (KIND == kGateUp) {
@@ -838,7 +690,6 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
     } else {
         wrow0 = min(col, g.N - 1);
     }
-    const size_t w0 = size_t(e) * Nw + wrow0, w1 = size_t(e) * Nw + wrow1;
 
     f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
     const int nblk = K / 128 / SPLITK;
@@ -854,30 +705,55 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
         uint32_t sg, su;           // NVFP4 scale pairs
     };
     auto ld16 = [](const void* p) __attribute__((always_inline)) { return *reinterpret_cast<const uint4*>(p); };
-    const uint16_t* pw0 = static_cast<const uint16_t*>(g.w) + w0 * K + 32 * q;
-    const uint16_t* pw1 = static_cast<const uint16_t*>(g.w) + w1 * K + 32 * q;
+    // bf16 (packed): lane's 16 bytes of stage st of its gate/down row and of its up row
+    const uint16_t* pw0 = nullptr;
+    const uint16_t* pw1 = nullptr;
+    if constexpr (WFMT == kWBF16) {
+        const int nst = K / 32;
+        int t, r_a;
+        if (KIND == kGateUp) {
+            t = col >> 7;
+            r_a = ((col >> 6) & 1) * 128 + (col & 63);  // gate tile row; the up row is 64 below
+        } else {
+            t = wrow0 >> 8;
+            r_a = wrow0 & 255;
+        }
+        const int ntiles = (KIND == kGateUp) ? g.F / 128 : g.N / 256;
+        const uint16_t* blk = static_cast<const uint16_t*>(g.w) + (size_t(e) * ntiles + t) * size_t(nst) * 8192;
+        pw0 = blk + r_a * 32 + (q ^ ((r_a >> 1) & 3)) * 8;
+        if (KIND == kGateUp) {
+            const int r_u = r_a + 64;
+            pw1 = blk + r_u * 32 + (q ^ ((r_u >> 1) & 3)) * 8;
+        }
+    }
+    const size_t w0 = size_t(e) * Nw + wrow0, w1 = size_t(e) * Nw + wrow1;
     const uint8_t* pq0 = static_cast<const uint8_t*>(g.w) + w0 * (K / 2) + 16 * q;
     const uint8_t* pq1 = static_cast<const uint8_t*>(g.w) + w1 * (K / 2) + 16 * q;
     const uint8_t* ps0 = g.wscale + w0 * (K / 16) + 2 * q;
     const uint8_t* ps1 = g.wscale + w1 * (K / 16) + 2 * q;
     auto load = [&](Blk& b, int j) __attribute__((always_inline)) {
         const int k = 128 * j;
-        b.a0 = ld16(pa + k);
-        b.a1 = ld16(pa + k + 8);
-        b.a2 = ld16(pa + k + 16);
-        b.a3 = ld16(pa + k + 24);
         if constexpr (WFMT == kWBF16) {
-            b.g0 = ld16(pw0 + k);
-            b.g1 = ld16(pw0 + k + 8);
-            b.g2 = ld16(pw0 + k + 16);
-            b.g3 = ld16(pw0 + k + 24);
+            b.a0 = ld16(pa + k);
+            b.a1 = ld16(pa + k + 32);
+            b.a2 = ld16(pa + k + 64);
+            b.a3 = ld16(pa + k + 96);
+            const size_t so = size_t(4 * j) * 8192;  // stage 4 j
+            b.g0 = ld16(pw0 + so);
+            b.g1 = ld16(pw0 + so + 8192);
+            b.g2 = ld16(pw0 + so + 16384);
+            b.g3 = ld16(pw0 + so + 24576);
             if constexpr (KIND == kGateUp) {
-                b.u0 = ld16(pw1 + k);
-                b.u1 = ld16(pw1 + k + 8);
-                b.u2 = ld16(pw1 + k + 16);
-                b.u3 = ld16(pw1 + k + 24);
+                b.u0 = ld16(pw1 + so);
+                b.u1 = ld16(pw1 + so + 8192);
+                b.u2 = ld16(pw1 + so + 16384);
+                b.u3 = ld16(pw1 + so + 24576);
             }
         } else {
+            b.a0 = ld16(pa + k);
+            b.a1 = ld16(pa + k + 8);
+            b.a2 = ld16(pa + k + 16);
+            b.a3 = ld16(pa + k + 24);
             b.pg = ld16(pq0 + 64 * j);
             b.sg = *reinterpret_cast<const uint16_t*>(ps0 + 8 * j);
             if constexpr (KIND == kGateUp) {
@@ -1047,17 +923,10 @@ template <int BM, int BN, int WM, int WN>
 static void launch_mfma(const GemmArgs& g, int max_tiles, hipStream_t s) {
     const int ncols = g.kind == kGateUp ? g.F / (BN / 2) : (g.N + BN - 1) / BN;
     dim3 grid(max_tiles, ncols), block(WM * WN * 64);
-    if (g.kind == kGateUp) {
-        if (g.wfmt == kWBF16)
-            hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, kGateUp, kWBF16>), grid, block, 0, s, g);
-        else
-            hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, kGateUp, kWNVFP4>), grid, block, 0, s, g);
-    } else {
-        if (g.wfmt == kWBF16)
-            hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, kDown, kWBF16>), grid, block, 0, s, g);
-        else
-            hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, kDown, kWNVFP4>), grid, block, 0, s, g);
-    }
+    if (g.kind == kGateUp)
+        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, kGateUp, kWNVFP4>), grid, block, 0, s, g);
+    else
+        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, kDown, kWNVFP4>), grid, block, 0, s, g);
 }
 
 // Work items of the prefill kernels: (row tile, column tile) pairs, a multiple of 8 blocks so
@@ -1077,14 +946,8 @@ hipError_t launch_gemm(const GemmArgs& g, int family, int max_tiles, hipStream_t
             hipLaunchKernelGGL((gemm_f32_kernel<kGateUp>), grid, block, 0, s, g);
         else
             hipLaunchKernelGGL((gemm_f32_kernel<kDown>), grid, block, 0, s, g);
-    } else if (family == kFamPrefill && g.wfmt == kWBF16 && g.F % 128 == 0) {
+    } else if (family == kFamPrefill && g.wfmt == kWBF16) {  // packed weights: F % 128 == 0, H % 256 == 0
         const dim3 grid = prefill_grid(g, max_tiles, 256);
-        if (up)
-            hipLaunchKernelGGL((gemm_prefill_bf16_v2_kernel<kGateUp>), grid, dim3(256), 0, s, g);
-        else
-            hipLaunchKernelGGL((gemm_prefill_bf16_v2_kernel<kDown>), grid, dim3(256), 0, s, g);
-    } else if (family == kFamPrefill && g.wfmt == kWBF16) {
-        const dim3 grid = prefill_grid(g, max_tiles, 128);
         if (up)
             hipLaunchKernelGGL((gemm_prefill_bf16_kernel<kGateUp>), grid, dim3(256), 0, s, g);
         else
@@ -1113,7 +976,7 @@ hipError_t launch_gemm(const GemmArgs& g, int family, int max_tiles, hipStream_t
             else    { if (split == 1) MOE_DEC(kDown, kWNVFP4, 1);   else if (split == 2) MOE_DEC(kDown, kWNVFP4, 2);   else MOE_DEC(kDown, kWNVFP4, 4); }
         }
 #undef MOE_DEC
-    } else {
+    } else {  // NVFP4 with K % 128 != 0
         launch_mfma<DC_BM, DC_BN, DC_WM, DC_WN>(g, max_tiles, s);
     }
     return hipGetLastError();

@@ -1,0 +1,48 @@
+// pack.hip -- one-time rewrite of bf16 expert weights into the packed layout of moe.h.
+//
+// Each (expert, 256-row tile, 32-element stage) block becomes the byte image of an LDS slot of
+// the grouped GEMMs (rows 64 bytes, chunk c of row r in slot c ^ ((r >> 1) & 3)), so that the
+// kernels stream every stage of a weight tile as one contiguous 16 KiB read and 16 rows of a
+// stage as one contiguous 1 KiB.  Row-strided reads of the same bytes (256 rows, 8 KiB apart,
+// 64 bytes each) reach about three quarters of the HBM bandwidth of contiguous ones on MI355X.
+#include "device.h"
+#include "launch.h"
+
+namespace moe {
+
+// One thread per 16-byte destination chunk (grid-stride).  kind 0: w13 (gate/up tiles of 128
+// hid columns), kind 1: w2 (tiles of 256 output rows).
+__global__ __launch_bounds__(256) void pack_bf16_kernel(const uint4* __restrict__ src,
+                                                        uint4* __restrict__ dst, int kind, int E,
+                                                        int F, int H) {
+    const int K = kind == 0 ? H : F;                 // input elements per weight row
+    const int Nw = kind == 0 ? 2 * F : H;            // weight rows per expert
+    const int ntiles = kind == 0 ? F / 128 : H / 256;
+    const int nst = K / 32;
+    const long total = long(E) * ntiles * nst * 1024;
+    for (long d = long(blockIdx.x) * blockDim.x + threadIdx.x; d < total; d += long(gridDim.x) * blockDim.x) {
+        const long blk = d >> 10;
+        const int w = int(d & 1023), r = w >> 2, slot = w & 3;
+        const int c = slot ^ ((r >> 1) & 3);
+        const int st = int(blk % nst);
+        const long et = blk / nst;
+        const int t = int(et % ntiles), e = int(et / ntiles);
+        int wrow;
+        if (kind == 0) {
+            const int q = r & 127;
+            const int f = 128 * t + 64 * (r >> 7) + (q & 63);
+            wrow = q < 64 ? f : F + f;
+        } else {
+            wrow = 256 * t + r;
+        }
+        dst[d] = src[((long(e) * Nw + wrow) * K + st * 32 + c * 8) / 8];
+    }
+}
+
+hipError_t launch_pack_bf16(const void* src, void* dst, int kind, int E, int F, int H, hipStream_t s) {
+    hipLaunchKernelGGL(pack_bf16_kernel, dim3(8192), dim3(256), 0, s, static_cast<const uint4*>(src),
+                       static_cast<uint4*>(dst), kind, E, F, H);
+    return hipGetLastError();
+}
+
+}  // namespace moe

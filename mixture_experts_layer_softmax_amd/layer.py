@@ -49,12 +49,20 @@ class MoELayer:
         wk = "bf16" if wdt == "bf16" else None
         self.w13 = to_device(inputs["w13"], d, wk)
         self.w2 = to_device(inputs["w2"], d, wk)
+        layout = lib.LAYOUT_ROW_MAJOR
+        if wdt == "bf16":  # the library consumes bf16 expert weights in its packed layout
+            p13 = torch.empty_like(self.w13)
+            p2 = torch.empty_like(self.w2)
+            lib.pack_weights(self.problem, self.w13, self.w2, p13, p2)
+            torch.cuda.current_stream(d).synchronize()
+            self.w13, self.w2 = p13, p2
+            layout = lib.LAYOUT_PACKED
         self.w13_scale = to_device(inputs.get("w13_scale"), d)
         self.w2_scale = to_device(inputs.get("w2_scale"), d)
         self.w13_gscale = to_device(inputs.get("w13_gscale"), d)
         self.w2_gscale = to_device(inputs.get("w2_gscale"), d)
         self.weights = lib.weights(self.w13, self.w2, self.w13_scale, self.w2_scale,
-                                   self.w13_gscale, self.w2_gscale)
+                                   self.w13_gscale, self.w2_gscale, layout)
         self._ws_tokens = -1
         self.ws = None
 

@@ -22,8 +22,9 @@ DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "nvfp4": MOE_NVFP4}
 PATHS = {"auto": PATH_AUTO, "prefill": PATH_PREFILL, "decode": PATH_DECODE}
 
 #: every symbol the header declares
-EXPORTS = ("moe_status_string", "moe_workspace_size", "moe_route", "moe_permute",
-           "moe_grouped_gemm", "moe_combine", "moe_forward")
+EXPORTS = ("moe_status_string", "moe_workspace_size", "moe_packed_weights_size", "moe_pack_weights",
+           "moe_route", "moe_permute", "moe_grouped_gemm", "moe_combine", "moe_forward")
+LAYOUT_ROW_MAJOR, LAYOUT_PACKED = 0, 1
 
 
 class MoeError(RuntimeError):
@@ -40,7 +41,8 @@ class Problem(C.Structure):
 
 class ExpertWeights(C.Structure):
     _fields_ = [("w13", C.c_void_p), ("w2", C.c_void_p), ("w13_scale", C.c_void_p),
-                ("w2_scale", C.c_void_p), ("w13_gscale", C.c_void_p), ("w2_gscale", C.c_void_p)]
+                ("w2_scale", C.c_void_p), ("w13_gscale", C.c_void_p), ("w2_gscale", C.c_void_p),
+                ("layout", C.c_int32)]
 
 
 _lock = threading.Lock()
@@ -62,6 +64,10 @@ def load() -> C.CDLL:
             L.moe_status_string.argtypes = [i32]
             L.moe_workspace_size.restype = i32
             L.moe_workspace_size.argtypes = [P, C.POINTER(C.c_size_t)]
+            L.moe_packed_weights_size.restype = i32
+            L.moe_packed_weights_size.argtypes = [P, C.POINTER(C.c_size_t), C.POINTER(C.c_size_t)]
+            L.moe_pack_weights.restype = i32
+            L.moe_pack_weights.argtypes = [P, vp, vp, vp, vp, vp]
             L.moe_route.restype = i32
             L.moe_route.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
             L.moe_permute.restype = i32
@@ -110,9 +116,22 @@ def workspace_size(p: Problem) -> int:
     return n.value
 
 
-def weights(w13, w2, w13_scale=None, w2_scale=None, w13_gscale=None, w2_gscale=None) -> ExpertWeights:
+def weights(w13, w2, w13_scale=None, w2_scale=None, w13_gscale=None, w2_gscale=None,
+            layout=LAYOUT_ROW_MAJOR) -> ExpertWeights:
     return ExpertWeights(*[t.data_ptr() if t is not None else None
-                           for t in (w13, w2, w13_scale, w2_scale, w13_gscale, w2_gscale)])
+                           for t in (w13, w2, w13_scale, w2_scale, w13_gscale, w2_gscale)],
+                         int(layout))
+
+
+def packed_weights_size(p: Problem):
+    a, b = C.c_size_t(0), C.c_size_t(0)
+    _check(load().moe_packed_weights_size(C.byref(p), C.byref(a), C.byref(b)), "moe_packed_weights_size")
+    return a.value, b.value
+
+
+def pack_weights(p, w13, w2, w13_packed, w2_packed, stream=None):
+    _check(load().moe_pack_weights(C.byref(p), _ptr(w13), _ptr(w2), _ptr(w13_packed),
+                                   _ptr(w2_packed), _stream(stream)), "moe_pack_weights")
 
 
 def route(p, x, w_router, bias, topk_ids, topk_w, ws, stream=None):

@@ -68,6 +68,8 @@ def _call_route(L, p, x=FAKE, wr=FAKE, ids=FAKE, w=FAKE, ws=FAKE, nbytes=1 << 40
     (dict(experts=513), lib.MOE_ERR_INVALID_ARGUMENT),
     (dict(hidden=100), lib.MOE_ERR_UNSUPPORTED),
     (dict(ffn=96), lib.MOE_ERR_UNSUPPORTED),
+    (dict(hidden=192), lib.MOE_ERR_UNSUPPORTED),
+    (dict(ffn=192), lib.MOE_ERR_UNSUPPORTED),
     (dict(act="f32", wdt="bf16"), lib.MOE_ERR_UNSUPPORTED),
     (dict(act="bf16", wdt="f32"), lib.MOE_ERR_UNSUPPORTED),
     (dict(act="f32", wdt="nvfp4"), lib.MOE_ERR_UNSUPPORTED),
@@ -93,10 +95,10 @@ def test_pointer_validation(L):
 def test_gemm_and_forward_validation(L):
     V = C.c_void_p
     p = lib.problem(16, 256, 8, 2, 128, wdt="nvfp4")
-    w = lib.ExpertWeights(FAKE, FAKE, None, None, None, None)  # NVFP4 without scales
+    w = lib.ExpertWeights(FAKE, FAKE, None, None, None, None, 0)  # NVFP4 without scales
     assert L.moe_grouped_gemm(C.byref(p), 0, V(FAKE), None, V(FAKE), C.byref(w), V(FAKE), V(FAKE),
                               1 << 40, None) == lib.MOE_ERR_INVALID_ARGUMENT
-    w = lib.ExpertWeights(FAKE, FAKE, FAKE, FAKE, None, None)
+    w = lib.ExpertWeights(FAKE, FAKE, FAKE, FAKE, None, None, 0)
     assert L.moe_grouped_gemm(C.byref(p), 7, V(FAKE), None, V(FAKE), C.byref(w), V(FAKE), V(FAKE),
                               1 << 40, None) == lib.MOE_ERR_INVALID_ARGUMENT  # bad kind
     assert L.moe_grouped_gemm(C.byref(p), 1, V(FAKE), V(FAKE), V(FAKE), C.byref(w), V(FAKE),
@@ -104,3 +106,18 @@ def test_gemm_and_forward_validation(L):
     assert L.moe_forward(C.byref(p), V(FAKE), V(FAKE), None, C.byref(w), V(FAKE), None, None, None,
                          None, None, None, V(FAKE), 10, None) == lib.MOE_ERR_WORKSPACE_TOO_SMALL
     assert L.moe_combine(C.byref(p), None, V(FAKE), V(FAKE), V(FAKE), None) == lib.MOE_ERR_INVALID_ARGUMENT
+    # layouts: bf16 weights must be packed, NVFP4 weights row-major
+    pb = lib.problem(16, 256, 8, 2, 128, wdt="bf16")
+    for layout, status in ((0, lib.MOE_ERR_INVALID_ARGUMENT), (1, lib.MOE_ERR_WORKSPACE_TOO_SMALL)):
+        wb = lib.ExpertWeights(FAKE, FAKE, None, None, None, None, layout)
+        assert L.moe_forward(C.byref(pb), V(FAKE), V(FAKE), None, C.byref(wb), V(FAKE), None, None,
+                             None, None, None, None, V(FAKE), 10, None) == status
+    w = lib.ExpertWeights(FAKE, FAKE, FAKE, FAKE, None, None, 1)
+    assert L.moe_forward(C.byref(p), V(FAKE), V(FAKE), None, C.byref(w), V(FAKE), None, None, None,
+                         None, None, None, V(FAKE), 1 << 40, None) == lib.MOE_ERR_INVALID_ARGUMENT
+    # packing: bf16 only, no aliasing, shapes the layout can tile
+    assert L.moe_pack_weights(C.byref(p), V(FAKE), V(FAKE), V(FAKE + 4096), V(FAKE + 8192),
+                              None) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_pack_weights(C.byref(pb), V(FAKE), None, V(FAKE), None, None) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_pack_weights(C.byref(lib.problem(16, 192, 8, 2, 128)), V(FAKE), None, V(FAKE + 4096),
+                              None, None) == lib.MOE_ERR_UNSUPPORTED

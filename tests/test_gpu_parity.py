@@ -23,7 +23,7 @@ W = synth.Workload
 SMALL = {
     "small_bf16": W("small_bf16", 512, 512, 8, 2, 256, "bf16", "bf16", 11, "normal"),
     "small_nvfp4": W("small_nvfp4", 384, 512, 16, 4, 256, "bf16", "nvfp4", 12, "normal"),
-    "ragged_bf16": W("ragged_bf16", 77, 192, 5, 3, 320, "bf16", "bf16", 13, "normal"),
+    "ragged_bf16": W("ragged_bf16", 77, 256, 5, 3, 384, "bf16", "bf16", 13, "normal"),
     "ragged_nvfp4": W("ragged_nvfp4", 77, 192, 5, 3, 320, "bf16", "nvfp4", 14, "normal"),
     "tiny": synth.WORKLOADS["tiny"],
 }
@@ -120,11 +120,11 @@ def test_permute_matches_oracle(T, E, k):
     # skewed loads: draw experts with unequal probabilities, distinct within a token
     pr = rng.dirichlet(np.full(E, 0.3))
     ids = np.array([rng.choice(E, size=k, replace=False, p=pr) for _ in range(T)], dtype=np.int32)
-    H = 64
+    H = 256
     x = synth.to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
     note("permute T=%d E=%d k=%d" % (T, E, k))
     counts, offsets, st, ip = O.permute(ids, E)
-    p = lib.problem(T, H, E, k, 64)
+    p = lib.problem(T, H, E, k, 128)
     ws = torch.empty(lib.workspace_size(p), dtype=torch.uint8, device="cuda")
     g = dict(counts=torch.empty(E, dtype=torch.int32, device="cuda"),
              offsets=torch.empty(E + 1, dtype=torch.int32, device="cuda"),
@@ -211,7 +211,7 @@ def test_down_matches_oracle(name, path):
 def test_down_with_one_hot_rows_returns_exact_weights(wdt, path):
     """hid row r = unit vector at f_r: y_perm[r, h] must be W2[e][h, f_r] exactly (the 4-bit
     value decodes exactly to bf16), which pins the weight decode and the tile index maps."""
-    E, H, F = 3, 192, 128
+    E, H, F = 3, (256 if wdt == "bf16" else 192), 128
     wl = W("onehot", 1, H, E, 1, F, "bf16", wdt, 21, "none")
     inp = synth.generate(wl)
     inp.pop("w13_gscale", None)
@@ -235,6 +235,43 @@ def test_down_with_one_hot_rows_returns_exact_weights(wdt, path):
     assert np.array_equal(act_f64(to_host(y_perm)), ref)
 
 
+def test_packed_weight_layout_matches_its_definition():
+    """The packed layout rebuilt independently with numpy from its definition in moe.h."""
+    E, H, F = 2, 512, 256
+    wl = W("pack", 1, H, E, 1, F, "bf16", "bf16", 71, "none")
+    inp = synth.generate(wl)
+    p = lib.problem(1, H, E, 1, F)
+    w13 = to_device(inp["w13"], "cuda", "bf16")
+    w2 = to_device(inp["w2"], "cuda", "bf16")
+    p13, p2 = torch.empty_like(w13), torch.empty_like(w2)
+    note("pack layout")
+    lib.pack_weights(p, w13, w2, p13, p2)
+    torch.cuda.synchronize()
+
+    def expect(w, kind):
+        K = H if kind == 0 else F
+        tiles = F // 128 if kind == 0 else H // 256
+        out = np.empty(w.size, dtype=np.uint16)
+        i = 0
+        for e in range(E):
+            for t in range(tiles):
+                for st in range(K // 32):
+                    for r in range(256):
+                        if kind == 0:
+                            f = 128 * t + 64 * (r // 128) + (r % 64)
+                            row = f if r % 128 < 64 else F + f
+                        else:
+                            row = 256 * t + r
+                        for slot in range(4):
+                            c = slot ^ ((r >> 1) & 3)
+                            out[i:i + 8] = w[e, row, st * 32 + c * 8: st * 32 + c * 8 + 8]
+                            i += 8
+        return out
+
+    assert np.array_equal(to_host(p13).ravel(), expect(inp["w13"], 0))
+    assert np.array_equal(to_host(p2).ravel(), expect(inp["w2"], 1))
+
+
 # ---------------------------------------------------------------------------------------
 # combine
 # ---------------------------------------------------------------------------------------
@@ -250,7 +287,7 @@ def test_combine_matches_oracle(act):
     if act == "bf16":
         yp = synth.to_bf16_bits(yp)
     ref = O.combine(act_f64(yp), ip, w.astype(np.float64))
-    p = lib.problem(T, H, 16, k, 64, act, act)
+    p = lib.problem(T, H, 16, k, 128, act, act)
     y = torch.empty(T, H, dtype=torch.float32 if act == "f32" else torch.bfloat16, device="cuda")
     note("combine act=%s" % act)
     lib.combine(p, to_device(yp, "cuda"), dev_i32(ip), to_device(w, "cuda"), y)
@@ -379,14 +416,14 @@ def test_all_tokens_on_the_same_experts(wdt):
 
 @pytest.mark.parametrize("E,k", [(4, 4), (1, 1), (16, 16)])
 def test_k_equals_e(E, k):
-    wl = W("keqe", 40, 128, E, k, 64, "bf16", "bf16", 41 + E, "normal")
+    wl = W("keqe", 40, 256, E, k, 128, "bf16", "bf16", 41 + E, "normal")
     inp = synth.generate(wl)
     note("k=E=%d" % E)
     _check_forward(wl, inp, MoELayer.from_workload(wl, inp))
 
 
 def test_full_softmax_weights_option():
-    wl = W("nr", 50, 128, 8, 3, 64, "bf16", "bf16", 51, "normal", renormalize=False)
+    wl = W("nr", 50, 256, 8, 3, 128, "bf16", "bf16", 51, "normal", renormalize=False)
     inp = synth.generate(wl)
     note("renormalize=0")
     _check_forward(wl, inp, MoELayer.from_workload(wl, inp))
