@@ -105,6 +105,34 @@ def cpu_baseline(wl, inputs, budget_s: float):
                        "combine) in fp64, %.1f s" % (n, wl.tokens, spent), seconds=spent)
 
 
+def measured_peaks(torch, lib):
+    """What this machine sustains: the bf16 MFMA probe (8 blocks per CU) and a 4 GiB HBM read
+    stream (moe_probe.h), best of three timed runs each, on the current stream."""
+    def best(fn, runs=3):
+        fn()
+        torch.cuda.synchronize()
+        t = []
+        for _ in range(runs):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            work = fn()
+            b.record()
+            torch.cuda.synchronize()
+            t.append((work, a.elapsed_time(b) * 1e-3))
+        return max(w / s for w, s in t)
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(8 * cus, dtype=torch.float32, device="cuda:0")
+    flops = best(lambda: lib.probe_mfma_bf16(8 * cus, 20000, sink))
+    buf = torch.empty(4 * 2 ** 30, dtype=torch.uint8, device="cuda:0")
+    word = torch.empty(1, dtype=torch.int32, device="cuda:0")
+    rate = best(lambda: lib.probe_read(buf, word))
+    del buf
+    return dict(mfma_bf16_tflops=flops / 1e12, hbm_read_gbs=rate / 1e9,
+                probes="bf16 MFMA loop, %d blocks x 4 wavefronts x 20000 x 8 v_mfma_f32_16x16x32_bf16; "
+                       "read stream over 4 GiB" % (8 * cus))
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -114,6 +142,8 @@ def main() -> int:
     ap.add_argument("--flush", choices=("auto", "on", "off"), default="auto")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probes", action="store_true",
+                    help="skip the measured-peak probes (bf16 MFMA loop, 4 GiB read stream)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run one 512 MiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -186,6 +216,8 @@ def main() -> int:
     torch.cuda.synchronize()
     gemm1_ms = timed(gemm1, args.steps)  # includes the ~5 us tile-list kernel it launches first
 
+    peaks = None if args.no_probes else measured_peaks(torch, lib)
+
     if args.calibration_copy:
         a = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device="cuda:0")
         b = torch.empty_like(a)
@@ -202,6 +234,9 @@ def main() -> int:
         roof = dict(bound="mfma", achieved=gflops / (gemm1_ms * 1e-3) / 1e12,
                     peak=PEAK_BF16_FLOPS / 1e12, unit="TFLOP/s")
     roof["frac"] = roof["achieved"] / roof["peak"]
+    if peaks:
+        mp = peaks["hbm_read_gbs"] if roof["bound"] == "hbm" else peaks["mfma_bf16_tflops"]
+        roof["frac_measured"] = roof["achieved"] / mp
     roof["traffic"] = measured_traffic(wl.name)
     roof["kernel"] = "grouped gate/up GEMM + SwiGLU (%s weights)" % wl.wdt
     roof["kernel_ms"] = gemm1_ms
@@ -220,6 +255,10 @@ def main() -> int:
                layer_mfma_frac=flops / (ms_per_step * 1e-3) / PEAK_BF16_FLOPS,
                layer_hbm_frac=nbytes / (ms_per_step * 1e-3) / PEAK_HBM_BYTES,
                wall_s=wall, roofline=roof)
+    if peaks:
+        out["measured_peaks"] = peaks
+        out["layer_mfma_frac_measured"] = flops / (ms_per_step * 1e-3) / (peaks["mfma_bf16_tflops"] * 1e12)
+        out["layer_hbm_frac_measured"] = nbytes / (ms_per_step * 1e-3) / (peaks["hbm_read_gbs"] * 1e9)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl, inputs, args.cpu_budget)

@@ -1,0 +1,39 @@
+/*
+ * moe_probe.h -- measurement aids for the MoE layer library on MI355X (gfx950).
+ *
+ * Two microkernels that measure what the box actually sustains, so that a benchmark can state
+ * its kernels' roofline fractions against measured peaks beside the data-sheet ones
+ * (bf16 dense MFMA 2.5 PFLOP/s, HBM3E 8 TB/s).  They compute nothing of the layer.
+ * Same conventions as moe.h: device pointers owned by the caller, work enqueued on `stream`
+ * (a hipStream_t, NULL = default stream), return codes only, arguments validated on the host
+ * before any HIP call.
+ */
+#ifndef MOE_MI355X_PROBE_H
+#define MOE_MI355X_PROBE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Dense bf16 MFMA issue rate: `blocks` blocks of 256 threads; every wavefront runs `iters`
+ * rounds of 8 independent v_mfma_f32_16x16x32_bf16 (16x16x32 multiply-adds each) on register
+ * operands.  Work = blocks * 4 * iters * 8 * 16384 FLOP.  out: device float[blocks], written
+ * (one value per block) so the chains stay live.  blocks in [1, 1<<20], iters in [1, 1<<24],
+ * else MOE_ERR_INVALID_ARGUMENT. */
+moe_status moe_probe_mfma_bf16(int32_t blocks, int32_t iters, float* out, void* stream);
+
+/* HBM read stream: every 16-byte word of buf[0, bytes) is read once by 16-byte loads, four in
+ * flight per thread, grid-stride over 8192 blocks of 256 threads.  out: device uint32_t[1],
+ * written only for one particular XOR of the data (so the loads cannot be elided).  bytes must
+ * be a positive multiple of 16 and buf 16-byte aligned, else MOE_ERR_INVALID_ARGUMENT. */
+moe_status moe_probe_read(const void* buf, size_t bytes, uint32_t* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_PROBE_H */

@@ -50,6 +50,9 @@ __device__ void emit_tiles(int e, int E, int count, int start, int bm, Tile* til
 }
 
 // One block of kMaxExperts threads: counts, offsets, per-chunk bases, GEMM tile lists.
+// Thread e walks expert e's column of the chunk histograms twice (totals, then bases with the
+// expert's offset added), 32 chunks per batch of independent loads so that the walk costs a
+// few memory round trips rather than one per chunk.
 __global__ __launch_bounds__(kMaxExperts) void scan_kernel(const int32_t* __restrict__ hist,
                                                            int nchunks, int E,
                                                            int32_t* __restrict__ base,
@@ -58,13 +61,16 @@ __global__ __launch_bounds__(kMaxExperts) void scan_kernel(const int32_t* __rest
                                                            Tile* tiles1, int* tile_count1, int bm1,
                                                            Tile* tiles2, int* tile_count2,
                                                            int bm2, int cap) {
+    constexpr int kBatch = 32;
     const int e = threadIdx.x;
     int run = 0;
     if (e < E) {
-        for (int c = 0; c < nchunks; ++c) {
-            const int h = hist[size_t(c) * E + e];
-            base[size_t(c) * E + e] = run;
-            run += h;
+        for (int c0 = 0; c0 < nchunks; c0 += kBatch) {
+            int h[kBatch];
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i) h[i] = (c0 + i < nchunks) ? hist[size_t(c0 + i) * E + e] : 0;
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i) run += h[i];
         }
     }
     int total;
@@ -72,7 +78,17 @@ __global__ __launch_bounds__(kMaxExperts) void scan_kernel(const int32_t* __rest
     if (e < E) {
         if (counts) counts[e] = run;
         offsets[e] = start;
-        for (int c = 0; c < nchunks; ++c) base[size_t(c) * E + e] += start;
+        int acc = start;
+        for (int c0 = 0; c0 < nchunks; c0 += kBatch) {
+            int h[kBatch];
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i) h[i] = (c0 + i < nchunks) ? hist[size_t(c0 + i) * E + e] : 0;
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i) {
+                if (c0 + i < nchunks) base[size_t(c0 + i) * E + e] = acc;
+                acc += h[i];
+            }
+        }
     }
     if (e == 0) offsets[E] = total;
     if (tiles1) emit_tiles(e, E, run, start, bm1, tiles1, tile_count1, cap);

@@ -23,7 +23,8 @@ PATHS = {"auto": PATH_AUTO, "prefill": PATH_PREFILL, "decode": PATH_DECODE}
 
 #: every symbol the header declares
 EXPORTS = ("moe_status_string", "moe_workspace_size", "moe_packed_weights_size", "moe_pack_weights",
-           "moe_route", "moe_permute", "moe_grouped_gemm", "moe_combine", "moe_forward")
+           "moe_route", "moe_permute", "moe_grouped_gemm", "moe_combine", "moe_forward",
+           "moe_probe_mfma_bf16", "moe_probe_read")
 LAYOUT_ROW_MAJOR, LAYOUT_PACKED = 0, 1
 
 
@@ -76,6 +77,10 @@ def load() -> C.CDLL:
             L.moe_grouped_gemm.argtypes = [P, i32, vp, vp, vp, C.POINTER(ExpertWeights), vp, vp, sz, vp]
             L.moe_combine.restype = i32
             L.moe_combine.argtypes = [P, vp, vp, vp, vp, vp]
+            L.moe_probe_mfma_bf16.restype = i32
+            L.moe_probe_mfma_bf16.argtypes = [C.c_int32, C.c_int32, vp, vp]
+            L.moe_probe_read.restype = i32
+            L.moe_probe_read.argtypes = [vp, sz, vp, vp]
             L.moe_forward.restype = i32
             L.moe_forward.argtypes = [P, vp, vp, vp, C.POINTER(ExpertWeights), vp, vp, vp, vp, vp,
                                       vp, vp, vp, sz, vp]
@@ -164,3 +169,17 @@ def forward(p, x, w_router, bias, w: ExpertWeights, y, ws, topk_ids=None, topk_w
                               _ptr(topk_ids), _ptr(topk_w), _ptr(counts), _ptr(offsets),
                               _ptr(sorted_token), _ptr(inv_perm), _ptr(ws),
                               ws.numel() * ws.element_size(), _stream(stream)), "moe_forward")
+
+
+def probe_mfma_bf16(blocks, iters, out, stream=None):
+    """Launch the bf16 MFMA rate probe (moe_probe.h); returns its FLOP count."""
+    _check(load().moe_probe_mfma_bf16(int(blocks), int(iters), _ptr(out), _stream(stream)),
+           "moe_probe_mfma_bf16")
+    return float(blocks) * 4 * iters * 8 * 16384
+
+
+def probe_read(buf, out, stream=None):
+    """Launch the HBM read-stream probe over all of ``buf``; returns the bytes read."""
+    n = buf.numel() * buf.element_size()
+    _check(load().moe_probe_read(_ptr(buf), n, _ptr(out), _stream(stream)), "moe_probe_read")
+    return float(n)

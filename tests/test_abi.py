@@ -8,11 +8,12 @@ import pytest
 
 from mixture_experts_layer_softmax_amd import lib, synth
 
-HEADER = os.path.join(os.path.dirname(__file__), "..", "include", "moe.h")
+INCLUDE = os.path.join(os.path.dirname(__file__), "..", "include")
 
 
 def declared():
-    text = open(HEADER).read()
+    text = "".join(open(os.path.join(INCLUDE, f)).read() for f in sorted(os.listdir(INCLUDE))
+                   if f.endswith(".h"))
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(moe_\w+)\(", text, re.M)))
 
 
@@ -121,3 +122,14 @@ def test_gemm_and_forward_validation(L):
     assert L.moe_pack_weights(C.byref(pb), V(FAKE), None, V(FAKE), None, None) == lib.MOE_ERR_INVALID_ARGUMENT
     assert L.moe_pack_weights(C.byref(lib.problem(16, 192, 8, 2, 128)), V(FAKE), None, V(FAKE + 4096),
                               None, None) == lib.MOE_ERR_UNSUPPORTED
+
+
+def test_probe_validation(L):
+    V = C.c_void_p
+    assert L.moe_probe_mfma_bf16(0, 1, V(FAKE), None) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_probe_mfma_bf16(1, 0, V(FAKE), None) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_probe_mfma_bf16(1, 1, None, None) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_probe_read(V(FAKE), 0, V(FAKE), None) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_probe_read(V(FAKE), 100, V(FAKE), None) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_probe_read(V(FAKE + 8), 1024, V(FAKE), None) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_probe_read(None, 1024, V(FAKE), None) == lib.MOE_ERR_INVALID_ARGUMENT
