@@ -8,10 +8,11 @@ workload is the prefill-shaped layer (4096 tokens, hidden 4096, 128 experts, top
 1536, bf16, router bias N(0,1)); ``--workload`` selects another one (tiny, decode1, decode8,
 decode64, nvfp4_decode, nvfp4_prefill).  Prints one JSON line.
 
-Timing: W untimed steps, then K steps between two events on the launch stream.  Decode-shaped
-workloads (whose selected weights fit in the 256 MiB Infinity Cache) overwrite a 1 GiB buffer
-before every timed step and time each step with its own event pair, so that weights come from
-HBM; the flush is outside the timed intervals.
+Timing: W untimed steps, then K steps between two events on the launch stream.  Workloads
+whose selected weights are small enough to stay cached between steps (under 1.5 GiB) read a
+1 GiB buffer before every timed step and time each step with its own event pair, so that
+weights come from HBM; the flush is outside the timed intervals (``--flush-mode write``
+overwrites the buffer instead, for comparison).
 
 Besides the step time it measures, with events on the same stream, the average duration of
 the dominant kernel (the gate/up grouped GEMM, launched alone through ``moe_grouped_gemm`` on
@@ -140,6 +141,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="prefill")
     ap.add_argument("--flush", choices=("auto", "on", "off"), default="auto")
+    ap.add_argument("--flush-mode", choices=("read", "write"), default="read",
+                    help="evict caches by reading (default) or by writing a 1 GiB buffer")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probes", action="store_true",
@@ -173,7 +176,17 @@ def main() -> int:
     active = int((counts > 0).sum())
     w_bytes = active * 3.0 * wl.hidden * wl.ffn * bytes_per_weight(wl.wdt)
     flush = args.flush == "on" or (args.flush == "auto" and w_bytes < 1.5 * 2 ** 30)
-    scratch = torch.empty(2 ** 30, dtype=torch.uint8, device="cuda:0") if flush else None
+    scratch = torch.ones(2 ** 30, dtype=torch.uint8, device="cuda:0") if flush else None
+    scratch_word = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+
+    def evict():
+        # Reading 1 GiB of other data displaces the layer's weights from L2 and the 256 MiB
+        # Infinity Cache.  Writing it instead would leave dirty lines whose write-back lands
+        # inside the next timed interval and competes with the weight stream.
+        if args.flush_mode == "read":
+            lib.probe_read(scratch, scratch_word)
+        else:
+            scratch.fill_(1)
 
     def timed(fn, steps):
         """Mean ms per call of fn over `steps` calls on the current stream."""
@@ -188,7 +201,7 @@ def main() -> int:
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(steps)]
         for a, b in evs:
-            scratch.fill_(1)  # evict L2 and the Infinity Cache
+            evict()
             a.record()
             fn()
             b.record()
@@ -250,7 +263,8 @@ def main() -> int:
                config=dict(workload=describe(wl), tokens=wl.tokens, hidden=wl.hidden,
                            experts=wl.experts, top_k=wl.top_k, ffn=wl.ffn, weights=wl.wdt,
                            active_experts=active, max_expert_rows=int(counts.max()),
-                           cache_flushed=bool(flush)),
+                           cache_flushed=bool(flush),
+                           flush_mode=args.flush_mode if flush else None),
                layer_tflops=flops / (ms_per_step * 1e-3) / 1e12,
                layer_mfma_frac=flops / (ms_per_step * 1e-3) / PEAK_BF16_FLOPS,
                layer_hbm_frac=nbytes / (ms_per_step * 1e-3) / PEAK_HBM_BYTES,

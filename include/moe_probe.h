@@ -27,10 +27,11 @@ extern "C" {
  * else MOE_ERR_INVALID_ARGUMENT. */
 moe_status moe_probe_mfma_bf16(int32_t blocks, int32_t iters, float* out, void* stream);
 
-/* HBM read stream: every 16-byte word of buf[0, bytes) is read once by 16-byte loads, four in
- * flight per thread, grid-stride over 8192 blocks of 256 threads.  out: device uint32_t[1],
- * written only for one particular XOR of the data (so the loads cannot be elided).  bytes must
- * be a positive multiple of 16 and buf 16-byte aligned, else MOE_ERR_INVALID_ARGUMENT. */
+/* HBM read stream: every 16-byte word of buf[0, bytes) is read once by 16-byte loads; 16384
+ * blocks of 256 threads take contiguous 32 KiB chunks in turn, eight loads in flight per
+ * thread.  out: device uint32_t[1], written only for one particular XOR of the data (so the
+ * loads cannot be elided).  bytes must be a positive multiple of 16 and buf 16-byte aligned,
+ * else MOE_ERR_INVALID_ARGUMENT. */
 moe_status moe_probe_read(const void* buf, size_t bytes, uint32_t* out, void* stream);
 
 #ifdef __cplusplus

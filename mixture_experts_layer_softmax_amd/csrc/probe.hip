@@ -33,16 +33,25 @@ __global__ __launch_bounds__(256) void mfma_probe_kernel(int iters, float* __res
     if (tid == 0) out[blockIdx.x] = v;
 }
 
+// Each block step reads one contiguous 32 KiB chunk, eight 16-byte loads per thread issued
+// before any is used; the words past the last whole chunk are read grid-stride.
 __global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict__ p, long n16,
                                                          uint32_t* __restrict__ out) {
-    const long stride = long(gridDim.x) * blockDim.x;
-    long i = long(blockIdx.x) * blockDim.x + threadIdx.x;
+    constexpr int U = 8;
+    constexpr long kChunk = 256L * U;
+    const long nch = n16 / kChunk;
     uint32_t acc = 0;
-    for (; i + 3 * stride < n16; i += 4 * stride) {
-        const uint4 v0 = p[i], v1 = p[i + stride], v2 = p[i + 2 * stride], v3 = p[i + 3 * stride];
-        acc ^= v0.x ^ v1.y ^ v2.z ^ v3.w;
+    for (long c = blockIdx.x; c < nch; c += gridDim.x) {
+        const uint4* q = p + c * kChunk + threadIdx.x;
+        uint4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = q[u * 256];
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].w;
     }
-    for (; i < n16; i += stride) acc ^= p[i].x;
+    for (long i = nch * kChunk + long(blockIdx.x) * blockDim.x + threadIdx.x; i < n16;
+         i += long(gridDim.x) * blockDim.x)
+        acc ^= p[i].x;
     if (acc == 0x9e3779b9u) out[0] = acc;
 }
 
@@ -62,7 +71,7 @@ extern "C" moe_status moe_probe_read(const void* buf, size_t bytes, uint32_t* ou
     if (!buf || !out || bytes == 0 || (bytes & 15u) || (reinterpret_cast<uintptr_t>(buf) & 15u) ||
         (reinterpret_cast<uintptr_t>(out) & 3u))
         return MOE_ERR_INVALID_ARGUMENT;
-    hipLaunchKernelGGL(moe::read_probe_kernel, dim3(8192), dim3(256), 0,
+    hipLaunchKernelGGL(moe::read_probe_kernel, dim3(16384), dim3(256), 0,
                        static_cast<hipStream_t>(stream), static_cast<const uint4*>(buf),
                        long(bytes / 16), out);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
