@@ -105,9 +105,9 @@ moe_status check_weights(const moe_problem& p, const moe_expert_weights* w) {
         return MOE_ERR_INVALID_ARGUMENT;
     if (p.w_dtype == MOE_NVFP4) {
         if (!w->w13_scale || !w->w2_scale) return MOE_ERR_INVALID_ARGUMENT;
-        // scale rows are H/16 or F/16 bytes: 2-byte loads need even offsets
-        if ((reinterpret_cast<uintptr_t>(w->w13_scale) & 1u) || (reinterpret_cast<uintptr_t>(w->w2_scale) & 1u))
-            return MOE_ERR_INVALID_ARGUMENT;
+        // the decode kernel reads scales in 2- and 8-byte pieces; like every pointer of the ABI
+        // the scale arrays must be 16-byte aligned
+        if (!aligned(w->w13_scale) || !aligned(w->w2_scale)) return MOE_ERR_INVALID_ARGUMENT;
         if ((reinterpret_cast<uintptr_t>(w->w13_gscale) & 3u) || (reinterpret_cast<uintptr_t>(w->w2_gscale) & 3u))
             return MOE_ERR_INVALID_ARGUMENT;
     }

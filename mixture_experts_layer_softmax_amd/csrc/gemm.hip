@@ -32,15 +32,14 @@ constexpr int BK = 64;  // K elements per LDS stage (8 chunks of 16 bytes in bf1
 
 __device__ __forceinline__ int lds_slot(int row, int ch) { return row * 8 + (ch ^ (row & 7)); }
 
-// E4M3 (FN) byte -> its value in fp32 (integer decode; subnormals included).
+// E4M3 (FN) byte -> its value in fp32 (integer decode; subnormals included).  Both cases are
+// computed and selected, so the decode is straight-line code with no divergent branch.
 __device__ __forceinline__ float e4m3_value(uint32_t c) {
     const uint32_t e = (c >> 3) & 15, m = c & 7;
-    float v;
-    if (e == 0)
-        v = float(m) * 0x1p-9f;
-    else
-        v = __uint_as_float(((e + 120u) << 23) | (m << 20));
-    return (c & 0x80) ? -v : v;
+    const float sub = float(m) * 0x1p-9f;
+    const float nrm = __uint_as_float(((e + 120u) << 23) | (m << 20));
+    const float v = e ? nrm : sub;
+    return __uint_as_float(__float_as_uint(v) | ((c & 0x80u) << 24));
 }
 
 // 8 nibbles (elements 0..7, even element in the low nibble) times their block scale -> 8 bf16.
@@ -656,7 +655,7 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_v4_kernel(GemmArgs g) {
 // and are added in a fixed order (deterministic).
 // ---------------------------------------------------------------------------------------
 
-template <int KIND, int WFMT, int SPLITK>
+template <int KIND, int WFMT, int SPLITK, bool WIN4 = false>
 __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
     constexpr int CG = 4 / SPLITK;              // column groups per block
     constexpr int NB = (KIND == kGateUp) ? 2 : 1;  // weight row sets per column group
@@ -681,7 +680,7 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
     const int rr = min(r0 + n, r1 - 1);
     int src = g.a_rows ? g.a_rows[rr] : rr;
     src = src < 0 ? 0 : (src >= g.a_rows_limit ? g.a_rows_limit - 1 : src);
-    const uint16_t* pa = static_cast<const uint16_t*>(g.a) + size_t(src) * K + (WFMT == kWBF16 ? 8 : 32) * q;
+    const uint16_t* pa = static_cast<const uint16_t*>(g.a) + size_t(src) * K + (WFMT == kWBF16 ? 8 : WIN4 ? 128 : 32) * q;
     const int col = min(cg, ncg - 1) * 16 + n;
     int wrow0, wrow1 = 0;
     if (KIND == kGateUp) {
@@ -727,10 +726,10 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
         }
     }
     const size_t w0 = size_t(e) * Nw + wrow0, w1 = size_t(e) * Nw + wrow1;
-    const uint8_t* pq0 = static_cast<const uint8_t*>(g.w) + w0 * (K / 2) + 16 * q;
-    const uint8_t* pq1 = static_cast<const uint8_t*>(g.w) + w1 * (K / 2) + 16 * q;
-    const uint8_t* ps0 = g.wscale + w0 * (K / 16) + 2 * q;
-    const uint8_t* ps1 = g.wscale + w1 * (K / 16) + 2 * q;
+    const uint8_t* pq0 = static_cast<const uint8_t*>(g.w) + w0 * (K / 2) + (WIN4 ? 64 : 16) * q;
+    const uint8_t* pq1 = static_cast<const uint8_t*>(g.w) + w1 * (K / 2) + (WIN4 ? 64 : 16) * q;
+    const uint8_t* ps0 = g.wscale + w0 * (K / 16) + (WIN4 ? 8 : 2) * q;
+    const uint8_t* ps1 = g.wscale + w1 * (K / 16) + (WIN4 ? 8 : 2) * q;
     auto load = [&](Blk& b, int j) __attribute__((always_inline)) {
         const int k = 128 * j;
         if constexpr (WFMT == kWBF16) {
@@ -792,7 +791,64 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
             }
         }
     };
-    if (live && nblk > 0) {
+    if constexpr (WFMT == kWNVFP4 && WIN4) {
+        // NVFP4, 512-wide windows (nblk % 4 == 0): inside window w lane q owns the 128
+        // contiguous elements 512 w + 128 q .. +127, so its 8 block scales are 8 contiguous
+        // bytes (one 8-byte load per window and row instead of one 2-byte load per block);
+        // 128-wide block jj of the window is that range's jj-th 32 elements, MFMA i of the
+        // block its elements 32 jj + 8 i .. +7 (the same permutation of K on both operands).
+        struct QBlk {
+            uint4 a0, a1, a2, a3, pg, pu;
+        };
+        auto qload = [&](QBlk& b, int j) __attribute__((always_inline)) {
+            const int w = j >> 2, jj = j & 3;
+            const uint16_t* xa = pa + 512 * w + 32 * jj;
+            b.a0 = ld16(xa);
+            b.a1 = ld16(xa + 8);
+            b.a2 = ld16(xa + 16);
+            b.a3 = ld16(xa + 24);
+            b.pg = ld16(pq0 + 256 * w + 16 * jj);
+            if constexpr (KIND == kGateUp) b.pu = ld16(pq1 + 256 * w + 16 * jj);
+        };
+        auto sload = [&](uint2& sg, uint2& su, int w) __attribute__((always_inline)) {
+            sg = *reinterpret_cast<const uint2*>(ps0 + 32 * w);
+            if constexpr (KIND == kGateUp) su = *reinterpret_cast<const uint2*>(ps1 + 32 * w);
+        };
+        auto qmma = [&](f32x4_t& acc, const QBlk& b, const uint4& p, uint2 sc, int jj) __attribute__((always_inline)) {
+            const uint32_t word = (jj < 2) ? sc.x : sc.y;
+            const int sh = (jj & 1) * 16;
+            const float fa = e4m3_value((word >> sh) & 0xffu), fb = e4m3_value((word >> (sh + 8)) & 0xffu);
+            mma(acc, b.a0, dequant8(p.x, fa));
+            mma(acc, b.a1, dequant8(p.y, fa));
+            mma(acc, b.a2, dequant8(p.z, fb));
+            mma(acc, b.a3, dequant8(p.w, fb));
+        };
+        auto qcompute = [&](const QBlk& b, uint2 sg, uint2 su, int jj) __attribute__((always_inline)) {
+            qmma(acc0, b, b.pg, sg, jj);
+            if constexpr (KIND == kGateUp) qmma(acc1, b, b.pu, su, jj);
+        };
+        if (live && nblk > 0) {
+            const int wlast = (jend >> 2) - 1;
+            QBlk x0{}, x1{};
+            uint2 sg0{}, su0{}, sg1{}, su1{};
+            sload(sg0, su0, j0 >> 2);
+            qload(x0, j0);
+            qload(x1, j0 + 1);
+            for (int j = j0; j < jend; j += 4) {  // loads past the end re-read the last block
+                qcompute(x0, sg0, su0, 0);
+                qload(x0, min(j + 2, jend - 1));
+                qcompute(x1, sg0, su0, 1);
+                qload(x1, min(j + 3, jend - 1));
+                sload(sg1, su1, min((j >> 2) + 1, wlast));
+                qcompute(x0, sg0, su0, 2);
+                qload(x0, min(j + 4, jend - 1));
+                qcompute(x1, sg0, su0, 3);
+                qload(x1, min(j + 5, jend - 1));
+                sg0 = sg1;
+                su0 = su1;
+            }
+        }
+    } else if (live && nblk > 0) {
         Blk x0{}, x1{};
         load(x0, j0);
         load(x1, min(j0 + 1, jend - 1));  // past the end: a harmless re-read of the last block
@@ -971,6 +1027,11 @@ hipError_t launch_gemm(const GemmArgs& g, int family, int max_tiles, hipStream_t
         if (g.wfmt == kWBF16) {
             if (up) { if (split == 1) MOE_DEC(kGateUp, kWBF16, 1); else if (split == 2) MOE_DEC(kGateUp, kWBF16, 2); else MOE_DEC(kGateUp, kWBF16, 4); }
             else    { if (split == 1) MOE_DEC(kDown, kWBF16, 1);   else if (split == 2) MOE_DEC(kDown, kWBF16, 2);   else MOE_DEC(kDown, kWBF16, 4); }
+        } else if ((g.K / 128 / split) % 4 == 0) {  // 512-wide scale windows
+#define MOE_DEC4(KD, SK) hipLaunchKernelGGL((gemm_decode_kernel<KD, kWNVFP4, SK, true>), grid, block, 0, s, g)
+            if (up) { if (split == 1) MOE_DEC4(kGateUp, 1); else if (split == 2) MOE_DEC4(kGateUp, 2); else MOE_DEC4(kGateUp, 4); }
+            else    { if (split == 1) MOE_DEC4(kDown, 1);   else if (split == 2) MOE_DEC4(kDown, 2);   else MOE_DEC4(kDown, 4); }
+#undef MOE_DEC4
         } else {
             if (up) { if (split == 1) MOE_DEC(kGateUp, kWNVFP4, 1); else if (split == 2) MOE_DEC(kGateUp, kWNVFP4, 2); else MOE_DEC(kGateUp, kWNVFP4, 4); }
             else    { if (split == 1) MOE_DEC(kDown, kWNVFP4, 1);   else if (split == 2) MOE_DEC(kDown, kWNVFP4, 2);   else MOE_DEC(kDown, kWNVFP4, 4); }

@@ -25,6 +25,8 @@ SMALL = {
     "small_nvfp4": W("small_nvfp4", 384, 512, 16, 4, 256, "bf16", "nvfp4", 12, "normal"),
     "ragged_bf16": W("ragged_bf16", 77, 256, 5, 3, 384, "bf16", "bf16", 13, "normal"),
     "ragged_nvfp4": W("ragged_nvfp4", 77, 192, 5, 3, 320, "bf16", "nvfp4", 14, "normal"),
+    # K = 2048 on both GEMMs: the NVFP4 decode kernel takes its 512-wide scale windows
+    "win4_nvfp4": W("win4_nvfp4", 8, 2048, 16, 2, 2048, "bf16", "nvfp4", 15, "normal"),
     "tiny": synth.WORKLOADS["tiny"],
 }
 
@@ -152,7 +154,8 @@ def _routed(wl, inp):
     return r, expert_of_row
 
 
-@pytest.mark.parametrize("name", ["tiny", "small_bf16", "small_nvfp4", "ragged_bf16", "ragged_nvfp4"])
+@pytest.mark.parametrize("name", ["tiny", "small_bf16", "small_nvfp4", "ragged_bf16", "ragged_nvfp4",
+                                  "win4_nvfp4"])
 @pytest.mark.parametrize("path", ["prefill", "decode"])
 def test_gate_up_matches_oracle(name, path):
     wl = SMALL[name]
@@ -181,7 +184,8 @@ def test_gate_up_matches_oracle(name, path):
     assert torch.equal(hid, hid2)
 
 
-@pytest.mark.parametrize("name", ["tiny", "small_bf16", "small_nvfp4", "ragged_bf16", "ragged_nvfp4"])
+@pytest.mark.parametrize("name", ["tiny", "small_bf16", "small_nvfp4", "ragged_bf16", "ragged_nvfp4",
+                                  "win4_nvfp4"])
 @pytest.mark.parametrize("path", ["prefill", "decode"])
 def test_down_matches_oracle(name, path):
     wl = SMALL[name]
@@ -316,8 +320,8 @@ def _check_forward(wl, inp, layer, tokens=None, path=None):
     return y
 
 
-FWD_CASES = ["tiny", "small_bf16", "small_nvfp4", "ragged_bf16", "ragged_nvfp4", "decode1",
-             "decode8", "nvfp4_decode"]
+FWD_CASES = ["tiny", "small_bf16", "small_nvfp4", "ragged_bf16", "ragged_nvfp4", "win4_nvfp4",
+             "decode1", "decode8", "nvfp4_decode"]
 
 
 @pytest.mark.parametrize("name", FWD_CASES)
