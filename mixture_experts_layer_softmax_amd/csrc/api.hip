@@ -312,11 +312,20 @@ moe_status moe_forward(const moe_problem* p, const void* x, const void* w_router
     int* tcount = at<int>(workspace, L.tcount);
     Tile* tiles = at<Tile>(workspace, L.tiles1);
 
-    MOE_TRY(run_route(*p, x, w_router, router_bias, ids, tw, L, workspace, s));
     DispatchArgs d{ids, p->num_tokens, p->top_k, p->num_experts, at<int32_t>(workspace, L.hist),
                    at<int32_t>(workspace, L.base), counts, off, st, ip, tiles, tcount, L.bm,
                    nullptr, nullptr, 0, L.max_tiles};
-    MOE_TRY(dev(launch_dispatch(d, s)));
+    // up to 8 tokens (one per wavefront of the dispatch block): logits, then selection and
+    // dispatch in one single-block launch; larger batches select with one wavefront per token
+    if (p->num_tokens <= kMaxExperts / kWave) {
+        RouteArgs r{x, w_router, router_bias, at<float>(workspace, L.logits), p->num_tokens, p->hidden,
+                    p->num_experts, p->act_dtype == MOE_BF16};
+        MOE_TRY(dev(launch_router_logits(r, s)));
+        MOE_TRY(dev(launch_select_dispatch_small(r.logits, p->renormalize, ids, tw, d, s)));
+    } else {
+        MOE_TRY(run_route(*p, x, w_router, router_bias, ids, tw, L, workspace, s));
+        MOE_TRY(dev(launch_dispatch(d, s)));
+    }
     void* hid = at<void>(workspace, L.hid);
     void* yperm = at<void>(workspace, L.yperm);
     GemmArgs g1 = gemm_args(*p, kGateUp, x, st, tiles, tcount, *w, hid);

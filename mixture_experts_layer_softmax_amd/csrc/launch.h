@@ -59,6 +59,10 @@ hipError_t launch_router_logits(const RouteArgs& a, hipStream_t s);
 hipError_t launch_topk(const float* logits, int T, int E, int k, int renorm, int32_t* ids,
                        float* w, hipStream_t s);
 hipError_t launch_dispatch(const DispatchArgs& d, hipStream_t s);
+// T <= kChunkTokens: top-k of the logits (ids/weights into tw_ids/tw) and the dispatch of
+// d in one single-block launch (d.ids, d.hist and d.base are not used).
+hipError_t launch_select_dispatch_small(const float* logits, int renorm, int32_t* tw_ids, float* tw,
+                                        const DispatchArgs& d, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int n, int value, hipStream_t s);
 hipError_t launch_tiles_from_offsets(const int32_t* offsets, int E, int A, int bm, Tile* tiles,
                                      int* tile_count, int cap, hipStream_t s);

@@ -11,6 +11,7 @@
 // chunk, i.e. one block, which is the pages' decode case.
 #include "device.h"
 #include "launch.h"
+#include "select.h"
 
 namespace moe {
 
@@ -28,25 +29,6 @@ __global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ i
         atomicAdd(&cnt[clamp_expert(ids[a], E)], 1);
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += blockDim.x) hist[size_t(c) * E + e] = cnt[e];
-}
-
-// Write the tile list of one grouped GEMM with row-tile height bm from per-expert counts
-// (thread e handles expert e; `start` = exclusive row offset of expert e).
-// At most `cap` tiles are written (a bound that valid counts never reach).
-__device__ void emit_tiles(int e, int E, int count, int start, int bm, Tile* tiles,
-                           int* tile_count, int cap) {
-    const int nt = (e < E) ? (count + bm - 1) / bm : 0;
-    int total;
-    const int first = block_exclusive_scan<kMaxExperts>(nt, &total);
-    for (int i = 0; i < nt && first + i < cap; ++i) {
-        Tile t;
-        t.expert = e;
-        t.row0 = start + i * bm;
-        t.row1 = min(start + count, start + (i + 1) * bm);
-        t.pad = 0;
-        tiles[first + i] = t;
-    }
-    if (threadIdx.x == 0) *tile_count = min(total, cap);
 }
 
 // One block of kMaxExperts threads: counts, offsets, per-chunk bases, GEMM tile lists.
@@ -179,6 +161,93 @@ hipError_t launch_fill_i32(int32_t* p, int n, int value, hipStream_t s) {
     if (n <= 0) return hipSuccess;
     hipLaunchKernelGGL(fill_i32_kernel, dim3((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024), dim3(256),
                        0, s, p, n, value);
+    return hipGetLastError();
+}
+
+// Small decode batches (any T <= 64; used for T <= 8, one token per wavefront): top-k
+// selection and the whole dispatch (histogram, scan, tile lists, stable scatter) in one block
+// of kMaxExperts threads, so a decode step spends one launch here instead of four.  Same results as topk_kernel +
+// hist/scan/scatter: ids of a token in selection order, rows of an expert in (t, j) order.
+template <int EPL>
+__global__ __launch_bounds__(kMaxExperts) void select_dispatch_small_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int renorm, int32_t* __restrict__ ids,
+    float* __restrict__ tw, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_token, int32_t* __restrict__ inv_perm, Tile* tiles1,
+    int* tile_count1, int bm1, Tile* tiles2, int* tile_count2, int bm2, int cap) {
+    constexpr int NW = kMaxExperts / kWave;
+    __shared__ int sids[kChunkTokens * kMaxTopK];
+    __shared__ int cnt[kMaxExperts];
+    __shared__ int wc[NW][kMaxExperts];
+    const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+    for (int t = w; t < T; t += NW)
+        topk_token<EPL>(logits + size_t(t) * E, E, k, renorm, ids + size_t(t) * k, tw + size_t(t) * k,
+                        sids + t * k);
+    if (tid < E) cnt[tid] = 0;
+    __syncthreads();
+    const int A = T * k;
+    for (int a = tid; a < A; a += kMaxExperts) atomicAdd(&cnt[clamp_expert(sids[a], E)], 1);
+    __syncthreads();
+    const int c = tid < E ? cnt[tid] : 0;
+    int total;
+    const int start = block_exclusive_scan<kMaxExperts>(c, &total);
+    if (tid < E) {
+        if (counts) counts[tid] = c;
+        offsets[tid] = start;
+    }
+    if (tid == 0) offsets[E] = total;
+    if (tiles1) emit_tiles(tid, E, c, start, bm1, tiles1, tile_count1, cap);
+    if (tiles2) emit_tiles(tid, E, c, start, bm2, tiles2, tile_count2, cap);
+    __syncthreads();
+    if (tid < E) cnt[tid] = start;  // next free row of each expert
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
+    for (int r0 = 0; r0 < A; r0 += kMaxExperts) {
+        for (int i = tid; i < NW * kMaxExperts; i += kMaxExperts) (&wc[0][0])[i] = 0;
+        __syncthreads();
+        const int a = r0 + tid;
+        const bool valid = a < A;
+        const int id = valid ? clamp_expert(sids[a], E) : 0;
+        uint64_t peers = __ballot(valid);
+        for (int b = 0; b < nbits; ++b) {
+            const bool bit = (id >> b) & 1;
+            const uint64_t m = __ballot(valid && bit);
+            peers &= bit ? m : ~m;
+        }
+        const int rank = __popcll(peers & lanemask_lt());
+        if (valid && rank == 0) wc[w][id] = __popcll(peers);
+        __syncthreads();
+        if (valid) {
+            int prefix = 0;
+            for (int ww = 0; ww < w; ++ww) prefix += wc[ww][id];
+            const int pos = cnt[id] + prefix + rank;
+            sorted_token[pos] = a / k;
+            inv_perm[a] = pos;
+        }
+        __syncthreads();
+        if (tid < E) {
+            int add = 0;
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww) add += wc[ww][tid];
+            cnt[tid] += add;
+        }
+        __syncthreads();
+    }
+    (void)lane;
+}
+
+hipError_t launch_select_dispatch_small(const float* logits, int renorm, int32_t* tw_ids,
+                                        float* tw, const DispatchArgs& d, hipStream_t s) {
+    const int epl = (d.E + kWave - 1) / kWave;
+#define MOE_SDS(N)                                                                                  \
+    hipLaunchKernelGGL((select_dispatch_small_kernel<N>), dim3(1), dim3(kMaxExperts), 0, s, logits, \
+                       d.T, d.E, d.k, renorm, tw_ids, tw, d.counts, d.offsets, d.sorted_token,      \
+                       d.inv_perm, d.tiles1, d.tile_count1, d.bm1, d.tiles2, d.tile_count2, d.bm2,  \
+                       d.tile_cap)
+    if (epl <= 1) MOE_SDS(1);
+    else if (epl <= 2) MOE_SDS(2);
+    else if (epl <= 4) MOE_SDS(4);
+    else MOE_SDS(8);
+#undef MOE_SDS
     return hipGetLastError();
 }
 

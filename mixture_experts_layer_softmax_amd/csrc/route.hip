@@ -12,6 +12,7 @@
 // 16 contiguous bytes per bf16 chunk, so a wavefront reads 1 KiB contiguous per row and step.
 #include "device.h"
 #include "launch.h"
+#include "select.h"
 
 namespace moe {
 
@@ -51,6 +52,8 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const void* __restri
         for (int j = 0; j < TN; ++j)
             wrr[j] = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(wr) +
                                                     size_t(min(e0 + j, E - 1)) * H);
+        // small blocks (decode batches): unroll so that several chunks' loads are in flight
+#pragma unroll(NO <= 2 ? 8 : 1)
         for (int c = lane; c < nchunks; c += kWave) {
             uint4 xv[TM], wv[TN];
 #pragma unroll
@@ -142,94 +145,15 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const void* __restri
     }
 }
 
-// One wavefront per token: k rounds of a wave-wide argmax over (logit desc, expert asc),
-// then the softmax weights in fp32.  Always yields k distinct valid experts (memory safe even
-// for non-finite logits).
+// One wavefront per token.
 template <int EPL>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E,
                                                    int k, int renorm, int32_t* __restrict__ ids,
                                                    float* __restrict__ w) {
-    const int lane = lane_id();
     const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
     if (t >= T) return;
-    constexpr int NONE = 0x7fffffff;
-    float v[EPL];
-    bool live[EPL];
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-        const int e = lane + kWave * i;
-        live[i] = e < E;
-        v[i] = live[i] ? logits[size_t(t) * E + e] : 0.0f;
-    }
-    float selv[kMaxTopK];
-    int sele[kMaxTopK];
-#pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) {
-        selv[j] = 0.0f;
-        sele[j] = 0;
-    }
-    for (int j = 0; j < k; ++j) {
-        float bv = 0.0f;
-        int be = NONE;
-#pragma unroll
-        for (int i = 0; i < EPL; ++i)
-            if (live[i] && (be == NONE || v[i] > bv)) {  // ascending e within a lane
-                bv = v[i];
-                be = lane + kWave * i;
-            }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const float ov = __shfl_xor(bv, off);
-            const int oe = __shfl_xor(be, off);
-            const bool take = oe != NONE && (be == NONE || ov > bv || (ov == bv && oe < be));
-            if (take) {
-                bv = ov;
-                be = oe;
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < EPL; ++i)
-            if (be == lane + kWave * i) live[i] = false;
-#pragma unroll
-        for (int jj = 0; jj < kMaxTopK; ++jj)
-            if (jj == j) {
-                selv[jj] = bv;
-                sele[jj] = be;
-            }
-    }
-    // weights: exp(l_j - l_0) / z
-    float z = 0.0f;
-    if (renorm) {
-        for (int j = 0; j < k; ++j) {
-            float s = 0.0f;
-#pragma unroll
-            for (int jj = 0; jj < kMaxTopK; ++jj)
-                if (jj == j) s = selv[jj];
-            z += expf(s - selv[0]);
-        }
-    } else {
-        float part = 0.0f;
-#pragma unroll
-        for (int i = 0; i < EPL; ++i) {
-            const int e = lane + kWave * i;
-            if (e < E) part += expf(logits[size_t(t) * E + e] - selv[0]);
-        }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
-        z = part;
-    }
-    if (lane < k) {
-        float s = 0.0f;
-        int e = 0;
-#pragma unroll
-        for (int jj = 0; jj < kMaxTopK; ++jj)
-            if (jj == lane) {
-                s = selv[jj];
-                e = sele[jj];
-            }
-        ids[size_t(t) * k + lane] = e;
-        w[size_t(t) * k + lane] = expf(s - selv[0]) / z;
-    }
+    topk_token<EPL>(logits + size_t(t) * E, E, k, renorm, ids + size_t(t) * k, w + size_t(t) * k,
+                    nullptr);
 }
 
 // ---------------------------------------------------------------------------------------

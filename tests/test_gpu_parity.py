@@ -426,6 +426,16 @@ def test_k_equals_e(E, k):
     _check_forward(wl, inp, MoELayer.from_workload(wl, inp))
 
 
+@pytest.mark.parametrize("T,E,k", [(1, 8, 8), (8, 512, 16), (3, 5, 2), (8, 128, 8)])
+def test_small_batch_single_launch_dispatch(T, E, k):
+    """Batches of up to 8 tokens select and dispatch in one single-block launch; routing
+    outputs stay bit-exact and the layer output within tolerance."""
+    wl = W("smallsel", T, 256, E, k, 128, "bf16", "bf16", 71 + E + T, "normal")
+    inp = synth.generate(wl)
+    note("small-batch dispatch T=%d E=%d k=%d" % (T, E, k))
+    _check_forward(wl, inp, MoELayer.from_workload(wl, inp))
+
+
 def test_full_softmax_weights_option():
     wl = W("nr", 50, 256, 8, 3, 128, "bf16", "bf16", 51, "normal", renormalize=False)
     inp = synth.generate(wl)
