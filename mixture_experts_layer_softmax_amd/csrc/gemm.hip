@@ -9,18 +9,22 @@
 // Work is a list of (expert, row range) tiles written on the device by dispatch, so the host
 // never reads the routing; blocks past the list's end exit at once.
 //
-// bf16 path: v_mfma_f32_16x16x32_bf16, fp32 accumulate.  A block stages 64-wide K slices of
-// its activation rows (gathered through the dispatch map, no permuted copy of x) and of its
-// weight rows in LDS, double buffered, with 16-byte chunks XOR-swizzled by row so that the
-// MFMA operand reads are free of bank conflicts.  Gate and up rows that feed the same hid
-// column sit in the same wavefront, so SwiGLU is applied to accumulators in registers.
+// Kernels (all v_mfma_f32_16x16x32_bf16 with fp32 accumulation, except the fp32 one):
+//   gemm_prefill_bf16_kernel   many rows per expert, bf16 weights in the packed stage layout
+//                              of moe.h: 256 x 256 tiles, operands DMA'd into an LDS ring
+//   gemm_prefill_nvfp4_kernel  the same for NVFP4 weights: raw nibbles and scales DMA'd and
+//                              decoded to bf16 in LDS by the block
+//   gemm_decode_kernel         few rows per expert: weights stream straight into MFMA
+//                              operand registers (bf16 packed, or NVFP4 row-major)
+//   gemm_bf16_kernel           NVFP4 shapes the two above do not tile (F % 128 or K % 128)
+//   gemm_f32_kernel            fp32 layers (SIMT)
+// Gate and up rows that feed the same hid column sit in the same wavefront, so SwiGLU is
+// applied to accumulators in registers.  Activation rows are gathered through the dispatch
+// map (no permuted copy of x).
 //
 // NVFP4 weights (E2M1 nibbles, E4M3 scale per 16 along K, fp32 per-expert scale) are decoded
-// on the way into LDS: e2m1 * e4m3 has at most 6 significant bits, so it is exact in bf16 and
-// the MFMA sees the exact weight; the per-expert scale multiplies the fp32 accumulator.
-#include <tuple>
-#include <type_traits>
-
+// before the MFMA: e2m1 * e4m3 has at most 6 significant bits, so it is exact in bf16 and the
+// MFMA sees the exact weight; the per-expert scale multiplies the fp32 accumulator.
 #include "device.h"
 #include "launch.h"
 
@@ -275,6 +279,16 @@ __device__ __forceinline__ void dma16(const void* src, const void* lds_base) {
                  : "memory");
 }
 
+// 4 bytes per lane from global memory straight into LDS: lane l writes lds_base + 4*l.
+__device__ __forceinline__ void dma4(const void* src, const void* lds_base) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+        static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_base)));
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+                 :
+                 : "v"(src), "s"(m0)
+                 : "memory");
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------------------
@@ -439,24 +453,32 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_bf16_kernel(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Prefill kernel v4 (bf16 and NVFP4 weights): 256 x 256 block tile, 4 wavefronts (2 x 2) of
-// 128 x 128 (256 fp32 accumulators per lane in AGPRs), K in 32-wide stages.
+// Prefill kernel, NVFP4 weights: the bf16 kernel's 256 x 256 tile, four 128 x 128
+// wavefronts and activation DMA ring; the weights are DMA'd raw (16 nibble bytes and one
+// 4-byte scale word per weight row and stage, straight from the row-major NVFP4 arrays) and
+// decoded by the block into a bf16 LDS slot: thread t decodes weight row t (e2m1 * e4m3 is
+// exact in bf16) after issuing the MFMAs of the current stage, so the decode overlaps the
+// matrix core.  The per-expert fp32 scale multiplies the accumulators.
 //
-// Operands are staged through registers: plain 16-byte global loads run three stages ahead of
-// the MFMAs, and each stage is written to one of two LDS slots after the MFMAs of the previous
-// stage.  (On gfx950 an LDS read waits for the same wavefront's outstanding global->LDS DMA
-// loads, so a wavefront that both DMAs and reads LDS cannot keep DMA in flight across its
-// reads; ordinary loads into registers do not hold LDS reads back.)  NVFP4 weights are staged
-// packed (16 bytes + 2 scale bytes per row and stage) and decoded to exact bf16 on their way
-// into LDS.  Rows are 64 bytes in LDS, chunk c of row r at slot c ^ ((r >> 1) & 3).
+// Iteration i: activation stage i+1 and raw weight stage i+2 have landed (issued three
+// iterations earlier); read the fragments of stage i+1 (activations from ring slot (i+1)%4,
+// decoded weights from bf16 slot (i+1)%2); DMA activation stage i+4 (slot i%4) and raw weight
+// stage i+5 (raw slot (i+1)%4); run the MFMAs of stage i; decode raw stage i+2 (raw slot
+// (i+2)%4) into bf16 slot i%2.  Every wavefront issues six DMA instructions per iteration
+// (four activation, one nibble, one scale), so "landed" is a fixed load count.  Thread t
+// decodes the raw row its own lane DMA'd, so its wait covers its data; the barrier publishes
+// the decoded slot to the other wavefronts.
 // ---------------------------------------------------------------------------------------
 
-template <int KIND, int WFMT>
-__global__ __launch_bounds__(256, 1) void gemm_prefill_v4_kernel(GemmArgs g) {
+template <int KIND>
+__global__ __launch_bounds__(256, 1) void gemm_prefill_nvfp4_kernel(GemmArgs g) {
     constexpr int BM = 256, BN = 256, BKS = 32;
+    constexpr int A_DMA = BM / 16 / 4;
     constexpr int HALF = (KIND == kGateUp) ? BN / 2 : BN;
-    __shared__ uint4 sA[2][BM * 4];
-    __shared__ uint4 sB[2][BN * 4];
+    __shared__ uint4 sA0[BM * 4], sA1[BM * 4], sA2[BM * 4], sA3[BM * 4];
+    __shared__ uint4 sN0[BN], sN1[BN], sN2[BN], sN3[BN];     // raw nibbles of weight row r
+    __shared__ uint32_t sS0[BN], sS1[BN], sS2[BN], sS3[BN];  // raw scale word of weight row r
+    __shared__ uint4 sB0[BN * 4], sB1[BN * 4];               // decoded bf16 stages
 
     const int ncols = (KIND == kGateUp) ? g.F / HALF : (g.N + BN - 1) / BN;
     const int items = *g.tile_count * ncols;
@@ -474,143 +496,122 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_v4_kernel(GemmArgs g) {
     const int K = g.K;
     const int Nw = (KIND == kGateUp) ? 2 * g.F : g.N;
 
-    auto wrow_of = [&](int row) -> int {
-        if (KIND == kGateUp) {  // per wavefront column: 64 gate rows, then the matching up rows
-            const int q = row & 127;
-            const int f = nt * HALF + (row >> 7) * 64 + (q & 63);
-            return q < 64 ? f : g.F + f;
-        }
-        return min(nt * BN + row, g.N - 1);
-    };
-
-    // A: thread loads rows (tid >> 2) + 64 i, chunk tid & 3 (i = 0..3)
-    auto a_ptr = [&](int i) -> const uint16_t* {
-        const int row = (tid >> 2) + 64 * i;
+    const char* pa[A_DMA];
+#pragma unroll
+    for (int i = 0; i < A_DMA; ++i) {
+        const int row = (i * 4 + wave) * 16 + (lane >> 2);
+        const int ch = (lane & 3) ^ ((row >> 1) & 3);
         const int rr = min(r0 + row, r1 - 1);
         int src = g.a_rows ? g.a_rows[rr] : rr;
         src = src < 0 ? 0 : (src >= g.a_rows_limit ? g.a_rows_limit - 1 : src);
-        return static_cast<const uint16_t*>(g.a) + size_t(src) * K + (tid & 3) * 8;
-    };
-    const uint16_t* const pa0 = a_ptr(0);
-    const uint16_t* const pa1 = a_ptr(1);
-    const uint16_t* const pa2 = a_ptr(2);
-    const uint16_t* const pa3 = a_ptr(3);
-    // B bf16: the same map as A; B NVFP4: thread tid owns weight row tid (16 packed bytes and
-    // 2 scale bytes per stage)
-    auto b_ptr = [&](int i) -> const uint16_t* {
-        return static_cast<const uint16_t*>(g.w) + (size_t(e) * Nw + wrow_of((tid >> 2) + 64 * i)) * K + (tid & 3) * 8;
-    };
-    const uint16_t* pb0 = nullptr;
-    const uint16_t* pb1 = nullptr;
-    const uint16_t* pb2 = nullptr;
-    const uint16_t* pb3 = nullptr;
-    const uint8_t* pq = nullptr;
-    const uint8_t* ps = nullptr;
-    if constexpr (WFMT == kWBF16) {
-        pb0 = b_ptr(0);
-        pb1 = b_ptr(1);
-        pb2 = b_ptr(2);
-        pb3 = b_ptr(3);
-    } else {
-        const size_t wr_ = size_t(e) * Nw + wrow_of(tid);
-        pq = static_cast<const uint8_t*>(g.w) + wr_ * (K / 2);
-        ps = g.wscale + wr_ * (K / 16);
+        pa[i] = static_cast<const char*>(g.a) + (size_t(src) * K + ch * 8) * 2;
     }
+    // raw weights: thread t moves (and later decodes) weight row t of the tile; for gate/up,
+    // per wavefront column 64 gate rows then the matching up rows, as in the other kernels
+    int wrow;
+    if (KIND == kGateUp) {
+        const int q = tid & 127;
+        const int f = nt * HALF + (tid >> 7) * 64 + (q & 63);
+        wrow = q < 64 ? f : g.F + f;
+    } else {
+        wrow = min(nt * BN + tid, g.N - 1);
+    }
+    const size_t wrow_g = size_t(e) * Nw + wrow;
+    const char* const pq = static_cast<const char*>(g.w) + wrow_g * (K / 2);
+    const char* const ps = reinterpret_cast<const char*>(g.wscale) + wrow_g * (K / 16);
 
-    // three register stages with named fields (no arrays) so that they stay in VGPRs
-    struct Stage {
-        uint4 a0, a1, a2, a3, b0, b1, b2, b3;
-        uint32_t sc;
-    };
-    Stage st0{}, st1{}, st2{};
-    auto ld16 = [](const void* p) __attribute__((always_inline)) { return *reinterpret_cast<const uint4*>(p); };
-    auto gload = [&](Stage& r, int k0) __attribute__((always_inline)) {
-        r.a0 = ld16(pa0 + k0);
-        r.a1 = ld16(pa1 + k0);
-        r.a2 = ld16(pa2 + k0);
-        r.a3 = ld16(pa3 + k0);
-        if constexpr (WFMT == kWBF16) {
-            r.b0 = ld16(pb0 + k0);
-            r.b1 = ld16(pb1 + k0);
-            r.b2 = ld16(pb2 + k0);
-            r.b3 = ld16(pb3 + k0);
-        } else {
-            r.b0 = ld16(pq + k0 / 2);
-            r.sc = *reinterpret_cast<const uint16_t*>(ps + k0 / 16);
-        }
-    };
-    const int arow = tid >> 2, ach = tid & 3;
-    auto swrite = [&](const Stage& r, int slot) __attribute__((always_inline)) {
-        sA[slot][lds_slot32(arow, ach)] = r.a0;
-        sA[slot][lds_slot32(arow + 64, ach)] = r.a1;
-        sA[slot][lds_slot32(arow + 128, ach)] = r.a2;
-        sA[slot][lds_slot32(arow + 192, ach)] = r.a3;
-        if constexpr (WFMT == kWBF16) {
-            sB[slot][lds_slot32(arow, ach)] = r.b0;
-            sB[slot][lds_slot32(arow + 64, ach)] = r.b1;
-            sB[slot][lds_slot32(arow + 128, ach)] = r.b2;
-            sB[slot][lds_slot32(arow + 192, ach)] = r.b3;
-        } else {
-            const float s0 = e4m3_value(r.sc & 0xffu);
-            const float s1 = e4m3_value((r.sc >> 8) & 0xffu);
-            sB[slot][lds_slot32(tid, 0)] = dequant8(r.b0.x, s0);
-            sB[slot][lds_slot32(tid, 1)] = dequant8(r.b0.y, s0);
-            sB[slot][lds_slot32(tid, 2)] = dequant8(r.b0.z, s1);
-            sB[slot][lds_slot32(tid, 3)] = dequant8(r.b0.w, s1);
-        }
-    };
+#define MOE_ISSUE_A(SA, K0)                                                                     \
+    do {                                                                                        \
+        const int k0_ = (K0);                                                                   \
+        _Pragma("unroll") for (int i = 0; i < A_DMA; ++i)                                       \
+            dma16(pa[i] + k0_ * 2, &SA[(i * 4 + wave) * 64]);                                   \
+    } while (0)
+    // nibbles of stage k0/32, and the scale word holding its two scales (stages 2m, 2m+1)
+#define MOE_ISSUE_W(SN, SS, K0)                                                                 \
+    do {                                                                                        \
+        const int k0_ = (K0);                                                                   \
+        dma16(pq + k0_ / 2, &SN[wave * 64]);                                                    \
+        dma4(ps + ((k0_ >> 4) & ~3), &SS[wave * 64]);                                           \
+    } while (0)
+#define MOE_DECODE(SN, SS, SB, K0)                                                              \
+    do {                                                                                        \
+        const uint4 nib_ = SN[tid];                                                             \
+        const uint32_t sw_ = SS[tid] >> ((((K0) >> 5) & 1) * 16);                               \
+        const float s0_ = e4m3_value(sw_ & 0xffu), s1_ = e4m3_value((sw_ >> 8) & 0xffu);          \
+        SB[lds_slot32(tid, 0)] = dequant8(nib_.x, s0_);                                         \
+        SB[lds_slot32(tid, 1)] = dequant8(nib_.y, s0_);                                         \
+        SB[lds_slot32(tid, 2)] = dequant8(nib_.z, s1_);                                         \
+        SB[lds_slot32(tid, 3)] = dequant8(nib_.w, s1_);                                         \
+    } while (0)
+#define MOE_READ(SA, SB, AF, BF)                                                                \
+    do {                                                                                        \
+        const int ch_ = lane >> 4;                                                              \
+        _Pragma("unroll") for (int ni = 0; ni < 8; ++ni) BF[ni] =                               \
+            __builtin_bit_cast(bf16x8_t, SB[lds_slot32(wc * 128 + ni * 16 + (lane & 15), ch_)]); \
+        _Pragma("unroll") for (int mi = 0; mi < 8; ++mi) AF[mi] =                               \
+            __builtin_bit_cast(bf16x8_t, SA[lds_slot32((mi * 2 + wr) * 16 + (lane & 15), ch_)]); \
+    } while (0)
+#define MOE_MFMA(AF, BF)                                                                        \
+    do {                                                                                        \
+        _Pragma("unroll") for (int mi = 0; mi < 8; ++mi) {                                      \
+            if (mi * 2 + wr < nsub) {                                                           \
+                _Pragma("unroll") for (int ni = 0; ni < 8; ++ni) acc[mi][ni] =                  \
+                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(AF[mi], BF[ni], acc[mi][ni], 0, 0, 0); \
+            }                                                                                   \
+        }                                                                                       \
+    } while (0)
 
     f32x4_t acc[8][8];
 #pragma unroll
     for (int mi = 0; mi < 8; ++mi)
 #pragma unroll
         for (int ni = 0; ni < 8; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    bf16x8_t a0[8], b0[8], a1[8], b1[8];
 
-    auto step = [&](int slot) __attribute__((always_inline)) {
-        const int ch = lane >> 4;
-        bf16x8_t bf[8];
-#pragma unroll
-        for (int ni = 0; ni < 8; ++ni)
-            bf[ni] = __builtin_bit_cast(bf16x8_t, sB[slot][lds_slot32(wc * 128 + ni * 16 + (lane & 15), ch)]);
-#pragma unroll
-        for (int mi = 0; mi < 8; ++mi) {
-            if (mi * 2 + wr < nsub) {
-                const bf16x8_t af =
-                    __builtin_bit_cast(bf16x8_t, sA[slot][lds_slot32((mi * 2 + wr) * 16 + (lane & 15), ch)]);
-#pragma unroll
-                for (int ni = 0; ni < 8; ++ni)
-                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[ni], acc[mi][ni], 0, 0, 0);
-            }
-        }
-    };
-
-    // iteration s: barrier; MFMAs of stage s from slot s%2 (its fragments read first); loads of
-    // stage s+3 into register set s%3; then stage s+1 (register set (s+1)%3) into slot (s+1)%2.
     const int nk = K / BKS;
     const int last = (nk - 1) * BKS;
-    gload(st0, 0);
-    gload(st1, min(BKS, last));
-    gload(st2, min(2 * BKS, last));
-    swrite(st0, 0);
-    for (int s = 0;; s += 6) {
-#define MOE_V4_ITER(S, RS, RN, SLOT)                                             \
-        __builtin_amdgcn_s_waitcnt(vm_wait_lgkm0(63));                          \
-        block_barrier();                                                        \
-        step(SLOT);                                                             \
-        gload(st##RS, min((s + S + 3) * BKS, last));                            \
-        if (s + S + 1 >= nk) break;                                             \
-        swrite(st##RN, (SLOT) ^ 1);
-        MOE_V4_ITER(0, 0, 1, 0)
-        MOE_V4_ITER(1, 1, 2, 1)
-        MOE_V4_ITER(2, 2, 0, 0)
-        MOE_V4_ITER(3, 0, 1, 1)
-        MOE_V4_ITER(4, 1, 2, 0)
-        MOE_V4_ITER(5, 2, 0, 1)
-#undef MOE_V4_ITER
+    // prologue: raw stages 0 and 1, activation stage 0; decode both; then activation stages
+    // 1..3 and raw stages 2..4 in the steady-state issue order
+    MOE_ISSUE_W(sN0, sS0, 0);
+    MOE_ISSUE_W(sN1, sS1, min(1 * BKS, last));
+    MOE_ISSUE_A(sA0, 0);
+    wait_vm_lgkm0<0>();
+    block_barrier();
+    MOE_DECODE(sN0, sS0, sB0, 0);
+    MOE_DECODE(sN1, sS1, sB1, min(1 * BKS, last));
+    wait_vm_lgkm0<0>();
+    block_barrier();
+    MOE_READ(sA0, sB0, a0, b0);
+    MOE_ISSUE_A(sA1, min(1 * BKS, last));
+    MOE_ISSUE_W(sN2, sS2, min(2 * BKS, last));
+    MOE_ISSUE_A(sA2, min(2 * BKS, last));
+    MOE_ISSUE_W(sN3, sS3, min(3 * BKS, last));
+    MOE_ISSUE_A(sA3, min(3 * BKS, last));
+    MOE_ISSUE_W(sN0, sS0, min(4 * BKS, last));
+    for (int s = 0;; s += 4) {
+#define MOE_IT(S, FA, FB, GA, GB, SAr, SBr, SAw, SNw, SSw, SNd, SSd, SBd)      \
+        wait_vm_lgkm0<12>();                                                 \
+        block_barrier();                                                     \
+        MOE_READ(SAr, SBr, GA, GB);                                          \
+        MOE_ISSUE_A(SAw, min((s + S + 4) * BKS, last));                      \
+        MOE_ISSUE_W(SNw, SSw, min((s + S + 5) * BKS, last));                 \
+        MOE_MFMA(FA, FB);                                                    \
+        if (s + S + 1 >= nk) break;                                          \
+        MOE_DECODE(SNd, SSd, SBd, min((s + S + 2) * BKS, last));
+        MOE_IT(0, a0, b0, a1, b1, sA1, sB1, sA0, sN1, sS1, sN2, sS2, sB0)
+        MOE_IT(1, a1, b1, a0, b0, sA2, sB0, sA1, sN2, sS2, sN3, sS3, sB1)
+        MOE_IT(2, a0, b0, a1, b1, sA3, sB1, sA2, sN3, sS3, sN0, sS0, sB0)
+        MOE_IT(3, a1, b1, a0, b0, sA0, sB0, sA3, sN0, sS0, sN1, sS1, sB1)
+#undef MOE_IT
     }
-    __builtin_amdgcn_s_waitcnt(vm_wait_lgkm0(0));  // drain the clamped tail loads
+    wait_vm_lgkm0<0>();
+#undef MOE_ISSUE_A
+#undef MOE_ISSUE_W
+#undef MOE_DECODE
+#undef MOE_READ
+#undef MOE_MFMA
 
-    const float gs = (WFMT == kWNVFP4 && g.gscale) ? g.gscale[e] : 1.0f;
+    const float gs = g.gscale ? g.gscale[e] : 1.0f;
     uint16_t* out = static_cast<uint16_t*>(g.out);
 #pragma unroll
     for (int mi = 0; mi < 8; ++mi) {
@@ -1011,9 +1012,9 @@ hipError_t launch_gemm(const GemmArgs& g, int family, int max_tiles, hipStream_t
     } else if (family == kFamPrefill && g.F % 128 == 0) {
         const dim3 grid = prefill_grid(g, max_tiles, 256);
         if (up)
-            hipLaunchKernelGGL((gemm_prefill_v4_kernel<kGateUp, kWNVFP4>), grid, dim3(256), 0, s, g);
+            hipLaunchKernelGGL((gemm_prefill_nvfp4_kernel<kGateUp>), grid, dim3(256), 0, s, g);
         else
-            hipLaunchKernelGGL((gemm_prefill_v4_kernel<kDown, kWNVFP4>), grid, dim3(256), 0, s, g);
+            hipLaunchKernelGGL((gemm_prefill_nvfp4_kernel<kDown>), grid, dim3(256), 0, s, g);
     } else if (family == kFamPrefill) {
         launch_mfma<PF_BM, PF_BN, PF_WM, PF_WN>(g, max_tiles, s);
     } else if (g.K % 128 == 0) {
