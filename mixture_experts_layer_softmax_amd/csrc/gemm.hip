@@ -241,18 +241,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Prefill kernel, bf16 weights: 256 x 128 block tile, 4 wavefronts (2 x 2) of 128 x 64,
-// K in 64-wide stages through a 3-slot LDS ring filled by direct global->LDS loads
-// (global_load_lds_dwordx4: each wavefront instruction moves 8 rows x 128 bytes straight into
-// LDS without passing through registers), so two stages are in flight while the third is
-// consumed.  The XOR swizzle is applied on the global side: lane l of an instruction lands at
-// LDS chunk l, so it fetches the source chunk that belongs there.  Each slot is its own LDS
-// object so that the compiler can tell the slots apart and does not wait for in-flight loads
-// before reading the current one; waits on the load counter are explicit.
-//
-// The 16 row-groups of 16 rows are interleaved over the two wavefront rows, and groups past
-// the tile's last row skip their MFMAs, so a ragged expert tail costs MFMA time in proportion
-// to its rows (the tile height adapts to skewed expert loads in steps of 16 rows).
+// Helpers of the prefill kernels: explicit load-counter waits, a block barrier, and direct
+// global->LDS loads issued from inline asm (each LDS slot is its own LDS object so that the
+// compiler can tell the slots apart; waits on the load counter are explicit).
 // ---------------------------------------------------------------------------------------
 
 namespace {
@@ -292,14 +283,19 @@ __device__ __forceinline__ void dma4(const void* src, const void* lds_base) {
 }  // namespace
 
 // ---------------------------------------------------------------------------------------
-// Prefill kernel, bf16 weights: 256 x 256 block tile, 4 wavefronts (2 x 2) of 128 x 128
-// (256 fp32 accumulators per lane, held in AGPRs), K in 32-wide stages.  A 4-slot LDS ring
-// (4 x 32 KiB) is filled by direct global->LDS loads and the operand fragments of the next
-// stage are read from LDS into registers while the 64 MFMAs of the current stage run.  Rows
-// are 64 bytes in LDS; the 16-byte chunk c of row r sits in slot c ^ ((r >> 1) & 3), which
-// keeps the fragment reads (8 consecutive rows, one chunk) on distinct banks.  Activation
-// rows are gathered through the dispatch map; weights come in the packed layout, where every
-// stage of a 256-row tile is already this LDS image (one contiguous 16 KiB read).
+// Prefill kernel, bf16 weights: 256 x 256 block tile, 8 wavefronts (2 x 4) of 128 x 64, two
+// per SIMD (128 fp32 accumulators and about 250 registers per lane each), so that while one
+// wavefront waits for LDS data the other issues MFMAs.  K in 32-wide stages; a 4-slot LDS ring
+// (4 x 32 KiB) is filled by direct global->LDS loads (each wavefront moves two 1 KiB groups of
+// activation rows and two of weight rows per stage) and the operand fragments of the next
+// stage are read from LDS into registers while the MFMAs of the current stage run.  Rows are 64
+// bytes in LDS; the 16-byte chunk c of row r sits in slot c ^ ((r >> 1) & 3), which keeps the
+// fragment reads (8 consecutive rows, one chunk) on distinct banks.  Activation rows are
+// gathered through the dispatch map; weights come in the packed layout, where every stage of a
+// 256-row tile is already this LDS image (one contiguous 16 KiB read).  The 16 groups of 16
+// rows alternate between the two wavefront rows and groups past the tile's last row skip their
+// MFMAs.  For gate/up, wavefront column c holds weight row groups {0, 1, 4, 5} + 8 (c >> 1) +
+// 2 (c & 1) of the tile's 16: 32 gate rows and the 32 up rows of the same hid columns.
 // ---------------------------------------------------------------------------------------
 
 namespace {
@@ -307,12 +303,9 @@ __device__ __forceinline__ int lds_slot32(int row, int ch) { return row * 4 + (c
 }  // namespace
 
 template <int KIND>
-__global__ __launch_bounds__(256, 1) void gemm_prefill_bf16_kernel(GemmArgs g) {
+__global__ __launch_bounds__(512, 1) void gemm_prefill_bf16_kernel(GemmArgs g) {
     constexpr int BM = 256, BN = 256, BKS = 32;
-    constexpr int A_DMA = BM / 16 / 4;  // 16-row groups (1 KiB) per wavefront per stage
-    constexpr int B_DMA = BN / 16 / 4;
-    constexpr int LOADS = A_DMA + B_DMA;
-    constexpr int HALF = (KIND == kGateUp) ? BN / 2 : BN;  // output columns per block
+    constexpr int HALF = (KIND == kGateUp) ? BN / 2 : BN;
     __shared__ uint4 sA0[BM * 4], sA1[BM * 4], sA2[BM * 4], sA3[BM * 4];
     __shared__ uint4 sB0[BN * 4], sB1[BN * 4], sB2[BN * 4], sB3[BN * 4];
 
@@ -327,105 +320,105 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_bf16_kernel(GemmArgs g) {
     const int nsub = (r1 - r0 + 15) / 16;
     const int nt = item % ncols;
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wr = wave >> 1, wc = wave & 1;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7
+    const int wr = wave >> 2, wc = wave & 3;                      // 2 x 4 wavefronts
     const int K = g.K;
-    const int Nw = (KIND == kGateUp) ? 2 * g.F : g.N;
 
-    const char* pa[A_DMA];
-    const char* pb[B_DMA];
+    const char* pa[2];
 #pragma unroll
-    for (int i = 0; i < A_DMA; ++i) {
-        const int row = (i * 4 + wave) * 16 + (lane >> 2);
+    for (int i = 0; i < 2; ++i) {
+        const int row = (i * 8 + wave) * 16 + (lane >> 2);
         const int ch = (lane & 3) ^ ((row >> 1) & 3);
         const int rr = min(r0 + row, r1 - 1);
         int src = g.a_rows ? g.a_rows[rr] : rr;
         src = src < 0 ? 0 : (src >= g.a_rows_limit ? g.a_rows_limit - 1 : src);
         pa[i] = static_cast<const char*>(g.a) + (size_t(src) * K + ch * 8) * 2;
     }
-    // packed weights: block (e, nt, stage) is the 16 KiB image of the LDS slot; wavefront
-    // instruction i moves its bytes [1 KiB (i * 4 + wave), +1 KiB) (ncols equals the packed
-    // tile count: F/128 gate/up tiles, H/256 down tiles)
     const char* const wblk = static_cast<const char*>(g.w) + (size_t(e) * ncols + nt) * size_t(K / BKS) * 16384;
+    const char* pb[2];
 #pragma unroll
-    for (int i = 0; i < B_DMA; ++i) pb[i] = wblk + (i * 4 + wave) * 1024 + lane * 16;
+    for (int i = 0; i < 2; ++i) pb[i] = wblk + (i * 8 + wave) * 1024 + lane * 16;
+    // B row groups of this wavefront: gate/up -> two gate groups and the matching up groups
+    int gb[4];
+    if (KIND == kGateUp) {
+        const int base = (wc >> 1) * 8 + (wc & 1) * 2;
+        gb[0] = base; gb[1] = base + 1; gb[2] = base + 4; gb[3] = base + 5;
+    } else {
+        gb[0] = 4 * wc; gb[1] = 4 * wc + 1; gb[2] = 4 * wc + 2; gb[3] = 4 * wc + 3;
+    }
 
-#define MOE_ISSUE2(SA, SB, K0)                                                                  \
+#define MOE_ISSUE8(SA, SB, K0)                                                                  \
     do {                                                                                        \
         const int k0_ = (K0);                                                                   \
-        _Pragma("unroll") for (int i = 0; i < A_DMA; ++i)                                       \
-            dma16(pa[i] + k0_ * 2, &SA[(i * 4 + wave) * 64]);                                   \
-        _Pragma("unroll") for (int i = 0; i < B_DMA; ++i)                                       \
-            dma16(pb[i] + k0_ * 512, &SB[(i * 4 + wave) * 64]);                                 \
+        _Pragma("unroll") for (int i = 0; i < 2; ++i)                                           \
+            dma16(pa[i] + k0_ * 2, &SA[(i * 8 + wave) * 64]);                                   \
+        _Pragma("unroll") for (int i = 0; i < 2; ++i)                                           \
+            dma16(pb[i] + k0_ * 512, &SB[(i * 8 + wave) * 64]);                                 \
     } while (0)
-#define MOE_READ2(SA, SB, AF, BF)                                                               \
+#define MOE_READ8(SA, SB, AF, BF)                                                               \
     do {                                                                                        \
         const int ch_ = lane >> 4;                                                              \
-        _Pragma("unroll") for (int ni = 0; ni < 8; ++ni) BF[ni] =                               \
-            __builtin_bit_cast(bf16x8_t, SB[lds_slot32(wc * 128 + ni * 16 + (lane & 15), ch_)]); \
+        _Pragma("unroll") for (int ni = 0; ni < 4; ++ni) BF[ni] =                               \
+            __builtin_bit_cast(bf16x8_t, SB[lds_slot32(gb[ni] * 16 + (lane & 15), ch_)]);        \
         _Pragma("unroll") for (int mi = 0; mi < 8; ++mi) AF[mi] =                               \
             __builtin_bit_cast(bf16x8_t, SA[lds_slot32((mi * 2 + wr) * 16 + (lane & 15), ch_)]); \
     } while (0)
-#define MOE_MFMA2(AF, BF)                                                                       \
+#define MOE_MFMA8(AF, BF)                                                                       \
     do {                                                                                        \
         _Pragma("unroll") for (int mi = 0; mi < 8; ++mi) {                                      \
             if (mi * 2 + wr < nsub) {                                                           \
-                _Pragma("unroll") for (int ni = 0; ni < 8; ++ni) acc[mi][ni] =                  \
+                _Pragma("unroll") for (int ni = 0; ni < 4; ++ni) acc[mi][ni] =                  \
                     __builtin_amdgcn_mfma_f32_16x16x32_bf16(AF[mi], BF[ni], acc[mi][ni], 0, 0, 0); \
             }                                                                                   \
         }                                                                                       \
     } while (0)
 
-    f32x4_t acc[8][8];
+    f32x4_t acc[8][4];
 #pragma unroll
     for (int mi = 0; mi < 8; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 8; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    bf16x8_t a0[8], b0[8], a1[8], b1[8];
+        for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    bf16x8_t a0[8], b0[4], a1[8], b1[4];
 
-    // Stage s lives in slot s % 4.  Iteration s: wait for stage s+1, barrier, read its
-    // fragments, refill the slot of stage s (already in registers) with stage s+4, and run
-    // the MFMAs of stage s.  Loads per iteration are unconditional (clamped to the last stage)
-    // so that the load counter always holds exactly two stages after stage s+1.
     const int nk = K / BKS;
     const int last = (nk - 1) * BKS;
-    MOE_ISSUE2(sA0, sB0, 0);
-    MOE_ISSUE2(sA1, sB1, min(1 * BKS, last));
-    MOE_ISSUE2(sA2, sB2, min(2 * BKS, last));
-    wait_vm_lgkm0<2 * LOADS>();
+    MOE_ISSUE8(sA0, sB0, 0);
+    MOE_ISSUE8(sA1, sB1, min(1 * BKS, last));
+    MOE_ISSUE8(sA2, sB2, min(2 * BKS, last));
+    wait_vm_lgkm0<8>();
     block_barrier();
-    MOE_READ2(sA0, sB0, a0, b0);
-    MOE_ISSUE2(sA3, sB3, min(3 * BKS, last));
+    MOE_READ8(sA0, sB0, a0, b0);
+    MOE_ISSUE8(sA3, sB3, min(3 * BKS, last));
     for (int s = 0;; s += 4) {
-        wait_vm_lgkm0<2 * LOADS>();  // stage s+1 landed; stage s fragments in a0/b0
+        wait_vm_lgkm0<8>();
         block_barrier();
-        MOE_READ2(sA1, sB1, a1, b1);
-        MOE_ISSUE2(sA0, sB0, min((s + 4) * BKS, last));
-        MOE_MFMA2(a0, b0);
+        MOE_READ8(sA1, sB1, a1, b1);
+        MOE_ISSUE8(sA0, sB0, min((s + 4) * BKS, last));
+        MOE_MFMA8(a0, b0);
         if (s + 1 >= nk) break;
-        wait_vm_lgkm0<2 * LOADS>();
+        wait_vm_lgkm0<8>();
         block_barrier();
-        MOE_READ2(sA2, sB2, a0, b0);
-        MOE_ISSUE2(sA1, sB1, min((s + 5) * BKS, last));
-        MOE_MFMA2(a1, b1);
+        MOE_READ8(sA2, sB2, a0, b0);
+        MOE_ISSUE8(sA1, sB1, min((s + 5) * BKS, last));
+        MOE_MFMA8(a1, b1);
         if (s + 2 >= nk) break;
-        wait_vm_lgkm0<2 * LOADS>();
+        wait_vm_lgkm0<8>();
         block_barrier();
-        MOE_READ2(sA3, sB3, a1, b1);
-        MOE_ISSUE2(sA2, sB2, min((s + 6) * BKS, last));
-        MOE_MFMA2(a0, b0);
+        MOE_READ8(sA3, sB3, a1, b1);
+        MOE_ISSUE8(sA2, sB2, min((s + 6) * BKS, last));
+        MOE_MFMA8(a0, b0);
         if (s + 3 >= nk) break;
-        wait_vm_lgkm0<2 * LOADS>();
+        wait_vm_lgkm0<8>();
         block_barrier();
-        MOE_READ2(sA0, sB0, a0, b0);
-        MOE_ISSUE2(sA3, sB3, min((s + 7) * BKS, last));
-        MOE_MFMA2(a1, b1);
+        MOE_READ8(sA0, sB0, a0, b0);
+        MOE_ISSUE8(sA3, sB3, min((s + 7) * BKS, last));
+        MOE_MFMA8(a1, b1);
         if (s + 4 >= nk) break;
     }
     wait_vm_lgkm0<0>();
-#undef MOE_ISSUE2
-#undef MOE_READ2
-#undef MOE_MFMA2
+#undef MOE_ISSUE8
+#undef MOE_READ8
+#undef MOE_MFMA8
 
     uint16_t* out = static_cast<uint16_t*>(g.out);
 #pragma unroll
@@ -437,14 +430,14 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_bf16_kernel(GemmArgs g) {
             if (row >= r1) continue;
             if (KIND == kGateUp) {
 #pragma unroll
-                for (int ni = 0; ni < 4; ++ni) {
-                    const int col = nt * HALF + wc * 64 + ni * 16 + (lane & 15);
-                    out[size_t(row) * g.F + col] = (uint16_t)bf16_rne(silu_mul(acc[mi][ni][i], acc[mi][ni + 4][i]));
+                for (int ni = 0; ni < 2; ++ni) {
+                    const int col = nt * HALF + (wc >> 1) * 64 + (wc & 1) * 32 + ni * 16 + (lane & 15);
+                    out[size_t(row) * g.F + col] = (uint16_t)bf16_rne(silu_mul(acc[mi][ni][i], acc[mi][ni + 2][i]));
                 }
             } else {
 #pragma unroll
-                for (int ni = 0; ni < 8; ++ni) {
-                    const int col = nt * BN + wc * 128 + ni * 16 + (lane & 15);
+                for (int ni = 0; ni < 4; ++ni) {
+                    const int col = nt * BN + wc * 64 + ni * 16 + (lane & 15);
                     if (col < g.N) out[size_t(row) * g.N + col] = (uint16_t)bf16_rne(acc[mi][ni][i]);
                 }
             }
@@ -471,9 +464,8 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_bf16_kernel(GemmArgs g) {
 // ---------------------------------------------------------------------------------------
 
 template <int KIND>
-__global__ __launch_bounds__(256, 1) void gemm_prefill_nvfp4_kernel(GemmArgs g) {
+__global__ __launch_bounds__(512, 1) void gemm_prefill_nvfp4_kernel(GemmArgs g) {
     constexpr int BM = 256, BN = 256, BKS = 32;
-    constexpr int A_DMA = BM / 16 / 4;
     constexpr int HALF = (KIND == kGateUp) ? BN / 2 : BN;
     __shared__ uint4 sA0[BM * 4], sA1[BM * 4], sA2[BM * 4], sA3[BM * 4];
     __shared__ uint4 sN0[BN], sN1[BN], sN2[BN], sN3[BN];     // raw nibbles of weight row r
@@ -491,63 +483,74 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_nvfp4_kernel(GemmArgs g) 
     const int nsub = (r1 - r0 + 15) / 16;
     const int nt = item % ncols;
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wr = wave >> 1, wc = wave & 1;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7
+    const int wr = wave >> 2, wc = wave & 3;                      // 2 x 4 wavefronts
     const int K = g.K;
     const int Nw = (KIND == kGateUp) ? 2 * g.F : g.N;
 
-    const char* pa[A_DMA];
+    const char* pa[2];
 #pragma unroll
-    for (int i = 0; i < A_DMA; ++i) {
-        const int row = (i * 4 + wave) * 16 + (lane >> 2);
+    for (int i = 0; i < 2; ++i) {
+        const int row = (i * 8 + wave) * 16 + (lane >> 2);
         const int ch = (lane & 3) ^ ((row >> 1) & 3);
         const int rr = min(r0 + row, r1 - 1);
         int src = g.a_rows ? g.a_rows[rr] : rr;
         src = src < 0 ? 0 : (src >= g.a_rows_limit ? g.a_rows_limit - 1 : src);
         pa[i] = static_cast<const char*>(g.a) + (size_t(src) * K + ch * 8) * 2;
     }
-    // raw weights: thread t moves (and later decodes) weight row t of the tile; for gate/up,
-    // per wavefront column 64 gate rows then the matching up rows, as in the other kernels
+    // raw weights: wavefronts 0..3 move the nibbles and wavefronts 4..7 the scale words of
+    // weight rows 64 (wave & 3) + lane; tile row r holds, per 128-row half, 64 gate rows then
+    // the matching up rows (the packed bf16 order)
+    const int mrow = (wave & 3) * 64 + lane;
     int wrow;
     if (KIND == kGateUp) {
-        const int q = tid & 127;
-        const int f = nt * HALF + (tid >> 7) * 64 + (q & 63);
+        const int q = mrow & 127;
+        const int f = nt * HALF + (mrow >> 7) * 64 + (q & 63);
         wrow = q < 64 ? f : g.F + f;
     } else {
-        wrow = min(nt * BN + tid, g.N - 1);
+        wrow = min(nt * BN + mrow, g.N - 1);
     }
     const size_t wrow_g = size_t(e) * Nw + wrow;
     const char* const pq = static_cast<const char*>(g.w) + wrow_g * (K / 2);
     const char* const ps = reinterpret_cast<const char*>(g.wscale) + wrow_g * (K / 16);
+    int gb[4];  // weight row groups of this wavefront (gate/up: two gate groups, their up groups)
+    if (KIND == kGateUp) {
+        const int base = (wc >> 1) * 8 + (wc & 1) * 2;
+        gb[0] = base; gb[1] = base + 1; gb[2] = base + 4; gb[3] = base + 5;
+    } else {
+        gb[0] = 4 * wc; gb[1] = 4 * wc + 1; gb[2] = 4 * wc + 2; gb[3] = 4 * wc + 3;
+    }
 
 #define MOE_ISSUE_A(SA, K0)                                                                     \
     do {                                                                                        \
         const int k0_ = (K0);                                                                   \
-        _Pragma("unroll") for (int i = 0; i < A_DMA; ++i)                                       \
-            dma16(pa[i] + k0_ * 2, &SA[(i * 4 + wave) * 64]);                                   \
+        _Pragma("unroll") for (int i = 0; i < 2; ++i)                                           \
+            dma16(pa[i] + k0_ * 2, &SA[(i * 8 + wave) * 64]);                                   \
     } while (0)
     // nibbles of stage k0/32, and the scale word holding its two scales (stages 2m, 2m+1)
 #define MOE_ISSUE_W(SN, SS, K0)                                                                 \
     do {                                                                                        \
         const int k0_ = (K0);                                                                   \
-        dma16(pq + k0_ / 2, &SN[wave * 64]);                                                    \
-        dma4(ps + ((k0_ >> 4) & ~3), &SS[wave * 64]);                                           \
+        if (wave < 4)                                                                           \
+            dma16(pq + k0_ / 2, &SN[wave * 64]);                                                \
+        else                                                                                    \
+            dma4(ps + ((k0_ >> 4) & ~3), &SS[(wave - 4) * 64]);                                 \
     } while (0)
+    // thread t decodes half h = t & 1 of weight row t >> 1: chunks 2h, 2h+1 with scale h
 #define MOE_DECODE(SN, SS, SB, K0)                                                              \
     do {                                                                                        \
-        const uint4 nib_ = SN[tid];                                                             \
-        const uint32_t sw_ = SS[tid] >> ((((K0) >> 5) & 1) * 16);                               \
-        const float s0_ = e4m3_value(sw_ & 0xffu), s1_ = e4m3_value((sw_ >> 8) & 0xffu);          \
-        SB[lds_slot32(tid, 0)] = dequant8(nib_.x, s0_);                                         \
-        SB[lds_slot32(tid, 1)] = dequant8(nib_.y, s0_);                                         \
-        SB[lds_slot32(tid, 2)] = dequant8(nib_.z, s1_);                                         \
-        SB[lds_slot32(tid, 3)] = dequant8(nib_.w, s1_);                                         \
+        const int row_ = tid >> 1, h_ = tid & 1;                                                \
+        const uint2 nib_ = reinterpret_cast<const uint2*>(SN)[row_ * 2 + h_];                   \
+        const uint32_t sw_ = SS[row_] >> ((((K0) >> 5) & 1) * 16 + 8 * h_);                     \
+        const float sc_ = e4m3_value(sw_ & 0xffu);                                              \
+        SB[lds_slot32(row_, 2 * h_)] = dequant8(nib_.x, sc_);                                   \
+        SB[lds_slot32(row_, 2 * h_ + 1)] = dequant8(nib_.y, sc_);                               \
     } while (0)
 #define MOE_READ(SA, SB, AF, BF)                                                                \
     do {                                                                                        \
         const int ch_ = lane >> 4;                                                              \
-        _Pragma("unroll") for (int ni = 0; ni < 8; ++ni) BF[ni] =                               \
-            __builtin_bit_cast(bf16x8_t, SB[lds_slot32(wc * 128 + ni * 16 + (lane & 15), ch_)]); \
+        _Pragma("unroll") for (int ni = 0; ni < 4; ++ni) BF[ni] =                               \
+            __builtin_bit_cast(bf16x8_t, SB[lds_slot32(gb[ni] * 16 + (lane & 15), ch_)]);        \
         _Pragma("unroll") for (int mi = 0; mi < 8; ++mi) AF[mi] =                               \
             __builtin_bit_cast(bf16x8_t, SA[lds_slot32((mi * 2 + wr) * 16 + (lane & 15), ch_)]); \
     } while (0)
@@ -555,18 +558,18 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_nvfp4_kernel(GemmArgs g) 
     do {                                                                                        \
         _Pragma("unroll") for (int mi = 0; mi < 8; ++mi) {                                      \
             if (mi * 2 + wr < nsub) {                                                           \
-                _Pragma("unroll") for (int ni = 0; ni < 8; ++ni) acc[mi][ni] =                  \
+                _Pragma("unroll") for (int ni = 0; ni < 4; ++ni) acc[mi][ni] =                  \
                     __builtin_amdgcn_mfma_f32_16x16x32_bf16(AF[mi], BF[ni], acc[mi][ni], 0, 0, 0); \
             }                                                                                   \
         }                                                                                       \
     } while (0)
 
-    f32x4_t acc[8][8];
+    f32x4_t acc[8][4];
 #pragma unroll
     for (int mi = 0; mi < 8; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 8; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    bf16x8_t a0[8], b0[8], a1[8], b1[8];
+        for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    bf16x8_t a0[8], b0[4], a1[8], b1[4];
 
     const int nk = K / BKS;
     const int last = (nk - 1) * BKS;
@@ -590,7 +593,7 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_nvfp4_kernel(GemmArgs g) 
     MOE_ISSUE_W(sN0, sS0, min(4 * BKS, last));
     for (int s = 0;; s += 4) {
 #define MOE_IT(S, FA, FB, GA, GB, SAr, SBr, SAw, SNw, SSw, SNd, SSd, SBd)      \
-        wait_vm_lgkm0<12>();                                                 \
+        wait_vm_lgkm0<6>();                                                  \
         block_barrier();                                                     \
         MOE_READ(SAr, SBr, GA, GB);                                          \
         MOE_ISSUE_A(SAw, min((s + S + 4) * BKS, last));                      \
@@ -622,15 +625,15 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_nvfp4_kernel(GemmArgs g) 
             if (row >= r1) continue;
             if (KIND == kGateUp) {
 #pragma unroll
-                for (int ni = 0; ni < 4; ++ni) {
-                    const int col = nt * HALF + wc * 64 + ni * 16 + (lane & 15);
+                for (int ni = 0; ni < 2; ++ni) {
+                    const int col = nt * HALF + (wc >> 1) * 64 + (wc & 1) * 32 + ni * 16 + (lane & 15);
                     out[size_t(row) * g.F + col] =
-                        (uint16_t)bf16_rne(silu_mul(acc[mi][ni][i] * gs, acc[mi][ni + 4][i] * gs));
+                        (uint16_t)bf16_rne(silu_mul(acc[mi][ni][i] * gs, acc[mi][ni + 2][i] * gs));
                 }
             } else {
 #pragma unroll
-                for (int ni = 0; ni < 8; ++ni) {
-                    const int col = nt * BN + wc * 128 + ni * 16 + (lane & 15);
+                for (int ni = 0; ni < 4; ++ni) {
+                    const int col = nt * BN + wc * 64 + ni * 16 + (lane & 15);
                     if (col < g.N) out[size_t(row) * g.N + col] = (uint16_t)bf16_rne(acc[mi][ni][i] * gs);
                 }
             }
@@ -1006,15 +1009,15 @@ hipError_t launch_gemm(const GemmArgs& g, int family, int max_tiles, hipStream_t
     } else if (family == kFamPrefill && g.wfmt == kWBF16) {  // packed weights: F % 128 == 0, H % 256 == 0
         const dim3 grid = prefill_grid(g, max_tiles, 256);
         if (up)
-            hipLaunchKernelGGL((gemm_prefill_bf16_kernel<kGateUp>), grid, dim3(256), 0, s, g);
+            hipLaunchKernelGGL((gemm_prefill_bf16_kernel<kGateUp>), grid, dim3(512), 0, s, g);
         else
-            hipLaunchKernelGGL((gemm_prefill_bf16_kernel<kDown>), grid, dim3(256), 0, s, g);
+            hipLaunchKernelGGL((gemm_prefill_bf16_kernel<kDown>), grid, dim3(512), 0, s, g);
     } else if (family == kFamPrefill && g.F % 128 == 0) {
         const dim3 grid = prefill_grid(g, max_tiles, 256);
         if (up)
-            hipLaunchKernelGGL((gemm_prefill_nvfp4_kernel<kGateUp>), grid, dim3(256), 0, s, g);
+            hipLaunchKernelGGL((gemm_prefill_nvfp4_kernel<kGateUp>), grid, dim3(512), 0, s, g);
         else
-            hipLaunchKernelGGL((gemm_prefill_nvfp4_kernel<kDown>), grid, dim3(256), 0, s, g);
+            hipLaunchKernelGGL((gemm_prefill_nvfp4_kernel<kDown>), grid, dim3(512), 0, s, g);
     } else if (family == kFamPrefill) {
         launch_mfma<PF_BM, PF_BN, PF_WM, PF_WN>(g, max_tiles, s);
     } else if (g.K % 128 == 0) {
