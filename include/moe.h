@@ -35,7 +35,9 @@
  *  - T = 0 is a successful no-op (token-sized buffers and the workspace may then be NULL;
  *    moe_permute and moe_forward still set counts/offsets, when given, to zero).
  *  - Determinism: identical inputs give bitwise identical outputs (no floating-point atomics).
- *  - Non-finite inputs give unspecified (but memory-safe) results.
+ *  - Non-finite inputs give unspecified (but memory-safe) values; the routing stays valid:
+ *    every token still gets k distinct experts in [0, E) (a NaN logit ranks below every
+ *    number) and the permutation stays a bijection.
  *
  * Routing contract (bit-exact):
  *  - logits l[t,e] are fp32 in a canonical order: H is cut into chunks of 8 consecutive

@@ -8,8 +8,9 @@ namespace moe {
 
 // Top-k of one token by one wavefront: k rounds of a wave-wide argmax over (logit desc,
 // expert asc), then the softmax weights in fp32.  `row` is the token's E logits; ids and w
-// receive k values each (and ids_lds too, when given).  Always yields k distinct valid experts
-// (memory safe even for non-finite logits).
+// receive k values each (and ids_lds too, when given).  NaN logits rank below every number, so
+// the comparison is a total order and every lane agrees on each winner: always k distinct valid
+// experts, also for non-finite logits (whose weights are then unspecified).
 template <int EPL>
 __device__ __forceinline__ void topk_token(const float* __restrict__ row, int E, int k, int renorm,
                                            int32_t* __restrict__ ids, float* __restrict__ w,
@@ -23,6 +24,7 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ row, int E,
         const int e = lane + kWave * i;
         live[i] = e < E;
         v[i] = live[i] ? row[e] : 0.0f;
+        if (v[i] != v[i]) v[i] = -__builtin_inff();  // NaN ranks last: a total order for selection
     }
     float selv[kMaxTopK];
     int sele[kMaxTopK];

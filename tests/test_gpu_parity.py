@@ -449,3 +449,59 @@ def test_single_token_prefill_path_and_large_batch_decode_path():
         inp = synth.generate(wl)
         note("forced path %s T=%d" % (path, T))
         _check_forward(wl, inp, MoELayer.from_workload(wl, inp, path=path))
+
+
+# ---------------------------------------------------------------------------------------
+# limits, streams, non-finite inputs
+# ---------------------------------------------------------------------------------------
+
+def test_largest_expert_count_and_top_k_at_prefill_size():
+    """E = 512 experts, k = 16 (the ABI's limits) with 2048 tokens: many partially filled
+    tiles per launch on the prefill path; routing bit-exact, outputs on sampled tokens."""
+    wl = W("maxek", 2048, 256, 512, 16, 128, "bf16", "bf16", 91, "normal")
+    inp = synth.generate(wl)
+    note("E=512 k=16 T=2048")
+    layer = MoELayer.from_workload(wl, inp)
+    toks = np.array([0, 1, 777, 1500, 2047])
+    _check_forward(wl, inp, layer, tokens=toks)
+
+
+def test_forward_on_a_side_stream_matches_the_default_stream():
+    wl = SMALL["small_nvfp4"]
+    inp = inputs_of(wl)
+    layer = MoELayer.from_workload(wl, inp)
+    x = layer.act_tensor(inp["x"])
+    note("side stream")
+    y0 = layer.forward(x).clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        y1 = layer.forward(x, stream=side.cuda_stream)
+    side.synchronize()
+    assert torch.equal(y0, y1)
+
+
+def test_non_finite_inputs_stay_memory_safe_and_route_validly():
+    """Non-finite activations give unspecified values but valid, distinct expert ids and a
+    complete permutation (the header's promise)."""
+    wl = W("nonfinite", 64, 256, 16, 4, 128, "bf16", "bf16", 93, "normal")
+    inp = synth.generate(wl)
+    x = inp["x"].copy()
+    x[3, :] = 0x7FC0   # NaN
+    x[5, 7] = 0x7F80   # +Inf
+    x[9, 0] = 0xFF80   # -Inf
+    inp["x"] = x
+    layer = MoELayer.from_workload(wl, inp)
+    note("non-finite inputs")
+    for path in ("prefill", "decode"):
+        y, dbg = layer.forward(layer.act_tensor(x), debug=True, path=path)
+        torch.cuda.synchronize()
+        ids = dbg["topk_ids"].cpu().numpy()
+        assert ids.min() >= 0 and ids.max() < wl.experts
+        assert all(len(set(r)) == wl.top_k for r in ids)
+        ip = dbg["inv_perm"].cpu().numpy()
+        assert np.array_equal(np.sort(ip), np.arange(wl.assignments))
+        st = dbg["sorted_token"].cpu().numpy()
+        assert np.array_equal(st[ip], np.arange(wl.assignments) // wl.top_k)
+        good = [t for t in range(wl.tokens) if t not in (3, 5, 9)]
+        assert np.isfinite(act_f64(to_host(y))[good]).all()
