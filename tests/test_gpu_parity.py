@@ -27,6 +27,7 @@ SMALL = {
     "ragged_nvfp4": W("ragged_nvfp4", 77, 192, 5, 3, 320, "bf16", "nvfp4", 14, "normal"),
     # K = 2048 on both GEMMs: the NVFP4 decode kernel takes its 512-wide scale windows
     "win4_nvfp4": W("win4_nvfp4", 8, 2048, 16, 2, 2048, "bf16", "nvfp4", 15, "normal"),
+    "ragged_f32": W("ragged_f32", 33, 128, 5, 2, 192, "f32", "f32", 16, "normal"),
     "tiny": synth.WORKLOADS["tiny"],
 }
 
@@ -155,7 +156,7 @@ def _routed(wl, inp):
 
 
 @pytest.mark.parametrize("name", ["tiny", "small_bf16", "small_nvfp4", "ragged_bf16", "ragged_nvfp4",
-                                  "win4_nvfp4"])
+                                  "win4_nvfp4", "ragged_f32"])
 @pytest.mark.parametrize("path", ["prefill", "decode"])
 def test_gate_up_matches_oracle(name, path):
     wl = SMALL[name]
@@ -185,7 +186,7 @@ def test_gate_up_matches_oracle(name, path):
 
 
 @pytest.mark.parametrize("name", ["tiny", "small_bf16", "small_nvfp4", "ragged_bf16", "ragged_nvfp4",
-                                  "win4_nvfp4"])
+                                  "win4_nvfp4", "ragged_f32"])
 @pytest.mark.parametrize("path", ["prefill", "decode"])
 def test_down_matches_oracle(name, path):
     wl = SMALL[name]
@@ -321,7 +322,7 @@ def _check_forward(wl, inp, layer, tokens=None, path=None):
 
 
 FWD_CASES = ["tiny", "small_bf16", "small_nvfp4", "ragged_bf16", "ragged_nvfp4", "win4_nvfp4",
-             "decode1", "decode8", "nvfp4_decode"]
+             "ragged_f32", "decode1", "decode8", "nvfp4_decode"]
 
 
 @pytest.mark.parametrize("name", FWD_CASES)
@@ -426,7 +427,8 @@ def test_k_equals_e(E, k):
     _check_forward(wl, inp, MoELayer.from_workload(wl, inp))
 
 
-@pytest.mark.parametrize("T,E,k", [(1, 8, 8), (8, 512, 16), (3, 5, 2), (8, 128, 8)])
+@pytest.mark.parametrize("T,E,k", [(1, 8, 8), (8, 512, 16), (3, 5, 2), (8, 128, 8), (5, 1, 1),
+                                   (2, 3, 3)])
 def test_small_batch_single_launch_dispatch(T, E, k):
     """Batches of up to 8 tokens select and dispatch in one single-block launch; routing
     outputs stay bit-exact and the layer output within tolerance."""
