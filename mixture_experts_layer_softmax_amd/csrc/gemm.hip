@@ -446,26 +446,32 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_bf16_kernel(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Prefill kernel, NVFP4 weights: the bf16 kernel's 256 x 256 tile, four 128 x 128
-// wavefronts and activation DMA ring; the weights are DMA'd raw (16 nibble bytes and one
-// 4-byte scale word per weight row and stage, straight from the row-major NVFP4 arrays) and
-// decoded by the block into a bf16 LDS slot: thread t decodes weight row t (e2m1 * e4m3 is
-// exact in bf16) after issuing the MFMAs of the current stage, so the decode overlaps the
-// matrix core.  The per-expert fp32 scale multiplies the accumulators.
+// Prefill kernel, NVFP4 weights: the bf16 kernel's 256 x 256 tile and activation DMA ring with
+// NW = 4 wavefronts (2 x 2, 128 x 128 each) or NW = 8 (2 x 4, 128 x 64 each; measured: 8 for
+// the down GEMM, 4 for gate/up); the weights are DMA'd raw (16 nibble bytes and one 4-byte
+// scale word per weight row and stage, straight from the row-major NVFP4 arrays) and decoded
+// by the block into a bf16 LDS slot (e2m1 * e4m3 is exact in bf16) after the MFMAs of the
+// current stage are issued, so the decode overlaps the matrix core.  The per-expert fp32 scale
+// multiplies the accumulators.
 //
 // Iteration i: activation stage i+1 and raw weight stage i+2 have landed (issued three
 // iterations earlier); read the fragments of stage i+1 (activations from ring slot (i+1)%4,
 // decoded weights from bf16 slot (i+1)%2); DMA activation stage i+4 (slot i%4) and raw weight
 // stage i+5 (raw slot (i+1)%4); run the MFMAs of stage i; decode raw stage i+2 (raw slot
-// (i+2)%4) into bf16 slot i%2.  Every wavefront issues six DMA instructions per iteration
-// (four activation, one nibble, one scale), so "landed" is a fixed load count.  Thread t
-// decodes the raw row its own lane DMA'd, so its wait covers its data; the barrier publishes
-// the decoded slot to the other wavefronts.
+// (i+2)%4) into bf16 slot i%2.  Every wavefront issues the same number of DMA instructions
+// per iteration (NW = 4: four activation, one nibble, one scale; NW = 8: two activation and
+// one nibble or scale), so "landed" is a fixed load count; the barrier at the top of the
+// iteration also publishes each raw row to the thread that decodes it.
 // ---------------------------------------------------------------------------------------
 
-template <int KIND>
-__global__ __launch_bounds__(512, 1) void gemm_prefill_nvfp4_kernel(GemmArgs g) {
+template <int KIND, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void gemm_prefill_nvfp4_kernel(GemmArgs g) {
+    static_assert(NW == 4 || NW == 8, "4 or 8 wavefronts");
     constexpr int BM = 256, BN = 256, BKS = 32;
+    constexpr int NC = NW / 2;        // wavefront columns
+    constexpr int NB = 16 / NC;       // 16-row weight groups per wavefront
+    constexpr int A_DMA = 16 / NW;    // activation DMA instructions per wavefront and stage
+    constexpr int OPS = A_DMA + (NW == 4 ? 2 : 1);  // DMA instructions per wavefront and stage
     constexpr int HALF = (KIND == kGateUp) ? BN / 2 : BN;
     __shared__ uint4 sA0[BM * 4], sA1[BM * 4], sA2[BM * 4], sA3[BM * 4];
     __shared__ uint4 sN0[BN], sN1[BN], sN2[BN], sN3[BN];     // raw nibbles of weight row r
@@ -483,24 +489,24 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_nvfp4_kernel(GemmArgs g) 
     const int nsub = (r1 - r0 + 15) / 16;
     const int nt = item % ncols;
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7
-    const int wr = wave >> 2, wc = wave & 3;                      // 2 x 4 wavefronts
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wr = wave / NC, wc = wave % NC;
     const int K = g.K;
     const int Nw = (KIND == kGateUp) ? 2 * g.F : g.N;
 
-    const char* pa[2];
+    const char* pa[A_DMA];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int row = (i * 8 + wave) * 16 + (lane >> 2);
+    for (int i = 0; i < A_DMA; ++i) {
+        const int row = (i * NW + wave) * 16 + (lane >> 2);
         const int ch = (lane & 3) ^ ((row >> 1) & 3);
         const int rr = min(r0 + row, r1 - 1);
         int src = g.a_rows ? g.a_rows[rr] : rr;
         src = src < 0 ? 0 : (src >= g.a_rows_limit ? g.a_rows_limit - 1 : src);
         pa[i] = static_cast<const char*>(g.a) + (size_t(src) * K + ch * 8) * 2;
     }
-    // raw weights: wavefronts 0..3 move the nibbles and wavefronts 4..7 the scale words of
-    // weight rows 64 (wave & 3) + lane; tile row r holds, per 128-row half, 64 gate rows then
-    // the matching up rows (the packed bf16 order)
+    // raw weights: wavefront w moves the nibbles (NW = 4: and the scale words) of weight rows
+    // 64 (w & 3) + lane, for NW = 8 wavefronts 4..7 the scale words; tile row r holds, per
+    // 128-row half, 64 gate rows then the matching up rows (the packed bf16 order)
     const int mrow = (wave & 3) * 64 + lane;
     int wrow;
     if (KIND == kGateUp) {
@@ -513,43 +519,63 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_nvfp4_kernel(GemmArgs g) 
     const size_t wrow_g = size_t(e) * Nw + wrow;
     const char* const pq = static_cast<const char*>(g.w) + wrow_g * (K / 2);
     const char* const ps = reinterpret_cast<const char*>(g.wscale) + wrow_g * (K / 16);
-    int gb[4];  // weight row groups of this wavefront (gate/up: two gate groups, their up groups)
-    if (KIND == kGateUp) {
-        const int base = (wc >> 1) * 8 + (wc & 1) * 2;
-        gb[0] = base; gb[1] = base + 1; gb[2] = base + 4; gb[3] = base + 5;
-    } else {
-        gb[0] = 4 * wc; gb[1] = 4 * wc + 1; gb[2] = 4 * wc + 2; gb[3] = 4 * wc + 3;
+    // weight row groups of this wavefront: gate/up, NB/2 gate groups then their up groups
+    int gb[NB];
+    int gcol;  // first hid column (gate/up) or output column (down) of this wavefront
+#pragma unroll
+    for (int ni = 0; ni < NB; ++ni) {
+        if (KIND == kGateUp) {
+            const int base = NW == 4 ? wc * 8 : (wc >> 1) * 8 + (wc & 1) * 2;
+            gb[ni] = base + (ni < NB / 2 ? ni : 4 + ni - NB / 2);
+        } else {
+            gb[ni] = NB * wc + ni;
+        }
     }
+    if (KIND == kGateUp)
+        gcol = nt * HALF + (NW == 4 ? wc * 64 : (wc >> 1) * 64 + (wc & 1) * 32);
+    else
+        gcol = nt * BN + wc * NB * 16;
 
 #define MOE_ISSUE_A(SA, K0)                                                                     \
     do {                                                                                        \
         const int k0_ = (K0);                                                                   \
-        _Pragma("unroll") for (int i = 0; i < 2; ++i)                                           \
-            dma16(pa[i] + k0_ * 2, &SA[(i * 8 + wave) * 64]);                                   \
+        _Pragma("unroll") for (int i = 0; i < A_DMA; ++i)                                       \
+            dma16(pa[i] + k0_ * 2, &SA[(i * NW + wave) * 64]);                                  \
     } while (0)
     // nibbles of stage k0/32, and the scale word holding its two scales (stages 2m, 2m+1)
 #define MOE_ISSUE_W(SN, SS, K0)                                                                 \
     do {                                                                                        \
         const int k0_ = (K0);                                                                   \
-        if (wave < 4)                                                                           \
-            dma16(pq + k0_ / 2, &SN[wave * 64]);                                                \
-        else                                                                                    \
-            dma4(ps + ((k0_ >> 4) & ~3), &SS[(wave - 4) * 64]);                                 \
+        if (NW == 4 || wave < 4)                                                                \
+            dma16(pq + k0_ / 2, &SN[(wave & 3) * 64]);                                          \
+        if (NW == 4 || wave >= 4)                                                               \
+            dma4(ps + ((k0_ >> 4) & ~3), &SS[(wave & 3) * 64]);                                 \
     } while (0)
-    // thread t decodes half h = t & 1 of weight row t >> 1: chunks 2h, 2h+1 with scale h
+    // NW = 4: thread t decodes weight row t; NW = 8: half h = t & 1 of row t >> 1 (chunks
+    // 2h, 2h+1, scale h)
 #define MOE_DECODE(SN, SS, SB, K0)                                                              \
     do {                                                                                        \
-        const int row_ = tid >> 1, h_ = tid & 1;                                                \
-        const uint2 nib_ = reinterpret_cast<const uint2*>(SN)[row_ * 2 + h_];                   \
-        const uint32_t sw_ = SS[row_] >> ((((K0) >> 5) & 1) * 16 + 8 * h_);                     \
-        const float sc_ = e4m3_value(sw_ & 0xffu);                                              \
-        SB[lds_slot32(row_, 2 * h_)] = dequant8(nib_.x, sc_);                                   \
-        SB[lds_slot32(row_, 2 * h_ + 1)] = dequant8(nib_.y, sc_);                               \
+        if constexpr (NW == 4) {                                                                \
+            const uint4 nib_ = SN[tid];                                                         \
+            const uint32_t sw_ = SS[tid] >> ((((K0) >> 5) & 1) * 16);                           \
+            const float s0_ = e4m3_value(sw_ & 0xffu), s1_ = e4m3_value((sw_ >> 8) & 0xffu);      \
+            SB[lds_slot32(tid, 0)] = dequant8(nib_.x, s0_);                                     \
+            SB[lds_slot32(tid, 1)] = dequant8(nib_.y, s0_);                                     \
+            SB[lds_slot32(tid, 2)] = dequant8(nib_.z, s1_);                                     \
+            SB[lds_slot32(tid, 3)] = dequant8(nib_.w, s1_);                                     \
+        } else {                                                                                \
+            const int row_ = tid >> 1, h_ = tid & 1;                                            \
+            const uint2 nib_ = reinterpret_cast<const uint2*>(SN)[row_ * 2 + h_];               \
+            const uint32_t sw_ = SS[row_] >> ((((K0) >> 5) & 1) * 16 + 8 * h_);                 \
+            const float sc_ = e4m3_value(sw_ & 0xffu);                                          \
+            SB[lds_slot32(row_, 2 * h_)] = dequant8(nib_.x, sc_);                               \
+            SB[lds_slot32(row_, 2 * h_ + 1)] = dequant8(nib_.y, sc_);                           \
+        }                                                                                       \
     } while (0)
 #define MOE_READ(SA, SB, AF, BF)                                                                \
     do {                                                                                        \
         const int ch_ = lane >> 4;                                                              \
-        _Pragma("unroll") for (int ni = 0; ni < 4; ++ni) BF[ni] =                               \
+        _Pragma("unroll") for (int ni = 0; ni < NB; ++ni) BF[ni] =                              \
             __builtin_bit_cast(bf16x8_t, SB[lds_slot32(gb[ni] * 16 + (lane & 15), ch_)]);        \
         _Pragma("unroll") for (int mi = 0; mi < 8; ++mi) AF[mi] =                               \
             __builtin_bit_cast(bf16x8_t, SA[lds_slot32((mi * 2 + wr) * 16 + (lane & 15), ch_)]); \
@@ -558,18 +584,18 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_nvfp4_kernel(GemmArgs g) 
     do {                                                                                        \
         _Pragma("unroll") for (int mi = 0; mi < 8; ++mi) {                                      \
             if (mi * 2 + wr < nsub) {                                                           \
-                _Pragma("unroll") for (int ni = 0; ni < 4; ++ni) acc[mi][ni] =                  \
+                _Pragma("unroll") for (int ni = 0; ni < NB; ++ni) acc[mi][ni] =                 \
                     __builtin_amdgcn_mfma_f32_16x16x32_bf16(AF[mi], BF[ni], acc[mi][ni], 0, 0, 0); \
             }                                                                                   \
         }                                                                                       \
     } while (0)
 
-    f32x4_t acc[8][4];
+    f32x4_t acc[8][NB];
 #pragma unroll
     for (int mi = 0; mi < 8; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    bf16x8_t a0[8], b0[4], a1[8], b1[4];
+        for (int ni = 0; ni < NB; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    bf16x8_t a0[8], b0[NB], a1[8], b1[NB];
 
     const int nk = K / BKS;
     const int last = (nk - 1) * BKS;
@@ -593,7 +619,7 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_nvfp4_kernel(GemmArgs g) 
     MOE_ISSUE_W(sN0, sS0, min(4 * BKS, last));
     for (int s = 0;; s += 4) {
 #define MOE_IT(S, FA, FB, GA, GB, SAr, SBr, SAw, SNw, SSw, SNd, SSd, SBd)      \
-        wait_vm_lgkm0<6>();                                                  \
+        wait_vm_lgkm0<2 * OPS>();                                            \
         block_barrier();                                                     \
         MOE_READ(SAr, SBr, GA, GB);                                          \
         MOE_ISSUE_A(SAw, min((s + S + 4) * BKS, last));                      \
@@ -625,15 +651,15 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_nvfp4_kernel(GemmArgs g) 
             if (row >= r1) continue;
             if (KIND == kGateUp) {
 #pragma unroll
-                for (int ni = 0; ni < 2; ++ni) {
-                    const int col = nt * HALF + (wc >> 1) * 64 + (wc & 1) * 32 + ni * 16 + (lane & 15);
+                for (int ni = 0; ni < NB / 2; ++ni) {
+                    const int col = gcol + ni * 16 + (lane & 15);
                     out[size_t(row) * g.F + col] =
-                        (uint16_t)bf16_rne(silu_mul(acc[mi][ni][i] * gs, acc[mi][ni + 2][i] * gs));
+                        (uint16_t)bf16_rne(silu_mul(acc[mi][ni][i] * gs, acc[mi][ni + NB / 2][i] * gs));
                 }
             } else {
 #pragma unroll
-                for (int ni = 0; ni < 4; ++ni) {
-                    const int col = nt * BN + wc * 64 + ni * 16 + (lane & 15);
+                for (int ni = 0; ni < NB; ++ni) {
+                    const int col = gcol + ni * 16 + (lane & 15);
                     if (col < g.N) out[size_t(row) * g.N + col] = (uint16_t)bf16_rne(acc[mi][ni][i] * gs);
                 }
             }
@@ -1015,9 +1041,9 @@ hipError_t launch_gemm(const GemmArgs& g, int family, int max_tiles, hipStream_t
     } else if (family == kFamPrefill && g.F % 128 == 0) {
         const dim3 grid = prefill_grid(g, max_tiles, 256);
         if (up)
-            hipLaunchKernelGGL((gemm_prefill_nvfp4_kernel<kGateUp>), grid, dim3(512), 0, s, g);
+            hipLaunchKernelGGL((gemm_prefill_nvfp4_kernel<kGateUp, 4>), grid, dim3(256), 0, s, g);
         else
-            hipLaunchKernelGGL((gemm_prefill_nvfp4_kernel<kDown>), grid, dim3(512), 0, s, g);
+            hipLaunchKernelGGL((gemm_prefill_nvfp4_kernel<kDown, 8>), grid, dim3(512), 0, s, g);
     } else if (family == kFamPrefill) {
         launch_mfma<PF_BM, PF_BN, PF_WM, PF_WN>(g, max_tiles, s);
     } else if (g.K % 128 == 0) {
