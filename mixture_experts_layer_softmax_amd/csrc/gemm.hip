@@ -16,7 +16,7 @@
 //                              decoded to bf16 in LDS by the block
 //   gemm_decode_kernel         few rows per expert: weights stream straight into MFMA
 //                              operand registers (bf16 packed, or NVFP4 row-major)
-//   gemm_bf16_kernel           NVFP4 shapes the two above do not tile (F % 128 or K % 128)
+//   gemm_fallback_kernel       NVFP4 shapes the two above do not tile (F % 128 or K % 128)
 //   gemm_f32_kernel            fp32 layers (SIMT)
 // Gate and up rows that feed the same hid column sit in the same wavefront, so SwiGLU is
 // applied to accumulators in registers.  Activation rows are gathered through the dispatch
@@ -70,11 +70,13 @@ __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f +
 
 }  // namespace
 
-// BM x BN block tile, WM x WN wavefronts.  For the gate/up kind the BN weight rows of a block
-// are, per wavefront column, NI/2 16-row groups of gate rows followed by the matching up rows;
-// the block writes BN/2 hid columns.
+// Fallback grouped GEMM for the NVFP4 shapes the kernels below do not tile (F % 128 != 0 for
+// prefill, K % 128 != 0 for decode): BM x BN block tile, WM x WN wavefronts, operands staged
+// through registers into a double-buffered LDS tile (64-wide K slices, XOR-swizzled chunks).
+// For the gate/up kind the BN weight rows of a block are, per wavefront column, NI/2 16-row
+// groups of gate rows followed by the matching up rows; the block writes BN/2 hid columns.
 template <int BM, int BN, int WM, int WN, int KIND, int WFMT>
-__global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmArgs g) {
+__global__ __launch_bounds__(WM* WN * 64) void gemm_fallback_kernel(GemmArgs g) {
     constexpr int NT = WM * WN * 64;
     constexpr int MI = BM / WM / 16;
     constexpr int NI = BN / WN / 16;
@@ -1010,9 +1012,9 @@ static void launch_mfma(const GemmArgs& g, int max_tiles, hipStream_t s) {
     const int ncols = g.kind == kGateUp ? g.F / (BN / 2) : (g.N + BN - 1) / BN;
     dim3 grid(max_tiles, ncols), block(WM * WN * 64);
     if (g.kind == kGateUp)
-        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, kGateUp, kWNVFP4>), grid, block, 0, s, g);
+        hipLaunchKernelGGL((gemm_fallback_kernel<BM, BN, WM, WN, kGateUp, kWNVFP4>), grid, block, 0, s, g);
     else
-        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, kDown, kWNVFP4>), grid, block, 0, s, g);
+        hipLaunchKernelGGL((gemm_fallback_kernel<BM, BN, WM, WN, kDown, kWNVFP4>), grid, block, 0, s, g);
 }
 
 // Work items of the prefill kernels: (row tile, column tile) pairs, a multiple of 8 blocks so

@@ -178,7 +178,7 @@ __global__ __launch_bounds__(kMaxExperts) void select_dispatch_small_kernel(
     __shared__ int sids[kChunkTokens * kMaxTopK];
     __shared__ int cnt[kMaxExperts];
     __shared__ int wc[NW][kMaxExperts];
-    const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+    const int tid = threadIdx.x, w = tid / kWave;
     for (int t = w; t < T; t += NW)
         topk_token<EPL>(logits + size_t(t) * E, E, k, renorm, ids + size_t(t) * k, tw + size_t(t) * k,
                         sids + t * k);
@@ -232,7 +232,6 @@ __global__ __launch_bounds__(kMaxExperts) void select_dispatch_small_kernel(
         }
         __syncthreads();
     }
-    (void)lane;
 }
 
 hipError_t launch_select_dispatch_small(const float* logits, int renorm, int32_t* tw_ids,
