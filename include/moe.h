@@ -26,7 +26,8 @@
  *    once the caller has synchronised the stream.
  *  - Errors are return codes; nothing is thrown and nothing aborts.  All arguments are
  *    validated on the host before any HIP call: MOE_ERR_INVALID_ARGUMENT for a null required
- *    pointer, a misaligned pointer, negative sizes, k < 1, k > E, k > 16 or E > 512;
+ *    pointer, a misaligned pointer, negative sizes, k < 1, k > E, k > 16, E > 512 or an
+ *    expert range outside [0, E);
  *    MOE_ERR_UNSUPPORTED for shapes with no compiled kernel (H % 64, F % 64 != 0; bf16
  *    weights with H % 256 or F % 128 != 0; bf16 activations with fp32 weights or the
  *    reverse; NVFP4 with fp32 activations), and MOE_ERR_INVALID_ARGUMENT for weights not in
@@ -90,7 +91,27 @@ typedef struct {
     int32_t w_dtype;      /* MOE_F32 (with F32 acts) | MOE_BF16 | MOE_NVFP4 (with BF16 acts) */
     int32_t renormalize;  /* 1: softmax over the selected k (default); 0: full softmax */
     int32_t path;         /* moe_path */
+    int32_t expert_begin;  /* expert parallelism: the caller holds the experts           */
+    int32_t local_experts; /* [expert_begin, expert_begin + local_experts); 0 = all E    */
 } moe_problem;
+
+/* Expert parallelism with replicated inputs ("CuTeDSL at Perplexity", section
+ * Mixture-of-Experts Dispatch/Combine: with tensor parallelism every rank sees every token,
+ * its dispatch keeps only the tokens routed to the experts it holds, and a local combine is
+ * followed by an all-reduce across ranks; "Hosting Qwen on Blackwell", section Expert Parallel,
+ * for prefill).  With local_experts = n > 0 the caller holds experts [b, b + n), b =
+ * expert_begin:
+ *  - routing is unchanged: logits, selection and weights always cover all E experts;
+ *  - dispatch keeps only the assignments whose expert is held: counts[e] = 0 for the others,
+ *    offsets[E] = the number of dispatched rows A_local, inv_perm = -1 for every assignment
+ *    that is not dispatched; rows of held experts keep the stable (t, j) order, so they are
+ *    exactly the rows [offsets[b], offsets[b+n]) of the dispatch over all experts;
+ *  - the expert weights (and NVFP4 scales) hold the n experts only: expert e is at index e - b;
+ *  - combine skips assignments with inv_perm < 0, so y is this caller's partial output (zero
+ *    for a token with no held expert).  Summing the partial outputs of a partition of the
+ *    experts (the all-reduce, which is the caller's) gives the layer's output.
+ * Rows of hid, y_perm and x_perm past A_local are unspecified.  expert_begin = local_experts =
+ * 0 (a zero-initialised struct) is the single-GPU layer. */
 
 /* Weight layouts.  bf16 expert weights are consumed in the PACKED layout written by
  * moe_pack_weights; fp32 and NVFP4 expert weights in the ROW_MAJOR layout described below.
@@ -127,6 +148,8 @@ moe_status moe_workspace_size(const moe_problem* p, size_t* bytes);
 
 /* Bytes of the packed w13 and w2 of problem `p` (bf16 weights only).  Host only. */
 moe_status moe_packed_weights_size(const moe_problem* p, size_t* w13_bytes, size_t* w2_bytes);
+/* (both sizes and moe_pack_weights below cover the held experts only: local_experts of them
+ * when it is non-zero, else all E) */
 
 /* Rewrite row-major bf16 expert weights w13 [E,2F,H] and w2 [E,H,F] into the PACKED layout
  * (see moe_layout).  A one-time transform of static weights; the outputs must not alias the
@@ -157,14 +180,16 @@ moe_status moe_permute(const moe_problem* p, const int32_t* topk_ids, int32_t* c
  *                  hid W2[e]^T, in act_dtype.
  * fp32 accumulation; NVFP4 weights are decoded exactly to bf16 inside the kernel.
  * `offsets` [E+1] is read on the device; values are clamped to [0, A] so that a malformed
- * table cannot make the kernel reach past the A rows of `a`/`out`. */
+ * table cannot make the kernel reach past the A rows of `a`/`out`.  Only the rows of held
+ * experts are computed (all experts unless local_experts is set); other rows are untouched. */
 moe_status moe_grouped_gemm(const moe_problem* p, moe_gemm_kind kind, const void* a,
                             const int32_t* a_rows, const int32_t* offsets,
                             const moe_expert_weights* w, void* out, void* workspace,
                             size_t workspace_bytes, void* stream);
 
 /* Combine.  y[t] = sum_j topk_w[t,j] * y_perm[inv_perm[t*k+j]] accumulated in fp32 in
- * ascending j and rounded once to act_dtype.  y_perm [A,H], y [T,H] in act_dtype. */
+ * ascending j and rounded once to act_dtype; assignments with inv_perm < 0 (not dispatched
+ * to this caller's experts) are skipped.  y_perm [A,H], y [T,H] in act_dtype. */
 moe_status moe_combine(const moe_problem* p, const void* y_perm, const int32_t* inv_perm,
                        const float* topk_w, void* y, void* stream);
 

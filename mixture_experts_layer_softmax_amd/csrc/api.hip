@@ -31,6 +31,10 @@ struct Layout {
 
 int act_bytes(const moe_problem& p) { return p.act_dtype == MOE_F32 ? 4 : 2; }
 
+// Held experts [ebegin, eend): all E unless local_experts is set (expert parallelism).
+int ebegin(const moe_problem& p) { return p.local_experts ? p.expert_begin : 0; }
+int eend(const moe_problem& p) { return p.local_experts ? p.expert_begin + p.local_experts : p.num_experts; }
+
 int family_of(const moe_problem& p) {
     if (p.act_dtype == MOE_F32) return kFamSimtF32;
     int path = p.path;
@@ -47,6 +51,10 @@ moe_status check_problem(const moe_problem* p) {
         p->num_experts > kMaxExperts || p->top_k < 1 || p->top_k > kMaxTopK ||
         p->top_k > p->num_experts || (p->renormalize != 0 && p->renormalize != 1) ||
         p->path < MOE_PATH_AUTO || p->path > MOE_PATH_DECODE)
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (p->expert_begin < 0 || p->local_experts < 0 ||
+        long(p->expert_begin) + p->local_experts > p->num_experts ||
+        (p->local_experts == 0 && p->expert_begin != 0))
         return MOE_ERR_INVALID_ARGUMENT;
     if (p->act_dtype != MOE_F32 && p->act_dtype != MOE_BF16) return MOE_ERR_INVALID_ARGUMENT;
     if (p->w_dtype != MOE_F32 && p->w_dtype != MOE_BF16 && p->w_dtype != MOE_NVFP4)
@@ -185,7 +193,7 @@ moe_status moe_workspace_size(const moe_problem* p, size_t* bytes) {
 moe_status moe_packed_weights_size(const moe_problem* p, size_t* w13_bytes, size_t* w2_bytes) {
     MOE_TRY(check_problem(p));
     if (p->w_dtype != MOE_BF16 || !w13_bytes || !w2_bytes) return MOE_ERR_INVALID_ARGUMENT;
-    const size_t E = p->num_experts, H = p->hidden, F = p->ffn;
+    const size_t E = eend(*p) - ebegin(*p), H = p->hidden, F = p->ffn;  // held experts
     *w13_bytes = E * 2 * F * H * 2;
     *w2_bytes = E * H * F * 2;
     return MOE_OK;
@@ -201,8 +209,9 @@ moe_status moe_pack_weights(const moe_problem* p, const void* w13, const void* w
         if (q && !aligned(q)) return MOE_ERR_INVALID_ARGUMENT;
     if ((w13 && w13 == w13_packed) || (w2 && w2 == w2_packed)) return MOE_ERR_INVALID_ARGUMENT;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (w13) MOE_TRY(dev(launch_pack_bf16(w13, w13_packed, 0, p->num_experts, p->ffn, p->hidden, s)));
-    if (w2) MOE_TRY(dev(launch_pack_bf16(w2, w2_packed, 1, p->num_experts, p->ffn, p->hidden, s)));
+    const int held = eend(*p) - ebegin(*p);
+    if (w13) MOE_TRY(dev(launch_pack_bf16(w13, w13_packed, 0, held, p->ffn, p->hidden, s)));
+    if (w2) MOE_TRY(dev(launch_pack_bf16(w2, w2_packed, 1, held, p->ffn, p->hidden, s)));
     return MOE_OK;
 }
 
@@ -239,7 +248,7 @@ moe_status moe_permute(const moe_problem* p, const int32_t* topk_ids, int32_t* c
     const Layout L = layout(*p);
     DispatchArgs d{topk_ids, p->num_tokens, p->top_k, p->num_experts, at<int32_t>(workspace, L.hist),
                    at<int32_t>(workspace, L.base), counts, offsets, sorted_token, inv_perm,
-                   nullptr, nullptr, 0, nullptr, nullptr, 0, L.max_tiles};
+                   nullptr, nullptr, 0, nullptr, nullptr, 0, L.max_tiles, ebegin(*p), eend(*p)};
     MOE_TRY(dev(launch_dispatch(d, s)));
     if (x)
         MOE_TRY(dev(launch_gather_rows(x, sorted_token, x_perm, p->num_tokens * p->top_k,
@@ -264,8 +273,9 @@ moe_status moe_grouped_gemm(const moe_problem* p, moe_gemm_kind kind, const void
     hipStream_t s = static_cast<hipStream_t>(stream);
     Tile* tiles = at<Tile>(workspace, L.tiles1);
     int* tcount = at<int>(workspace, L.tcount);
-    MOE_TRY(dev(launch_tiles_from_offsets(offsets, p->num_experts, p->num_tokens * p->top_k, L.bm,
-                                          tiles, tcount, L.max_tiles, s)));
+    MOE_TRY(dev(launch_tiles_from_offsets(offsets, p->num_experts, ebegin(*p), eend(*p),
+                                          p->num_tokens * p->top_k, L.bm, tiles, tcount,
+                                          L.max_tiles, s)));
     GemmArgs g = gemm_args(*p, kind == MOE_GEMM_GATE_UP_SWIGLU ? kGateUp : kDown, a, a_rows, tiles,
                            tcount, *w, out);
     return dev(launch_gemm(g, L.family, L.max_tiles, s));
@@ -314,7 +324,7 @@ moe_status moe_forward(const moe_problem* p, const void* x, const void* w_router
 
     DispatchArgs d{ids, p->num_tokens, p->top_k, p->num_experts, at<int32_t>(workspace, L.hist),
                    at<int32_t>(workspace, L.base), counts, off, st, ip, tiles, tcount, L.bm,
-                   nullptr, nullptr, 0, L.max_tiles};
+                   nullptr, nullptr, 0, L.max_tiles, ebegin(*p), eend(*p)};
     // up to 8 tokens (one per wavefront of the dispatch block): logits, then selection and
     // dispatch in one single-block launch; larger batches select with one wavefront per token
     if (p->num_tokens <= kMaxExperts / kWave) {

@@ -4,7 +4,9 @@
 // kernel uses the positions dispatch assigned to gather a token's expert rows and accumulates
 // them in registers with vectorised accesses, then writes the final token.  Here: one block
 // per token, 16-byte loads of y_perm rows, fp32 accumulation in ascending slot order, one
-// rounding to the output type.
+// rounding to the output type.  Slots with a negative row were not dispatched here (their
+// expert is held by another rank under expert parallelism) and are skipped, so the result is
+// the local part of the combine that the pages follow with an all-reduce.
 #include "device.h"
 #include "launch.h"
 
@@ -18,16 +20,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
     const int t = blockIdx.x;
     int rows[kMaxTopK];
     float ws[kMaxTopK];
+    int n = 0;  // dispatched slots of this token, in ascending j
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j) {
-        if (j < k) {
-            int r = inv_perm[size_t(t) * k + j];
-            rows[j] = r < 0 ? 0 : (r >= A ? A - 1 : r);
-            ws[j] = w[size_t(t) * k + j];
-        } else {
-            rows[j] = 0;
-            ws[j] = 0.0f;
-        }
+        rows[j] = 0;
+        ws[j] = 0.0f;
+    }
+    for (int j = 0; j < k; ++j) {
+        const int r = inv_perm[size_t(t) * k + j];
+        if (r < 0) continue;
+        rows[n] = r >= A ? A - 1 : r;
+        ws[n] = w[size_t(t) * k + j];
+        ++n;
     }
     if (BF16) {
         const uint4* src = static_cast<const uint4*>(y_perm);
@@ -35,7 +39,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
         const int nv = H / 8;
         for (int v = threadIdx.x; v < nv; v += blockDim.x) {
             float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            for (int j = 0; j < k; ++j) {
+            for (int j = 0; j < n; ++j) {
                 const uint4 q = src[size_t(rows[j]) * nv + v];
                 const uint32_t u[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
@@ -53,7 +57,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
         const int nv = H / 4;
         for (int v = threadIdx.x; v < nv; v += blockDim.x) {
             float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-            for (int j = 0; j < k; ++j) {
+            for (int j = 0; j < n; ++j) {
                 const float4 q = src[size_t(rows[j]) * nv + v];
                 acc.x = __builtin_fmaf(ws[j], q.x, acc.x);
                 acc.y = __builtin_fmaf(ws[j], q.y, acc.y);

@@ -33,6 +33,7 @@ struct DispatchArgs {
     int* tile_count2;
     int bm2;
     int tile_cap;        // capacity of each tile list
+    int ebegin, eend;    // held experts [ebegin, eend): only their assignments are dispatched
 };
 
 enum GemmKind { kGateUp = 0, kDown = 1 };
@@ -64,7 +65,7 @@ hipError_t launch_dispatch(const DispatchArgs& d, hipStream_t s);
 hipError_t launch_select_dispatch_small(const float* logits, int renorm, int32_t* tw_ids, float* tw,
                                         const DispatchArgs& d, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int n, int value, hipStream_t s);
-hipError_t launch_tiles_from_offsets(const int32_t* offsets, int E, int A, int bm, Tile* tiles,
+hipError_t launch_tiles_from_offsets(const int32_t* offsets, int E, int eb, int ee, int A, int bm, Tile* tiles,
                                      int* tile_count, int cap, hipStream_t s);
 hipError_t launch_gather_rows(const void* x, const int32_t* sorted_token, void* x_perm, int A,
                               int T, int row_bytes, hipStream_t s);

@@ -18,15 +18,17 @@ namespace moe {
 // hist[c, e] = number of assignments of chunk c routed to expert e (integer atomics on LDS:
 // the counts do not depend on their order).
 __global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ ids, int T, int k,
-                                                   int E, int32_t* __restrict__ hist) {
+                                                   int E, int eb, int ee, int32_t* __restrict__ hist) {
     __shared__ int cnt[kMaxExperts];
     const int c = blockIdx.x;
     for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
     __syncthreads();
     const int a0 = c * kChunkTokens * k;
     const int a1 = min(T, (c + 1) * kChunkTokens) * k;
-    for (int a = a0 + threadIdx.x; a < a1; a += blockDim.x)
-        atomicAdd(&cnt[clamp_expert(ids[a], E)], 1);
+    for (int a = a0 + threadIdx.x; a < a1; a += blockDim.x) {
+        const int id = clamp_expert(ids[a], E);
+        if (id >= eb && id < ee) atomicAdd(&cnt[id], 1);  // only held experts are dispatched
+    }
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += blockDim.x) hist[size_t(c) * E + e] = cnt[e];
 }
@@ -42,7 +44,7 @@ __global__ __launch_bounds__(kMaxExperts) void scan_kernel(const int32_t* __rest
                                                            int32_t* __restrict__ offsets,
                                                            Tile* tiles1, int* tile_count1, int bm1,
                                                            Tile* tiles2, int* tile_count2,
-                                                           int bm2, int cap) {
+                                                           int bm2, int cap, int eb) {
     constexpr int kBatch = 32;
     const int e = threadIdx.x;
     int run = 0;
@@ -73,30 +75,31 @@ __global__ __launch_bounds__(kMaxExperts) void scan_kernel(const int32_t* __rest
         }
     }
     if (e == 0) offsets[E] = total;
-    if (tiles1) emit_tiles(e, E, run, start, bm1, tiles1, tile_count1, cap);
-    if (tiles2) emit_tiles(e, E, run, start, bm2, tiles2, tile_count2, cap);
+    if (tiles1) emit_tiles(e, E, run, start, bm1, tiles1, tile_count1, cap, eb);
+    if (tiles2) emit_tiles(e, E, run, start, bm2, tiles2, tile_count2, cap, eb);
 }
 
 // Tile list straight from caller-supplied offsets (stand-alone grouped GEMM entry point).
 // Offsets are clamped to [0, A] so that no tile reaches past the A dispatched rows.
 __global__ __launch_bounds__(kMaxExperts) void tiles_from_offsets_kernel(
-    const int32_t* __restrict__ offsets, int E, int A, int bm, Tile* tiles, int* tile_count,
-    int cap) {
+    const int32_t* __restrict__ offsets, int E, int eb, int ee, int A, int bm, Tile* tiles,
+    int* tile_count, int cap) {
     const int e = threadIdx.x;
     int start = 0, count = 0;
-    if (e < E) {
+    if (e >= eb && e < ee) {  // rows of experts that are not held are never computed
         start = min(max(offsets[e], 0), A);
         const int end = min(max(offsets[e + 1], start), A);
         count = end - start;
     }
-    emit_tiles(e, E, count, start, bm, tiles, tile_count, cap);
+    emit_tiles(e, E, count, start, bm, tiles, tile_count, cap, eb);
 }
 
 // Stable scatter of one chunk.  Assignments are taken 256 at a time in (t, j) order; within a
 // wave, lanes holding the same expert find each other with one ballot per id bit, and wave
 // totals are prefix-summed across the 4 waves through LDS.
 __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict__ ids, int T, int k,
-                                                      int E, const int32_t* __restrict__ base,
+                                                      int E, int eb, int ee,
+                                                      const int32_t* __restrict__ base,
                                                       int32_t* __restrict__ sorted_token,
                                                       int32_t* __restrict__ inv_perm) {
     __shared__ int cnt[kMaxExperts];
@@ -112,8 +115,10 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
         for (int i = threadIdx.x; i < 4 * kMaxExperts; i += blockDim.x) (&wc[0][0])[i] = 0;
         __syncthreads();
         const int a = r0 + threadIdx.x;
-        const bool valid = a < a1;
-        const int id = valid ? clamp_expert(ids[a], E) : 0;
+        const int id0 = a < a1 ? clamp_expert(ids[a], E) : 0;
+        const bool valid = a < a1 && id0 >= eb && id0 < ee;
+        if (a < a1 && !valid) inv_perm[a] = -1;  // routed to an expert that is not held
+        const int id = valid ? id0 : 0;
         uint64_t peers = __ballot(valid);
         for (int b = 0; b < nbits; ++b) {
             const bool bit = (id >> b) & 1;
@@ -173,7 +178,7 @@ __global__ __launch_bounds__(kMaxExperts) void select_dispatch_small_kernel(
     const float* __restrict__ logits, int T, int E, int k, int renorm, int32_t* __restrict__ ids,
     float* __restrict__ tw, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ sorted_token, int32_t* __restrict__ inv_perm, Tile* tiles1,
-    int* tile_count1, int bm1, Tile* tiles2, int* tile_count2, int bm2, int cap) {
+    int* tile_count1, int bm1, Tile* tiles2, int* tile_count2, int bm2, int cap, int eb, int ee) {
     constexpr int NW = kMaxExperts / kWave;
     __shared__ int sids[kChunkTokens * kMaxTopK];
     __shared__ int cnt[kMaxExperts];
@@ -185,7 +190,10 @@ __global__ __launch_bounds__(kMaxExperts) void select_dispatch_small_kernel(
     if (tid < E) cnt[tid] = 0;
     __syncthreads();
     const int A = T * k;
-    for (int a = tid; a < A; a += kMaxExperts) atomicAdd(&cnt[clamp_expert(sids[a], E)], 1);
+    for (int a = tid; a < A; a += kMaxExperts) {
+        const int id = clamp_expert(sids[a], E);
+        if (id >= eb && id < ee) atomicAdd(&cnt[id], 1);
+    }
     __syncthreads();
     const int c = tid < E ? cnt[tid] : 0;
     int total;
@@ -195,8 +203,8 @@ __global__ __launch_bounds__(kMaxExperts) void select_dispatch_small_kernel(
         offsets[tid] = start;
     }
     if (tid == 0) offsets[E] = total;
-    if (tiles1) emit_tiles(tid, E, c, start, bm1, tiles1, tile_count1, cap);
-    if (tiles2) emit_tiles(tid, E, c, start, bm2, tiles2, tile_count2, cap);
+    if (tiles1) emit_tiles(tid, E, c, start, bm1, tiles1, tile_count1, cap, eb);
+    if (tiles2) emit_tiles(tid, E, c, start, bm2, tiles2, tile_count2, cap, eb);
     __syncthreads();
     if (tid < E) cnt[tid] = start;  // next free row of each expert
     int nbits = 0;
@@ -205,8 +213,10 @@ __global__ __launch_bounds__(kMaxExperts) void select_dispatch_small_kernel(
         for (int i = tid; i < NW * kMaxExperts; i += kMaxExperts) (&wc[0][0])[i] = 0;
         __syncthreads();
         const int a = r0 + tid;
-        const bool valid = a < A;
-        const int id = valid ? clamp_expert(sids[a], E) : 0;
+        const int id0 = a < A ? clamp_expert(sids[a], E) : 0;
+        const bool valid = a < A && id0 >= eb && id0 < ee;
+        if (a < A && !valid) inv_perm[a] = -1;
+        const int id = valid ? id0 : 0;
         uint64_t peers = __ballot(valid);
         for (int b = 0; b < nbits; ++b) {
             const bool bit = (id >> b) & 1;
@@ -241,7 +251,7 @@ hipError_t launch_select_dispatch_small(const float* logits, int renorm, int32_t
     hipLaunchKernelGGL((select_dispatch_small_kernel<N>), dim3(1), dim3(kMaxExperts), 0, s, logits, \
                        d.T, d.E, d.k, renorm, tw_ids, tw, d.counts, d.offsets, d.sorted_token,      \
                        d.inv_perm, d.tiles1, d.tile_count1, d.bm1, d.tiles2, d.tile_count2, d.bm2,  \
-                       d.tile_cap)
+                       d.tile_cap, d.ebegin, d.eend)
     if (epl <= 1) MOE_SDS(1);
     else if (epl <= 2) MOE_SDS(2);
     else if (epl <= 4) MOE_SDS(4);
@@ -252,19 +262,20 @@ hipError_t launch_select_dispatch_small(const float* logits, int renorm, int32_t
 
 hipError_t launch_dispatch(const DispatchArgs& d, hipStream_t s) {
     const int nch = (d.T + kChunkTokens - 1) / kChunkTokens;
-    hipLaunchKernelGGL(hist_kernel, dim3(nch), dim3(256), 0, s, d.ids, d.T, d.k, d.E, d.hist);
+    hipLaunchKernelGGL(hist_kernel, dim3(nch), dim3(256), 0, s, d.ids, d.T, d.k, d.E, d.ebegin, d.eend,
+                       d.hist);
     hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kMaxExperts), 0, s, d.hist, nch, d.E, d.base,
                        d.counts, d.offsets, d.tiles1, d.tile_count1, d.bm1, d.tiles2,
-                       d.tile_count2, d.bm2, d.tile_cap);
-    hipLaunchKernelGGL(scatter_kernel, dim3(nch), dim3(256), 0, s, d.ids, d.T, d.k, d.E, d.base,
-                       d.sorted_token, d.inv_perm);
+                       d.tile_count2, d.bm2, d.tile_cap, d.ebegin);
+    hipLaunchKernelGGL(scatter_kernel, dim3(nch), dim3(256), 0, s, d.ids, d.T, d.k, d.E, d.ebegin,
+                       d.eend, d.base, d.sorted_token, d.inv_perm);
     return hipGetLastError();
 }
 
-hipError_t launch_tiles_from_offsets(const int32_t* offsets, int E, int A, int bm, Tile* tiles,
-                                     int* tile_count, int cap, hipStream_t s) {
-    hipLaunchKernelGGL(tiles_from_offsets_kernel, dim3(1), dim3(kMaxExperts), 0, s, offsets, E, A,
-                       bm, tiles, tile_count, cap);
+hipError_t launch_tiles_from_offsets(const int32_t* offsets, int E, int eb, int ee, int A, int bm,
+                                     Tile* tiles, int* tile_count, int cap, hipStream_t s) {
+    hipLaunchKernelGGL(tiles_from_offsets_kernel, dim3(1), dim3(kMaxExperts), 0, s, offsets, E, eb,
+                       ee, A, bm, tiles, tile_count, cap);
     return hipGetLastError();
 }
 

@@ -99,16 +99,17 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ row, int E,
 }
 
 // Write the tile list of one grouped GEMM with row-tile height bm from per-expert counts
-// (thread e handles expert e; `start` = exclusive row offset of expert e).
-// At most `cap` tiles are written (a bound that valid counts never reach).
+// (thread e handles expert e; `start` = exclusive row offset of expert e).  A tile names its
+// expert by weight index e - ebase (the caller's first held expert; experts not held have no
+// rows).  At most `cap` tiles are written (a bound that valid counts never reach).
 __device__ __forceinline__ void emit_tiles(int e, int E, int count, int start, int bm, Tile* tiles,
-                           int* tile_count, int cap) {
+                           int* tile_count, int cap, int ebase) {
     const int nt = (e < E) ? (count + bm - 1) / bm : 0;
     int total;
     const int first = block_exclusive_scan<kMaxExperts>(nt, &total);
     for (int i = 0; i < nt && first + i < cap; ++i) {
         Tile t;
-        t.expert = e;
+        t.expert = e - ebase;
         t.row0 = start + i * bm;
         t.row1 = min(start + count, start + (i + 1) * bm);
         t.pad = 0;

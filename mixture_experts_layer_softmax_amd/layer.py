@@ -37,12 +37,15 @@ def bf16_bits_to_f64(a: np.ndarray) -> np.ndarray:
 
 class MoELayer:
     def __init__(self, tokens, hidden, experts, top_k, ffn, act, wdt, inputs: dict,
-                 device="cuda:0", renormalize=True, path="auto"):
+                 device="cuda:0", renormalize=True, path="auto", expert_begin=0, local_experts=0):
+        """``inputs`` holds the weights of the held experts only when ``local_experts`` is set
+        (expert parallelism: experts [expert_begin, expert_begin + local_experts))."""
         self.device = torch.device(device)
         self.T, self.H, self.E, self.k, self.F = tokens, hidden, experts, top_k, ffn
         self.act, self.wdt = act, wdt
         self.renormalize, self.path = renormalize, path
-        self.problem = lib.problem(tokens, hidden, experts, top_k, ffn, act, wdt, renormalize, path)
+        self.expert_begin, self.local_experts = expert_begin, local_experts
+        self.problem = self.problem_for(tokens)
         d = self.device
         self.w_router = to_device(inputs["w_router"], d, "bf16" if act == "bf16" else None)
         self.bias = to_device(inputs.get("bias"), d)
@@ -67,13 +70,16 @@ class MoELayer:
         self.ws = None
 
     @classmethod
-    def from_workload(cls, wl, inputs, device="cuda:0", path="auto"):
+    def from_workload(cls, wl, inputs, device="cuda:0", path="auto", expert_begin=0,
+                      local_experts=0):
         return cls(wl.tokens, wl.hidden, wl.experts, wl.top_k, wl.ffn, wl.act, wl.wdt, inputs,
-                   device=device, renormalize=wl.renormalize, path=path)
+                   device=device, renormalize=wl.renormalize, path=path,
+                   expert_begin=expert_begin, local_experts=local_experts)
 
     def problem_for(self, tokens: int, path: str | None = None):
         return lib.problem(tokens, self.H, self.E, self.k, self.F, self.act, self.wdt,
-                           self.renormalize, path or self.path)
+                           self.renormalize, path or self.path, self.expert_begin,
+                           self.local_experts)
 
     def workspace(self, tokens: int, path: str | None = None) -> torch.Tensor:
         n = lib.workspace_size(self.problem_for(tokens, path))

@@ -37,7 +37,8 @@ class MoeError(RuntimeError):
 class Problem(C.Structure):
     _fields_ = [("num_tokens", C.c_int32), ("hidden", C.c_int32), ("num_experts", C.c_int32),
                 ("top_k", C.c_int32), ("ffn", C.c_int32), ("act_dtype", C.c_int32),
-                ("w_dtype", C.c_int32), ("renormalize", C.c_int32), ("path", C.c_int32)]
+                ("w_dtype", C.c_int32), ("renormalize", C.c_int32), ("path", C.c_int32),
+                ("expert_begin", C.c_int32), ("local_experts", C.c_int32)]
 
 
 class ExpertWeights(C.Structure):
@@ -93,9 +94,12 @@ def status_string(s: int) -> str:
 
 
 def problem(tokens, hidden, experts, top_k, ffn, act="bf16", wdt="bf16", renormalize=True,
-            path="auto") -> Problem:
+            path="auto", expert_begin=0, local_experts=0) -> Problem:
+    """``expert_begin``/``local_experts``: the held expert range under expert parallelism
+    (0/0 = all experts)."""
     return Problem(int(tokens), int(hidden), int(experts), int(top_k), int(ffn), DTYPES[act],
-                   DTYPES[wdt], int(bool(renormalize)), PATHS[path])
+                   DTYPES[wdt], int(bool(renormalize)), PATHS[path], int(expert_begin),
+                   int(local_experts))
 
 
 def _ptr(t):

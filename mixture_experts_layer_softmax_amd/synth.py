@@ -6,7 +6,7 @@ per-expert fp32 global scale).  It holds none of the layer's arithmetic: no logi
 selection, no permutation, no expert FFN, no decoding of the 4-bit format.  Both the GPU
 library and the CPU oracle read exactly the bytes returned here.
 
-Workloads (the five layer shapes this library is measured on):
+Workloads (the layer shapes this library is measured on):
 
 =============== ======= ====== ==== === ==== ================ ========================
 name            tokens  hidden  E    k   F    weights/acts     router bias
@@ -16,7 +16,12 @@ prefill         4096    4096    128  8   1536 bf16 / bf16      b_e ~ N(0,1) (ske
 decode{1,8,64}  1/8/64  4096    128  8   1536 bf16 / bf16      none
 nvfp4_decode    16      4096    256  8   2048 nvfp4 / bf16     none
 nvfp4_prefill   8192    4096    256  8   2048 nvfp4 / bf16     +beta on a 10 % hot set
+prefill6000     6000    4096    128  8   1536 bf16 / bf16      none (about 375 rows/expert)
 =============== ======= ====== ==== === ==== ================ ========================
+
+``prefill6000`` is the prefill example of "Hosting Qwen on Blackwell" (section Prefill: an
+input of about 6000 tokens gives about 375 tokens per expert); run with a held expert range it
+is one expert-parallel rank's share of that prefill.
 
 Distributions: activations N(0,1); router, gate/up and down weights N(0, 0.02).
 Random streams: ``numpy.random.default_rng([seed, tensor_id, sub])`` drawing float32
@@ -79,6 +84,7 @@ WORKLOADS = {
     "decode64": Workload("decode64", 64, 4096, 128, 8, 1536, "bf16", "bf16", 303, "none", x_sub=64),
     "nvfp4_decode": Workload("nvfp4_decode", 16, 4096, 256, 8, 2048, "bf16", "nvfp4", 404, "none"),
     "nvfp4_prefill": Workload("nvfp4_prefill", 8192, 4096, 256, 8, 2048, "bf16", "nvfp4", 505, "hot"),
+    "prefill6000": Workload("prefill6000", 6000, 4096, 128, 8, 1536, "bf16", "bf16", 606, "none"),
 }
 
 T_X, T_WR, T_BIAS, T_W13, T_W2, T_HOT = range(6)

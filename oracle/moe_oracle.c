@@ -20,6 +20,12 @@
  *           a = t*k + j by expert: sorted_token[pos] = t, inv_perm[a] = pos.
  *  expert   SwiGLU FFN (SiLU(gate) * up, then down), gate rows first in W13; no biases.
  *  combine  y[t] = sum_j w[t,j] * y_perm[inv_perm[t*k+j]].
+ *  held     expert parallelism with replicated inputs (same article, same section: with
+ *           tensor parallelism the local dispatch selects only the tokens routed to the
+ *           experts of the current rank, and the local combine is followed by an all-reduce):
+ *           given a held range [eb, ee), permute keeps only assignments whose expert lies in
+ *           it (the others get inv_perm = -1 and no row), and combine skips them, so y is the
+ *           rank's partial sum.  eb = 0, ee = E is the single-GPU layer.
  *
  * Floating point: every value is decoded exactly into double (its own bf16 / E2M1 / E4M3
  * decoders) and every sum after routing is accumulated in double.  Parity pins: see the tests.
@@ -183,16 +189,21 @@ void oracle_select(int64_t T, int64_t E, int k, const float* logits, int renorm,
 /* permute                                                                                */
 /* ------------------------------------------------------------------------------------ */
 
-void oracle_permute(int64_t T, int k, int64_t E, const int32_t* ids, int32_t* counts,
-                    int32_t* offsets, int32_t* sorted_token, int32_t* inv_perm) {
+void oracle_permute(int64_t T, int k, int64_t E, int64_t eb, int64_t ee, const int32_t* ids,
+                    int32_t* counts, int32_t* offsets, int32_t* sorted_token, int32_t* inv_perm) {
     int64_t A = T * k;
     for (int64_t e = 0; e < E; ++e) counts[e] = 0;
-    for (int64_t a = 0; a < A; ++a) counts[ids[a]] += 1;
+    for (int64_t a = 0; a < A; ++a)
+        if (ids[a] >= eb && ids[a] < ee) counts[ids[a]] += 1;
     offsets[0] = 0;
     for (int64_t e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
     int32_t* next = (int32_t*)malloc(sizeof(int32_t) * (size_t)(E > 0 ? E : 1));
     for (int64_t e = 0; e < E; ++e) next[e] = offsets[e];
     for (int64_t a = 0; a < A; ++a) { /* row-major (t, j) order: stable */
+        if (ids[a] < eb || ids[a] >= ee) { /* expert not held: not dispatched */
+            inv_perm[a] = -1;
+            continue;
+        }
         int32_t pos = next[ids[a]]++;
         sorted_token[pos] = (int32_t)(a / k);
         inv_perm[a] = pos;
@@ -307,7 +318,8 @@ void oracle_combine(int64_t T, int k, int64_t H, const double* y_perm, const int
     for (int64_t t = 0; t < T; ++t)
         for (int64_t h = 0; h < H; ++h) {
             double s = 0.0;
-            for (int j = 0; j < k; ++j) s += w[t * k + j] * y_perm[(int64_t)inv_perm[t * k + j] * H + h];
+            for (int j = 0; j < k; ++j)
+                if (inv_perm[t * k + j] >= 0) s += w[t * k + j] * y_perm[(int64_t)inv_perm[t * k + j] * H + h];
             y[t * H + h] = s;
         }
 }

@@ -54,7 +54,7 @@ def lib() -> C.CDLL:
             L.oracle_logit.argtypes = [vp, vp, i32, i64, i32, C.c_float]
             L.oracle_router_logits.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp]
             L.oracle_select.argtypes = [i64, i64, i32, vp, i32, vp, vp]
-            L.oracle_permute.argtypes = [i64, i32, i64, vp, vp, vp, vp, vp]
+            L.oracle_permute.argtypes = [i64, i32, i64, i64, i64, vp, vp, vp, vp, vp]
             L.oracle_expert_rows.argtypes = [i64, i64, i32, i32, vp, vp, vp, vp, vp, vp, vp, i64,
                                              vp, vp, vp, vp]
             L.oracle_down_rows.argtypes = [i64, i64, i32, vp, vp, vp, i64, vp, vp, vp]
@@ -135,15 +135,27 @@ def select(logits: np.ndarray, k: int, renormalize: bool = True):
     return ids, w
 
 
-def permute(ids: np.ndarray, num_experts: int):
+def _held(num_experts: int, held):
+    if held is None:
+        return 0, num_experts
+    b, n = int(held[0]), int(held[1])
+    assert 0 <= b and 0 < n and b + n <= num_experts
+    return b, b + n
+
+
+def permute(ids: np.ndarray, num_experts: int, held=None):
+    """Dispatch; ``held = (begin, count)`` keeps only the assignments of experts
+    [begin, begin + count) (expert parallelism), the others get inv_perm = -1.
+    ``sorted_token`` has offsets[E] meaningful entries."""
     ids = np.ascontiguousarray(ids, dtype=np.int32)
     T, k = ids.shape
     A = T * k
+    eb, ee = _held(num_experts, held)
     counts = np.empty(num_experts, dtype=np.int32)
     offsets = np.empty(num_experts + 1, dtype=np.int32)
-    sorted_token = np.empty(A, dtype=np.int32)
+    sorted_token = np.full(A, -1, dtype=np.int32)
     inv_perm = np.empty(A, dtype=np.int32)
-    lib().oracle_permute(T, int(k), num_experts, _P(ids), _P(counts), _P(offsets),
+    lib().oracle_permute(T, int(k), num_experts, eb, ee, _P(ids), _P(counts), _P(offsets),
                          _P(sorted_token), _P(inv_perm))
     return counts, offsets, sorted_token, inv_perm
 
@@ -202,33 +214,40 @@ def combine(y_perm: np.ndarray, inv_perm: np.ndarray, w: np.ndarray) -> np.ndarr
     return y
 
 
-def route(inputs: dict, top_k: int, renormalize: bool = True) -> dict:
-    """Router logits, selection, weights and the dispatch permutation of every token."""
+def route(inputs: dict, top_k: int, renormalize: bool = True, held=None) -> dict:
+    """Router logits, selection, weights and the dispatch permutation of every token
+    (``held``: see permute)."""
     logits = router_logits(inputs["x"], inputs["w_router"], inputs.get("bias"))
     E = logits.shape[1]
     ids, w = select(logits, top_k, renormalize)
-    counts, offsets, sorted_token, inv_perm = permute(ids, E)
+    counts, offsets, sorted_token, inv_perm = permute(ids, E, held)
     return dict(logits=logits, topk_ids=ids, topk_w=w, counts=counts, offsets=offsets,
                 sorted_token=sorted_token, inv_perm=inv_perm)
 
 
 def forward(inputs: dict, top_k: int, wdt: str, ffn: int, renormalize: bool = True,
-            tokens=None, routed: dict | None = None) -> dict:
+            tokens=None, routed: dict | None = None, held=None) -> dict:
     """The whole layer.  ``tokens`` (optional) restricts the expert FFN and combine to a
     sample of tokens; routing and dispatch always cover every token.  ``y`` then has one row
-    per sampled token, in the order given."""
-    r = routed if routed is not None else route(inputs, top_k, renormalize)
+    per sampled token, in the order given.  ``held = (begin, count)``: expert parallelism, the
+    inputs hold the weights of experts [begin, begin + count) only and ``y`` is this share's
+    partial output (see permute)."""
+    r = routed if routed is not None else route(inputs, top_k, renormalize, held)
     T = r["topk_ids"].shape[0]
+    eb = 0 if held is None else int(held[0])
     toks = np.arange(T, dtype=np.int64) if tokens is None else np.asarray(tokens, dtype=np.int64)
     k = top_k
     # rows of the permuted buffer that the chosen tokens own, found through inv_perm
     slots = (toks[:, None] * k + np.arange(k)[None, :]).ravel()
-    pos = r["inv_perm"][slots]
+    pos_all = r["inv_perm"][slots]
+    kept = pos_all >= 0
+    pos = pos_all[kept]
     expert_of_pos = np.searchsorted(r["offsets"], pos, side="right") - 1
-    rows = expert_rows(inputs, wdt, ffn, r["sorted_token"][pos], expert_of_pos)
-    # combine through a compact y_perm holding just those rows
-    local = np.arange(pos.size, dtype=np.int32).reshape(toks.size, k)
-    y = combine(rows, local, r["topk_w"][toks])
+    rows = expert_rows(inputs, wdt, ffn, r["sorted_token"][pos], expert_of_pos - eb)
+    # combine through a compact y_perm holding just those rows (-1: not dispatched here)
+    local = np.full(pos_all.size, -1, dtype=np.int32)
+    local[kept] = np.arange(pos.size, dtype=np.int32)
+    y = combine(rows, local.reshape(toks.size, k), r["topk_w"][toks])
     out = dict(r)
     out.update(y=y, tokens=toks)
     return out

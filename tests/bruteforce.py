@@ -68,8 +68,9 @@ def select(logits, k, renormalize=True):
     return ids, w
 
 
-def layer(inputs, logits, k, wdt, renormalize=True):
-    """y[T,H] in fp64, one token at a time."""
+def layer(inputs, logits, k, wdt, renormalize=True, keep=None):
+    """y[T,H] in fp64, one token at a time.  ``keep(e)`` (optional) limits the sum to the
+    experts it accepts (one rank's share under expert parallelism)."""
     x = act_f64(inputs["x"])
     w13, w2 = dense_weights(inputs, wdt)
     F = w2.shape[2]
@@ -78,6 +79,8 @@ def layer(inputs, logits, k, wdt, renormalize=True):
     for t in range(x.shape[0]):
         for j in range(k):
             e = ids[t, j]
+            if keep is not None and not keep(e):
+                continue
             g = w13[e, :F] @ x[t]
             u = w13[e, F:] @ x[t]
             h = g / (1.0 + np.exp(-g)) * u

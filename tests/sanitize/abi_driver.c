@@ -56,6 +56,20 @@ int main(void) {
 
     EXPECT(moe_packed_weights_size(&ok, &a, &b), MOE_OK);
     if (a != (size_t)8 * 2 * 128 * 256 * 2 || b != (size_t)8 * 256 * 128 * 2) g_bad = 1;
+
+    /* held expert ranges (expert parallelism) */
+    p = ok; p.expert_begin = 2;                      /* a start without a count */
+    EXPECT(moe_workspace_size(&p, &n), MOE_ERR_INVALID_ARGUMENT);
+    p = ok; p.expert_begin = 4; p.local_experts = 5; /* past E */
+    EXPECT(moe_workspace_size(&p, &n), MOE_ERR_INVALID_ARGUMENT);
+    p = ok; p.expert_begin = -1; p.local_experts = 2;
+    EXPECT(moe_workspace_size(&p, &n), MOE_ERR_INVALID_ARGUMENT);
+    p = ok; p.local_experts = -1;
+    EXPECT(moe_workspace_size(&p, &n), MOE_ERR_INVALID_ARGUMENT);
+    p = ok; p.expert_begin = 4; p.local_experts = 4;
+    EXPECT(moe_workspace_size(&p, &n), MOE_OK);
+    EXPECT(moe_packed_weights_size(&p, &a, &b), MOE_OK); /* the 4 held experts only */
+    if (a != (size_t)4 * 2 * 128 * 256 * 2 || b != (size_t)4 * 256 * 128 * 2) g_bad = 1;
     EXPECT(moe_pack_weights(&ok, FAKE, NULL, FAKE, NULL, NULL), MOE_ERR_INVALID_ARGUMENT);
     EXPECT(moe_pack_weights(&ok, MIS, NULL, FAKE, NULL, NULL), MOE_ERR_INVALID_ARGUMENT);
 

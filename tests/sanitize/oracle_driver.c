@@ -13,8 +13,8 @@ void oracle_router_logits(int64_t T, int64_t H, int64_t E, int dt, const void* x
                           const float* bias, float* logits);
 void oracle_select(int64_t T, int64_t E, int k, const float* logits, int renorm, int32_t* ids,
                    double* w);
-void oracle_permute(int64_t T, int k, int64_t E, const int32_t* ids, int32_t* counts,
-                    int32_t* offsets, int32_t* sorted_token, int32_t* inv_perm);
+void oracle_permute(int64_t T, int k, int64_t E, int64_t eb, int64_t ee, const int32_t* ids,
+                    int32_t* counts, int32_t* offsets, int32_t* sorted_token, int32_t* inv_perm);
 void oracle_expert_rows(int64_t H, int64_t F, int act_dt, int wdt, const void* x, const void* w13,
                         const void* w2, const uint8_t* w13_scale, const uint8_t* w2_scale,
                         const float* w13_gscale, const float* w2_gscale, int64_t nrows,
@@ -96,7 +96,7 @@ static int run_case(int T, int H, int E, int k, int F, int act, int wdt, int ren
 
     oracle_router_logits(T, H, E, act, x, wr, bias, logits);
     oracle_select(T, E, k, logits, renorm, ids, w);
-    oracle_permute(T, k, E, ids, counts, offsets, st, ip);
+    oracle_permute(T, k, E, 0, E, ids, counts, offsets, st, ip);
     for (int e = 0; e < E; ++e)
         for (int r = offsets[e]; r < offsets[e + 1]; ++r) rexp[r] = e;
     oracle_expert_rows(H, F, act, wdt, x, w13, w2, s13, s2, g13, g2, A, st, rexp, yperm, hid);
@@ -113,6 +113,21 @@ static int run_case(int T, int H, int E, int k, int F, int act, int wdt, int ren
     }
     for (int64_t i = 0; i < (int64_t)T * H; ++i)
         if (!isfinite(y[i])) bad = 1;
+    /* a held expert range (expert parallelism): upper half of the experts */
+    {
+        const int eb = E / 2;
+        oracle_permute(T, k, E, eb, E, ids, counts, offsets, st, ip);
+        int held = 0;
+        for (int a = 0; a < A; ++a) {
+            const int in = ids[a] >= eb;
+            held += in;
+            if (in ? (ip[a] < 0 || ip[a] >= offsets[E] || st[ip[a]] != a / k) : ip[a] != -1) bad = 1;
+        }
+        if (offsets[E] != held) bad = 1;
+        oracle_combine(T, k, H, yperm, ip, w, y);
+        for (int64_t i = 0; i < (int64_t)T * H; ++i)
+            if (!isfinite(y[i])) bad = 1;
+    }
     printf("case T=%d H=%d E=%d k=%d F=%d act=%d wdt=%d renorm=%d: %s\n", T, H, E, k, F, act, wdt,
            renorm, bad ? "FAILED" : "ok");
 

@@ -252,6 +252,72 @@ def test_permute_then_unpermute_is_identity():
         assert np.array_equal(back[:, j], x)
 
 
+@pytest.mark.parametrize("b,n", [(0, 128), (0, 32), (32, 32), (96, 32), (5, 1), (127, 1)])
+def test_held_dispatch_is_the_stable_sort_restricted_to_held_experts(b, n):
+    """Expert parallelism: the dispatch of a held range is numpy's stable sort of the
+    assignments routed to held experts, i.e. exactly the rows [offsets[b], offsets[b+n]) of the
+    dispatch over all experts; the other assignments get inv_perm = -1."""
+    rng = np.random.default_rng(13)
+    T, E, k = 300, 128, 8
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    counts, offsets, st, ip = O.permute(ids, E, held=(b, n))
+    flat = ids.ravel()
+    held = (flat >= b) & (flat < b + n)
+    want_counts = np.bincount(flat[held], minlength=E)
+    assert np.array_equal(counts, want_counts)
+    assert offsets[0] == 0 and np.array_equal(offsets[1:], np.cumsum(want_counts))
+    order = np.argsort(np.where(held, flat, E), kind="stable")[: held.sum()]
+    assert np.array_equal(st[: held.sum()], order // k)
+    assert np.all(ip[~held] == -1)
+    assert np.array_equal(ip[order], np.arange(held.sum()))
+    # the same rows as the full dispatch's slice
+    _, off_all, st_all, ip_all = O.permute(ids, E)
+    lo, hi = off_all[b], off_all[b + n]
+    assert np.array_equal(st[: held.sum()], st_all[lo:hi])
+    assert np.array_equal(ip[held], ip_all[held] - lo)
+
+
+def _share(inp, b, n):
+    """The inputs a rank holding experts [b, b+n) sees: every token, its experts' weights."""
+    out = dict(inp)
+    for key in ("w13", "w2", "w13_scale", "w2_scale", "w13_gscale", "w2_gscale"):
+        if inp.get(key) is not None:
+            out[key] = np.ascontiguousarray(inp[key][b:b + n])
+    return out
+
+
+@pytest.mark.parametrize("wdt", ["f32", "bf16", "nvfp4"])
+def test_partial_outputs_over_an_expert_partition_sum_to_the_layer(wdt):
+    wl, inp = _tiny(wdt=wdt, T=24, H=64, E=8, k=3, F=48)
+    full = O.forward(inp, wl.top_k, wl.wdt, wl.ffn)
+    total = np.zeros_like(full["y"])
+    for b, n in ((0, 3), (3, 2), (5, 3)):
+        part = O.forward(_share(inp, b, n), wl.top_k, wl.wdt, wl.ffn, held=(b, n))
+        assert np.array_equal(part["topk_ids"], full["topk_ids"])
+        # a token's partial output is the weighted sum over its held experts only
+        y_bf, _, _ = BF.layer(inp, full["logits"], wl.top_k, wdt, keep=lambda e: b <= e < b + n)
+        np.testing.assert_allclose(part["y"], y_bf, rtol=1e-10, atol=1e-13)
+        total += part["y"]
+    np.testing.assert_allclose(total, full["y"], rtol=1e-12, atol=1e-14)
+
+
+def test_held_range_of_all_experts_is_the_single_gpu_layer():
+    wl, inp = _tiny(T=16, E=8, k=2)
+    a = O.forward(inp, 2, wl.wdt, wl.ffn)
+    b = O.forward(inp, 2, wl.wdt, wl.ffn, held=(0, 8))
+    for key in ("counts", "offsets", "sorted_token", "inv_perm", "y"):
+        assert np.array_equal(a[key], b[key]), key
+
+
+def test_token_with_no_held_expert_gets_zero():
+    wl, inp = _tiny(T=40, E=8, k=1)
+    e = int(O.route(inp, 1)["topk_ids"][0, 0])  # an expert that some token picks
+    r = O.forward(_share(inp, e, 1), 1, wl.wdt, wl.ffn, held=(e, 1))
+    none = r["topk_ids"][:, 0] != e
+    assert none.any() and (~none).any()
+    assert np.all(r["y"][none] == 0.0) and np.all(np.abs(r["y"][~none]).max(1) > 0)
+
+
 def test_pages_load_example_tokens_per_expert():
     g = json.load(open(os.path.join(GOLD, "pages_values.json")))["prefill_tokens_per_expert"]
     rng = np.random.default_rng(11)
