@@ -6,7 +6,19 @@ A step is one ``moe_forward`` call (router -> dispatch -> gate/up GEMM + SwiGLU 
 -> combine) over one batch of seeded synthetic inputs already resident in HBM.  The default
 workload is the prefill-shaped layer (4096 tokens, hidden 4096, 128 experts, top-8, expert FFN
 1536, bf16, router bias N(0,1)); ``--workload`` selects another one (tiny, decode1, decode8,
-decode64, nvfp4_decode, nvfp4_prefill).  Prints one JSON line.
+decode64, nvfp4_decode, nvfp4_prefill, prefill6000).  Prints one JSON line.
+
+Shapes of "Hosting Qwen on Blackwell" (sections Prefill, Expert Parallel and the grouped MoE
+GEMM benchmark there):
+  --workload prefill6000 [--ep-size N --ep-rank r]
+        the ~6000-token prefill (about 375 rows per expert); with N > 1, the share of rank r
+        of N expert-parallel ranks: every token is routed, the rank holds experts
+        [r E/N, (r+1) E/N) and returns its partial output (the all-reduce that sums the
+        partial outputs is the caller's and is not timed).  Any workload takes --ep-size.
+  --workload grouped1 [--ep-size N]
+        the grouped MoE GEMM with every expert given one token: gate/up + SwiGLU then down
+        through moe_grouped_gemm on E/N experts (hidden 4096, expert ffn 1536, bf16), one row
+        each; reports the latency of the pair.
 
 Timing: W untimed steps, then K steps between two events on the launch stream.  Workloads
 whose selected weights are small enough to stay cached between steps (under 1.5 GiB) read a
@@ -49,24 +61,25 @@ def bytes_per_weight(wdt: str) -> float:
     return {"f32": 4.0, "bf16": 2.0, "nvfp4": 0.5 + 1.0 / 16}[wdt]
 
 
-def layer_work(wl, active: int):
-    """Algorithmic FLOPs and HBM bytes of one layer call: router + expert FFN FLOPs; the
-    active experts' weights once, the router weight, tokens in and out (intermediates
-    excluded: the method need not send them to HBM)."""
+def layer_work(wl, active: int, rows: int):
+    """Algorithmic FLOPs and HBM bytes of one layer call: router + expert FFN FLOPs of the
+    `rows` dispatched assignments; the active experts' weights once, the router weight,
+    tokens in and out (intermediates excluded: the method need not send them to HBM)."""
     act = 4 if wl.act == "f32" else 2
-    flops = 2.0 * wl.tokens * wl.hidden * wl.experts + 6.0 * wl.hidden * wl.ffn * wl.assignments
+    flops = 2.0 * wl.tokens * wl.hidden * wl.experts + 6.0 * wl.hidden * wl.ffn * rows
     nbytes = (active * 3.0 * wl.hidden * wl.ffn * bytes_per_weight(wl.wdt)
               + wl.experts * wl.hidden * act + 2.0 * wl.tokens * wl.hidden * act)
     return flops, nbytes
 
 
-def gate_up_work(wl, active: int):
-    """Algorithmic FLOPs and bytes of one gate/up grouped-GEMM launch: the active experts'
-    gate/up weights once, each token row once, the hid output once."""
+def gate_up_work(wl, active: int, rows: int, tokens_read: int):
+    """Algorithmic FLOPs and bytes of one gate/up grouped-GEMM launch over `rows` dispatched
+    rows: the active experts' gate/up weights once, each token row it reads once, the hid
+    output once."""
     act = 4 if wl.act == "f32" else 2
-    flops = 4.0 * wl.hidden * wl.ffn * wl.assignments
+    flops = 4.0 * wl.hidden * wl.ffn * rows
     nbytes = (active * 2.0 * wl.ffn * wl.hidden * bytes_per_weight(wl.wdt)
-              + wl.tokens * wl.hidden * act + wl.assignments * wl.ffn * act)
+              + tokens_read * wl.hidden * act + rows * wl.ffn * act)
     return flops, nbytes
 
 
@@ -86,7 +99,7 @@ def measured_traffic(workload: str):
     return e.get("bytes_per_launch")
 
 
-def cpu_baseline(wl, inputs, budget_s: float):
+def cpu_baseline(wl, inputs, budget_s: float, held=None):
     """The oracle (as it stands) on a sub-batch of the same workload's tokens."""
     from oracle import oracle as O
 
@@ -96,7 +109,7 @@ def cpu_baseline(wl, inputs, budget_s: float):
     while True:
         sub["x"] = inputs["x"][:n]
         t0 = time.perf_counter()
-        O.forward(sub, wl.top_k, wl.wdt, wl.ffn, wl.renormalize)
+        O.forward(sub, wl.top_k, wl.wdt, wl.ffn, wl.renormalize, held=held)
         spent = time.perf_counter() - t0
         if spent >= budget_s / 4 or n >= wl.tokens:
             break
@@ -134,48 +147,9 @@ def measured_peaks(torch, lib):
                        "read stream over 4 GiB" % (8 * cus))
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="prefill")
-    ap.add_argument("--flush", choices=("auto", "on", "off"), default="auto")
-    ap.add_argument("--flush-mode", choices=("read", "write"), default="read",
-                    help="evict caches by reading (default) or by writing a 1 GiB buffer")
-    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-probes", action="store_true",
-                    help="skip the measured-peak probes (bf16 MFMA loop, 4 GiB read stream)")
-    ap.add_argument("--calibration-copy", action="store_true",
-                    help="also run one 512 MiB device copy (counter calibration)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print("bench.py measures one GPU only: this layer is built and measured on a single "
-              "MI355X (no sharding, no collectives); --gpus %d is not supported" % args.gpus,
-              file=sys.stderr)
-        return 2
-
-    import torch
-
-    from mixture_experts_layer_softmax_amd import lib, synth
-    from mixture_experts_layer_softmax_amd.layer import MoELayer
-
-    wl = synth.WORKLOADS[args.workload]
-    print("[bench] generating %s" % describe(wl), file=sys.stderr, flush=True)
-    inputs = synth.generate(wl)
-    torch.cuda.set_device(0)
-    layer = MoELayer.from_workload(wl, inputs, device="cuda:0")
-    x = layer.act_tensor(inputs["x"])
-    y = layer.empty_act(wl.tokens, wl.hidden)
-
-    # routing of this batch (also gives the realised number of active experts)
-    _, dbg = layer.forward(x, debug=True)
-    torch.cuda.synchronize()
-    counts = dbg["counts"].cpu().numpy()
-    active = int((counts > 0).sum())
-    w_bytes = active * 3.0 * wl.hidden * wl.ffn * bytes_per_weight(wl.wdt)
-    flush = args.flush == "on" or (args.flush == "auto" and w_bytes < 1.5 * 2 ** 30)
+def make_timer(torch, lib, flush: bool, flush_mode: str):
+    """timed(fn, steps) -> mean ms per call of fn on the current stream.  With `flush`, caches
+    are evicted before every call (outside its timed interval)."""
     scratch = torch.ones(2 ** 30, dtype=torch.uint8, device="cuda:0") if flush else None
     scratch_word = torch.zeros(1, dtype=torch.int32, device="cuda:0")
 
@@ -183,13 +157,12 @@ def main() -> int:
         # Reading 1 GiB of other data displaces the layer's weights from L2 and the 256 MiB
         # Infinity Cache.  Writing it instead would leave dirty lines whose write-back lands
         # inside the next timed interval and competes with the weight stream.
-        if args.flush_mode == "read":
+        if flush_mode == "read":
             lib.probe_read(scratch, scratch_word)
         else:
             scratch.fill_(1)
 
     def timed(fn, steps):
-        """Mean ms per call of fn over `steps` calls on the current stream."""
         if not flush:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
@@ -207,6 +180,154 @@ def main() -> int:
             b.record()
         torch.cuda.synchronize()
         return sum(a.elapsed_time(b) for a, b in evs) / steps
+
+    return timed
+
+
+def bench_grouped1(args) -> int:
+    """Grouped MoE GEMM with every expert given one token ("Hosting Qwen on Blackwell": the
+    grouped GEMM benchmark across expert-parallel configurations activates every expert with a
+    single token).  One rank of --ep-size holds E/N experts with one row each; a step is the
+    gate/up + SwiGLU launch and the down launch of moe_grouped_gemm."""
+    import numpy as np
+    import torch
+
+    from mixture_experts_layer_softmax_amd import lib, synth
+    from mixture_experts_layer_softmax_amd.layer import MoELayer
+
+    E, H, F = 128, 4096, 1536
+    if E % args.ep_size:
+        print("--ep-size must divide the %d experts" % E, file=sys.stderr)
+        return 2
+    n = E // args.ep_size
+    b = args.ep_rank * n
+    wl = synth.Workload("grouped1", n, H, E, 1, F, "bf16", "bf16", 707, "none")
+    print("[bench] grouped GEMM, one token for each of experts [%d, %d) of %d" % (b, b + n, E),
+          file=sys.stderr, flush=True)
+    inputs = synth.generate(wl, experts=range(b, b + n))
+    torch.cuda.set_device(0)
+    held = dict(expert_begin=b, local_experts=n) if n < E else {}
+    layer = MoELayer.from_workload(wl, inputs, device="cuda:0", **held)
+    p = layer.problem_for(n)
+    ws = layer.workspace(n)
+    x = layer.act_tensor(inputs["x"])  # row i is the token of expert b + i
+    offsets = torch.from_numpy(np.clip(np.arange(E + 1) - b, 0, n).astype(np.int32)).cuda()
+    hid = layer.empty_act(n, F)
+    yp = layer.empty_act(n, H)
+
+    def step():
+        lib.grouped_gemm(p, lib.GATE_UP_SWIGLU, x, None, offsets, layer.weights, hid, ws)
+        lib.grouped_gemm(p, lib.DOWN, hid, None, offsets, layer.weights, yp, ws)
+
+    w_bytes = n * 3.0 * H * F * 2
+    flush = args.flush == "on" or (args.flush == "auto" and w_bytes < 1.5 * 2 ** 30)
+    timed = make_timer(torch, lib, flush, args.flush_mode)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms = timed(step, args.steps)
+    wall = time.perf_counter() - t0
+    nbytes = w_bytes + n * (H + F + F + H) * 2.0  # weights once; x, hid out/in, y_perm out
+    flops = n * 6.0 * H * F
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    peaks = None if args.no_probes else measured_peaks(torch, lib)
+    roof = dict(bound="hbm", achieved=gbs, peak=PEAK_HBM_BYTES / 1e9, unit="GB/s",
+                frac=gbs * 1e9 / PEAK_HBM_BYTES, traffic=None,
+                kernel="grouped gate/up + down GEMM pair, one row per expert", kernel_ms=ms,
+                algorithmic_bytes=nbytes, algorithmic_flops=flops)
+    if peaks:
+        roof["frac_measured"] = gbs / peaks["hbm_read_gbs"]
+    out = dict(metric="grouped MoE GEMM latency, every expert given one token", value=ms * 1e3,
+               unit="us", n_gpus=1, steps=args.steps, warmup=args.warmup, ms_per_step=ms,
+               higher_is_better=False, scaling="weak", vs_baseline=None, dtype="bf16",
+               data="synthetic (seeded)",
+               config=dict(workload="grouped1: one token for each of %d experts (rank %d of %d "
+                                    "expert-parallel ranks over %d experts), hidden %d, expert "
+                                    "ffn %d, bf16" % (n, args.ep_rank, args.ep_size, E, H, F),
+                           experts=n, hidden=H, ffn=F, ep_size=args.ep_size, ep_rank=args.ep_rank,
+                           cache_flushed=bool(flush)),
+               wall_s=wall, roofline=roof)
+    if peaks:
+        out["measured_peaks"] = peaks
+    if not args.no_cpu_baseline:
+        from oracle import oracle as O
+
+        O.build()
+        t1 = time.perf_counter()
+        O.expert_rows(inputs, "bf16", F, np.arange(n), np.arange(n))
+        spent = time.perf_counter() - t1
+        out["cpu_baseline"] = dict(value=spent * 1e6, unit="us", cores=O.max_threads(), kind="oracle",
+                                   sample="all %d rows: gate/up, SwiGLU and down in fp64" % n,
+                                   seconds=spent)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prefill")
+    ap.add_argument("--flush", choices=("auto", "on", "off"), default="auto")
+    ap.add_argument("--flush-mode", choices=("read", "write"), default="read",
+                    help="evict caches by reading (default) or by writing a 1 GiB buffer")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probes", action="store_true",
+                    help="skip the measured-peak probes (bf16 MFMA loop, 4 GiB read stream)")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="also run one 512 MiB device copy (counter calibration)")
+    ap.add_argument("--ep-size", type=int, default=1,
+                    help="expert-parallel degree whose one-rank share is measured (one GPU)")
+    ap.add_argument("--ep-rank", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this layer is built and measured on a single "
+              "MI355X (no collectives); --gpus %d is not supported.  One expert-parallel rank's "
+              "share is measured with --ep-size N --ep-rank r." % args.gpus, file=sys.stderr)
+        return 2
+    if args.ep_size < 1 or not 0 <= args.ep_rank < args.ep_size:
+        print("--ep-rank must lie in [0, --ep-size)", file=sys.stderr)
+        return 2
+    if args.workload == "grouped1":
+        return bench_grouped1(args)
+
+    import torch
+
+    from mixture_experts_layer_softmax_amd import lib, synth
+    from mixture_experts_layer_softmax_amd.layer import MoELayer
+
+    wl = synth.WORKLOADS[args.workload]
+    held = None
+    if args.ep_size > 1:
+        if wl.experts % args.ep_size:
+            print("--ep-size must divide the %d experts" % wl.experts, file=sys.stderr)
+            return 2
+        n = wl.experts // args.ep_size
+        held = (args.ep_rank * n, n)
+    print("[bench] generating %s%s" % (describe(wl), "" if held is None else
+          ", experts [%d, %d) of rank %d/%d" % (held[0], held[0] + held[1], args.ep_rank, args.ep_size)),
+          file=sys.stderr, flush=True)
+    inputs = synth.generate(wl, experts=None if held is None else range(held[0], held[0] + held[1]))
+    torch.cuda.set_device(0)
+    layer = MoELayer.from_workload(wl, inputs, device="cuda:0",
+                                   expert_begin=0 if held is None else held[0],
+                                   local_experts=0 if held is None else held[1])
+    x = layer.act_tensor(inputs["x"])
+    y = layer.empty_act(wl.tokens, wl.hidden)
+
+    # routing of this batch (also gives the realised number of active experts)
+    _, dbg = layer.forward(x, debug=True)
+    torch.cuda.synchronize()
+    counts = dbg["counts"].cpu().numpy()
+    active = int((counts > 0).sum())
+    rows = int(counts.sum())  # dispatched rows: every assignment, or those of the held experts
+    tokens_read = int(((dbg["inv_perm"].reshape(wl.tokens, wl.top_k) >= 0).any(1)).sum().item())
+    w_bytes = active * 3.0 * wl.hidden * wl.ffn * bytes_per_weight(wl.wdt)
+    flush = args.flush == "on" or (args.flush == "auto" and w_bytes < 1.5 * 2 ** 30)
+    timed = make_timer(torch, lib, flush, args.flush_mode)
 
     print("[bench] warmup %d, timed %d steps%s" % (args.warmup, args.steps, " (flushed)" if flush else ""),
           file=sys.stderr, flush=True)
@@ -237,8 +358,8 @@ def main() -> int:
         b.copy_(a)
         torch.cuda.synchronize()
 
-    flops, nbytes = layer_work(wl, active)
-    gflops, gbytes = gate_up_work(wl, active)
+    flops, nbytes = layer_work(wl, active, rows)
+    gflops, gbytes = gate_up_work(wl, active, rows, tokens_read)
     t_mfma, t_hbm = gflops / PEAK_BF16_FLOPS, gbytes / PEAK_HBM_BYTES
     if t_hbm >= t_mfma:
         roof = dict(bound="hbm", achieved=gbytes / (gemm1_ms * 1e-3) / 1e9, peak=PEAK_HBM_BYTES / 1e9,
@@ -273,9 +394,13 @@ def main() -> int:
         out["measured_peaks"] = peaks
         out["layer_mfma_frac_measured"] = flops / (ms_per_step * 1e-3) / (peaks["mfma_bf16_tflops"] * 1e12)
         out["layer_hbm_frac_measured"] = nbytes / (ms_per_step * 1e-3) / (peaks["hbm_read_gbs"] * 1e9)
+    if held is not None:
+        out["config"].update(ep_size=args.ep_size, ep_rank=args.ep_rank,
+                             held_experts=[held[0], held[0] + held[1]], dispatched_rows=rows,
+                             output="partial (this rank's experts); the all-reduce is not timed")
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(wl, inputs, args.cpu_budget)
+        out["cpu_baseline"] = cpu_baseline(wl, inputs, args.cpu_budget, held)
     print(json.dumps(out), flush=True)
     return 0
 

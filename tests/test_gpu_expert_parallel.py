@@ -183,3 +183,32 @@ def test_prefill6000_share_of_four_ranks_sampled():
     e = rel_err(act_f64(to_host(y))[toks], ref["y"])
     note("  %d of %d rows held; y rel err %.3e on %d tokens" % (a_local, wl.assignments, e, toks.size))
     assert e <= TOL
+
+
+@pytest.mark.parametrize("ep", [1, 8])
+def test_grouped_gemm_one_token_per_expert_full_size(ep):
+    """The grouped MoE GEMM benchmark shape of "Hosting Qwen on Blackwell" (every expert given
+    one token; hidden 4096, expert ffn 1536), for all 128 experts and for one rank of eight:
+    the gate/up + SwiGLU and down launches against the oracle's expert rows."""
+    E, H, F = 128, 4096, 1536
+    n = E // ep
+    b = (ep - 1) * n
+    wl = W("grouped1", n, H, E, 1, F, "bf16", "bf16", 707, "none")
+    note("grouped gemm, one token for each of experts [%d, %d)" % (b, b + n))
+    inp = synth.generate(wl, experts=range(b, b + n))
+    held = dict(expert_begin=b, local_experts=n) if n < E else {}
+    layer = MoELayer.from_workload(wl, inp, **held)
+    p = layer.problem_for(n)
+    ws = layer.workspace(n)
+    x = layer.act_tensor(inp["x"])
+    offsets = torch.from_numpy(np.clip(np.arange(E + 1) - b, 0, n).astype(np.int32)).cuda()
+    hid = layer.empty_act(n, F)
+    yp = layer.empty_act(n, H)
+    lib.grouped_gemm(p, lib.GATE_UP_SWIGLU, x, None, offsets, layer.weights, hid, ws)
+    lib.grouped_gemm(p, lib.DOWN, hid, None, offsets, layer.weights, yp, ws)
+    torch.cuda.synchronize()
+    ref_y, ref_h = O.expert_rows(inp, "bf16", F, np.arange(n), np.arange(n), want_hid=True)
+    eh = rel_err(act_f64(to_host(hid)), ref_h)
+    ey = rel_err(act_f64(to_host(yp)), ref_y)
+    note("  hid rel err %.3e, y rel err %.3e" % (eh, ey))
+    assert eh <= TOL and ey <= TOL
