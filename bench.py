@@ -6,7 +6,7 @@ A step is one ``moe_forward`` call (router -> dispatch -> gate/up GEMM + SwiGLU 
 -> combine) over one batch of seeded synthetic inputs already resident in HBM.  The default
 workload is the prefill-shaped layer (4096 tokens, hidden 4096, 128 experts, top-8, expert FFN
 1536, bf16, router bias N(0,1)); ``--workload`` selects another one (tiny, decode1, decode8,
-decode64, nvfp4_decode, nvfp4_prefill, prefill6000).  Prints one JSON line.
+decode64, nvfp4_decode, nvfp4_prefill, prefill6000, mxfp8_prefill).  Prints one JSON line.
 
 Shapes of "Hosting Qwen on Blackwell" (sections Prefill, Expert Parallel and the grouped MoE
 GEMM benchmark there):
@@ -46,6 +46,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_FLOPS = 2.5e15   # MI355X dense bf16 MFMA
+PEAK_FP8_FLOPS = 5.0e15    # MI355X dense fp8 MFMA (the MXFP8 layer's block-scaled products)
 PEAK_HBM_BYTES = 8.0e12    # MI355X HBM3E
 METRIC = "MoE layer tokens/s at 1 GPU; % MFMA peak (prefill) / % HBM BW (decode)"
 GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_softmax_amd", "csrc", "gemm.hip")
@@ -58,7 +59,12 @@ def describe(wl) -> str:
 
 
 def bytes_per_weight(wdt: str) -> float:
-    return {"f32": 4.0, "bf16": 2.0, "nvfp4": 0.5 + 1.0 / 16}[wdt]
+    return {"f32": 4.0, "bf16": 2.0, "nvfp4": 0.5 + 1.0 / 16, "mxfp8": 1.0 + 1.0 / 32}[wdt]
+
+
+def mfma_peak(wl) -> float:
+    """Dense MFMA peak of the dtype the expert GEMMs multiply in (NVFP4 is decoded to bf16)."""
+    return PEAK_FP8_FLOPS if wl.wdt == "mxfp8" else PEAK_BF16_FLOPS
 
 
 def layer_work(wl, active: int, rows: int):
@@ -360,19 +366,23 @@ def main() -> int:
 
     flops, nbytes = layer_work(wl, active, rows)
     gflops, gbytes = gate_up_work(wl, active, rows, tokens_read)
-    t_mfma, t_hbm = gflops / PEAK_BF16_FLOPS, gbytes / PEAK_HBM_BYTES
+    peak_mfma = mfma_peak(wl)
+    t_mfma, t_hbm = gflops / peak_mfma, gbytes / PEAK_HBM_BYTES
     if t_hbm >= t_mfma:
         roof = dict(bound="hbm", achieved=gbytes / (gemm1_ms * 1e-3) / 1e9, peak=PEAK_HBM_BYTES / 1e9,
                     unit="GB/s")
     else:
         roof = dict(bound="mfma", achieved=gflops / (gemm1_ms * 1e-3) / 1e12,
-                    peak=PEAK_BF16_FLOPS / 1e12, unit="TFLOP/s")
+                    peak=peak_mfma / 1e12, unit="TFLOP/s")
     roof["frac"] = roof["achieved"] / roof["peak"]
     if peaks:
-        mp = peaks["hbm_read_gbs"] if roof["bound"] == "hbm" else peaks["mfma_bf16_tflops"]
-        roof["frac_measured"] = roof["achieved"] / mp
+        if roof["bound"] == "hbm":
+            roof["frac_measured"] = roof["achieved"] / peaks["hbm_read_gbs"]
+        elif wl.wdt != "mxfp8":  # the probe measures the bf16 rate only
+            roof["frac_measured"] = roof["achieved"] / peaks["mfma_bf16_tflops"]
     roof["traffic"] = measured_traffic(wl.name)
-    roof["kernel"] = "grouped gate/up GEMM + SwiGLU (%s weights)" % wl.wdt
+    roof["kernel"] = "grouped gate/up GEMM + SwiGLU (%s weights%s)" % (
+        wl.wdt, ", input quantization included" if wl.wdt == "mxfp8" else "")
     roof["kernel_ms"] = gemm1_ms
     roof["algorithmic_bytes"] = gbytes
     roof["algorithmic_flops"] = gflops
@@ -380,19 +390,21 @@ def main() -> int:
     tok_s = wl.tokens / (ms_per_step * 1e-3)
     out = dict(metric=METRIC, value=tok_s, unit="tokens/s", n_gpus=1, steps=args.steps,
                warmup=args.warmup, ms_per_step=ms_per_step, higher_is_better=True,
-               scaling="weak", vs_baseline=None, dtype=wl.act, data="synthetic (seeded)",
+               scaling="weak", vs_baseline=None, dtype="fp8" if wl.wdt == "mxfp8" else wl.act,
+               data="synthetic (seeded)",
                config=dict(workload=describe(wl), tokens=wl.tokens, hidden=wl.hidden,
                            experts=wl.experts, top_k=wl.top_k, ffn=wl.ffn, weights=wl.wdt,
                            active_experts=active, max_expert_rows=int(counts.max()),
                            cache_flushed=bool(flush),
                            flush_mode=args.flush_mode if flush else None),
                layer_tflops=flops / (ms_per_step * 1e-3) / 1e12,
-               layer_mfma_frac=flops / (ms_per_step * 1e-3) / PEAK_BF16_FLOPS,
+               layer_mfma_frac=flops / (ms_per_step * 1e-3) / peak_mfma,
                layer_hbm_frac=nbytes / (ms_per_step * 1e-3) / PEAK_HBM_BYTES,
                wall_s=wall, roofline=roof)
     if peaks:
         out["measured_peaks"] = peaks
-        out["layer_mfma_frac_measured"] = flops / (ms_per_step * 1e-3) / (peaks["mfma_bf16_tflops"] * 1e12)
+        if wl.wdt != "mxfp8":
+            out["layer_mfma_frac_measured"] = flops / (ms_per_step * 1e-3) / (peaks["mfma_bf16_tflops"] * 1e12)
         out["layer_hbm_frac_measured"] = nbytes / (ms_per_step * 1e-3) / (peaks["hbm_read_gbs"] * 1e9)
     if held is not None:
         out["config"].update(ep_size=args.ep_size, ep_rank=args.ep_rank,

@@ -71,8 +71,18 @@ typedef enum {
 
 /* Storage formats.  MOE_NVFP4 (weights only): 4-bit E2M1 values, two per byte with the even
  * element in the low nibble, one E4M3 (FN) scale per 16 consecutive elements along the input
- * dimension, and an optional fp32 scale per expert and matrix: w = e2m1 * e4m3 * gscale. */
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_NVFP4 = 2 } moe_dtype;
+ * dimension, and an optional fp32 scale per expert and matrix: w = e2m1 * e4m3 * gscale.
+ * MOE_MXFP8 (weights only; OCP microscaling formats v1.0, the scheme "Hosting Qwen on
+ * Blackwell" deploys, section Quantization): one E4M3 (FN) byte per element and one E8M0 scale
+ * byte s per 32 consecutive elements along the input dimension: w = e4m3 * 2^(s - 127).  An
+ * MXFP8 layer also runs its activations in MXFP8: the bf16 x rows are quantized before the
+ * gate/up GEMM and the hid rows before the down GEMM, per block of 32 along K, with the shared
+ * exponent X = floor(log2(max |v|)) - 8 (X = -127 for an all-zero block, clamped to
+ * [-127, 127]) and elements v / 2^X clamped to +-448 and rounded to the nearest E4M3 value,
+ * ties to the even code (sign kept); the GEMMs multiply on the block-scaled fp8 matrix cores
+ * with fp32 accumulation.  Outputs (hid, y_perm, y) stay bf16.  Needs H % 256 == 0 and
+ * F % 128 == 0, bf16 activations; weights and E8M0 scales are ROW_MAJOR. */
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_NVFP4 = 2, MOE_MXFP8 = 3 } moe_dtype;
 
 typedef enum { MOE_GEMM_GATE_UP_SWIGLU = 0, MOE_GEMM_DOWN = 1 } moe_gemm_kind;
 
@@ -88,7 +98,7 @@ typedef struct {
     int32_t top_k;        /* k, 1..min(E,16) */
     int32_t ffn;          /* F, multiple of 64 */
     int32_t act_dtype;    /* MOE_F32 | MOE_BF16: x, router weight, hid, y_perm, y */
-    int32_t w_dtype;      /* MOE_F32 (with F32 acts) | MOE_BF16 | MOE_NVFP4 (with BF16 acts) */
+    int32_t w_dtype;      /* MOE_F32 (with F32 acts) | MOE_BF16 | MOE_NVFP4 | MOE_MXFP8 (BF16 acts) */
     int32_t renormalize;  /* 1: softmax over the selected k (default); 0: full softmax */
     int32_t path;         /* moe_path */
     int32_t expert_begin;  /* expert parallelism: the caller holds the experts           */
@@ -129,10 +139,10 @@ typedef struct {
 typedef enum { MOE_LAYOUT_ROW_MAJOR = 0, MOE_LAYOUT_PACKED = 1 } moe_layout;
 
 typedef struct {
-    const void* w13;              /* [E,2F,H] fp32 or packed bf16, or NVFP4 bytes [E,2F,H/2] */
-    const void* w2;               /* [E,H,F] fp32 or packed bf16, or NVFP4 bytes [E,H,F/2] */
-    const uint8_t* w13_scale;     /* NVFP4 only: E4M3 [E,2F,H/16] */
-    const uint8_t* w2_scale;      /* NVFP4 only: E4M3 [E,H,F/16] */
+    const void* w13;              /* [E,2F,H] fp32, packed bf16 or MXFP8 E4M3 bytes; NVFP4 bytes [E,2F,H/2] */
+    const void* w2;               /* [E,H,F] fp32, packed bf16 or MXFP8 E4M3 bytes; NVFP4 bytes [E,H,F/2] */
+    const uint8_t* w13_scale;     /* NVFP4: E4M3 [E,2F,H/16]; MXFP8: E8M0 [E,2F,H/32] */
+    const uint8_t* w2_scale;      /* NVFP4: E4M3 [E,H,F/16]; MXFP8: E8M0 [E,H,F/32] */
     const float* w13_gscale;      /* NVFP4 only, nullable (=> 1.0): fp32 [E] */
     const float* w2_gscale;       /* NVFP4 only, nullable (=> 1.0): fp32 [E] */
     int32_t layout;               /* moe_layout: PACKED for bf16, ROW_MAJOR otherwise */
@@ -178,7 +188,9 @@ moe_status moe_permute(const moe_problem* p, const int32_t* topk_ids, int32_t* c
  *                  projections by w13[e]: out is hid [A,F] in act_dtype.
  *  DOWN:           input a = hid [A,F] (a_rows must be NULL); out = y_perm [A,H] =
  *                  hid W2[e]^T, in act_dtype.
- * fp32 accumulation; NVFP4 weights are decoded exactly to bf16 inside the kernel.
+ * fp32 accumulation; NVFP4 weights are decoded exactly to bf16 inside the kernel; for MXFP8
+ * the bf16 input rows are first quantized to MXFP8 (into the workspace) and the product runs
+ * on the block-scaled fp8 matrix cores.
  * `offsets` [E+1] is read on the device; values are clamped to [0, A] so that a malformed
  * table cannot make the kernel reach past the A rows of `a`/`out`.  Only the rows of held
  * experts are computed (all experts unless local_experts is set); other rows are untouched. */
@@ -192,6 +204,12 @@ moe_status moe_grouped_gemm(const moe_problem* p, moe_gemm_kind kind, const void
  * to this caller's experts) are skipped.  y_perm [A,H], y [T,H] in act_dtype. */
 moe_status moe_combine(const moe_problem* p, const void* y_perm, const int32_t* inv_perm,
                        const float* topk_w, void* y, void* stream);
+
+/* MXFP8 quantization of bf16 rows, the layer's own activation step (rule under moe_dtype):
+ * x [rows, K] bf16 -> codes [rows, K] E4M3 and scales [rows, K/32] E8M0, all row-major.
+ * For callers that keep activations in MXFP8.  K % 32 == 0; x and codes 16-byte aligned. */
+moe_status moe_quantize_mxfp8(const void* x, int64_t rows, int32_t K, uint8_t* codes, uint8_t* scales,
+                              void* stream);
 
 /* The whole layer: route -> dispatch -> gate/up GEMM + SwiGLU -> down GEMM -> combine.
  * y [T,H] in act_dtype.  The routing/dispatch outputs are optional (NULL = keep them in the

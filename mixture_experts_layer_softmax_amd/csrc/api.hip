@@ -25,7 +25,7 @@ bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0
 
 struct Layout {
     size_t logits, ids, w, hist, base, counts, offsets, sorted, inv, tiles1, tiles2, tcount, hid,
-        yperm, total;
+        yperm, xq, xs, hq, hs, total;
     int family, bm, max_tiles;
 };
 
@@ -35,8 +35,13 @@ int act_bytes(const moe_problem& p) { return p.act_dtype == MOE_F32 ? 4 : 2; }
 int ebegin(const moe_problem& p) { return p.local_experts ? p.expert_begin : 0; }
 int eend(const moe_problem& p) { return p.local_experts ? p.expert_begin + p.local_experts : p.num_experts; }
 
+int wfmt_of(const moe_problem& p) {
+    return p.w_dtype == MOE_F32 ? kWF32 : p.w_dtype == MOE_BF16 ? kWBF16 : p.w_dtype == MOE_NVFP4 ? kWNVFP4 : kWMXFP8;
+}
+
 int family_of(const moe_problem& p) {
     if (p.act_dtype == MOE_F32) return kFamSimtF32;
+    if (p.w_dtype == MOE_MXFP8) return kFamPrefill;  // one MXFP8 kernel family (256-row tiles)
     int path = p.path;
     if (path == MOE_PATH_AUTO) {
         const long A = long(p.num_tokens) * p.top_k;
@@ -57,10 +62,13 @@ moe_status check_problem(const moe_problem* p) {
         (p->local_experts == 0 && p->expert_begin != 0))
         return MOE_ERR_INVALID_ARGUMENT;
     if (p->act_dtype != MOE_F32 && p->act_dtype != MOE_BF16) return MOE_ERR_INVALID_ARGUMENT;
-    if (p->w_dtype != MOE_F32 && p->w_dtype != MOE_BF16 && p->w_dtype != MOE_NVFP4)
+    if (p->w_dtype != MOE_F32 && p->w_dtype != MOE_BF16 && p->w_dtype != MOE_NVFP4 &&
+        p->w_dtype != MOE_MXFP8)
         return MOE_ERR_INVALID_ARGUMENT;
     if (p->hidden % 64 || p->ffn % 64) return MOE_ERR_UNSUPPORTED;
-    if (p->w_dtype == MOE_BF16 && (p->hidden % 256 || p->ffn % 128)) return MOE_ERR_UNSUPPORTED;
+    if ((p->w_dtype == MOE_BF16 || p->w_dtype == MOE_MXFP8) && (p->hidden % 256 || p->ffn % 128))
+        return MOE_ERR_UNSUPPORTED;
+    if (p->w_dtype == MOE_MXFP8 && p->act_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
     if (p->act_dtype == MOE_F32 && p->w_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
     if (p->act_dtype == MOE_BF16 && p->w_dtype == MOE_F32) return MOE_ERR_UNSUPPORTED;
     if (long(p->num_tokens) * p->top_k > (1L << 30) || long(p->num_tokens) * p->hidden > (1L << 40))
@@ -74,7 +82,7 @@ Layout layout(const moe_problem& p) {
     const size_t A = T * k;
     const size_t nch = (T + kChunkTokens - 1) / kChunkTokens;
     L.family = family_of(p);
-    L.bm = gemm_tile_rows(L.family, p.w_dtype == MOE_F32 ? kWF32 : p.w_dtype == MOE_BF16 ? kWBF16 : kWNVFP4, p.ffn);
+    L.bm = gemm_tile_rows(L.family, wfmt_of(p), p.ffn);
     L.max_tiles = int((A + L.bm - 1) / L.bm + (A < E ? A : E) + 1);
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t r = o; o += up(bytes > 0 ? bytes : 1); return r; };
@@ -92,6 +100,11 @@ Layout layout(const moe_problem& p) {
     L.tcount = take(4 * sizeof(int));
     L.hid = take(A * F * act_bytes(p));
     L.yperm = take(A * H * act_bytes(p));
+    const bool mx = p.w_dtype == MOE_MXFP8;  // MXFP8 copies of the GEMM inputs (codes + scales)
+    L.xq = take(mx ? A * H : 0);
+    L.xs = take(mx ? A * H / 32 : 0);
+    L.hq = take(mx ? A * F : 0);
+    L.hs = take(mx ? A * F / 32 : 0);
     L.total = o;
     return L;
 }
@@ -111,6 +124,10 @@ moe_status check_weights(const moe_problem& p, const moe_expert_weights* w) {
     if (!w || !w->w13 || !w->w2 || !aligned(w->w13) || !aligned(w->w2)) return MOE_ERR_INVALID_ARGUMENT;
     if (w->layout != (p.w_dtype == MOE_BF16 ? MOE_LAYOUT_PACKED : MOE_LAYOUT_ROW_MAJOR))
         return MOE_ERR_INVALID_ARGUMENT;
+    if (p.w_dtype == MOE_MXFP8) {
+        if (!w->w13_scale || !w->w2_scale || !aligned(w->w13_scale) || !aligned(w->w2_scale))
+            return MOE_ERR_INVALID_ARGUMENT;
+    }
     if (p.w_dtype == MOE_NVFP4) {
         if (!w->w13_scale || !w->w2_scale) return MOE_ERR_INVALID_ARGUMENT;
         // the decode kernel reads scales in 2- and 8-byte pieces; like every pointer of the ABI
@@ -148,7 +165,7 @@ GemmArgs gemm_args(const moe_problem& p, int kind, const void* a, const int32_t*
     g.out = out;
     g.F = p.ffn;
     g.kind = kind;
-    g.wfmt = p.w_dtype == MOE_F32 ? kWF32 : p.w_dtype == MOE_BF16 ? kWBF16 : kWNVFP4;
+    g.wfmt = wfmt_of(p);
     const int A = p.num_tokens * p.top_k;
     if (kind == kGateUp) {
         g.K = p.hidden;
@@ -166,6 +183,19 @@ GemmArgs gemm_args(const moe_problem& p, int kind, const void* a, const int32_t*
         g.a_rows_limit = A;
     }
     return g;
+}
+
+// MXFP8: quantize the GEMM's bf16 input rows (g.a_rows_limit of them) to E4M3 codes + E8M0
+// scales in the workspace and point the GEMM at them.  Other formats: nothing to do.
+moe_status mx_input(const moe_problem& p, GemmArgs& g, void* ws, const Layout& L, hipStream_t s) {
+    if (p.w_dtype != MOE_MXFP8) return MOE_OK;
+    const bool up = g.kind == kGateUp;
+    uint8_t* codes = at<uint8_t>(ws, up ? L.xq : L.hq);
+    uint8_t* scales = at<uint8_t>(ws, up ? L.xs : L.hs);
+    MOE_TRY(dev(launch_mx_quantize(g.a, g.a_rows_limit, g.K, codes, scales, s)));
+    g.a = codes;
+    g.ascale = scales;
+    return MOE_OK;
 }
 
 }  // namespace
@@ -278,6 +308,7 @@ moe_status moe_grouped_gemm(const moe_problem* p, moe_gemm_kind kind, const void
                                           L.max_tiles, s)));
     GemmArgs g = gemm_args(*p, kind == MOE_GEMM_GATE_UP_SWIGLU ? kGateUp : kDown, a, a_rows, tiles,
                            tcount, *w, out);
+    MOE_TRY(mx_input(*p, g, workspace, L, s));
     return dev(launch_gemm(g, L.family, L.max_tiles, s));
 }
 
@@ -291,6 +322,15 @@ moe_status moe_combine(const moe_problem* p, const void* y_perm, const int32_t* 
     return dev(launch_combine(y_perm, inv_perm, topk_w, y, p->num_tokens, p->top_k, p->hidden,
                               p->num_tokens * p->top_k, p->act_dtype == MOE_BF16,
                               static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_quantize_mxfp8(const void* x, int64_t rows, int32_t K, uint8_t* codes, uint8_t* scales,
+                              void* stream) {
+    if (rows < 0 || K <= 0 || K % 32) return MOE_ERR_INVALID_ARGUMENT;
+    if (rows == 0) return MOE_OK;
+    if (!x || !codes || !scales || !aligned(x) || !aligned(codes)) return MOE_ERR_INVALID_ARGUMENT;
+    if (rows > (1L << 40) / K) return MOE_ERR_UNSUPPORTED;
+    return dev(launch_mx_quantize(x, rows, K, codes, scales, static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_forward(const moe_problem* p, const void* x, const void* w_router,
@@ -339,8 +379,10 @@ moe_status moe_forward(const moe_problem* p, const void* x, const void* w_router
     void* hid = at<void>(workspace, L.hid);
     void* yperm = at<void>(workspace, L.yperm);
     GemmArgs g1 = gemm_args(*p, kGateUp, x, st, tiles, tcount, *w, hid);
+    MOE_TRY(mx_input(*p, g1, workspace, L, s));
     MOE_TRY(dev(launch_gemm(g1, L.family, L.max_tiles, s)));
     GemmArgs g2 = gemm_args(*p, kDown, hid, nullptr, tiles, tcount, *w, yperm);
+    MOE_TRY(mx_input(*p, g2, workspace, L, s));
     MOE_TRY(dev(launch_gemm(g2, L.family, L.max_tiles, s)));
     return dev(launch_combine(yperm, ip, tw, y, p->num_tokens, p->top_k, p->hidden,
                               p->num_tokens * p->top_k, p->act_dtype == MOE_BF16, s));

@@ -74,4 +74,7 @@ __device__ int block_exclusive_scan(int v, int* total) {
     return r;
 }
 
+// SwiGLU of one (gate, up) pair: silu(g) * u with silu(g) = g / (1 + e^-g).
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+
 }  // namespace moe

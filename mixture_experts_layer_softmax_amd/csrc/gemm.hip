@@ -27,6 +27,7 @@
 // MFMA sees the exact weight; the per-expert scale multiplies the fp32 accumulator.
 #include "device.h"
 #include "launch.h"
+#include "lds_dma.h"
 
 namespace moe {
 
@@ -65,8 +66,6 @@ __device__ __forceinline__ uint4 dequant8(uint32_t word, float s) {
     }
     return make_uint4(o[0], o[1], o[2], o[3]);
 }
-
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
 }  // namespace
 
@@ -242,47 +241,6 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_fallback_kernel(GemmArgs g) 
         }
 }
 
-// ---------------------------------------------------------------------------------------
-// Helpers of the prefill kernels: explicit load-counter waits, a block barrier, and direct
-// global->LDS loads issued from inline asm (each LDS slot is its own LDS object so that the
-// compiler can tell the slots apart; waits on the load counter are explicit).
-// ---------------------------------------------------------------------------------------
-
-namespace {
-
-constexpr int vm_wait_lgkm0(int n) { return (n & 15) | (7 << 4) | (0 << 8) | ((n >> 4) << 14); }
-
-__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
-
-template <int N>
-__device__ __forceinline__ void wait_vm_lgkm0() {
-    __builtin_amdgcn_s_waitcnt(vm_wait_lgkm0(N));
-}
-
-// 16 bytes per lane from global memory straight into LDS: lane l writes lds_base + 16*l.
-// Issued through inline asm (setting M0 itself) so that the compiler does not treat the
-// write as pending LDS data and wait for it before unrelated LDS reads; the caller owns the
-// load counter.  M0 has no other use in the kernels that call this.
-__device__ __forceinline__ void dma16(const void* src, const void* lds_base) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-        static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_base)));
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(src), "s"(m0)
-                 : "memory");
-}
-
-// 4 bytes per lane from global memory straight into LDS: lane l writes lds_base + 4*l.
-__device__ __forceinline__ void dma4(const void* src, const void* lds_base) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-        static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_base)));
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-                 :
-                 : "v"(src), "s"(m0)
-                 : "memory");
-}
-
-}  // namespace
 
 // ---------------------------------------------------------------------------------------
 // Prefill kernel, bf16 weights: 256 x 256 block tile, 8 wavefronts (2 x 4) of 128 x 64, two
@@ -300,9 +258,6 @@ __device__ __forceinline__ void dma4(const void* src, const void* lds_base) {
 // 2 (c & 1) of the tile's 16: 32 gate rows and the 32 up rows of the same hid columns.
 // ---------------------------------------------------------------------------------------
 
-namespace {
-__device__ __forceinline__ int lds_slot32(int row, int ch) { return row * 4 + (ch ^ ((row >> 1) & 3)); }
-}  // namespace
 
 template <int KIND>
 __global__ __launch_bounds__(512, 1) void gemm_prefill_bf16_kernel(GemmArgs g) {
@@ -1026,6 +981,7 @@ static dim3 prefill_grid(const GemmArgs& g, int max_tiles, int bn) {
 
 hipError_t launch_gemm(const GemmArgs& g, int family, int max_tiles, hipStream_t s) {
     if (max_tiles <= 0) return hipSuccess;
+    if (g.wfmt == kWMXFP8) return launch_gemm_mxfp8(g, max_tiles, s);  // mx.hip
     const bool up = g.kind == kGateUp;
     if (family == kFamSimtF32) {
         const int ncols = up ? g.F / 32 : (g.N + 63) / 64;

@@ -37,7 +37,7 @@ struct DispatchArgs {
 };
 
 enum GemmKind { kGateUp = 0, kDown = 1 };
-enum WeightFmt { kWF32 = 0, kWBF16 = 1, kWNVFP4 = 2 };
+enum WeightFmt { kWF32 = 0, kWBF16 = 1, kWNVFP4 = 2, kWMXFP8 = 3 };
 enum GemmFamily { kFamSimtF32 = 0, kFamPrefill = 1, kFamDecode = 2 };
 
 struct GemmArgs {
@@ -47,7 +47,8 @@ struct GemmArgs {
     const Tile* tiles;
     const int* tile_count;
     const void* w;          // [E, Nw, K] values or [E, Nw, K/2] packed nibbles
-    const uint8_t* wscale;  // [E, Nw, K/16] (NVFP4)
+    const uint8_t* wscale;  // [E, Nw, K/16] (NVFP4) or [E, Nw, K/32] (MXFP8)
+    const uint8_t* ascale;  // MXFP8: E8M0 scales of `a` [rows, K/32] (a holds E4M3 codes)
     const float* gscale;    // [E] or null (NVFP4)
     void* out;              // [A, N]
     int K, N, F;            // reduction length, output columns, gate/up split
@@ -67,6 +68,11 @@ hipError_t launch_select_dispatch_small(const float* logits, int renorm, int32_t
 hipError_t launch_fill_i32(int32_t* p, int n, int value, hipStream_t s);
 hipError_t launch_tiles_from_offsets(const int32_t* offsets, int E, int eb, int ee, int A, int bm, Tile* tiles,
                                      int* tile_count, int cap, hipStream_t s);
+// MXFP8 (mx.hip): bf16 rows [rows, K] -> E4M3 codes [rows, K] + E8M0 scales [rows, K/32];
+// the grouped GEMM on block-scaled fp8 MFMA (256-row tiles).
+hipError_t launch_mx_quantize(const void* in, long rows, int K, uint8_t* codes, uint8_t* scales,
+                              hipStream_t s);
+hipError_t launch_gemm_mxfp8(const GemmArgs& g, int max_tiles, hipStream_t s);
 hipError_t launch_gather_rows(const void* x, const int32_t* sorted_token, void* x_perm, int A,
                               int T, int row_bytes, hipStream_t s);
 hipError_t launch_gemm(const GemmArgs& g, int family, int max_tiles, hipStream_t s);

@@ -1,0 +1,50 @@
+// lds_dma.h -- helpers of the LDS-staged GEMM kernels (gemm.hip, mx.hip): explicit load-counter
+// waits, a block barrier, direct global->LDS loads issued from inline asm (each LDS slot is its
+// own LDS object so that the compiler can tell the slots apart; waits on the load counter are
+// explicit), and the swizzled slot of a 16-byte chunk in a 64-byte LDS row.
+#pragma once
+
+#include "device.h"
+
+namespace moe {
+namespace {
+
+// s_waitcnt operand: vmcnt <= n, lgkmcnt = 0 (expcnt left at its maximum).
+constexpr int vm_wait_lgkm0(int n) { return (n & 15) | (7 << 4) | (0 << 8) | ((n >> 4) << 14); }
+
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+    __builtin_amdgcn_s_waitcnt(vm_wait_lgkm0(N));
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane l writes lds_base + 16*l.
+// Issued through inline asm (setting M0 itself) so that the compiler does not treat the
+// write as pending LDS data and wait for it before unrelated LDS reads; the caller owns the
+// load counter.  M0 has no other use in the kernels that call this.
+__device__ __forceinline__ void dma16(const void* src, const void* lds_base) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+        static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_base)));
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(m0)
+                 : "memory");
+}
+
+// 4 bytes per lane from global memory straight into LDS: lane l writes lds_base + 4*l.
+__device__ __forceinline__ void dma4(const void* src, const void* lds_base) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+        static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_base)));
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+                 :
+                 : "v"(src), "s"(m0)
+                 : "memory");
+}
+
+// 64-byte LDS rows of four 16-byte chunks: chunk ch of row r sits in slot ch ^ ((r >> 1) & 3),
+// so that the fragment reads of 8 consecutive rows at one chunk hit distinct banks.
+__device__ __forceinline__ int lds_slot32(int row, int ch) { return row * 4 + (ch ^ ((row >> 1) & 3)); }
+
+}  // namespace
+}  // namespace moe

@@ -1,0 +1,303 @@
+// mx.hip -- the MXFP8 layer on gfx950's block-scaled fp8 matrix cores.
+//
+// MXFP8 (OCP microscaling formats v1.0): E4M3 elements with one E8M0 scale 2^(s-127) per 32
+// consecutive elements along K; "Hosting Qwen on Blackwell" (section Quantization) deploys its
+// MoE weights in it, and "CuTeDSL at Perplexity" (section Blackwell) notes the per-32-element
+// absolute-maximum reductions its activation quantizers need.  Two kernels:
+//   mx_quantize_kernel        bf16 rows -> E4M3 codes + E8M0 scales, one thread per block of 32
+//                             (x before the gate/up GEMM, hid before the down GEMM)
+//   gemm_prefill_mxfp8_kernel the grouped GEMM of gemm.hip's bf16 prefill kernel (256 x 256
+//                             block tile, 8 wavefronts of 128 x 64, 4-slot LDS ring of 64-byte
+//                             rows filled by direct global->LDS loads) on
+//                             v_mfma_scale_f32_32x32x64_f8f6f4: one 64-wide K stage of the
+//                             ring is one MFMA K step.
+//
+// Operand layout of v_mfma_scale_f32_32x32x64_f8f6f4 (measured on the hardware against exact
+// CPU products): lane l feeds row l & 31 of its operand; lane group g = l >> 5 supplies the
+// K elements [16g, 16g + 16) in bytes 0..15 and [32 + 16g, 48 + 16g) in bytes 16..31, and the
+// E8M0 scale of the 32-element block g (elements [32g, 32g + 32)) in its scale operand.  With
+// 64-byte LDS rows of four 16-byte chunks, lane group g reads chunks g and g + 2.  The result
+// is the usual 32 x 32 accumulator layout: element i of lane l is row 8 (i / 4) + 4 (l >> 5) +
+// (i % 4), column l & 31.
+#include "device.h"
+#include "launch.h"
+#include "lds_dma.h"
+
+namespace moe {
+
+typedef __attribute__((ext_vector_type(8))) int i32x8_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+
+// ---------------------------------------------------------------------------------------
+// Activation quantizer.  Per block of 32 bf16 values v: X = floor(log2 max|v|) - 8 (-127 for an
+// all-zero block, at least -127), scale byte X + 127; element code = the E4M3 value nearest to
+// min(|v| 2^-X, 448), ties to the even code, with the sign bit of v.  Every step is exact in
+// fp32 (bf16 times a power of two), so the codes are a pure function of the bf16 input.
+// ---------------------------------------------------------------------------------------
+
+__device__ __forceinline__ uint32_t e4m3_code(float q) {  // 0 <= q <= 448
+    if (q < 0.015625f) return uint32_t(__builtin_rintf(q * 512.0f));  // subnormal grid m 2^-9
+    const uint32_t u = __float_as_uint(q);
+    const uint32_t e = (u >> 23) - 127u + 7u;           // biased E4M3 exponent, 1..15
+    const uint32_t mant = u & 0x7fffffu;
+    const uint32_t r = mant + 0x7ffffu + ((mant >> 20) & 1u);  // round 23 -> 3 bits, nearest even
+    return (e << 3) + (r >> 20);                         // a carry moves into the exponent
+}
+
+__global__ __launch_bounds__(256) void mx_quantize_kernel(const uint4* __restrict__ in, long nblocks,
+                                                          uint4* __restrict__ codes,
+                                                          uint8_t* __restrict__ scales) {
+    for (long b = long(blockIdx.x) * blockDim.x + threadIdx.x; b < nblocks;
+         b += long(gridDim.x) * blockDim.x) {
+        uint32_t w[16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint4 q = in[b * 4 + i];
+            w[4 * i] = q.x; w[4 * i + 1] = q.y; w[4 * i + 2] = q.z; w[4 * i + 3] = q.w;
+        }
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            amax = fmaxf(amax, fabsf(bf16_lo(w[i])));
+            amax = fmaxf(amax, fabsf(bf16_hi(w[i])));
+        }
+        const uint32_t amax_bits = __float_as_uint(amax);
+        int X = -127;  // floor(log2 amax) - 8 from the exponent field; subnormal amax gives <= -127
+        if (amax > 0.0f) X = max(int((amax_bits >> 23) & 0xffu) - 127 - 8, -127);
+        const float inv = __uint_as_float(uint32_t(127 - X) << 23);  // 2^-X, normal for X in [-127, 119]
+        uint32_t out[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int e = 4 * i + j;                       // element 0..31
+                const uint32_t bits = (e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xffffu);
+                const float v = __uint_as_float(bits << 16);
+                const float q = fminf(fabsf(v) * inv, 448.0f);
+                const uint32_t c = e4m3_code(q) | ((bits >> 8) & 0x80u);
+                word |= c << (8 * j);
+            }
+            out[i] = word;
+        }
+        codes[b * 2] = make_uint4(out[0], out[1], out[2], out[3]);
+        codes[b * 2 + 1] = make_uint4(out[4], out[5], out[6], out[7]);
+        scales[b] = uint8_t(X + 127);
+    }
+}
+
+hipError_t launch_mx_quantize(const void* in, long rows, int K, uint8_t* codes, uint8_t* scales,
+                              hipStream_t s) {
+    const long nb = rows * (K / 32);
+    if (nb <= 0) return hipSuccess;
+    const long want = (nb + 255) / 256;
+    const int blocks = int(want < 16384 ? want : 16384);
+    hipLaunchKernelGGL(mx_quantize_kernel, dim3(blocks), dim3(256), 0, s, static_cast<const uint4*>(in),
+                       nb, reinterpret_cast<uint4*>(codes), scales);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------
+// MXFP8 grouped GEMM, prefill tiles.  a: E4M3 codes [rows, K] (gathered through a_rows for
+// gate/up), ascale: E8M0 [rows, K/32]; w: E4M3 codes [E, Nw, K] row-major, wscale [E, Nw, K/32].
+// Block tile 256 x 256; wavefronts 2 x 4 of 128 x 64: wavefront (wr, wc) holds the 32-row
+// groups 2 mi + wr (mi = 0..3) and two 32-column weight groups.  For gate/up the tile's 256
+// weight rows are 128 gate rows f = 128 nt + r then the 128 matching up rows F + f, and
+// wavefront column wc takes gate group wc and up group 4 + wc, i.e. hid columns
+// 128 nt + 32 wc + (0..31), so SwiGLU applies to accumulators in registers.
+//
+// Pipeline: K in 64-wide stages (64-byte rows), a 4-slot LDS ring filled by dma16 exactly as in
+// the bf16 kernel (each wavefront moves two 16-row groups of activations and two of weights per
+// stage), plus the E8M0 scales: one dma4 per wavefront per stage pair (4 scale bytes = 4 blocks
+// = 2 stages of one row; wavefronts 0-3 activation rows, 4-7 weight rows) into one of three
+// scale slots, issued with the pair's even stage.  Each wavefront issues 5 DMA instructions on
+// even stages and 4 on odd ones, so "stage s+1 landed while s+2 and s+3 are in flight" is
+// always a load count of 9.  A scale slot is rewritten 4 stages after its pair's last read,
+// behind at least one barrier.
+// ---------------------------------------------------------------------------------------
+
+template <int KIND>
+__global__ __launch_bounds__(512, 1) void gemm_prefill_mxfp8_kernel(GemmArgs g) {
+    constexpr int BM = 256, BN = 256;
+    constexpr int HALF = (KIND == kGateUp) ? BN / 2 : BN;
+    __shared__ uint4 sA0[BM * 4], sA1[BM * 4], sA2[BM * 4], sA3[BM * 4];
+    __shared__ uint4 sB0[BN * 4], sB1[BN * 4], sB2[BN * 4], sB3[BN * 4];
+    __shared__ uint32_t tS[3][BM + BN];  // per stage pair: 4 scale bytes per activation row, then per weight row
+
+    const int ncols = (KIND == kGateUp) ? g.F / HALF : (g.N + BN - 1) / BN;
+    const int items = *g.tile_count * ncols;
+    const int run = (items + 7) >> 3;
+    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+    const int item = xcd * run + j;
+    if (j >= run || item >= items) return;
+    const Tile tile = g.tiles[item / ncols];
+    const int e = tile.expert, r0 = tile.row0, r1 = tile.row1;
+    const int nsub = (r1 - r0 + 31) / 32;  // 32-row groups holding rows
+    const int nt = item % ncols;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7
+    const int wr = wave >> 2, wc = wave & 3;
+    const int K = g.K, KB = K / 32;
+    const int Nw = (KIND == kGateUp) ? 2 * g.F : g.N;
+
+    auto weight_row = [&](int r) {  // weight row (of this expert) behind tile row r
+        if (KIND == kGateUp) return r < 128 ? nt * 128 + r : g.F + nt * 128 + (r - 128);
+        return nt * BN + r;
+    };
+    auto act_row = [&](int r) {  // row of `a` behind tile row r (padded rows repeat the last)
+        const int rr = min(r0 + r, r1 - 1);
+        int src = g.a_rows ? g.a_rows[rr] : rr;
+        return src < 0 ? 0 : (src >= g.a_rows_limit ? g.a_rows_limit - 1 : src);
+    };
+    const char* pa[2];
+    const char* pb[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int row = (i * 8 + wave) * 16 + (lane >> 2);
+        const int ch = (lane & 3) ^ ((row >> 1) & 3);
+        pa[i] = static_cast<const char*>(g.a) + size_t(act_row(row)) * K + ch * 16;
+        pb[i] = static_cast<const char*>(g.w) + (size_t(e) * Nw + weight_row(row)) * K + ch * 16;
+    }
+    const char* psc;  // this lane's 4 scale bytes per stage pair
+    {
+        const int row = (wave & 3) * 64 + lane;
+        psc = wave < 4 ? reinterpret_cast<const char*>(g.ascale) + size_t(act_row(row)) * KB
+                       : reinterpret_cast<const char*>(g.wscale) + (size_t(e) * Nw + weight_row(row)) * KB;
+    }
+    const int sc_off = (wave < 4 ? 0 : BM) + (wave & 3) * 64;  // this wavefront's scale rows in a slot
+
+    const int nk = K / 64;
+    const int last = nk - 1;
+    // weight / activation groups of this wavefront (32 rows each)
+    const int gbn0 = (KIND == kGateUp) ? wc : 2 * wc;
+    const int gbn1 = (KIND == kGateUp) ? 4 + wc : 2 * wc + 1;
+    const int g2 = lane >> 5;  // lane group: chunks g2 and g2 + 2, scale block g2
+
+#define MOE_MXISSUE(SA, SB, ST)                                                               \
+    do {                                                                                      \
+        const int st_ = min((ST), last);                                                      \
+        _Pragma("unroll") for (int i = 0; i < 2; ++i)                                         \
+            dma16(pa[i] + st_ * 64, &SA[(i * 8 + wave) * 64]);                                \
+        _Pragma("unroll") for (int i = 0; i < 2; ++i)                                         \
+            dma16(pb[i] + st_ * 64, &SB[(i * 8 + wave) * 64]);                                \
+        if (((ST) & 1) == 0)                                                                  \
+            dma4(psc + (st_ >> 1) * 4, &tS[((ST) >> 1) % 3][sc_off]);                         \
+    } while (0)
+#define MOE_MXFRAG(S, ROW, F)                                                                 \
+    do {                                                                                      \
+        const uint4 lo_ = S[lds_slot32((ROW), g2)];                                           \
+        const uint4 hi_ = S[lds_slot32((ROW), g2 + 2)];                                       \
+        F = i32x8_t{int(lo_.x), int(lo_.y), int(lo_.z), int(lo_.w),                           \
+                    int(hi_.x), int(hi_.y), int(hi_.z), int(hi_.w)};                           \
+    } while (0)
+#define MOE_MXREAD(SA, SB, ST, AF, BF, AS, BS)                                                \
+    do {                                                                                      \
+        const uint8_t* t_ = reinterpret_cast<const uint8_t*>(&tS[((ST) >> 1) % 3][0]);        \
+        const int q_ = ((ST) & 1) * 2 + g2;                                                   \
+        MOE_MXFRAG(SB, gbn0 * 32 + (lane & 31), BF[0]);                                       \
+        MOE_MXFRAG(SB, gbn1 * 32 + (lane & 31), BF[1]);                                       \
+        BS[0] = t_[(BM + gbn0 * 32 + (lane & 31)) * 4 + q_];                                  \
+        BS[1] = t_[(BM + gbn1 * 32 + (lane & 31)) * 4 + q_];                                  \
+        _Pragma("unroll") for (int mi = 0; mi < 4; ++mi) {                                    \
+            MOE_MXFRAG(SA, (mi * 2 + wr) * 32 + (lane & 31), AF[mi]);                         \
+            AS[mi] = t_[((mi * 2 + wr) * 32 + (lane & 31)) * 4 + q_];                         \
+        }                                                                                     \
+    } while (0)
+#define MOE_MXMFMA(AF, BF, AS, BS)                                                            \
+    do {                                                                                      \
+        _Pragma("unroll") for (int mi = 0; mi < 4; ++mi) {                                    \
+            if (mi * 2 + wr < nsub) {                                                         \
+                _Pragma("unroll") for (int ni = 0; ni < 2; ++ni) acc[mi][ni] =                \
+                    __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(AF[mi], BF[ni], acc[mi][ni], \
+                                                                    0, 0, 0, AS[mi], 0, BS[ni]); \
+            }                                                                                 \
+        }                                                                                     \
+    } while (0)
+
+    f32x16_t acc[4][2];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.0f;
+    // One set of fragment registers: the MFMAs of stage s are issued first, then the fragments
+    // of stage s+1 are read into the same registers (the MFMAs have taken their operands by
+    // then); the other wavefront on the SIMD covers the wait.
+    i32x8_t af[4], bf[2];
+    int as[4], bs[2];
+
+    MOE_MXISSUE(sA0, sB0, 0);
+    MOE_MXISSUE(sA1, sB1, 1);
+    MOE_MXISSUE(sA2, sB2, 2);
+    wait_vm_lgkm0<9>();  // stage 0 (and its scales) landed
+    block_barrier();
+    MOE_MXREAD(sA0, sB0, 0, af, bf, as, bs);
+    MOE_MXISSUE(sA3, sB3, 3);
+    for (int s = 0;; s += 4) {
+        MOE_MXMFMA(af, bf, as, bs);
+        if (s + 1 >= nk) break;
+        wait_vm_lgkm0<9>();  // stage s+1 landed (s+2, s+3 in flight); every wavefront read stage s
+        block_barrier();
+        MOE_MXREAD(sA1, sB1, s + 1, af, bf, as, bs);
+        MOE_MXISSUE(sA0, sB0, s + 4);
+        MOE_MXMFMA(af, bf, as, bs);
+        if (s + 2 >= nk) break;
+        wait_vm_lgkm0<9>();
+        block_barrier();
+        MOE_MXREAD(sA2, sB2, s + 2, af, bf, as, bs);
+        MOE_MXISSUE(sA1, sB1, s + 5);
+        MOE_MXMFMA(af, bf, as, bs);
+        if (s + 3 >= nk) break;
+        wait_vm_lgkm0<9>();
+        block_barrier();
+        MOE_MXREAD(sA3, sB3, s + 3, af, bf, as, bs);
+        MOE_MXISSUE(sA2, sB2, s + 6);
+        MOE_MXMFMA(af, bf, as, bs);
+        if (s + 4 >= nk) break;
+        wait_vm_lgkm0<9>();
+        block_barrier();
+        MOE_MXREAD(sA0, sB0, s + 4, af, bf, as, bs);
+        MOE_MXISSUE(sA3, sB3, s + 7);
+    }
+    wait_vm_lgkm0<0>();
+#undef MOE_MXISSUE
+#undef MOE_MXFRAG
+#undef MOE_MXREAD
+#undef MOE_MXMFMA
+
+    uint16_t* out = static_cast<uint16_t*>(g.out);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+        if (mi * 2 + wr >= nsub) continue;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int row = r0 + (mi * 2 + wr) * 32 + 8 * (i / 4) + 4 * g2 + (i % 4);
+            if (row >= r1) continue;
+            if (KIND == kGateUp) {
+                const int col = nt * HALF + wc * 32 + (lane & 31);
+                out[size_t(row) * g.F + col] = (uint16_t)bf16_rne(silu_mul(acc[mi][0][i], acc[mi][1][i]));
+            } else {
+#pragma unroll
+                for (int ni = 0; ni < 2; ++ni) {
+                    const int col = nt * BN + wc * 64 + ni * 32 + (lane & 31);
+                    if (col < g.N) out[size_t(row) * g.N + col] = (uint16_t)bf16_rne(acc[mi][ni][i]);
+                }
+            }
+        }
+    }
+}
+
+// Blocks: (row tile, column tile) pairs, a multiple of 8 so that every XCD walks the same number.
+hipError_t launch_gemm_mxfp8(const GemmArgs& g, int max_tiles, hipStream_t s) {
+    if (max_tiles <= 0) return hipSuccess;
+    const int ncols = g.kind == kGateUp ? g.F / 128 : (g.N + 255) / 256;
+    const dim3 grid(((max_tiles * ncols + 7) / 8) * 8);
+    if (g.kind == kGateUp)
+        hipLaunchKernelGGL((gemm_prefill_mxfp8_kernel<kGateUp>), grid, dim3(512), 0, s, g);
+    else
+        hipLaunchKernelGGL((gemm_prefill_mxfp8_kernel<kDown>), grid, dim3(512), 0, s, g);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -15,16 +15,16 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmoe_mi355x.so")
 
 MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_DEVICE = range(5)
-MOE_F32, MOE_BF16, MOE_NVFP4 = 0, 1, 2
+MOE_F32, MOE_BF16, MOE_NVFP4, MOE_MXFP8 = 0, 1, 2, 3
 GATE_UP_SWIGLU, DOWN = 0, 1
 PATH_AUTO, PATH_PREFILL, PATH_DECODE = 0, 1, 2
-DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "nvfp4": MOE_NVFP4}
+DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "nvfp4": MOE_NVFP4, "mxfp8": MOE_MXFP8}
 PATHS = {"auto": PATH_AUTO, "prefill": PATH_PREFILL, "decode": PATH_DECODE}
 
 #: every symbol the header declares
 EXPORTS = ("moe_status_string", "moe_workspace_size", "moe_packed_weights_size", "moe_pack_weights",
            "moe_route", "moe_permute", "moe_grouped_gemm", "moe_combine", "moe_forward",
-           "moe_probe_mfma_bf16", "moe_probe_read")
+           "moe_quantize_mxfp8", "moe_probe_mfma_bf16", "moe_probe_read")
 LAYOUT_ROW_MAJOR, LAYOUT_PACKED = 0, 1
 
 
@@ -78,6 +78,8 @@ def load() -> C.CDLL:
             L.moe_grouped_gemm.argtypes = [P, i32, vp, vp, vp, C.POINTER(ExpertWeights), vp, vp, sz, vp]
             L.moe_combine.restype = i32
             L.moe_combine.argtypes = [P, vp, vp, vp, vp, vp]
+            L.moe_quantize_mxfp8.restype = i32
+            L.moe_quantize_mxfp8.argtypes = [vp, C.c_int64, C.c_int32, vp, vp, vp]
             L.moe_probe_mfma_bf16.restype = i32
             L.moe_probe_mfma_bf16.argtypes = [C.c_int32, C.c_int32, vp, vp]
             L.moe_probe_read.restype = i32
@@ -173,6 +175,13 @@ def forward(p, x, w_router, bias, w: ExpertWeights, y, ws, topk_ids=None, topk_w
                               _ptr(topk_ids), _ptr(topk_w), _ptr(counts), _ptr(offsets),
                               _ptr(sorted_token), _ptr(inv_perm), _ptr(ws),
                               ws.numel() * ws.element_size(), _stream(stream)), "moe_forward")
+
+
+def quantize_mxfp8(x, codes, scales, stream=None):
+    """MXFP8 quantization of bf16 rows x [rows, K] into codes [rows, K] / scales [rows, K/32]."""
+    rows, K = x.shape
+    _check(load().moe_quantize_mxfp8(_ptr(x), int(rows), int(K), _ptr(codes), _ptr(scales),
+                                     _stream(stream)), "moe_quantize_mxfp8")
 
 
 def probe_mfma_bf16(blocks, iters, out, stream=None):

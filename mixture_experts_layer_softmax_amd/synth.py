@@ -17,6 +17,7 @@ decode{1,8,64}  1/8/64  4096    128  8   1536 bf16 / bf16      none
 nvfp4_decode    16      4096    256  8   2048 nvfp4 / bf16     none
 nvfp4_prefill   8192    4096    256  8   2048 nvfp4 / bf16     +beta on a 10 % hot set
 prefill6000     6000    4096    128  8   1536 bf16 / bf16      none (about 375 rows/expert)
+mxfp8_prefill   4096    4096    128  8   1536 mxfp8 / bf16     as prefill (same seed, same routing)
 =============== ======= ====== ==== === ==== ================ ========================
 
 ``prefill6000`` is the prefill example of "Hosting Qwen on Blackwell" (section Prefill: an
@@ -85,6 +86,9 @@ WORKLOADS = {
     "nvfp4_decode": Workload("nvfp4_decode", 16, 4096, 256, 8, 2048, "bf16", "nvfp4", 404, "none"),
     "nvfp4_prefill": Workload("nvfp4_prefill", 8192, 4096, 256, 8, 2048, "bf16", "nvfp4", 505, "hot"),
     "prefill6000": Workload("prefill6000", 6000, 4096, 128, 8, 1536, "bf16", "bf16", 606, "none"),
+    # the prefill workload's seed: same tokens, router and bias (same routing), its expert
+    # weights drawn from the same streams and encoded in MXFP8 instead of bf16
+    "mxfp8_prefill": Workload("mxfp8_prefill", 4096, 4096, 128, 8, 1536, "bf16", "mxfp8", 202, "normal"),
 }
 
 T_X, T_WR, T_BIAS, T_W13, T_W2, T_HOT = range(6)
@@ -130,6 +134,27 @@ def _e4m3_codes(s: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     t = torch.from_numpy(np.minimum(s, np.float32(448.0)).astype(np.float32))
     f8 = t.to(torch.float8_e4m3fn)
     return f8.view(torch.uint8).numpy().copy(), f8.to(torch.float32).numpy()
+
+
+def quantize_mxfp8(w: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Encode one expert matrix ``w[N, K]`` (float32) as MXFP8 along K (OCP microscaling
+    formats v1.0): per block of 32, the shared exponent X = floor(log2(amax)) - 8 (-127 for an
+    all-zero block), stored as the E8M0 byte X + 127, and elements w / 2^X clamped to +-448 and
+    rounded to the nearest E4M3 value (ties to even).  Returns ``(codes[N, K], scales[N, K/32])``.
+    """
+    import torch
+
+    n, k = w.shape
+    assert k % 32 == 0
+    blocks = np.ascontiguousarray(w, dtype=np.float32).reshape(n, k // 32, 32)
+    amax = np.max(np.abs(blocks), axis=2)
+    _, ex = np.frexp(amax)  # amax = m 2^ex with m in [0.5, 1): floor(log2 amax) = ex - 1
+    X = np.where(amax > 0, ex.astype(np.int32) - 1 - 8, -127)
+    X = np.clip(X, -127, 127)
+    v = np.ldexp(blocks, (-X)[:, :, None]).astype(np.float32)
+    v = np.clip(v, np.float32(-448.0), np.float32(448.0))
+    codes = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+    return codes.reshape(n, k), (X + 127).astype(np.uint8)
 
 
 def quantize_nvfp4(w: np.ndarray) -> tuple[np.ndarray, np.ndarray, np.float32]:
@@ -224,6 +249,18 @@ def gen_experts(wl: Workload, experts=None) -> dict:
             w2[i] = b if wl.wdt == "f32" else to_bf16_bits(b)
 
         out.update(w13=w13, w2=w2)
+    elif wl.wdt == "mxfp8":
+        w13 = np.empty((n, 2 * F, H), dtype=np.uint8)
+        w2 = np.empty((n, H, F), dtype=np.uint8)
+        s13 = np.empty((n, 2 * F, H // 32), dtype=np.uint8)
+        s2 = np.empty((n, H, F // 32), dtype=np.uint8)
+
+        def job(i):
+            e = ids[i]
+            w13[i], s13[i] = quantize_mxfp8(_expert_matrix(wl, T_W13, e, (2 * F, H)))
+            w2[i], s2[i] = quantize_mxfp8(_expert_matrix(wl, T_W2, e, (H, F)))
+
+        out.update(w13=w13, w2=w2, w13_scale=s13, w2_scale=s2)
     else:
         w13 = np.empty((n, 2 * F, H // 2), dtype=np.uint8)
         w2 = np.empty((n, H, F // 2), dtype=np.uint8)

@@ -20,6 +20,18 @@
  *           a = t*k + j by expert: sorted_token[pos] = t, inv_perm[a] = pos.
  *  expert   SwiGLU FFN (SiLU(gate) * up, then down), gate rows first in W13; no biases.
  *  combine  y[t] = sum_j w[t,j] * y_perm[inv_perm[t*k+j]].
+ *  MXFP8    (OCP microscaling formats v1.0, the MXFP8 scheme "Hosting Qwen on Blackwell" deploys,
+ *           section Quantization, and whose 32-element absolute-maximum reductions "CuTeDSL at
+ *           Perplexity" mentions, section Blackwell): weights are E4M3 values with one E8M0
+ *           scale (2^(s-127)) per 32 consecutive elements along K.  The layer quantizes its
+ *           activations the same way on the fly: x before the gate/up projection and hid before
+ *           the down projection, each block of 32 along K taking the shared exponent
+ *           X = floor(log2(max|v|)) - 8 (8 = the largest E4M3 exponent; X = -127 for an all-zero
+ *           block, X clamped to [-127, 127]) and elements v / 2^X clamped to +-448 and rounded to
+ *           the nearest E4M3 value, ties to the even code.  What gets quantized are the layer's
+ *           bf16 activations: x is bf16 already, and hid, an activation of the layer like x, is
+ *           rounded to bf16 (nearest even) first.  Products of decoded values are then
+ *           accumulated in double like every other format.
  *  held     expert parallelism with replicated inputs (same article, same section: with
  *           tensor parallelism the local dispatch selects only the tokens routed to the
  *           experts of the current rank, and the local combine is followed by an all-reduce):
@@ -39,7 +51,7 @@
 #include <omp.h>
 #endif
 
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_NVFP4 = 2 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_NVFP4 = 2, ORC_MXFP8 = 3 };
 
 /* ------------------------------------------------------------------------------------ */
 /* decoders                                                                              */
@@ -72,6 +84,9 @@ static double dec_e4m3(uint8_t code) {
     return s ? -mag : mag;
 }
 
+/* E8M0 (OCP MX v1.0 scale): 2^(code - 127); code 255 is NaN. */
+static double dec_e8m0(uint8_t code) { return code == 255 ? NAN : ldexp(1.0, (int)code - 127); }
+
 /* Decoded values of every E2M1 and E4M3 code, filled once from the decoders above. */
 static double g_e2m1[16], g_e4m3[256];
 static int g_tables_ready = 0;
@@ -97,12 +112,68 @@ void oracle_decode_e2m1(const uint8_t* codes, double* out, int64_t n) {
 void oracle_decode_e4m3(const uint8_t* codes, double* out, int64_t n) {
     for (int64_t i = 0; i < n; ++i) out[i] = dec_e4m3(codes[i]);
 }
+void oracle_decode_e8m0(const uint8_t* codes, double* out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = dec_e8m0(codes[i]);
+}
+
+/* Nearest E4M3 code of a magnitude a in [0, 448]; on a tie the code with the even mantissa
+ * (even code) wins.  Binary search over the ascending positive codes 0..126. */
+static uint8_t e4m3_nearest(double a) {
+    int lo = 0, hi = 126; /* g_e4m3[lo] <= a <= g_e4m3[hi] */
+    while (hi - lo > 1) {
+        int mid = (lo + hi) / 2;
+        if (g_e4m3[mid] <= a) lo = mid; else hi = mid;
+    }
+    double dl = a - g_e4m3[lo], dh = g_e4m3[hi] - a;
+    if (dl < dh) return (uint8_t)lo;
+    if (dh < dl) return (uint8_t)hi;
+    return (uint8_t)((lo & 1) ? hi : lo);
+}
+
+/* MX quantization of one block of 32 values (see the header): codes[32], the E8M0 scale code,
+ * and the decoded values (what the quantized block stands for). */
+static void mx_quantize_block(const double* v, uint8_t* codes, uint8_t* scale, double* dec) {
+    double amax = 0.0;
+    for (int i = 0; i < 32; ++i) amax = fmax(amax, fabs(v[i]));
+    int X = -127;
+    if (amax > 0.0) {
+        int ex;
+        frexp(amax, &ex); /* amax = m 2^ex, m in [0.5, 1): floor(log2 amax) = ex - 1 */
+        X = ex - 1 - 8;
+        if (X < -127) X = -127;
+        if (X > 127) X = 127;
+    }
+    *scale = (uint8_t)(X + 127);
+    for (int i = 0; i < 32; ++i) {
+        double q = fabs(ldexp(v[i], -X));
+        if (q > 448.0) q = 448.0;
+        uint8_t c = e4m3_nearest(q);
+        int neg = signbit(v[i]) != 0;
+        codes[i] = (uint8_t)(c | (neg ? 0x80 : 0));
+        dec[i] = (neg ? -g_e4m3[c] : g_e4m3[c]) * ldexp(1.0, X);
+    }
+}
+
+/* MX quantization of n blocks of 32 values each (v[n*32]): codes[n*32], scales[n], and the
+ * decoded values dec[n*32] (any output may be NULL). */
+void oracle_mx_quantize(const double* v, int64_t nblocks, uint8_t* codes, uint8_t* scales, double* dec) {
+    init_tables();
+#pragma omp parallel for schedule(static)
+    for (int64_t b = 0; b < nblocks; ++b) {
+        uint8_t c[32], s;
+        double d[32];
+        mx_quantize_block(v + b * 32, c, &s, d);
+        if (codes) memcpy(codes + b * 32, c, 32);
+        if (scales) scales[b] = s;
+        if (dec) memcpy(dec + b * 32, d, sizeof d);
+    }
+}
 
 /* Element (n, k) of one expert weight matrix with K columns, decoded to double. */
 typedef struct {
     int dt;                 /* ORC_F32 | ORC_BF16 | ORC_NVFP4 */
     const void* w;          /* [rows, K] values, or packed nibbles [rows, K/2] */
-    const uint8_t* scale;   /* NVFP4: E4M3 [rows, K/16] */
+    const uint8_t* scale;   /* NVFP4: E4M3 [rows, K/16]; MXFP8: E8M0 [rows, K/32] */
     double gscale;          /* NVFP4: per-expert fp32 second-level scale */
     int64_t K;
 } wmat;
@@ -110,6 +181,9 @@ typedef struct {
 static double wget(const wmat* m, int64_t n, int64_t k) {
     if (m->dt == ORC_F32) return ((const float*)m->w)[n * m->K + k];
     if (m->dt == ORC_BF16) return (double)dec_bf16_f(((const uint16_t*)m->w)[n * m->K + k]);
+    if (m->dt == ORC_MXFP8)
+        return g_e4m3[((const uint8_t*)m->w)[n * m->K + k]] *
+               ldexp(1.0, (int)m->scale[n * (m->K / 32) + k / 32] - 127);
     {
         uint8_t byte = ((const uint8_t*)m->w)[n * (m->K / 2) + k / 2];
         uint8_t code = (k & 1) ? (byte >> 4) : (byte & 15); /* even k in the low nibble */
@@ -238,6 +312,11 @@ static void expert_mats(const experts_t* ex, int64_t e, wmat* g13, wmat* g2) {
         g2->scale = ex->w2_scale + e * H * (F / 16);
         g13->gscale = ex->w13_gscale ? ex->w13_gscale[e] : 1.0;
         g2->gscale = ex->w2_gscale ? ex->w2_gscale[e] : 1.0;
+    } else if (ex->wdt == ORC_MXFP8) {
+        if (ex->w13) g13->w = (const uint8_t*)ex->w13 + e * (2 * F) * H;
+        g2->w = (const uint8_t*)ex->w2 + e * H * F;
+        if (ex->w13_scale) g13->scale = ex->w13_scale + e * (2 * F) * (H / 32);
+        g2->scale = ex->w2_scale + e * H * (F / 32);
     } else {
         size_t es = ex->wdt == ORC_F32 ? 4 : 2;
         if (ex->w13) g13->w = (const char*)ex->w13 + (size_t)(e * 2 * F * H) * es;
@@ -245,7 +324,25 @@ static void expert_mats(const experts_t* ex, int64_t e, wmat* g13, wmat* g2) {
     }
 }
 
-/* hid[0:F] = silu(W13[e][0:F] . x) * (W13[e][F:2F] . x), silu(g) = g / (1 + e^-g), in double. */
+/* v rounded to the nearest bf16 value (8 significant bits), ties to even; directly from
+ * double (no intermediate float), bf16 subnormals on the grid 2^-133. */
+static double round_bf16(double v) {
+    if (v == 0.0 || !isfinite(v)) return v;
+    int e;
+    frexp(v, &e); /* |v| = m 2^e, m in [0.5, 1) */
+    int q = e - 8; /* quantum of 8 significant bits */
+    if (q < -133) q = -133;
+    return ldexp(nearbyint(ldexp(v, -q)), q); /* nearbyint: round to nearest even */
+}
+
+/* Replace v[0:n] by its MX-quantized value (MXFP8 layers quantize their activations). */
+static void mx_requantize(double* v, int64_t n) {
+    uint8_t c[32], s;
+    for (int64_t b = 0; b < n / 32; ++b) mx_quantize_block(v + 32 * b, c, &s, v + 32 * b);
+}
+
+/* hid[0:F] = silu(W13[e][0:F] . x) * (W13[e][F:2F] . x), silu(g) = g / (1 + e^-g), in double.
+ * (For MXFP8 the caller passes the MX-quantized x.) */
 static void gate_up_row(const experts_t* ex, int64_t e, const double* x, double* hid) {
     wmat g13, g2;
     expert_mats(ex, e, &g13, &g2);
@@ -260,16 +357,25 @@ static void gate_up_row(const experts_t* ex, int64_t e, const double* x, double*
     }
 }
 
-/* y[0:H] = W2[e] . hid, in double. */
+/* y[0:H] = W2[e] . hid, in double (for MXFP8, W2[e] . MX(hid)). */
 static void down_row(const experts_t* ex, int64_t e, const double* hid, double* y) {
     wmat g13, g2;
     expert_mats(ex, e, &g13, &g2);
     int64_t H = ex->H, F = ex->F;
+    const double* h_in = hid;
+    double* hq = NULL;
+    if (ex->wdt == ORC_MXFP8) {
+        hq = (double*)malloc(sizeof(double) * (size_t)F);
+        for (int64_t f = 0; f < F; ++f) hq[f] = round_bf16(hid[f]); /* hid is a bf16 activation */
+        mx_requantize(hq, F);
+        h_in = hq;
+    }
     for (int64_t h = 0; h < H; ++h) {
         double s = 0.0;
-        for (int64_t f = 0; f < F; ++f) s += wget(&g2, h, f) * hid[f];
+        for (int64_t f = 0; f < F; ++f) s += wget(&g2, h, f) * h_in[f];
         y[h] = s;
     }
+    free(hq);
 }
 
 /* Expert FFN of a list of assignment rows: row r runs expert row_expert[r] on token
@@ -289,6 +395,7 @@ void oracle_expert_rows(int64_t H, int64_t F, int act_dt, int wdt, const void* x
         for (int64_t r = 0; r < nrows; ++r) {
             int64_t t = row_token[r];
             for (int64_t h = 0; h < H; ++h) xr[h] = (double)act_f(x, act_dt, t * H + h);
+            if (wdt == ORC_MXFP8) mx_requantize(xr, H);
             gate_up_row(&ex, row_expert[r], xr, hid);
             if (out) down_row(&ex, row_expert[r], hid, out + r * H);
             if (hid_out) memcpy(hid_out + r * F, hid, sizeof(double) * (size_t)F);

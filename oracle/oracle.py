@@ -21,8 +21,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "moe_oracle.c")
 _OUT = os.path.join(_HERE, "_build", "libmoe_oracle.so")
 
-F32, BF16, NVFP4 = 0, 1, 2
-_DT = {"f32": F32, "bf16": BF16, "nvfp4": NVFP4}
+F32, BF16, NVFP4, MXFP8 = 0, 1, 2, 3
+_DT = {"f32": F32, "bf16": BF16, "nvfp4": NVFP4, "mxfp8": MXFP8}
 
 _lock = threading.Lock()
 _lib = None
@@ -59,8 +59,9 @@ def lib() -> C.CDLL:
                                              vp, vp, vp, vp]
             L.oracle_down_rows.argtypes = [i64, i64, i32, vp, vp, vp, i64, vp, vp, vp]
             L.oracle_combine.argtypes = [i64, i32, i64, vp, vp, vp, vp]
-            for n in ("oracle_decode_bf16", "oracle_decode_e2m1", "oracle_decode_e4m3"):
+            for n in ("oracle_decode_bf16", "oracle_decode_e2m1", "oracle_decode_e4m3", "oracle_decode_e8m0"):
                 getattr(L, n).argtypes = [vp, vp, i64]
+            L.oracle_mx_quantize.argtypes = [vp, i64, vp, vp, vp]
             L.oracle_set_threads.argtypes = [i32]
             L.oracle_max_threads.restype = i32
             _lib = L
@@ -98,6 +99,29 @@ def decode_e4m3(codes: np.ndarray) -> np.ndarray:
     out = np.empty(c.shape, dtype=np.float64)
     lib().oracle_decode_e4m3(_P(c), _P(out), c.size)
     return out
+
+
+def decode_e8m0(codes: np.ndarray) -> np.ndarray:
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(c.shape, dtype=np.float64)
+    lib().oracle_decode_e8m0(_P(c), _P(out), c.size)
+    return out
+
+
+def mx_quantize(values: np.ndarray):
+    """MX (E4M3 + E8M0 per 32 along the last axis) quantization of values given as float64,
+    float32 or bf16 bits: returns (codes uint8 [..., K], scales uint8 [..., K/32],
+    decoded float64 [..., K])."""
+    v = values
+    if v.dtype == np.uint16:
+        v = decode_bf16(v)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    assert v.shape[-1] % 32 == 0
+    codes = np.empty(v.shape, dtype=np.uint8)
+    scales = np.empty(v.shape[:-1] + (v.shape[-1] // 32,), dtype=np.uint8)
+    dec = np.empty(v.shape, dtype=np.float64)
+    lib().oracle_mx_quantize(_P(v), v.size // 32, _P(codes), _P(scales), _P(dec))
+    return codes, scales, dec
 
 
 # ---------------------------------------------------------------------------------------
@@ -172,7 +196,7 @@ def expert_rows(inputs: dict, wdt: str, ffn: int, row_token, row_expert, want_hi
     g = lambda k: None if inputs.get(k) is None else np.ascontiguousarray(inputs[k])
     w13, w2 = g("w13"), g("w2")
     s13, s2, g13, g2 = g("w13_scale"), g("w2_scale"), g("w13_gscale"), g("w2_gscale")
-    if wdt == "nvfp4":
+    if wdt in ("nvfp4", "mxfp8"):
         assert w13.dtype == np.uint8 and s13 is not None and s2 is not None
     lib().oracle_expert_rows(H, ffn, _act_dt(x), _DT[wdt], _P(x), _P(w13), _P(w2), _P(s13), _P(s2),
                              _P(g13), _P(g2), n, _P(rt), _P(re), _P(out), _P(hid))

@@ -41,6 +41,9 @@ def dense_weights(inputs, wdt):
         return inputs["w13"].astype(np.float64), inputs["w2"].astype(np.float64)
     if wdt == "bf16":
         return bf16_to_f64(inputs["w13"]), bf16_to_f64(inputs["w2"])
+    if wdt == "mxfp8":
+        return tuple(e4m3_to_f64(inputs[w]) * np.repeat(np.exp2(inputs[s].astype(np.float64) - 127), 32, axis=2)
+                     for w, s in (("w13", "w13_scale"), ("w2", "w2_scale")))
     out = []
     for w, s, g in (("w13", "w13_scale", "w13_gscale"), ("w2", "w2_scale", "w2_gscale")):
         p = inputs[w]
@@ -50,6 +53,28 @@ def dense_weights(inputs, wdt):
         gs = inputs[g].astype(np.float64)[:, None, None]
         out.append(vals * sc * gs)
     return out[0], out[1]
+
+
+# the 127 non-negative finite E4M3 values in code order (torch's float8_e4m3fn decode)
+E4M3_POS = torch.arange(127, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def mx_round_trip(v):
+    """MX quantization of a float64 vector (OCP MX v1.0: per 32 elements the E8M0 exponent
+    X = floor(log2 amax) - 8, elements v / 2^X clamped to +-448 and rounded to the nearest E4M3
+    value, ties to the even code), returned decoded."""
+    b = np.asarray(v, dtype=np.float64).reshape(-1, 32)
+    amax = np.abs(b).max(axis=1)
+    X = np.full(amax.shape, -127.0)
+    nz = amax > 0
+    X[nz] = np.clip(np.floor(np.log2(amax[nz])) - 8, -127, 127)
+    q = np.minimum(np.abs(b) * np.exp2(-X)[:, None], 448.0)
+    hi = np.clip(np.searchsorted(E4M3_POS, q, side="left"), 1, 126)  # E4M3_POS[hi-1] < q <= E4M3_POS[hi]
+    lo = hi - 1
+    dl, dh = q - E4M3_POS[lo], E4M3_POS[hi] - q
+    code = np.where(dl < dh, lo, np.where(dh < dl, hi, np.where(lo % 2 == 0, lo, hi)))
+    code = np.where(q == 0, 0, code)
+    return (np.copysign(E4M3_POS[code], b) * np.exp2(X)[:, None]).reshape(np.shape(v))
 
 
 def select(logits, k, renormalize=True):
@@ -76,6 +101,8 @@ def layer(inputs, logits, k, wdt, renormalize=True, keep=None):
     F = w2.shape[2]
     ids, w = select(logits, k, renormalize)
     y = np.zeros_like(x)
+    if wdt == "mxfp8":  # the layer quantizes its activations before each projection
+        x = np.stack([mx_round_trip(r) for r in x])
     for t in range(x.shape[0]):
         for j in range(k):
             e = ids[t, j]
@@ -84,5 +111,8 @@ def layer(inputs, logits, k, wdt, renormalize=True, keep=None):
             g = w13[e, :F] @ x[t]
             u = w13[e, F:] @ x[t]
             h = g / (1.0 + np.exp(-g)) * u
+            if wdt == "mxfp8":  # hid, a bf16 activation, rounded to bf16 and MX-quantized
+                m, ex = np.frexp(h)
+                h = mx_round_trip(np.ldexp(np.rint(m * 256.0) / 256.0, ex))
             y[t] += w[t, j] * (w2[e] @ h)
     return y, ids, w

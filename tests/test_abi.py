@@ -45,10 +45,13 @@ def test_workspace_size_of_every_workload(L, name):
     p = lib.problem(wl.tokens, wl.hidden, wl.experts, wl.top_k, wl.ffn, wl.act, wl.wdt)
     n = lib.workspace_size(p)
     A = wl.assignments
-    # the intermediates dominate: hid [A,F] and y_perm [A,H]
+    # the intermediates dominate: hid [A,F] and y_perm [A,H] (+ their MXFP8 copies: codes and scales)
     act = 4 if wl.act == "f32" else 2
-    assert n >= A * (wl.ffn + wl.hidden) * act
-    assert n < A * (wl.ffn + wl.hidden) * act + 64 * 2 ** 20
+    inter = A * (wl.ffn + wl.hidden) * act
+    if wl.wdt == "mxfp8":
+        inter += A * (wl.ffn + wl.hidden) * 33 // 32
+    assert n >= inter
+    assert n < inter + 64 * 2 ** 20
 
 
 FAKE = 1 << 20  # an aligned address that is never dereferenced: validation fails first
@@ -74,6 +77,9 @@ def _call_route(L, p, x=FAKE, wr=FAKE, ids=FAKE, w=FAKE, ws=FAKE, nbytes=1 << 40
     (dict(act="f32", wdt="bf16"), lib.MOE_ERR_UNSUPPORTED),
     (dict(act="bf16", wdt="f32"), lib.MOE_ERR_UNSUPPORTED),
     (dict(act="f32", wdt="nvfp4"), lib.MOE_ERR_UNSUPPORTED),
+    (dict(act="f32", wdt="mxfp8"), lib.MOE_ERR_UNSUPPORTED),
+    (dict(wdt="mxfp8", hidden=192), lib.MOE_ERR_UNSUPPORTED),
+    (dict(wdt="mxfp8", ffn=192), lib.MOE_ERR_UNSUPPORTED),
 ])
 def test_problem_validation(L, kw, status):
     base = dict(tokens=16, hidden=256, experts=8, top_k=2, ffn=128, act="bf16", wdt="bf16")
@@ -122,6 +128,23 @@ def test_gemm_and_forward_validation(L):
     assert L.moe_pack_weights(C.byref(pb), V(FAKE), None, V(FAKE), None, None) == lib.MOE_ERR_INVALID_ARGUMENT
     assert L.moe_pack_weights(C.byref(lib.problem(16, 192, 8, 2, 128)), V(FAKE), None, V(FAKE + 4096),
                               None, None) == lib.MOE_ERR_UNSUPPORTED
+
+
+def test_mxfp8_validation(L):
+    V = C.c_void_p
+    p = lib.problem(16, 256, 8, 2, 128, wdt="mxfp8")
+    w = lib.ExpertWeights(FAKE, FAKE, None, None, None, None, 0)  # MXFP8 without scales
+    assert L.moe_forward(C.byref(p), V(FAKE), V(FAKE), None, C.byref(w), V(FAKE), None, None, None,
+                         None, None, None, V(FAKE), 1 << 40, None) == lib.MOE_ERR_INVALID_ARGUMENT
+    w = lib.ExpertWeights(FAKE, FAKE, FAKE, FAKE, None, None, 1)  # packed layout: bf16 only
+    assert L.moe_forward(C.byref(p), V(FAKE), V(FAKE), None, C.byref(w), V(FAKE), None, None, None,
+                         None, None, None, V(FAKE), 1 << 40, None) == lib.MOE_ERR_INVALID_ARGUMENT
+    q = L.moe_quantize_mxfp8
+    assert q(V(FAKE), 4, 48, V(FAKE), V(FAKE), None) == lib.MOE_ERR_INVALID_ARGUMENT    # K % 32
+    assert q(V(FAKE), -1, 64, V(FAKE), V(FAKE), None) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert q(V(FAKE + 8), 4, 64, V(FAKE), V(FAKE), None) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert q(V(FAKE), 4, 64, None, V(FAKE), None) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert q(None, 0, 64, None, None, None) == lib.MOE_OK                               # no rows
 
 
 def test_probe_validation(L):

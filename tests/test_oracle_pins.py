@@ -64,6 +64,66 @@ def test_e2m1_decoder_matches_spec_table():
     assert np.signbit(got[8])  # code 0b1000 is negative zero
 
 
+def test_e8m0_decoder_is_a_power_of_two_per_code():
+    """OCP MX v1.0 scale format: code c stands for 2^(c - 127); 255 is NaN."""
+    d = O.decode_e8m0(np.arange(256, dtype=np.uint8))
+    assert np.array_equal(d[:255], np.exp2(np.arange(255) - 127.0)) and np.isnan(d[255])
+
+
+def test_mx_quantizer_hand_values():
+    """Blocks worked by hand from the OCP MX definition (shared exponent floor(log2 amax) - 8,
+    E4M3 elements clamped to 448, nearest even)."""
+    def q(first, rest=0.0):
+        v = np.full(32, rest)
+        v[0] = first
+        c, sc, d = O.mx_quantize(v)
+        return int(c[0]), int(sc[0]), float(d[0])
+    assert q(1.0) == (0x78, 119, 1.0)            # 1.0 / 2^-8 = 256 = E4M3 0.1111.000
+    assert q(1.75) == (0x7E, 119, 1.75)          # 448: the largest E4M3 value
+    assert q(1.99)[:2] == (0x7E, 119)            # 509 clamps to 448
+    assert q(-3.0) == (0x80 | 0x78 | 0x04, 120, -3.0)  # 384 = 1.5 * 2^8 -> 0.1111.100, sign bit
+    c, sc, d = O.mx_quantize(np.zeros(32))
+    assert np.all(c == 0) and sc[0] == 0 and np.all(d == 0)
+    # 1 + 1/16 scales to 272, halfway between 256 (code 0x78, even) and 288 (0x79): ties to even
+    v = np.zeros(32)
+    v[0], v[1] = 1.0, 1.0625
+    c, _, _ = O.mx_quantize(v)
+    assert c[1] == 0x78
+    v[1] = 1.0625 + 2.0 ** -40                   # just above the midpoint
+    assert O.mx_quantize(v)[0][1] == 0x79
+
+
+def test_mx_quantizer_matches_numpy_reference_on_wide_ranges():
+    rng = np.random.default_rng(21)
+    n = 32 * 512
+    v = rng.standard_normal(n) * np.exp2(rng.integers(-40, 40, n))  # small elements underflow
+    v[:32] = 0.0                                                   # an all-zero block
+    v[32:64] = -0.0
+    v[64:96] = np.exp2(rng.integers(-5, 5, 32).astype(float))      # amax exactly a power of two
+    v[96:128] = (rng.integers(0, 16, 32) * 2 + 1) * 2.0 ** -5      # many midpoints of the E4M3 grid
+    _, _, dec = O.mx_quantize(v)
+    assert np.array_equal(dec, BF.mx_round_trip(v))
+    c, sc, _ = O.mx_quantize(v)
+    assert np.all(c[32:64] == 0x80)                                # -0 keeps its sign
+    # each normal, unclamped element is within half an E4M3 step (1/16 relative); clamped ones
+    # (scaled into (448, 512)) are set to 448 exactly
+    scaled = np.abs(v) * np.exp2(-(sc.repeat(32).astype(float) - 127))
+    normal = (scaled >= 2.0 ** -6) & (scaled <= 448)
+    assert np.all(np.abs(dec - v)[normal] <= np.abs(v)[normal] / 16)
+    clamped = scaled > 448
+    assert clamped.any() and np.all(np.abs(dec[clamped]) == 448 * np.exp2(sc.repeat(32)[clamped] - 127.0))
+
+
+def test_mx_quantizer_is_idempotent_and_matches_the_generator():
+    rng = np.random.default_rng(22)
+    w = (rng.standard_normal((16, 256)) * 0.02).astype(np.float32)
+    c, sc, dec = O.mx_quantize(w.astype(np.float64))
+    c2, sc2, dec2 = O.mx_quantize(dec)
+    assert np.array_equal(c, c2) and np.array_equal(sc, sc2) and np.array_equal(dec, dec2)
+    gc, gs = synth.quantize_mxfp8(w)
+    assert np.array_equal(gc, c) and np.array_equal(gs, sc)
+
+
 def test_generator_bf16_rounding_matches_torch():
     a = np.random.default_rng(0).standard_normal(100000).astype(np.float32) * 3
     a[:4] = [1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -1.0 - 2 ** -8, 0.0]  # exact ties go to even
@@ -286,9 +346,9 @@ def _share(inp, b, n):
     return out
 
 
-@pytest.mark.parametrize("wdt", ["f32", "bf16", "nvfp4"])
+@pytest.mark.parametrize("wdt", ["f32", "bf16", "nvfp4", "mxfp8"])
 def test_partial_outputs_over_an_expert_partition_sum_to_the_layer(wdt):
-    wl, inp = _tiny(wdt=wdt, T=24, H=64, E=8, k=3, F=48)
+    wl, inp = _tiny(wdt=wdt, T=24, H=64, E=8, k=3, F=64 if wdt == "mxfp8" else 48)
     full = O.forward(inp, wl.top_k, wl.wdt, wl.ffn)
     total = np.zeros_like(full["y"])
     for b, n in ((0, 3), (3, 2), (5, 3)):
@@ -375,9 +435,9 @@ def test_top1_combine_returns_the_expert_row():
     assert np.array_equal(r["y"], rows)
 
 
-@pytest.mark.parametrize("wdt", ["f32", "bf16", "nvfp4"])
+@pytest.mark.parametrize("wdt", ["f32", "bf16", "nvfp4", "mxfp8"])
 def test_layer_matches_per_token_bruteforce(wdt):
-    wl, inp = _tiny(wdt=wdt, T=24, H=64, E=8, k=3, F=48)
+    wl, inp = _tiny(wdt=wdt, T=24, H=64, E=8, k=3, F=64 if wdt == "mxfp8" else 48)
     r = O.forward(inp, wl.top_k, wl.wdt, wl.ffn)
     y, ids, w = BF.layer(inp, r["logits"], wl.top_k, wdt)
     assert np.array_equal(r["topk_ids"], ids)
