@@ -29,8 +29,9 @@
  *    pointer, a misaligned pointer, negative sizes, k < 1, k > E, k > 16, E > 512 or an
  *    expert range outside [0, E);
  *    MOE_ERR_UNSUPPORTED for shapes with no compiled kernel (H % 64, F % 64 != 0; bf16
- *    weights with H % 256 or F % 128 != 0; bf16 activations with fp32 weights or the
- *    reverse; NVFP4 with fp32 activations), and MOE_ERR_INVALID_ARGUMENT for weights not in
+ *    weights with H % 256 or F % 128 != 0; MXFP8 with H % 512 or F % 512 != 0; bf16
+ *    activations with fp32 weights or the reverse; NVFP4 or MXFP8 with fp32 activations), and
+ *    MOE_ERR_INVALID_ARGUMENT for weights not in
  *    the layout their dtype requires (moe_layout);
  *    MOE_ERR_WORKSPACE_TOO_SMALL; MOE_ERR_DEVICE when a launch reports an error.
  *  - T = 0 is a successful no-op (token-sized buffers and the workspace may then be NULL;
@@ -80,8 +81,8 @@ typedef enum {
  * exponent X = floor(log2(max |v|)) - 8 (X = -127 for an all-zero block, clamped to
  * [-127, 127]) and elements v / 2^X clamped to +-448 and rounded to the nearest E4M3 value,
  * ties to the even code (sign kept); the GEMMs multiply on the block-scaled fp8 matrix cores
- * with fp32 accumulation.  Outputs (hid, y_perm, y) stay bf16.  Needs H % 256 == 0 and
- * F % 128 == 0, bf16 activations; weights and E8M0 scales are ROW_MAJOR. */
+ * with fp32 accumulation.  Outputs (hid, y_perm, y) stay bf16.  Needs H % 512 == 0 and
+ * F % 512 == 0, bf16 activations; weights and E8M0 scales are ROW_MAJOR. */
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_NVFP4 = 2, MOE_MXFP8 = 3 } moe_dtype;
 
 typedef enum { MOE_GEMM_GATE_UP_SWIGLU = 0, MOE_GEMM_DOWN = 1 } moe_gemm_kind;

@@ -66,8 +66,9 @@ moe_status check_problem(const moe_problem* p) {
         p->w_dtype != MOE_MXFP8)
         return MOE_ERR_INVALID_ARGUMENT;
     if (p->hidden % 64 || p->ffn % 64) return MOE_ERR_UNSUPPORTED;
-    if ((p->w_dtype == MOE_BF16 || p->w_dtype == MOE_MXFP8) && (p->hidden % 256 || p->ffn % 128))
-        return MOE_ERR_UNSUPPORTED;
+    if (p->w_dtype == MOE_BF16 && (p->hidden % 256 || p->ffn % 128)) return MOE_ERR_UNSUPPORTED;
+    // MXFP8: 256-row tiles, and E8M0 scales loaded 16 per row (8 stages of 64) at a time
+    if (p->w_dtype == MOE_MXFP8 && (p->hidden % 512 || p->ffn % 512)) return MOE_ERR_UNSUPPORTED;
     if (p->w_dtype == MOE_MXFP8 && p->act_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
     if (p->act_dtype == MOE_F32 && p->w_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
     if (p->act_dtype == MOE_BF16 && p->w_dtype == MOE_F32) return MOE_ERR_UNSUPPORTED;

@@ -106,14 +106,19 @@ hipError_t launch_mx_quantize(const void* in, long rows, int K, uint8_t* codes, 
 // wavefront column wc takes gate group wc and up group 4 + wc, i.e. hid columns
 // 128 nt + 32 wc + (0..31), so SwiGLU applies to accumulators in registers.
 //
-// Pipeline: K in 64-wide stages (64-byte rows), a 4-slot LDS ring filled by dma16 exactly as in
-// the bf16 kernel (each wavefront moves two 16-row groups of activations and two of weights per
-// stage), plus the E8M0 scales: one dma4 per wavefront per stage pair (4 scale bytes = 4 blocks
-// = 2 stages of one row; wavefronts 0-3 activation rows, 4-7 weight rows) into one of three
-// scale slots, issued with the pair's even stage.  Each wavefront issues 5 DMA instructions on
-// even stages and 4 on odd ones, so "stage s+1 landed while s+2 and s+3 are in flight" is
-// always a load count of 9.  A scale slot is rewritten 4 stages after its pair's last read,
-// behind at least one barrier.
+// Pipeline: K in 64-wide stages (64-byte rows), a 4-slot LDS ring filled by dma16 as in the
+// bf16 kernel (each wavefront moves two 16-row groups of activations and two of weights per
+// stage).  E8M0 scales come in chunks of 8 stages: 16 scale bytes per row (one dma16 per
+// wavefront per chunk: wavefronts 0-3 activation rows, 4-7 weight rows) into one of two scale
+// slots, issued with the chunk's first stage; a slot is rewritten 16 stages after it was
+// filled, long after its last read and behind a barrier.  Needs K % 512 == 0.
+//
+// Iteration s: issue the MFMAs of stage s from the fragment registers; wait until stage s+1 has
+// landed (a wavefront issues 4 or 5 DMA instructions per stage, so at most 8 outstanding ones
+// means stage s+1 and every earlier one are in LDS) and pass the barrier that publishes it and
+// frees stage s's ring slot; read stage s+1's fragments into the same registers (the MFMAs have
+// taken their operands by then; the other wavefront on the SIMD covers the wait); issue the
+// loads of stage s+4.  Two fragment sets do not fit beside 128 accumulators in 256 registers.
 // ---------------------------------------------------------------------------------------
 
 template <int KIND>
@@ -122,7 +127,7 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_mxfp8_kernel(GemmArgs g) 
     constexpr int HALF = (KIND == kGateUp) ? BN / 2 : BN;
     __shared__ uint4 sA0[BM * 4], sA1[BM * 4], sA2[BM * 4], sA3[BM * 4];
     __shared__ uint4 sB0[BN * 4], sB1[BN * 4], sB2[BN * 4], sB3[BN * 4];
-    __shared__ uint32_t tS[3][BM + BN];  // per stage pair: 4 scale bytes per activation row, then per weight row
+    __shared__ uint4 tS[2][BM + BN];  // per chunk of 8 stages: 16 scale bytes per activation row, then per weight row
 
     const int ncols = (KIND == kGateUp) ? g.F / HALF : (g.N + BN - 1) / BN;
     const int items = *g.tile_count * ncols;
@@ -158,7 +163,7 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_mxfp8_kernel(GemmArgs g) 
         pa[i] = static_cast<const char*>(g.a) + size_t(act_row(row)) * K + ch * 16;
         pb[i] = static_cast<const char*>(g.w) + (size_t(e) * Nw + weight_row(row)) * K + ch * 16;
     }
-    const char* psc;  // this lane's 4 scale bytes per stage pair
+    const char* psc;  // this lane's row of scales: 16 bytes per chunk of 8 stages
     {
         const int row = (wave & 3) * 64 + lane;
         psc = wave < 4 ? reinterpret_cast<const char*>(g.ascale) + size_t(act_row(row)) * KB
@@ -168,8 +173,7 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_mxfp8_kernel(GemmArgs g) 
 
     const int nk = K / 64;
     const int last = nk - 1;
-    // weight / activation groups of this wavefront (32 rows each)
-    const int gbn0 = (KIND == kGateUp) ? wc : 2 * wc;
+    const int gbn0 = (KIND == kGateUp) ? wc : 2 * wc;  // this wavefront's two 32-row weight groups
     const int gbn1 = (KIND == kGateUp) ? 4 + wc : 2 * wc + 1;
     const int g2 = lane >> 5;  // lane group: chunks g2 and g2 + 2, scale block g2
 
@@ -180,36 +184,36 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_mxfp8_kernel(GemmArgs g) 
             dma16(pa[i] + st_ * 64, &SA[(i * 8 + wave) * 64]);                                \
         _Pragma("unroll") for (int i = 0; i < 2; ++i)                                         \
             dma16(pb[i] + st_ * 64, &SB[(i * 8 + wave) * 64]);                                \
-        if (((ST) & 1) == 0)                                                                  \
-            dma4(psc + (st_ >> 1) * 4, &tS[((ST) >> 1) % 3][sc_off]);                         \
+        if (((ST) & 7) == 0)                                                                  \
+            dma16(psc + (st_ >> 3) * 16, &tS[((ST) >> 3) & 1][sc_off]);                      \
     } while (0)
 #define MOE_MXFRAG(S, ROW, F)                                                                 \
     do {                                                                                      \
-        const uint4 lo_ = S[lds_slot32((ROW), g2)];                                           \
-        const uint4 hi_ = S[lds_slot32((ROW), g2 + 2)];                                       \
-        F = i32x8_t{int(lo_.x), int(lo_.y), int(lo_.z), int(lo_.w),                           \
-                    int(hi_.x), int(hi_.y), int(hi_.z), int(hi_.w)};                           \
+        typedef __attribute__((ext_vector_type(4))) int i32x4_t_;                             \
+        const i32x4_t_ lo_ = __builtin_bit_cast(i32x4_t_, S[lds_slot32((ROW), g2)]);          \
+        const i32x4_t_ hi_ = __builtin_bit_cast(i32x4_t_, S[lds_slot32((ROW), g2 + 2)]);      \
+        F = __builtin_shufflevector(lo_, hi_, 0, 1, 2, 3, 4, 5, 6, 7);                        \
     } while (0)
-#define MOE_MXREAD(SA, SB, ST, AF, BF, AS, BS)                                                \
+#define MOE_MXSCALE(ST, ROW) \
+    (int)reinterpret_cast<const uint8_t*>(&tS[((ST) >> 3) & 1][0])[(ROW) * 16 + ((ST) & 7) * 2 + g2]
+#define MOE_MXREAD(SA, SB, ST)                                                                \
     do {                                                                                      \
-        const uint8_t* t_ = reinterpret_cast<const uint8_t*>(&tS[((ST) >> 1) % 3][0]);        \
-        const int q_ = ((ST) & 1) * 2 + g2;                                                   \
-        MOE_MXFRAG(SB, gbn0 * 32 + (lane & 31), BF[0]);                                       \
-        MOE_MXFRAG(SB, gbn1 * 32 + (lane & 31), BF[1]);                                       \
-        BS[0] = t_[(BM + gbn0 * 32 + (lane & 31)) * 4 + q_];                                  \
-        BS[1] = t_[(BM + gbn1 * 32 + (lane & 31)) * 4 + q_];                                  \
+        MOE_MXFRAG(SB, gbn0 * 32 + (lane & 31), bf[0]);                                       \
+        MOE_MXFRAG(SB, gbn1 * 32 + (lane & 31), bf[1]);                                       \
+        bs[0] = MOE_MXSCALE((ST), BM + gbn0 * 32 + (lane & 31));                              \
+        bs[1] = MOE_MXSCALE((ST), BM + gbn1 * 32 + (lane & 31));                              \
         _Pragma("unroll") for (int mi = 0; mi < 4; ++mi) {                                    \
-            MOE_MXFRAG(SA, (mi * 2 + wr) * 32 + (lane & 31), AF[mi]);                         \
-            AS[mi] = t_[((mi * 2 + wr) * 32 + (lane & 31)) * 4 + q_];                         \
+            MOE_MXFRAG(SA, (mi * 2 + wr) * 32 + (lane & 31), af[mi]);                         \
+            as[mi] = MOE_MXSCALE((ST), (mi * 2 + wr) * 32 + (lane & 31));                     \
         }                                                                                     \
     } while (0)
-#define MOE_MXMFMA(AF, BF, AS, BS)                                                            \
+#define MOE_MXMFMA()                                                                          \
     do {                                                                                      \
         _Pragma("unroll") for (int mi = 0; mi < 4; ++mi) {                                    \
             if (mi * 2 + wr < nsub) {                                                         \
                 _Pragma("unroll") for (int ni = 0; ni < 2; ++ni) acc[mi][ni] =                \
-                    __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(AF[mi], BF[ni], acc[mi][ni], \
-                                                                    0, 0, 0, AS[mi], 0, BS[ni]); \
+                    __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[mi], bf[ni], acc[mi][ni], \
+                                                                    0, 0, 0, as[mi], 0, bs[ni]); \
             }                                                                                 \
         }                                                                                     \
     } while (0)
@@ -221,48 +225,46 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_mxfp8_kernel(GemmArgs g) 
         for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.0f;
-    // One set of fragment registers: the MFMAs of stage s are issued first, then the fragments
-    // of stage s+1 are read into the same registers (the MFMAs have taken their operands by
-    // then); the other wavefront on the SIMD covers the wait.
     i32x8_t af[4], bf[2];
     int as[4], bs[2];
 
     MOE_MXISSUE(sA0, sB0, 0);
     MOE_MXISSUE(sA1, sB1, 1);
     MOE_MXISSUE(sA2, sB2, 2);
-    wait_vm_lgkm0<9>();  // stage 0 (and its scales) landed
+    wait_vm_lgkm0<8>();  // stage 0 (and the first scale chunk) landed
     block_barrier();
-    MOE_MXREAD(sA0, sB0, 0, af, bf, as, bs);
+    MOE_MXREAD(sA0, sB0, 0);
     MOE_MXISSUE(sA3, sB3, 3);
     for (int s = 0;; s += 4) {
-        MOE_MXMFMA(af, bf, as, bs);
+        MOE_MXMFMA();
         if (s + 1 >= nk) break;
-        wait_vm_lgkm0<9>();  // stage s+1 landed (s+2, s+3 in flight); every wavefront read stage s
+        wait_vm_lgkm0<8>();
         block_barrier();
-        MOE_MXREAD(sA1, sB1, s + 1, af, bf, as, bs);
+        MOE_MXREAD(sA1, sB1, s + 1);
         MOE_MXISSUE(sA0, sB0, s + 4);
-        MOE_MXMFMA(af, bf, as, bs);
+        MOE_MXMFMA();
         if (s + 2 >= nk) break;
-        wait_vm_lgkm0<9>();
+        wait_vm_lgkm0<8>();
         block_barrier();
-        MOE_MXREAD(sA2, sB2, s + 2, af, bf, as, bs);
+        MOE_MXREAD(sA2, sB2, s + 2);
         MOE_MXISSUE(sA1, sB1, s + 5);
-        MOE_MXMFMA(af, bf, as, bs);
+        MOE_MXMFMA();
         if (s + 3 >= nk) break;
-        wait_vm_lgkm0<9>();
+        wait_vm_lgkm0<8>();
         block_barrier();
-        MOE_MXREAD(sA3, sB3, s + 3, af, bf, as, bs);
+        MOE_MXREAD(sA3, sB3, s + 3);
         MOE_MXISSUE(sA2, sB2, s + 6);
-        MOE_MXMFMA(af, bf, as, bs);
+        MOE_MXMFMA();
         if (s + 4 >= nk) break;
-        wait_vm_lgkm0<9>();
+        wait_vm_lgkm0<8>();
         block_barrier();
-        MOE_MXREAD(sA0, sB0, s + 4, af, bf, as, bs);
+        MOE_MXREAD(sA0, sB0, s + 4);
         MOE_MXISSUE(sA3, sB3, s + 7);
     }
     wait_vm_lgkm0<0>();
 #undef MOE_MXISSUE
 #undef MOE_MXFRAG
+#undef MOE_MXSCALE
 #undef MOE_MXREAD
 #undef MOE_MXMFMA
 

@@ -78,8 +78,8 @@ def _call_route(L, p, x=FAKE, wr=FAKE, ids=FAKE, w=FAKE, ws=FAKE, nbytes=1 << 40
     (dict(act="bf16", wdt="f32"), lib.MOE_ERR_UNSUPPORTED),
     (dict(act="f32", wdt="nvfp4"), lib.MOE_ERR_UNSUPPORTED),
     (dict(act="f32", wdt="mxfp8"), lib.MOE_ERR_UNSUPPORTED),
-    (dict(wdt="mxfp8", hidden=192), lib.MOE_ERR_UNSUPPORTED),
-    (dict(wdt="mxfp8", ffn=192), lib.MOE_ERR_UNSUPPORTED),
+    (dict(wdt="mxfp8", hidden=256, ffn=512), lib.MOE_ERR_UNSUPPORTED),
+    (dict(wdt="mxfp8", hidden=512, ffn=256), lib.MOE_ERR_UNSUPPORTED),
 ])
 def test_problem_validation(L, kw, status):
     base = dict(tokens=16, hidden=256, experts=8, top_k=2, ffn=128, act="bf16", wdt="bf16")
@@ -132,7 +132,7 @@ def test_gemm_and_forward_validation(L):
 
 def test_mxfp8_validation(L):
     V = C.c_void_p
-    p = lib.problem(16, 256, 8, 2, 128, wdt="mxfp8")
+    p = lib.problem(16, 512, 8, 2, 512, wdt="mxfp8")
     w = lib.ExpertWeights(FAKE, FAKE, None, None, None, None, 0)  # MXFP8 without scales
     assert L.moe_forward(C.byref(p), V(FAKE), V(FAKE), None, C.byref(w), V(FAKE), None, None, None,
                          None, None, None, V(FAKE), 1 << 40, None) == lib.MOE_ERR_INVALID_ARGUMENT

@@ -19,9 +19,9 @@ pytestmark = pytest.mark.gpu
 TOL = 2e-2
 W = synth.Workload
 SMALL = {
-    "small_mxfp8": W("small_mxfp8", 384, 512, 16, 4, 256, "bf16", "mxfp8", 17, "normal"),
-    "ragged_mxfp8": W("ragged_mxfp8", 77, 256, 5, 3, 384, "bf16", "mxfp8", 18, "normal"),
-    "one_token_mxfp8": W("one_token_mxfp8", 1, 512, 8, 2, 128, "bf16", "mxfp8", 19, "none"),
+    "small_mxfp8": W("small_mxfp8", 384, 512, 16, 4, 512, "bf16", "mxfp8", 17, "normal"),
+    "ragged_mxfp8": W("ragged_mxfp8", 77, 1024, 5, 3, 1536, "bf16", "mxfp8", 18, "normal"),
+    "one_token_mxfp8": W("one_token_mxfp8", 1, 512, 8, 2, 512, "bf16", "mxfp8", 19, "none"),
 }
 
 
