@@ -82,7 +82,8 @@ typedef enum {
  * [-127, 127]) and elements v / 2^X clamped to +-448 and rounded to the nearest E4M3 value,
  * ties to the even code (sign kept); the GEMMs multiply on the block-scaled fp8 matrix cores
  * with fp32 accumulation.  Outputs (hid, y_perm, y) stay bf16.  Needs H % 512 == 0 and
- * F % 512 == 0, bf16 activations; weights and E8M0 scales are ROW_MAJOR. */
+ * F % 512 == 0, bf16 activations; the E4M3 codes are PACKED (moe_layout), the E8M0 scales
+ * row-major. */
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_NVFP4 = 2, MOE_MXFP8 = 3 } moe_dtype;
 
 typedef enum { MOE_GEMM_GATE_UP_SWIGLU = 0, MOE_GEMM_DOWN = 1 } moe_gemm_kind;
@@ -124,24 +125,25 @@ typedef struct {
  * Rows of hid, y_perm and x_perm past A_local are unspecified.  expert_begin = local_experts =
  * 0 (a zero-initialised struct) is the single-GPU layer. */
 
-/* Weight layouts.  bf16 expert weights are consumed in the PACKED layout written by
- * moe_pack_weights; fp32 and NVFP4 expert weights in the ROW_MAJOR layout described below.
+/* Weight layouts.  bf16 expert weights and MXFP8 codes are consumed in the PACKED layout
+ * written by moe_pack_weights; fp32 and NVFP4 expert weights in the ROW_MAJOR layout described
+ * below (MXFP8 scales stay row-major).
  *
- * PACKED (bf16 only; needs H % 256 == 0 and F % 128 == 0; same byte size as row-major):
- * weights are cut into tiles of 256 weight rows and stages of 32 consecutive input elements;
- * each (expert, tile, stage) block is 16 KiB = 256 rows x 4 chunks of 8 bf16, and chunk c of
- * tile row r is stored in slot c ^ ((r >> 1) & 3) of that row.  Blocks are ordered
- * [expert][tile][stage].
- *   w13: F/128 tiles of H/32 stages; tile row r of tile t is the gate row
+ * PACKED (bf16 and MXFP8 codes; needs H % 256 == 0 and F % 128 == 0; same byte size as
+ * row-major): weights are cut into tiles of 256 weight rows and stages of 64 bytes of a row
+ * (32 bf16 or 64 E4M3 elements); each (expert, tile, stage) block is 16 KiB = 256 rows x 4
+ * chunks of 16 bytes, and chunk c of tile row r is stored in slot c ^ ((r >> 1) & 3) of that
+ * row.  Blocks are ordered [expert][tile][stage].
+ *   w13: F/128 tiles of H/32 (bf16) or H/64 (MXFP8) stages; tile row r of tile t is the gate row
  *        f = 128 t + 64 (r / 128) + (r % 64) when r % 128 < 64, else the up row F + f.
- *   w2:  H/256 tiles of F/32 stages; tile row r of tile t is weight row 256 t + r.
+ *   w2:  H/256 tiles of F/32 or F/64 stages; tile row r of tile t is weight row 256 t + r.
  * One stage of one tile is then one contiguous 16 KiB read that lands in LDS unchanged, and
  * 16 consecutive rows of one stage are one contiguous 1 KiB. */
 typedef enum { MOE_LAYOUT_ROW_MAJOR = 0, MOE_LAYOUT_PACKED = 1 } moe_layout;
 
 typedef struct {
-    const void* w13;              /* [E,2F,H] fp32, packed bf16 or MXFP8 E4M3 bytes; NVFP4 bytes [E,2F,H/2] */
-    const void* w2;               /* [E,H,F] fp32, packed bf16 or MXFP8 E4M3 bytes; NVFP4 bytes [E,H,F/2] */
+    const void* w13;              /* [E,2F,H] fp32, packed bf16 or packed MXFP8 codes; NVFP4 bytes [E,2F,H/2] */
+    const void* w2;               /* [E,H,F] fp32, packed bf16 or packed MXFP8 codes; NVFP4 bytes [E,H,F/2] */
     const uint8_t* w13_scale;     /* NVFP4: E4M3 [E,2F,H/16]; MXFP8: E8M0 [E,2F,H/32] */
     const uint8_t* w2_scale;      /* NVFP4: E4M3 [E,H,F/16]; MXFP8: E8M0 [E,H,F/32] */
     const float* w13_gscale;      /* NVFP4 only, nullable (=> 1.0): fp32 [E] */
@@ -157,13 +159,13 @@ const char* moe_status_string(moe_status s);
  * MOE_ERR_UNSUPPORTED for problems the entry points would reject. */
 moe_status moe_workspace_size(const moe_problem* p, size_t* bytes);
 
-/* Bytes of the packed w13 and w2 of problem `p` (bf16 weights only).  Host only. */
+/* Bytes of the packed w13 and w2 of problem `p` (bf16 or MXFP8 weights).  Host only. */
 moe_status moe_packed_weights_size(const moe_problem* p, size_t* w13_bytes, size_t* w2_bytes);
 /* (both sizes and moe_pack_weights below cover the held experts only: local_experts of them
  * when it is non-zero, else all E) */
 
-/* Rewrite row-major bf16 expert weights w13 [E,2F,H] and w2 [E,H,F] into the PACKED layout
- * (see moe_layout).  A one-time transform of static weights; the outputs must not alias the
+/* Rewrite row-major bf16 expert weights (or MXFP8 E4M3 codes) w13 [E,2F,H] and w2 [E,H,F]
+ * into the PACKED layout (see moe_layout).  A one-time transform of static weights; the outputs must not alias the
  * inputs.  Either pair (w13 -> w13_packed, w2 -> w2_packed) may be NULL to skip it. */
 moe_status moe_pack_weights(const moe_problem* p, const void* w13, const void* w2,
                             void* w13_packed, void* w2_packed, void* stream);

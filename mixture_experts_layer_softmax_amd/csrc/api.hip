@@ -123,7 +123,8 @@ moe_status check_ws(const moe_problem& p, void* ws, size_t bytes) {
 
 moe_status check_weights(const moe_problem& p, const moe_expert_weights* w) {
     if (!w || !w->w13 || !w->w2 || !aligned(w->w13) || !aligned(w->w2)) return MOE_ERR_INVALID_ARGUMENT;
-    if (w->layout != (p.w_dtype == MOE_BF16 ? MOE_LAYOUT_PACKED : MOE_LAYOUT_ROW_MAJOR))
+    const bool packed = p.w_dtype == MOE_BF16 || p.w_dtype == MOE_MXFP8;
+    if (w->layout != (packed ? MOE_LAYOUT_PACKED : MOE_LAYOUT_ROW_MAJOR))
         return MOE_ERR_INVALID_ARGUMENT;
     if (p.w_dtype == MOE_MXFP8) {
         if (!w->w13_scale || !w->w2_scale || !aligned(w->w13_scale) || !aligned(w->w2_scale))
@@ -223,17 +224,19 @@ moe_status moe_workspace_size(const moe_problem* p, size_t* bytes) {
 
 moe_status moe_packed_weights_size(const moe_problem* p, size_t* w13_bytes, size_t* w2_bytes) {
     MOE_TRY(check_problem(p));
-    if (p->w_dtype != MOE_BF16 || !w13_bytes || !w2_bytes) return MOE_ERR_INVALID_ARGUMENT;
+    if ((p->w_dtype != MOE_BF16 && p->w_dtype != MOE_MXFP8) || !w13_bytes || !w2_bytes)
+        return MOE_ERR_INVALID_ARGUMENT;
     const size_t E = eend(*p) - ebegin(*p), H = p->hidden, F = p->ffn;  // held experts
-    *w13_bytes = E * 2 * F * H * 2;
-    *w2_bytes = E * H * F * 2;
+    const size_t es = p->w_dtype == MOE_BF16 ? 2 : 1;
+    *w13_bytes = E * 2 * F * H * es;
+    *w2_bytes = E * H * F * es;
     return MOE_OK;
 }
 
 moe_status moe_pack_weights(const moe_problem* p, const void* w13, const void* w2, void* w13_packed,
                             void* w2_packed, void* stream) {
     MOE_TRY(check_problem(p));
-    if (p->w_dtype != MOE_BF16) return MOE_ERR_INVALID_ARGUMENT;
+    if (p->w_dtype != MOE_BF16 && p->w_dtype != MOE_MXFP8) return MOE_ERR_INVALID_ARGUMENT;
     if ((w13 == nullptr) != (w13_packed == nullptr) || (w2 == nullptr) != (w2_packed == nullptr))
         return MOE_ERR_INVALID_ARGUMENT;
     for (const void* q : {w13, w2, (const void*)w13_packed, (const void*)w2_packed})
@@ -241,8 +244,9 @@ moe_status moe_pack_weights(const moe_problem* p, const void* w13, const void* w
     if ((w13 && w13 == w13_packed) || (w2 && w2 == w2_packed)) return MOE_ERR_INVALID_ARGUMENT;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int held = eend(*p) - ebegin(*p);
-    if (w13) MOE_TRY(dev(launch_pack_bf16(w13, w13_packed, 0, held, p->ffn, p->hidden, s)));
-    if (w2) MOE_TRY(dev(launch_pack_bf16(w2, w2_packed, 1, held, p->ffn, p->hidden, s)));
+    const int es = p->w_dtype == MOE_BF16 ? 2 : 1;
+    if (w13) MOE_TRY(dev(launch_pack_bf16(w13, w13_packed, 0, held, p->ffn, p->hidden, es, s)));
+    if (w2) MOE_TRY(dev(launch_pack_bf16(w2, w2_packed, 1, held, p->ffn, p->hidden, es, s)));
     return MOE_OK;
 }
 

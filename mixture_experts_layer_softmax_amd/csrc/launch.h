@@ -76,7 +76,9 @@ hipError_t launch_gemm_mxfp8(const GemmArgs& g, int max_tiles, hipStream_t s);
 hipError_t launch_gather_rows(const void* x, const int32_t* sorted_token, void* x_perm, int A,
                               int T, int row_bytes, hipStream_t s);
 hipError_t launch_gemm(const GemmArgs& g, int family, int max_tiles, hipStream_t s);
-hipError_t launch_pack_bf16(const void* src, void* dst, int kind, int E, int F, int H, hipStream_t s);
+// esize: bytes per element (2: bf16, 1: MXFP8 codes)
+hipError_t launch_pack_bf16(const void* src, void* dst, int kind, int E, int F, int H, int esize,
+                            hipStream_t s);
 hipError_t launch_combine(const void* y_perm, const int32_t* inv_perm, const float* w, void* y,
                           int T, int k, int H, int A, bool bf16, hipStream_t s);
 

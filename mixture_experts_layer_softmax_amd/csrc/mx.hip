@@ -99,16 +99,18 @@ hipError_t launch_mx_quantize(const void* in, long rows, int K, uint8_t* codes, 
 
 // ---------------------------------------------------------------------------------------
 // MXFP8 grouped GEMM, prefill tiles.  a: E4M3 codes [rows, K] (gathered through a_rows for
-// gate/up), ascale: E8M0 [rows, K/32]; w: E4M3 codes [E, Nw, K] row-major, wscale [E, Nw, K/32].
-// Block tile 256 x 256; wavefronts 2 x 4 of 128 x 64: wavefront (wr, wc) holds the 32-row
-// groups 2 mi + wr (mi = 0..3) and two 32-column weight groups.  For gate/up the tile's 256
-// weight rows are 128 gate rows f = 128 nt + r then the 128 matching up rows F + f, and
-// wavefront column wc takes gate group wc and up group 4 + wc, i.e. hid columns
-// 128 nt + 32 wc + (0..31), so SwiGLU applies to accumulators in registers.
+// gate/up), ascale: E8M0 [rows, K/32]; w: E4M3 codes in the PACKED layout of moe.h (each stage
+// of a 256-row weight tile is one contiguous 16 KiB block, exactly the LDS image; a stage is 64
+// fp8 elements here), wscale: E8M0 [E, Nw, K/32] row-major.  Block tile 256 x 256; wavefronts
+// 2 x 4 of 128 x 64: wavefront (wr, wc) holds the 32-row groups 2 mi + wr (mi = 0..3) and two
+// 32-row weight groups.  In a gate/up tile, rows 128 h + (0..63) are gate rows
+// f = 128 nt + 64 h + (0..63) and rows 128 h + 64 + (0..63) the matching up rows F + f, so
+// wavefront column wc takes weight groups 4 (wc >> 1) + (wc & 1) (gate) and that + 2 (up): hid
+// columns 128 nt + 64 (wc >> 1) + 32 (wc & 1) + (0..31), and SwiGLU applies in registers.
 //
 // Pipeline: K in 64-wide stages (64-byte rows), a 4-slot LDS ring filled by dma16 as in the
-// bf16 kernel (each wavefront moves two 16-row groups of activations and two of weights per
-// stage).  E8M0 scales come in chunks of 8 stages: 16 scale bytes per row (one dma16 per
+// bf16 kernel (each wavefront moves two 16-row groups of activations, gathered, and two 1 KiB
+// pieces of the packed weight stage per stage).  E8M0 scales come in chunks of 8 stages: 16 scale bytes per row (one dma16 per
 // wavefront per chunk: wavefronts 0-3 activation rows, 4-7 weight rows) into one of two scale
 // slots, issued with the chunk's first stage; a slot is rewritten 16 stages after it was
 // filled, long after its last read and behind a barrier.  Needs K % 512 == 0.
@@ -146,7 +148,10 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_mxfp8_kernel(GemmArgs g) 
     const int Nw = (KIND == kGateUp) ? 2 * g.F : g.N;
 
     auto weight_row = [&](int r) {  // weight row (of this expert) behind tile row r
-        if (KIND == kGateUp) return r < 128 ? nt * 128 + r : g.F + nt * 128 + (r - 128);
+        if (KIND == kGateUp) {
+            const int q = r & 127, f = nt * 128 + 64 * (r >> 7) + (q & 63);
+            return q < 64 ? f : g.F + f;
+        }
         return nt * BN + r;
     };
     auto act_row = [&](int r) {  // row of `a` behind tile row r (padded rows repeat the last)
@@ -154,6 +159,8 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_mxfp8_kernel(GemmArgs g) 
         int src = g.a_rows ? g.a_rows[rr] : rr;
         return src < 0 ? 0 : (src >= g.a_rows_limit ? g.a_rows_limit - 1 : src);
     };
+    const int nk = K / 64;
+    const char* const wblk = static_cast<const char*>(g.w) + (size_t(e) * ncols + nt) * size_t(nk) * 16384;
     const char* pa[2];
     const char* pb[2];
 #pragma unroll
@@ -161,7 +168,7 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_mxfp8_kernel(GemmArgs g) 
         const int row = (i * 8 + wave) * 16 + (lane >> 2);
         const int ch = (lane & 3) ^ ((row >> 1) & 3);
         pa[i] = static_cast<const char*>(g.a) + size_t(act_row(row)) * K + ch * 16;
-        pb[i] = static_cast<const char*>(g.w) + (size_t(e) * Nw + weight_row(row)) * K + ch * 16;
+        pb[i] = wblk + (i * 8 + wave) * 1024 + lane * 16;
     }
     const char* psc;  // this lane's row of scales: 16 bytes per chunk of 8 stages
     {
@@ -171,10 +178,9 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_mxfp8_kernel(GemmArgs g) 
     }
     const int sc_off = (wave < 4 ? 0 : BM) + (wave & 3) * 64;  // this wavefront's scale rows in a slot
 
-    const int nk = K / 64;
     const int last = nk - 1;
-    const int gbn0 = (KIND == kGateUp) ? wc : 2 * wc;  // this wavefront's two 32-row weight groups
-    const int gbn1 = (KIND == kGateUp) ? 4 + wc : 2 * wc + 1;
+    const int gbn0 = (KIND == kGateUp) ? 4 * (wc >> 1) + (wc & 1) : 2 * wc;  // this wavefront's two
+    const int gbn1 = (KIND == kGateUp) ? gbn0 + 2 : 2 * wc + 1;              // 32-row weight groups
     const int g2 = lane >> 5;  // lane group: chunks g2 and g2 + 2, scale block g2
 
 #define MOE_MXISSUE(SA, SB, ST)                                                               \
@@ -183,7 +189,7 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_mxfp8_kernel(GemmArgs g) 
         _Pragma("unroll") for (int i = 0; i < 2; ++i)                                         \
             dma16(pa[i] + st_ * 64, &SA[(i * 8 + wave) * 64]);                                \
         _Pragma("unroll") for (int i = 0; i < 2; ++i)                                         \
-            dma16(pb[i] + st_ * 64, &SB[(i * 8 + wave) * 64]);                                \
+            dma16(pb[i] + size_t(st_) * 16384, &SB[(i * 8 + wave) * 64]);                     \
         if (((ST) & 7) == 0)                                                                  \
             dma16(psc + (st_ >> 3) * 16, &tS[((ST) >> 3) & 1][sc_off]);                      \
     } while (0)
@@ -277,7 +283,7 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_mxfp8_kernel(GemmArgs g) 
             const int row = r0 + (mi * 2 + wr) * 32 + 8 * (i / 4) + 4 * g2 + (i % 4);
             if (row >= r1) continue;
             if (KIND == kGateUp) {
-                const int col = nt * HALF + wc * 32 + (lane & 31);
+                const int col = nt * HALF + 64 * (wc >> 1) + 32 * (wc & 1) + (lane & 31);
                 out[size_t(row) * g.F + col] = (uint16_t)bf16_rne(silu_mul(acc[mi][0][i], acc[mi][1][i]));
             } else {
 #pragma unroll

@@ -1,4 +1,6 @@
-// pack.hip -- one-time rewrite of bf16 expert weights into the packed layout of moe.h.
+// pack.hip -- one-time rewrite of bf16 or MXFP8 (E4M3 codes) expert weights into the packed
+// layout of moe.h.  A stage is 64 bytes of a row either way (32 bf16 or 64 fp8 elements); the
+// kernel moves 16-byte chunks and counts a row in 2-byte units.
 //
 // Each (expert, 256-row tile, 32-element stage) block becomes the byte image of an LDS slot of
 // the grouped GEMMs (rows 64 bytes, chunk c of row r in slot c ^ ((r >> 1) & 3)), so that the
@@ -11,11 +13,11 @@
 namespace moe {
 
 // One thread per 16-byte destination chunk (grid-stride).  kind 0: w13 (gate/up tiles of 128
-// hid columns), kind 1: w2 (tiles of 256 output rows).
+// hid columns), kind 1: w2 (tiles of 256 output rows); esize = bytes per element (2 or 1).
 __global__ __launch_bounds__(256) void pack_bf16_kernel(const uint4* __restrict__ src,
                                                         uint4* __restrict__ dst, int kind, int E,
-                                                        int F, int H) {
-    const int K = kind == 0 ? H : F;                 // input elements per weight row
+                                                        int F, int H, int esize) {
+    const int K = (kind == 0 ? H : F) * esize / 2;   // 2-byte units per weight row
     const int Nw = kind == 0 ? 2 * F : H;            // weight rows per expert
     const int ntiles = kind == 0 ? F / 128 : H / 256;
     const int nst = K / 32;
@@ -39,9 +41,10 @@ __global__ __launch_bounds__(256) void pack_bf16_kernel(const uint4* __restrict_
     }
 }
 
-hipError_t launch_pack_bf16(const void* src, void* dst, int kind, int E, int F, int H, hipStream_t s) {
+hipError_t launch_pack_bf16(const void* src, void* dst, int kind, int E, int F, int H, int esize,
+                            hipStream_t s) {
     hipLaunchKernelGGL(pack_bf16_kernel, dim3(8192), dim3(256), 0, s, static_cast<const uint4*>(src),
-                       static_cast<uint4*>(dst), kind, E, F, H);
+                       static_cast<uint4*>(dst), kind, E, F, H, esize);
     return hipGetLastError();
 }
 

@@ -53,7 +53,7 @@ class MoELayer:
         self.w13 = to_device(inputs["w13"], d, wk)
         self.w2 = to_device(inputs["w2"], d, wk)
         layout = lib.LAYOUT_ROW_MAJOR
-        if wdt == "bf16":  # the library consumes bf16 expert weights in its packed layout
+        if wdt in ("bf16", "mxfp8"):  # bf16 weights and MXFP8 codes are consumed packed
             p13 = torch.empty_like(self.w13)
             p2 = torch.empty_like(self.w2)
             lib.pack_weights(self.problem, self.w13, self.w2, p13, p2)

@@ -122,7 +122,7 @@ def test_gemm_and_forward_validation(L):
     w = lib.ExpertWeights(FAKE, FAKE, FAKE, FAKE, None, None, 1)
     assert L.moe_forward(C.byref(p), V(FAKE), V(FAKE), None, C.byref(w), V(FAKE), None, None, None,
                          None, None, None, V(FAKE), 1 << 40, None) == lib.MOE_ERR_INVALID_ARGUMENT
-    # packing: bf16 only, no aliasing, shapes the layout can tile
+    # packing: bf16 or MXFP8 only (p is NVFP4 here), no aliasing, shapes the layout can tile
     assert L.moe_pack_weights(C.byref(p), V(FAKE), V(FAKE), V(FAKE + 4096), V(FAKE + 8192),
                               None) == lib.MOE_ERR_INVALID_ARGUMENT
     assert L.moe_pack_weights(C.byref(pb), V(FAKE), None, V(FAKE), None, None) == lib.MOE_ERR_INVALID_ARGUMENT
@@ -136,9 +136,11 @@ def test_mxfp8_validation(L):
     w = lib.ExpertWeights(FAKE, FAKE, None, None, None, None, 0)  # MXFP8 without scales
     assert L.moe_forward(C.byref(p), V(FAKE), V(FAKE), None, C.byref(w), V(FAKE), None, None, None,
                          None, None, None, V(FAKE), 1 << 40, None) == lib.MOE_ERR_INVALID_ARGUMENT
-    w = lib.ExpertWeights(FAKE, FAKE, FAKE, FAKE, None, None, 1)  # packed layout: bf16 only
+    w = lib.ExpertWeights(FAKE, FAKE, FAKE, FAKE, None, None, 0)  # MXFP8 codes must be packed
     assert L.moe_forward(C.byref(p), V(FAKE), V(FAKE), None, C.byref(w), V(FAKE), None, None, None,
                          None, None, None, V(FAKE), 1 << 40, None) == lib.MOE_ERR_INVALID_ARGUMENT
+    a, b = lib.packed_weights_size(p)
+    assert a == 8 * 2 * 512 * 512 and b == 8 * 512 * 512  # one byte per code
     q = L.moe_quantize_mxfp8
     assert q(V(FAKE), 4, 48, V(FAKE), V(FAKE), None) == lib.MOE_ERR_INVALID_ARGUMENT    # K % 32
     assert q(V(FAKE), -1, 64, V(FAKE), V(FAKE), None) == lib.MOE_ERR_INVALID_ARGUMENT
