@@ -49,7 +49,7 @@ PEAK_BF16_FLOPS = 2.5e15   # MI355X dense bf16 MFMA
 PEAK_FP8_FLOPS = 5.0e15    # MI355X dense fp8 MFMA (the MXFP8 layer's block-scaled products)
 PEAK_HBM_BYTES = 8.0e12    # MI355X HBM3E
 METRIC = "MoE layer tokens/s at 1 GPU; % MFMA peak (prefill) / % HBM BW (decode)"
-GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_softmax_amd", "csrc", "gemm.hip")
+CSRC = os.path.join(ROOT, "mixture_experts_layer_softmax_amd", "csrc")
 TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -89,18 +89,24 @@ def gate_up_work(wl, active: int, rows: int, tokens_read: int):
     return flops, nbytes
 
 
-def source_hash() -> str:
-    return hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()[:16]
+def kernel_source(wdt: str) -> str:
+    """File of the gate/up GEMM kernel of a weight format."""
+    return os.path.join(CSRC, "mx.hip" if wdt == "mxfp8" else "gemm.hip")
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per gate/up launch from the committed counter summary, if it is current."""
+def source_hash(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str, wdt: str):
+    """HBM bytes per gate/up launch from the committed counter summary, if it was taken on the
+    current source of that kernel."""
     try:
         d = json.load(open(TRAFFIC))
     except (OSError, ValueError):
         return None
     e = d.get(workload)
-    if not e or e.get("gemm_source_sha256_16") != source_hash():
+    if not e or e.get("gemm_source_sha256_16") != source_hash(kernel_source(wdt)):
         return None
     return e.get("bytes_per_launch")
 
@@ -380,7 +386,7 @@ def main() -> int:
             roof["frac_measured"] = roof["achieved"] / peaks["hbm_read_gbs"]
         elif wl.wdt != "mxfp8":  # the probe measures the bf16 rate only
             roof["frac_measured"] = roof["achieved"] / peaks["mfma_bf16_tflops"]
-    roof["traffic"] = measured_traffic(wl.name)
+    roof["traffic"] = measured_traffic(wl.name, wl.wdt) if held is None else None
     roof["kernel"] = "grouped gate/up GEMM + SwiGLU (%s weights%s)" % (
         wl.wdt, ", input quantization included" if wl.wdt == "mxfp8" else "")
     roof["kernel_ms"] = gemm1_ms
