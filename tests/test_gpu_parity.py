@@ -507,3 +507,35 @@ def test_non_finite_inputs_stay_memory_safe_and_route_validly():
         assert np.array_equal(st[ip], np.arange(wl.assignments) // wl.top_k)
         good = [t for t in range(wl.tokens) if t not in (3, 5, 9)]
         assert np.isfinite(act_f64(to_host(y))[good]).all()
+
+
+@pytest.mark.parametrize("name,T", [("decode1", 1), ("decode8", 8), ("nvfp4_decode", 3), ("small_bf16", 5)])
+def test_small_batch_forward_equals_its_stages(name, T):
+    """moe_forward on batches of up to 8 tokens (single-block selection and dispatch) must equal
+    route -> permute -> two grouped GEMMs -> combine through the stage entry points, bit for bit."""
+    base = SMALL.get(name) or synth.WORKLOADS[name]
+    wl = base.with_tokens(T, x_sub=100 + T)
+    inp = inputs_of(wl)
+    layer = MoELayer.from_workload(wl, inp)
+    x = layer.act_tensor(inp["x"])
+    note("forward vs stages %s T=%d" % (name, T))
+    y_fused = layer.forward(x)
+    p = layer.problem_for(T)
+    ws = layer.workspace(T)
+    A, dev = T * wl.top_k, "cuda"
+    ids = torch.empty(T, wl.top_k, dtype=torch.int32, device=dev)
+    tw = torch.empty(T, wl.top_k, dtype=torch.float32, device=dev)
+    counts = torch.empty(wl.experts, dtype=torch.int32, device=dev)
+    offsets = torch.empty(wl.experts + 1, dtype=torch.int32, device=dev)
+    st = torch.empty(A, dtype=torch.int32, device=dev)
+    ip = torch.empty(A, dtype=torch.int32, device=dev)
+    lib.route(p, x, layer.w_router, layer.bias, ids, tw, ws)
+    lib.permute(p, ids, counts, offsets, st, ip, ws)
+    hid = layer.empty_act(A, wl.ffn)
+    yp = layer.empty_act(A, wl.hidden)
+    lib.grouped_gemm(p, lib.GATE_UP_SWIGLU, x, st, offsets, layer.weights, hid, ws)
+    lib.grouped_gemm(p, lib.DOWN, hid, None, offsets, layer.weights, yp, ws)
+    y_stages = layer.empty_act(T, wl.hidden)
+    lib.combine(p, yp, ip, tw, y_stages)
+    torch.cuda.synchronize()
+    assert torch.equal(y_fused.view(torch.int16), y_stages.view(torch.int16))
