@@ -6,7 +6,8 @@ A step is one ``moe_forward`` call (router -> dispatch -> gate/up GEMM + SwiGLU 
 -> combine) over one batch of seeded synthetic inputs already resident in HBM.  The default
 workload is the prefill-shaped layer (4096 tokens, hidden 4096, 128 experts, top-8, expert FFN
 1536, bf16, router bias N(0,1)); ``--workload`` selects another one (tiny, decode1, decode8,
-decode64, nvfp4_decode, nvfp4_prefill, prefill6000, mxfp8_prefill).  Prints one JSON line.
+decode64, nvfp4_decode, nvfp4_prefill, prefill6000, mxfp8_prefill, mxfp4_prefill).  Prints one
+JSON line.
 
 Shapes of "Hosting Qwen on Blackwell" (sections Prefill, Expert Parallel and the grouped MoE
 GEMM benchmark there):
@@ -59,12 +60,14 @@ def describe(wl) -> str:
 
 
 def bytes_per_weight(wdt: str) -> float:
-    return {"f32": 4.0, "bf16": 2.0, "nvfp4": 0.5 + 1.0 / 16, "mxfp8": 1.0 + 1.0 / 32}[wdt]
+    return {"f32": 4.0, "bf16": 2.0, "nvfp4": 0.5 + 1.0 / 16, "mxfp8": 1.0 + 1.0 / 32,
+            "mxfp4": 0.5 + 1.0 / 32}[wdt]
 
 
 def mfma_peak(wl) -> float:
-    """Dense MFMA peak of the dtype the expert GEMMs multiply in (NVFP4 is decoded to bf16)."""
-    return PEAK_FP8_FLOPS if wl.wdt == "mxfp8" else PEAK_BF16_FLOPS
+    """Dense MFMA peak of the dtype the expert GEMMs multiply in (NVFP4 is decoded to bf16;
+    MXFP4 weights multiply fp8 activations, priced at the fp8 rate)."""
+    return PEAK_FP8_FLOPS if wl.wdt.startswith("mx") else PEAK_BF16_FLOPS
 
 
 def layer_work(wl, active: int, rows: int):
@@ -91,7 +94,7 @@ def gate_up_work(wl, active: int, rows: int, tokens_read: int):
 
 def kernel_source(wdt: str) -> str:
     """File of the gate/up GEMM kernel of a weight format."""
-    return os.path.join(CSRC, "mx.hip" if wdt == "mxfp8" else "gemm.hip")
+    return os.path.join(CSRC, "mx.hip" if wdt.startswith("mx") else "gemm.hip")
 
 
 def source_hash(path: str) -> str:
@@ -384,11 +387,11 @@ def main() -> int:
     if peaks:
         if roof["bound"] == "hbm":
             roof["frac_measured"] = roof["achieved"] / peaks["hbm_read_gbs"]
-        elif wl.wdt != "mxfp8":  # the probe measures the bf16 rate only
+        elif not wl.wdt.startswith("mx"):  # the probe measures the bf16 rate only
             roof["frac_measured"] = roof["achieved"] / peaks["mfma_bf16_tflops"]
     roof["traffic"] = measured_traffic(wl.name, wl.wdt) if held is None else None
     roof["kernel"] = "grouped gate/up GEMM + SwiGLU (%s weights%s)" % (
-        wl.wdt, ", input quantization included" if wl.wdt == "mxfp8" else "")
+        wl.wdt, ", input quantization included" if wl.wdt.startswith("mx") else "")
     roof["kernel_ms"] = gemm1_ms
     roof["algorithmic_bytes"] = gbytes
     roof["algorithmic_flops"] = gflops
@@ -396,7 +399,8 @@ def main() -> int:
     tok_s = wl.tokens / (ms_per_step * 1e-3)
     out = dict(metric=METRIC, value=tok_s, unit="tokens/s", n_gpus=1, steps=args.steps,
                warmup=args.warmup, ms_per_step=ms_per_step, higher_is_better=True,
-               scaling="weak", vs_baseline=None, dtype="fp8" if wl.wdt == "mxfp8" else wl.act,
+               scaling="weak", vs_baseline=None,
+               dtype={"mxfp8": "fp8", "mxfp4": "fp8 x fp4"}.get(wl.wdt, wl.act),
                data="synthetic (seeded)",
                config=dict(workload=describe(wl), tokens=wl.tokens, hidden=wl.hidden,
                            experts=wl.experts, top_k=wl.top_k, ffn=wl.ffn, weights=wl.wdt,
@@ -409,7 +413,7 @@ def main() -> int:
                wall_s=wall, roofline=roof)
     if peaks:
         out["measured_peaks"] = peaks
-        if wl.wdt != "mxfp8":
+        if not wl.wdt.startswith("mx"):
             out["layer_mfma_frac_measured"] = flops / (ms_per_step * 1e-3) / (peaks["mfma_bf16_tflops"] * 1e12)
         out["layer_hbm_frac_measured"] = nbytes / (ms_per_step * 1e-3) / (peaks["hbm_read_gbs"] * 1e9)
     if held is not None:

@@ -83,8 +83,14 @@ typedef enum {
  * ties to the even code (sign kept); the GEMMs multiply on the block-scaled fp8 matrix cores
  * with fp32 accumulation.  Outputs (hid, y_perm, y) stay bf16.  Needs H % 512 == 0 and
  * F % 512 == 0, bf16 activations; the E4M3 codes are PACKED (moe_layout), the E8M0 scales
+ * row-major.
+ * MOE_MXFP4 (weights only; OCP MX v1.0 with E2M1 elements, which "Hosting Qwen on Blackwell"
+ * evaluates beside MXFP8): two E2M1 values per byte, even element in the low nibble, one E8M0
+ * scale per 32 along the input dimension: w = e2m1 * 2^(s - 127).  Activations run in MXFP8
+ * exactly as for MOE_MXFP8; the GEMMs multiply fp8 activations by fp4 weights on the
+ * block-scaled matrix cores.  Same shape rules; codes PACKED (the 4-bit variant below), scales
  * row-major. */
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_NVFP4 = 2, MOE_MXFP8 = 3 } moe_dtype;
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_NVFP4 = 2, MOE_MXFP8 = 3, MOE_MXFP4 = 4 } moe_dtype;
 
 typedef enum { MOE_GEMM_GATE_UP_SWIGLU = 0, MOE_GEMM_DOWN = 1 } moe_gemm_kind;
 
@@ -100,7 +106,7 @@ typedef struct {
     int32_t top_k;        /* k, 1..min(E,16) */
     int32_t ffn;          /* F, multiple of 64 */
     int32_t act_dtype;    /* MOE_F32 | MOE_BF16: x, router weight, hid, y_perm, y */
-    int32_t w_dtype;      /* MOE_F32 (with F32 acts) | MOE_BF16 | MOE_NVFP4 | MOE_MXFP8 (BF16 acts) */
+    int32_t w_dtype;      /* MOE_F32 (with F32 acts) | MOE_BF16 | MOE_NVFP4 | MOE_MXFP8 | MOE_MXFP4 (BF16 acts) */
     int32_t renormalize;  /* 1: softmax over the selected k (default); 0: full softmax */
     int32_t path;         /* moe_path */
     int32_t expert_begin;  /* expert parallelism: the caller holds the experts           */
@@ -137,15 +143,18 @@ typedef struct {
  *   w13: F/128 tiles of H/32 (bf16) or H/64 (MXFP8) stages; tile row r of tile t is the gate row
  *        f = 128 t + 64 (r / 128) + (r % 64) when r % 128 < 64, else the up row F + f.
  *   w2:  H/256 tiles of F/32 or F/64 stages; tile row r of tile t is weight row 256 t + r.
+ * PACKED for MXFP4 codes: the same tiles and row order, stages of 64 elements = 32 bytes of a
+ * row; each (expert, tile, stage) block is 8 KiB = 256 rows x 2 chunks of 16 bytes, chunk c of
+ * tile row r in slot c ^ ((r >> 2) & 1).
  * One stage of one tile is then one contiguous 16 KiB read that lands in LDS unchanged, and
  * 16 consecutive rows of one stage are one contiguous 1 KiB. */
 typedef enum { MOE_LAYOUT_ROW_MAJOR = 0, MOE_LAYOUT_PACKED = 1 } moe_layout;
 
 typedef struct {
-    const void* w13;              /* [E,2F,H] fp32, packed bf16 or packed MXFP8 codes; NVFP4 bytes [E,2F,H/2] */
-    const void* w2;               /* [E,H,F] fp32, packed bf16 or packed MXFP8 codes; NVFP4 bytes [E,H,F/2] */
-    const uint8_t* w13_scale;     /* NVFP4: E4M3 [E,2F,H/16]; MXFP8: E8M0 [E,2F,H/32] */
-    const uint8_t* w2_scale;      /* NVFP4: E4M3 [E,H,F/16]; MXFP8: E8M0 [E,H,F/32] */
+    const void* w13;              /* [E,2F,H] fp32, packed bf16 / MXFP8 codes; NVFP4 bytes [E,2F,H/2]; packed MXFP4 */
+    const void* w2;               /* [E,H,F] fp32, packed bf16 / MXFP8 codes; NVFP4 bytes [E,H,F/2]; packed MXFP4 */
+    const uint8_t* w13_scale;     /* NVFP4: E4M3 [E,2F,H/16]; MXFP8, MXFP4: E8M0 [E,2F,H/32] */
+    const uint8_t* w2_scale;      /* NVFP4: E4M3 [E,H,F/16]; MXFP8, MXFP4: E8M0 [E,H,F/32] */
     const float* w13_gscale;      /* NVFP4 only, nullable (=> 1.0): fp32 [E] */
     const float* w2_gscale;       /* NVFP4 only, nullable (=> 1.0): fp32 [E] */
     int32_t layout;               /* moe_layout: PACKED for bf16, ROW_MAJOR otherwise */
@@ -159,13 +168,13 @@ const char* moe_status_string(moe_status s);
  * MOE_ERR_UNSUPPORTED for problems the entry points would reject. */
 moe_status moe_workspace_size(const moe_problem* p, size_t* bytes);
 
-/* Bytes of the packed w13 and w2 of problem `p` (bf16 or MXFP8 weights).  Host only. */
+/* Bytes of the packed w13 and w2 of problem `p` (bf16, MXFP8 or MXFP4 weights).  Host only. */
 moe_status moe_packed_weights_size(const moe_problem* p, size_t* w13_bytes, size_t* w2_bytes);
 /* (both sizes and moe_pack_weights below cover the held experts only: local_experts of them
  * when it is non-zero, else all E) */
 
-/* Rewrite row-major bf16 expert weights (or MXFP8 E4M3 codes) w13 [E,2F,H] and w2 [E,H,F]
- * into the PACKED layout (see moe_layout).  A one-time transform of static weights; the outputs must not alias the
+/* Rewrite row-major bf16 expert weights (or MXFP8 / MXFP4 codes) w13 [E,2F,H] and w2 [E,H,F]
+ * (MXFP4: bytes [E,2F,H/2], [E,H,F/2]) into the PACKED layout (see moe_layout).  A one-time transform of static weights; the outputs must not alias the
  * inputs.  Either pair (w13 -> w13_packed, w2 -> w2_packed) may be NULL to skip it. */
 moe_status moe_pack_weights(const moe_problem* p, const void* w13, const void* w2,
                             void* w13_packed, void* w2_packed, void* stream);

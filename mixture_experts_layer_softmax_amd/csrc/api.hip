@@ -36,12 +36,20 @@ int ebegin(const moe_problem& p) { return p.local_experts ? p.expert_begin : 0; 
 int eend(const moe_problem& p) { return p.local_experts ? p.expert_begin + p.local_experts : p.num_experts; }
 
 int wfmt_of(const moe_problem& p) {
-    return p.w_dtype == MOE_F32 ? kWF32 : p.w_dtype == MOE_BF16 ? kWBF16 : p.w_dtype == MOE_NVFP4 ? kWNVFP4 : kWMXFP8;
+    switch (p.w_dtype) {
+        case MOE_F32: return kWF32;
+        case MOE_BF16: return kWBF16;
+        case MOE_NVFP4: return kWNVFP4;
+        case MOE_MXFP8: return kWMXFP8;
+        default: return kWMXFP4;
+    }
 }
+
+bool is_mx(const moe_problem& p) { return p.w_dtype == MOE_MXFP8 || p.w_dtype == MOE_MXFP4; }
 
 int family_of(const moe_problem& p) {
     if (p.act_dtype == MOE_F32) return kFamSimtF32;
-    if (p.w_dtype == MOE_MXFP8) return kFamPrefill;  // one MXFP8 kernel family (256-row tiles)
+    if (is_mx(p)) return kFamPrefill;  // one MX kernel family (256-row tiles)
     int path = p.path;
     if (path == MOE_PATH_AUTO) {
         const long A = long(p.num_tokens) * p.top_k;
@@ -62,14 +70,12 @@ moe_status check_problem(const moe_problem* p) {
         (p->local_experts == 0 && p->expert_begin != 0))
         return MOE_ERR_INVALID_ARGUMENT;
     if (p->act_dtype != MOE_F32 && p->act_dtype != MOE_BF16) return MOE_ERR_INVALID_ARGUMENT;
-    if (p->w_dtype != MOE_F32 && p->w_dtype != MOE_BF16 && p->w_dtype != MOE_NVFP4 &&
-        p->w_dtype != MOE_MXFP8)
-        return MOE_ERR_INVALID_ARGUMENT;
+    if (p->w_dtype < MOE_F32 || p->w_dtype > MOE_MXFP4) return MOE_ERR_INVALID_ARGUMENT;
     if (p->hidden % 64 || p->ffn % 64) return MOE_ERR_UNSUPPORTED;
     if (p->w_dtype == MOE_BF16 && (p->hidden % 256 || p->ffn % 128)) return MOE_ERR_UNSUPPORTED;
     // MXFP8: 256-row tiles, and E8M0 scales loaded 16 per row (8 stages of 64) at a time
-    if (p->w_dtype == MOE_MXFP8 && (p->hidden % 512 || p->ffn % 512)) return MOE_ERR_UNSUPPORTED;
-    if (p->w_dtype == MOE_MXFP8 && p->act_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+    if (is_mx(*p) && (p->hidden % 512 || p->ffn % 512)) return MOE_ERR_UNSUPPORTED;
+    if (is_mx(*p) && p->act_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
     if (p->act_dtype == MOE_F32 && p->w_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
     if (p->act_dtype == MOE_BF16 && p->w_dtype == MOE_F32) return MOE_ERR_UNSUPPORTED;
     if (long(p->num_tokens) * p->top_k > (1L << 30) || long(p->num_tokens) * p->hidden > (1L << 40))
@@ -101,7 +107,7 @@ Layout layout(const moe_problem& p) {
     L.tcount = take(4 * sizeof(int));
     L.hid = take(A * F * act_bytes(p));
     L.yperm = take(A * H * act_bytes(p));
-    const bool mx = p.w_dtype == MOE_MXFP8;  // MXFP8 copies of the GEMM inputs (codes + scales)
+    const bool mx = is_mx(p);  // MXFP8 copies of the GEMM inputs (codes + scales)
     L.xq = take(mx ? A * H : 0);
     L.xs = take(mx ? A * H / 32 : 0);
     L.hq = take(mx ? A * F : 0);
@@ -123,10 +129,10 @@ moe_status check_ws(const moe_problem& p, void* ws, size_t bytes) {
 
 moe_status check_weights(const moe_problem& p, const moe_expert_weights* w) {
     if (!w || !w->w13 || !w->w2 || !aligned(w->w13) || !aligned(w->w2)) return MOE_ERR_INVALID_ARGUMENT;
-    const bool packed = p.w_dtype == MOE_BF16 || p.w_dtype == MOE_MXFP8;
+    const bool packed = p.w_dtype == MOE_BF16 || is_mx(p);
     if (w->layout != (packed ? MOE_LAYOUT_PACKED : MOE_LAYOUT_ROW_MAJOR))
         return MOE_ERR_INVALID_ARGUMENT;
-    if (p.w_dtype == MOE_MXFP8) {
+    if (is_mx(p)) {
         if (!w->w13_scale || !w->w2_scale || !aligned(w->w13_scale) || !aligned(w->w2_scale))
             return MOE_ERR_INVALID_ARGUMENT;
     }
@@ -190,7 +196,7 @@ GemmArgs gemm_args(const moe_problem& p, int kind, const void* a, const int32_t*
 // MXFP8: quantize the GEMM's bf16 input rows (g.a_rows_limit of them) to E4M3 codes + E8M0
 // scales in the workspace and point the GEMM at them.  Other formats: nothing to do.
 moe_status mx_input(const moe_problem& p, GemmArgs& g, void* ws, const Layout& L, hipStream_t s) {
-    if (p.w_dtype != MOE_MXFP8) return MOE_OK;
+    if (!is_mx(p)) return MOE_OK;
     const bool up = g.kind == kGateUp;
     uint8_t* codes = at<uint8_t>(ws, up ? L.xq : L.hq);
     uint8_t* scales = at<uint8_t>(ws, up ? L.xs : L.hs);
@@ -224,19 +230,19 @@ moe_status moe_workspace_size(const moe_problem* p, size_t* bytes) {
 
 moe_status moe_packed_weights_size(const moe_problem* p, size_t* w13_bytes, size_t* w2_bytes) {
     MOE_TRY(check_problem(p));
-    if ((p->w_dtype != MOE_BF16 && p->w_dtype != MOE_MXFP8) || !w13_bytes || !w2_bytes)
+    if ((p->w_dtype != MOE_BF16 && !is_mx(*p)) || !w13_bytes || !w2_bytes)
         return MOE_ERR_INVALID_ARGUMENT;
     const size_t E = eend(*p) - ebegin(*p), H = p->hidden, F = p->ffn;  // held experts
-    const size_t es = p->w_dtype == MOE_BF16 ? 2 : 1;
-    *w13_bytes = E * 2 * F * H * es;
-    *w2_bytes = E * H * F * es;
+    const size_t num = p->w_dtype == MOE_BF16 ? 2 : 1, den = p->w_dtype == MOE_MXFP4 ? 2 : 1;
+    *w13_bytes = E * 2 * F * H * num / den;
+    *w2_bytes = E * H * F * num / den;
     return MOE_OK;
 }
 
 moe_status moe_pack_weights(const moe_problem* p, const void* w13, const void* w2, void* w13_packed,
                             void* w2_packed, void* stream) {
     MOE_TRY(check_problem(p));
-    if (p->w_dtype != MOE_BF16 && p->w_dtype != MOE_MXFP8) return MOE_ERR_INVALID_ARGUMENT;
+    if (p->w_dtype != MOE_BF16 && !is_mx(*p)) return MOE_ERR_INVALID_ARGUMENT;
     if ((w13 == nullptr) != (w13_packed == nullptr) || (w2 == nullptr) != (w2_packed == nullptr))
         return MOE_ERR_INVALID_ARGUMENT;
     for (const void* q : {w13, w2, (const void*)w13_packed, (const void*)w2_packed})
@@ -244,6 +250,12 @@ moe_status moe_pack_weights(const moe_problem* p, const void* w13, const void* w
     if ((w13 && w13 == w13_packed) || (w2 && w2 == w2_packed)) return MOE_ERR_INVALID_ARGUMENT;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int held = eend(*p) - ebegin(*p);
+    if (p->w_dtype == MOE_MXFP4) {
+        if (p->hidden % 512 || p->ffn % 512) return MOE_ERR_UNSUPPORTED;  // whole 32-byte stages
+        if (w13) MOE_TRY(dev(launch_pack_fp4(w13, w13_packed, 0, held, p->ffn, p->hidden, s)));
+        if (w2) MOE_TRY(dev(launch_pack_fp4(w2, w2_packed, 1, held, p->ffn, p->hidden, s)));
+        return MOE_OK;
+    }
     const int es = p->w_dtype == MOE_BF16 ? 2 : 1;
     if (w13) MOE_TRY(dev(launch_pack_bf16(w13, w13_packed, 0, held, p->ffn, p->hidden, es, s)));
     if (w2) MOE_TRY(dev(launch_pack_bf16(w2, w2_packed, 1, held, p->ffn, p->hidden, es, s)));

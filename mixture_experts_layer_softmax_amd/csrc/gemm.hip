@@ -981,7 +981,7 @@ static dim3 prefill_grid(const GemmArgs& g, int max_tiles, int bn) {
 
 hipError_t launch_gemm(const GemmArgs& g, int family, int max_tiles, hipStream_t s) {
     if (max_tiles <= 0) return hipSuccess;
-    if (g.wfmt == kWMXFP8) return launch_gemm_mxfp8(g, max_tiles, s);  // mx.hip
+    if (g.wfmt == kWMXFP8 || g.wfmt == kWMXFP4) return launch_gemm_mxfp8(g, max_tiles, s);  // mx.hip
     const bool up = g.kind == kGateUp;
     if (family == kFamSimtF32) {
         const int ncols = up ? g.F / 32 : (g.N + 63) / 64;

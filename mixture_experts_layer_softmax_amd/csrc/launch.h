@@ -37,7 +37,7 @@ struct DispatchArgs {
 };
 
 enum GemmKind { kGateUp = 0, kDown = 1 };
-enum WeightFmt { kWF32 = 0, kWBF16 = 1, kWNVFP4 = 2, kWMXFP8 = 3 };
+enum WeightFmt { kWF32 = 0, kWBF16 = 1, kWNVFP4 = 2, kWMXFP8 = 3, kWMXFP4 = 4 };
 enum GemmFamily { kFamSimtF32 = 0, kFamPrefill = 1, kFamDecode = 2 };
 
 struct GemmArgs {
@@ -79,6 +79,8 @@ hipError_t launch_gemm(const GemmArgs& g, int family, int max_tiles, hipStream_t
 // esize: bytes per element (2: bf16, 1: MXFP8 codes)
 hipError_t launch_pack_bf16(const void* src, void* dst, int kind, int E, int F, int H, int esize,
                             hipStream_t s);
+// MXFP4 codes (two E2M1 per byte) into 8 KiB stage blocks
+hipError_t launch_pack_fp4(const void* src, void* dst, int kind, int E, int F, int H, hipStream_t s);
 hipError_t launch_combine(const void* y_perm, const int32_t* inv_perm, const float* w, void* y,
                           int T, int k, int H, int A, bool bf16, hipStream_t s);
 

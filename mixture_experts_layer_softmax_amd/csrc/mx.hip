@@ -14,11 +14,17 @@
 //
 // Operand layout of v_mfma_scale_f32_32x32x64_f8f6f4 (measured on the hardware against exact
 // CPU products): lane l feeds row l & 31 of its operand; lane group g = l >> 5 supplies the
-// K elements [16g, 16g + 16) in bytes 0..15 and [32 + 16g, 48 + 16g) in bytes 16..31, and the
-// E8M0 scale of the 32-element block g (elements [32g, 32g + 32)) in its scale operand.  With
-// 64-byte LDS rows of four 16-byte chunks, lane group g reads chunks g and g + 2.  The result
-// is the usual 32 x 32 accumulator layout: element i of lane l is row 8 (i / 4) + 4 (l >> 5) +
-// (i % 4), column l & 31.
+// E8M0 scale of the 32-element block g (elements [32g, 32g + 32)) in its scale operand.  An fp8
+// operand holds the K elements [16g, 16g + 16) in bytes 0..15 and [32 + 16g, 48 + 16g) in
+// bytes 16..31: with 64-byte LDS rows of four 16-byte chunks, lane group g reads chunks g and
+// g + 2.  An fp4 (E2M1, format 4) operand holds elements [32g, 32g + 32) in its first 16 bytes,
+// the even element in the low nibble: with 32-byte rows, lane group g reads chunk g.  The
+// result is the usual 32 x 32 accumulator layout: element i of lane l is row
+// 8 (i / 4) + 4 (l >> 5) + (i % 4), column l & 31.
+//
+// MXFP4 weights (E2M1 + E8M0 per 32) run through the same GEMM with BF4 = 1: fp8 activations
+// times fp4 weights, 32-byte weight rows per stage (8 KiB packed blocks, chunk c of row r in
+// slot c ^ ((r >> 2) & 1)), one weight DMA per wavefront per stage.
 #include "device.h"
 #include "launch.h"
 #include "lds_dma.h"
@@ -123,12 +129,14 @@ hipError_t launch_mx_quantize(const void* in, long rows, int K, uint8_t* codes, 
 // loads of stage s+4.  Two fragment sets do not fit beside 128 accumulators in 256 registers.
 // ---------------------------------------------------------------------------------------
 
-template <int KIND>
+template <int KIND, int BF4>
 __global__ __launch_bounds__(512, 1) void gemm_prefill_mxfp8_kernel(GemmArgs g) {
     constexpr int BM = 256, BN = 256;
     constexpr int HALF = (KIND == kGateUp) ? BN / 2 : BN;
+    constexpr int BCH = BF4 ? 2 : 4;             // 16-byte chunks per weight row per stage
+    constexpr int NDMA = 2 + (BF4 ? 1 : 2);      // DMA instructions per wavefront per stage (+ scales)
     __shared__ uint4 sA0[BM * 4], sA1[BM * 4], sA2[BM * 4], sA3[BM * 4];
-    __shared__ uint4 sB0[BN * 4], sB1[BN * 4], sB2[BN * 4], sB3[BN * 4];
+    __shared__ uint4 sB0[BN * BCH], sB1[BN * BCH], sB2[BN * BCH], sB3[BN * BCH];
     __shared__ uint4 tS[2][BM + BN];  // per chunk of 8 stages: 16 scale bytes per activation row, then per weight row
 
     const int ncols = (KIND == kGateUp) ? g.F / HALF : (g.N + BN - 1) / BN;
@@ -160,7 +168,7 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_mxfp8_kernel(GemmArgs g) 
         return src < 0 ? 0 : (src >= g.a_rows_limit ? g.a_rows_limit - 1 : src);
     };
     const int nk = K / 64;
-    const char* const wblk = static_cast<const char*>(g.w) + (size_t(e) * ncols + nt) * size_t(nk) * 16384;
+    const char* const wblk = static_cast<const char*>(g.w) + (size_t(e) * ncols + nt) * size_t(nk) * (BN * BCH * 16);
     const char* pa[2];
     const char* pb[2];
 #pragma unroll
@@ -168,7 +176,7 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_mxfp8_kernel(GemmArgs g) 
         const int row = (i * 8 + wave) * 16 + (lane >> 2);
         const int ch = (lane & 3) ^ ((row >> 1) & 3);
         pa[i] = static_cast<const char*>(g.a) + size_t(act_row(row)) * K + ch * 16;
-        pb[i] = wblk + (i * 8 + wave) * 1024 + lane * 16;
+        pb[i] = wblk + (BF4 ? wave : i * 8 + wave) * 1024 + lane * 16;
     }
     const char* psc;  // this lane's row of scales: 16 bytes per chunk of 8 stages
     {
@@ -188,8 +196,8 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_mxfp8_kernel(GemmArgs g) 
         const int st_ = min((ST), last);                                                      \
         _Pragma("unroll") for (int i = 0; i < 2; ++i)                                         \
             dma16(pa[i] + st_ * 64, &SA[(i * 8 + wave) * 64]);                                \
-        _Pragma("unroll") for (int i = 0; i < 2; ++i)                                         \
-            dma16(pb[i] + size_t(st_) * 16384, &SB[(i * 8 + wave) * 64]);                     \
+        _Pragma("unroll") for (int i = 0; i < (BF4 ? 1 : 2); ++i)                             \
+            dma16(pb[i] + size_t(st_) * (BN * BCH * 16), &SB[(i * 8 + wave) * 64]);           \
         if (((ST) & 7) == 0)                                                                  \
             dma16(psc + (st_ >> 3) * 16, &tS[((ST) >> 3) & 1][sc_off]);                      \
     } while (0)
@@ -202,10 +210,21 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_mxfp8_kernel(GemmArgs g) 
     } while (0)
 #define MOE_MXSCALE(ST, ROW) \
     (int)reinterpret_cast<const uint8_t*>(&tS[((ST) >> 3) & 1][0])[(ROW) * 16 + ((ST) & 7) * 2 + g2]
+#define MOE_MXFRAG4(S, ROW, F)                                                                \
+    do {                                                                                      \
+        const int r4_ = (ROW);                                                                \
+        const uint4 c_ = S[r4_ * 2 + (g2 ^ ((r4_ >> 2) & 1))];                                \
+        F = i32x8_t{int(c_.x), int(c_.y), int(c_.z), int(c_.w), 0, 0, 0, 0};                  \
+    } while (0)
 #define MOE_MXREAD(SA, SB, ST)                                                                \
     do {                                                                                      \
-        MOE_MXFRAG(SB, gbn0 * 32 + (lane & 31), bf[0]);                                       \
-        MOE_MXFRAG(SB, gbn1 * 32 + (lane & 31), bf[1]);                                       \
+        if (BF4) {                                                                            \
+            MOE_MXFRAG4(SB, gbn0 * 32 + (lane & 31), bf[0]);                                  \
+            MOE_MXFRAG4(SB, gbn1 * 32 + (lane & 31), bf[1]);                                  \
+        } else {                                                                              \
+            MOE_MXFRAG(SB, gbn0 * 32 + (lane & 31), bf[0]);                                   \
+            MOE_MXFRAG(SB, gbn1 * 32 + (lane & 31), bf[1]);                                   \
+        }                                                                                     \
         bs[0] = MOE_MXSCALE((ST), BM + gbn0 * 32 + (lane & 31));                              \
         bs[1] = MOE_MXSCALE((ST), BM + gbn1 * 32 + (lane & 31));                              \
         _Pragma("unroll") for (int mi = 0; mi < 4; ++mi) {                                    \
@@ -219,7 +238,7 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_mxfp8_kernel(GemmArgs g) 
             if (mi * 2 + wr < nsub) {                                                         \
                 _Pragma("unroll") for (int ni = 0; ni < 2; ++ni) acc[mi][ni] =                \
                     __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[mi], bf[ni], acc[mi][ni], \
-                                                                    0, 0, 0, as[mi], 0, bs[ni]); \
+                                                                    0, BF4 ? 4 : 0, 0, as[mi], 0, bs[ni]); \
             }                                                                                 \
         }                                                                                     \
     } while (0)
@@ -237,32 +256,32 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_mxfp8_kernel(GemmArgs g) 
     MOE_MXISSUE(sA0, sB0, 0);
     MOE_MXISSUE(sA1, sB1, 1);
     MOE_MXISSUE(sA2, sB2, 2);
-    wait_vm_lgkm0<8>();  // stage 0 (and the first scale chunk) landed
+    wait_vm_lgkm0<2 * NDMA>();  // stage 0 (and the first scale chunk) landed
     block_barrier();
     MOE_MXREAD(sA0, sB0, 0);
     MOE_MXISSUE(sA3, sB3, 3);
     for (int s = 0;; s += 4) {
         MOE_MXMFMA();
         if (s + 1 >= nk) break;
-        wait_vm_lgkm0<8>();
+        wait_vm_lgkm0<2 * NDMA>();
         block_barrier();
         MOE_MXREAD(sA1, sB1, s + 1);
         MOE_MXISSUE(sA0, sB0, s + 4);
         MOE_MXMFMA();
         if (s + 2 >= nk) break;
-        wait_vm_lgkm0<8>();
+        wait_vm_lgkm0<2 * NDMA>();
         block_barrier();
         MOE_MXREAD(sA2, sB2, s + 2);
         MOE_MXISSUE(sA1, sB1, s + 5);
         MOE_MXMFMA();
         if (s + 3 >= nk) break;
-        wait_vm_lgkm0<8>();
+        wait_vm_lgkm0<2 * NDMA>();
         block_barrier();
         MOE_MXREAD(sA3, sB3, s + 3);
         MOE_MXISSUE(sA2, sB2, s + 6);
         MOE_MXMFMA();
         if (s + 4 >= nk) break;
-        wait_vm_lgkm0<8>();
+        wait_vm_lgkm0<2 * NDMA>();
         block_barrier();
         MOE_MXREAD(sA0, sB0, s + 4);
         MOE_MXISSUE(sA3, sB3, s + 7);
@@ -271,6 +290,7 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_mxfp8_kernel(GemmArgs g) 
 #undef MOE_MXISSUE
 #undef MOE_MXFRAG
 #undef MOE_MXSCALE
+#undef MOE_MXFRAG4
 #undef MOE_MXREAD
 #undef MOE_MXMFMA
 
@@ -297,14 +317,19 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_mxfp8_kernel(GemmArgs g) 
 }
 
 // Blocks: (row tile, column tile) pairs, a multiple of 8 so that every XCD walks the same number.
+// MXFP8 weights (kWMXFP8) and MXFP4 weights (kWMXFP4), both with MXFP8 activations.
 hipError_t launch_gemm_mxfp8(const GemmArgs& g, int max_tiles, hipStream_t s) {
     if (max_tiles <= 0) return hipSuccess;
     const int ncols = g.kind == kGateUp ? g.F / 128 : (g.N + 255) / 256;
     const dim3 grid(((max_tiles * ncols + 7) / 8) * 8);
-    if (g.kind == kGateUp)
-        hipLaunchKernelGGL((gemm_prefill_mxfp8_kernel<kGateUp>), grid, dim3(512), 0, s, g);
-    else
-        hipLaunchKernelGGL((gemm_prefill_mxfp8_kernel<kDown>), grid, dim3(512), 0, s, g);
+    const bool f4 = g.wfmt == kWMXFP4;
+    if (g.kind == kGateUp) {
+        if (f4) hipLaunchKernelGGL((gemm_prefill_mxfp8_kernel<kGateUp, 1>), grid, dim3(512), 0, s, g);
+        else hipLaunchKernelGGL((gemm_prefill_mxfp8_kernel<kGateUp, 0>), grid, dim3(512), 0, s, g);
+    } else {
+        if (f4) hipLaunchKernelGGL((gemm_prefill_mxfp8_kernel<kDown, 1>), grid, dim3(512), 0, s, g);
+        else hipLaunchKernelGGL((gemm_prefill_mxfp8_kernel<kDown, 0>), grid, dim3(512), 0, s, g);
+    }
     return hipGetLastError();
 }
 

@@ -1,6 +1,7 @@
-// pack.hip -- one-time rewrite of bf16 or MXFP8 (E4M3 codes) expert weights into the packed
-// layout of moe.h.  A stage is 64 bytes of a row either way (32 bf16 or 64 fp8 elements); the
-// kernel moves 16-byte chunks and counts a row in 2-byte units.
+// pack.hip -- one-time rewrite of bf16, MXFP8 (E4M3 codes) or MXFP4 (E2M1 codes) expert weights
+// into the packed layouts of moe.h.  For bf16 and MXFP8 a stage is 64 bytes of a row (32 bf16 or
+// 64 fp8 elements; pack_bf16_kernel moves 16-byte chunks and counts a row in 2-byte units); for
+// MXFP4 a stage of 64 elements is 32 bytes (pack_fp4_kernel).
 //
 // Each (expert, 256-row tile, 32-element stage) block becomes the byte image of an LDS slot of
 // the grouped GEMMs (rows 64 bytes, chunk c of row r in slot c ^ ((r >> 1) & 3)), so that the
@@ -39,6 +40,42 @@ __global__ __launch_bounds__(256) void pack_bf16_kernel(const uint4* __restrict_
         }
         dst[d] = src[((long(e) * Nw + wrow) * K + st * 32 + c * 8) / 8];
     }
+}
+
+// MXFP4 codes (two E2M1 per byte, K/2 bytes per row): one thread per 16-byte destination chunk
+// of 8 KiB (expert, tile, stage) blocks: 256 rows x 2 chunks, chunk c of row r in slot
+// c ^ ((r >> 2) & 1); tiles and row order as above.
+__global__ __launch_bounds__(256) void pack_fp4_kernel(const uint4* __restrict__ src,
+                                                       uint4* __restrict__ dst, int kind, int E,
+                                                       int F, int H) {
+    const int Kb = (kind == 0 ? H : F) / 2;          // bytes per weight row
+    const int Nw = kind == 0 ? 2 * F : H;
+    const int ntiles = kind == 0 ? F / 128 : H / 256;
+    const int nst = Kb / 32;
+    const long total = long(E) * ntiles * nst * 512;
+    for (long d = long(blockIdx.x) * blockDim.x + threadIdx.x; d < total; d += long(gridDim.x) * blockDim.x) {
+        const long blk = d >> 9;
+        const int w = int(d & 511), r = w >> 1, slot = w & 1;
+        const int c = slot ^ ((r >> 2) & 1);
+        const int st = int(blk % nst);
+        const long et = blk / nst;
+        const int t = int(et % ntiles), e = int(et / ntiles);
+        int wrow;
+        if (kind == 0) {
+            const int q = r & 127;
+            const int f = 128 * t + 64 * (r >> 7) + (q & 63);
+            wrow = q < 64 ? f : F + f;
+        } else {
+            wrow = 256 * t + r;
+        }
+        dst[d] = src[((long(e) * Nw + wrow) * Kb + st * 32 + c * 16) / 16];
+    }
+}
+
+hipError_t launch_pack_fp4(const void* src, void* dst, int kind, int E, int F, int H, hipStream_t s) {
+    hipLaunchKernelGGL(pack_fp4_kernel, dim3(8192), dim3(256), 0, s, static_cast<const uint4*>(src),
+                       static_cast<uint4*>(dst), kind, E, F, H);
+    return hipGetLastError();
 }
 
 hipError_t launch_pack_bf16(const void* src, void* dst, int kind, int E, int F, int H, int esize,

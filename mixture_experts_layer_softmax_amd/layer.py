@@ -53,7 +53,7 @@ class MoELayer:
         self.w13 = to_device(inputs["w13"], d, wk)
         self.w2 = to_device(inputs["w2"], d, wk)
         layout = lib.LAYOUT_ROW_MAJOR
-        if wdt in ("bf16", "mxfp8"):  # bf16 weights and MXFP8 codes are consumed packed
+        if wdt in ("bf16", "mxfp8", "mxfp4"):  # bf16 weights and MX codes are consumed packed
             p13 = torch.empty_like(self.w13)
             p2 = torch.empty_like(self.w2)
             lib.pack_weights(self.problem, self.w13, self.w2, p13, p2)

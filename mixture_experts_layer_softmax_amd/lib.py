@@ -15,10 +15,10 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmoe_mi355x.so")
 
 MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_DEVICE = range(5)
-MOE_F32, MOE_BF16, MOE_NVFP4, MOE_MXFP8 = 0, 1, 2, 3
+MOE_F32, MOE_BF16, MOE_NVFP4, MOE_MXFP8, MOE_MXFP4 = 0, 1, 2, 3, 4
 GATE_UP_SWIGLU, DOWN = 0, 1
 PATH_AUTO, PATH_PREFILL, PATH_DECODE = 0, 1, 2
-DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "nvfp4": MOE_NVFP4, "mxfp8": MOE_MXFP8}
+DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "nvfp4": MOE_NVFP4, "mxfp8": MOE_MXFP8, "mxfp4": MOE_MXFP4}
 PATHS = {"auto": PATH_AUTO, "prefill": PATH_PREFILL, "decode": PATH_DECODE}
 
 #: every symbol the header declares

@@ -18,6 +18,7 @@ nvfp4_decode    16      4096    256  8   2048 nvfp4 / bf16     none
 nvfp4_prefill   8192    4096    256  8   2048 nvfp4 / bf16     +beta on a 10 % hot set
 prefill6000     6000    4096    128  8   1536 bf16 / bf16      none (about 375 rows/expert)
 mxfp8_prefill   4096    4096    128  8   1536 mxfp8 / bf16     as prefill (same seed, same routing)
+mxfp4_prefill   4096    4096    128  8   1536 mxfp4 / bf16     as prefill (same seed, same routing)
 =============== ======= ====== ==== === ==== ================ ========================
 
 ``prefill6000`` is the prefill example of "Hosting Qwen on Blackwell" (section Prefill: an
@@ -89,6 +90,7 @@ WORKLOADS = {
     # the prefill workload's seed: same tokens, router and bias (same routing), its expert
     # weights drawn from the same streams and encoded in MXFP8 instead of bf16
     "mxfp8_prefill": Workload("mxfp8_prefill", 4096, 4096, 128, 8, 1536, "bf16", "mxfp8", 202, "normal"),
+    "mxfp4_prefill": Workload("mxfp4_prefill", 4096, 4096, 128, 8, 1536, "bf16", "mxfp4", 202, "normal"),
 }
 
 T_X, T_WR, T_BIAS, T_W13, T_W2, T_HOT = range(6)
@@ -155,6 +157,25 @@ def quantize_mxfp8(w: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     v = np.clip(v, np.float32(-448.0), np.float32(448.0))
     codes = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
     return codes.reshape(n, k), (X + 127).astype(np.uint8)
+
+
+def quantize_mxfp4(w: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Encode one expert matrix ``w[N, K]`` (float32) as MXFP4 along K (OCP microscaling
+    formats v1.0, E2M1 elements): per block of 32, X = floor(log2(amax)) - 2 (2 = the largest
+    E2M1 exponent; -127 for an all-zero block), stored as the E8M0 byte X + 127, and elements
+    w / 2^X clamped to +-6 and rounded to the nearest E2M1 value (ties to the even code).
+    Returns ``(packed[N, K/2] uint8, scales[N, K/32])``, even element in the low nibble."""
+    n, k = w.shape
+    assert k % 32 == 0
+    blocks = np.ascontiguousarray(w, dtype=np.float32).reshape(n, k // 32, 32)
+    amax = np.max(np.abs(blocks), axis=2)
+    _, ex = np.frexp(amax)
+    X = np.where(amax > 0, ex.astype(np.int32) - 1 - 2, -127)
+    X = np.clip(X, -127, 127)
+    v = np.ldexp(blocks, (-X)[:, :, None]).astype(np.float32)
+    codes = _e2m1_codes(v).reshape(n, k)  # nearest, ties to even, saturating at 6
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return packed, (X + 127).astype(np.uint8)
 
 
 def quantize_nvfp4(w: np.ndarray) -> tuple[np.ndarray, np.ndarray, np.float32]:
@@ -259,6 +280,18 @@ def gen_experts(wl: Workload, experts=None) -> dict:
             e = ids[i]
             w13[i], s13[i] = quantize_mxfp8(_expert_matrix(wl, T_W13, e, (2 * F, H)))
             w2[i], s2[i] = quantize_mxfp8(_expert_matrix(wl, T_W2, e, (H, F)))
+
+        out.update(w13=w13, w2=w2, w13_scale=s13, w2_scale=s2)
+    elif wl.wdt == "mxfp4":
+        w13 = np.empty((n, 2 * F, H // 2), dtype=np.uint8)
+        w2 = np.empty((n, H, F // 2), dtype=np.uint8)
+        s13 = np.empty((n, 2 * F, H // 32), dtype=np.uint8)
+        s2 = np.empty((n, H, F // 32), dtype=np.uint8)
+
+        def job(i):
+            e = ids[i]
+            w13[i], s13[i] = quantize_mxfp4(_expert_matrix(wl, T_W13, e, (2 * F, H)))
+            w2[i], s2[i] = quantize_mxfp4(_expert_matrix(wl, T_W2, e, (H, F)))
 
         out.update(w13=w13, w2=w2, w13_scale=s13, w2_scale=s2)
     else:

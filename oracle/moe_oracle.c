@@ -32,6 +32,9 @@
  *           bf16 activations: x is bf16 already, and hid, an activation of the layer like x, is
  *           rounded to bf16 (nearest even) first.  Products of decoded values are then
  *           accumulated in double like every other format.
+ *  MXFP4    the same layer with E2M1 weights (two per byte, even element in the low nibble):
+ *           w = e2m1 * 2^(s-127) with one E8M0 scale s per 32 elements along K; activations
+ *           in MXFP8 exactly as above (the pages evaluate MXFP4 weights beside MXFP8).
  *  held     expert parallelism with replicated inputs (same article, same section: with
  *           tensor parallelism the local dispatch selects only the tokens routed to the
  *           experts of the current rank, and the local combine is followed by an all-reduce):
@@ -51,7 +54,7 @@
 #include <omp.h>
 #endif
 
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_NVFP4 = 2, ORC_MXFP8 = 3 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_NVFP4 = 2, ORC_MXFP8 = 3, ORC_MXFP4 = 4 };
 
 /* ------------------------------------------------------------------------------------ */
 /* decoders                                                                              */
@@ -184,6 +187,11 @@ static double wget(const wmat* m, int64_t n, int64_t k) {
     if (m->dt == ORC_MXFP8)
         return g_e4m3[((const uint8_t*)m->w)[n * m->K + k]] *
                ldexp(1.0, (int)m->scale[n * (m->K / 32) + k / 32] - 127);
+    if (m->dt == ORC_MXFP4) {
+        uint8_t byte = ((const uint8_t*)m->w)[n * (m->K / 2) + k / 2];
+        uint8_t code = (k & 1) ? (byte >> 4) : (byte & 15); /* even k in the low nibble */
+        return g_e2m1[code] * ldexp(1.0, (int)m->scale[n * (m->K / 32) + k / 32] - 127);
+    }
     {
         uint8_t byte = ((const uint8_t*)m->w)[n * (m->K / 2) + k / 2];
         uint8_t code = (k & 1) ? (byte >> 4) : (byte & 15); /* even k in the low nibble */
@@ -312,6 +320,11 @@ static void expert_mats(const experts_t* ex, int64_t e, wmat* g13, wmat* g2) {
         g2->scale = ex->w2_scale + e * H * (F / 16);
         g13->gscale = ex->w13_gscale ? ex->w13_gscale[e] : 1.0;
         g2->gscale = ex->w2_gscale ? ex->w2_gscale[e] : 1.0;
+    } else if (ex->wdt == ORC_MXFP4) {
+        if (ex->w13) g13->w = (const uint8_t*)ex->w13 + e * (2 * F) * (H / 2);
+        g2->w = (const uint8_t*)ex->w2 + e * H * (F / 2);
+        if (ex->w13_scale) g13->scale = ex->w13_scale + e * (2 * F) * (H / 32);
+        g2->scale = ex->w2_scale + e * H * (F / 32);
     } else if (ex->wdt == ORC_MXFP8) {
         if (ex->w13) g13->w = (const uint8_t*)ex->w13 + e * (2 * F) * H;
         g2->w = (const uint8_t*)ex->w2 + e * H * F;
@@ -364,7 +377,7 @@ static void down_row(const experts_t* ex, int64_t e, const double* hid, double* 
     int64_t H = ex->H, F = ex->F;
     const double* h_in = hid;
     double* hq = NULL;
-    if (ex->wdt == ORC_MXFP8) {
+    if (ex->wdt == ORC_MXFP8 || ex->wdt == ORC_MXFP4) {
         hq = (double*)malloc(sizeof(double) * (size_t)F);
         for (int64_t f = 0; f < F; ++f) hq[f] = round_bf16(hid[f]); /* hid is a bf16 activation */
         mx_requantize(hq, F);
@@ -395,7 +408,7 @@ void oracle_expert_rows(int64_t H, int64_t F, int act_dt, int wdt, const void* x
         for (int64_t r = 0; r < nrows; ++r) {
             int64_t t = row_token[r];
             for (int64_t h = 0; h < H; ++h) xr[h] = (double)act_f(x, act_dt, t * H + h);
-            if (wdt == ORC_MXFP8) mx_requantize(xr, H);
+            if (wdt == ORC_MXFP8 || wdt == ORC_MXFP4) mx_requantize(xr, H);
             gate_up_row(&ex, row_expert[r], xr, hid);
             if (out) down_row(&ex, row_expert[r], hid, out + r * H);
             if (hid_out) memcpy(hid_out + r * F, hid, sizeof(double) * (size_t)F);

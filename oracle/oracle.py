@@ -21,8 +21,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "moe_oracle.c")
 _OUT = os.path.join(_HERE, "_build", "libmoe_oracle.so")
 
-F32, BF16, NVFP4, MXFP8 = 0, 1, 2, 3
-_DT = {"f32": F32, "bf16": BF16, "nvfp4": NVFP4, "mxfp8": MXFP8}
+F32, BF16, NVFP4, MXFP8, MXFP4 = 0, 1, 2, 3, 4
+_DT = {"f32": F32, "bf16": BF16, "nvfp4": NVFP4, "mxfp8": MXFP8, "mxfp4": MXFP4}
 
 _lock = threading.Lock()
 _lib = None
@@ -196,7 +196,7 @@ def expert_rows(inputs: dict, wdt: str, ffn: int, row_token, row_expert, want_hi
     g = lambda k: None if inputs.get(k) is None else np.ascontiguousarray(inputs[k])
     w13, w2 = g("w13"), g("w2")
     s13, s2, g13, g2 = g("w13_scale"), g("w2_scale"), g("w13_gscale"), g("w2_gscale")
-    if wdt in ("nvfp4", "mxfp8"):
+    if wdt in ("nvfp4", "mxfp8", "mxfp4"):
         assert w13.dtype == np.uint8 and s13 is not None and s2 is not None
     lib().oracle_expert_rows(H, ffn, _act_dt(x), _DT[wdt], _P(x), _P(w13), _P(w2), _P(s13), _P(s2),
                              _P(g13), _P(g2), n, _P(rt), _P(re), _P(out), _P(hid))

@@ -44,6 +44,13 @@ def dense_weights(inputs, wdt):
     if wdt == "mxfp8":
         return tuple(e4m3_to_f64(inputs[w]) * np.repeat(np.exp2(inputs[s].astype(np.float64) - 127), 32, axis=2)
                      for w, s in (("w13", "w13_scale"), ("w2", "w2_scale")))
+    if wdt == "mxfp4":
+        out = []
+        for w, s in (("w13", "w13_scale"), ("w2", "w2_scale")):
+            p = inputs[w]
+            codes = np.stack([p & 15, p >> 4], axis=-1).reshape(p.shape[0], p.shape[1], -1)
+            out.append(e2m1_to_f64(codes) * np.repeat(np.exp2(inputs[s].astype(np.float64) - 127), 32, axis=2))
+        return out[0], out[1]
     out = []
     for w, s, g in (("w13", "w13_scale", "w13_gscale"), ("w2", "w2_scale", "w2_gscale")):
         p = inputs[w]
@@ -101,7 +108,7 @@ def layer(inputs, logits, k, wdt, renormalize=True, keep=None):
     F = w2.shape[2]
     ids, w = select(logits, k, renormalize)
     y = np.zeros_like(x)
-    if wdt == "mxfp8":  # the layer quantizes its activations before each projection
+    if wdt in ("mxfp8", "mxfp4"):  # the layer quantizes its activations before each projection
         x = np.stack([mx_round_trip(r) for r in x])
     for t in range(x.shape[0]):
         for j in range(k):
@@ -111,7 +118,7 @@ def layer(inputs, logits, k, wdt, renormalize=True, keep=None):
             g = w13[e, :F] @ x[t]
             u = w13[e, F:] @ x[t]
             h = g / (1.0 + np.exp(-g)) * u
-            if wdt == "mxfp8":  # hid, a bf16 activation, rounded to bf16 and MX-quantized
+            if wdt in ("mxfp8", "mxfp4"):  # hid, a bf16 activation, rounded to bf16 and MX-quantized
                 m, ex = np.frexp(h)
                 h = mx_round_trip(np.ldexp(np.rint(m * 256.0) / 256.0, ex))
             y[t] += w[t, j] * (w2[e] @ h)

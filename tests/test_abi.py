@@ -48,7 +48,7 @@ def test_workspace_size_of_every_workload(L, name):
     # the intermediates dominate: hid [A,F] and y_perm [A,H] (+ their MXFP8 copies: codes and scales)
     act = 4 if wl.act == "f32" else 2
     inter = A * (wl.ffn + wl.hidden) * act
-    if wl.wdt == "mxfp8":
+    if wl.wdt.startswith("mx"):
         inter += A * (wl.ffn + wl.hidden) * 33 // 32
     assert n >= inter
     assert n < inter + 64 * 2 ** 20
@@ -80,6 +80,8 @@ def _call_route(L, p, x=FAKE, wr=FAKE, ids=FAKE, w=FAKE, ws=FAKE, nbytes=1 << 40
     (dict(act="f32", wdt="mxfp8"), lib.MOE_ERR_UNSUPPORTED),
     (dict(wdt="mxfp8", hidden=256, ffn=512), lib.MOE_ERR_UNSUPPORTED),
     (dict(wdt="mxfp8", hidden=512, ffn=256), lib.MOE_ERR_UNSUPPORTED),
+    (dict(wdt="mxfp4", hidden=256, ffn=512), lib.MOE_ERR_UNSUPPORTED),
+    (dict(act="f32", wdt="mxfp4"), lib.MOE_ERR_UNSUPPORTED),
 ])
 def test_problem_validation(L, kw, status):
     base = dict(tokens=16, hidden=256, experts=8, top_k=2, ffn=128, act="bf16", wdt="bf16")
@@ -141,6 +143,8 @@ def test_mxfp8_validation(L):
                          None, None, None, V(FAKE), 1 << 40, None) == lib.MOE_ERR_INVALID_ARGUMENT
     a, b = lib.packed_weights_size(p)
     assert a == 8 * 2 * 512 * 512 and b == 8 * 512 * 512  # one byte per code
+    a, b = lib.packed_weights_size(lib.problem(16, 512, 8, 2, 512, wdt="mxfp4"))
+    assert a == 8 * 2 * 512 * 256 and b == 8 * 512 * 256  # two codes per byte
     q = L.moe_quantize_mxfp8
     assert q(V(FAKE), 4, 48, V(FAKE), V(FAKE), None) == lib.MOE_ERR_INVALID_ARGUMENT    # K % 32
     assert q(V(FAKE), -1, 64, V(FAKE), V(FAKE), None) == lib.MOE_ERR_INVALID_ARGUMENT

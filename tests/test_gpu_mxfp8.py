@@ -1,4 +1,5 @@
-"""GPU parity of the MXFP8 layer (block-scaled fp8 matrix cores) against the CPU oracle.
+"""GPU parity of the MX layers (MXFP8 and MXFP4 weights, MXFP8 activations, block-scaled
+matrix cores) against the CPU oracle.
 
 The activation quantizer is an integer decision on exact bf16 inputs, so its codes and scales
 must match the oracle's bit for bit.  The layer outputs are held to the same 2e-2 max relative
@@ -18,11 +19,13 @@ pytestmark = pytest.mark.gpu
 
 TOL = 2e-2
 W = synth.Workload
-SMALL = {
-    "small_mxfp8": W("small_mxfp8", 384, 512, 16, 4, 512, "bf16", "mxfp8", 17, "normal"),
-    "ragged_mxfp8": W("ragged_mxfp8", 77, 1024, 5, 3, 1536, "bf16", "mxfp8", 18, "normal"),
-    "one_token_mxfp8": W("one_token_mxfp8", 1, 512, 8, 2, 512, "bf16", "mxfp8", 19, "none"),
-}
+SMALL = {}
+for _wdt in ("mxfp8", "mxfp4"):
+    SMALL.update({
+        "small_" + _wdt: W("small_" + _wdt, 384, 512, 16, 4, 512, "bf16", _wdt, 17, "normal"),
+        "ragged_" + _wdt: W("ragged_" + _wdt, 77, 1024, 5, 3, 1536, "bf16", _wdt, 18, "normal"),
+        "one_token_" + _wdt: W("one_token_" + _wdt, 1, 512, 8, 2, 512, "bf16", _wdt, 19, "none"),
+    })
 
 
 def note(msg):
@@ -82,13 +85,14 @@ def _check_forward(wl, inp, layer, tokens=None):
 def test_forward_matches_oracle(name):
     wl = SMALL[name]
     inp = synth.generate(wl)
-    note("mxfp8 forward %s" % name)
+    note("MX forward %s" % name)
     _check_forward(wl, inp, MoELayer.from_workload(wl, inp))
 
 
+@pytest.mark.parametrize("wdt", ["mxfp8", "mxfp4"])
 @pytest.mark.parametrize("kind", [lib.GATE_UP_SWIGLU, lib.DOWN])
-def test_grouped_gemm_matches_oracle(kind):
-    wl = SMALL["small_mxfp8"]
+def test_grouped_gemm_matches_oracle(kind, wdt):
+    wl = SMALL["small_" + wdt]
     inp = synth.generate(wl)
     layer = MoELayer.from_workload(wl, inp)
     r = O.route(inp, wl.top_k)
@@ -97,25 +101,26 @@ def test_grouped_gemm_matches_oracle(kind):
     p = layer.problem_for(wl.tokens)
     ws = layer.workspace(wl.tokens)
     offsets = torch.from_numpy(r["offsets"]).cuda()
-    note("mxfp8 grouped gemm kind %d" % kind)
+    note("%s grouped gemm kind %d" % (wdt, kind))
     if kind == lib.GATE_UP_SWIGLU:
         out = layer.empty_act(A, wl.ffn)
         lib.grouped_gemm(p, kind, layer.act_tensor(inp["x"]), torch.from_numpy(r["sorted_token"]).cuda(),
                          offsets, layer.weights, out, ws)
-        ref = O.gate_up_rows(inp, "mxfp8", wl.ffn, r["sorted_token"], expert_of_row)
+        ref = O.gate_up_rows(inp, wdt, wl.ffn, r["sorted_token"], expert_of_row)
     else:
         hid = synth.to_bf16_bits(np.random.default_rng(3).standard_normal((A, wl.ffn)).astype(np.float32) * 0.05)
         out = layer.empty_act(A, wl.hidden)
         lib.grouped_gemm(p, kind, to_device(hid, "cuda"), None, offsets, layer.weights, out, ws)
-        ref = O.down_rows(inp, "mxfp8", wl.hidden, bf16_bits_to_f64(hid), expert_of_row)
+        ref = O.down_rows(inp, wdt, wl.hidden, bf16_bits_to_f64(hid), expert_of_row)
     torch.cuda.synchronize()
     e = rel_err(bf16_bits_to_f64(to_host(out)), ref)
     note("  rel err %.3e" % e)
     assert e <= TOL
 
 
-def test_expert_parallel_share():
-    wl = SMALL["small_mxfp8"]
+@pytest.mark.parametrize("wdt", ["mxfp8", "mxfp4"])
+def test_expert_parallel_share(wdt):
+    wl = SMALL["small_" + wdt]
     b, n = 4, 8
     inp = synth.generate(wl, experts=range(b, b + n))
     layer = MoELayer.from_workload(wl, inp, expert_begin=b, local_experts=n)
@@ -125,16 +130,17 @@ def test_expert_parallel_share():
     ref = O.forward(inp, wl.top_k, wl.wdt, wl.ffn, held=(b, n))
     assert np.array_equal(dbg["inv_perm"].cpu().numpy().reshape(ref["inv_perm"].shape), ref["inv_perm"])
     e = rel_err(bf16_bits_to_f64(to_host(y)), ref["y"])
-    note("  mxfp8 share [%d, %d): y rel err %.3e" % (b, b + n, e))
+    note("  %s share [%d, %d): y rel err %.3e" % (wdt, b, b + n, e))
     assert e <= TOL
 
 
-def test_full_size_sampled():
-    wl = synth.WORKLOADS["mxfp8_prefill"]
-    note("mxfp8_prefill: generating inputs")
+@pytest.mark.parametrize("name", ["mxfp8_prefill", "mxfp4_prefill"])
+def test_full_size_sampled(name):
+    wl = synth.WORKLOADS[name]
+    note("%s: generating inputs" % name)
     inp = synth.generate(wl)
     layer = MoELayer.from_workload(wl, inp)
     rng = np.random.default_rng(98)
     toks = np.unique(np.concatenate([[0, wl.tokens - 1], rng.choice(wl.tokens, 10, replace=False)]))
-    note("mxfp8_prefill: running")
+    note("%s: running" % name)
     _check_forward(wl, inp, layer, tokens=toks)

@@ -124,6 +124,33 @@ def test_mx_quantizer_is_idempotent_and_matches_the_generator():
     assert np.array_equal(gc, c) and np.array_equal(gs, sc)
 
 
+def test_mxfp4_encoding_hand_values_and_round_trip():
+    """OCP MX v1.0 with E2M1 elements: shared exponent floor(log2 amax) - 2, elements clamped to
+    6 and rounded to the nearest E2M1 value (ties to even); checked against hand-worked blocks and
+    the per-element error bound, decoded with the brute force's own E2M1 table."""
+    def enc(first, rest=0.0):
+        w = np.full((1, 32), rest, dtype=np.float32)
+        w[0, 0] = first
+        packed, sc = synth.quantize_mxfp4(w)
+        return int(packed[0, 0] & 15), int(sc[0, 0])
+    assert enc(1.0) == (6, 125)        # 1.0 / 2^-2 = 4 = E2M1 code 6
+    assert enc(1.5) == (7, 125)        # 6: the largest E2M1 value
+    assert enc(1.9) == (7, 125)        # 7.6 clamps to 6
+    assert enc(-0.75) == (8 | 7, 124)  # amax 0.75 -> X = -3, -0.75 / 2^-3 = -6
+    assert enc(0.0) == (0, 0)          # all-zero block
+    rng = np.random.default_rng(23)
+    w = (rng.standard_normal((64, 256)) * 0.02).astype(np.float32)
+    packed, sc = synth.quantize_mxfp4(w)
+    codes = np.stack([packed & 15, packed >> 4], axis=-1).reshape(64, 256)
+    X = np.repeat(sc.astype(np.float64) - 127, 32, axis=1)
+    dec = BF.e2m1_to_f64(codes) * np.exp2(X)
+    scaled = np.abs(w) * np.exp2(-X)
+    normal = (scaled >= 1.0) & (scaled <= 6.0)      # E2M1 normals: one mantissa bit
+    assert np.all(np.abs(dec - w)[normal] <= np.abs(w)[normal] / 4 + 1e-12)
+    assert np.all(np.abs(dec - w)[scaled < 1.0] <= 0.25 * np.exp2(X)[scaled < 1.0] + 1e-12)
+    assert np.all(np.abs(dec)[scaled > 6.0] == 6.0 * np.exp2(X)[scaled > 6.0])
+
+
 def test_generator_bf16_rounding_matches_torch():
     a = np.random.default_rng(0).standard_normal(100000).astype(np.float32) * 3
     a[:4] = [1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -1.0 - 2 ** -8, 0.0]  # exact ties go to even
@@ -346,9 +373,9 @@ def _share(inp, b, n):
     return out
 
 
-@pytest.mark.parametrize("wdt", ["f32", "bf16", "nvfp4", "mxfp8"])
+@pytest.mark.parametrize("wdt", ["f32", "bf16", "nvfp4", "mxfp8", "mxfp4"])
 def test_partial_outputs_over_an_expert_partition_sum_to_the_layer(wdt):
-    wl, inp = _tiny(wdt=wdt, T=24, H=64, E=8, k=3, F=64 if wdt == "mxfp8" else 48)
+    wl, inp = _tiny(wdt=wdt, T=24, H=64, E=8, k=3, F=64 if wdt.startswith("mx") else 48)
     full = O.forward(inp, wl.top_k, wl.wdt, wl.ffn)
     total = np.zeros_like(full["y"])
     for b, n in ((0, 3), (3, 2), (5, 3)):
@@ -435,9 +462,9 @@ def test_top1_combine_returns_the_expert_row():
     assert np.array_equal(r["y"], rows)
 
 
-@pytest.mark.parametrize("wdt", ["f32", "bf16", "nvfp4", "mxfp8"])
+@pytest.mark.parametrize("wdt", ["f32", "bf16", "nvfp4", "mxfp8", "mxfp4"])
 def test_layer_matches_per_token_bruteforce(wdt):
-    wl, inp = _tiny(wdt=wdt, T=24, H=64, E=8, k=3, F=64 if wdt == "mxfp8" else 48)
+    wl, inp = _tiny(wdt=wdt, T=24, H=64, E=8, k=3, F=64 if wdt.startswith("mx") else 48)
     r = O.forward(inp, wl.top_k, wl.wdt, wl.ffn)
     y, ids, w = BF.layer(inp, r["logits"], wl.top_k, wdt)
     assert np.array_equal(r["topk_ids"], ids)
