@@ -19,6 +19,8 @@ nvfp4_prefill   8192    4096    256  8   2048 nvfp4 / bf16     +beta on a 10 % h
 prefill6000     6000    4096    128  8   1536 bf16 / bf16      none (about 375 rows/expert)
 mxfp8_prefill   4096    4096    128  8   1536 mxfp8 / bf16     as prefill (same seed, same routing)
 mxfp4_prefill   4096    4096    128  8   1536 mxfp4 / bf16     as prefill (same seed, same routing)
+mxfp{8,4}_      64      4096    128  8   1536 mx / bf16        as decode64 (same seed, same routing)
+  decode64
 =============== ======= ====== ==== === ==== ================ ========================
 
 ``prefill6000`` is the prefill example of "Hosting Qwen on Blackwell" (section Prefill: an
@@ -91,6 +93,9 @@ WORKLOADS = {
     # weights drawn from the same streams and encoded in MXFP8 instead of bf16
     "mxfp8_prefill": Workload("mxfp8_prefill", 4096, 4096, 128, 8, 1536, "bf16", "mxfp8", 202, "normal"),
     "mxfp4_prefill": Workload("mxfp4_prefill", 4096, 4096, 128, 8, 1536, "bf16", "mxfp4", 202, "normal"),
+    # the decode T=64 batch (same tokens, router and routing) with MX expert weights
+    "mxfp8_decode64": Workload("mxfp8_decode64", 64, 4096, 128, 8, 1536, "bf16", "mxfp8", 303, "none", x_sub=64),
+    "mxfp4_decode64": Workload("mxfp4_decode64", 64, 4096, 128, 8, 1536, "bf16", "mxfp4", 303, "none", x_sub=64),
 }
 
 T_X, T_WR, T_BIAS, T_W13, T_W2, T_HOT = range(6)

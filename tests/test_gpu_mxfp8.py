@@ -134,7 +134,7 @@ def test_expert_parallel_share(wdt):
     assert e <= TOL
 
 
-@pytest.mark.parametrize("name", ["mxfp8_prefill", "mxfp4_prefill"])
+@pytest.mark.parametrize("name", ["mxfp8_prefill", "mxfp4_prefill", "mxfp8_decode64", "mxfp4_decode64"])
 def test_full_size_sampled(name):
     wl = synth.WORKLOADS[name]
     note("%s: generating inputs" % name)
