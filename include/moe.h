@@ -132,8 +132,12 @@ typedef struct {
  * 0 (a zero-initialised struct) is the single-GPU layer. */
 
 /* Weight layouts.  bf16 expert weights and MXFP8 codes are consumed in the PACKED layout
- * written by moe_pack_weights; fp32 and NVFP4 expert weights in the ROW_MAJOR layout described
- * below (MXFP8 scales stay row-major).
+ * written by moe_pack_weights; fp32 expert weights in the ROW_MAJOR layout described below
+ * (MXFP8 scales stay row-major).  NVFP4 weights are accepted in either layout: ROW_MAJOR
+ * (bytes and E4M3 scales as described in moe_expert_weights, any shape the problem rules
+ * allow) or PACKED (bytes by moe_pack_weights and scales by moe_pack_scales, both packed;
+ * needs H % 256 == 0 and F % 128 == 0).  Both give the same layer; PACKED is read with whole
+ * cache lines by the decode and prefill kernels.
  *
  * PACKED (bf16 and MXFP8 codes; needs H % 256 == 0 and F % 128 == 0; same byte size as
  * row-major): weights are cut into tiles of 256 weight rows and stages of 64 bytes of a row
@@ -146,6 +150,11 @@ typedef struct {
  * PACKED for MXFP4 codes: the same tiles and row order, stages of 64 elements = 32 bytes of a
  * row; each (expert, tile, stage) block is 8 KiB = 256 rows x 2 chunks of 16 bytes, chunk c of
  * tile row r in slot c ^ ((r >> 2) & 1).
+ * PACKED for NVFP4: the same tiles and row order, stages of 32 elements; each (expert, tile,
+ * stage) block of the bytes is 4 KiB = 256 rows x 16 bytes (tile row r at byte 16 r, no
+ * slots), and each (expert, tile, stage pair) block of the scales is 1 KiB = 256 rows x the 4
+ * scale bytes of stages 2m and 2m+1 of that row (tile row r at byte 4 r).  Blocks are ordered
+ * [expert][tile][stage] and [expert][tile][stage pair].
  * One stage of one tile is then one contiguous 16 KiB read that lands in LDS unchanged, and
  * 16 consecutive rows of one stage are one contiguous 1 KiB. */
 typedef enum { MOE_LAYOUT_ROW_MAJOR = 0, MOE_LAYOUT_PACKED = 1 } moe_layout;
@@ -157,7 +166,7 @@ typedef struct {
     const uint8_t* w2_scale;      /* NVFP4: E4M3 [E,H,F/16]; MXFP8, MXFP4: E8M0 [E,H,F/32] */
     const float* w13_gscale;      /* NVFP4 only, nullable (=> 1.0): fp32 [E] */
     const float* w2_gscale;       /* NVFP4 only, nullable (=> 1.0): fp32 [E] */
-    int32_t layout;               /* moe_layout: PACKED for bf16, ROW_MAJOR otherwise */
+    int32_t layout;               /* moe_layout: PACKED for bf16 and MX, ROW_MAJOR for fp32, either for NVFP4 */
 } moe_expert_weights;
 
 /* Text of a status code (static storage). */
@@ -168,16 +177,27 @@ const char* moe_status_string(moe_status s);
  * MOE_ERR_UNSUPPORTED for problems the entry points would reject. */
 moe_status moe_workspace_size(const moe_problem* p, size_t* bytes);
 
-/* Bytes of the packed w13 and w2 of problem `p` (bf16, MXFP8 or MXFP4 weights).  Host only. */
+/* Bytes of the packed w13 and w2 of problem `p` (bf16, MXFP8, MXFP4 or NVFP4 weights; for
+ * NVFP4 the bytes, not the scales, whose packed size equals their row-major size).  Host only. */
 moe_status moe_packed_weights_size(const moe_problem* p, size_t* w13_bytes, size_t* w2_bytes);
 /* (both sizes and moe_pack_weights below cover the held experts only: local_experts of them
  * when it is non-zero, else all E) */
 
-/* Rewrite row-major bf16 expert weights (or MXFP8 / MXFP4 codes) w13 [E,2F,H] and w2 [E,H,F]
- * (MXFP4: bytes [E,2F,H/2], [E,H,F/2]) into the PACKED layout (see moe_layout).  A one-time transform of static weights; the outputs must not alias the
- * inputs.  Either pair (w13 -> w13_packed, w2 -> w2_packed) may be NULL to skip it. */
+/* Rewrite row-major bf16 expert weights (or MXFP8 / MXFP4 codes, or NVFP4 bytes) w13 [E,2F,H]
+ * and w2 [E,H,F] (MXFP4 and NVFP4: bytes [E,2F,H/2], [E,H,F/2]) into the PACKED layout (see
+ * moe_layout).  A one-time transform of static weights; the outputs must not alias the
+ * inputs.  Either pair (w13 -> w13_packed, w2 -> w2_packed) may be NULL to skip it.
+ * MOE_ERR_UNSUPPORTED for shapes the PACKED layout does not cover. */
 moe_status moe_pack_weights(const moe_problem* p, const void* w13, const void* w2,
                             void* w13_packed, void* w2_packed, void* stream);
+
+/* NVFP4 only: rewrite the row-major E4M3 scales w13_scale [E,2F,H/16] and w2_scale [E,H,F/16]
+ * into the PACKED layout of NVFP4 scales (see moe_layout); same byte sizes.  The outputs must
+ * not alias the inputs; either pair may be NULL to skip it.
+ * MOE_ERR_INVALID_ARGUMENT for other weight formats, MOE_ERR_UNSUPPORTED unless H % 256 == 0
+ * and F % 128 == 0. */
+moe_status moe_pack_scales(const moe_problem* p, const uint8_t* w13_scale, const uint8_t* w2_scale,
+                           uint8_t* w13_scale_packed, uint8_t* w2_scale_packed, void* stream);
 
 /* Route.  x [T,H] and w_router [E,H] in act_dtype; router_bias fp32 [E] or NULL.
  * Writes topk_ids int32 [T,k] and topk_w fp32 [T,k] (routing contract above). */

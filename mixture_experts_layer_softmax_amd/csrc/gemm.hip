@@ -421,7 +421,7 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_bf16_kernel(GemmArgs g) {
 // iteration also publishes each raw row to the thread that decodes it.
 // ---------------------------------------------------------------------------------------
 
-template <int KIND, int NW>
+template <int KIND, int NW, bool PK>
 __global__ __launch_bounds__(NW * 64, 1) void gemm_prefill_nvfp4_kernel(GemmArgs g) {
     static_assert(NW == 4 || NW == 8, "4 or 8 wavefronts");
     constexpr int BM = 256, BN = 256, BKS = 32;
@@ -474,8 +474,13 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_prefill_nvfp4_kernel(GemmArgs
         wrow = min(nt * BN + mrow, g.N - 1);
     }
     const size_t wrow_g = size_t(e) * Nw + wrow;
-    const char* const pq = static_cast<const char*>(g.w) + wrow_g * (K / 2);
-    const char* const ps = reinterpret_cast<const char*>(g.wscale) + wrow_g * (K / 16);
+    // PK: tile nt of the PACKED layout holds exactly these rows in this order (row mrow at
+    // 16 mrow of each 4 KiB stage block and at 4 mrow of each 1 KiB stage-pair scale block)
+    const size_t tb = size_t(e) * ((KIND == kGateUp) ? g.F / 128 : g.N / 256) + nt;
+    const char* const pq = PK ? static_cast<const char*>(g.w) + tb * (K / 32) * 4096 + mrow * 16
+                              : static_cast<const char*>(g.w) + wrow_g * (K / 2);
+    const char* const ps = PK ? reinterpret_cast<const char*>(g.wscale) + tb * (K / 64) * 1024 + mrow * 4
+                              : reinterpret_cast<const char*>(g.wscale) + wrow_g * (K / 16);
     // weight row groups of this wavefront: gate/up, NB/2 gate groups then their up groups
     int gb[NB];
     int gcol;  // first hid column (gate/up) or output column (down) of this wavefront
@@ -504,9 +509,9 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_prefill_nvfp4_kernel(GemmArgs
     do {                                                                                        \
         const int k0_ = (K0);                                                                   \
         if (NW == 4 || wave < 4)                                                                \
-            dma16(pq + k0_ / 2, &SN[(wave & 3) * 64]);                                          \
+            dma16(pq + (PK ? (k0_ >> 5) * 4096 : k0_ / 2), &SN[(wave & 3) * 64]);               \
         if (NW == 4 || wave >= 4)                                                               \
-            dma4(ps + ((k0_ >> 4) & ~3), &SS[(wave & 3) * 64]);                                 \
+            dma4(ps + (PK ? (k0_ >> 6) * 1024 : ((k0_ >> 4) & ~3)), &SS[(wave & 3) * 64]);      \
     } while (0)
     // NW = 4: thread t decodes weight row t; NW = 8: half h = t & 1 of row t >> 1 (chunks
     // 2h, 2h+1, scale h)
@@ -642,8 +647,11 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_prefill_nvfp4_kernel(GemmArgs
 // and are added in a fixed order (deterministic).
 // ---------------------------------------------------------------------------------------
 
-template <int KIND, int WFMT, int SPLITK, bool WIN4 = false>
+// NVL (NVFP4 only): 0 row-major bytes, 128-wide K blocks; 1 row-major, 512-wide windows;
+// 2 PACKED bytes and scales (the 128-wide block mapping, read from [tile][stage] blocks).
+template <int KIND, int WFMT, int SPLITK, int NVL = 0>
 __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
+    constexpr bool WIN4 = NVL == 1;
     constexpr int CG = 4 / SPLITK;              // column groups per block
     constexpr int NB = (KIND == kGateUp) ? 2 : 1;  // weight row sets per column group
     __shared__ f32x4_t red[4][NB][64];
@@ -717,6 +725,27 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
     const uint8_t* pq1 = static_cast<const uint8_t*>(g.w) + w1 * (K / 2) + (WIN4 ? 64 : 16) * q;
     const uint8_t* ps0 = g.wscale + w0 * (K / 16) + (WIN4 ? 8 : 2) * q;
     const uint8_t* ps1 = g.wscale + w1 * (K / 16) + (WIN4 ? 8 : 2) * q;
+    int ssh = 0;  // NVL 2: bit offset of this lane's stage in its stage-pair scale word
+    if constexpr (WFMT == kWNVFP4 && NVL == 2) {
+        // lane q of K block j takes stage 4 j + q: bytes at 16 r of the stage's 4 KiB block,
+        // scales in the word at 4 r of stage pair 2 j + q / 2 (1 KiB blocks), half q & 1
+        const int nst = K / 32;
+        int t, r_a;
+        if (KIND == kGateUp) {
+            t = col >> 7;
+            r_a = ((col >> 6) & 1) * 128 + (col & 63);  // gate tile row; the up row is 64 below
+        } else {
+            t = wrow0 >> 8;
+            r_a = wrow0 & 255;
+        }
+        const int ntiles = (KIND == kGateUp) ? g.F / 128 : g.N / 256;
+        const size_t tb = size_t(e) * ntiles + t;
+        pq0 = static_cast<const uint8_t*>(g.w) + tb * nst * 4096 + (q * 256 + r_a) * 16;
+        pq1 = pq0 + 64 * 16;
+        ps0 = g.wscale + tb * (nst / 2) * 1024 + ((q >> 1) * 256 + r_a) * 4;
+        ps1 = ps0 + 64 * 4;
+        ssh = (q & 1) * 16;
+    }
     auto load = [&](Blk& b, int j) __attribute__((always_inline)) {
         const int k = 128 * j;
         if constexpr (WFMT == kWBF16) {
@@ -740,11 +769,20 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
             b.a1 = ld16(pa + k + 8);
             b.a2 = ld16(pa + k + 16);
             b.a3 = ld16(pa + k + 24);
-            b.pg = ld16(pq0 + 64 * j);
-            b.sg = *reinterpret_cast<const uint16_t*>(ps0 + 8 * j);
-            if constexpr (KIND == kGateUp) {
-                b.pu = ld16(pq1 + 64 * j);
-                b.su = *reinterpret_cast<const uint16_t*>(ps1 + 8 * j);
+            if constexpr (NVL == 2) {  // e4m3_value reads only the low 8 bits of its argument
+                b.pg = ld16(pq0 + 16384 * j);
+                b.sg = *reinterpret_cast<const uint32_t*>(ps0 + 2048 * j) >> ssh;
+                if constexpr (KIND == kGateUp) {
+                    b.pu = ld16(pq1 + 16384 * j);
+                    b.su = *reinterpret_cast<const uint32_t*>(ps1 + 2048 * j) >> ssh;
+                }
+            } else {
+                b.pg = ld16(pq0 + 64 * j);
+                b.sg = *reinterpret_cast<const uint16_t*>(ps0 + 8 * j);
+                if constexpr (KIND == kGateUp) {
+                    b.pu = ld16(pq1 + 64 * j);
+                    b.su = *reinterpret_cast<const uint16_t*>(ps1 + 8 * j);
+                }
             }
         }
     };
@@ -998,11 +1036,16 @@ hipError_t launch_gemm(const GemmArgs& g, int family, int max_tiles, hipStream_t
             hipLaunchKernelGGL((gemm_prefill_bf16_kernel<kDown>), grid, dim3(512), 0, s, g);
     } else if (family == kFamPrefill && g.F % 128 == 0) {
         const dim3 grid = prefill_grid(g, max_tiles, 256);
-        if (up)
-            hipLaunchKernelGGL((gemm_prefill_nvfp4_kernel<kGateUp, 4>), grid, dim3(256), 0, s, g);
+        if (up && g.wpacked)
+            hipLaunchKernelGGL((gemm_prefill_nvfp4_kernel<kGateUp, 4, true>), grid, dim3(256), 0, s, g);
+        else if (up)
+            hipLaunchKernelGGL((gemm_prefill_nvfp4_kernel<kGateUp, 4, false>), grid, dim3(256), 0, s, g);
+        else if (g.wpacked)
+            hipLaunchKernelGGL((gemm_prefill_nvfp4_kernel<kDown, 8, true>), grid, dim3(512), 0, s, g);
         else
-            hipLaunchKernelGGL((gemm_prefill_nvfp4_kernel<kDown, 8>), grid, dim3(512), 0, s, g);
+            hipLaunchKernelGGL((gemm_prefill_nvfp4_kernel<kDown, 8, false>), grid, dim3(512), 0, s, g);
     } else if (family == kFamPrefill) {
+        if (g.wpacked) return hipErrorInvalidValue;  // PACKED NVFP4 needs F % 128 == 0
         launch_mfma<PF_BM, PF_BN, PF_WM, PF_WN>(g, max_tiles, s);
     } else if (g.K % 128 == 0) {
         // split K until there are about 4 wavefronts per SIMD (4096) for the worst-case tile count
@@ -1015,8 +1058,13 @@ hipError_t launch_gemm(const GemmArgs& g, int family, int max_tiles, hipStream_t
         if (g.wfmt == kWBF16) {
             if (up) { if (split == 1) MOE_DEC(kGateUp, kWBF16, 1); else if (split == 2) MOE_DEC(kGateUp, kWBF16, 2); else MOE_DEC(kGateUp, kWBF16, 4); }
             else    { if (split == 1) MOE_DEC(kDown, kWBF16, 1);   else if (split == 2) MOE_DEC(kDown, kWBF16, 2);   else MOE_DEC(kDown, kWBF16, 4); }
+        } else if (g.wpacked) {
+#define MOE_DECP(KD, SK) hipLaunchKernelGGL((gemm_decode_kernel<KD, kWNVFP4, SK, 2>), grid, block, 0, s, g)
+            if (up) { if (split == 1) MOE_DECP(kGateUp, 1); else if (split == 2) MOE_DECP(kGateUp, 2); else MOE_DECP(kGateUp, 4); }
+            else    { if (split == 1) MOE_DECP(kDown, 1);   else if (split == 2) MOE_DECP(kDown, 2);   else MOE_DECP(kDown, 4); }
+#undef MOE_DECP
         } else if ((g.K / 128 / split) % 4 == 0) {  // 512-wide scale windows
-#define MOE_DEC4(KD, SK) hipLaunchKernelGGL((gemm_decode_kernel<KD, kWNVFP4, SK, true>), grid, block, 0, s, g)
+#define MOE_DEC4(KD, SK) hipLaunchKernelGGL((gemm_decode_kernel<KD, kWNVFP4, SK, 1>), grid, block, 0, s, g)
             if (up) { if (split == 1) MOE_DEC4(kGateUp, 1); else if (split == 2) MOE_DEC4(kGateUp, 2); else MOE_DEC4(kGateUp, 4); }
             else    { if (split == 1) MOE_DEC4(kDown, 1);   else if (split == 2) MOE_DEC4(kDown, 2);   else MOE_DEC4(kDown, 4); }
 #undef MOE_DEC4
@@ -1026,6 +1074,7 @@ hipError_t launch_gemm(const GemmArgs& g, int family, int max_tiles, hipStream_t
         }
 #undef MOE_DEC
     } else {  // NVFP4 with K % 128 != 0
+        if (g.wpacked) return hipErrorInvalidValue;  // PACKED NVFP4 needs H % 256, F % 128 == 0
         launch_mfma<DC_BM, DC_BN, DC_WM, DC_WN>(g, max_tiles, s);
     }
     return hipGetLastError();

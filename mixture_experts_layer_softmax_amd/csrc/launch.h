@@ -48,6 +48,7 @@ struct GemmArgs {
     const int* tile_count;
     const void* w;          // [E, Nw, K] values or [E, Nw, K/2] packed nibbles
     const uint8_t* wscale;  // [E, Nw, K/16] (NVFP4) or [E, Nw, K/32] (MXFP8)
+    int wpacked;            // NVFP4: bytes and scales in the PACKED layout (tile/stage blocks)
     const uint8_t* ascale;  // MXFP8: E8M0 scales of `a` [rows, K/32] (a holds E4M3 codes)
     const float* gscale;    // [E] or null (NVFP4)
     void* out;              // [A, N]
@@ -80,6 +81,10 @@ hipError_t launch_gemm(const GemmArgs& g, int family, int max_tiles, hipStream_t
 hipError_t launch_pack_bf16(const void* src, void* dst, int kind, int E, int F, int H, int esize,
                             hipStream_t s);
 // MXFP4 codes (two E2M1 per byte) into 8 KiB stage blocks
+// NVFP4 PACKED layout: bytes (16 per row and 32-element stage) or E4M3 scales (4 per row and
+// stage pair) of w13 (kind 0) or w2 (kind 1) into [expert][tile][stage] blocks of 256 rows.
+hipError_t launch_pack_nvfp4(const void* src, void* dst, int kind, int E, int F, int H, bool scales,
+                             hipStream_t s);
 hipError_t launch_pack_fp4(const void* src, void* dst, int kind, int E, int F, int H, hipStream_t s);
 hipError_t launch_combine(const void* y_perm, const int32_t* inv_perm, const float* w, void* y,
                           int T, int k, int H, int A, bool bf16, hipStream_t s);

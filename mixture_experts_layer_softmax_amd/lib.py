@@ -23,7 +23,7 @@ PATHS = {"auto": PATH_AUTO, "prefill": PATH_PREFILL, "decode": PATH_DECODE}
 
 #: every symbol the header declares
 EXPORTS = ("moe_status_string", "moe_workspace_size", "moe_packed_weights_size", "moe_pack_weights",
-           "moe_route", "moe_permute", "moe_grouped_gemm", "moe_combine", "moe_forward",
+           "moe_pack_scales", "moe_route", "moe_permute", "moe_grouped_gemm", "moe_combine", "moe_forward",
            "moe_quantize_mxfp8", "moe_probe_mfma_bf16", "moe_probe_read")
 LAYOUT_ROW_MAJOR, LAYOUT_PACKED = 0, 1
 
@@ -70,6 +70,8 @@ def load() -> C.CDLL:
             L.moe_packed_weights_size.argtypes = [P, C.POINTER(C.c_size_t), C.POINTER(C.c_size_t)]
             L.moe_pack_weights.restype = i32
             L.moe_pack_weights.argtypes = [P, vp, vp, vp, vp, vp]
+            L.moe_pack_scales.restype = i32
+            L.moe_pack_scales.argtypes = [P, vp, vp, vp, vp, vp]
             L.moe_route.restype = i32
             L.moe_route.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
             L.moe_permute.restype = i32
@@ -143,6 +145,11 @@ def packed_weights_size(p: Problem):
 def pack_weights(p, w13, w2, w13_packed, w2_packed, stream=None):
     _check(load().moe_pack_weights(C.byref(p), _ptr(w13), _ptr(w2), _ptr(w13_packed),
                                    _ptr(w2_packed), _stream(stream)), "moe_pack_weights")
+
+
+def pack_scales(p, w13_scale, w2_scale, w13_scale_packed, w2_scale_packed, stream=None):
+    _check(load().moe_pack_scales(C.byref(p), _ptr(w13_scale), _ptr(w2_scale), _ptr(w13_scale_packed),
+                                  _ptr(w2_scale_packed), _stream(stream)), "moe_pack_scales")
 
 
 def route(p, x, w_router, bias, topk_ids, topk_w, ws, stream=None):

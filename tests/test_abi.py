@@ -115,18 +115,39 @@ def test_gemm_and_forward_validation(L):
     assert L.moe_forward(C.byref(p), V(FAKE), V(FAKE), None, C.byref(w), V(FAKE), None, None, None,
                          None, None, None, V(FAKE), 10, None) == lib.MOE_ERR_WORKSPACE_TOO_SMALL
     assert L.moe_combine(C.byref(p), None, V(FAKE), V(FAKE), V(FAKE), None) == lib.MOE_ERR_INVALID_ARGUMENT
-    # layouts: bf16 weights must be packed, NVFP4 weights row-major
+    # layouts: bf16 weights must be packed; NVFP4 weights row-major or, where the shape
+    # tiles (H % 256, F % 128), packed
     pb = lib.problem(16, 256, 8, 2, 128, wdt="bf16")
     for layout, status in ((0, lib.MOE_ERR_INVALID_ARGUMENT), (1, lib.MOE_ERR_WORKSPACE_TOO_SMALL)):
         wb = lib.ExpertWeights(FAKE, FAKE, None, None, None, None, layout)
         assert L.moe_forward(C.byref(pb), V(FAKE), V(FAKE), None, C.byref(wb), V(FAKE), None, None,
                              None, None, None, None, V(FAKE), 10, None) == status
-    w = lib.ExpertWeights(FAKE, FAKE, FAKE, FAKE, None, None, 1)
+    p192 = lib.problem(16, 192, 8, 2, 128, wdt="nvfp4")
+    for layout, status in ((1, lib.MOE_ERR_UNSUPPORTED), (2, lib.MOE_ERR_INVALID_ARGUMENT)):
+        w = lib.ExpertWeights(FAKE, FAKE, FAKE, FAKE, None, None, layout)
+        assert L.moe_forward(C.byref(p192), V(FAKE), V(FAKE), None, C.byref(w), V(FAKE), None, None,
+                             None, None, None, None, V(FAKE), 1 << 40, None) == status
+    w = lib.ExpertWeights(FAKE, FAKE, FAKE, FAKE, None, None, 1)  # packed NVFP4 is validated
     assert L.moe_forward(C.byref(p), V(FAKE), V(FAKE), None, C.byref(w), V(FAKE), None, None, None,
-                         None, None, None, V(FAKE), 1 << 40, None) == lib.MOE_ERR_INVALID_ARGUMENT
-    # packing: bf16 or MXFP8 only (p is NVFP4 here), no aliasing, shapes the layout can tile
-    assert L.moe_pack_weights(C.byref(p), V(FAKE), V(FAKE), V(FAKE + 4096), V(FAKE + 8192),
+                         None, None, None, V(FAKE), 10, None) == lib.MOE_ERR_WORKSPACE_TOO_SMALL
+    # packing: not for fp32 weights, no aliasing, shapes the layout can tile
+    pf = lib.problem(16, 256, 8, 2, 128, act="f32", wdt="f32")
+    assert L.moe_pack_weights(C.byref(pf), V(FAKE), V(FAKE), V(FAKE + 4096), V(FAKE + 8192),
                               None) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_pack_weights(C.byref(p192), V(FAKE), None, V(FAKE + 4096), None,
+                              None) == lib.MOE_ERR_UNSUPPORTED
+    # NVFP4 scales: NVFP4 only, pairs, no aliasing, alignment, shapes the layout can tile
+    ps = L.moe_pack_scales
+    assert ps(C.byref(pb), V(FAKE), None, V(FAKE + 4096), None, None) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert ps(C.byref(p), V(FAKE), None, None, None, None) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert ps(C.byref(p), V(FAKE), None, V(FAKE), None, None) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert ps(C.byref(p), V(FAKE + 4), None, V(FAKE + 4096), None, None) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert ps(C.byref(p192), V(FAKE), None, V(FAKE + 4096), None, None) == lib.MOE_ERR_UNSUPPORTED
+    assert ps(C.byref(p), None, None, None, None, None) == lib.MOE_OK  # nothing to pack
+    a, b = lib.packed_weights_size(p)
+    assert a == 8 * 2 * 128 * 128 and b == 8 * 256 * 64  # NVFP4 bytes, two values per byte
+    with pytest.raises(lib.MoeError):
+        lib.packed_weights_size(p192)
     assert L.moe_pack_weights(C.byref(pb), V(FAKE), None, V(FAKE), None, None) == lib.MOE_ERR_INVALID_ARGUMENT
     assert L.moe_pack_weights(C.byref(lib.problem(16, 192, 8, 2, 128)), V(FAKE), None, V(FAKE + 4096),
                               None, None) == lib.MOE_ERR_UNSUPPORTED

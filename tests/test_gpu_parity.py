@@ -47,6 +47,14 @@ def _env():
 _CACHE = {}
 
 
+def case(name):
+    """Workload of a case name; a name ending in _rm keeps NVFP4 weights row-major (the other
+    NVFP4 cases are packed wherever the shape allows it)."""
+    rm = name.endswith("_rm")
+    base = name[:-3] if rm else name
+    return SMALL.get(base) or synth.WORKLOADS[base], ("row_major" if rm else "packed")
+
+
 def inputs_of(wl):
     key = (wl.name, wl.tokens, wl.x_sub)
     if key not in _CACHE:
@@ -155,16 +163,16 @@ def _routed(wl, inp):
     return r, expert_of_row
 
 
-@pytest.mark.parametrize("name", ["tiny", "small_bf16", "small_nvfp4", "ragged_bf16", "ragged_nvfp4",
-                                  "win4_nvfp4", "ragged_f32"])
+@pytest.mark.parametrize("name", ["tiny", "small_bf16", "small_nvfp4", "small_nvfp4_rm", "ragged_bf16",
+                                  "ragged_nvfp4", "win4_nvfp4", "win4_nvfp4_rm", "ragged_f32"])
 @pytest.mark.parametrize("path", ["prefill", "decode"])
 def test_gate_up_matches_oracle(name, path):
-    wl = SMALL[name]
+    wl, layout = case(name)
     inp = inputs_of(wl)
     note("gate_up %s path=%s" % (name, path))
     r, eor = _routed(wl, inp)
     ref = O.gate_up_rows(inp, wl.wdt, wl.ffn, r["sorted_token"], eor)
-    layer = MoELayer.from_workload(wl, inp, path=path)
+    layer = MoELayer.from_workload(wl, inp, path=path, nvfp4_layout=layout)
     p = layer.problem_for(wl.tokens)
     ws = layer.workspace(wl.tokens)
     A = wl.assignments
@@ -185,11 +193,11 @@ def test_gate_up_matches_oracle(name, path):
     assert torch.equal(hid, hid2)
 
 
-@pytest.mark.parametrize("name", ["tiny", "small_bf16", "small_nvfp4", "ragged_bf16", "ragged_nvfp4",
-                                  "win4_nvfp4", "ragged_f32"])
+@pytest.mark.parametrize("name", ["tiny", "small_bf16", "small_nvfp4", "small_nvfp4_rm", "ragged_bf16",
+                                  "ragged_nvfp4", "win4_nvfp4", "win4_nvfp4_rm", "ragged_f32"])
 @pytest.mark.parametrize("path", ["prefill", "decode"])
 def test_down_matches_oracle(name, path):
-    wl = SMALL[name]
+    wl, layout = case(name)
     inp = inputs_of(wl)
     note("down %s path=%s" % (name, path))
     r, eor = _routed(wl, inp)
@@ -199,7 +207,7 @@ def test_down_matches_oracle(name, path):
     if wl.act == "bf16":
         hid_host = synth.to_bf16_bits(hid_host)
     ref = O.down_rows(inp, wl.wdt, wl.hidden, act_f64(hid_host), eor)
-    layer = MoELayer.from_workload(wl, inp, path=path)
+    layer = MoELayer.from_workload(wl, inp, path=path, nvfp4_layout=layout)
     p = layer.problem_for(wl.tokens)
     ws = layer.workspace(wl.tokens)
     y_perm = layer.empty_act(A, wl.hidden)
@@ -211,12 +219,15 @@ def test_down_matches_oracle(name, path):
     assert e <= TOL
 
 
-@pytest.mark.parametrize("wdt", ["bf16", "nvfp4"])
+@pytest.mark.parametrize("wdt", ["bf16", "nvfp4", "nvfp4_packed"])
 @pytest.mark.parametrize("path", ["prefill", "decode"])
 def test_down_with_one_hot_rows_returns_exact_weights(wdt, path):
     """hid row r = unit vector at f_r: y_perm[r, h] must be W2[e][h, f_r] exactly (the 4-bit
-    value decodes exactly to bf16), which pins the weight decode and the tile index maps."""
-    E, H, F = 3, (256 if wdt == "bf16" else 192), 128
+    value decodes exactly to bf16), which pins the weight decode and the tile index maps
+    (NVFP4: row-major at H = 192, packed at H = 256)."""
+    layout = "packed" if wdt == "nvfp4_packed" else "row_major"
+    wdt = "nvfp4" if wdt == "nvfp4_packed" else wdt
+    E, H, F = 3, (192 if wdt == "nvfp4" and layout == "row_major" else 256), 128
     wl = W("onehot", 1, H, E, 1, F, "bf16", wdt, 21, "none")
     inp = synth.generate(wl)
     inp.pop("w13_gscale", None)
@@ -228,7 +239,9 @@ def test_down_with_one_hot_rows_returns_exact_weights(wdt, path):
     hid[np.arange(A), f_of_row] = 1.0
     hid_bits = synth.to_bf16_bits(hid)
     ref = O.down_rows(inp, wdt, H, act_f64(hid_bits), e_of_row)
-    layer = MoELayer(A, H, E, 1, F, "bf16", wdt, inp, path=path)
+    layer = MoELayer(A, H, E, 1, F, "bf16", wdt, inp, path=path, nvfp4_layout=layout)
+    assert layer.layout == (lib.LAYOUT_ROW_MAJOR if wdt == "nvfp4" and layout == "row_major"
+                            else lib.LAYOUT_PACKED)
     p = layer.problem_for(A)
     ws = layer.workspace(A)
     y_perm = layer.empty_act(A, H)
@@ -277,6 +290,61 @@ def test_packed_weight_layout_matches_its_definition():
     assert np.array_equal(to_host(p2).ravel(), expect(inp["w2"], 1))
 
 
+def test_packed_nvfp4_layout_matches_its_definition():
+    """The packed NVFP4 bytes and scales rebuilt independently with numpy from their definition
+    in moe.h (tiles of 256 rows in the bf16 row order; 16 bytes per row and stage, 4 scale bytes
+    per row and stage pair)."""
+    E, H, F = 2, 512, 256
+    wl = W("pack4", 1, H, E, 1, F, "bf16", "nvfp4", 72, "none")
+    inp = synth.generate(wl)
+    p = lib.problem(1, H, E, 1, F, "bf16", "nvfp4")
+    dev = {k: to_device(inp[k], "cuda") for k in ("w13", "w2", "w13_scale", "w2_scale")}
+    out = {k: torch.empty_like(v) for k, v in dev.items()}
+    note("packed NVFP4 layout")
+    lib.pack_weights(p, dev["w13"], dev["w2"], out["w13"], out["w2"])
+    lib.pack_scales(p, dev["w13_scale"], dev["w2_scale"], out["w13_scale"], out["w2_scale"])
+    torch.cuda.synchronize()
+
+    def expect(w, kind, unit):
+        rows_of_tile, ntiles = 256, (F // 128 if kind == 0 else H // 256)
+        out = []
+        for e in range(E):
+            for t in range(ntiles):
+                for st in range(w.shape[2] // unit):
+                    for r in range(rows_of_tile):
+                        if kind == 0:
+                            f = 128 * t + 64 * (r // 128) + (r % 64)
+                            row = f if r % 128 < 64 else F + f
+                        else:
+                            row = 256 * t + r
+                        out.append(w[e, row, st * unit:(st + 1) * unit])
+        return np.concatenate(out)
+
+    for key, kind, unit in (("w13", 0, 16), ("w2", 1, 16), ("w13_scale", 0, 4), ("w2_scale", 1, 4)):
+        assert np.array_equal(out[key].cpu().numpy().ravel(), expect(inp[key], kind, unit)), key
+
+
+@pytest.mark.parametrize("name", ["small_nvfp4", "win4_nvfp4"])
+def test_nvfp4_layouts_agree(name):
+    """Packed and row-major NVFP4 weights give the same layer: bit for bit on the prefill
+    kernels (same arithmetic, other addresses), within the bar on the decode kernels (another
+    order of K)."""
+    wl = SMALL[name]
+    inp = inputs_of(wl)
+    a = MoELayer.from_workload(wl, inp, nvfp4_layout="packed")
+    b = MoELayer.from_workload(wl, inp, nvfp4_layout="row_major")
+    assert a.layout == lib.LAYOUT_PACKED and b.layout == lib.LAYOUT_ROW_MAJOR
+    x = a.act_tensor(inp["x"])
+    note("NVFP4 layouts %s" % name)
+    ya = a.forward(x, path="prefill").clone()
+    yb = b.forward(x, path="prefill").clone()
+    da = a.forward(x, path="decode").clone()
+    db = b.forward(x, path="decode")
+    torch.cuda.synchronize()
+    assert torch.equal(ya, yb)
+    assert rel_err(act_f64(to_host(da)), act_f64(to_host(db))) <= TOL
+
+
 # ---------------------------------------------------------------------------------------
 # combine
 # ---------------------------------------------------------------------------------------
@@ -322,15 +390,15 @@ def _check_forward(wl, inp, layer, tokens=None, path=None):
 
 
 FWD_CASES = ["tiny", "small_bf16", "small_nvfp4", "ragged_bf16", "ragged_nvfp4", "win4_nvfp4",
-             "ragged_f32", "decode1", "decode8", "nvfp4_decode"]
+             "win4_nvfp4_rm", "ragged_f32", "decode1", "decode8", "nvfp4_decode", "nvfp4_decode_rm"]
 
 
 @pytest.mark.parametrize("name", FWD_CASES)
 def test_forward_matches_oracle(name):
-    wl = SMALL.get(name) or synth.WORKLOADS[name]
+    wl, layout = case(name)
     inp = inputs_of(wl)
     note("forward %s" % name)
-    layer = MoELayer.from_workload(wl, inp)
+    layer = MoELayer.from_workload(wl, inp, nvfp4_layout=layout)
     _check_forward(wl, inp, layer)
 
 
@@ -509,10 +577,12 @@ def test_non_finite_inputs_stay_memory_safe_and_route_validly():
         assert np.isfinite(act_f64(to_host(y))[good]).all()
 
 
-@pytest.mark.parametrize("name,T", [("decode1", 1), ("decode8", 8), ("nvfp4_decode", 3), ("small_bf16", 5)])
+@pytest.mark.parametrize("name,T", [("decode1", 1), ("decode8", 8), ("nvfp4_decode", 3), ("small_bf16", 5),
+                                    ("nvfp4_decode", 16), ("decode8", 17)])
 def test_small_batch_forward_equals_its_stages(name, T):
-    """moe_forward on batches of up to 8 tokens (single-block selection and dispatch) must equal
-    route -> permute -> two grouped GEMMs -> combine through the stage entry points, bit for bit."""
+    """moe_forward on batches of up to 16 tokens (single-block selection and dispatch) must equal
+    route -> permute -> two grouped GEMMs -> combine through the stage entry points, bit for bit
+    (T = 17: the first batch size past the single-block path)."""
     base = SMALL.get(name) or synth.WORKLOADS[name]
     wl = base.with_tokens(T, x_sub=100 + T)
     inp = inputs_of(wl)
