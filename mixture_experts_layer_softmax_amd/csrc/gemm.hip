@@ -647,11 +647,8 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_prefill_nvfp4_kernel(GemmArgs
 // and are added in a fixed order (deterministic).
 // ---------------------------------------------------------------------------------------
 
-// NVL (NVFP4 only): 0 row-major bytes, 128-wide K blocks; 1 row-major, 512-wide windows;
-// 2 PACKED bytes and scales (the 128-wide block mapping, read from [tile][stage] blocks).
-template <int KIND, int WFMT, int SPLITK, int NVL = 0>
+template <int KIND, int WFMT, int SPLITK, bool WIN4 = false>
 __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
-    constexpr bool WIN4 = NVL == 1;
     constexpr int CG = 4 / SPLITK;              // column groups per block
     constexpr int NB = (KIND == kGateUp) ? 2 : 1;  // weight row sets per column group
     __shared__ f32x4_t red[4][NB][64];
@@ -725,27 +722,6 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
     const uint8_t* pq1 = static_cast<const uint8_t*>(g.w) + w1 * (K / 2) + (WIN4 ? 64 : 16) * q;
     const uint8_t* ps0 = g.wscale + w0 * (K / 16) + (WIN4 ? 8 : 2) * q;
     const uint8_t* ps1 = g.wscale + w1 * (K / 16) + (WIN4 ? 8 : 2) * q;
-    int ssh = 0;  // NVL 2: bit offset of this lane's stage in its stage-pair scale word
-    if constexpr (WFMT == kWNVFP4 && NVL == 2) {
-        // lane q of K block j takes stage 4 j + q: bytes at 16 r of the stage's 4 KiB block,
-        // scales in the word at 4 r of stage pair 2 j + q / 2 (1 KiB blocks), half q & 1
-        const int nst = K / 32;
-        int t, r_a;
-        if (KIND == kGateUp) {
-            t = col >> 7;
-            r_a = ((col >> 6) & 1) * 128 + (col & 63);  // gate tile row; the up row is 64 below
-        } else {
-            t = wrow0 >> 8;
-            r_a = wrow0 & 255;
-        }
-        const int ntiles = (KIND == kGateUp) ? g.F / 128 : g.N / 256;
-        const size_t tb = size_t(e) * ntiles + t;
-        pq0 = static_cast<const uint8_t*>(g.w) + tb * nst * 4096 + (q * 256 + r_a) * 16;
-        pq1 = pq0 + 64 * 16;
-        ps0 = g.wscale + tb * (nst / 2) * 1024 + ((q >> 1) * 256 + r_a) * 4;
-        ps1 = ps0 + 64 * 4;
-        ssh = (q & 1) * 16;
-    }
     auto load = [&](Blk& b, int j) __attribute__((always_inline)) {
         const int k = 128 * j;
         if constexpr (WFMT == kWBF16) {
@@ -769,20 +745,11 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
             b.a1 = ld16(pa + k + 8);
             b.a2 = ld16(pa + k + 16);
             b.a3 = ld16(pa + k + 24);
-            if constexpr (NVL == 2) {  // e4m3_value reads only the low 8 bits of its argument
-                b.pg = ld16(pq0 + 16384 * j);
-                b.sg = *reinterpret_cast<const uint32_t*>(ps0 + 2048 * j) >> ssh;
-                if constexpr (KIND == kGateUp) {
-                    b.pu = ld16(pq1 + 16384 * j);
-                    b.su = *reinterpret_cast<const uint32_t*>(ps1 + 2048 * j) >> ssh;
-                }
-            } else {
-                b.pg = ld16(pq0 + 64 * j);
-                b.sg = *reinterpret_cast<const uint16_t*>(ps0 + 8 * j);
-                if constexpr (KIND == kGateUp) {
-                    b.pu = ld16(pq1 + 64 * j);
-                    b.su = *reinterpret_cast<const uint16_t*>(ps1 + 8 * j);
-                }
+            b.pg = ld16(pq0 + 64 * j);
+            b.sg = *reinterpret_cast<const uint16_t*>(ps0 + 8 * j);
+            if constexpr (KIND == kGateUp) {
+                b.pu = ld16(pq1 + 64 * j);
+                b.su = *reinterpret_cast<const uint16_t*>(ps1 + 8 * j);
             }
         }
     };
@@ -912,6 +879,136 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs g) {
             out[size_t(row) * g.F + col] = (uint16_t)bf16_rne(silu_mul(acc0[i] * gs, acc1[i] * gs));
         } else if (col < g.N) {
             out[size_t(row) * g.N + col] = (uint16_t)bf16_rne(acc0[i] * gs);
+        }
+    }
+}
+
+// Decode kernel for PACKED NVFP4 weights.  Lane (n, q) of a wavefront owns weight row n of
+// each of the wavefront's NCG consecutive 16-row groups (gate/up: the gate rows and the matching
+// up rows) and K-group q: in 128-wide K block j it takes stage 4 j + q of those rows (16 bytes
+// at 16 r of the stage's 4 KiB block of the tile) and the scale word at 4 r of stage pair
+// 2 j + q / 2 (half q & 1).  A row group c lies 16 c rows below the first in the same tile, so
+// one base address serves all of them.  The activation fragments of a block are loaded once
+// and feed the MFMAs of every group: activation bytes per weight byte fall by NCG, which
+// relieves the L1-to-register return path that the 4-bit weights otherwise share with
+// activations four times their size.  Two K blocks in flight; SPLITK wavefronts split K and
+// meet in LDS in a fixed order.
+template <int KIND, int SPLITK, int NCG>
+__global__ __launch_bounds__(256) void gemm_decode_nvfp4p_kernel(GemmArgs g) {
+    static_assert(NCG == 1 || NCG == 2 || NCG == 4, "row groups must stay inside a 64-row half");
+    constexpr int WPB = 4 / SPLITK;                 // group sets per block
+    constexpr int NB = (KIND == kGateUp) ? 2 : 1;   // gate and up rows, or down rows
+    __shared__ f32x4_t red[SPLITK > 1 ? 4 : 1][NB * NCG][64];
+
+    const int ncg = (KIND == kGateUp) ? g.F / 16 : g.N / 16;  // F % 128 == 0, N % 256 == 0
+    const int per_tile = (ncg + WPB * NCG - 1) / (WPB * NCG);
+    const int item = blockIdx.x;
+    if (item >= *g.tile_count * per_tile) return;
+    const Tile tile = g.tiles[item / per_tile];
+    const int e = tile.expert, r0 = tile.row0, r1 = tile.row1;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int cgw = ((item % per_tile) * WPB + wave / SPLITK) * NCG;  // first group, NCG-aligned
+    const int kp = wave % SPLITK;
+    const bool live = cgw < ncg;  // uniform per wavefront; ncg % NCG == 0, so all NCG groups exist
+    const int K = g.K, nst = K / 32;
+    const int n = lane & 15, q = lane >> 4;
+
+    const int rr = min(r0 + n, r1 - 1);
+    int src = g.a_rows ? g.a_rows[rr] : rr;
+    src = src < 0 ? 0 : (src >= g.a_rows_limit ? g.a_rows_limit - 1 : src);
+    const uint16_t* pa = static_cast<const uint16_t*>(g.a) + size_t(src) * K + 32 * q;
+    const int col = min(cgw, ncg - NCG) * 16 + n;  // column of group 0 (clamped for idle waves)
+    int t, r_a;
+    if (KIND == kGateUp) {
+        t = col >> 7;
+        r_a = ((col >> 6) & 1) * 128 + (col & 63);  // gate tile row; the up row is 64 below
+    } else {
+        t = col >> 8;
+        r_a = col & 255;
+    }
+    const size_t tb = size_t(e) * ((KIND == kGateUp) ? g.F / 128 : g.N / 256) + t;
+    const uint8_t* pq = static_cast<const uint8_t*>(g.w) + tb * nst * 4096 + (q * 256 + r_a) * 16;
+    const uint8_t* ps = g.wscale + tb * (nst / 2) * 1024 + ((q >> 1) * 256 + r_a) * 4;
+    const int ssh = (q & 1) * 16;
+
+    f32x4_t acc[NB * NCG];
+#pragma unroll
+    for (int i = 0; i < NB * NCG; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int nblk = K / 128 / SPLITK;
+    const int j0 = kp * nblk, jend = j0 + nblk;
+
+    struct Blk {
+        uint4 a[4];             // activations, MFMA i = 0..3
+        uint4 p[NB * NCG];      // bytes: group c gate (or down) at c, up at NCG + c
+        uint32_t sc[NB * NCG];  // scale words shifted to this lane's stage
+    };
+    auto ld16 = [](const void* p) __attribute__((always_inline)) { return *reinterpret_cast<const uint4*>(p); };
+    auto load = [&](Blk& b, int j) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) b.a[i] = ld16(pa + 128 * j + 8 * i);
+#pragma unroll
+        for (int h = 0; h < NB; ++h)
+#pragma unroll
+            for (int c = 0; c < NCG; ++c) {
+                b.p[h * NCG + c] = ld16(pq + 16384 * j + h * 1024 + c * 256);
+                b.sc[h * NCG + c] = *reinterpret_cast<const uint32_t*>(ps + 2048 * j + h * 256 + c * 64) >> ssh;
+            }
+    };
+    auto mma = [&](f32x4_t& a, const uint4& x, const uint4& w) __attribute__((always_inline)) {
+        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, x), __builtin_bit_cast(bf16x8_t, w), a, 0, 0, 0);
+    };
+    auto compute = [&](const Blk& b) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < NB * NCG; ++i) {  // e4m3_value reads only the low 8 bits
+            const float fa = e4m3_value(b.sc[i]), fb = e4m3_value(b.sc[i] >> 8);
+            mma(acc[i], b.a[0], dequant8(b.p[i].x, fa));
+            mma(acc[i], b.a[1], dequant8(b.p[i].y, fa));
+            mma(acc[i], b.a[2], dequant8(b.p[i].z, fb));
+            mma(acc[i], b.a[3], dequant8(b.p[i].w, fb));
+        }
+    };
+    if (live && nblk > 0) {
+        Blk x0, x1;
+        load(x0, j0);
+        load(x1, min(j0 + 1, jend - 1));  // past the end: a harmless re-read of the last block
+        for (int j = j0;; j += 2) {
+            compute(x0);
+            if (j + 1 >= jend) break;
+            load(x0, min(j + 2, jend - 1));
+            compute(x1);
+            if (j + 2 >= jend) break;
+            load(x1, min(j + 3, jend - 1));
+        }
+    }
+
+    if constexpr (SPLITK > 1) {
+#pragma unroll
+        for (int i = 0; i < NB * NCG; ++i) red[wave][i][lane] = acc[i];
+        __syncthreads();
+        if (kp != 0) return;
+#pragma unroll
+        for (int i = 0; i < NB * NCG; ++i) {
+            acc[i] = red[wave][i][lane];
+#pragma unroll
+            for (int p = 1; p < SPLITK; ++p) acc[i] += red[wave + p][i][lane];
+        }
+    }
+    if (!live) return;
+
+    const float gs = g.gscale ? g.gscale[e] : 1.0f;
+    uint16_t* out = static_cast<uint16_t*>(g.out);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = r0 + 4 * q + i;
+        if (row >= r1) continue;
+#pragma unroll
+        for (int c = 0; c < NCG; ++c) {
+            const int cc = col + 16 * c;
+            if (KIND == kGateUp)
+                out[size_t(row) * g.F + cc] = (uint16_t)bf16_rne(silu_mul(acc[c][i] * gs, acc[NCG + c][i] * gs));
+            else
+                out[size_t(row) * g.N + cc] = (uint16_t)bf16_rne(acc[c][i] * gs);
         }
     }
 }
@@ -1047,6 +1144,20 @@ hipError_t launch_gemm(const GemmArgs& g, int family, int max_tiles, hipStream_t
     } else if (family == kFamPrefill) {
         if (g.wpacked) return hipErrorInvalidValue;  // PACKED NVFP4 needs F % 128 == 0
         launch_mfma<PF_BM, PF_BN, PF_WM, PF_WN>(g, max_tiles, s);
+    } else if (g.wpacked) {  // PACKED NVFP4 decode: NCG row groups per wavefront
+        // measured on the NVFP4 decode shape (T=16, H4096, F2048): the down GEMM (activations
+        // four times the weight bytes at NCG = 1) is 20 % faster with NCG = 2 than with 1 and
+        // faster than with 4; gate/up (activations twice the weight bytes) is fastest with 1
+        constexpr int NCG_UP = 1, NCG_DOWN = 2;
+        const int ncg = up ? g.F / 16 / NCG_UP : g.N / 16 / NCG_DOWN;  // wavefront group sets
+        int split = 1;
+        while (split < 4 && long(max_tiles) * ncg * split < 4096 && g.K % (128 * split * 2) == 0) split *= 2;
+        const int wpb = 4 / split;
+        dim3 grid(max_tiles * ((ncg + wpb - 1) / wpb)), block(256);
+#define MOE_DECP(KD, SK, NC) hipLaunchKernelGGL((gemm_decode_nvfp4p_kernel<KD, SK, NC>), grid, block, 0, s, g)
+        if (up) { if (split == 1) MOE_DECP(kGateUp, 1, NCG_UP); else if (split == 2) MOE_DECP(kGateUp, 2, NCG_UP); else MOE_DECP(kGateUp, 4, NCG_UP); }
+        else    { if (split == 1) MOE_DECP(kDown, 1, NCG_DOWN);   else if (split == 2) MOE_DECP(kDown, 2, NCG_DOWN);   else MOE_DECP(kDown, 4, NCG_DOWN); }
+#undef MOE_DECP
     } else if (g.K % 128 == 0) {
         // split K until there are about 4 wavefronts per SIMD (4096) for the worst-case tile count
         const int ncg = up ? g.F / 16 : (g.N + 15) / 16;
@@ -1058,13 +1169,8 @@ hipError_t launch_gemm(const GemmArgs& g, int family, int max_tiles, hipStream_t
         if (g.wfmt == kWBF16) {
             if (up) { if (split == 1) MOE_DEC(kGateUp, kWBF16, 1); else if (split == 2) MOE_DEC(kGateUp, kWBF16, 2); else MOE_DEC(kGateUp, kWBF16, 4); }
             else    { if (split == 1) MOE_DEC(kDown, kWBF16, 1);   else if (split == 2) MOE_DEC(kDown, kWBF16, 2);   else MOE_DEC(kDown, kWBF16, 4); }
-        } else if (g.wpacked) {
-#define MOE_DECP(KD, SK) hipLaunchKernelGGL((gemm_decode_kernel<KD, kWNVFP4, SK, 2>), grid, block, 0, s, g)
-            if (up) { if (split == 1) MOE_DECP(kGateUp, 1); else if (split == 2) MOE_DECP(kGateUp, 2); else MOE_DECP(kGateUp, 4); }
-            else    { if (split == 1) MOE_DECP(kDown, 1);   else if (split == 2) MOE_DECP(kDown, 2);   else MOE_DECP(kDown, 4); }
-#undef MOE_DECP
         } else if ((g.K / 128 / split) % 4 == 0) {  // 512-wide scale windows
-#define MOE_DEC4(KD, SK) hipLaunchKernelGGL((gemm_decode_kernel<KD, kWNVFP4, SK, 1>), grid, block, 0, s, g)
+#define MOE_DEC4(KD, SK) hipLaunchKernelGGL((gemm_decode_kernel<KD, kWNVFP4, SK, true>), grid, block, 0, s, g)
             if (up) { if (split == 1) MOE_DEC4(kGateUp, 1); else if (split == 2) MOE_DEC4(kGateUp, 2); else MOE_DEC4(kGateUp, 4); }
             else    { if (split == 1) MOE_DEC4(kDown, 1);   else if (split == 2) MOE_DEC4(kDown, 2);   else MOE_DEC4(kDown, 4); }
 #undef MOE_DEC4
