@@ -49,7 +49,6 @@ bool is_mx(const moe_problem& p) { return p.w_dtype == MOE_MXFP8 || p.w_dtype ==
 
 int family_of(const moe_problem& p) {
     if (p.act_dtype == MOE_F32) return kFamSimtF32;
-    if (is_mx(p)) return kFamPrefill;  // one MX kernel family (256-row tiles)
     int path = p.path;
     if (path == MOE_PATH_AUTO) {
         const long A = long(p.num_tokens) * p.top_k;

@@ -1094,6 +1094,7 @@ constexpr int DC_BM = 16, DC_BN = 64, DC_WM = 1, DC_WN = 2;
 int gemm_tile_rows(int family, int wfmt, int ffn) {
     if (family == kFamSimtF32) return 64;
     if (family == kFamPrefill) return (wfmt == kWBF16 || ffn % 128 == 0) ? 256 : PF_BM;
+    if (wfmt == kWMXFP8 || wfmt == kWMXFP4) return 32;  // the MX decode kernel's 32 x 32 MFMA tiles
     return DC_BM;
 }
 
@@ -1116,7 +1117,7 @@ static dim3 prefill_grid(const GemmArgs& g, int max_tiles, int bn) {
 
 hipError_t launch_gemm(const GemmArgs& g, int family, int max_tiles, hipStream_t s) {
     if (max_tiles <= 0) return hipSuccess;
-    if (g.wfmt == kWMXFP8 || g.wfmt == kWMXFP4) return launch_gemm_mxfp8(g, max_tiles, s);  // mx.hip
+    if (g.wfmt == kWMXFP8 || g.wfmt == kWMXFP4) return launch_gemm_mxfp8(g, family, max_tiles, s);  // mx.hip
     const bool up = g.kind == kGateUp;
     if (family == kFamSimtF32) {
         const int ncols = up ? g.F / 32 : (g.N + 63) / 64;

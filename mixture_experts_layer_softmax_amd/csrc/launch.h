@@ -70,10 +70,10 @@ hipError_t launch_fill_i32(int32_t* p, int n, int value, hipStream_t s);
 hipError_t launch_tiles_from_offsets(const int32_t* offsets, int E, int eb, int ee, int A, int bm, Tile* tiles,
                                      int* tile_count, int cap, hipStream_t s);
 // MXFP8 (mx.hip): bf16 rows [rows, K] -> E4M3 codes [rows, K] + E8M0 scales [rows, K/32];
-// the grouped GEMM on block-scaled fp8 MFMA (256-row tiles).
+// the grouped GEMM on block-scaled fp8 MFMA (prefill: 256-row tiles; decode: 32-row tiles).
 hipError_t launch_mx_quantize(const void* in, long rows, int K, uint8_t* codes, uint8_t* scales,
                               hipStream_t s);
-hipError_t launch_gemm_mxfp8(const GemmArgs& g, int max_tiles, hipStream_t s);
+hipError_t launch_gemm_mxfp8(const GemmArgs& g, int family, int max_tiles, hipStream_t s);
 hipError_t launch_gather_rows(const void* x, const int32_t* sorted_token, void* x_perm, int A,
                               int T, int row_bytes, hipStream_t s);
 hipError_t launch_gemm(const GemmArgs& g, int family, int max_tiles, hipStream_t s);

@@ -316,10 +316,204 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_mxfp8_kernel(GemmArgs g) 
     }
 }
 
-// Blocks: (row tile, column tile) pairs, a multiple of 8 so that every XCD walks the same number.
-// MXFP8 weights (kWMXFP8) and MXFP4 weights (kWMXFP4), both with MXFP8 activations.
-hipError_t launch_gemm_mxfp8(const GemmArgs& g, int max_tiles, hipStream_t s) {
+// ---------------------------------------------------------------------------------------
+// MX decode kernel: few rows per expert (row tiles of 32), so the layer streams the selected
+// experts' weights once, from the packed layout straight into MFMA operand registers (no
+// LDS).  Lane l = 32 g + n of a wavefront feeds operand row n (token row n of the tile for the
+// activations, weight row n of a 32-row group for the weights) and K half g of the
+// v_mfma_scale_f32_32x32x64_f8f6f4 layout above: per 64-wide stage an fp8 operand takes chunks
+// g and g + 2 of its row's four 16-byte chunks, an fp4 operand chunk g of its two, and the
+// lane supplies the E8M0 scale of block 2 s + g.  Scales are loaded 16 bytes (8 stages) per
+// row at a time, one chunk ahead.  A wavefront owns two 32-row weight groups that share the
+// activation fragments: gate/up, the gate and up rows of 32 hid columns (SwiGLU in
+// registers); down, 64 output columns.  Two stages in flight; SPLITK wavefronts of a block
+// split the stages and meet in LDS in a fixed order.
+// ---------------------------------------------------------------------------------------
+
+template <int KIND, int BF4, int SPLITK>
+__global__ __launch_bounds__(256) void gemm_decode_mx_kernel(GemmArgs g) {
+    constexpr int NG = 2;                       // weight row groups per wavefront
+    constexpr int WPB = 4 / SPLITK;             // group pairs per block
+    constexpr int BCH = BF4 ? 2 : 4;            // 16-byte chunks per weight row and stage
+    constexpr size_t SBLK = size_t(256) * BCH * 16;  // bytes of one (tile, stage) block
+    __shared__ f32x16_t red[SPLITK > 1 ? 4 : 1][NG][64];
+
+    const int nsets = (KIND == kGateUp) ? g.F / 32 : g.N / 64;
+    const int per_tile = (nsets + WPB - 1) / WPB;
+    const int item = blockIdx.x;
+    if (item >= *g.tile_count * per_tile) return;
+    const Tile tile = g.tiles[item / per_tile];
+    const int e = tile.expert, r0 = tile.row0, r1 = tile.row1;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int set = (item % per_tile) * WPB + wave / SPLITK;
+    const int kp = wave % SPLITK;
+    const bool live = set < nsets;  // uniform per wavefront
+    const int K = g.K, nst = K / 64;
+    const int n = lane & 31, g2 = lane >> 5;
+
+    const int rr = min(r0 + n, r1 - 1);
+    int src = g.a_rows ? g.a_rows[rr] : rr;
+    src = src < 0 ? 0 : (src >= g.a_rows_limit ? g.a_rows_limit - 1 : src);
+    const uint8_t* pa = static_cast<const uint8_t*>(g.a) + size_t(src) * K + 16 * g2;
+    const uint8_t* psa = g.ascale + size_t(src) * (K / 32);
+
+    // the wavefront's weight rows: tile t, tile rows trow[h], weight rows wrow[h]
+    const int sc = min(set, nsets - 1);  // idle wavefronts stay in bounds
+    const int c0 = sc * (KIND == kGateUp ? 32 : 64);
+    int t, trow[NG], wrow[NG];
+    if (KIND == kGateUp) {
+        t = c0 >> 7;
+        trow[0] = ((c0 >> 6) & 1) * 128 + (c0 & 63) + n;  // gate row; the up row is 64 below
+        trow[1] = trow[0] + 64;
+        wrow[0] = c0 + n;
+        wrow[1] = g.F + c0 + n;
+    } else {
+        t = c0 >> 8;
+        trow[0] = (c0 & 255) + n;
+        trow[1] = trow[0] + 32;
+        wrow[0] = c0 + n;
+        wrow[1] = c0 + 32 + n;
+    }
+    const int ntiles = (KIND == kGateUp) ? g.F / 128 : g.N / 256;
+    const int Nw = (KIND == kGateUp) ? 2 * g.F : g.N;
+    const uint8_t* wt = static_cast<const uint8_t*>(g.w) + (size_t(e) * ntiles + t) * nst * SBLK;
+    int off0[NG], off1[NG];
+    const uint8_t* psw[NG];
+#pragma unroll
+    for (int h = 0; h < NG; ++h) {
+        const int r = trow[h];
+        if (BF4) {
+            off0[h] = r * 32 + ((g2 ^ ((r >> 2) & 1)) * 16);
+            off1[h] = 0;
+        } else {
+            off0[h] = r * 64 + ((g2 ^ ((r >> 1) & 3)) * 16);
+            off1[h] = r * 64 + (((g2 + 2) ^ ((r >> 1) & 3)) * 16);
+        }
+        psw[h] = g.wscale + (size_t(e) * Nw + wrow[h]) * (K / 32);
+    }
+
+    f32x16_t acc[NG];
+#pragma unroll
+    for (int h = 0; h < NG; ++h)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[h][i] = 0.0f;
+    const int per = nst / SPLITK;  // a multiple of 8 (launcher)
+    const int s0 = kp * per, s1 = s0 + per;
+
+    typedef __attribute__((ext_vector_type(4))) int i32x4_t;
+    auto ld16 = [](const void* p) __attribute__((always_inline)) {
+        return __builtin_bit_cast(i32x4_t, *reinterpret_cast<const uint4*>(p));
+    };
+    struct Stg {
+        i32x8_t a;
+        i32x4_t b0[NG], b1[NG];
+    };
+    struct Scl {
+        uint4 a, w[NG];
+    };
+    auto load = [&](Stg& x, int st) __attribute__((always_inline)) {
+        const i32x4_t lo = ld16(pa + 64 * st), hi = ld16(pa + 64 * st + 32);
+        x.a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        const uint8_t* blk = wt + size_t(st) * SBLK;
+#pragma unroll
+        for (int h = 0; h < NG; ++h) {
+            x.b0[h] = ld16(blk + off0[h]);
+            if (!BF4) x.b1[h] = ld16(blk + off1[h]);
+        }
+    };
+    auto sload = [&](Scl& c, int chunk) __attribute__((always_inline)) {
+        c.a = *reinterpret_cast<const uint4*>(psa + 16 * chunk);
+#pragma unroll
+        for (int h = 0; h < NG; ++h) c.w[h] = *reinterpret_cast<const uint4*>(psw[h] + 16 * chunk);
+    };
+    auto byte_of = [](const uint4& v, int i) __attribute__((always_inline)) {
+        const uint32_t w = (i >> 2) == 0 ? v.x : (i >> 2) == 1 ? v.y : (i >> 2) == 2 ? v.z : v.w;
+        return int((w >> ((i & 3) * 8)) & 0xffu);
+    };
+    auto compute = [&](const Stg& x, const Scl& c, int st) __attribute__((always_inline)) {
+        const int bi = (st & 7) * 2 + g2;
+        const int as = byte_of(c.a, bi);
+#pragma unroll
+        for (int h = 0; h < NG; ++h) {
+            const i32x4_t z = {0, 0, 0, 0};
+            const i32x8_t b = __builtin_shufflevector(x.b0[h], BF4 ? z : x.b1[h], 0, 1, 2, 3, 4, 5, 6, 7);
+            acc[h] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x.a, b, acc[h], 0, BF4 ? 4 : 0, 0, as,
+                                                                     0, byte_of(c.w[h], bi));
+        }
+    };
+    if (live && per > 0) {
+        const int clast = (s1 - 1) >> 3;
+        Stg x0, x1;
+        Scl cur, nxt;
+        sload(cur, s0 >> 3);
+        sload(nxt, min((s0 >> 3) + 1, clast));
+        load(x0, s0);
+        load(x1, min(s0 + 1, s1 - 1));  // past the end: a harmless re-read of the last stage
+        for (int st = s0;; st += 2) {   // chunk boundaries (st % 8 == 0) fall on even stages
+            if ((st & 7) == 0 && st != s0) {
+                cur = nxt;
+                sload(nxt, min((st >> 3) + 1, clast));
+            }
+            compute(x0, cur, st);
+            if (st + 1 >= s1) break;
+            load(x0, min(st + 2, s1 - 1));
+            compute(x1, cur, st + 1);
+            if (st + 2 >= s1) break;
+            load(x1, min(st + 3, s1 - 1));
+        }
+    }
+
+    if constexpr (SPLITK > 1) {
+#pragma unroll
+        for (int h = 0; h < NG; ++h) red[wave][h][lane] = acc[h];
+        __syncthreads();
+        if (kp != 0) return;
+#pragma unroll
+        for (int h = 0; h < NG; ++h) {
+            acc[h] = red[wave][h][lane];
+#pragma unroll
+            for (int p = 1; p < SPLITK; ++p) acc[h] += red[wave + p][h][lane];
+        }
+    }
+    if (!live) return;
+
+    uint16_t* out = static_cast<uint16_t*>(g.out);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int row = r0 + 8 * (i / 4) + 4 * g2 + (i % 4);
+        if (row >= r1) continue;
+        if (KIND == kGateUp) {
+            out[size_t(row) * g.F + c0 + n] = (uint16_t)bf16_rne(silu_mul(acc[0][i], acc[1][i]));
+        } else {
+#pragma unroll
+            for (int h = 0; h < NG; ++h) out[size_t(row) * g.N + c0 + 32 * h + n] = (uint16_t)bf16_rne(acc[h][i]);
+        }
+    }
+}
+
+// Prefill blocks: (row tile, column tile) pairs, a multiple of 8 so that every XCD walks the
+// same number.  Decode blocks: (row tile, group pairs of four wavefronts), K split until there are
+// about 4 wavefronts per SIMD for the worst-case tile count.  MXFP8 weights (kWMXFP8) and MXFP4
+// weights (kWMXFP4), both with MXFP8 activations.
+hipError_t launch_gemm_mxfp8(const GemmArgs& g, int family, int max_tiles, hipStream_t s) {
     if (max_tiles <= 0) return hipSuccess;
+    if (family == kFamDecode) {
+        const bool up = g.kind == kGateUp, f4 = g.wfmt == kWMXFP4;
+        const int nsets = up ? g.F / 32 : g.N / 64, nst = g.K / 64;  // K % 512 == 0
+        int split = 1;
+        while (split < 4 && long(max_tiles) * nsets * split < 4096 && nst % (8 * split * 2) == 0) split *= 2;
+        const int wpb = 4 / split;
+        const dim3 grid(max_tiles * ((nsets + wpb - 1) / wpb)), block(256);
+#define MOE_MXD(KD, F4, SK) hipLaunchKernelGGL((gemm_decode_mx_kernel<KD, F4, SK>), grid, block, 0, s, g)
+#define MOE_MXD_SPLIT(KD, F4) \
+    do { if (split == 1) MOE_MXD(KD, F4, 1); else if (split == 2) MOE_MXD(KD, F4, 2); else MOE_MXD(KD, F4, 4); } while (0)
+        if (up) { if (f4) MOE_MXD_SPLIT(kGateUp, 1); else MOE_MXD_SPLIT(kGateUp, 0); }
+        else    { if (f4) MOE_MXD_SPLIT(kDown, 1);   else MOE_MXD_SPLIT(kDown, 0); }
+#undef MOE_MXD_SPLIT
+#undef MOE_MXD
+        return hipGetLastError();
+    }
     const int ncols = g.kind == kGateUp ? g.F / 128 : (g.N + 255) / 256;
     const dim3 grid(((max_tiles * ncols + 7) / 8) * 8);
     const bool f4 = g.wfmt == kWMXFP4;

@@ -25,6 +25,8 @@ for _wdt in ("mxfp8", "mxfp4"):
         "small_" + _wdt: W("small_" + _wdt, 384, 512, 16, 4, 512, "bf16", _wdt, 17, "normal"),
         "ragged_" + _wdt: W("ragged_" + _wdt, 77, 1024, 5, 3, 1536, "bf16", _wdt, 18, "normal"),
         "one_token_" + _wdt: W("one_token_" + _wdt, 1, 512, 8, 2, 512, "bf16", _wdt, 19, "none"),
+        # K = 2048 on both GEMMs and few rows: the decode kernel splits K over 4 wavefronts
+        "split_" + _wdt: W("split_" + _wdt, 4, 2048, 8, 2, 2048, "bf16", _wdt, 20, "normal"),
     })
 
 
@@ -81,20 +83,22 @@ def _check_forward(wl, inp, layer, tokens=None):
     assert e <= TOL
 
 
+@pytest.mark.parametrize("path", ["prefill", "decode"])
 @pytest.mark.parametrize("name", sorted(SMALL))
-def test_forward_matches_oracle(name):
+def test_forward_matches_oracle(name, path):
     wl = SMALL[name]
     inp = synth.generate(wl)
-    note("MX forward %s" % name)
-    _check_forward(wl, inp, MoELayer.from_workload(wl, inp))
+    note("MX forward %s path=%s" % (name, path))
+    _check_forward(wl, inp, MoELayer.from_workload(wl, inp, path=path))
 
 
+@pytest.mark.parametrize("path", ["prefill", "decode"])
 @pytest.mark.parametrize("wdt", ["mxfp8", "mxfp4"])
 @pytest.mark.parametrize("kind", [lib.GATE_UP_SWIGLU, lib.DOWN])
-def test_grouped_gemm_matches_oracle(kind, wdt):
+def test_grouped_gemm_matches_oracle(kind, wdt, path):
     wl = SMALL["small_" + wdt]
     inp = synth.generate(wl)
-    layer = MoELayer.from_workload(wl, inp)
+    layer = MoELayer.from_workload(wl, inp, path=path)
     r = O.route(inp, wl.top_k)
     A = wl.assignments
     expert_of_row = np.searchsorted(r["offsets"], np.arange(A), side="right") - 1
@@ -118,12 +122,13 @@ def test_grouped_gemm_matches_oracle(kind, wdt):
     assert e <= TOL
 
 
+@pytest.mark.parametrize("path", ["prefill", "decode"])
 @pytest.mark.parametrize("wdt", ["mxfp8", "mxfp4"])
-def test_expert_parallel_share(wdt):
+def test_expert_parallel_share(wdt, path):
     wl = SMALL["small_" + wdt]
     b, n = 4, 8
     inp = synth.generate(wl, experts=range(b, b + n))
-    layer = MoELayer.from_workload(wl, inp, expert_begin=b, local_experts=n)
+    layer = MoELayer.from_workload(wl, inp, path=path, expert_begin=b, local_experts=n)
     x = layer.act_tensor(inp["x"])
     y, dbg = layer.forward(x, debug=True)
     torch.cuda.synchronize()
@@ -132,6 +137,35 @@ def test_expert_parallel_share(wdt):
     e = rel_err(bf16_bits_to_f64(to_host(y)), ref["y"])
     note("  %s share [%d, %d): y rel err %.3e" % (wdt, b, b + n, e))
     assert e <= TOL
+
+
+@pytest.mark.parametrize("wdt", ["mxfp8", "mxfp4"])
+@pytest.mark.parametrize("path", ["prefill", "decode"])
+def test_down_with_one_hot_rows_returns_exact_weights(wdt, path):
+    """hid row r = unit vector at f_r: its MXFP8 form is exact (scale 2^-8, code 256), so
+    y_perm[r, h] must equal the decoded weight W2[e][h, f_r] exactly (an E4M3 or E2M1 value
+    times a power of two, exact in bf16); this pins the weight layout, the chunk slots and the
+    scale bytes of both MX kernels."""
+    E, H, F = 3, 512, 512
+    wl = W("onehot_" + wdt, 1, H, E, 1, F, "bf16", wdt, 23, "none")
+    inp = synth.generate(wl)
+    A = E * F
+    f_of_row = np.tile(np.arange(F), E)
+    e_of_row = np.repeat(np.arange(E), F).astype(np.int32)
+    hid = np.zeros((A, F), np.float32)
+    hid[np.arange(A), f_of_row] = 1.0
+    hid_bits = synth.to_bf16_bits(hid)
+    ref = O.down_rows(inp, wdt, H, bf16_bits_to_f64(hid_bits), e_of_row)
+    layer = MoELayer(A, H, E, 1, F, "bf16", wdt, inp, path=path)
+    p = layer.problem_for(A)
+    ws = layer.workspace(A)
+    y_perm = layer.empty_act(A, H)
+    offsets = np.arange(E + 1, dtype=np.int32) * F
+    note("MX one-hot down wdt=%s path=%s" % (wdt, path))
+    lib.grouped_gemm(p, lib.DOWN, to_device(hid_bits, "cuda"), None, torch.from_numpy(offsets).cuda(),
+                     layer.weights, y_perm, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_bits_to_f64(to_host(y_perm)), ref)
 
 
 @pytest.mark.parametrize("name", ["mxfp8_prefill", "mxfp4_prefill", "mxfp8_decode64", "mxfp4_decode64"])
