@@ -427,40 +427,46 @@ __global__ __launch_bounds__(256) void gemm_decode_mx_kernel(GemmArgs g) {
 #pragma unroll
         for (int h = 0; h < NG; ++h) c.w[h] = *reinterpret_cast<const uint4*>(psw[h] + 16 * chunk);
     };
-    auto byte_of = [](const uint4& v, int i) __attribute__((always_inline)) {
-        const uint32_t w = (i >> 2) == 0 ? v.x : (i >> 2) == 1 ? v.y : (i >> 2) == 2 ? v.z : v.w;
-        return int((w >> ((i & 3) * 8)) & 0xffu);
+    // stage 2 p + odd of a chunk: scale byte 4 p + 2 odd + g2 of the chunk's 16, i.e. word p,
+    // bit offset (2 odd + g2) * 8 (p and odd are compile-time constants below)
+    auto word = [](const uint4& v, int p) __attribute__((always_inline)) {
+        return p == 0 ? v.x : p == 1 ? v.y : p == 2 ? v.z : v.w;
     };
-    auto compute = [&](const Stg& x, const Scl& c, int st) __attribute__((always_inline)) {
-        const int bi = (st & 7) * 2 + g2;
-        const int as = byte_of(c.a, bi);
+    auto compute = [&](const Stg& x, const Scl& c, int p, int odd) __attribute__((always_inline)) {
+        const int sh = (2 * odd + g2) * 8;
+        const int as = int((word(c.a, p) >> sh) & 0xffu);
 #pragma unroll
         for (int h = 0; h < NG; ++h) {
             const i32x4_t z = {0, 0, 0, 0};
             const i32x8_t b = __builtin_shufflevector(x.b0[h], BF4 ? z : x.b1[h], 0, 1, 2, 3, 4, 5, 6, 7);
-            acc[h] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x.a, b, acc[h], 0, BF4 ? 4 : 0, 0, as,
-                                                                     0, byte_of(c.w[h], bi));
+            acc[h] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                x.a, b, acc[h], 0, BF4 ? 4 : 0, 0, as, 0, int((word(c.w[h], p) >> sh) & 0xffu));
         }
     };
     if (live && per > 0) {
-        const int clast = (s1 - 1) >> 3;
+        const int c0s = s0 >> 3, clast = (s1 - 1) >> 3;
         Stg x0, x1;
         Scl cur, nxt;
-        sload(cur, s0 >> 3);
-        sload(nxt, min((s0 >> 3) + 1, clast));
+        sload(cur, c0s);
+        sload(nxt, min(c0s + 1, clast));
         load(x0, s0);
-        load(x1, min(s0 + 1, s1 - 1));  // past the end: a harmless re-read of the last stage
-        for (int st = s0;; st += 2) {   // chunk boundaries (st % 8 == 0) fall on even stages
-            if ((st & 7) == 0 && st != s0) {
+        load(x1, s0 + 1);
+        // whole chunks of 8 stages (per is a multiple of 8), two stages in flight; the last
+        // pair's loads re-read the last stage (cache hits), which keeps one loop exit and one
+        // set of accumulators
+        for (int ch = c0s; ch <= clast; ++ch) {
+            if (ch != c0s) {
                 cur = nxt;
-                sload(nxt, min((st >> 3) + 1, clast));
+                sload(nxt, min(ch + 1, clast));
             }
-            compute(x0, cur, st);
-            if (st + 1 >= s1) break;
-            load(x0, min(st + 2, s1 - 1));
-            compute(x1, cur, st + 1);
-            if (st + 2 >= s1) break;
-            load(x1, min(st + 3, s1 - 1));
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const int st = ch * 8 + 2 * p;
+                compute(x0, cur, p, 0);
+                load(x0, min(st + 2, s1 - 1));
+                compute(x1, cur, p, 1);
+                load(x1, min(st + 3, s1 - 1));
+            }
         }
     }
 
