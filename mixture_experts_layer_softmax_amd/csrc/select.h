@@ -6,8 +6,36 @@
 
 namespace moe {
 
+// Wave-wide reductions on the DPP lane network (no LDS round trips): within rows of 16 by
+// quad permutes and mirrors, then across rows by the row-15 / row-31 broadcasts, so that lane 63
+// holds the result, which is read out as a wave-uniform value.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ int dpp_i32(int v) {
+    return __builtin_amdgcn_update_dpp(v, v, CTRL, ROW_MASK, 0xf, false);
+}
+__device__ __forceinline__ float wave_max_f32(float v) {
+    v = fmaxf(v, __int_as_float(dpp_i32<0xb1>(__float_as_int(v))));        // quad_perm [1,0,3,2]
+    v = fmaxf(v, __int_as_float(dpp_i32<0x4e>(__float_as_int(v))));        // quad_perm [2,3,0,1]
+    v = fmaxf(v, __int_as_float(dpp_i32<0x141>(__float_as_int(v))));       // row_half_mirror
+    v = fmaxf(v, __int_as_float(dpp_i32<0x140>(__float_as_int(v))));       // row_mirror
+    v = fmaxf(v, __int_as_float(dpp_i32<0x142, 0xa>(__float_as_int(v))));  // row_bcast:15
+    v = fmaxf(v, __int_as_float(dpp_i32<0x143, 0xc>(__float_as_int(v))));  // row_bcast:31
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+__device__ __forceinline__ int wave_min_i32(int v) {
+    v = min(v, dpp_i32<0xb1>(v));
+    v = min(v, dpp_i32<0x4e>(v));
+    v = min(v, dpp_i32<0x141>(v));
+    v = min(v, dpp_i32<0x140>(v));
+    v = min(v, dpp_i32<0x142, 0xa>(v));
+    v = min(v, dpp_i32<0x143, 0xc>(v));
+    return __builtin_amdgcn_readlane(v, 63);
+}
+
 // Top-k of one token by one wavefront: k rounds of a wave-wide argmax over (logit desc,
-// expert asc), then the softmax weights in fp32.  `row` is the token's E logits; ids and w
+// expert asc), then the softmax weights in fp32.  A round takes the largest value (a DPP max;
+// fmaxf is exact), then the smallest expert index among the lanes whose candidate equals it
+// (+0 and -0 compare equal, as in a plain comparison).  `row` is the token's E logits; ids and w
 // receive k values each (and ids_lds too, when given).  NaN logits rank below every number, so
 // the comparison is a total order and every lane agrees on each winner: always k distinct valid
 // experts, also for non-finite logits (whose weights are then unspecified).
@@ -34,7 +62,7 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ row, int E,
         sele[j] = 0;
     }
     for (int j = 0; j < k; ++j) {
-        float bv = 0.0f;
+        float bv = -__builtin_inff();
         int be = NONE;
 #pragma unroll
         for (int i = 0; i < EPL; ++i)
@@ -42,16 +70,10 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ row, int E,
                 bv = v[i];
                 be = lane + kWave * i;
             }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const float ov = __shfl_xor(bv, off);
-            const int oe = __shfl_xor(be, off);
-            const bool take = oe != NONE && (be == NONE || ov > bv || (ov == bv && oe < be));
-            if (take) {
-                bv = ov;
-                be = oe;
-            }
-        }
+        // a lane without a candidate holds -inf and NONE, so it never takes the index round
+        const float m = wave_max_f32(bv);
+        be = wave_min_i32((be != NONE && bv == m) ? be : NONE);
+        bv = m;
 #pragma unroll
         for (int i = 0; i < EPL; ++i)
             if (be == lane + kWave * i) live[i] = false;

@@ -101,6 +101,40 @@ def test_route_matches_oracle(name):
     np.testing.assert_allclose(w.cpu().numpy(), ref["topk_w"], rtol=W_RTOL, atol=0)
 
 
+@pytest.mark.parametrize("T,E,k", [(1, 64, 8), (5, 200, 8), (16, 256, 8), (16, 33, 16), (40, 64, 8),
+                                   (300, 200, 6)])
+def test_route_with_exact_ties_matches_oracle(T, E, k):
+    """Many equal logits: token rows are one-hot, so every logit is exactly one router weight
+    (plus bias), and the router weights take five values (-1, -0, 0, 1, 2).  The selection must
+    order them by value and then by expert index, like the oracle, on the single-launch path
+    (moe_forward, up to 16 tokens) and on the one-wavefront-per-token path (moe_route)."""
+    rng = np.random.default_rng(T * 7 + E)
+    H, F = 256, 128
+    x = np.zeros((T, H), np.float32)
+    x[np.arange(T), rng.integers(0, H, T)] = 1.0
+    wr = rng.choice(np.array([-1.0, -0.0, 0.0, 1.0, 2.0], np.float32), size=(E, H))
+    bias = rng.choice(np.array([0.0, 1.0], np.float32), size=E)
+    wl = W("ties", T, H, E, k, F, "bf16", "bf16", 95, "none")
+    inp = synth.generate(wl)
+    inp.update(x=synth.to_bf16_bits(x), w_router=synth.to_bf16_bits(wr), bias=bias)
+    ref = O.route(inp, k)
+    note("route with ties T=%d E=%d k=%d" % (T, E, k))
+    p = lib.problem(T, H, E, k, F)
+    ws = torch.empty(lib.workspace_size(p), dtype=torch.uint8, device="cuda")
+    ids = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, k, dtype=torch.float32, device="cuda")
+    xd, wd = to_device(inp["x"], "cuda", "bf16"), to_device(inp["w_router"], "cuda", "bf16")
+    lib.route(p, xd, wd, to_device(bias, "cuda"), ids, w, ws)
+    layer = MoELayer.from_workload(wl, inp)
+    _, dbg = layer.forward(xd, debug=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(ids.cpu().numpy(), ref["topk_ids"])
+    np.testing.assert_allclose(w.cpu().numpy(), ref["topk_w"], rtol=W_RTOL, atol=0)
+    assert np.array_equal(dbg["topk_ids"].cpu().numpy(), ref["topk_ids"])
+    for key in ("counts", "offsets", "sorted_token", "inv_perm"):
+        assert np.array_equal(dbg[key].cpu().numpy().reshape(ref[key].shape), ref[key]), key
+
+
 def test_route_small_and_large_batch_kernels_agree():
     """Batches under 64 tokens use one-token wavefronts, larger ones 8x8 blocks: same logits."""
     wl = synth.WORKLOADS["decode64"]
