@@ -82,6 +82,11 @@ moe_status check_problem(const moe_problem* p) {
     return MOE_OK;
 }
 
+// moe_forward on the bf16 prefill kernels hands hid from the gate/up GEMM to the down GEMM in
+// the packed tile image, so that the down GEMM reads each stage of a row tile as one contiguous
+// 16 KiB, like its weights, instead of 256 rows of 64 bytes each
+bool hid_packed(const moe_problem& p) { return family_of(p) == kFamPrefill && p.w_dtype == MOE_BF16; }
+
 Layout layout(const moe_problem& p) {
     Layout L{};
     const size_t T = p.num_tokens, E = p.num_experts, k = p.top_k, H = p.hidden, F = p.ffn;
@@ -104,7 +109,8 @@ Layout layout(const moe_problem& p) {
     L.tiles1 = take(size_t(L.max_tiles) * sizeof(Tile));
     L.tiles2 = take(size_t(L.max_tiles) * sizeof(Tile));
     L.tcount = take(4 * sizeof(int));
-    L.hid = take(A * F * act_bytes(p));
+    // bf16 prefill forward: hid in the packed tile image (every tile a full 256 rows)
+    L.hid = take(hid_packed(p) ? size_t(L.max_tiles) * 256 * F * 2 : A * F * act_bytes(p));
     L.yperm = take(A * H * act_bytes(p));
     const bool mx = is_mx(p);  // MXFP8 copies of the GEMM inputs (codes + scales)
     L.xq = take(mx ? A * H : 0);
@@ -437,9 +443,11 @@ moe_status moe_forward(const moe_problem* p, const void* x, const void* w_router
     void* hid = at<void>(workspace, L.hid);
     void* yperm = at<void>(workspace, L.yperm);
     GemmArgs g1 = gemm_args(*p, kGateUp, x, st, tiles, tcount, *w, hid);
+    g1.hid_packed = hid_packed(*p);
     MOE_TRY(mx_input(*p, g1, workspace, L, s));
     MOE_TRY(dev(launch_gemm(g1, L.family, L.max_tiles, s)));
     GemmArgs g2 = gemm_args(*p, kDown, hid, nullptr, tiles, tcount, *w, yperm);
+    g2.hid_packed = hid_packed(*p);  // both GEMMs walk the same tile list
     MOE_TRY(mx_input(*p, g2, workspace, L, s));
     MOE_TRY(dev(launch_gemm(g2, L.family, L.max_tiles, s)));
     return dev(launch_combine(yperm, ip, tw, y, p->num_tokens, p->top_k, p->hidden,

@@ -282,8 +282,17 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_bf16_kernel(GemmArgs g) {
     const int K = g.K;
 
     const char* pa[2];
+    // A operand: gathered rows (64 bytes per row and stage), or for the down GEMM of a forward
+    // the packed hid image of this row tile (one contiguous 16 KiB per stage, like the weights)
+    const bool apk = KIND == kDown && g.hid_packed;
+    const int astep = apk ? 512 : 2;  // bytes per K element along the A stream
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
+        if (apk) {
+            pa[i] = static_cast<const char*>(g.a) + size_t(item / ncols) * size_t(K / BKS) * 16384 +
+                    (i * 8 + wave) * 1024 + lane * 16;
+            continue;
+        }
         const int row = (i * 8 + wave) * 16 + (lane >> 2);
         const int ch = (lane & 3) ^ ((row >> 1) & 3);
         const int rr = min(r0 + row, r1 - 1);
@@ -308,7 +317,7 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_bf16_kernel(GemmArgs g) {
     do {                                                                                        \
         const int k0_ = (K0);                                                                   \
         _Pragma("unroll") for (int i = 0; i < 2; ++i)                                           \
-            dma16(pa[i] + k0_ * 2, &SA[(i * 8 + wave) * 64]);                                   \
+            dma16(pa[i] + k0_ * astep, &SA[(i * 8 + wave) * 64]);                               \
         _Pragma("unroll") for (int i = 0; i < 2; ++i)                                           \
             dma16(pb[i] + k0_ * 512, &SB[(i * 8 + wave) * 64]);                                 \
     } while (0)
@@ -389,7 +398,14 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_bf16_kernel(GemmArgs g) {
 #pragma unroll
                 for (int ni = 0; ni < 2; ++ni) {
                     const int col = nt * HALF + (wc >> 1) * 64 + (wc & 1) * 32 + ni * 16 + (lane & 15);
-                    out[size_t(row) * g.F + col] = (uint16_t)bf16_rne(silu_mul(acc[mi][ni][i], acc[mi][ni + 2][i]));
+                    const uint16_t h = (uint16_t)bf16_rne(silu_mul(acc[mi][ni][i], acc[mi][ni + 2][i]));
+                    if (g.hid_packed) {  // tile row tr, stage col / 32, chunk (col / 8) % 4 in its slot
+                        const int tr = row - r0;
+                        const size_t blk = size_t(item / ncols) * (g.F / BKS) + (col >> 5);
+                        out[blk * 8192 + tr * 32 + ((((col >> 3) & 3) ^ ((tr >> 1) & 3)) << 3) + (col & 7)] = h;
+                    } else {
+                        out[size_t(row) * g.F + col] = h;
+                    }
                 }
             } else {
 #pragma unroll

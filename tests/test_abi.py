@@ -45,9 +45,14 @@ def test_workspace_size_of_every_workload(L, name):
     p = lib.problem(wl.tokens, wl.hidden, wl.experts, wl.top_k, wl.ffn, wl.act, wl.wdt)
     n = lib.workspace_size(p)
     A = wl.assignments
-    # the intermediates dominate: hid [A,F] and y_perm [A,H] (+ their MXFP8 copies: codes and scales)
+    # the intermediates dominate: hid [A,F] and y_perm [A,H] (+ their MXFP8 copies: codes and
+    # scales); the bf16 prefill forward keeps hid as full 256-row tiles (the worst-case tile
+    # count: ceil(A / 256) + min(A, E) + 1)
     act = 4 if wl.act == "f32" else 2
-    inter = A * (wl.ffn + wl.hidden) * act
+    hid_rows = A
+    if wl.wdt == "bf16" and A >= 16 * wl.experts:
+        hid_rows = ((A + 255) // 256 + min(A, wl.experts) + 1) * 256
+    inter = (hid_rows * wl.ffn + A * wl.hidden) * act
     if wl.wdt.startswith("mx"):
         inter += A * (wl.ffn + wl.hidden) * 33 // 32
     assert n >= inter
