@@ -613,12 +613,12 @@ def test_non_finite_inputs_stay_memory_safe_and_route_validly():
 
 @pytest.mark.parametrize("name,T", [("decode1", 1), ("decode8", 8), ("nvfp4_decode", 3), ("small_bf16", 5),
                                     ("nvfp4_decode", 16), ("decode8", 17), ("small_bf16", 384),
-                                    ("ragged_bf16", 77)])
+                                    ("ragged_bf16", 77), ("small_nvfp4", 384)])
 def test_forward_equals_its_stages(name, T):
     """moe_forward must equal route -> permute -> two grouped GEMMs -> combine through the stage
     entry points, bit for bit: on batches of up to 16 tokens (single-block selection and
-    dispatch; T = 17 is the first size past it) and on the bf16 prefill kernels, where the
-    forward hands hid over in the packed tile image and the stage entry points row-major."""
+    dispatch; T = 17 is the first size past it) and on the prefill kernels (the bf16 forward
+    hands hid over in the packed tile image, the stage entry points row-major)."""
     base = SMALL.get(name) or synth.WORKLOADS[name]
     wl = base.with_tokens(T, x_sub=100 + T)
     inp = inputs_of(wl)
