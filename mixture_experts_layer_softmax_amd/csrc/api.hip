@@ -429,8 +429,9 @@ moe_status moe_forward(const moe_problem* p, const void* x, const void* w_router
                    nullptr, nullptr, 0, L.max_tiles, ebegin(*p), eend(*p)};
     // up to 16 tokens (two per wavefront of the dispatch block): logits, then selection and
     // dispatch in one single-block launch; larger batches select with one wavefront per token
-    // (measured on MI355X: one launch instead of four saves about 5 us at 16 tokens, while at 64
-    // tokens the serial selection in one block costs more than it saves)
+    // (measured on MI355X: one launch instead of four saves about 5 us at 16 tokens; up to 32
+    // tokens the two are within noise, at 48 and 64 tokens the serial selection in one block
+    // costs 6-12 us more than it saves)
     if (p->num_tokens <= 2 * (kMaxExperts / kWave)) {
         RouteArgs r{x, w_router, router_bias, at<float>(workspace, L.logits), p->num_tokens, p->hidden,
                     p->num_experts, p->act_dtype == MOE_BF16};
