@@ -427,12 +427,12 @@ moe_status moe_forward(const moe_problem* p, const void* x, const void* w_router
     DispatchArgs d{ids, p->num_tokens, p->top_k, p->num_experts, at<int32_t>(workspace, L.hist),
                    at<int32_t>(workspace, L.base), counts, off, st, ip, tiles, tcount, L.bm,
                    nullptr, nullptr, 0, L.max_tiles, ebegin(*p), eend(*p)};
-    // up to 16 tokens (two per wavefront of the dispatch block): logits, then selection and
+    // up to 32 tokens (four per wavefront of the dispatch block): logits, then selection and
     // dispatch in one single-block launch; larger batches select with one wavefront per token
-    // (measured on MI355X: one launch instead of four saves about 5 us at 16 tokens; up to 32
-    // tokens the two are within noise, at 48 and 64 tokens the serial selection in one block
-    // costs 6-12 us more than it saves)
-    if (p->num_tokens <= 2 * (kMaxExperts / kWave)) {
+    // (measured on MI355X: one launch instead of four saves about 5 us at 16 tokens and 4 us for
+    // 32 tokens over 8 experts, is neutral at 24-32 tokens over 128 experts, and at 48 and 64
+    // tokens the serial selection in one block costs 3-12 us more than it saves)
+    if (p->num_tokens <= 4 * (kMaxExperts / kWave)) {
         RouteArgs r{x, w_router, router_bias, at<float>(workspace, L.logits), p->num_tokens, p->hidden,
                     p->num_experts, p->act_dtype == MOE_BF16};
         MOE_TRY(dev(launch_router_logits(r, s)));

@@ -169,10 +169,11 @@ hipError_t launch_fill_i32(int32_t* p, int n, int value, hipStream_t s) {
     return hipGetLastError();
 }
 
-// Small decode batches (any T <= 64; used for T <= 8, one token per wavefront): top-k
+// Small decode batches (any T <= 64; used for T <= 32, up to four tokens per wavefront): top-k
 // selection and the whole dispatch (histogram, scan, tile lists, stable scatter) in one block
-// of kMaxExperts threads, so a decode step spends one launch here instead of four.  Same results as topk_kernel +
-// hist/scan/scatter: ids of a token in selection order, rows of an expert in (t, j) order.
+// of kMaxExperts threads, so a decode step spends one launch here instead of four.  Same results
+// as topk_kernel + hist/scan/scatter: ids of a token in selection order, rows of an expert in
+// (t, j) order.
 template <int EPL>
 __global__ __launch_bounds__(kMaxExperts) void select_dispatch_small_kernel(
     const float* __restrict__ logits, int T, int E, int k, int renorm, int32_t* __restrict__ ids,

@@ -107,7 +107,7 @@ def test_route_with_exact_ties_matches_oracle(T, E, k):
     """Many equal logits: token rows are one-hot, so every logit is exactly one router weight
     (plus bias), and the router weights take five values (-1, -0, 0, 1, 2).  The selection must
     order them by value and then by expert index, like the oracle, on the single-launch path
-    (moe_forward, up to 16 tokens) and on the one-wavefront-per-token path (moe_route)."""
+    (moe_forward, up to 32 tokens) and on the one-wavefront-per-token path (moe_route)."""
     rng = np.random.default_rng(T * 7 + E)
     H, F = 256, 128
     x = np.zeros((T, H), np.float32)
@@ -530,10 +530,10 @@ def test_k_equals_e(E, k):
 
 
 @pytest.mark.parametrize("T,E,k", [(1, 8, 8), (8, 512, 16), (3, 5, 2), (8, 128, 8), (5, 1, 1),
-                                   (2, 3, 3)])
+                                   (2, 3, 3), (20, 64, 8), (32, 7, 3), (32, 512, 16)])
 def test_small_batch_single_launch_dispatch(T, E, k):
-    """Batches of up to 8 tokens select and dispatch in one single-block launch; routing
-    outputs stay bit-exact and the layer output within tolerance."""
+    """Batches of up to 32 tokens select and dispatch in one single-block launch (up to four
+    tokens per wavefront); routing outputs stay bit-exact and the layer output within tolerance."""
     wl = W("smallsel", T, 256, E, k, 128, "bf16", "bf16", 71 + E + T, "normal")
     inp = synth.generate(wl)
     note("small-batch dispatch T=%d E=%d k=%d" % (T, E, k))
@@ -612,12 +612,12 @@ def test_non_finite_inputs_stay_memory_safe_and_route_validly():
 
 
 @pytest.mark.parametrize("name,T", [("decode1", 1), ("decode8", 8), ("nvfp4_decode", 3), ("small_bf16", 5),
-                                    ("nvfp4_decode", 16), ("decode8", 17), ("small_bf16", 384),
+                                    ("nvfp4_decode", 16), ("decode8", 32), ("decode8", 33), ("small_bf16", 384),
                                     ("ragged_bf16", 77), ("small_nvfp4", 384)])
 def test_forward_equals_its_stages(name, T):
     """moe_forward must equal route -> permute -> two grouped GEMMs -> combine through the stage
-    entry points, bit for bit: on batches of up to 16 tokens (single-block selection and
-    dispatch; T = 17 is the first size past it) and on the prefill kernels (the bf16 forward
+    entry points, bit for bit: on batches of up to 32 tokens (single-block selection and
+    dispatch; T = 33 is the first size past it) and on the prefill kernels (the bf16 forward
     hands hid over in the packed tile image, the stage entry points row-major)."""
     base = SMALL.get(name) or synth.WORKLOADS[name]
     wl = base.with_tokens(T, x_sub=100 + T)
