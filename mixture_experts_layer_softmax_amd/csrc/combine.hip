@@ -3,10 +3,11 @@
 // "CuTeDSL at Perplexity", section Mixture-of-Experts Dispatch/Combine, Local: the combine
 // kernel uses the positions dispatch assigned to gather a token's expert rows and accumulates
 // them in registers with vectorised accesses, then writes the final token.  Here: one block
-// per token, 16-byte loads of y_perm rows, fp32 accumulation in ascending slot order, one
-// rounding to the output type.  Slots with a negative row were not dispatched here (their
-// expert is held by another rank under expert parallelism) and are skipped, so the result is
-// the local part of the combine that the pages follow with an all-reduce.
+// per token, 16-byte loads of y_perm rows (all rows of a vector issued before the first FMA),
+// fp32 accumulation in ascending slot order, one rounding to the output type.  Slots with a
+// negative row were not dispatched here (their expert is held by another rank under expert
+// parallelism) and are skipped, so the result is the local part of the combine that the pages
+// follow with an all-reduce.
 #include "device.h"
 #include "launch.h"
 
@@ -18,30 +19,37 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
                                                       const float* __restrict__ w,
                                                       void* __restrict__ y, int k, int H, int A) {
     const int t = blockIdx.x;
+    // slot j of the token at index j (compile-time indices keep everything in registers);
+    // slots with a negative row are skipped, which keeps the ascending order of the others
     int rows[kMaxTopK];
     float ws[kMaxTopK];
-    int n = 0;  // dispatched slots of this token, in ascending j
+    bool ok[kMaxTopK];
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j) {
         rows[j] = 0;
         ws[j] = 0.0f;
-    }
-    for (int j = 0; j < k; ++j) {
-        const int r = inv_perm[size_t(t) * k + j];
-        if (r < 0) continue;
-        rows[n] = r >= A ? A - 1 : r;
-        ws[n] = w[size_t(t) * k + j];
-        ++n;
+        ok[j] = false;
+        if (j < k) {
+            const int r = inv_perm[size_t(t) * k + j];
+            ok[j] = r >= 0;
+            rows[j] = r < 0 ? 0 : (r >= A ? A - 1 : r);
+            ws[j] = w[size_t(t) * k + j];
+        }
     }
     if (BF16) {
         const uint4* src = static_cast<const uint4*>(y_perm);
         uint4* dst = static_cast<uint4*>(y);
         const int nv = H / 8;
         for (int v = threadIdx.x; v < nv; v += blockDim.x) {
+            uint4 q[kMaxTopK];  // all of this vector's row loads in flight before the first FMA
+#pragma unroll
+            for (int j = 0; j < kMaxTopK; ++j)
+                if (ok[j]) q[j] = src[size_t(rows[j]) * nv + v];
             float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            for (int j = 0; j < n; ++j) {
-                const uint4 q = src[size_t(rows[j]) * nv + v];
-                const uint32_t u[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+            for (int j = 0; j < kMaxTopK; ++j) {
+                if (!ok[j]) continue;
+                const uint32_t u[4] = {q[j].x, q[j].y, q[j].z, q[j].w};
 #pragma unroll
                 for (int p = 0; p < 4; ++p) {
                     acc[2 * p] = __builtin_fmaf(ws[j], bf16_lo(u[p]), acc[2 * p]);
@@ -56,13 +64,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
         float4* dst = static_cast<float4*>(y);
         const int nv = H / 4;
         for (int v = threadIdx.x; v < nv; v += blockDim.x) {
+            float4 q[kMaxTopK];
+#pragma unroll
+            for (int j = 0; j < kMaxTopK; ++j)
+                if (ok[j]) q[j] = src[size_t(rows[j]) * nv + v];
             float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-            for (int j = 0; j < n; ++j) {
-                const float4 q = src[size_t(rows[j]) * nv + v];
-                acc.x = __builtin_fmaf(ws[j], q.x, acc.x);
-                acc.y = __builtin_fmaf(ws[j], q.y, acc.y);
-                acc.z = __builtin_fmaf(ws[j], q.z, acc.z);
-                acc.w = __builtin_fmaf(ws[j], q.w, acc.w);
+#pragma unroll
+            for (int j = 0; j < kMaxTopK; ++j) {
+                if (!ok[j]) continue;
+                acc.x = __builtin_fmaf(ws[j], q[j].x, acc.x);
+                acc.y = __builtin_fmaf(ws[j], q[j].y, acc.y);
+                acc.z = __builtin_fmaf(ws[j], q[j].z, acc.z);
+                acc.w = __builtin_fmaf(ws[j], q[j].w, acc.w);
             }
             dst[size_t(t) * nv + v] = acc;
         }
