@@ -1105,6 +1105,11 @@ namespace {
 // wavefronts of 16 x 32 (weight streaming, many blocks for few rows).
 constexpr int PF_BM = 128, PF_BN = 128, PF_WM = 2, PF_WN = 2;   // NVFP4 prefill
 constexpr int DC_BM = 16, DC_BN = 64, DC_WM = 1, DC_WN = 2;
+// Decode GEMMs split K over up to 4 wavefronts of a block until the worst-case tile count gives
+// this many wavefronts.  Measured on MI355X (forward, one process): 32768 against 4096 makes
+// decode T=8 322.7 -> 305.5 us, T=24 641.7 -> 621.0 us, T=64 812.7 -> 792.1 us, and the NVFP4
+// decode GEMMs (T=16) 183.5 / 103.9 -> 178.2 / 97.2 us; 16384 gains only at T=8.
+constexpr long kDecodeWaves = 32768;
 }  // namespace
 
 int gemm_tile_rows(int family, int wfmt, int ffn) {
@@ -1170,7 +1175,7 @@ hipError_t launch_gemm(const GemmArgs& g, int family, int max_tiles, hipStream_t
         constexpr int NCG_UP = 1, NCG_DOWN = 2;
         const int ncg = up ? g.F / 16 / NCG_UP : g.N / 16 / NCG_DOWN;  // wavefront group sets
         int split = 1;
-        while (split < 4 && long(max_tiles) * ncg * split < 4096 && g.K % (128 * split * 2) == 0) split *= 2;
+        while (split < 4 && long(max_tiles) * ncg * split < kDecodeWaves && g.K % (128 * split * 2) == 0) split *= 2;
         const int wpb = 4 / split;
         dim3 grid(max_tiles * ((ncg + wpb - 1) / wpb)), block(256);
 #define MOE_DECP(KD, SK, NC) hipLaunchKernelGGL((gemm_decode_nvfp4p_kernel<KD, SK, NC>), grid, block, 0, s, g)
@@ -1178,10 +1183,10 @@ hipError_t launch_gemm(const GemmArgs& g, int family, int max_tiles, hipStream_t
         else    { if (split == 1) MOE_DECP(kDown, 1, NCG_DOWN);   else if (split == 2) MOE_DECP(kDown, 2, NCG_DOWN);   else MOE_DECP(kDown, 4, NCG_DOWN); }
 #undef MOE_DECP
     } else if (g.K % 128 == 0) {
-        // split K until there are about 4 wavefronts per SIMD (4096) for the worst-case tile count
+        // split K until the worst-case tile count gives kDecodeWaves wavefronts
         const int ncg = up ? g.F / 16 : (g.N + 15) / 16;
         int split = 1;
-        while (split < 4 && long(max_tiles) * ncg * split < 4096 && g.K % (128 * split * 2) == 0) split *= 2;
+        while (split < 4 && long(max_tiles) * ncg * split < kDecodeWaves && g.K % (128 * split * 2) == 0) split *= 2;
         const int cgb = 4 / split;
         dim3 grid(max_tiles * ((ncg + cgb - 1) / cgb)), block(256);
 #define MOE_DEC(KD, WF, SK) hipLaunchKernelGGL((gemm_decode_kernel<KD, WF, SK>), grid, block, 0, s, g)
