@@ -25,6 +25,7 @@ CASES = {
     "small_bf16": W("small_bf16", 512, 512, 8, 2, 256, "bf16", "bf16", 11, "normal"),
     "small_nvfp4": W("small_nvfp4", 384, 512, 16, 4, 256, "bf16", "nvfp4", 12, "normal"),
     "ragged_f32": W("ragged_f32", 33, 128, 5, 2, 192, "f32", "f32", 16, "normal"),
+    "decode1": synth.WORKLOADS["decode1"],
     "decode8": synth.WORKLOADS["decode8"],
     "decode64": synth.WORKLOADS["decode64"],
 }
@@ -81,7 +82,8 @@ def run_share(wl, sub, b, n, tokens=None, path=None):
 
 
 @pytest.mark.parametrize("name,b,n", [("small_bf16", 0, 3), ("small_bf16", 3, 5), ("small_bf16", 7, 1),
-                                      ("small_nvfp4", 4, 8), ("ragged_f32", 1, 3), ("decode8", 32, 32),
+                                      ("small_nvfp4", 4, 8), ("ragged_f32", 1, 3), ("decode1", 0, 64),
+                                      ("decode1", 64, 64), ("decode8", 32, 32),
                                       ("decode64", 96, 32)])
 def test_share_matches_oracle(name, b, n):
     wl = CASES[name]

@@ -29,6 +29,8 @@ SMALL = {
     "win4_nvfp4": W("win4_nvfp4", 8, 2048, 16, 2, 2048, "bf16", "nvfp4", 15, "normal"),
     "ragged_f32": W("ragged_f32", 33, 128, 5, 2, 192, "f32", "f32", 16, "normal"),
     "tiny": synth.WORKLOADS["tiny"],
+    # top-16 routing with F = 128 (one token: 16 slots through the single-block dispatch)
+    "k16_bf16": W("k16_bf16", 64, 512, 32, 16, 128, "bf16", "bf16", 41, "normal"),
 }
 
 
@@ -613,7 +615,8 @@ def test_non_finite_inputs_stay_memory_safe_and_route_validly():
 
 @pytest.mark.parametrize("name,T", [("decode1", 1), ("decode8", 8), ("nvfp4_decode", 3), ("small_bf16", 5),
                                     ("nvfp4_decode", 16), ("decode8", 32), ("decode8", 33), ("small_bf16", 384),
-                                    ("ragged_bf16", 77), ("small_nvfp4", 384)])
+                                    ("ragged_bf16", 77), ("small_nvfp4", 384), ("k16_bf16", 1),
+                                    ("small_bf16", 1)])
 def test_forward_equals_its_stages(name, T):
     """moe_forward must equal route -> permute -> two grouped GEMMs -> combine through the stage
     entry points, bit for bit: on batches of up to 32 tokens (single-block selection and
