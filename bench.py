@@ -126,9 +126,9 @@ def cpu_baseline(wl, inputs, budget_s: float, held=None):
         t0 = time.perf_counter()
         O.forward(sub, wl.top_k, wl.wdt, wl.ffn, wl.renormalize, held=held)
         spent = time.perf_counter() - t0
-        if spent >= budget_s / 4 or n >= wl.tokens:
+        if spent >= budget_s / 2 or n >= wl.tokens:  # a final sample of 10-20 s at the default
             break
-        n = min(wl.tokens, int(n * max(2.0, budget_s / 4 / max(spent, 1e-3))))
+        n = min(wl.tokens, int(n * max(2.0, budget_s / 2 / max(spent, 1e-3))))
     return dict(value=n / spent, unit="tokens/s", cores=O.max_threads(), kind="oracle",
                 sample="first %d of the %d tokens, whole layer (route, dispatch, expert FFNs, "
                        "combine) in fp64, %.1f s" % (n, wl.tokens, spent), seconds=spent)
