@@ -43,6 +43,19 @@ __device__ __forceinline__ int clamp_expert(int e, int E) {
     return e < 0 ? 0 : (e >= E ? E - 1 : e);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wavefront on the DPP lane network: shifts by 1, 2,
+// 4 and 8 within rows of 16 (lanes shifted in from outside the row add 0), then the last lane of
+// row 0 into row 1 and of row 2 into row 3, then lane 31 into rows 2 and 3.
+__device__ __forceinline__ int wave_inclusive_scan_i32(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return x;
+}
+
 // Exclusive prefix sum over v for threads 0..n-1 of a block of NT threads (n <= NT <= 1024).
 // Returns the exclusive prefix; *total receives the sum.  All threads must call it.
 template <int NT>
@@ -50,12 +63,7 @@ __device__ int block_exclusive_scan(int v, int* total) {
     __shared__ int s_wave[NT / kWave];
     __shared__ int s_total;
     const int lane = lane_id(), w = threadIdx.x / kWave;
-    int x = v;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        int y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
+    const int x = wave_inclusive_scan_i32(v);
     if (lane == kWave - 1) s_wave[w] = x;
     __syncthreads();
     if (threadIdx.x == 0) {
