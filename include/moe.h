@@ -24,6 +24,10 @@
  *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only enqueues work
  *    on it; nothing synchronises and no device data is read on the host.  Results are valid
  *    once the caller has synchronised the stream.
+ *  - What is enqueued is kernel launches only (no memset, no copy), so a call may be
+ *    captured into a HIP graph and replayed.  Grids are sized from the host-side problem
+ *    fields alone, so a replay is valid for new contents of the same buffers (other tokens,
+ *    other routings), not for another moe_problem.
  *  - Errors are return codes; nothing is thrown and nothing aborts.  All arguments are
  *    validated on the host before any HIP call: MOE_ERR_INVALID_ARGUMENT for a null required
  *    pointer, a misaligned pointer, negative sizes, k < 1, k > E, k > 16, E > 512 or an
