@@ -48,7 +48,7 @@ int wfmt_of(const moe_problem& p) {
 bool is_mx(const moe_problem& p) { return p.w_dtype == MOE_MXFP8 || p.w_dtype == MOE_MXFP4; }
 
 int family_of(const moe_problem& p) {
-    if (p.act_dtype == MOE_F32) return kFamSimtF32;
+    if (p.act_dtype == MOE_F32) return kFamF32;
     int path = p.path;
     if (path == MOE_PATH_AUTO) {
         const long A = long(p.num_tokens) * p.top_k;

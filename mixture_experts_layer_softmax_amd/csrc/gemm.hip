@@ -17,7 +17,7 @@
 //   gemm_decode_kernel         few rows per expert: weights stream straight into MFMA
 //                              operand registers (bf16 packed, or NVFP4 row-major)
 //   gemm_fallback_kernel       NVFP4 shapes the two above do not tile (F % 128 or K % 128)
-//   gemm_f32_kernel            fp32 layers (SIMT)
+//   gemm_f32_kernel            fp32 layers (fp32 MFMA)
 // Gate and up rows that feed the same hid column sit in the same wavefront, so SwiGLU is
 // applied to accumulators in registers.  Activation rows are gathered through the dispatch
 // map (no permuted copy of x).
@@ -1029,17 +1029,25 @@ __global__ __launch_bounds__(256) void gemm_decode_nvfp4p_kernel(GemmArgs g) {
     }
 }
 
-// fp32 activations and weights: a plain 64 x 64 SIMT tile, 4 x 4 outputs per thread.  For the
-// gate/up kind, B columns 0..31 are gate rows and 32..63 the matching up rows (32 hid columns).
+// fp32 activations and weights on the fp32 matrix cores (v_mfma_f32_16x16x4_f32): a 64 x 64
+// block tile (64 dispatched rows, 64 weight rows), 4 wavefronts (2 x 2) of 32 x 32, K
+// in 16-wide stages through a two-slot LDS ring; the next stage's elements are loaded into
+// registers while the current stage's MFMAs run.  An MFMA step takes 4 consecutive k: lane l
+// supplies row l % 16 of A and column l % 16 of B at k = k0 + l / 16 and receives rows
+// 4 (l / 16) + i, column l % 16, of the 16 x 16 result.  LDS rows are padded to 80 floats so
+// that the four k rows one fragment read touches start 16 banks apart.  For the gate/up kind a
+// wavefront holds 16 gate columns (B columns 16 wn ...) and the 16 matching up columns
+// (32 + 16 wn ...), so SwiGLU pairs registers of one lane.
 template <int KIND>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
-    constexpr int TB = 64, TK = 16;
-    __shared__ float sA[TK][TB + 4];
-    __shared__ float sB[TK][TB + 4];
+    constexpr int TB = 64, TK = 16, LD = TB + 16;
+    __shared__ float sA[2][TK][LD];
+    __shared__ float sB[2][TK][LD];
     if (int(blockIdx.x) >= *g.tile_count) return;
     const Tile tile = g.tiles[blockIdx.x];
     const int e = tile.expert, r0 = tile.row0, r1 = tile.row1;
-    const int nt = blockIdx.y, tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
+    const int nt = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+    const int wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
     const int K = g.K;
     const int Nw = (KIND == kGateUp) ? 2 * g.F : g.N;
     const float* A = static_cast<const float*>(g.a);
@@ -1048,54 +1056,84 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
         if (KIND == kGateUp) return n < 32 ? nt * 32 + n : g.F + nt * 32 + (n - 32);
         return min(nt * TB + n, g.N - 1);
     };
-    // columns of this thread
-    int cols[4];
+    // staged element it of this thread: tile row idx / 16, k offset idx % 16 within the stage
+    const float* pa[4];
+    const float* pb[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-        cols[j] = (KIND == kGateUp) ? ((j < 2) ? tx * 2 + j : 32 + tx * 2 + (j - 2)) : tx * 4 + j;
-    float acc[4][4] = {};
-    for (int k0 = 0; k0 < K; k0 += TK) {
+    for (int it = 0; it < 4; ++it) {
+        const int idx = tid + it * 256, row = idx / TK, kk = idx % TK;
+        const int rr = min(r0 + row, r1 - 1);
+        int src = g.a_rows ? g.a_rows[rr] : rr;
+        src = src < 0 ? 0 : (src >= g.a_rows_limit ? g.a_rows_limit - 1 : src);
+        pa[it] = A + size_t(src) * K + kk;
+        pb[it] = W + (size_t(e) * Nw + brow(row)) * K + kk;
+    }
+    int bcol[2];
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+        bcol[ni] = (KIND == kGateUp ? (ni == 0 ? 16 * wn : 32 + 16 * wn) : 32 * wn + 16 * ni) + (lane & 15);
+    f32x4_t acc[2][2];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float ra[4], rb[4];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        ra[it] = pa[it][0];
+        rb[it] = pb[it][0];
+    }
+    const int nk = K / TK;
+    for (int st = 0; st < nk; ++st) {
+        const int buf = st & 1;
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
             const int idx = tid + it * 256, row = idx / TK, kk = idx % TK;
-            const int rr = min(r0 + row, r1 - 1);
-            int src = g.a_rows ? g.a_rows[rr] : rr;
-            src = src < 0 ? 0 : (src >= g.a_rows_limit ? g.a_rows_limit - 1 : src);
-            sA[kk][row] = A[size_t(src) * K + k0 + kk];
-            sB[kk][row] = W[(size_t(e) * Nw + brow(row)) * K + k0 + kk];
+            sA[buf][kk][row] = ra[it];
+            sB[buf][kk][row] = rb[it];
         }
+        // one barrier per stage: slot buf is written again only at stage st + 2, after every
+        // thread has passed the barrier of stage st + 1 and so finished reading it
         __syncthreads();
+        if (st + 1 < nk) {
 #pragma unroll
-        for (int kk = 0; kk < TK; ++kk) {
-            float av[4], bv[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) av[i] = sA[kk][ty * 4 + i];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) bv[j] = sB[kk][cols[j]];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(av[i], bv[j], acc[i][j]);
+            for (int it = 0; it < 4; ++it) {
+                ra[it] = pa[it][(st + 1) * TK];
+                rb[it] = pb[it][(st + 1) * TK];
+            }
         }
-        __syncthreads();
+#pragma unroll
+        for (int k4 = 0; k4 < TK; k4 += 4) {
+            const int kr = k4 + (lane >> 4);
+            float af[2], bf[2];
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi) af[mi] = sA[buf][kr][wm * 32 + mi * 16 + (lane & 15)];
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni) bf[ni] = sB[buf][kr][bcol[ni]];
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < 2; ++ni)
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[mi], bf[ni], acc[mi][ni], 0, 0, 0);
+        }
     }
     float* out = static_cast<float*>(g.out);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = r0 + ty * 4 + i;
-        if (row >= r1) continue;
-        if (KIND == kGateUp) {
+    for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-                out[size_t(row) * g.F + nt * 32 + tx * 2 + j] = silu_mul(acc[i][j], acc[i][j + 2]);
-        } else {
+        for (int i = 0; i < 4; ++i) {
+            const int row = r0 + wm * 32 + mi * 16 + 4 * (lane >> 4) + i;
+            if (row >= r1) continue;
+            if (KIND == kGateUp) {
+                out[size_t(row) * g.F + nt * 32 + 16 * wn + (lane & 15)] = silu_mul(acc[mi][0][i], acc[mi][1][i]);
+            } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int col = nt * TB + tx * 4 + j;
-                if (col < g.N) out[size_t(row) * g.N + col] = acc[i][j];
+                for (int ni = 0; ni < 2; ++ni) {
+                    const int col = nt * TB + 32 * wn + 16 * ni + (lane & 15);
+                    if (col < g.N) out[size_t(row) * g.N + col] = acc[mi][ni][i];
+                }
             }
         }
-    }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1113,7 +1151,7 @@ constexpr long kDecodeWaves = 32768;
 }  // namespace
 
 int gemm_tile_rows(int family, int wfmt, int ffn) {
-    if (family == kFamSimtF32) return 64;
+    if (family == kFamF32) return 64;
     if (family == kFamPrefill) return (wfmt == kWBF16 || ffn % 128 == 0) ? 256 : PF_BM;
     if (wfmt == kWMXFP8 || wfmt == kWMXFP4) return 32;  // the MX decode kernel's 32 x 32 MFMA tiles
     return DC_BM;
@@ -1140,7 +1178,7 @@ hipError_t launch_gemm(const GemmArgs& g, int family, int max_tiles, hipStream_t
     if (max_tiles <= 0) return hipSuccess;
     if (g.wfmt == kWMXFP8 || g.wfmt == kWMXFP4) return launch_gemm_mxfp8(g, family, max_tiles, s);  // mx.hip
     const bool up = g.kind == kGateUp;
-    if (family == kFamSimtF32) {
+    if (family == kFamF32) {
         const int ncols = up ? g.F / 32 : (g.N + 63) / 64;
         dim3 grid(max_tiles, ncols), block(256);
         if (up)

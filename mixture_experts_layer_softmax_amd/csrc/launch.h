@@ -38,7 +38,7 @@ struct DispatchArgs {
 
 enum GemmKind { kGateUp = 0, kDown = 1 };
 enum WeightFmt { kWF32 = 0, kWBF16 = 1, kWNVFP4 = 2, kWMXFP8 = 3, kWMXFP4 = 4 };
-enum GemmFamily { kFamSimtF32 = 0, kFamPrefill = 1, kFamDecode = 2 };
+enum GemmFamily { kFamF32 = 0, kFamPrefill = 1, kFamDecode = 2 };
 
 struct GemmArgs {
     const void* a;          // activations: bf16 or fp32, row length K
