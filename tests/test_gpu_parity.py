@@ -31,6 +31,10 @@ SMALL = {
     "tiny": synth.WORKLOADS["tiny"],
     # top-16 routing with F = 128 (one token: 16 slots through the single-block dispatch)
     "k16_bf16": W("k16_bf16", 64, 512, 32, 16, 128, "bf16", "bf16", 41, "normal"),
+    # MX layers: the forward's gate/up epilogue writes hid as MXFP8 itself
+    "small_mxfp8": W("small_mxfp8", 384, 512, 16, 4, 512, "bf16", "mxfp8", 17, "normal"),
+    "small_mxfp4": W("small_mxfp4", 384, 512, 16, 4, 512, "bf16", "mxfp4", 17, "normal"),
+    "split_mxfp8": W("split_mxfp8", 4, 2048, 8, 2, 2048, "bf16", "mxfp8", 20, "normal"),
 }
 
 
@@ -620,12 +624,15 @@ def test_non_finite_inputs_stay_memory_safe_and_route_validly():
 @pytest.mark.parametrize("name,T", [("decode1", 1), ("decode8", 8), ("nvfp4_decode", 3), ("small_bf16", 5),
                                     ("nvfp4_decode", 16), ("decode8", 32), ("decode8", 33), ("small_bf16", 384),
                                     ("ragged_bf16", 77), ("small_nvfp4", 384), ("k16_bf16", 1),
-                                    ("small_bf16", 1)])
+                                    ("small_bf16", 1), ("small_mxfp8", 5), ("small_mxfp8", 384),
+                                    ("small_mxfp4", 5), ("small_mxfp4", 384), ("split_mxfp8", 4)])
 def test_forward_equals_its_stages(name, T):
     """moe_forward must equal route -> permute -> two grouped GEMMs -> combine through the stage
     entry points, bit for bit: on batches of up to 32 tokens (single-block selection and
-    dispatch; T = 33 is the first size past it) and on the prefill kernels (the bf16 forward
-    hands hid over in the packed tile image, the stage entry points row-major)."""
+    dispatch; T = 33 is the first size past it), on the prefill kernels (the bf16 forward
+    hands hid over in the packed tile image, the stage entry points row-major) and on the MX
+    kernels (the forward's gate/up epilogue quantizes hid to MXFP8 itself, the stage entry
+    points store bf16 hid and the down GEMM quantizes it)."""
     base = SMALL.get(name) or synth.WORKLOADS[name]
     wl = base.with_tokens(T, x_sub=100 + T)
     inp = inputs_of(wl)
