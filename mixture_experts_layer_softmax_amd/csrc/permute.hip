@@ -169,18 +169,19 @@ hipError_t launch_fill_i32(int32_t* p, int n, int value, hipStream_t s) {
     return hipGetLastError();
 }
 
-// Small decode batches (any T <= 64; used for T <= 32, up to four tokens per wavefront): top-k
-// selection and the whole dispatch (histogram, scan, tile lists, stable scatter) in one block
-// of kMaxExperts threads, so a decode step spends one launch here instead of four.  Same results
+// Small decode batches (any T <= 64; used for T <= 32): top-k selection and the whole dispatch
+// (histogram, scan, tile lists, stable scatter) in one block of NT threads, so a decode step
+// spends one launch here instead of four.  Wavefront w selects tokens w, w + NT/64, ... one
+// after the other.  Same results
 // as topk_kernel + hist/scan/scatter: ids of a token in selection order, rows of an expert in
 // (t, j) order.
-template <int EPL>
-__global__ __launch_bounds__(kMaxExperts) void select_dispatch_small_kernel(
+template <int EPL, int NT>
+__global__ __launch_bounds__(NT) void select_dispatch_small_kernel(
     const float* __restrict__ logits, int T, int E, int k, int renorm, int32_t* __restrict__ ids,
     float* __restrict__ tw, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ sorted_token, int32_t* __restrict__ inv_perm, Tile* tiles1,
     int* tile_count1, int bm1, Tile* tiles2, int* tile_count2, int bm2, int cap, int eb, int ee) {
-    constexpr int NW = kMaxExperts / kWave;
+    constexpr int NW = NT / kWave;
     __shared__ int sids[kChunkTokens * kMaxTopK];
     __shared__ int cnt[kMaxExperts];
     __shared__ int wc[NW][kMaxExperts];
@@ -191,27 +192,27 @@ __global__ __launch_bounds__(kMaxExperts) void select_dispatch_small_kernel(
     if (tid < E) cnt[tid] = 0;
     __syncthreads();
     const int A = T * k;
-    for (int a = tid; a < A; a += kMaxExperts) {
+    for (int a = tid; a < A; a += NT) {
         const int id = clamp_expert(sids[a], E);
         if (id >= eb && id < ee) atomicAdd(&cnt[id], 1);
     }
     __syncthreads();
     const int c = tid < E ? cnt[tid] : 0;
     int total;
-    const int start = block_exclusive_scan<kMaxExperts>(c, &total);
+    const int start = block_exclusive_scan<NT>(c, &total);
     if (tid < E) {
         if (counts) counts[tid] = c;
         offsets[tid] = start;
     }
     if (tid == 0) offsets[E] = total;
-    if (tiles1) emit_tiles(tid, E, c, start, bm1, tiles1, tile_count1, cap, eb);
-    if (tiles2) emit_tiles(tid, E, c, start, bm2, tiles2, tile_count2, cap, eb);
+    if (tiles1) emit_tiles<NT>(tid, E, c, start, bm1, tiles1, tile_count1, cap, eb);
+    if (tiles2) emit_tiles<NT>(tid, E, c, start, bm2, tiles2, tile_count2, cap, eb);
     __syncthreads();
     if (tid < E) cnt[tid] = start;  // next free row of each expert
     int nbits = 0;
     while ((1 << nbits) < E) ++nbits;
-    for (int r0 = 0; r0 < A; r0 += kMaxExperts) {
-        for (int i = tid; i < NW * kMaxExperts; i += kMaxExperts) (&wc[0][0])[i] = 0;
+    for (int r0 = 0; r0 < A; r0 += NT) {
+        for (int i = tid; i < NW * kMaxExperts; i += NT) (&wc[0][0])[i] = 0;
         __syncthreads();
         const int a = r0 + tid;
         const int id0 = a < A ? clamp_expert(sids[a], E) : 0;
@@ -248,15 +249,25 @@ __global__ __launch_bounds__(kMaxExperts) void select_dispatch_small_kernel(
 hipError_t launch_select_dispatch_small(const float* logits, int renorm, int32_t* tw_ids,
                                         float* tw, const DispatchArgs& d, hipStream_t s) {
     const int epl = (d.E + kWave - 1) / kWave;
-#define MOE_SDS(N)                                                                                  \
-    hipLaunchKernelGGL((select_dispatch_small_kernel<N>), dim3(1), dim3(kMaxExperts), 0, s, logits, \
+#define MOE_SDS(N, NT)                                                                              \
+    hipLaunchKernelGGL((select_dispatch_small_kernel<N, NT>), dim3(1), dim3(NT), 0, s, logits,      \
                        d.T, d.E, d.k, renorm, tw_ids, tw, d.counts, d.offsets, d.sorted_token,      \
                        d.inv_perm, d.tiles1, d.tile_count1, d.bm1, d.tiles2, d.tile_count2, d.bm2,  \
                        d.tile_cap, d.ebegin, d.eend)
-    if (epl <= 1) MOE_SDS(1);
-    else if (epl <= 2) MOE_SDS(2);
-    else if (epl <= 4) MOE_SDS(4);
-    else MOE_SDS(8);
+    // 16 wavefronts once there are more than 8 tokens, so that each selects at most two of 32
+    // (kernel trace, median us, 512 -> 1024 threads: T=16 over 256 experts 13.8 -> 12.5, T=32
+    // over 128 16.4 -> 14.4; but T=1 6.0 -> 6.7 and T=8 7.4 -> 7.5, so 8 wavefronts there)
+    if (d.T > 8) {
+        if (epl <= 1) MOE_SDS(1, 1024);
+        else if (epl <= 2) MOE_SDS(2, 1024);
+        else if (epl <= 4) MOE_SDS(4, 1024);
+        else MOE_SDS(8, 1024);
+    } else {
+        if (epl <= 1) MOE_SDS(1, 512);
+        else if (epl <= 2) MOE_SDS(2, 512);
+        else if (epl <= 4) MOE_SDS(4, 512);
+        else MOE_SDS(8, 512);
+    }
 #undef MOE_SDS
     return hipGetLastError();
 }

@@ -124,11 +124,13 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ row, int E,
 // (thread e handles expert e; `start` = exclusive row offset of expert e).  A tile names its
 // expert by weight index e - ebase (the caller's first held expert; experts not held have no
 // rows).  At most `cap` tiles are written (a bound that valid counts never reach).
+// NT is the block size (every thread calls this).
+template <int NT = kMaxExperts>
 __device__ __forceinline__ void emit_tiles(int e, int E, int count, int start, int bm, Tile* tiles,
                            int* tile_count, int cap, int ebase) {
     const int nt = (e < E) ? (count + bm - 1) / bm : 0;
     int total;
-    const int first = block_exclusive_scan<kMaxExperts>(nt, &total);
+    const int first = block_exclusive_scan<NT>(nt, &total);
     for (int i = 0; i < nt && first + i < cap; ++i) {
         Tile t;
         t.expert = e - ebase;
