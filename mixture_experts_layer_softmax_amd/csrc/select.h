@@ -54,13 +54,10 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ row, int E,
         v[i] = live[i] ? row[e] : 0.0f;
         if (v[i] != v[i]) v[i] = -__builtin_inff();  // NaN ranks last: a total order for selection
     }
-    float selv[kMaxTopK];
-    int sele[kMaxTopK];
-#pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) {
-        selv[j] = 0.0f;
-        sele[j] = 0;
-    }
+    // lane j < k keeps the j-th selection (value and expert); m0 is the first (largest) value
+    float mysv = 0.0f;
+    int myse = 0;
+    float m0 = 0.0f;
     for (int j = 0; j < k; ++j) {
         float bv = -__builtin_inff();
         int be = NONE;
@@ -74,49 +71,36 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ row, int E,
         const float m = wave_max_f32(bv);
         be = wave_min_i32((be != NONE && bv == m) ? be : NONE);
         bv = m;
+        if (j == 0) m0 = bv;
 #pragma unroll
         for (int i = 0; i < EPL; ++i)
             if (be == lane + kWave * i) live[i] = false;
-#pragma unroll
-        for (int jj = 0; jj < kMaxTopK; ++jj)
-            if (jj == j) {
-                selv[jj] = bv;
-                sele[jj] = be;
-            }
+        if (lane == j) {
+            mysv = bv;
+            myse = be;
+        }
     }
-    // weights: exp(l_j - l_0) / z
+    // weights: exp(l_j - l_0) / z; z sums the k terms in selection order (renormalised) or
+    // every logit's term (full softmax)
     float z = 0.0f;
     if (renorm) {
-        for (int j = 0; j < k; ++j) {
-            float s = 0.0f;
-#pragma unroll
-            for (int jj = 0; jj < kMaxTopK; ++jj)
-                if (jj == j) s = selv[jj];
-            z += expf(s - selv[0]);
-        }
+        for (int j = 0; j < k; ++j)
+            z += expf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(mysv), j)) - m0);
     } else {
         float part = 0.0f;
 #pragma unroll
         for (int i = 0; i < EPL; ++i) {
             const int e = lane + kWave * i;
-            if (e < E) part += expf(row[e] - selv[0]);
+            if (e < E) part += expf(row[e] - m0);
         }
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
         z = part;
     }
     if (lane < k) {
-        float s = 0.0f;
-        int e = 0;
-#pragma unroll
-        for (int jj = 0; jj < kMaxTopK; ++jj)
-            if (jj == lane) {
-                s = selv[jj];
-                e = sele[jj];
-            }
-        ids[lane] = e;
-        w[lane] = expf(s - selv[0]) / z;
-        if (ids_lds) ids_lds[lane] = e;
+        ids[lane] = myse;
+        w[lane] = expf(mysv - m0) / z;
+        if (ids_lds) ids_lds[lane] = myse;
     }
 }
 
