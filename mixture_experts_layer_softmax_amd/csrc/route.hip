@@ -160,11 +160,23 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
 
 hipError_t launch_router_logits(const RouteArgs& a, hipStream_t s) {
     const int T = a.T, E = a.E;
-    // large batches: 8x8 (token, expert) blocks per wave for operand reuse; small batches:
-    // one token and 2 experts per wave, or one expert per wave while that still leaves at most
-    // 512 blocks (every wave waits for the same memory latency, so more of them finish sooner:
-    // decode T=1 with E=128 measured about 1 us less per forward, bit-identical logits).
-    if (T >= 64 && E >= 8) {
+    // large batches: 8x8 (token, expert) blocks per wave for operand reuse, 4x4 below 384 tokens
+    // (four times the wavefronts, each with a quarter of the serial FMA work; kernel trace,
+    // median us, 8x8 -> 4x4 at E=128: T=64 17.5 -> 12.0, T=128 17.5 -> 12.4, T=256 18.0 -> 14.4,
+    // but T=512 19.3 -> 20.8 and T=4096 85.7 -> 126.3); small batches: one token and 2 experts
+    // per wave, or one expert per wave while that still leaves at most 512 blocks (every wave
+    // waits for the same memory latency, so more of them finish sooner: decode T=1 with E=128
+    // measured about 1 us less per forward).  All shapes give bit-identical logits.
+    if (T >= 64 && T < 384 && E >= 8) {
+        const long waves = long((T + 3) / 4) * ((E + 3) / 4);
+        dim3 grid((waves + 3) / 4), block(256);
+        if (a.bf16)
+            hipLaunchKernelGGL((router_logits_kernel<true, 4, 4>), grid, block, 0, s, a.x, a.wr,
+                               a.bias, a.logits, T, a.H, E);
+        else
+            hipLaunchKernelGGL((router_logits_kernel<false, 4, 4>), grid, block, 0, s, a.x, a.wr,
+                               a.bias, a.logits, T, a.H, E);
+    } else if (T >= 64 && E >= 8) {
         const long waves = long((T + 7) / 8) * ((E + 7) / 8);
         dim3 grid((waves + 3) / 4), block(256);
         if (a.bf16)
