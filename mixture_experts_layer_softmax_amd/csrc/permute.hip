@@ -172,15 +172,15 @@ hipError_t launch_fill_i32(int32_t* p, int n, int value, hipStream_t s) {
 // Small decode batches (any T <= 64; used for T <= 32): top-k selection and the whole dispatch
 // (histogram, scan, tile lists, stable scatter) in one block of NT threads, so a decode step
 // spends one launch here instead of four.  Wavefront w selects tokens w, w + NT/64, ... one
-// after the other.  Same results
-// as topk_kernel + hist/scan/scatter: ids of a token in selection order, rows of an expert in
-// (t, j) order.
+// after the other; thread e < E then owns expert e.  Same results as topk_kernel +
+// hist/scan/scatter: ids of a token in selection order, rows of an expert in (t, j) order.
 template <int EPL, int NT>
 __global__ __launch_bounds__(NT) void select_dispatch_small_kernel(
     const float* __restrict__ logits, int T, int E, int k, int renorm, int32_t* __restrict__ ids,
     float* __restrict__ tw, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ sorted_token, int32_t* __restrict__ inv_perm, Tile* tiles1,
     int* tile_count1, int bm1, Tile* tiles2, int* tile_count2, int bm2, int cap, int eb, int ee) {
+    static_assert(NT >= kMaxExperts && NT % kWave == 0, "a thread per expert");
     constexpr int NW = NT / kWave;
     __shared__ int sids[kChunkTokens * kMaxTopK];
     __shared__ int cnt[kMaxExperts];
