@@ -386,34 +386,54 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_bf16_kernel(GemmArgs g) {
 #undef MOE_READ8
 #undef MOE_MFMA8
 
-    uint16_t* out = static_cast<uint16_t*>(g.out);
+    // Epilogue through LDS: every wavefront is past its last fragment read once all have reached
+    // the barrier, so each takes one 16 KiB ring array for its output tile (128 rows, 64 bf16
+    // columns; 32 hid columns for gate/up), writes its results there in the MFMA layout and
+    // reads them back as 16-byte row chunks for full-width global stores.  Chunk c8 of tile row
+    // lr sits in slot c8 ^ ((lr >> 2) & (W / 8 - 1)), so the four row groups of one LDS write
+    // (rows 4 apart) fall on different banks.
+    block_barrier();
+    constexpr int W = (KIND == kGateUp) ? 32 : 64;  // columns per wavefront
+    constexpr int SM = W / 8 - 1;
+    uint16_t* const stg = reinterpret_cast<uint16_t*>(
+        wave == 0 ? sA0 : wave == 1 ? sA1 : wave == 2 ? sA2 : wave == 3 ? sA3 :
+        wave == 4 ? sB0 : wave == 5 ? sB1 : wave == 6 ? sB2 : sB3);
 #pragma unroll
     for (int mi = 0; mi < 8; ++mi) {
         if (mi * 2 + wr >= nsub) continue;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int row = r0 + (mi * 2 + wr) * 16 + 4 * (lane >> 4) + i;
-            if (row >= r1) continue;
-            if (KIND == kGateUp) {
+            const int lr = mi * 16 + 4 * (lane >> 4) + i;
 #pragma unroll
-                for (int ni = 0; ni < 2; ++ni) {
-                    const int col = nt * HALF + (wc >> 1) * 64 + (wc & 1) * 32 + ni * 16 + (lane & 15);
-                    const uint16_t h = (uint16_t)bf16_rne(silu_mul(acc[mi][ni][i], acc[mi][ni + 2][i]));
-                    if (g.hid_packed) {  // tile row tr, stage col / 32, chunk (col / 8) % 4 in its slot
-                        const int tr = row - r0;
-                        const size_t blk = size_t(item / ncols) * (g.F / BKS) + (col >> 5);
-                        out[blk * 8192 + tr * 32 + ((((col >> 3) & 3) ^ ((tr >> 1) & 3)) << 3) + (col & 7)] = h;
-                    } else {
-                        out[size_t(row) * g.F + col] = h;
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int ni = 0; ni < 4; ++ni) {
-                    const int col = nt * BN + wc * 64 + ni * 16 + (lane & 15);
-                    if (col < g.N) out[size_t(row) * g.N + col] = (uint16_t)bf16_rne(acc[mi][ni][i]);
-                }
+            for (int ni = 0; ni < W / 16; ++ni) {
+                const int lc = ni * 16 + (lane & 15);
+                const float v = (KIND == kGateUp) ? silu_mul(acc[mi][ni][i], acc[mi][ni + 2][i]) : acc[mi][ni][i];
+                stg[lr * W + ((((lc >> 3) ^ (lr >> 2)) & SM) << 3) + (lc & 7)] = (uint16_t)bf16_rne(v);
             }
+        }
+    }
+    // the LDS unit keeps one wavefront's accesses in order; this keeps the compiler from moving
+    // the 16-byte reads (another type than the 2-byte writes) above them
+    asm volatile("" ::: "memory");
+    const int colbase = (KIND == kGateUp) ? nt * HALF + (wc >> 1) * 64 + (wc & 1) * 32 : nt * BN + wc * 64;
+    uint16_t* out = static_cast<uint16_t*>(g.out);
+#pragma unroll
+    for (int it = 0; it < 128 * (W / 8) / 64; ++it) {
+        const int q = it * 64 + lane, lr = q / (W / 8), c8 = q % (W / 8);
+        const int tr = ((lr >> 4) * 2 + wr) * 16 + (lr & 15);  // row within the block tile
+        const int row = r0 + tr;
+        if ((tr >> 4) >= nsub || row >= r1) continue;
+        const uint4 v = *reinterpret_cast<const uint4*>(&stg[lr * W + (((c8 ^ (lr >> 2)) & SM) << 3)]);
+        const int col = colbase + c8 * 8;
+        if (KIND == kGateUp) {
+            if (g.hid_packed) {  // tile row tr, stage col / 32, chunk (col / 8) % 4 in its slot
+                const size_t blk = size_t(item / ncols) * (g.F / BKS) + (col >> 5);
+                *reinterpret_cast<uint4*>(&out[blk * 8192 + tr * 32 + ((((col >> 3) & 3) ^ ((tr >> 1) & 3)) << 3)]) = v;
+            } else {
+                *reinterpret_cast<uint4*>(&out[size_t(row) * g.F + col]) = v;
+            }
+        } else if (col < g.N) {
+            *reinterpret_cast<uint4*>(&out[size_t(row) * g.N + col]) = v;
         }
     }
 }
