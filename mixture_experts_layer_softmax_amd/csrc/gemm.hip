@@ -639,29 +639,49 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_prefill_nvfp4_kernel(GemmArgs
 #undef MOE_MFMA
 
     const float gs = g.gscale ? g.gscale[e] : 1.0f;
+    // Epilogue through LDS, as in the bf16 kernel, in two rounds of 64 tile rows (the ring's
+    // activation arrays hold a 64-row slice of every wavefront's output: W columns of bf16,
+    // at most 16 KiB): write the slice in the MFMA layout, read it back as 16-byte row chunks.
+    block_barrier();
+    constexpr int W = (KIND == kGateUp ? NB / 2 : NB) * 16;  // columns per wavefront
+    constexpr int SM = W / 8 - 1;
+    static_assert(64 * W * 2 * (NW / 4) <= 16384, "a 64-row slice per wavefront fits its array");
+    uint16_t* const stg = reinterpret_cast<uint16_t*>(
+        (wave & 3) == 0 ? sA0 : (wave & 3) == 1 ? sA1 : (wave & 3) == 2 ? sA2 : sA3) + (wave >> 2) * 64 * W;
     uint16_t* out = static_cast<uint16_t*>(g.out);
 #pragma unroll
-    for (int mi = 0; mi < 8; ++mi) {
-        if (mi * 2 + wr >= nsub) continue;
+    for (int half = 0; half < 2; ++half) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = r0 + (mi * 2 + wr) * 16 + 4 * (lane >> 4) + i;
-            if (row >= r1) continue;
-            if (KIND == kGateUp) {
+        for (int m4 = 0; m4 < 4; ++m4) {
+            const int mi = 4 * half + m4;
+            if (mi * 2 + wr >= nsub) continue;
 #pragma unroll
-                for (int ni = 0; ni < NB / 2; ++ni) {
-                    const int col = gcol + ni * 16 + (lane & 15);
-                    out[size_t(row) * g.F + col] =
-                        (uint16_t)bf16_rne(silu_mul(acc[mi][ni][i] * gs, acc[mi][ni + NB / 2][i] * gs));
-                }
-            } else {
+            for (int i = 0; i < 4; ++i) {
+                const int lr = m4 * 16 + 4 * (lane >> 4) + i;
 #pragma unroll
-                for (int ni = 0; ni < NB; ++ni) {
-                    const int col = gcol + ni * 16 + (lane & 15);
-                    if (col < g.N) out[size_t(row) * g.N + col] = (uint16_t)bf16_rne(acc[mi][ni][i] * gs);
+                for (int ni = 0; ni < W / 16; ++ni) {
+                    const int lc = ni * 16 + (lane & 15);
+                    const float v = (KIND == kGateUp) ? silu_mul(acc[mi][ni][i] * gs, acc[mi][ni + NB / 2][i] * gs)
+                                                      : acc[mi][ni][i] * gs;
+                    stg[lr * W + ((((lc >> 3) ^ (lr >> 2)) & SM) << 3) + (lc & 7)] = (uint16_t)bf16_rne(v);
                 }
             }
         }
+        asm volatile("" ::: "memory");  // reads of another type after the writes (one wavefront: in order)
+#pragma unroll
+        for (int it = 0; it < W / 8; ++it) {
+            const int q = it * 64 + lane, lr = q / (W / 8), c8 = q % (W / 8);
+            const int mi = 4 * half + (lr >> 4);
+            const int row = r0 + (mi * 2 + wr) * 16 + (lr & 15);
+            if (mi * 2 + wr >= nsub || row >= r1) continue;
+            const uint4 v = *reinterpret_cast<const uint4*>(&stg[lr * W + (((c8 ^ (lr >> 2)) & SM) << 3)]);
+            const int col = gcol + c8 * 8;
+            if (KIND == kGateUp)
+                *reinterpret_cast<uint4*>(&out[size_t(row) * g.F + col]) = v;
+            else if (col < g.N)
+                *reinterpret_cast<uint4*>(&out[size_t(row) * g.N + col]) = v;
+        }
+        asm volatile("" ::: "memory");  // the next round's writes after these reads
     }
 }
 
