@@ -294,25 +294,49 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_mxfp8_kernel(GemmArgs g) 
 #undef MOE_MXREAD
 #undef MOE_MXMFMA
 
+    // Epilogue through LDS (as in the bf16 kernel): once every wavefront is past its last
+    // fragment read, each stages a 64-row slice of its output (W bf16 columns, chunk slots
+    // XOR-swizzled by row) in half of one activation ring array, in two rounds, and stores the
+    // slice as 16-byte row chunks.
+    block_barrier();
+    constexpr int W = (KIND == kGateUp) ? 32 : 64;  // columns per wavefront
+    constexpr int SM = W / 8 - 1;
+    uint16_t* const stg = reinterpret_cast<uint16_t*>(
+        (wave & 3) == 0 ? sA0 : (wave & 3) == 1 ? sA1 : (wave & 3) == 2 ? sA2 : sA3) + (wave >> 2) * 64 * W;
+    const int colbase = (KIND == kGateUp) ? nt * HALF + 64 * (wc >> 1) + 32 * (wc & 1) : nt * BN + wc * 64;
     uint16_t* out = static_cast<uint16_t*>(g.out);
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-        if (mi * 2 + wr >= nsub) continue;
+    for (int half = 0; half < 2; ++half) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int row = r0 + (mi * 2 + wr) * 32 + 8 * (i / 4) + 4 * g2 + (i % 4);
-            if (row >= r1) continue;
-            if (KIND == kGateUp) {
-                const int col = nt * HALF + 64 * (wc >> 1) + 32 * (wc & 1) + (lane & 31);
-                out[size_t(row) * g.F + col] = (uint16_t)bf16_rne(silu_mul(acc[mi][0][i], acc[mi][1][i]));
-            } else {
+        for (int m2 = 0; m2 < 2; ++m2) {
+            const int mi = 2 * half + m2;
+            if (mi * 2 + wr >= nsub) continue;
 #pragma unroll
-                for (int ni = 0; ni < 2; ++ni) {
-                    const int col = nt * BN + wc * 64 + ni * 32 + (lane & 31);
-                    if (col < g.N) out[size_t(row) * g.N + col] = (uint16_t)bf16_rne(acc[mi][ni][i]);
+            for (int i = 0; i < 16; ++i) {
+                const int lr = m2 * 32 + 8 * (i / 4) + 4 * g2 + (i % 4);
+#pragma unroll
+                for (int ni = 0; ni < W / 32; ++ni) {
+                    const int lc = ni * 32 + (lane & 31);
+                    const float v = (KIND == kGateUp) ? silu_mul(acc[mi][0][i], acc[mi][1][i]) : acc[mi][ni][i];
+                    stg[lr * W + ((((lc >> 3) ^ (lr >> 2)) & SM) << 3) + (lc & 7)] = (uint16_t)bf16_rne(v);
                 }
             }
         }
+        asm volatile("" ::: "memory");  // reads of another type after the writes (one wavefront: in order)
+#pragma unroll
+        for (int it = 0; it < W / 8; ++it) {
+            const int q = it * 64 + lane, lr = q / (W / 8), c8 = q % (W / 8);
+            const int mi = 2 * half + (lr >> 5);
+            const int row = r0 + (mi * 2 + wr) * 32 + (lr & 31);
+            if (mi * 2 + wr >= nsub || row >= r1) continue;
+            const uint4 v = *reinterpret_cast<const uint4*>(&stg[lr * W + (((c8 ^ (lr >> 2)) & SM) << 3)]);
+            const int col = colbase + c8 * 8;
+            if (KIND == kGateUp)
+                *reinterpret_cast<uint4*>(&out[size_t(row) * g.F + col]) = v;
+            else if (col < g.N)
+                *reinterpret_cast<uint4*>(&out[size_t(row) * g.N + col]) = v;
+        }
+        asm volatile("" ::: "memory");  // the next round's writes after these reads
     }
 }
 
