@@ -14,7 +14,7 @@
 namespace moe {
 
 template <bool BF16>
-__global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y_perm,
+__global__ __launch_bounds__(512) void combine_kernel(const void* __restrict__ y_perm,
                                                       const int32_t* __restrict__ inv_perm,
                                                       const float* __restrict__ w,
                                                       void* __restrict__ y, int k, int H, int A) {
@@ -85,7 +85,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
 hipError_t launch_combine(const void* y_perm, const int32_t* inv_perm, const float* w, void* y,
                           int T, int k, int H, int A, bool bf16, hipStream_t s) {
     const int nv = bf16 ? H / 8 : H / 4;
-    const int threads = nv >= 256 ? 256 : ((nv + 63) / 64) * 64;
+    // one 16-byte vector per thread up to H = 4096 (bf16): kernel trace, median us, 256 -> 512
+    // threads: 4096-token prefill 58.4 -> 55.7, 64-token decode 6.1 -> 5.0
+    const int threads = nv >= 512 ? 512 : ((nv + 63) / 64) * 64;
     if (bf16)
         hipLaunchKernelGGL((combine_kernel<true>), dim3(T), dim3(threads), 0, s, y_perm, inv_perm, w,
                            y, k, H, A);
