@@ -93,6 +93,39 @@ def test_mx_quantizer_hand_values():
     assert O.mx_quantize(v)[0][1] == 0x79
 
 
+@pytest.mark.parametrize("wdt", ["mxfp8", "mxfp4"])
+def test_mx_down_projection_quantizes_the_bf16_hid(wdt):
+    """The MX layer's down projection quantizes hid as the layer's bf16 activation (the same
+    input moe_quantize_mxfp8 takes), not the exact value.  Hand-worked: a block whose only
+    non-zero element is 272.5 has amax in [256, 512), so X = 0.  Exactly, 272.5 lies above the
+    E4M3 midpoint 272 of 256 and 288 and rounds to 288 (code 0x79); rounded to bf16 first (8
+    significant bits, step 2 at 2^8) it becomes 272, the midpoint itself, which goes to the
+    even code 0x78 = 256.  With W2 one-hot (MXFP8: 1.0 = E4M3 256 (0x78) at scale 2^-8; MXFP4:
+    E2M1 4.0 (code 6) at scale 2^-2) the quantized hid element reads straight back as the output."""
+    H = F = 64
+    w = np.zeros((H, F), np.float32)
+    w[np.arange(H), np.arange(H)] = 1.0                # y[h] = MX(hid)[h]
+    if wdt == "mxfp8":
+        codes, scales = synth.quantize_mxfp8(w)
+        assert codes[0, 0] == 0x78 and scales[0, 0] == 119
+    else:
+        codes, scales = synth.quantize_mxfp4(w)
+        assert codes[0, 0] & 15 == 6 and scales[0, 0] == 125
+    inputs = dict(w2=codes[None], w2_scale=scales[None])
+    hid = np.zeros((2, F))
+    hid[0, 0] = 272.5                                  # the reading decides this code
+    hid[1, 0] = 272.0 + 2.0 ** -20                     # both readings: bf16 272 -> 256 as well
+    hid[:, 32] = 3.0                                   # second block: exactly representable
+    y = O.down_rows(inputs, wdt, H, hid, np.zeros(2, np.int32))
+    assert y[0, 0] == 256.0 and y[1, 0] == 256.0
+    assert np.all(y[:, 32] == 3.0)
+    rest = np.ones(H, bool)
+    rest[[0, 32]] = False
+    assert np.all(y[:, rest] == 0.0)
+    # the exact value would have given 288: what the quantizer does to the unrounded 272.5
+    assert O.mx_quantize(np.r_[272.5, np.zeros(31)])[2][0] == 288.0
+
+
 def test_mx_quantizer_matches_numpy_reference_on_wide_ranges():
     rng = np.random.default_rng(21)
     n = 32 * 512
