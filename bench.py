@@ -1,13 +1,15 @@
 """Benchmark of the MoE layer forward pass on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload nvfp4_prefill]
 
 A step is one ``moe_forward`` call (router -> dispatch -> gate/up GEMM + SwiGLU -> down GEMM
 -> combine) over one batch of seeded synthetic inputs already resident in HBM.  The default
-workload is the prefill-shaped layer (4096 tokens, hidden 4096, 128 experts, top-8, expert FFN
-1536, bf16, router bias N(0,1)); ``--workload`` selects another one (tiny, decode1, decode8,
-decode64, nvfp4_decode, nvfp4_prefill, prefill6000, mxfp8_prefill, mxfp4_prefill).  Prints one
-JSON line.
+workload is the largest single-GPU layer: 8192 tokens, hidden 4096, 256 experts, top-8, expert
+FFN 2048, 4-bit E2M1 weights with one E4M3 scale per 16 (decoded exactly to bf16 for the bf16
+matrix cores), bf16 activations, router bias on a 10 % hot set that receives half of the
+assignments.  ``--workload`` selects another one (tiny, prefill, decode1, decode8, decode64,
+nvfp4_decode, prefill6000, mxfp8_prefill, mxfp4_prefill, mxfp8_decode64, mxfp4_decode64).
+Prints one JSON line.
 
 Shapes of "Hosting Qwen on Blackwell" (sections Prefill, Expert Parallel and the grouped MoE
 GEMM benchmark there):
@@ -21,15 +23,16 @@ GEMM benchmark there):
         through moe_grouped_gemm on E/N experts (hidden 4096, expert ffn 1536, bf16), one row
         each; reports the latency of the pair.
 
-Timing: W untimed steps, then K steps between two events on the launch stream.  Workloads
-whose selected weights are small enough to stay cached between steps (under 1.5 GiB) read a
-1 GiB buffer before every timed step and time each step with its own event pair, so that
-weights come from HBM; the flush is outside the timed intervals (``--flush-mode write``
-overwrites the buffer instead, for comparison).
+Timing: W untimed steps, then K steps bracketed by a device synchronisation on both sides,
+with an event recorded on the launch stream before and after every step, so that the line
+carries the mean (``ms_per_step``, whole bracket / K) and the per-step median, p10 and p90.
+Workloads whose selected weights are small enough to stay cached between steps (under 1.5 GiB)
+read a 1 GiB buffer before every timed step, outside the step's event pair, so that weights
+come from HBM (``--flush-mode write`` overwrites the buffer instead, for comparison).
 
-Besides the step time it measures, with events on the same stream, the average duration of
-the dominant kernel (the gate/up grouped GEMM, launched alone through ``moe_grouped_gemm`` on
-the same routing) and reports it against the MI355X roofline.  ``traffic`` (HBM bytes per
+Besides the step time it measures, with an event pair per launch on the same stream, the
+duration of the dominant kernel (the gate/up grouped GEMM, launched alone through
+``moe_grouped_gemm`` on the same routing, K times) and reports it against the MI355X roofline.  ``traffic`` (HBM bytes per
 launch of that kernel) comes from the counter summary under profiles/ when it was taken on the
 current kernel source, else null.  The CPU oracle is timed on a bounded sub-batch of the same
 workload as a reported baseline.
@@ -83,12 +86,12 @@ def layer_work(wl, active: int, rows: int):
 
 def gate_up_work(wl, active: int, rows: int, tokens_read: int):
     """Algorithmic FLOPs and bytes of one gate/up grouped-GEMM launch over `rows` dispatched
-    rows: the active experts' gate/up weights once, each token row it reads once, the hid
-    output once."""
+    rows: the active experts' gate/up weights once and each token row it reads once.  The hid
+    it writes is an intermediate of the layer and is not counted, as in layer_work."""
     act = 4 if wl.act == "f32" else 2
     flops = 4.0 * wl.hidden * wl.ffn * rows
     nbytes = (active * 2.0 * wl.ffn * wl.hidden * bytes_per_weight(wl.wdt)
-              + tokens_read * wl.hidden * act + rows * wl.ffn * act)
+              + tokens_read * wl.hidden * act)
     return flops, nbytes
 
 
@@ -162,9 +165,29 @@ def measured_peaks(torch, lib):
                        "read stream over 4 GiB" % (8 * cus))
 
 
+def percentile(v, q):
+    """Linear-interpolated percentile q (0..100) of the list v."""
+    v = sorted(v)
+    if not v:
+        return None
+    x = (len(v) - 1) * q / 100.0
+    i = int(x)
+    j = min(i + 1, len(v) - 1)
+    return v[i] + (v[j] - v[i]) * (x - i)
+
+
+def step_stats(per_step):
+    """Mean, median, p10 and p90 (ms) of a list of per-call durations (ms)."""
+    return dict(mean=sum(per_step) / len(per_step), median=percentile(per_step, 50),
+                p10=percentile(per_step, 10), p90=percentile(per_step, 90), n=len(per_step))
+
+
 def make_timer(torch, lib, flush: bool, flush_mode: str):
-    """timed(fn, steps) -> mean ms per call of fn on the current stream.  With `flush`, caches
-    are evicted before every call (outside its timed interval)."""
+    """timed(fn, steps) -> dict(mean, median, p10, p90, n) in ms per call of fn on the current
+    stream, from an event recorded before and after every call.  Without `flush` the calls run
+    back to back (event i+1 both ends call i and starts call i+1, so the mean is the whole
+    bracket over the calls); with `flush` caches are evicted before every call, outside its
+    event pair."""
     scratch = torch.ones(2 ** 30, dtype=torch.uint8, device="cuda:0") if flush else None
     scratch_word = torch.zeros(1, dtype=torch.int32, device="cuda:0")
 
@@ -179,13 +202,16 @@ def make_timer(torch, lib, flush: bool, flush_mode: str):
 
     def timed(fn, steps):
         if not flush:
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(steps):
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+            evs[0].record()
+            for i in range(steps):
                 fn()
-            e1.record()
+                evs[i + 1].record()
             torch.cuda.synchronize()
-            return e0.elapsed_time(e1) / steps
+            per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+            out = step_stats(per)
+            out["mean"] = evs[0].elapsed_time(evs[steps]) / steps
+            return out
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(steps)]
         for a, b in evs:
@@ -194,9 +220,60 @@ def make_timer(torch, lib, flush: bool, flush_mode: str):
             fn()
             b.record()
         torch.cuda.synchronize()
-        return sum(a.elapsed_time(b) for a, b in evs) / steps
+        return step_stats([a.elapsed_time(b) for a, b in evs])
 
     return timed
+
+
+def _find_clocks(d):
+    """The gfx / memory clock entries (current, min, max; MHz) anywhere in amd-smi's JSON."""
+    if isinstance(d, list):
+        for v in d:
+            c = _find_clocks(v)
+            if c:
+                return c
+        return None
+    if not isinstance(d, dict):
+        return None
+    if "gfx_0" in d or "mem_0" in d:
+        out = {}
+        for key in ("gfx_0", "mem_0", "fclk_0", "socclk_0"):
+            v = d.get(key)
+            if isinstance(v, dict):
+                out[key] = {f: (v[f].get("value") if isinstance(v[f], dict) else v[f])
+                            for f in ("clk", "min_clk", "max_clk") if f in v}
+        return out
+    for v in d.values():
+        c = _find_clocks(v)
+        if c:
+            return c
+    return None
+
+
+def platform_info(torch):
+    """ROCm / HIP versions, the device name, and the GPU clocks as amd-smi reports them (a child
+    process; None where the tool is missing or says nothing parseable)."""
+    import subprocess
+
+    info = dict(hip=getattr(torch.version, "hip", None), torch=torch.__version__)
+    try:
+        info["rocm"] = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        info["rocm"] = None
+    try:
+        info["device"] = torch.cuda.get_device_name(0)
+    except Exception:  # pragma: no cover
+        info["device"] = None
+    clocks = None
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-g", "0", "--clock", "--json"], capture_output=True,
+                           text=True, timeout=30)
+        if r.returncode == 0 and r.stdout.strip():
+            clocks = _find_clocks(json.loads(r.stdout))
+    except (OSError, ValueError, subprocess.SubprocessError):
+        clocks = None
+    info["clocks_mhz"] = clocks
+    return info
 
 
 def bench_grouped1(args) -> int:
@@ -240,9 +317,12 @@ def bench_grouped1(args) -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ms = timed(step, args.steps)
+    st = timed(step, args.steps)
+    torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    ms = st["mean"]
     nbytes = w_bytes + n * (H + F + F + H) * 2.0  # weights once; x, hid out/in, y_perm out
     flops = n * 6.0 * H * F
     gbs = nbytes / (ms * 1e-3) / 1e9
@@ -255,6 +335,7 @@ def bench_grouped1(args) -> int:
         roof["frac_measured"] = gbs / peaks["hbm_read_gbs"]
     out = dict(metric="grouped MoE GEMM latency, every expert given one token", value=ms * 1e3,
                unit="us", n_gpus=1, steps=args.steps, warmup=args.warmup, ms_per_step=ms,
+               step_ms=dict(median=st["median"], p10=st["p10"], p90=st["p90"]),
                higher_is_better=False, scaling="weak", vs_baseline=None, dtype="bf16",
                data="synthetic (seeded)",
                config=dict(workload="grouped1: one token for each of %d experts (rank %d of %d "
@@ -284,7 +365,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="prefill")
+    ap.add_argument("--workload", default="nvfp4_prefill")
     ap.add_argument("--flush", choices=("auto", "on", "off"), default="auto")
     ap.add_argument("--flush-mode", choices=("read", "write"), default="read",
                     help="evict caches by reading (default) or by writing a 1 GiB buffer")
@@ -314,7 +395,12 @@ def main() -> int:
     from mixture_experts_layer_softmax_amd import lib, synth
     from mixture_experts_layer_softmax_amd.layer import MoELayer
 
+    if args.workload not in synth.WORKLOADS:
+        print("unknown workload %r (one of: %s, grouped1)" % (args.workload, ", ".join(synth.WORKLOADS)),
+              file=sys.stderr)
+        return 2
     wl = synth.WORKLOADS[args.workload]
+    plat = platform_info(torch)
     held = None
     if args.ep_size > 1:
         if wl.experts % args.ep_size:
@@ -349,12 +435,14 @@ def main() -> int:
     for _ in range(args.warmup):
         layer.forward(x, y=y)
     torch.cuda.synchronize()
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ms_per_step = timed(lambda: layer.forward(x, y=y), args.steps)
+    steps = timed(lambda: layer.forward(x, y=y), args.steps)
+    torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    ms_per_step = steps["mean"]
 
-    # the dominant kernel alone: gate/up grouped GEMM on the same routing, same stream
+    # the dominant kernel alone: gate/up grouped GEMM on the same routing, same stream, one event
+    # pair per launch (each launch also runs the ~5 us tile-list kernel first)
     p = layer.problem_for(wl.tokens)
     ws = layer.workspace(wl.tokens)
     hid = layer.empty_act(wl.assignments, wl.ffn)
@@ -363,7 +451,9 @@ def main() -> int:
     for _ in range(2):
         gemm1()
     torch.cuda.synchronize()
-    gemm1_ms = timed(gemm1, args.steps)  # includes the ~5 us tile-list kernel it launches first
+    print("[bench] dominant kernel, %d launches" % args.steps, file=sys.stderr, flush=True)
+    g1 = timed(gemm1, args.steps)
+    gemm1_ms = g1["mean"]
 
     peaks = None if args.no_probes else measured_peaks(torch, lib)
 
@@ -393,12 +483,15 @@ def main() -> int:
     roof["kernel"] = "grouped gate/up GEMM + SwiGLU (%s weights%s)" % (
         wl.wdt, ", input quantization included" if wl.wdt.startswith("mx") else "")
     roof["kernel_ms"] = gemm1_ms
+    roof["kernel_ms_median"] = g1["median"]
     roof["algorithmic_bytes"] = gbytes
     roof["algorithmic_flops"] = gflops
 
     tok_s = wl.tokens / (ms_per_step * 1e-3)
     out = dict(metric=METRIC, value=tok_s, unit="tokens/s", n_gpus=1, steps=args.steps,
-               warmup=args.warmup, ms_per_step=ms_per_step, higher_is_better=True,
+               warmup=args.warmup, ms_per_step=ms_per_step,
+               step_ms=dict(median=steps["median"], p10=steps["p10"], p90=steps["p90"]),
+               tokens_per_s_median=wl.tokens / (steps["median"] * 1e-3), higher_is_better=True,
                scaling="weak", vs_baseline=None,
                dtype={"mxfp8": "fp8", "mxfp4": "fp8 x fp4"}.get(wl.wdt, wl.act),
                data="synthetic (seeded)",
@@ -410,7 +503,7 @@ def main() -> int:
                layer_tflops=flops / (ms_per_step * 1e-3) / 1e12,
                layer_mfma_frac=flops / (ms_per_step * 1e-3) / peak_mfma,
                layer_hbm_frac=nbytes / (ms_per_step * 1e-3) / PEAK_HBM_BYTES,
-               wall_s=wall, roofline=roof)
+               wall_s=wall, roofline=roof, platform=plat)
     if peaks:
         out["measured_peaks"] = peaks
         if not wl.wdt.startswith("mx"):

@@ -35,8 +35,8 @@
  *    MOE_ERR_UNSUPPORTED for shapes with no compiled kernel (H % 64, F % 64 != 0; bf16
  *    weights with H % 256 or F % 128 != 0; MXFP8 with H % 512 or F % 512 != 0; bf16
  *    activations with fp32 weights or the reverse; NVFP4 or MXFP8 with fp32 activations), and
- *    MOE_ERR_INVALID_ARGUMENT for weights not in
- *    the layout their dtype requires (moe_layout);
+ *    MOE_ERR_INVALID_ARGUMENT for an unknown weight layout or PACKED fp32 weights
+ *    (moe_layout);
  *    MOE_ERR_WORKSPACE_TOO_SMALL; MOE_ERR_DEVICE when a launch reports an error.
  *  - T = 0 is a successful no-op (token-sized buffers and the workspace may then be NULL;
  *    moe_permute and moe_forward still set counts/offsets, when given, to zero).
@@ -86,14 +86,14 @@ typedef enum {
  * [-127, 127]) and elements v / 2^X clamped to +-448 and rounded to the nearest E4M3 value,
  * ties to the even code (sign kept); the GEMMs multiply on the block-scaled fp8 matrix cores
  * with fp32 accumulation.  Outputs (hid, y_perm, y) stay bf16.  Needs H % 512 == 0 and
- * F % 512 == 0, bf16 activations; the E4M3 codes are PACKED (moe_layout), the E8M0 scales
- * row-major.
+ * F % 512 == 0, bf16 activations; the E4M3 codes row-major or PACKED (moe_layout), the E8M0
+ * scales row-major.
  * MOE_MXFP4 (weights only; OCP MX v1.0 with E2M1 elements, which "Hosting Qwen on Blackwell"
  * evaluates beside MXFP8): two E2M1 values per byte, even element in the low nibble, one E8M0
  * scale per 32 along the input dimension: w = e2m1 * 2^(s - 127).  Activations run in MXFP8
  * exactly as for MOE_MXFP8; the GEMMs multiply fp8 activations by fp4 weights on the
- * block-scaled matrix cores.  Same shape rules; codes PACKED (the 4-bit variant below), scales
- * row-major. */
+ * block-scaled matrix cores.  Same shape rules; codes row-major or PACKED (the 4-bit variant
+ * below), scales row-major. */
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_NVFP4 = 2, MOE_MXFP8 = 3, MOE_MXFP4 = 4 } moe_dtype;
 
 typedef enum { MOE_GEMM_GATE_UP_SWIGLU = 0, MOE_GEMM_DOWN = 1 } moe_gemm_kind;
@@ -135,13 +135,17 @@ typedef struct {
  * Rows of hid, y_perm and x_perm past A_local are unspecified.  expert_begin = local_experts =
  * 0 (a zero-initialised struct) is the single-GPU layer. */
 
-/* Weight layouts.  bf16 expert weights and MXFP8 codes are consumed in the PACKED layout
- * written by moe_pack_weights; fp32 expert weights in the ROW_MAJOR layout described below
- * (MXFP8 scales stay row-major).  NVFP4 weights are accepted in either layout: ROW_MAJOR
- * (bytes and E4M3 scales as described in moe_expert_weights, any shape the problem rules
- * allow) or PACKED (bytes by moe_pack_weights and scales by moe_pack_scales, both packed;
- * needs H % 256 == 0 and F % 128 == 0).  Both give the same layer; PACKED is read with whole
- * cache lines by the decode and prefill kernels.
+/* Weight layouts.  Every weight format is accepted ROW_MAJOR, the dense [E,2F,H] / [E,H,F]
+ * layouts described in moe_expert_weights (MX and NVFP4: bytes [E,2F,H/2] ... for 4-bit
+ * codes, scales always row-major unless noted).  bf16, MXFP8 and MXFP4 weights are also
+ * accepted PACKED (written once by moe_pack_weights), and NVFP4 weights PACKED (bytes by
+ * moe_pack_weights and scales by moe_pack_scales, both packed; needs H % 256 == 0 and
+ * F % 128 == 0).  fp32 weights are ROW_MAJOR only.  Both layouts give bit-identical layers on
+ * the bf16 and MX kernels (the same values reach the same LDS image or operand registers in
+ * the same order) and on the NVFP4 prefill kernels; the NVFP4 decode kernels take K in another
+ * order for each layout (results within the tolerance of each other).  PACKED is the fast
+ * path: a stage of a 256-row tile is one contiguous block, where ROW_MAJOR reads 16 to 64
+ * bytes per weight row and stage, one cache line of each of many rows per load instruction.
  *
  * PACKED (bf16 and MXFP8 codes; needs H % 256 == 0 and F % 128 == 0; same byte size as
  * row-major): weights are cut into tiles of 256 weight rows and stages of 64 bytes of a row
@@ -164,13 +168,13 @@ typedef struct {
 typedef enum { MOE_LAYOUT_ROW_MAJOR = 0, MOE_LAYOUT_PACKED = 1 } moe_layout;
 
 typedef struct {
-    const void* w13;              /* [E,2F,H] fp32, packed bf16 / MXFP8 codes; NVFP4 bytes [E,2F,H/2]; packed MXFP4 */
-    const void* w2;               /* [E,H,F] fp32, packed bf16 / MXFP8 codes; NVFP4 bytes [E,H,F/2]; packed MXFP4 */
+    const void* w13;              /* [E,2F,H] fp32 / bf16 / MXFP8 codes; NVFP4, MXFP4 bytes [E,2F,H/2]; or PACKED */
+    const void* w2;               /* [E,H,F] fp32 / bf16 / MXFP8 codes; NVFP4, MXFP4 bytes [E,H,F/2]; or PACKED */
     const uint8_t* w13_scale;     /* NVFP4: E4M3 [E,2F,H/16]; MXFP8, MXFP4: E8M0 [E,2F,H/32] */
     const uint8_t* w2_scale;      /* NVFP4: E4M3 [E,H,F/16]; MXFP8, MXFP4: E8M0 [E,H,F/32] */
     const float* w13_gscale;      /* NVFP4 only, nullable (=> 1.0): fp32 [E] */
     const float* w2_gscale;       /* NVFP4 only, nullable (=> 1.0): fp32 [E] */
-    int32_t layout;               /* moe_layout: PACKED for bf16 and MX, ROW_MAJOR for fp32, either for NVFP4 */
+    int32_t layout;               /* moe_layout: ROW_MAJOR (any format) or PACKED (bf16, MX, NVFP4) */
 } moe_expert_weights;
 
 /* Text of a status code (static storage). */

@@ -137,15 +137,11 @@ bool nvfp4_packable(const moe_problem& p) { return p.hidden % 256 == 0 && p.ffn 
 
 moe_status check_weights(const moe_problem& p, const moe_expert_weights* w) {
     if (!w || !w->w13 || !w->w2 || !aligned(w->w13) || !aligned(w->w2)) return MOE_ERR_INVALID_ARGUMENT;
-    if (p.w_dtype == MOE_NVFP4) {
-        if (w->layout != MOE_LAYOUT_ROW_MAJOR && w->layout != MOE_LAYOUT_PACKED)
-            return MOE_ERR_INVALID_ARGUMENT;
-        if (w->layout == MOE_LAYOUT_PACKED && !nvfp4_packable(p)) return MOE_ERR_UNSUPPORTED;
-    } else {
-        const bool packed = p.w_dtype == MOE_BF16 || is_mx(p);
-        if (w->layout != (packed ? MOE_LAYOUT_PACKED : MOE_LAYOUT_ROW_MAJOR))
-            return MOE_ERR_INVALID_ARGUMENT;
-    }
+    // every format is accepted row-major; bf16, MX and NVFP4 weights also in the PACKED layout
+    // (fp32 weights are row-major only)
+    if (w->layout != MOE_LAYOUT_ROW_MAJOR && w->layout != MOE_LAYOUT_PACKED) return MOE_ERR_INVALID_ARGUMENT;
+    if (w->layout == MOE_LAYOUT_PACKED && p.w_dtype == MOE_F32) return MOE_ERR_INVALID_ARGUMENT;
+    if (w->layout == MOE_LAYOUT_PACKED && p.w_dtype == MOE_NVFP4 && !nvfp4_packable(p)) return MOE_ERR_UNSUPPORTED;
     if (is_mx(p)) {
         if (!w->w13_scale || !w->w2_scale || !aligned(w->w13_scale) || !aligned(w->w2_scale))
             return MOE_ERR_INVALID_ARGUMENT;
@@ -188,7 +184,7 @@ GemmArgs gemm_args(const moe_problem& p, int kind, const void* a, const int32_t*
     g.F = p.ffn;
     g.kind = kind;
     g.wfmt = wfmt_of(p);
-    g.wpacked = p.w_dtype == MOE_NVFP4 && w.layout == MOE_LAYOUT_PACKED;
+    g.wpacked = w.layout == MOE_LAYOUT_PACKED;
     const int A = p.num_tokens * p.top_k;
     if (kind == kGateUp) {
         g.K = p.hidden;

@@ -48,7 +48,8 @@ struct GemmArgs {
     const int* tile_count;
     const void* w;          // [E, Nw, K] values or [E, Nw, K/2] packed nibbles
     const uint8_t* wscale;  // [E, Nw, K/16] (NVFP4) or [E, Nw, K/32] (MXFP8)
-    int wpacked;            // NVFP4: bytes and scales in the PACKED layout (tile/stage blocks)
+    int wpacked;            // weights (NVFP4: bytes and scales) in the PACKED layout (tile/stage
+                            // blocks); 0: row-major
     int hid_packed;         // bf16 prefill inside moe_forward: gate/up writes hid and down reads
                             // it as [tile][stage] blocks of 256 rows x 64 bytes (the weights' image)
     const uint8_t* ascale;  // MXFP8: E8M0 scales of `a` [rows, K/32] (a holds E4M3 codes)

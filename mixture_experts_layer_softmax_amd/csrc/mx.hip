@@ -171,12 +171,23 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_mxfp8_kernel(GemmArgs g) 
     const char* const wblk = static_cast<const char*>(g.w) + (size_t(e) * ncols + nt) * size_t(nk) * (BN * BCH * 16);
     const char* pa[2];
     const char* pb[2];
+    // weights: packed (one contiguous (tile, stage) block per stage, the LDS image), or row-major
+    // (each lane fetches the chunk of its weight row that belongs in its LDS slot: 64 fp8 or 32
+    // fp4 bytes per row and stage; the same LDS image, so bit-identical results)
+    const size_t wst = g.wpacked ? size_t(BN) * BCH * 16 : BCH * 16;  // bytes per stage
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int row = (i * 8 + wave) * 16 + (lane >> 2);
         const int ch = (lane & 3) ^ ((row >> 1) & 3);
         pa[i] = static_cast<const char*>(g.a) + size_t(act_row(row)) * K + ch * 16;
-        pb[i] = wblk + (BF4 ? wave : i * 8 + wave) * 1024 + lane * 16;
+        if (g.wpacked) {
+            pb[i] = wblk + (BF4 ? wave : i * 8 + wave) * 1024 + lane * 16;
+        } else if (BF4) {  // 32 rows of 32 bytes per wavefront: lane l -> row 32 wave + l / 2, slot l & 1
+            const int r4 = wave * 32 + (lane >> 1), c4 = (lane & 1) ^ ((r4 >> 2) & 1);
+            pb[i] = static_cast<const char*>(g.w) + (size_t(e) * Nw + weight_row(r4)) * (K / 2) + c4 * 16;
+        } else {
+            pb[i] = static_cast<const char*>(g.w) + (size_t(e) * Nw + weight_row(row)) * K + ch * 16;
+        }
     }
     const char* psc;  // this lane's row of scales: 16 bytes per chunk of 8 stages
     {
@@ -197,7 +208,7 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_mxfp8_kernel(GemmArgs g) 
         _Pragma("unroll") for (int i = 0; i < 2; ++i)                                         \
             dma16(pa[i] + st_ * 64, &SA[(i * 8 + wave) * 64]);                                \
         _Pragma("unroll") for (int i = 0; i < (BF4 ? 1 : 2); ++i)                             \
-            dma16(pb[i] + size_t(st_) * (BN * BCH * 16), &SB[(i * 8 + wave) * 64]);           \
+            dma16(pb[i] + size_t(st_) * wst, &SB[(i * 8 + wave) * 64]);                       \
         if (((ST) & 7) == 0)                                                                  \
             dma16(psc + (st_ >> 3) * 16, &tS[((ST) >> 3) & 1][sc_off]);                      \
     } while (0)
@@ -402,17 +413,22 @@ __global__ __launch_bounds__(256) void gemm_decode_mx_kernel(GemmArgs g) {
     const int ntiles = (KIND == kGateUp) ? g.F / 128 : g.N / 256;
     const int Nw = (KIND == kGateUp) ? 2 * g.F : g.N;
     const uint8_t* wt = static_cast<const uint8_t*>(g.w) + (size_t(e) * ntiles + t) * nst * SBLK;
-    int off0[NG], off1[NG];
+    // packed: offsets of the lane's chunks inside a (tile, stage) block, SBLK bytes per stage;
+    // row-major: the lane's chunks of its own weight rows, 64 (fp8) or 32 (fp4) bytes per stage
+    size_t off0[NG], off1[NG];
     const uint8_t* psw[NG];
+    const size_t wst = g.wpacked ? SBLK : BCH * 16;
+    if (!g.wpacked) wt = static_cast<const uint8_t*>(g.w);
 #pragma unroll
     for (int h = 0; h < NG; ++h) {
         const int r = trow[h];
+        const size_t rm = (size_t(e) * Nw + wrow[h]) * (BF4 ? K / 2 : K);  // row-major row start
         if (BF4) {
-            off0[h] = r * 32 + ((g2 ^ ((r >> 2) & 1)) * 16);
+            off0[h] = g.wpacked ? size_t(r * 32 + ((g2 ^ ((r >> 2) & 1)) * 16)) : rm + 16 * g2;
             off1[h] = 0;
         } else {
-            off0[h] = r * 64 + ((g2 ^ ((r >> 1) & 3)) * 16);
-            off1[h] = r * 64 + (((g2 + 2) ^ ((r >> 1) & 3)) * 16);
+            off0[h] = g.wpacked ? size_t(r * 64 + ((g2 ^ ((r >> 1) & 3)) * 16)) : rm + 16 * g2;
+            off1[h] = g.wpacked ? size_t(r * 64 + (((g2 + 2) ^ ((r >> 1) & 3)) * 16)) : rm + 16 * (g2 + 2);
         }
         psw[h] = g.wscale + (size_t(e) * Nw + wrow[h]) * (K / 32);
     }
@@ -439,7 +455,7 @@ __global__ __launch_bounds__(256) void gemm_decode_mx_kernel(GemmArgs g) {
     auto load = [&](Stg& x, int st) __attribute__((always_inline)) {
         const i32x4_t lo = ld16(pa + 64 * st), hi = ld16(pa + 64 * st + 32);
         x.a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        const uint8_t* blk = wt + size_t(st) * SBLK;
+        const uint8_t* blk = wt + size_t(st) * wst;
 #pragma unroll
         for (int h = 0; h < NG; ++h) {
             x.b0[h] = ld16(blk + off0[h]);

@@ -38,11 +38,12 @@ def bf16_bits_to_f64(a: np.ndarray) -> np.ndarray:
 class MoELayer:
     def __init__(self, tokens, hidden, experts, top_k, ffn, act, wdt, inputs: dict,
                  device="cuda:0", renormalize=True, path="auto", expert_begin=0, local_experts=0,
-                 nvfp4_layout="packed"):
+                 weight_layout="packed"):
         """``inputs`` holds the weights of the held experts only when ``local_experts`` is set
-        (expert parallelism: experts [expert_begin, expert_begin + local_experts)).  NVFP4
-        weights are packed (bytes and scales) when ``nvfp4_layout`` is "packed" and the shape
-        allows it (H % 256 == 0, F % 128 == 0), else kept row-major."""
+        (expert parallelism: experts [expert_begin, expert_begin + local_experts)).  bf16 and MX
+        weights, and NVFP4 bytes and scales, are packed once (moe_pack_weights /
+        moe_pack_scales) when ``weight_layout`` is "packed" and the shape allows it (NVFP4:
+        H % 256 == 0, F % 128 == 0), else handed to the library row-major."""
         self.device = torch.device(device)
         self.T, self.H, self.E, self.k, self.F = tokens, hidden, experts, top_k, ffn
         self.act, self.wdt = act, wdt
@@ -56,7 +57,7 @@ class MoELayer:
         self.w13 = to_device(inputs["w13"], d, wk)
         self.w2 = to_device(inputs["w2"], d, wk)
         layout = lib.LAYOUT_ROW_MAJOR
-        if wdt in ("bf16", "mxfp8", "mxfp4"):  # bf16 weights and MX codes are consumed packed
+        if wdt in ("bf16", "mxfp8", "mxfp4") and weight_layout == "packed":
             p13 = torch.empty_like(self.w13)
             p2 = torch.empty_like(self.w2)
             lib.pack_weights(self.problem, self.w13, self.w2, p13, p2)
@@ -65,7 +66,7 @@ class MoELayer:
             layout = lib.LAYOUT_PACKED
         self.w13_scale = to_device(inputs.get("w13_scale"), d)
         self.w2_scale = to_device(inputs.get("w2_scale"), d)
-        if wdt == "nvfp4" and nvfp4_layout == "packed" and hidden % 256 == 0 and ffn % 128 == 0:
+        if wdt == "nvfp4" and weight_layout == "packed" and hidden % 256 == 0 and ffn % 128 == 0:
             tensors = (self.w13, self.w2, self.w13_scale, self.w2_scale)
             p13, p2, s13, s2 = (torch.empty_like(t) for t in tensors)
             lib.pack_weights(self.problem, self.w13, self.w2, p13, p2)
@@ -83,11 +84,11 @@ class MoELayer:
 
     @classmethod
     def from_workload(cls, wl, inputs, device="cuda:0", path="auto", expert_begin=0,
-                      local_experts=0, nvfp4_layout="packed"):
+                      local_experts=0, weight_layout="packed"):
         return cls(wl.tokens, wl.hidden, wl.experts, wl.top_k, wl.ffn, wl.act, wl.wdt, inputs,
                    device=device, renormalize=wl.renormalize, path=path,
                    expert_begin=expert_begin, local_experts=local_experts,
-                   nvfp4_layout=nvfp4_layout)
+                   weight_layout=weight_layout)
 
     def problem_for(self, tokens: int, path: str | None = None):
         return lib.problem(tokens, self.H, self.E, self.k, self.F, self.act, self.wdt,

@@ -1,0 +1,146 @@
+"""Summaries of rocprofv3 output for profiles/ (measurement tooling beside bench.py).
+
+    python profile_summary.py kernels RUN_DIR TAG --last K --cmd "rocprofv3 ... -- python3 bench.py ..."
+    python profile_summary.py traffic FETCH_DIR WRITE_DIR TAG WORKLOAD KERNEL SOURCE --cmd-fetch ... --cmd-write ...
+
+``kernels`` reads ``*_kernel_trace.csv`` of a ``rocprofv3 --kernel-trace`` run and writes
+``profiles/TAG_kernel_stats.md``: per kernel, every launch (what ``--stats`` prints) and the last
+K launches only.  bench.py launches each kernel of the forward K times in its timed steps after
+its warm-up, and the gate/up GEMM K more times alone (the launches its roofline figure times),
+so the last K launches of a kernel are the timed ones.
+
+``traffic`` reads the ``*_counter_collection.csv`` of two ``rocprofv3 --pmc FETCH_SIZE`` /
+``--pmc WRITE_SIZE`` runs of bench.py with ``--calibration-copy`` and writes
+``profiles/TAG_traffic.md`` and the WORKLOAD entry of ``profiles/traffic.json``: the dominant
+kernel's KiB per launch, scaled by what the same counter reads for the 512 MiB device copy at
+the end of the run, with the hash of the kernel's source file so that bench.py stops quoting
+it once the kernel changes.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def _one(pattern: str) -> str:
+    hits = sorted(glob.glob(pattern, recursive=True))
+    if not hits:
+        raise SystemExit("no file matches %s" % pattern)
+    return hits[0]
+
+
+def _short(name: str, n: int = 110) -> str:
+    return name if len(name) <= n else name[: n - 3] + "..."
+
+
+def kernels(run_dir: str, tag: str, last: int, cmd: str) -> str:
+    path = _one(os.path.join(run_dir, "**", "*kernel_trace.csv"))
+    launches = collections.defaultdict(list)  # name -> [(start, duration us)]
+    for r in csv.DictReader(open(path)):
+        t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+        launches[r["Kernel_Name"]].append((t0, (t1 - t0) / 1e3))
+    total = sum(d for v in launches.values() for _, d in v)
+    rows = []
+    for name, v in launches.items():
+        v.sort()
+        d = [x for _, x in v]
+        tail = d[-last:]
+        rows.append((sum(d), name, d, tail))
+    rows.sort(reverse=True)
+    out = ["# Kernel trace: %s" % tag, "", "Command (run from the repository root on one MI355X):", "",
+           "    " + cmd, "", "Then `python profile_summary.py kernels <run dir> %s --last %d`." % (tag, last), "",
+           "Durations in microseconds.  *All*: every launch of the run (warm-up and untimed launches "
+           "included, as `rocprofv3 --stats` counts them).  *Timed*: the last %d launches of each kernel, "
+           "which are the launches of bench.py's timed region." % last, "",
+           "| kernel | calls | all: average | timed: calls | timed: average | timed: median | timed: min | timed: max | share % |",
+           "|---|---|---|---|---|---|---|---|---|"]
+    for tot, name, d, tail in rows:
+        out.append("| `%s` | %d | %.1f | %d | %.1f | %.1f | %.1f | %.1f | %.2f |" % (
+            _short(name), len(d), sum(d) / len(d), len(tail), sum(tail) / len(tail),
+            statistics.median(tail), min(tail), max(tail), 100.0 * tot / total))
+    text = "\n".join(out) + "\n"
+    os.makedirs(PROFILES, exist_ok=True)
+    open(os.path.join(PROFILES, "%s_kernel_stats.md" % tag), "w").write(text)
+    return text
+
+
+def _per_launch(path: str):
+    agg = collections.defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        agg[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return agg
+
+
+def traffic(fetch_dir: str, write_dir: str, tag: str, workload: str, kernel: str, source: str,
+            cmd_fetch: str, cmd_write: str) -> str:
+    f = _per_launch(_one(os.path.join(fetch_dir, "**", "*counter_collection.csv")))
+    w = _per_launch(_one(os.path.join(write_dir, "**", "*counter_collection.csv")))
+    copy_f = max(f["__amd_rocclr_copyBuffer"])
+    copy_w = max(w["__amd_rocclr_copyBuffer"])
+    kf = [v for k, vs in f.items() if kernel in k for v in vs]
+    kw = [v for k, vs in w.items() if kernel in k for v in vs]
+    if not kf or not kw:
+        raise SystemExit("kernel %r not found in the counter files" % kernel)
+    copied = 512 * 1024  # KiB
+    ff, fw = copied / copy_f, copied / copy_w
+    fetch_b = sum(kf) / len(kf) * 1024 * ff
+    write_b = sum(kw) / len(kw) * 1024 * fw
+    src = os.path.join(ROOT, source)
+    h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    out = ["# HBM traffic counters: %s, %s workload" % (kernel, workload), "",
+           "Commands (one counter per run; bench.py ends with one 512 MiB device copy for calibration):", "",
+           "    " + cmd_fetch, "    " + cmd_write, "",
+           "Then `python profile_summary.py traffic <fetch dir> <write dir> %s %s '%s' %s`." % (tag, workload, kernel, source), "",
+           "| quantity | value |", "|---|---|",
+           "| calibration copy: FETCH_SIZE KiB read for 524288 KiB copied | %.1f (factor %.3f) |" % (copy_f, ff),
+           "| calibration copy: WRITE_SIZE KiB for 524288 KiB copied | %.1f (factor %.3f) |" % (copy_w, fw),
+           "| dominant kernel launches sampled | %d (fetch), %d (write) |" % (len(kf), len(kw)),
+           "| FETCH_SIZE per launch, raw KiB | %.1f |" % (sum(kf) / len(kf)),
+           "| WRITE_SIZE per launch, raw KiB | %.1f |" % (sum(kw) / len(kw)),
+           "| HBM bytes read per launch (scaled) | %.4g |" % fetch_b,
+           "| HBM bytes written per launch (scaled) | %.4g |" % write_b,
+           "| HBM bytes per launch (scaled) | %.4g |" % (fetch_b + write_b),
+           "| %s sha256 (first 16 hex) when taken | %s |" % (os.path.basename(source), h)]
+    text = "\n".join(out) + "\n"
+    open(os.path.join(PROFILES, "%s_traffic.md" % tag), "w").write(text)
+    tj = os.path.join(PROFILES, "traffic.json")
+    d = json.load(open(tj)) if os.path.exists(tj) else {}
+    d[workload] = dict(kernel=kernel, bytes_per_launch=fetch_b + write_b, read_bytes=fetch_b,
+                       write_bytes=write_b, fetch_factor=ff, write_factor=fw,
+                       gemm_source_sha256_16=h, summary="%s_traffic.md" % tag)
+    json.dump(d, open(tj, "w"), indent=1)
+    return text
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="what", required=True)
+    k = sub.add_parser("kernels")
+    k.add_argument("run_dir")
+    k.add_argument("tag")
+    k.add_argument("--last", type=int, required=True)
+    k.add_argument("--cmd", required=True)
+    t = sub.add_parser("traffic")
+    for a in ("fetch_dir", "write_dir", "tag", "workload", "kernel", "source"):
+        t.add_argument(a)
+    t.add_argument("--cmd-fetch", required=True)
+    t.add_argument("--cmd-write", required=True)
+    a = ap.parse_args()
+    if a.what == "kernels":
+        print(kernels(a.run_dir, a.tag, a.last, a.cmd))
+    else:
+        print(traffic(a.fetch_dir, a.write_dir, a.tag, a.workload, a.kernel, a.source, a.cmd_fetch,
+                      a.cmd_write))
+
+
+if __name__ == "__main__":
+    main()

@@ -85,10 +85,14 @@ int main(void) {
     memset(&w, 0, sizeof w);
     w.w13 = FAKE;
     w.w2 = FAKE;
-    w.layout = MOE_LAYOUT_ROW_MAJOR;  /* bf16 weights must be packed */
+    w.layout = 2;  /* no such layout */
     EXPECT(moe_forward(&ok, FAKE, FAKE, NULL, &w, FAKE, NULL, NULL, NULL, NULL, NULL, NULL, FAKE,
                        n, NULL),
            MOE_ERR_INVALID_ARGUMENT);
+    w.layout = MOE_LAYOUT_ROW_MAJOR;  /* bf16 weights row-major: accepted */
+    EXPECT(moe_forward(&ok, FAKE, FAKE, NULL, &w, FAKE, NULL, NULL, NULL, NULL, NULL, NULL, FAKE,
+                       16, NULL),
+           MOE_ERR_WORKSPACE_TOO_SMALL);
     w.layout = MOE_LAYOUT_PACKED;
     EXPECT(moe_forward(&ok, FAKE, FAKE, NULL, &w, FAKE, NULL, NULL, NULL, NULL, NULL, NULL, FAKE,
                        16, NULL),

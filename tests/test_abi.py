@@ -120,10 +120,11 @@ def test_gemm_and_forward_validation(L):
     assert L.moe_forward(C.byref(p), V(FAKE), V(FAKE), None, C.byref(w), V(FAKE), None, None, None,
                          None, None, None, V(FAKE), 10, None) == lib.MOE_ERR_WORKSPACE_TOO_SMALL
     assert L.moe_combine(C.byref(p), None, V(FAKE), V(FAKE), V(FAKE), None) == lib.MOE_ERR_INVALID_ARGUMENT
-    # layouts: bf16 weights must be packed; NVFP4 weights row-major or, where the shape
-    # tiles (H % 256, F % 128), packed
+    # layouts: bf16 weights row-major or packed, nothing else; NVFP4 weights row-major or, where
+    # the shape tiles (H % 256, F % 128), packed; fp32 weights row-major only
     pb = lib.problem(16, 256, 8, 2, 128, wdt="bf16")
-    for layout, status in ((0, lib.MOE_ERR_INVALID_ARGUMENT), (1, lib.MOE_ERR_WORKSPACE_TOO_SMALL)):
+    for layout, status in ((0, lib.MOE_ERR_WORKSPACE_TOO_SMALL), (1, lib.MOE_ERR_WORKSPACE_TOO_SMALL),
+                           (2, lib.MOE_ERR_INVALID_ARGUMENT), (-1, lib.MOE_ERR_INVALID_ARGUMENT)):
         wb = lib.ExpertWeights(FAKE, FAKE, None, None, None, None, layout)
         assert L.moe_forward(C.byref(pb), V(FAKE), V(FAKE), None, C.byref(wb), V(FAKE), None, None,
                              None, None, None, None, V(FAKE), 10, None) == status
@@ -132,6 +133,16 @@ def test_gemm_and_forward_validation(L):
         w = lib.ExpertWeights(FAKE, FAKE, FAKE, FAKE, None, None, layout)
         assert L.moe_forward(C.byref(p192), V(FAKE), V(FAKE), None, C.byref(w), V(FAKE), None, None,
                              None, None, None, None, V(FAKE), 1 << 40, None) == status
+    pf32 = lib.problem(16, 256, 8, 2, 128, act="f32", wdt="f32")
+    for layout, status in ((0, lib.MOE_ERR_WORKSPACE_TOO_SMALL), (1, lib.MOE_ERR_INVALID_ARGUMENT)):
+        wf = lib.ExpertWeights(FAKE, FAKE, None, None, None, None, layout)
+        assert L.moe_forward(C.byref(pf32), V(FAKE), V(FAKE), None, C.byref(wf), V(FAKE), None, None,
+                             None, None, None, None, V(FAKE), 10, None) == status
+    pmx = lib.problem(16, 512, 8, 2, 512, wdt="mxfp8")
+    for layout in (0, 1):  # MX codes row-major or packed
+        wm = lib.ExpertWeights(FAKE, FAKE, FAKE, FAKE, None, None, layout)
+        assert L.moe_forward(C.byref(pmx), V(FAKE), V(FAKE), None, C.byref(wm), V(FAKE), None, None,
+                             None, None, None, None, V(FAKE), 10, None) == lib.MOE_ERR_WORKSPACE_TOO_SMALL
     w = lib.ExpertWeights(FAKE, FAKE, FAKE, FAKE, None, None, 1)  # packed NVFP4 is validated
     assert L.moe_forward(C.byref(p), V(FAKE), V(FAKE), None, C.byref(w), V(FAKE), None, None, None,
                          None, None, None, V(FAKE), 10, None) == lib.MOE_ERR_WORKSPACE_TOO_SMALL
@@ -164,7 +175,7 @@ def test_mxfp8_validation(L):
     w = lib.ExpertWeights(FAKE, FAKE, None, None, None, None, 0)  # MXFP8 without scales
     assert L.moe_forward(C.byref(p), V(FAKE), V(FAKE), None, C.byref(w), V(FAKE), None, None, None,
                          None, None, None, V(FAKE), 1 << 40, None) == lib.MOE_ERR_INVALID_ARGUMENT
-    w = lib.ExpertWeights(FAKE, FAKE, FAKE, FAKE, None, None, 0)  # MXFP8 codes must be packed
+    w = lib.ExpertWeights(FAKE, FAKE, FAKE, FAKE, None, None, 3)  # no such layout
     assert L.moe_forward(C.byref(p), V(FAKE), V(FAKE), None, C.byref(w), V(FAKE), None, None, None,
                          None, None, None, V(FAKE), 1 << 40, None) == lib.MOE_ERR_INVALID_ARGUMENT
     a, b = lib.packed_weights_size(p)

@@ -15,6 +15,7 @@ import torch
 
 from mixture_experts_layer_softmax_amd import lib, synth
 from mixture_experts_layer_softmax_amd.layer import MoELayer, bf16_bits_to_f64, to_device, to_host
+from gpu_checks import check_experts_through_stages
 from oracle import oracle as O
 
 pytestmark = pytest.mark.gpu
@@ -141,9 +142,10 @@ def test_expert_parallel_share(wdt, path):
     assert e <= TOL
 
 
+@pytest.mark.parametrize("layout", ["packed", "row_major"])
 @pytest.mark.parametrize("wdt", ["mxfp8", "mxfp4"])
 @pytest.mark.parametrize("path", ["prefill", "decode"])
-def test_down_with_one_hot_rows_returns_exact_weights(wdt, path):
+def test_down_with_one_hot_rows_returns_exact_weights(wdt, path, layout):
     """hid row r = unit vector at f_r: its MXFP8 form is exact (scale 2^-8, code 256), so
     y_perm[r, h] must equal the decoded weight W2[e][h, f_r] exactly (an E4M3 or E2M1 value
     times a power of two, exact in bf16); this pins the weight layout, the chunk slots and the
@@ -158,20 +160,22 @@ def test_down_with_one_hot_rows_returns_exact_weights(wdt, path):
     hid[np.arange(A), f_of_row] = 1.0
     hid_bits = synth.to_bf16_bits(hid)
     ref = O.down_rows(inp, wdt, H, bf16_bits_to_f64(hid_bits), e_of_row)
-    layer = MoELayer(A, H, E, 1, F, "bf16", wdt, inp, path=path)
+    layer = MoELayer(A, H, E, 1, F, "bf16", wdt, inp, path=path, weight_layout=layout)
     p = layer.problem_for(A)
     ws = layer.workspace(A)
     y_perm = layer.empty_act(A, H)
     offsets = np.arange(E + 1, dtype=np.int32) * F
-    note("MX one-hot down wdt=%s path=%s" % (wdt, path))
+    note("MX one-hot down wdt=%s path=%s layout=%s" % (wdt, path, layout))
     lib.grouped_gemm(p, lib.DOWN, to_device(hid_bits, "cuda"), None, torch.from_numpy(offsets).cuda(),
                      layer.weights, y_perm, ws)
     torch.cuda.synchronize()
     assert np.array_equal(bf16_bits_to_f64(to_host(y_perm)), ref)
 
 
-@pytest.mark.parametrize("name", ["mxfp8_prefill", "mxfp4_prefill", "mxfp8_decode64", "mxfp4_decode64"])
-def test_full_size_sampled(name):
+@pytest.mark.parametrize("name", ["mxfp8_prefill", "mxfp4_prefill"])
+def test_full_size_prefill(name):
+    """Routing bit-exact on every token, the output on sampled tokens, and every hid and y_perm
+    row of three whole experts through the stage entry points (gpu_checks)."""
     wl = synth.WORKLOADS[name]
     note("%s: generating inputs" % name)
     inp = synth.generate(wl)
@@ -180,3 +184,31 @@ def test_full_size_sampled(name):
     toks = np.unique(np.concatenate([[0, wl.tokens - 1], rng.choice(wl.tokens, 10, replace=False)]))
     note("%s: running" % name)
     _check_forward(wl, inp, layer, tokens=toks)
+    note("%s: stage entry points, whole experts" % name)
+    check_experts_through_stages(wl, inp, layer, note)
+
+
+@pytest.mark.parametrize("name", ["mxfp8_decode64", "mxfp4_decode64"])
+def test_decode64_every_token(name):
+    wl = synth.WORKLOADS[name]
+    note("%s: generating inputs" % name)
+    inp = synth.generate(wl)
+    note("%s: all 64 tokens" % name)
+    _check_forward(wl, inp, MoELayer.from_workload(wl, inp))
+
+
+@pytest.mark.parametrize("wdt", ["mxfp8", "mxfp4"])
+@pytest.mark.parametrize("path", ["prefill", "decode"])
+def test_row_major_codes_give_the_packed_layer(wdt, path):
+    """MX codes handed over row-major give the packed layer bit for bit."""
+    wl = SMALL["ragged_" + wdt]
+    inp = synth.generate(wl)
+    a = MoELayer.from_workload(wl, inp, path=path)
+    b = MoELayer.from_workload(wl, inp, path=path, weight_layout="row_major")
+    assert a.layout == lib.LAYOUT_PACKED and b.layout == lib.LAYOUT_ROW_MAJOR
+    x = a.act_tensor(inp["x"])
+    note("MX row-major codes %s path=%s" % (wdt, path))
+    ya = a.forward(x).clone()
+    yb = b.forward(x)
+    torch.cuda.synchronize()
+    assert torch.equal(ya, yb)

@@ -3,7 +3,8 @@
 Bar: expert ids, counts, offsets, sorted_token and inv_perm bit-exact; routing weights within
 1e-5 relative; layer outputs within 2e-2 max relative error (max|y - ref| / max|ref|).
 Small shapes run the oracle on everything; the full-size workloads check routing and dispatch
-on every token and the layer output on a sample of tokens.
+on every token, the layer output on a sample of tokens (all 64 in the 64-token decode batch),
+and every row of three whole experts through the stage entry points.
 """
 import numpy as np
 import pytest
@@ -11,6 +12,7 @@ import torch
 
 from mixture_experts_layer_softmax_amd import lib, synth
 from mixture_experts_layer_softmax_amd.layer import MoELayer, bf16_bits_to_f64, to_device, to_host
+from gpu_checks import check_experts_through_stages
 from oracle import oracle as O
 
 pytestmark = pytest.mark.gpu
@@ -54,8 +56,8 @@ _CACHE = {}
 
 
 def case(name):
-    """Workload of a case name; a name ending in _rm keeps NVFP4 weights row-major (the other
-    NVFP4 cases are packed wherever the shape allows it)."""
+    """Workload of a case name; a name ending in _rm hands the weights over row-major (the other
+    cases pack bf16 and MX weights, and NVFP4 weights wherever the shape allows it)."""
     rm = name.endswith("_rm")
     base = name[:-3] if rm else name
     return SMALL.get(base) or synth.WORKLOADS[base], ("row_major" if rm else "packed")
@@ -207,8 +209,9 @@ def _routed(wl, inp):
     return r, expert_of_row
 
 
-@pytest.mark.parametrize("name", ["tiny", "small_bf16", "small_nvfp4", "small_nvfp4_rm", "ragged_bf16",
-                                  "ragged_nvfp4", "win4_nvfp4", "win4_nvfp4_rm", "ragged_f32"])
+@pytest.mark.parametrize("name", ["tiny", "small_bf16", "small_bf16_rm", "small_nvfp4", "small_nvfp4_rm",
+                                  "ragged_bf16", "ragged_bf16_rm", "ragged_nvfp4", "win4_nvfp4",
+                                  "win4_nvfp4_rm", "ragged_f32"])
 @pytest.mark.parametrize("path", ["prefill", "decode"])
 def test_gate_up_matches_oracle(name, path):
     wl, layout = case(name)
@@ -216,7 +219,7 @@ def test_gate_up_matches_oracle(name, path):
     note("gate_up %s path=%s" % (name, path))
     r, eor = _routed(wl, inp)
     ref = O.gate_up_rows(inp, wl.wdt, wl.ffn, r["sorted_token"], eor)
-    layer = MoELayer.from_workload(wl, inp, path=path, nvfp4_layout=layout)
+    layer = MoELayer.from_workload(wl, inp, path=path, weight_layout=layout)
     p = layer.problem_for(wl.tokens)
     ws = layer.workspace(wl.tokens)
     A = wl.assignments
@@ -237,8 +240,9 @@ def test_gate_up_matches_oracle(name, path):
     assert torch.equal(hid, hid2)
 
 
-@pytest.mark.parametrize("name", ["tiny", "small_bf16", "small_nvfp4", "small_nvfp4_rm", "ragged_bf16",
-                                  "ragged_nvfp4", "win4_nvfp4", "win4_nvfp4_rm", "ragged_f32"])
+@pytest.mark.parametrize("name", ["tiny", "small_bf16", "small_bf16_rm", "small_nvfp4", "small_nvfp4_rm",
+                                  "ragged_bf16", "ragged_bf16_rm", "ragged_nvfp4", "win4_nvfp4",
+                                  "win4_nvfp4_rm", "ragged_f32"])
 @pytest.mark.parametrize("path", ["prefill", "decode"])
 def test_down_matches_oracle(name, path):
     wl, layout = case(name)
@@ -251,7 +255,7 @@ def test_down_matches_oracle(name, path):
     if wl.act == "bf16":
         hid_host = synth.to_bf16_bits(hid_host)
     ref = O.down_rows(inp, wl.wdt, wl.hidden, act_f64(hid_host), eor)
-    layer = MoELayer.from_workload(wl, inp, path=path, nvfp4_layout=layout)
+    layer = MoELayer.from_workload(wl, inp, path=path, weight_layout=layout)
     p = layer.problem_for(wl.tokens)
     ws = layer.workspace(wl.tokens)
     y_perm = layer.empty_act(A, wl.hidden)
@@ -263,19 +267,17 @@ def test_down_matches_oracle(name, path):
     assert e <= TOL
 
 
-@pytest.mark.parametrize("wdt", ["bf16", "nvfp4", "nvfp4_packed"])
-@pytest.mark.parametrize("path", ["prefill", "decode"])
-def test_down_with_one_hot_rows_returns_exact_weights(wdt, path):
-    """hid row r = unit vector at f_r: y_perm[r, h] must be W2[e][h, f_r] exactly (the 4-bit
-    value decodes exactly to bf16), which pins the weight decode and the tile index maps
-    (NVFP4: row-major at H = 192, packed at H = 256)."""
-    layout = "packed" if wdt == "nvfp4_packed" else "row_major"
-    wdt = "nvfp4" if wdt == "nvfp4_packed" else wdt
-    E, H, F = 3, (192 if wdt == "nvfp4" and layout == "row_major" else 256), 128
-    wl = W("onehot", 1, H, E, 1, F, "bf16", wdt, 21, "none")
+def _one_hot_down(wdt, layout, path, H, inp_edit=None, seed=21):
+    """hid row r = unit vector at f_r through the down GEMM: y_perm[r, h] must be W2[e][h, f_r]
+    exactly (every weight format decodes exactly to bf16), which pins the weight decode and the
+    tile index maps.  Returns (GPU y_perm as float64, oracle)."""
+    E, F = 3, 128
+    wl = W("onehot", 1, H, E, 1, F, "bf16", wdt, seed, "none")
     inp = synth.generate(wl)
     inp.pop("w13_gscale", None)
     inp.pop("w2_gscale", None)  # per-expert scale 1.0: the product stays exact
+    if inp_edit:
+        inp_edit(inp)
     A = E * F
     f_of_row = np.tile(np.arange(F), E)
     e_of_row = np.repeat(np.arange(E), F).astype(np.int32)
@@ -283,18 +285,52 @@ def test_down_with_one_hot_rows_returns_exact_weights(wdt, path):
     hid[np.arange(A), f_of_row] = 1.0
     hid_bits = synth.to_bf16_bits(hid)
     ref = O.down_rows(inp, wdt, H, act_f64(hid_bits), e_of_row)
-    layer = MoELayer(A, H, E, 1, F, "bf16", wdt, inp, path=path, nvfp4_layout=layout)
-    assert layer.layout == (lib.LAYOUT_ROW_MAJOR if wdt == "nvfp4" and layout == "row_major"
-                            else lib.LAYOUT_PACKED)
+    layer = MoELayer(A, H, E, 1, F, "bf16", wdt, inp, path=path, weight_layout=layout)
+    want = lib.LAYOUT_PACKED if layout == "packed" and (wdt != "nvfp4" or H % 256 == 0) else lib.LAYOUT_ROW_MAJOR
+    assert layer.layout == want
     p = layer.problem_for(A)
     ws = layer.workspace(A)
     y_perm = layer.empty_act(A, H)
     offsets = np.arange(E + 1, dtype=np.int32) * F
-    note("one-hot down wdt=%s path=%s" % (wdt, path))
     lib.grouped_gemm(p, lib.DOWN, layer.act_tensor(hid_bits), None, dev_i32(offsets), layer.weights,
                      y_perm, ws)
     torch.cuda.synchronize()
-    assert np.array_equal(act_f64(to_host(y_perm)), ref)
+    return act_f64(to_host(y_perm)), ref
+
+
+@pytest.mark.parametrize("wdt,layout,H", [("bf16", "packed", 256), ("bf16", "row_major", 256),
+                                          ("nvfp4", "row_major", 192), ("nvfp4", "packed", 256),
+                                          ("nvfp4", "row_major", 256)])
+@pytest.mark.parametrize("path", ["prefill", "decode"])
+def test_down_with_one_hot_rows_returns_exact_weights(wdt, layout, H, path):
+    note("one-hot down wdt=%s layout=%s H=%d path=%s" % (wdt, layout, H, path))
+    got, ref = _one_hot_down(wdt, layout, path, H)
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("layout", ["row_major", "packed"])
+@pytest.mark.parametrize("path", ["prefill", "decode"])
+def test_nvfp4_every_finite_e4m3_scale_decodes_exactly(layout, path):
+    """Every finite non-negative E4M3 block scale, 0x00 to 0x7E, subnormals 0x01-0x07 (m 2^-9)
+    included, written over the down weights' scales with per-expert scale 1: the one-hot rows
+    must return e2m1 * e4m3 exactly ("CuTeDSL at Perplexity", section Blackwell support:
+    16-element NVFP4 blocks; E4M3 per the OCP 8-bit formats).  Each code covers many blocks,
+    and the nibbles hold every E2M1 code."""
+    H = 256
+
+    def sweep(inp):
+        s2 = inp["w2_scale"]
+        inp["w2_scale"] = (np.arange(s2.size) % 127).astype(np.uint8).reshape(s2.shape)
+        q = inp["w2"]
+        rng = np.random.default_rng(5)
+        inp["w2"] = rng.integers(0, 256, q.shape).astype(np.uint8)
+
+    note("NVFP4 scale sweep layout=%s path=%s" % (layout, path))
+    got, ref = _one_hot_down("nvfp4", layout, path, H, inp_edit=sweep)
+    assert np.all(np.isfinite(ref))
+    sub = np.abs(ref)[(ref != 0)].min()
+    assert sub <= 2.0 ** -9  # products of the subnormal scales are in the output
+    assert np.array_equal(got, ref)
 
 
 def test_packed_weight_layout_matches_its_definition():
@@ -368,25 +404,39 @@ def test_packed_nvfp4_layout_matches_its_definition():
         assert np.array_equal(out[key].cpu().numpy().ravel(), expect(inp[key], kind, unit)), key
 
 
-@pytest.mark.parametrize("name", ["small_nvfp4", "win4_nvfp4"])
-def test_nvfp4_layouts_agree(name):
-    """Packed and row-major NVFP4 weights give the same layer: bit for bit on the prefill
-    kernels (same arithmetic, other addresses), within the bar on the decode kernels (another
-    order of K)."""
+@pytest.mark.parametrize("name", ["small_nvfp4", "win4_nvfp4", "small_bf16", "ragged_bf16",
+                                  "small_mxfp8", "small_mxfp4", "split_mxfp8"])
+def test_weight_layouts_agree(name):
+    """Packed and row-major weights give the same layer: bit for bit on the bf16 and MX kernels
+    and the NVFP4 prefill kernels (same values in the same LDS image or operand registers, other
+    addresses), within the bar on the NVFP4 decode kernels (another order of K)."""
     wl = SMALL[name]
     inp = inputs_of(wl)
-    a = MoELayer.from_workload(wl, inp, nvfp4_layout="packed")
-    b = MoELayer.from_workload(wl, inp, nvfp4_layout="row_major")
+    a = MoELayer.from_workload(wl, inp, weight_layout="packed")
+    b = MoELayer.from_workload(wl, inp, weight_layout="row_major")
     assert a.layout == lib.LAYOUT_PACKED and b.layout == lib.LAYOUT_ROW_MAJOR
     x = a.act_tensor(inp["x"])
-    note("NVFP4 layouts %s" % name)
+    note("weight layouts %s" % name)
     ya = a.forward(x, path="prefill").clone()
     yb = b.forward(x, path="prefill").clone()
     da = a.forward(x, path="decode").clone()
     db = b.forward(x, path="decode")
     torch.cuda.synchronize()
     assert torch.equal(ya, yb)
-    assert rel_err(act_f64(to_host(da)), act_f64(to_host(db))) <= TOL
+    if wl.wdt == "nvfp4":
+        assert rel_err(act_f64(to_host(da)), act_f64(to_host(db))) <= TOL
+    else:
+        assert torch.equal(da, db)
+
+
+def test_row_major_layer_matches_oracle():
+    """A caller holding dense row-major bf16 weights gets the layer without packing them."""
+    wl = SMALL["ragged_bf16"]
+    inp = inputs_of(wl)
+    note("row-major bf16 layer")
+    layer = MoELayer.from_workload(wl, inp, weight_layout="row_major")
+    assert layer.layout == lib.LAYOUT_ROW_MAJOR
+    _check_forward(wl, inp, layer)
 
 
 # ---------------------------------------------------------------------------------------
@@ -442,20 +492,33 @@ def test_forward_matches_oracle(name):
     wl, layout = case(name)
     inp = inputs_of(wl)
     note("forward %s" % name)
-    layer = MoELayer.from_workload(wl, inp, nvfp4_layout=layout)
+    layer = MoELayer.from_workload(wl, inp, weight_layout=layout)
     _check_forward(wl, inp, layer)
 
 
-@pytest.mark.parametrize("name,sample", [("decode64", 16), ("prefill", 12), ("nvfp4_prefill", 12)])
-def test_forward_full_size_sampled(name, sample):
+def test_forward_decode64_every_token():
+    """The 64-token decode batch: the whole layer output of every token against the oracle."""
+    wl = synth.WORKLOADS["decode64"]
+    inp = inputs_of(wl)
+    note("forward decode64, all 64 tokens")
+    _check_forward(wl, inp, MoELayer.from_workload(wl, inp))
+
+
+@pytest.mark.parametrize("name", ["prefill", "nvfp4_prefill"])
+def test_forward_full_size(name):
+    """Full-size prefill layers: routing and dispatch of every token bit-exact, the layer output
+    on a sample of tokens, and through the stage entry points every hid and y_perm row of the
+    largest expert, a ragged one and the smallest one (gpu_checks)."""
     wl = synth.WORKLOADS[name]
     note("forward full size %s: generating inputs" % name)
     inp = inputs_of(wl)
     layer = MoELayer.from_workload(wl, inp)
     rng = np.random.default_rng(99)
-    toks = np.unique(np.concatenate([[0, wl.tokens - 1], rng.choice(wl.tokens, sample - 2, replace=False)]))
+    toks = np.unique(np.concatenate([[0, wl.tokens - 1], rng.choice(wl.tokens, 10, replace=False)]))
     note("forward full size %s: running" % name)
     _check_forward(wl, inp, layer, tokens=toks)
+    note("forward full size %s: stage entry points, whole experts" % name)
+    check_experts_through_stages(wl, inp, layer, note)
     del layer
     torch.cuda.empty_cache()
 
