@@ -20,7 +20,8 @@
  *  - Pointers are DEVICE memory owned by the caller, 16-byte aligned.  The library never
  *    allocates, frees or retains device memory; scratch comes from the caller's workspace
  *    (size from moe_workspace_size).  No global mutable state: calls on different streams
- *    with different workspaces may run concurrently.
+ *    with different workspaces may run concurrently.  (The one exception is
+ *    moe_forward_static, at the end of this header, whose scratch is a static per-GPU array.)
  *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only enqueues work
  *    on it; nothing synchronises and no device data is read on the host.  Results are valid
  *    once the caller has synchronised the stream.
@@ -71,7 +72,8 @@ typedef enum {
     MOE_ERR_INVALID_ARGUMENT = 1,
     MOE_ERR_UNSUPPORTED = 2,
     MOE_ERR_WORKSPACE_TOO_SMALL = 3,
-    MOE_ERR_DEVICE = 4
+    MOE_ERR_DEVICE = 4,
+    MOE_ERR_SCRATCH_TOO_SMALL = 5  /* moe_forward_static: the problem needs more than its scratch */
 } moe_status;
 
 /* Storage formats.  MOE_NVFP4 (weights only): 4-bit E2M1 values, two per byte with the even
@@ -259,6 +261,26 @@ moe_status moe_forward(const moe_problem* p, const void* x, const void* w_router
                        int32_t* topk_ids, float* topk_w, int32_t* counts, int32_t* offsets,
                        int32_t* sorted_token, int32_t* inv_perm, void* workspace,
                        size_t workspace_bytes, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): moe_forward without a workspace argument.  Every
+ * argument means what it means for moe_forward; the scratch comes from a static device array
+ * of MOE_STATIC_SCRATCH_BYTES that the library holds on each GPU it runs on until the process
+ * ends (its device address is looked up once per device, with that device current; the call
+ * uses the current device, which must be the stream's).  Nothing is allocated or freed.
+ *  - MOE_ERR_SCRATCH_TOO_SMALL, before any device work, when moe_workspace_size(p) exceeds
+ *    MOE_STATIC_SCRATCH_BYTES (decode-sized problems fit: for H 4096, F 1536, k 8 up to about
+ *    700 tokens; prefill-sized ones do not and take moe_forward with a workspace).
+ *  - Every call on a GPU uses that GPU's one array, which keeps the last call's contents;
+ *    nothing in it needs to start at zero (each call writes every byte it reads first).
+ *    Calls that overlap in time on one GPU (other streams, other host threads) race on it and
+ *    must be serialised by the caller.
+ *  - Otherwise as moe_forward (enqueues kernel launches only; capturable). */
+#define MOE_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status moe_forward_static(const moe_problem* p, const void* x, const void* w_router,
+                              const float* router_bias, const moe_expert_weights* w, void* y,
+                              int32_t* topk_ids, float* topk_w, int32_t* counts, int32_t* offsets,
+                              int32_t* sorted_token, int32_t* inv_perm, void* stream);
 
 #ifdef __cplusplus
 }

@@ -9,6 +9,7 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/moe.h"
 #include "launch.h"
@@ -159,6 +160,30 @@ moe_status check_weights(const moe_problem& p, const moe_expert_weights* w) {
 
 moe_status dev(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_DEVICE; }
 
+// Scratch of moe_forward_static: one array per GPU, in the library's device data, held until the
+// process ends.  Host code never uses the array's name as an address (on the host it is only a
+// stand-in for the symbol): the device address comes from hipGetSymbolAddress, taken once per
+// device with that device current, and is kept per device.
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[MOE_STATIC_SCRATCH_BYTES];
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+moe_status static_scratch(void** out) {
+    int d = 0;
+    if (hipGetDevice(&d) != hipSuccess) return MOE_ERR_DEVICE;
+    if (d < 0 || d >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+    std::call_once(g_scratch_once[d], [d] {
+        void* ptr = nullptr;
+        g_scratch_err[d] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        g_scratch_ptr[d] = ptr;
+    });
+    if (g_scratch_err[d] != hipSuccess || !g_scratch_ptr[d]) return MOE_ERR_DEVICE;
+    *out = g_scratch_ptr[d];
+    return MOE_OK;
+}
+
 #define MOE_TRY(x)                           \
     do {                                     \
         moe_status _s = (x);                 \
@@ -228,6 +253,7 @@ const char* moe_status_string(moe_status s) {
         case MOE_ERR_UNSUPPORTED: return "unsupported shape or dtype combination";
         case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
         case MOE_ERR_DEVICE: return "device error";
+        case MOE_ERR_SCRATCH_TOO_SMALL: return "problem needs more scratch than the static scratch buffer holds";
     }
     return "unknown status";
 }
@@ -449,6 +475,21 @@ moe_status moe_forward(const moe_problem* p, const void* x, const void* w_router
     MOE_TRY(dev(launch_gemm(g2, L.family, L.max_tiles, s)));
     return dev(launch_combine(yperm, ip, tw, y, p->num_tokens, p->top_k, p->hidden,
                               p->num_tokens * p->top_k, p->act_dtype == MOE_BF16, s));
+}
+
+moe_status moe_forward_static(const moe_problem* p, const void* x, const void* w_router,
+                              const float* router_bias, const moe_expert_weights* w, void* y,
+                              int32_t* topk_ids, float* topk_w, int32_t* counts, int32_t* offsets,
+                              int32_t* sorted_token, int32_t* inv_perm, void* stream) {
+    MOE_TRY(check_problem(p));
+    if (p->num_tokens == 0)  // no scratch needed
+        return moe_forward(p, x, w_router, router_bias, w, y, topk_ids, topk_w, counts, offsets,
+                           sorted_token, inv_perm, nullptr, 0, stream);
+    if (layout(*p).total > MOE_STATIC_SCRATCH_BYTES) return MOE_ERR_SCRATCH_TOO_SMALL;
+    void* ws = nullptr;
+    MOE_TRY(static_scratch(&ws));
+    return moe_forward(p, x, w_router, router_bias, w, y, topk_ids, topk_w, counts, offsets,
+                       sorted_token, inv_perm, ws, MOE_STATIC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

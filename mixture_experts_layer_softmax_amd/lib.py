@@ -14,7 +14,9 @@ import threading
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmoe_mi355x.so")
 
-MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_DEVICE = range(5)
+(MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_DEVICE,
+ MOE_ERR_SCRATCH_TOO_SMALL) = range(6)
+STATIC_SCRATCH_BYTES = 64 << 20  # MOE_STATIC_SCRATCH_BYTES
 MOE_F32, MOE_BF16, MOE_NVFP4, MOE_MXFP8, MOE_MXFP4 = 0, 1, 2, 3, 4
 GATE_UP_SWIGLU, DOWN = 0, 1
 PATH_AUTO, PATH_PREFILL, PATH_DECODE = 0, 1, 2
@@ -24,7 +26,7 @@ PATHS = {"auto": PATH_AUTO, "prefill": PATH_PREFILL, "decode": PATH_DECODE}
 #: every symbol the header declares
 EXPORTS = ("moe_status_string", "moe_workspace_size", "moe_packed_weights_size", "moe_pack_weights",
            "moe_pack_scales", "moe_route", "moe_permute", "moe_grouped_gemm", "moe_combine", "moe_forward",
-           "moe_quantize_mxfp8", "moe_probe_mfma_bf16", "moe_probe_read")
+           "moe_quantize_mxfp8", "moe_probe_mfma_bf16", "moe_probe_read", "moe_forward_static")
 LAYOUT_ROW_MAJOR, LAYOUT_PACKED = 0, 1
 
 
@@ -89,6 +91,9 @@ def load() -> C.CDLL:
             L.moe_forward.restype = i32
             L.moe_forward.argtypes = [P, vp, vp, vp, C.POINTER(ExpertWeights), vp, vp, vp, vp, vp,
                                       vp, vp, vp, sz, vp]
+            L.moe_forward_static.restype = i32
+            L.moe_forward_static.argtypes = [P, vp, vp, vp, C.POINTER(ExpertWeights), vp, vp, vp, vp,
+                                             vp, vp, vp, vp]
             _lib = L
     return _lib
 
@@ -182,6 +187,15 @@ def forward(p, x, w_router, bias, w: ExpertWeights, y, ws, topk_ids=None, topk_w
                               _ptr(topk_ids), _ptr(topk_w), _ptr(counts), _ptr(offsets),
                               _ptr(sorted_token), _ptr(inv_perm), _ptr(ws),
                               ws.numel() * ws.element_size(), _stream(stream)), "moe_forward")
+
+
+def forward_static(p, x, w_router, bias, w: ExpertWeights, y, topk_ids=None, topk_w=None,
+                   counts=None, offsets=None, sorted_token=None, inv_perm=None, stream=None):
+    """moe_forward_static: the layer with the library's static per-GPU scratch (no workspace)."""
+    _check(load().moe_forward_static(C.byref(p), _ptr(x), _ptr(w_router), _ptr(bias), C.byref(w),
+                                     _ptr(y), _ptr(topk_ids), _ptr(topk_w), _ptr(counts),
+                                     _ptr(offsets), _ptr(sorted_token), _ptr(inv_perm),
+                                     _stream(stream)), "moe_forward_static")
 
 
 def quantize_mxfp8(x, codes, scales, stream=None):

@@ -36,7 +36,25 @@ def test_every_declared_symbol_is_exported(L):
 def test_status_strings(L):
     assert lib.status_string(lib.MOE_OK) == "ok"
     assert "workspace" in lib.status_string(lib.MOE_ERR_WORKSPACE_TOO_SMALL)
+    assert "static scratch" in lib.status_string(lib.MOE_ERR_SCRATCH_TOO_SMALL)
     assert lib.status_string(99) == "unknown status"
+
+
+def test_forward_static_validation(L):
+    """moe_forward_static validates the problem and refuses one that does not fit its static
+    scratch before any HIP call (so these run without a GPU)."""
+    V = C.c_void_p
+    w = lib.ExpertWeights(FAKE, FAKE, None, None, None, None, 1)
+    bad = lib.problem(16, 256, 8, 0, 128)  # k = 0
+    assert L.moe_forward_static(C.byref(bad), V(FAKE), V(FAKE), None, C.byref(w), V(FAKE), None, None,
+                                None, None, None, None, None) == lib.MOE_ERR_INVALID_ARGUMENT
+    big = lib.problem(4096, 4096, 128, 8, 1536)
+    assert lib.workspace_size(big) > lib.STATIC_SCRATCH_BYTES
+    assert L.moe_forward_static(C.byref(big), V(FAKE), V(FAKE), None, C.byref(w), V(FAKE), None, None,
+                                None, None, None, None, None) == lib.MOE_ERR_SCRATCH_TOO_SMALL
+    # the decode shapes fit: 64 tokens of the 4096 x 1536 layer, 16 of the 256-expert NVFP4 one
+    assert lib.workspace_size(lib.problem(64, 4096, 128, 8, 1536)) <= lib.STATIC_SCRATCH_BYTES
+    assert lib.workspace_size(lib.problem(16, 4096, 256, 8, 2048, wdt="nvfp4")) <= lib.STATIC_SCRATCH_BYTES
 
 
 @pytest.mark.parametrize("name", sorted(synth.WORKLOADS))
