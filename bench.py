@@ -378,6 +378,8 @@ def main() -> int:
     ap.add_argument("--ep-size", type=int, default=1,
                     help="expert-parallel degree whose one-rank share is measured (one GPU)")
     ap.add_argument("--ep-rank", type=int, default=0)
+    ap.add_argument("--path", choices=("auto", "prefill", "decode", "fused"), default="auto",
+                    help="kernel family of moe_forward (fused: the single-launch decode kernel)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this layer is built and measured on a single "
@@ -413,7 +415,7 @@ def main() -> int:
           file=sys.stderr, flush=True)
     inputs = synth.generate(wl, experts=None if held is None else range(held[0], held[0] + held[1]))
     torch.cuda.set_device(0)
-    layer = MoELayer.from_workload(wl, inputs, device="cuda:0",
+    layer = MoELayer.from_workload(wl, inputs, device="cuda:0", path=args.path,
                                    expert_begin=0 if held is None else held[0],
                                    local_experts=0 if held is None else held[1])
     x = layer.act_tensor(inputs["x"])
@@ -499,7 +501,7 @@ def main() -> int:
                            experts=wl.experts, top_k=wl.top_k, ffn=wl.ffn, weights=wl.wdt,
                            active_experts=active, max_expert_rows=int(counts.max()),
                            cache_flushed=bool(flush),
-                           flush_mode=args.flush_mode if flush else None),
+                           flush_mode=args.flush_mode if flush else None, path=args.path),
                layer_tflops=flops / (ms_per_step * 1e-3) / 1e12,
                layer_mfma_frac=flops / (ms_per_step * 1e-3) / peak_mfma,
                layer_hbm_frac=nbytes / (ms_per_step * 1e-3) / PEAK_HBM_BYTES,

@@ -102,8 +102,21 @@ typedef enum { MOE_GEMM_GATE_UP_SWIGLU = 0, MOE_GEMM_DOWN = 1 } moe_gemm_kind;
 
 /* Kernel family.  AUTO picks DECODE when there are fewer than 16 assignments per expert on
  * average (weight streaming with small row tiles) and PREFILL otherwise (large MFMA tiles).
- * Both families give bit-identical routing and dispatch. */
-typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_PREFILL = 1, MOE_PATH_DECODE = 2 } moe_path;
+ * Both families give bit-identical routing and dispatch.
+ * DECODE_FUSED runs moe_forward's decode family as ONE cooperative launch ("CuTeDSL at
+ * Perplexity", section Grid synchronization: small decode batches as one kernel whose blocks
+ * meet at grid barriers): router logits, grid barrier, selection and dispatch repeated in
+ * every block, gate/up + SwiGLU, grid barrier, down, grid barrier, combine.  Same device code
+ * and order as DECODE, so the same routing and, with the same K split, the same outputs.  It
+ * covers bf16 activations with bf16 weights or PACKED NVFP4 weights, T <= 16, E <= 256,
+ * H % 512 == 0 and F % 512 == 0 (moe_forward returns MOE_ERR_UNSUPPORTED otherwise); the stage
+ * entry points treat it as DECODE.  Its barrier words live at the start of the workspace: a
+ * 64-bit sequence number that the kernel advances (any initial value works), and a 32-bit
+ * count of barrier waits that gave up (byte offset 8; every wait is bounded, so a grid that
+ * could not be co-resident ends with unspecified outputs and a non-zero count instead of
+ * hanging; the launch itself fails with MOE_ERR_DEVICE when the grid cannot be co-resident).
+ * The workspace must not be shared by calls that overlap in time. */
+typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_PREFILL = 1, MOE_PATH_DECODE = 2, MOE_PATH_DECODE_FUSED = 3 } moe_path;
 
 typedef struct {
     int32_t num_tokens;   /* T >= 0 */

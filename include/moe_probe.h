@@ -1,9 +1,10 @@
 /*
  * moe_probe.h -- measurement aids for the MoE layer library on MI355X (gfx950).
  *
- * Two microkernels that measure what the box actually sustains, so that a benchmark can state
- * its kernels' roofline fractions against measured peaks beside the data-sheet ones
- * (bf16 dense MFMA 2.5 PFLOP/s, HBM3E 8 TB/s).  They compute nothing of the layer.
+ * Microkernels that measure what the box actually sustains, so that a benchmark can state its
+ * kernels' roofline fractions against measured peaks beside the data-sheet ones (bf16 dense
+ * MFMA 2.5 PFLOP/s, HBM3E 8 TB/s), and what one grid barrier of the single-launch decode
+ * kernel costs.  They compute nothing of the layer.
  * Same conventions as moe.h: device pointers owned by the caller, work enqueued on `stream`
  * (a hipStream_t, NULL = default stream), return codes only, arguments validated on the host
  * before any HIP call.
@@ -33,6 +34,16 @@ moe_status moe_probe_mfma_bf16(int32_t blocks, int32_t iters, float* out, void* 
  * loads cannot be elided).  bytes must be a positive multiple of 16 and buf 16-byte aligned,
  * else MOE_ERR_INVALID_ARGUMENT. */
 moe_status moe_probe_read(const void* buf, size_t bytes, uint32_t* out, void* stream);
+
+/* Grid barriers alone: one cooperative launch of `blocks` blocks of 256 threads (they must fit
+ * on the device at once, else MOE_ERR_DEVICE) that pass `barriers` grid barriers of the
+ * single-launch decode kernel (MOE_PATH_DECODE_FUSED) in a row and do nothing else.  sync:
+ * device memory of MOE_PROBE_SYNC_BYTES, 16-byte aligned, any contents (it keeps a sequence
+ * number; at byte offset 8 a 32-bit count of barrier waits that gave up after `spin_limit`
+ * polls).  blocks in [1, 1024], barriers in [1, 65535], else MOE_ERR_INVALID_ARGUMENT. */
+#define MOE_PROBE_SYNC_BYTES 8256
+moe_status moe_probe_grid_barrier(int32_t blocks, int32_t barriers, void* sync, uint32_t spin_limit,
+                                  void* stream);
 
 #ifdef __cplusplus
 }

@@ -9,6 +9,7 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <cstdlib>
 #include <mutex>
 
 #include "../../include/moe.h"
@@ -25,7 +26,7 @@ size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 struct Layout {
-    size_t logits, ids, w, hist, base, counts, offsets, sorted, inv, tiles1, tiles2, tcount, hid,
+    size_t sync, logits, ids, w, hist, base, counts, offsets, sorted, inv, tiles1, tiles2, tcount, hid,
         yperm, xq, xs, hq, hs, total;
     int family, bm, max_tiles;
 };
@@ -55,7 +56,7 @@ int family_of(const moe_problem& p) {
         const long A = long(p.num_tokens) * p.top_k;
         path = (A < 16L * p.num_experts) ? MOE_PATH_DECODE : MOE_PATH_PREFILL;
     }
-    return path == MOE_PATH_DECODE ? kFamDecode : kFamPrefill;
+    return (path == MOE_PATH_DECODE || path == MOE_PATH_DECODE_FUSED) ? kFamDecode : kFamPrefill;
 }
 
 moe_status check_problem(const moe_problem* p) {
@@ -63,7 +64,7 @@ moe_status check_problem(const moe_problem* p) {
     if (p->num_tokens < 0 || p->hidden <= 0 || p->ffn <= 0 || p->num_experts < 1 ||
         p->num_experts > kMaxExperts || p->top_k < 1 || p->top_k > kMaxTopK ||
         p->top_k > p->num_experts || (p->renormalize != 0 && p->renormalize != 1) ||
-        p->path < MOE_PATH_AUTO || p->path > MOE_PATH_DECODE)
+        p->path < MOE_PATH_AUTO || p->path > MOE_PATH_DECODE_FUSED)
         return MOE_ERR_INVALID_ARGUMENT;
     if (p->expert_begin < 0 || p->local_experts < 0 ||
         long(p->expert_begin) + p->local_experts > p->num_experts ||
@@ -98,6 +99,7 @@ Layout layout(const moe_problem& p) {
     L.max_tiles = int((A + L.bm - 1) / L.bm + (A < E ? A : E) + 1);
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t r = o; o += up(bytes > 0 ? bytes : 1); return r; };
+    L.sync = take(sizeof(GridSync));  // grid-barrier words of the single-launch decode kernel
     L.logits = take(T * E * 4);
     L.ids = take(A * 4);
     L.w = take(A * 4);
@@ -159,6 +161,34 @@ moe_status check_weights(const moe_problem& p, const moe_expert_weights* w) {
 }
 
 moe_status dev(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_DEVICE; }
+
+// The single-launch decode kernel covers bf16 activations with bf16 weights (either layout) or
+// packed NVFP4 weights, up to kFusedMaxTokens tokens over up to kFusedMaxExperts experts, and K
+// a multiple of 512 in both GEMMs (its GEMVs split K over four wavefronts of 128-wide blocks).
+bool fused_eligible(const moe_problem& p, const moe_expert_weights& w) {
+    if (family_of(p) != kFamDecode || p.act_dtype != MOE_BF16) return false;
+    if (p.num_tokens > kFusedMaxTokens || p.num_experts > kFusedMaxExperts) return false;
+    if (p.hidden % 512 || p.ffn % 512) return false;
+    return p.w_dtype == MOE_BF16 || (p.w_dtype == MOE_NVFP4 && w.layout == MOE_LAYOUT_PACKED);
+}
+
+// MOE_PATH_DECODE_FUSED asks for the single-launch decode kernel; MOE_PATH_AUTO takes it for
+// eligible batches where it measured faster than the multi-launch decode path.
+bool use_fused(const moe_problem& p, const moe_expert_weights& w) {
+    if (!fused_eligible(p, w)) return false;
+    return p.path == MOE_PATH_DECODE_FUSED;
+}
+
+// Test and measurement hooks of the single-launch decode kernel, read from the environment:
+// MOE_FUSED_SPIN_LIMIT (polls before a barrier wait gives up, default 2^20) and
+// MOE_FUSED_BLOCKS_PER_CU (cap on the persistent grid, default: as many as fit).
+unsigned env_unsigned(const char* name, unsigned dflt) {
+    const char* v = std::getenv(name);
+    if (!v || !*v) return dflt;
+    char* end = nullptr;
+    const unsigned long x = std::strtoul(v, &end, 10);
+    return (end && *end == 0 && x <= 0xffffffffUL) ? unsigned(x) : dflt;
+}
 
 // Scratch of moe_forward_static: one array per GPU, in the library's device data, held until the
 // process ends.  Host code never uses the array's name as an address (on the host it is only a
@@ -465,6 +495,36 @@ moe_status moe_forward(const moe_problem* p, const void* x, const void* w_router
     }
     void* hid = at<void>(workspace, L.hid);
     void* yperm = at<void>(workspace, L.yperm);
+    if (p->path == MOE_PATH_DECODE_FUSED && !fused_eligible(*p, *w)) return MOE_ERR_UNSUPPORTED;
+    if (use_fused(*p, *w)) {
+        // the whole layer in one cooperative launch; routing outputs only where the caller asks
+        FusedArgs f{};
+        f.x = x;
+        f.wr = w_router;
+        f.bias = router_bias;
+        f.logits = at<float>(workspace, L.logits);
+        f.T = p->num_tokens;
+        f.H = p->hidden;
+        f.E = p->num_experts;
+        f.k = p->top_k;
+        f.renorm = p->renormalize;
+        f.eb = ebegin(*p);
+        f.ee = eend(*p);
+        f.ids = topk_ids;
+        f.tw = topk_w;
+        f.counts = counts;
+        f.offsets = offsets;
+        f.sorted_token = sorted_token;
+        f.inv_perm = inv_perm;
+        f.g1 = gemm_args(*p, kGateUp, x, nullptr, nullptr, nullptr, *w, hid);
+        f.g1.a_rows_limit = p->num_tokens;  // the kernel gathers token rows through its dispatch
+        f.g2 = gemm_args(*p, kDown, hid, nullptr, nullptr, nullptr, *w, yperm);
+        f.y_perm = yperm;
+        f.y = y;
+        f.sync = at<GridSync>(workspace, L.sync);
+        f.spin_limit = env_unsigned("MOE_FUSED_SPIN_LIMIT", 1u << 20);
+        return dev(launch_decode_fused(f, p->w_dtype == MOE_NVFP4, int(env_unsigned("MOE_FUSED_BLOCKS_PER_CU", 0)), s));
+    }
     GemmArgs g1 = gemm_args(*p, kGateUp, x, st, tiles, tcount, *w, hid);
     g1.hid_packed = hid_packed(*p);
     MOE_TRY(mx_input(*p, g1, workspace, L, s));

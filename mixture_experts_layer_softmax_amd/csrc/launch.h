@@ -60,7 +60,50 @@ struct GemmArgs {
     int wfmt;               // WeightFmt
 };
 
+// Single-launch decode (decode_fused.hip): batches of at most kFusedMaxTokens tokens over at
+// most kFusedMaxExperts experts run as one cooperative launch of at most kFusedMaxBlocks
+// blocks of 256 threads.
+constexpr int kFusedMaxTokens = 16;
+constexpr int kFusedMaxExperts = 256;
+constexpr int kFusedMaxBlocks = 1024;
+constexpr int kFusedMaxRows = kFusedMaxTokens * kMaxTopK;
+constexpr int kFusedTileCap = kFusedMaxRows / 16 + kFusedMaxExperts + 1;  // 16-row decode tiles
+
+// Grid-barrier words of the single-launch decode kernel (at the start of its workspace).
+struct GridSync {
+    uint64_t seq;         // calls made so far on this workspace (any initial value)
+    uint32_t timeouts;    // barrier waits that gave up (cumulative; zero it to watch a call)
+    uint32_t pad0;
+    uint64_t go;          // last barrier value released by block 0
+    uint64_t pad1[5];
+    uint64_t arrive[kFusedMaxBlocks];  // last barrier value each block reached
+};
+static_assert(sizeof(GridSync) == 8256, "MOE_PROBE_SYNC_BYTES in moe_probe.h");
+
+struct FusedArgs {
+    const void* x;        // [T,H] bf16
+    const void* wr;       // [E,H] bf16
+    const float* bias;    // [E] or null
+    float* logits;        // [T,E] (workspace)
+    int T, H, E, k, renorm, eb, ee;
+    int32_t* ids;         // routing outputs (each may be null)
+    float* tw;
+    int32_t* counts;
+    int32_t* offsets;
+    int32_t* sorted_token;
+    int32_t* inv_perm;
+    GemmArgs g1, g2;      // gate/up (a = x, out = hid) and down (a = hid, out = y_perm); their
+                          // tile lists and gather maps are set inside the kernel
+    void* y_perm;         // [A,H] bf16 (workspace)
+    void* y;              // [T,H] bf16
+    GridSync* sync;
+    unsigned spin_limit;  // polls before a barrier wait gives up
+};
+
 int gemm_tile_rows(int family, int wfmt, int ffn);
+// One cooperative launch of decode_fused_kernel for a bf16 (nv4 = 0) or packed NVFP4 (nv4 = 1)
+// layer; `blocks_per_cu` caps the persistent grid (0: as many as fit).
+hipError_t launch_decode_fused(const FusedArgs& a, bool nv4, int blocks_per_cu, hipStream_t s);
 hipError_t launch_router_logits(const RouteArgs& a, hipStream_t s);
 hipError_t launch_topk(const float* logits, int T, int E, int k, int renorm, int32_t* ids,
                        float* w, hipStream_t s);

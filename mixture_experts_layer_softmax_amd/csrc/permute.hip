@@ -169,81 +169,16 @@ hipError_t launch_fill_i32(int32_t* p, int n, int value, hipStream_t s) {
     return hipGetLastError();
 }
 
-// Small decode batches (any T <= 64; used for T <= 32): top-k selection and the whole dispatch
-// (histogram, scan, tile lists, stable scatter) in one block of NT threads, so a decode step
-// spends one launch here instead of four.  Wavefront w selects tokens w, w + NT/64, ... one
-// after the other; thread e < E then owns expert e.  Same results as topk_kernel +
-// hist/scan/scatter: ids of a token in selection order, rows of an expert in (t, j) order.
 template <int EPL, int NT>
 __global__ __launch_bounds__(NT) void select_dispatch_small_kernel(
     const float* __restrict__ logits, int T, int E, int k, int renorm, int32_t* __restrict__ ids,
     float* __restrict__ tw, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ sorted_token, int32_t* __restrict__ inv_perm, Tile* tiles1,
     int* tile_count1, int bm1, Tile* tiles2, int* tile_count2, int bm2, int cap, int eb, int ee) {
-    static_assert(NT >= kMaxExperts && NT % kWave == 0, "a thread per expert");
-    constexpr int NW = NT / kWave;
-    __shared__ int sids[kChunkTokens * kMaxTopK];
-    __shared__ int cnt[kMaxExperts];
-    __shared__ int wc[NW][kMaxExperts];
-    const int tid = threadIdx.x, w = tid / kWave;
-    for (int t = w; t < T; t += NW)
-        topk_token<EPL>(logits + size_t(t) * E, E, k, renorm, ids + size_t(t) * k, tw + size_t(t) * k,
-                        sids + t * k);
-    if (tid < E) cnt[tid] = 0;
-    __syncthreads();
-    const int A = T * k;
-    for (int a = tid; a < A; a += NT) {
-        const int id = clamp_expert(sids[a], E);
-        if (id >= eb && id < ee) atomicAdd(&cnt[id], 1);
-    }
-    __syncthreads();
-    const int c = tid < E ? cnt[tid] : 0;
-    int total;
-    const int start = block_exclusive_scan<NT>(c, &total);
-    if (tid < E) {
-        if (counts) counts[tid] = c;
-        offsets[tid] = start;
-    }
-    if (tid == 0) offsets[E] = total;
-    if (tiles1) emit_tiles<NT>(tid, E, c, start, bm1, tiles1, tile_count1, cap, eb);
-    if (tiles2) emit_tiles<NT>(tid, E, c, start, bm2, tiles2, tile_count2, cap, eb);
-    __syncthreads();
-    if (tid < E) cnt[tid] = start;  // next free row of each expert
-    int nbits = 0;
-    while ((1 << nbits) < E) ++nbits;
-    for (int r0 = 0; r0 < A; r0 += NT) {
-        for (int i = tid; i < NW * kMaxExperts; i += NT) (&wc[0][0])[i] = 0;
-        __syncthreads();
-        const int a = r0 + tid;
-        const int id0 = a < A ? clamp_expert(sids[a], E) : 0;
-        const bool valid = a < A && id0 >= eb && id0 < ee;
-        if (a < A && !valid) inv_perm[a] = -1;
-        const int id = valid ? id0 : 0;
-        uint64_t peers = __ballot(valid);
-        for (int b = 0; b < nbits; ++b) {
-            const bool bit = (id >> b) & 1;
-            const uint64_t m = __ballot(valid && bit);
-            peers &= bit ? m : ~m;
-        }
-        const int rank = __popcll(peers & lanemask_lt());
-        if (valid && rank == 0) wc[w][id] = __popcll(peers);
-        __syncthreads();
-        if (valid) {
-            int prefix = 0;
-            for (int ww = 0; ww < w; ++ww) prefix += wc[ww][id];
-            const int pos = cnt[id] + prefix + rank;
-            sorted_token[pos] = a / k;
-            inv_perm[a] = pos;
-        }
-        __syncthreads();
-        if (tid < E) {
-            int add = 0;
-#pragma unroll
-            for (int ww = 0; ww < NW; ++ww) add += wc[ww][tid];
-            cnt[tid] += add;
-        }
-        __syncthreads();
-    }
+    static_assert(NT >= kMaxExperts, "a thread per expert");
+    select_dispatch_block<EPL, NT>(logits, T, E, k, renorm, ids, tw, counts, offsets, sorted_token,
+                                   inv_perm, tiles1, tile_count1, bm1, tiles2, tile_count2, bm2, cap,
+                                   eb, ee);
 }
 
 hipError_t launch_select_dispatch_small(const float* logits, int renorm, int32_t* tw_ids,

@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 
 #include "device.h"
+#include "grid_sync.h"
+#include "launch.h"
 #include "moe_probe.h"
 
 namespace moe {
@@ -55,8 +57,34 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict
     if (acc == 0x9e3779b9u) out[0] = acc;
 }
 
+// `barriers` grid barriers in a row (grid_sync.h), nothing else: the cost of one barrier of the
+// single-launch decode kernel at this grid size.  Barrier values continue from the sequence
+// word of `gs` like the decode kernel's (v = 65536 S + i), so any initial contents work.
+__global__ __launch_bounds__(256) void barrier_probe_kernel(GridSync* gs, int barriers, unsigned spin_limit) {
+    __shared__ uint64_t s_seq;
+    if (threadIdx.x == 0) s_seq = load_agent(&gs->seq);
+    __syncthreads();
+    const uint64_t base = s_seq << 16;
+    for (int i = 1; i <= barriers; ++i) grid_barrier(gs, base + uint64_t(i), spin_limit);
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+        __hip_atomic_store(&gs->seq, s_seq + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 }  // namespace
 }  // namespace moe
+
+extern "C" moe_status moe_probe_grid_barrier(int32_t blocks, int32_t barriers, void* sync, uint32_t spin_limit,
+                                             void* stream) {
+    if (blocks < 1 || blocks > moe::kFusedMaxBlocks || barriers < 1 || barriers >= 65536 || !sync ||
+        (reinterpret_cast<uintptr_t>(sync) & 15u))
+        return MOE_ERR_INVALID_ARGUMENT;
+    moe::GridSync* gs = static_cast<moe::GridSync*>(sync);
+    void* params[] = {&gs, &barriers, &spin_limit};
+    const hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(moe::barrier_probe_kernel),
+                                                    dim3(blocks), dim3(256), params, 0,
+                                                    static_cast<hipStream_t>(stream));
+    return (e == hipSuccess && hipGetLastError() == hipSuccess) ? MOE_OK : MOE_ERR_DEVICE;
+}
 
 extern "C" moe_status moe_probe_mfma_bf16(int32_t blocks, int32_t iters, float* out, void* stream) {
     if (blocks < 1 || blocks > (1 << 20) || iters < 1 || iters > (1 << 24) || !out ||

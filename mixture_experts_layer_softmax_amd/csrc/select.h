@@ -1,5 +1,6 @@
 // select.h -- device building blocks shared by the routing and dispatch kernels: per-token
-// top-k selection by one wavefront, and the GEMM tile list of a dispatch.
+// top-k selection by one wavefront, the GEMM tile list of a dispatch, and the selection and
+// dispatch of a small batch by one block.
 #pragma once
 
 #include "device.h"
@@ -124,6 +125,84 @@ __device__ __forceinline__ void emit_tiles(int e, int E, int count, int start, i
         tiles[first + i] = t;
     }
     if (threadIdx.x == 0) *tile_count = min(total, cap);
+}
+
+// Small decode batches (any T <= 64): top-k selection and the whole dispatch (histogram, scan,
+// tile lists, stable scatter) by one block of NT >= E threads, so a decode step spends one
+// launch on it instead of four, or the single-launch decode kernel none.  Wavefront w selects
+// tokens w, w + NT/64, ... one after the other; thread e < E then owns expert e.  Same results
+// as topk_kernel + hist/scan/scatter: ids of a token in selection order, rows of an expert in
+// (t, j) order.  Output pointers may point to global memory or to the caller's LDS.  Every
+// thread of the block must call it.
+template <int EPL, int NT>
+__device__ __forceinline__ void select_dispatch_block(
+    const float* __restrict__ logits, int T, int E, int k, int renorm, int32_t* ids, float* tw,
+    int32_t* counts, int32_t* offsets, int32_t* sorted_token, int32_t* inv_perm, Tile* tiles1,
+    int* tile_count1, int bm1, Tile* tiles2, int* tile_count2, int bm2, int cap, int eb, int ee) {
+    static_assert(NT % kWave == 0 && NT <= kMaxExperts * 2, "whole wavefronts");
+    constexpr int NW = NT / kWave;
+    __shared__ int sids[kChunkTokens * kMaxTopK];
+    __shared__ int cnt[kMaxExperts];
+    __shared__ int wc[NW][kMaxExperts];
+    const int tid = threadIdx.x, w = tid / kWave;
+    for (int t = w; t < T; t += NW)
+        topk_token<EPL>(logits + size_t(t) * E, E, k, renorm, ids + size_t(t) * k, tw + size_t(t) * k,
+                        sids + t * k);
+    if (tid < E) cnt[tid] = 0;
+    __syncthreads();
+    const int A = T * k;
+    for (int a = tid; a < A; a += NT) {
+        const int id = clamp_expert(sids[a], E);
+        if (id >= eb && id < ee) atomicAdd(&cnt[id], 1);
+    }
+    __syncthreads();
+    const int c = tid < E ? cnt[tid] : 0;
+    int total;
+    const int start = block_exclusive_scan<NT>(c, &total);
+    if (tid < E) {
+        if (counts) counts[tid] = c;
+        offsets[tid] = start;
+    }
+    if (tid == 0) offsets[E] = total;
+    if (tiles1) emit_tiles<NT>(tid, E, c, start, bm1, tiles1, tile_count1, cap, eb);
+    if (tiles2) emit_tiles<NT>(tid, E, c, start, bm2, tiles2, tile_count2, cap, eb);
+    __syncthreads();
+    if (tid < E) cnt[tid] = start;  // next free row of each expert
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
+    for (int r0 = 0; r0 < A; r0 += NT) {
+        for (int i = tid; i < NW * kMaxExperts; i += NT) (&wc[0][0])[i] = 0;
+        __syncthreads();
+        const int a = r0 + tid;
+        const int id0 = a < A ? clamp_expert(sids[a], E) : 0;
+        const bool valid = a < A && id0 >= eb && id0 < ee;
+        if (a < A && !valid) inv_perm[a] = -1;
+        const int id = valid ? id0 : 0;
+        uint64_t peers = __ballot(valid);
+        for (int b = 0; b < nbits; ++b) {
+            const bool bit = (id >> b) & 1;
+            const uint64_t m = __ballot(valid && bit);
+            peers &= bit ? m : ~m;
+        }
+        const int rank = __popcll(peers & lanemask_lt());
+        if (valid && rank == 0) wc[w][id] = __popcll(peers);
+        __syncthreads();
+        if (valid) {
+            int prefix = 0;
+            for (int ww = 0; ww < w; ++ww) prefix += wc[ww][id];
+            const int pos = cnt[id] + prefix + rank;
+            sorted_token[pos] = a / k;
+            inv_perm[a] = pos;
+        }
+        __syncthreads();
+        if (tid < E) {
+            int add = 0;
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww) add += wc[ww][tid];
+            cnt[tid] += add;
+        }
+        __syncthreads();
+    }
 }
 
 }  // namespace moe

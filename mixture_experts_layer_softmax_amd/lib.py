@@ -19,14 +19,16 @@ LIB_PATH = os.path.join(PKG, "libmoe_mi355x.so")
 STATIC_SCRATCH_BYTES = 64 << 20  # MOE_STATIC_SCRATCH_BYTES
 MOE_F32, MOE_BF16, MOE_NVFP4, MOE_MXFP8, MOE_MXFP4 = 0, 1, 2, 3, 4
 GATE_UP_SWIGLU, DOWN = 0, 1
-PATH_AUTO, PATH_PREFILL, PATH_DECODE = 0, 1, 2
+PATH_AUTO, PATH_PREFILL, PATH_DECODE, PATH_DECODE_FUSED = 0, 1, 2, 3
 DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "nvfp4": MOE_NVFP4, "mxfp8": MOE_MXFP8, "mxfp4": MOE_MXFP4}
-PATHS = {"auto": PATH_AUTO, "prefill": PATH_PREFILL, "decode": PATH_DECODE}
+PATHS = {"auto": PATH_AUTO, "prefill": PATH_PREFILL, "decode": PATH_DECODE, "fused": PATH_DECODE_FUSED}
 
 #: every symbol the header declares
 EXPORTS = ("moe_status_string", "moe_workspace_size", "moe_packed_weights_size", "moe_pack_weights",
            "moe_pack_scales", "moe_route", "moe_permute", "moe_grouped_gemm", "moe_combine", "moe_forward",
-           "moe_quantize_mxfp8", "moe_probe_mfma_bf16", "moe_probe_read", "moe_forward_static")
+           "moe_quantize_mxfp8", "moe_probe_mfma_bf16", "moe_probe_read", "moe_forward_static",
+           "moe_probe_grid_barrier")
+PROBE_SYNC_BYTES = 8256  # MOE_PROBE_SYNC_BYTES
 LAYOUT_ROW_MAJOR, LAYOUT_PACKED = 0, 1
 
 
@@ -88,6 +90,8 @@ def load() -> C.CDLL:
             L.moe_probe_mfma_bf16.argtypes = [C.c_int32, C.c_int32, vp, vp]
             L.moe_probe_read.restype = i32
             L.moe_probe_read.argtypes = [vp, sz, vp, vp]
+            L.moe_probe_grid_barrier.restype = i32
+            L.moe_probe_grid_barrier.argtypes = [C.c_int32, C.c_int32, vp, C.c_uint32, vp]
             L.moe_forward.restype = i32
             L.moe_forward.argtypes = [P, vp, vp, vp, C.POINTER(ExpertWeights), vp, vp, vp, vp, vp,
                                       vp, vp, vp, sz, vp]
@@ -217,3 +221,9 @@ def probe_read(buf, out, stream=None):
     n = buf.numel() * buf.element_size()
     _check(load().moe_probe_read(_ptr(buf), n, _ptr(out), _stream(stream)), "moe_probe_read")
     return float(n)
+
+
+def probe_grid_barrier(blocks, barriers, sync, spin_limit=1 << 20, stream=None):
+    """Launch `barriers` grid barriers of the single-launch decode kernel on `blocks` blocks."""
+    _check(load().moe_probe_grid_barrier(int(blocks), int(barriers), _ptr(sync), int(spin_limit),
+                                         _stream(stream)), "moe_probe_grid_barrier")
