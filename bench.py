@@ -250,9 +250,10 @@ def _find_clocks(d):
     return None
 
 
-def platform_info(torch):
+def platform_info(torch, skip_clocks=False):
     """ROCm / HIP versions, the device name, and the GPU clocks as amd-smi reports them (a child
-    process; None where the tool is missing or says nothing parseable)."""
+    process; None where the tool is missing, says nothing parseable, runs under a profiler, or
+    skip_clocks is set)."""
     import subprocess
 
     info = dict(hip=getattr(torch.version, "hip", None), torch=torch.__version__)
@@ -265,6 +266,11 @@ def platform_info(torch):
     except Exception:  # pragma: no cover
         info["device"] = None
     clocks = None
+    if skip_clocks or any(k.startswith("ROCPROF") for k in os.environ):
+        # under a profiler the child would load the profiler's tool, which opens the GPU in the
+        # amd-smi launcher before it starts its interpreter: leave the clocks out there
+        info["clocks_mhz"] = None
+        return info
     try:
         r = subprocess.run(["amd-smi", "metric", "-g", "0", "--clock", "--json"], capture_output=True,
                            text=True, timeout=30)
@@ -373,6 +379,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probes", action="store_true",
                     help="skip the measured-peak probes (bf16 MFMA loop, 4 GiB read stream)")
+    ap.add_argument("--no-clocks", action="store_true",
+                    help="do not start amd-smi for the GPU clocks (also skipped under rocprofv3)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run one 512 MiB device copy (counter calibration)")
     ap.add_argument("--ep-size", type=int, default=1,
@@ -402,7 +410,7 @@ def main() -> int:
               file=sys.stderr)
         return 2
     wl = synth.WORKLOADS[args.workload]
-    plat = platform_info(torch)
+    plat = platform_info(torch, args.no_clocks)
     held = None
     if args.ep_size > 1:
         if wl.experts % args.ep_size:
