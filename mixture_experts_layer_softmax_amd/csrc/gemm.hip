@@ -232,7 +232,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_fallback_kernel(GemmArgs g) 
 // ---------------------------------------------------------------------------------------
 
 
-template <int KIND>
+template <int KIND, bool A32>
 __global__ __launch_bounds__(512, 1) void gemm_prefill_bf16_kernel(GemmArgs g) {
     constexpr int BM = 256, BN = 256, BKS = 32;
     constexpr int HALF = (KIND == kGateUp) ? BN / 2 : BN;
@@ -252,18 +252,24 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_bf16_kernel(GemmArgs g) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7
     const int wr = wave >> 2, wc = wave & 3;                      // 2 x 4 wavefronts
+    // row groups mi * 2 + wr < nsub of this wavefront hold rows: mi < na (a scalar count, so
+    // that each group's MFMAs sit behind one scalar compare and branch)
+    const int na = __builtin_amdgcn_readfirstlane((nsub - wr + 1) >> 1);
     const int K = g.K;
 
     const char* pa[2];
+    uint32_t va[2];  // the same as offsets from a_s (scalar-base loads: A32 or the packed hid)
     // A operand: gathered rows (64 bytes per row and stage), or for the down GEMM of a forward
     // the packed hid image of this row tile (one contiguous 16 KiB per stage, like the weights)
     const bool apk = KIND == kDown && g.hid_packed;
     const int astep = apk ? 512 : 2;  // bytes per K element along the A stream
+    const char* const a_s = static_cast<const char*>(g.a) +
+                            (apk ? size_t(item / ncols) * size_t(K / BKS) * 16384 : 0);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         if (apk) {
-            pa[i] = static_cast<const char*>(g.a) + size_t(item / ncols) * size_t(K / BKS) * 16384 +
-                    (i * 8 + wave) * 1024 + lane * 16;
+            va[i] = (i * 8 + wave) * 1024 + lane * 16;
+            pa[i] = a_s + va[i];
             continue;
         }
         const int row = (i * 8 + wave) * 16 + (lane >> 2);
@@ -271,15 +277,18 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_bf16_kernel(GemmArgs g) {
         const int rr = min(r0 + row, r1 - 1);
         int src = g.a_rows ? g.a_rows[rr] : rr;
         src = src < 0 ? 0 : (src >= g.a_rows_limit ? g.a_rows_limit - 1 : src);
-        pa[i] = static_cast<const char*>(g.a) + (size_t(src) * K + ch * 8) * 2;
+        pa[i] = a_s + (size_t(src) * K + ch * 8) * 2;
+        va[i] = static_cast<uint32_t>((size_t(src) * K + ch * 8) * 2);
     }
+    const bool a_scalar = apk || A32;
     // B operand: packed weights (each stage of the 256-row tile is one contiguous 16 KiB, the LDS
     // image), or row-major weights read like the gathered activations (64 bytes per weight row
     // and stage, the lane's chunk taken from the slot it lands in)
     const char* pb[2];
     size_t wst;  // bytes from one 32-element stage of the lane's chunk to the next
+    const char* const wblk = static_cast<const char*>(g.w) + (size_t(e) * ncols + nt) * size_t(K / BKS) * 16384;
+    const uint32_t vb = wave * 1024 + lane * 16;  // packed: the lane's place in a stage block (+ 8 KiB i)
     if (g.wpacked) {
-        const char* const wblk = static_cast<const char*>(g.w) + (size_t(e) * ncols + nt) * size_t(K / BKS) * 16384;
 #pragma unroll
         for (int i = 0; i < 2; ++i) pb[i] = wblk + (i * 8 + wave) * 1024 + lane * 16;
         wst = 16384;
@@ -312,10 +321,20 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_bf16_kernel(GemmArgs g) {
 #define MOE_ISSUE8(SA, SB, K0)                                                                  \
     do {                                                                                        \
         const int k0_ = (K0);                                                                   \
-        _Pragma("unroll") for (int i = 0; i < 2; ++i)                                           \
-            dma16(pa[i] + k0_ * astep, &SA[(i * 8 + wave) * 64]);                               \
-        _Pragma("unroll") for (int i = 0; i < 2; ++i)                                           \
-            dma16(pb[i] + (k0_ / BKS) * wst, &SB[(i * 8 + wave) * 64]);                         \
+        if (a_scalar) {                                                                         \
+            _Pragma("unroll") for (int i = 0; i < 2; ++i)                                       \
+                dma16s(a_s + size_t(k0_) * astep, va[i], &SA[(i * 8 + wave) * 64]);             \
+        } else {                                                                                \
+            _Pragma("unroll") for (int i = 0; i < 2; ++i)                                       \
+                dma16(pa[i] + k0_ * astep, &SA[(i * 8 + wave) * 64]);                           \
+        }                                                                                       \
+        if (g.wpacked) {                                                                        \
+            _Pragma("unroll") for (int i = 0; i < 2; ++i)                                       \
+                dma16s(wblk + size_t(k0_ / BKS) * 16384, vb + i * 8192, &SB[(i * 8 + wave) * 64]); \
+        } else {                                                                                \
+            _Pragma("unroll") for (int i = 0; i < 2; ++i)                                       \
+                dma16(pb[i] + (k0_ / BKS) * wst, &SB[(i * 8 + wave) * 64]);                     \
+        }                                                                                       \
     } while (0)
 #define MOE_READ8(SA, SB, AF, BF)                                                               \
     do {                                                                                        \
@@ -328,7 +347,7 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_bf16_kernel(GemmArgs g) {
 #define MOE_MFMA8(AF, BF)                                                                       \
     do {                                                                                        \
         _Pragma("unroll") for (int mi = 0; mi < 8; ++mi) {                                      \
-            if (mi * 2 + wr < nsub) {                                                           \
+            if (__builtin_expect(mi < na_, 1)) {                                                \
                 _Pragma("unroll") for (int ni = 0; ni < 4; ++ni) acc[mi][ni] =                  \
                     __builtin_amdgcn_mfma_f32_16x16x32_bf16(AF[mi], BF[ni], acc[mi][ni], 0, 0, 0); \
             }                                                                                   \
@@ -341,6 +360,7 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_bf16_kernel(GemmArgs g) {
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     bf16x8_t a0[8], b0[4], a1[8], b1[4];
+    int na_;  // na, re-read each stage so that the group tests stay scalar compares
 
     const int nk = K / BKS;
     const int last = (nk - 1) * BKS;
@@ -354,24 +374,32 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_bf16_kernel(GemmArgs g) {
     for (int s = 0;; s += 4) {
         wait_vm_lgkm0<8>();
         block_barrier();
+        na_ = na;
+        asm volatile("" : "+s"(na_));
         MOE_READ8(sA1, sB1, a1, b1);
         MOE_ISSUE8(sA0, sB0, min((s + 4) * BKS, last));
         MOE_MFMA8(a0, b0);
         if (s + 1 >= nk) break;
         wait_vm_lgkm0<8>();
         block_barrier();
+        na_ = na;
+        asm volatile("" : "+s"(na_));
         MOE_READ8(sA2, sB2, a0, b0);
         MOE_ISSUE8(sA1, sB1, min((s + 5) * BKS, last));
         MOE_MFMA8(a1, b1);
         if (s + 2 >= nk) break;
         wait_vm_lgkm0<8>();
         block_barrier();
+        na_ = na;
+        asm volatile("" : "+s"(na_));
         MOE_READ8(sA3, sB3, a1, b1);
         MOE_ISSUE8(sA2, sB2, min((s + 6) * BKS, last));
         MOE_MFMA8(a0, b0);
         if (s + 3 >= nk) break;
         wait_vm_lgkm0<8>();
         block_barrier();
+        na_ = na;
+        asm volatile("" : "+s"(na_));
         MOE_READ8(sA0, sB0, a0, b0);
         MOE_ISSUE8(sA3, sB3, min((s + 7) * BKS, last));
         MOE_MFMA8(a1, b1);
@@ -456,7 +484,7 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_bf16_kernel(GemmArgs g) {
 // iteration also publishes each raw row to the thread that decodes it.
 // ---------------------------------------------------------------------------------------
 
-template <int KIND, int NW, bool PK>
+template <int KIND, int NW, bool PK, bool A32>
 __global__ __launch_bounds__(NW * 64, 1) void gemm_prefill_nvfp4_kernel(GemmArgs g) {
     static_assert(NW == 4 || NW == 8, "4 or 8 wavefronts");
     constexpr int BM = 256, BN = 256, BKS = 32;
@@ -483,10 +511,16 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_prefill_nvfp4_kernel(GemmArgs
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wr = wave / NC, wc = wave % NC;
+    // row groups mi * 2 + wr < nsub of this wavefront hold rows: mi < na (a scalar count, so
+    // that each group's MFMAs sit behind one scalar compare and branch)
+    const int na = __builtin_amdgcn_readfirstlane((nsub - wr + 1) >> 1);
     const int K = g.K;
     const int Nw = (KIND == kGateUp) ? 2 * g.F : g.N;
 
+    // A32: every activation row offset fits 32 bits, so the loads take the scalar-base form
     const char* pa[A_DMA];
+    uint32_t va[A_DMA];
+    const char* const a_s = static_cast<const char*>(g.a);
 #pragma unroll
     for (int i = 0; i < A_DMA; ++i) {
         const int row = (i * NW + wave) * 16 + (lane >> 2);
@@ -494,7 +528,8 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_prefill_nvfp4_kernel(GemmArgs
         const int rr = min(r0 + row, r1 - 1);
         int src = g.a_rows ? g.a_rows[rr] : rr;
         src = src < 0 ? 0 : (src >= g.a_rows_limit ? g.a_rows_limit - 1 : src);
-        pa[i] = static_cast<const char*>(g.a) + (size_t(src) * K + ch * 8) * 2;
+        pa[i] = a_s + (size_t(src) * K + ch * 8) * 2;
+        va[i] = static_cast<uint32_t>((size_t(src) * K + ch * 8) * 2);
     }
     // raw weights: wavefront w moves the nibbles (NW = 4: and the scale words) of weight rows
     // 64 (w & 3) + lane, for NW = 8 wavefronts 4..7 the scale words; tile row r holds, per
@@ -518,6 +553,9 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_prefill_nvfp4_kernel(GemmArgs
                               : reinterpret_cast<const char*>(g.wscale) + wrow_g * (K / 16);
     // NW = 8: a wavefront moves either nibbles (waves 0-3) or scale words (4-7): one pointer
     const char* const pw = (NW == 8 && wave >= 4) ? ps : pq;
+    // PK: the tile's stage blocks as scalar bases, the row's place in a block as the offset
+    const char* const wq_s = static_cast<const char*>(g.w) + tb * (K / 32) * 4096;
+    const char* const ws_s = reinterpret_cast<const char*>(g.wscale) + tb * (K / 64) * 1024;
     // weight row groups of this wavefront: gate/up, NB/2 gate groups then their up groups
     int gb[NB];
     int gcol;  // first hid column (gate/up) or output column (down) of this wavefront
@@ -539,16 +577,24 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_prefill_nvfp4_kernel(GemmArgs
     do {                                                                                        \
         const int k0_ = (K0);                                                                   \
         _Pragma("unroll") for (int i = 0; i < A_DMA; ++i)                                       \
-            dma16(pa[i] + k0_ * 2, &SA[(i * NW + wave) * 64]);                                  \
+            if constexpr (A32) dma16s(a_s + k0_ * 2, va[i], &SA[(i * NW + wave) * 64]);       \
+            else dma16(pa[i] + k0_ * 2, &SA[(i * NW + wave) * 64]);                             \
     } while (0)
     // nibbles of stage k0/32, and the scale word holding its two scales (stages 2m, 2m+1)
 #define MOE_ISSUE_W(SN, SS, K0)                                                                 \
     do {                                                                                        \
         const int k0_ = (K0);                                                                   \
-        if (NW == 4 || wave < 4)                                                                \
-            dma16((NW == 8 ? pw : pq) + (PK ? (k0_ >> 5) * 4096 : k0_ / 2), &SN[(wave & 3) * 64]); \
-        if (NW == 4 || wave >= 4)                                                               \
-            dma4((NW == 8 ? pw : ps) + (PK ? (k0_ >> 6) * 1024 : ((k0_ >> 4) & ~3)), &SS[(wave & 3) * 64]); \
+        if constexpr (PK) {                                                                     \
+            if (NW == 4 || wave < 4)                                                            \
+                dma16s(wq_s + (k0_ >> 5) * 4096, mrow * 16, &SN[(wave & 3) * 64]);              \
+            if (NW == 4 || wave >= 4)                                                           \
+                dma4s(ws_s + (k0_ >> 6) * 1024, mrow * 4, &SS[(wave & 3) * 64]);                \
+        } else {                                                                                \
+            if (NW == 4 || wave < 4)                                                            \
+                dma16((NW == 8 ? pw : pq) + k0_ / 2, &SN[(wave & 3) * 64]);                     \
+            if (NW == 4 || wave >= 4)                                                           \
+                dma4((NW == 8 ? pw : ps) + ((k0_ >> 4) & ~3), &SS[(wave & 3) * 64]);            \
+        }                                                                                       \
     } while (0)
     // NW = 4: thread t decodes weight row t; NW = 8: half h = t & 1 of row t >> 1 (chunks
     // 2h, 2h+1, scale h)
@@ -557,7 +603,8 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_prefill_nvfp4_kernel(GemmArgs
         if constexpr (NW == 4) {                                                                \
             const uint4 nib_ = SN[tid];                                                         \
             const uint32_t sw_ = SS[tid] >> ((((K0) >> 5) & 1) * 16);                           \
-            const float s0_ = e4m3_value(sw_ & 0xffu), s1_ = e4m3_value((sw_ >> 8) & 0xffu);      \
+            const float s0_ = __builtin_amdgcn_cvt_scalef32_f32_fp8(sw_, 1.0f, 0);              \
+            const float s1_ = __builtin_amdgcn_cvt_scalef32_f32_fp8(sw_, 1.0f, 1);              \
             SB[lds_slot32(tid, 0)] = dequant8(nib_.x, s0_);                                     \
             SB[lds_slot32(tid, 1)] = dequant8(nib_.y, s0_);                                     \
             SB[lds_slot32(tid, 2)] = dequant8(nib_.z, s1_);                                     \
@@ -566,7 +613,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_prefill_nvfp4_kernel(GemmArgs
             const int row_ = tid >> 1, h_ = tid & 1;                                            \
             const uint2 nib_ = reinterpret_cast<const uint2*>(SN)[row_ * 2 + h_];               \
             const uint32_t sw_ = SS[row_] >> ((((K0) >> 5) & 1) * 16 + 8 * h_);                 \
-            const float sc_ = e4m3_value(sw_ & 0xffu);                                          \
+            const float sc_ = __builtin_amdgcn_cvt_scalef32_f32_fp8(sw_, 1.0f, 0);              \
             SB[lds_slot32(row_, 2 * h_)] = dequant8(nib_.x, sc_);                               \
             SB[lds_slot32(row_, 2 * h_ + 1)] = dequant8(nib_.y, sc_);                           \
         }                                                                                       \
@@ -579,10 +626,10 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_prefill_nvfp4_kernel(GemmArgs
         _Pragma("unroll") for (int mi = 0; mi < 8; ++mi) AF[mi] =                               \
             __builtin_bit_cast(bf16x8_t, SA[lds_slot32((mi * 2 + wr) * 16 + (lane & 15), ch_)]); \
     } while (0)
-#define MOE_MFMA(AF, BF)                                                                        \
+#define MOE_MFMA(AF, BF, FULLC)                                                                 \
     do {                                                                                        \
         _Pragma("unroll") for (int mi = 0; mi < 8; ++mi) {                                      \
-            if (mi * 2 + wr < nsub) {                                                           \
+            if (FULLC || __builtin_expect(mi < na_, 1)) {                                       \
                 _Pragma("unroll") for (int ni = 0; ni < NB; ++ni) acc[mi][ni] =                 \
                     __builtin_amdgcn_mfma_f32_16x16x32_bf16(AF[mi], BF[ni], acc[mi][ni], 0, 0, 0); \
             }                                                                                   \
@@ -590,16 +637,16 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_prefill_nvfp4_kernel(GemmArgs
     } while (0)
     // NW = 8: the MFMAs of one stage with the decode of raw stage K0 (into SB) interleaved: after
     // row group mi's MFMAs, output word mi of this thread's 8 (two chunks of four words)
-#define MOE_MFMA_DEC(AF, BF, SB, NIB, SW, K0)                                                   \
+#define MOE_MFMA_DEC(AF, BF, SB, NIB, SW, K0, FULLC)                                            \
     do {                                                                                        \
         typedef __attribute__((ext_vector_type(2))) float f2_;                                  \
         const int row_ = tid >> 1, h_ = tid & 1;                                                \
         const uint2 nib_ = NIB;                                                                 \
         const uint32_t sw_ = (SW) >> ((((K0) >> 5) & 1) * 16 + 8 * h_);                         \
-        const float sc_ = e4m3_value(sw_ & 0xffu);                                              \
+        const float sc_ = __builtin_amdgcn_cvt_scalef32_f32_fp8(sw_, 1.0f, 0);                  \
         uint32_t w_[8];                                                                         \
         _Pragma("unroll") for (int mi = 0; mi < 8; ++mi) {                                      \
-            if (mi * 2 + wr < nsub) {                                                           \
+            if (FULLC || __builtin_expect(mi < na_, 1)) {                                       \
                 _Pragma("unroll") for (int ni = 0; ni < NB; ++ni) acc[mi][ni] =                 \
                     __builtin_amdgcn_mfma_f32_16x16x32_bf16(AF[mi], BF[ni], acc[mi][ni], 0, 0, 0); \
             }                                                                                   \
@@ -646,10 +693,12 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_prefill_nvfp4_kernel(GemmArgs
     MOE_ISSUE_W(sN0, sS0, min(4 * BKS, last));
     uint2 nibd_ = make_uint2(0, 0);  // raw weight words this thread decodes in the next MFMA block
     uint32_t swd_ = 0;
-    for (int s = 0;; s += 4) {
-#define MOE_IT(S, FA, FB, GA, GB, SAr, SBr, SAw, SNw, SSw, SNd, SSd, SBd)      \
+    int na_;  // na, re-read each stage so that the group tests stay scalar compares
+#define MOE_IT(FULLC, S, FA, FB, GA, GB, SAr, SBr, SAw, SNw, SSw, SNd, SSd, SBd)      \
         wait_vm_lgkm0<2 * OPS>();                                            \
         block_barrier();                                                     \
+        na_ = na;                                                            \
+        asm volatile("" : "+s"(na_));                                        \
         if constexpr (NW == 8) {                                             \
             nibd_ = reinterpret_cast<const uint2*>(SNd)[tid];                \
             swd_ = SSd[tid >> 1];                                            \
@@ -658,19 +707,23 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_prefill_nvfp4_kernel(GemmArgs
         MOE_ISSUE_A(SAw, min((s + S + 4) * BKS, last));                      \
         MOE_ISSUE_W(SNw, SSw, min((s + S + 5) * BKS, last));                 \
         if constexpr (NW == 8) {                                             \
-            MOE_MFMA_DEC(FA, FB, SBd, nibd_, swd_, min((s + S + 2) * BKS, last)); \
+            MOE_MFMA_DEC(FA, FB, SBd, nibd_, swd_, min((s + S + 2) * BKS, last), FULLC); \
             if (s + S + 1 >= nk) break;                                      \
         } else {                                                             \
-            MOE_MFMA(FA, FB);                                                \
+            MOE_MFMA(FA, FB, FULLC);                                         \
             if (s + S + 1 >= nk) break;                                      \
             MOE_DECODE(SNd, SSd, SBd, min((s + S + 2) * BKS, last));         \
         }
-        MOE_IT(0, a0, b0, a1, b1, sA1, sB1, sA0, sN1, sS1, sN2, sS2, sB0)
-        MOE_IT(1, a1, b1, a0, b0, sA2, sB0, sA1, sN2, sS2, sN3, sS3, sB1)
-        MOE_IT(2, a0, b0, a1, b1, sA3, sB1, sA2, sN3, sS3, sN0, sS0, sB0)
-        MOE_IT(3, a1, b1, a0, b0, sA0, sB0, sA3, sN0, sS0, sN1, sS1, sB1)
-#undef MOE_IT
+#define MOE_LOOP(FULLC)                                                      \
+    for (int s = 0;; s += 4) {                                           \
+        MOE_IT(FULLC, 0, a0, b0, a1, b1, sA1, sB1, sA0, sN1, sS1, sN2, sS2, sB0) \
+        MOE_IT(FULLC, 1, a1, b1, a0, b0, sA2, sB0, sA1, sN2, sS2, sN3, sS3, sB1) \
+        MOE_IT(FULLC, 2, a0, b0, a1, b1, sA3, sB1, sA2, sN3, sS3, sN0, sS0, sB0) \
+        MOE_IT(FULLC, 3, a1, b1, a0, b0, sA0, sB0, sA3, sN0, sS0, sN1, sS1, sB1) \
     }
+    MOE_LOOP(false)
+#undef MOE_LOOP
+#undef MOE_IT
     wait_vm_lgkm0<0>();
 #undef MOE_ISSUE_A
 #undef MOE_ISSUE_W
@@ -899,22 +952,34 @@ hipError_t launch_gemm(const GemmArgs& g, int family, int max_tiles, hipStream_t
             hipLaunchKernelGGL((gemm_f32_kernel<kDown>), grid, block, 0, s, g);
     } else if (family == kFamPrefill && g.wfmt == kWBF16) {  // packed weights: F % 128 == 0, H % 256 == 0
         const dim3 grid = prefill_grid(g, max_tiles, 256);
-        if (up)
-            hipLaunchKernelGGL((gemm_prefill_bf16_kernel<kGateUp>), grid, dim3(512), 0, s, g);
+        // the scalar-base activation loads need every row offset below 4 GiB
+        const bool a32 = size_t(g.a_rows_limit) * size_t(g.K) * 2 <= 0xffffffffull;
+        if (up && a32)
+            hipLaunchKernelGGL((gemm_prefill_bf16_kernel<kGateUp, true>), grid, dim3(512), 0, s, g);
+        else if (up)
+            hipLaunchKernelGGL((gemm_prefill_bf16_kernel<kGateUp, false>), grid, dim3(512), 0, s, g);
+        else if (a32)
+            hipLaunchKernelGGL((gemm_prefill_bf16_kernel<kDown, true>), grid, dim3(512), 0, s, g);
         else
-            hipLaunchKernelGGL((gemm_prefill_bf16_kernel<kDown>), grid, dim3(512), 0, s, g);
+            hipLaunchKernelGGL((gemm_prefill_bf16_kernel<kDown, false>), grid, dim3(512), 0, s, g);
     } else if (family == kFamPrefill && g.wfmt == kWNVFP4 && g.F % 128 == 0) {
         const dim3 grid = prefill_grid(g, max_tiles, 256);
         // packed weights: 8 wavefronts for both kinds (gate/up 2.97 -> 2.69 ms against 4 on
         // the NVFP4 prefill shape); row-major: 4 for gate/up, where 4 measured faster
-        if (up && g.wpacked)
-            hipLaunchKernelGGL((gemm_prefill_nvfp4_kernel<kGateUp, 8, true>), grid, dim3(512), 0, s, g);
+        // the scalar-base activation loads need every row offset below 4 GiB
+        const bool a32 = size_t(g.a_rows_limit) * size_t(g.K) * 2 <= 0xffffffffull;
+        if (up && g.wpacked && a32)
+            hipLaunchKernelGGL((gemm_prefill_nvfp4_kernel<kGateUp, 8, true, true>), grid, dim3(512), 0, s, g);
+        else if (up && g.wpacked)
+            hipLaunchKernelGGL((gemm_prefill_nvfp4_kernel<kGateUp, 8, true, false>), grid, dim3(512), 0, s, g);
         else if (up)
-            hipLaunchKernelGGL((gemm_prefill_nvfp4_kernel<kGateUp, 4, false>), grid, dim3(256), 0, s, g);
+            hipLaunchKernelGGL((gemm_prefill_nvfp4_kernel<kGateUp, 4, false, false>), grid, dim3(256), 0, s, g);
+        else if (g.wpacked && a32)
+            hipLaunchKernelGGL((gemm_prefill_nvfp4_kernel<kDown, 8, true, true>), grid, dim3(512), 0, s, g);
         else if (g.wpacked)
-            hipLaunchKernelGGL((gemm_prefill_nvfp4_kernel<kDown, 8, true>), grid, dim3(512), 0, s, g);
+            hipLaunchKernelGGL((gemm_prefill_nvfp4_kernel<kDown, 8, true, false>), grid, dim3(512), 0, s, g);
         else
-            hipLaunchKernelGGL((gemm_prefill_nvfp4_kernel<kDown, 8, false>), grid, dim3(512), 0, s, g);
+            hipLaunchKernelGGL((gemm_prefill_nvfp4_kernel<kDown, 8, false, false>), grid, dim3(512), 0, s, g);
     } else if (family == kFamPrefill) {
         if (g.wfmt != kWNVFP4 || g.wpacked) return hipErrorInvalidValue;  // PACKED NVFP4 needs F % 128 == 0
         launch_mfma<PF_BM, PF_BN, PF_WM, PF_WN>(g, max_tiles, s);

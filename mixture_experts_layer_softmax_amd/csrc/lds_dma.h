@@ -42,6 +42,26 @@ __device__ __forceinline__ void dma4(const void* src, const void* lds_base) {
                  : "memory");
 }
 
+// The same two loads with a scalar base address and a 32-bit per-lane byte offset (the global
+// instruction's saddr form): the per-stage address step is a scalar add, with no 64-bit vector
+// address arithmetic per load.  The caller guarantees that every offset fits 32 bits.
+__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, const void* lds_base) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+        static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_base)));
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(m0)
+                 : "memory");
+}
+__device__ __forceinline__ void dma4s(const void* sbase, uint32_t voff, const void* lds_base) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+        static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_base)));
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(m0)
+                 : "memory");
+}
+
 // 64-byte LDS rows of four 16-byte chunks: chunk ch of row r sits in slot ch ^ ((r >> 1) & 3),
 // so that the fragment reads of 8 consecutive rows at one chunk hit distinct banks.
 __device__ __forceinline__ int lds_slot32(int row, int ch) { return row * 4 + (ch ^ ((row >> 1) & 3)); }
