@@ -603,8 +603,8 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_prefill_nvfp4_kernel(GemmArgs
         if constexpr (NW == 4) {                                                                \
             const uint4 nib_ = SN[tid];                                                         \
             const uint32_t sw_ = SS[tid] >> ((((K0) >> 5) & 1) * 16);                           \
-            const float s0_ = __builtin_amdgcn_cvt_scalef32_f32_fp8(sw_, 1.0f, 0);              \
-            const float s1_ = __builtin_amdgcn_cvt_scalef32_f32_fp8(sw_, 1.0f, 1);              \
+            const float s0_ = e4m3_value(sw_);                                                  \
+            const float s1_ = e4m3_value(sw_ >> 8);                                             \
             SB[lds_slot32(tid, 0)] = dequant8(nib_.x, s0_);                                     \
             SB[lds_slot32(tid, 1)] = dequant8(nib_.y, s0_);                                     \
             SB[lds_slot32(tid, 2)] = dequant8(nib_.z, s1_);                                     \
@@ -613,7 +613,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_prefill_nvfp4_kernel(GemmArgs
             const int row_ = tid >> 1, h_ = tid & 1;                                            \
             const uint2 nib_ = reinterpret_cast<const uint2*>(SN)[row_ * 2 + h_];               \
             const uint32_t sw_ = SS[row_] >> ((((K0) >> 5) & 1) * 16 + 8 * h_);                 \
-            const float sc_ = __builtin_amdgcn_cvt_scalef32_f32_fp8(sw_, 1.0f, 0);              \
+            const float sc_ = e4m3_value(sw_);                                                  \
             SB[lds_slot32(row_, 2 * h_)] = dequant8(nib_.x, sc_);                               \
             SB[lds_slot32(row_, 2 * h_ + 1)] = dequant8(nib_.y, sc_);                           \
         }                                                                                       \
@@ -643,7 +643,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_prefill_nvfp4_kernel(GemmArgs
         const int row_ = tid >> 1, h_ = tid & 1;                                                \
         const uint2 nib_ = NIB;                                                                 \
         const uint32_t sw_ = (SW) >> ((((K0) >> 5) & 1) * 16 + 8 * h_);                         \
-        const float sc_ = __builtin_amdgcn_cvt_scalef32_f32_fp8(sw_, 1.0f, 0);                  \
+        const float sc_ = e4m3_value(sw_);                                                      \
         uint32_t w_[8];                                                                         \
         _Pragma("unroll") for (int mi = 0; mi < 8; ++mi) {                                      \
             if (FULLC || __builtin_expect(mi < na_, 1)) {                                       \
