@@ -95,13 +95,19 @@ def gate_up_work(wl, active: int, rows: int, tokens_read: int):
     return flops, nbytes
 
 
-def kernel_source(wdt: str) -> str:
-    """File of the gate/up GEMM kernel of a weight format."""
-    return os.path.join(CSRC, "mx.hip" if wdt.startswith("mx") else "gemm.hip")
+def kernel_source(wdt: str) -> list:
+    """Source files of the gate/up GEMM kernel of a weight format (the kernel file and the
+    headers its kernels are built from)."""
+    kern = ["mx.hip"] if wdt.startswith("mx") else ["gemm.hip", "gemv.h"]
+    return [os.path.join(CSRC, f) for f in kern + ["lds_dma.h", "device.h", "launch.h"]]
 
 
-def source_hash(path: str) -> str:
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+def source_hash(paths) -> str:
+    """First 16 hex digits of the sha256 of the files' contents, concatenated in order."""
+    h = hashlib.sha256()
+    for p in ([paths] if isinstance(paths, str) else paths):
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str, wdt: str):

@@ -2,6 +2,7 @@
 
     python profile_summary.py kernels RUN_DIR TAG --last K --cmd "rocprofv3 ... -- python3 bench.py ..."
     python profile_summary.py traffic FETCH_DIR WRITE_DIR TAG WORKLOAD KERNEL SOURCE --cmd-fetch ... --cmd-write ...
+    python profile_summary.py bench RUN_DIR
 
 ``kernels`` reads ``*_kernel_trace.csv`` of a ``rocprofv3 --kernel-trace`` run and writes
 ``profiles/TAG_kernel_stats.md``: per kernel, every launch (what ``--stats`` prints) and the last
@@ -9,12 +10,17 @@ K launches only.  bench.py launches each kernel of the forward K times in its ti
 its warm-up, and the gate/up GEMM K more times alone (the launches its roofline figure times),
 so the last K launches of a kernel are the timed ones.
 
+``bench`` reads the bench.py JSON lines saved as ``NAME.json`` beside ``NAME.cmd`` (the command
+that printed it) in a directory, and writes ``profiles/bench_lines.md``: one row per run with
+the headline figures, then every line in full.
+
 ``traffic`` reads the ``*_counter_collection.csv`` of two ``rocprofv3 --pmc FETCH_SIZE`` /
 ``--pmc WRITE_SIZE`` runs of bench.py with ``--calibration-copy`` and writes
 ``profiles/TAG_traffic.md`` and the WORKLOAD entry of ``profiles/traffic.json``: the dominant
 kernel's KiB per launch, scaled by what the same counter reads for the 512 MiB device copy at
-the end of the run, with the hash of the kernel's source file so that bench.py stops quoting
-it once the kernel changes.
+the end of the run, with the hash of the kernel's source files (SOURCE: comma-separated paths
+from the repository root, in the order bench.kernel_source lists them) so that bench.py stops
+quoting it once the kernel changes.
 """
 from __future__ import annotations
 
@@ -94,8 +100,10 @@ def traffic(fetch_dir: str, write_dir: str, tag: str, workload: str, kernel: str
     ff, fw = copied / copy_f, copied / copy_w
     fetch_b = sum(kf) / len(kf) * 1024 * ff
     write_b = sum(kw) / len(kw) * 1024 * fw
-    src = os.path.join(ROOT, source)
-    h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in source.split(","):
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    h = h.hexdigest()[:16]
     out = ["# HBM traffic counters: %s, %s workload" % (kernel, workload), "",
            "Commands (one counter per run; bench.py ends with one 512 MiB device copy for calibration):", "",
            "    " + cmd_fetch, "    " + cmd_write, "",
@@ -109,7 +117,7 @@ def traffic(fetch_dir: str, write_dir: str, tag: str, workload: str, kernel: str
            "| HBM bytes read per launch (scaled) | %.4g |" % fetch_b,
            "| HBM bytes written per launch (scaled) | %.4g |" % write_b,
            "| HBM bytes per launch (scaled) | %.4g |" % (fetch_b + write_b),
-           "| %s sha256 (first 16 hex) when taken | %s |" % (os.path.basename(source), h)]
+           "| sha256 (first 16 hex) of %s when taken | %s |" % (", ".join(os.path.basename(f) for f in source.split(",")), h)]
     text = "\n".join(out) + "\n"
     open(os.path.join(PROFILES, "%s_traffic.md" % tag), "w").write(text)
     tj = os.path.join(PROFILES, "traffic.json")
@@ -118,6 +126,37 @@ def traffic(fetch_dir: str, write_dir: str, tag: str, workload: str, kernel: str
                        write_bytes=write_b, fetch_factor=ff, write_factor=fw,
                        gemm_source_sha256_16=h, summary="%s_traffic.md" % tag)
     json.dump(d, open(tj, "w"), indent=1)
+    return text
+
+
+def bench(run_dir: str) -> str:
+    rows, raw = [], []
+    for path in sorted(glob.glob(os.path.join(run_dir, "*.json"))):
+        name = os.path.splitext(os.path.basename(path))[0]
+        lines = [l for l in open(path).read().splitlines() if l.startswith("{")]
+        if not lines:
+            continue
+        d = json.loads(lines[-1])
+        cmd = open(os.path.join(run_dir, name + ".cmd")).read().strip()
+        st = d.get("step_ms") or {}
+        rf = d.get("roofline") or {}
+        rows.append("| %s | `%s` | %.6g %s | %s | %s | %s | %s |" % (
+            name, cmd, d["value"], d["unit"],
+            "%.4g / %.4g / %.4g" % (st["median"], st["p10"], st["p90"]) if st else "%.4g" % d["ms_per_step"],
+            ("%s: %.3g %s (%.1f %%)" % (rf.get("kernel", ""), rf["achieved"], rf["unit"], 100 * rf["frac"])) if rf else "",
+            ("%.4g" % rf["traffic"]) if rf.get("traffic") else "null",
+            d.get("config", {}).get("workload", "")))
+        raw.append("    " + lines[-1])
+    out = ["# bench.py lines, one MI355X", "",
+           "Each row is one run of the command shown, from the repository root; the table gives the",
+           "headline value, the step time in ms (median / p10 / p90 over the timed steps), the dominant",
+           "kernel's roofline figure and its measured HBM bytes per launch (`traffic`, null when no",
+           "counter summary matches the current kernel source). The full JSON lines follow.", "",
+           "Then `python profile_summary.py bench <run dir>`.", "",
+           "| run | command | value | step ms (median / p10 / p90) | dominant kernel | traffic B | workload |",
+           "|---|---|---|---|---|---|---|"] + rows + ["", "Full lines:", ""] + raw
+    text = "\n".join(out) + "\n"
+    open(os.path.join(PROFILES, "bench_lines.md"), "w").write(text)
     return text
 
 
@@ -134,8 +173,12 @@ def main() -> None:
         t.add_argument(a)
     t.add_argument("--cmd-fetch", required=True)
     t.add_argument("--cmd-write", required=True)
+    b = sub.add_parser("bench")
+    b.add_argument("run_dir")
     a = ap.parse_args()
-    if a.what == "kernels":
+    if a.what == "bench":
+        print(bench(a.run_dir))
+    elif a.what == "kernels":
         print(kernels(a.run_dir, a.tag, a.last, a.cmd))
     else:
         print(traffic(a.fetch_dir, a.write_dir, a.tag, a.workload, a.kernel, a.source, a.cmd_fetch,
