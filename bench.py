@@ -257,9 +257,10 @@ def _find_clocks(d):
 
 
 def platform_info(torch, skip_clocks=False):
-    """ROCm / HIP versions, the device name, and the GPU clocks as amd-smi reports them (a child
-    process; None where the tool is missing, says nothing parseable, runs under a profiler, or
-    skip_clocks is set)."""
+    """ROCm / HIP versions, the device name, and the GPU clocks as amd-smi reports them before
+    the run (a child process; None where the tool is missing, says nothing parseable, runs under
+    a profiler, or skip_clocks is set).  The current clock is sampled at idle; max_clk is the
+    clock cap the timed work runs under."""
     import subprocess
 
     info = dict(hip=getattr(torch.version, "hip", None), torch=torch.__version__)
@@ -275,7 +276,7 @@ def platform_info(torch, skip_clocks=False):
     if skip_clocks or any(k.startswith("ROCPROF") for k in os.environ):
         # under a profiler the child would load the profiler's tool, which opens the GPU in the
         # amd-smi launcher before it starts its interpreter: leave the clocks out there
-        info["clocks_mhz"] = None
+        info["clocks_mhz_before_run"] = None
         return info
     try:
         r = subprocess.run(["amd-smi", "metric", "-g", "0", "--clock", "--json"], capture_output=True,
@@ -284,7 +285,7 @@ def platform_info(torch, skip_clocks=False):
             clocks = _find_clocks(json.loads(r.stdout))
     except (OSError, ValueError, subprocess.SubprocessError):
         clocks = None
-    info["clocks_mhz"] = clocks
+    info["clocks_mhz_before_run"] = clocks  # sampled while the GPU idles: max_clk is the cap
     return info
 
 
