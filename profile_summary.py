@@ -3,6 +3,7 @@
     python profile_summary.py kernels RUN_DIR TAG --last K --cmd "rocprofv3 ... -- python3 bench.py ..."
     python profile_summary.py traffic FETCH_DIR WRITE_DIR TAG WORKLOAD KERNEL SOURCE --cmd-fetch ... --cmd-write ...
     python profile_summary.py bench RUN_DIR
+    python profile_summary.py counters TAG KERNEL DIR1 [DIR2 ...] --cmd ...
 
 ``kernels`` reads ``*_kernel_trace.csv`` of a ``rocprofv3 --kernel-trace`` run and writes
 ``profiles/TAG_kernel_stats.md``: per kernel, every launch (what ``--stats`` prints) and the last
@@ -13,6 +14,12 @@ so the last K launches of a kernel are the timed ones.
 ``bench`` reads the bench.py JSON lines saved as ``NAME.json`` beside ``NAME.cmd`` (the command
 that printed it) in a directory, and writes ``profiles/bench_lines.md``: one row per run with
 the headline figures, then every line in full.
+
+``counters`` reads the ``*_counter_collection.csv`` of one or more ``rocprofv3 --pmc`` runs
+(one counter pass each) and writes ``profiles/TAG_counters.md``: per counter, the average over
+the kernel's launches of its value summed over the hardware instances, and the ratios that the
+kernel analysis uses (MFMA busy share of the SIMD cycles, instructions per MFMA, LDS bank
+conflicts per LDS instruction).
 
 ``traffic`` reads the ``*_counter_collection.csv`` of two ``rocprofv3 --pmc FETCH_SIZE`` /
 ``--pmc WRITE_SIZE`` runs of bench.py with ``--calibration-copy`` and writes
@@ -160,6 +167,47 @@ def bench(run_dir: str) -> str:
     return text
 
 
+def counters(tag: str, kernel: str, dirs, cmd: str) -> str:
+    vals = {}
+    for d in dirs:
+        per = collections.defaultdict(lambda: collections.defaultdict(float))
+        for r in csv.DictReader(open(_one(os.path.join(d, "**", "*counter_collection.csv")))):
+            if kernel in r["Kernel_Name"]:
+                per[r["Counter_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
+        for name, by_dispatch in per.items():
+            vals[name] = (statistics.mean(by_dispatch.values()), len(by_dispatch))
+    if not vals:
+        raise SystemExit("kernel %r not found in the counter files" % kernel)
+    out = ["# SQ counters: %s" % kernel, "", "Command (one pass per counter set, from the repository root):", "",
+           "    " + cmd, "", "Then `python profile_summary.py counters %s '%s' <run dirs>`." % (tag, kernel), "",
+           "Values are per launch (average over the launches sampled), summed over the hardware",
+           "instances that report them.", "",
+           "| counter | per launch | launches |", "|---|---|---|"]
+    for name in sorted(vals):
+        out.append("| %s | %.4g | %d |" % (name, vals[name][0], vals[name][1]))
+    v = {k: x[0] for k, x in vals.items()}
+    ratios = []
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in v and "SQ_BUSY_CU_CYCLES" in v:
+        ratios.append(("MFMA pipes busy, share of SIMD cycles (MFMA_BUSY / (4 BUSY_CU))",
+                       v["SQ_VALU_MFMA_BUSY_CYCLES"] / (4 * v["SQ_BUSY_CU_CYCLES"])))
+    if "SQ_INSTS_MFMA" in v:
+        for k in ("SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS"):
+            if k in v:
+                label = "VALU (MFMA included)" if k == "SQ_INSTS_VALU" else k[9:]
+                ratios.append(("%s instructions per MFMA instruction" % label, v[k] / v["SQ_INSTS_MFMA"]))
+    if "SQ_LDS_BANK_CONFLICT" in v and "SQ_INSTS_LDS" in v:
+        ratios.append(("LDS bank-conflict cycles per LDS instruction", v["SQ_LDS_BANK_CONFLICT"] / v["SQ_INSTS_LDS"]))
+    if "SQ_WAIT_INST_ANY" in v and "SQ_WAVE_CYCLES" in v:
+        ratios.append(("wave cycles waiting to issue, share (WAIT_INST_ANY / WAVE_CYCLES)", v["SQ_WAIT_INST_ANY"] / v["SQ_WAVE_CYCLES"]))
+    if "SQ_WAIT_INST_LDS" in v and "SQ_WAVE_CYCLES" in v:
+        ratios.append(("wave cycles waiting to issue an LDS instruction, share", v["SQ_WAIT_INST_LDS"] / v["SQ_WAVE_CYCLES"]))
+    if ratios:
+        out += ["", "| derived | value |", "|---|---|"] + ["| %s | %.3f |" % r for r in ratios]
+    text = "\n".join(out) + "\n"
+    open(os.path.join(PROFILES, "%s_counters.md" % tag), "w").write(text)
+    return text
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -175,9 +223,16 @@ def main() -> None:
     t.add_argument("--cmd-write", required=True)
     b = sub.add_parser("bench")
     b.add_argument("run_dir")
+    c = sub.add_parser("counters")
+    c.add_argument("tag")
+    c.add_argument("kernel")
+    c.add_argument("dirs", nargs="+")
+    c.add_argument("--cmd", required=True)
     a = ap.parse_args()
     if a.what == "bench":
         print(bench(a.run_dir))
+    elif a.what == "counters":
+        print(counters(a.tag, a.kernel, a.dirs, a.cmd))
     elif a.what == "kernels":
         print(kernels(a.run_dir, a.tag, a.last, a.cmd))
     else:
