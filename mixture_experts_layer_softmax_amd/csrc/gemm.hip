@@ -245,10 +245,11 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_bf16_kernel(GemmArgs g) {
     const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
     const int item = xcd * run + j;
     if (j >= run || item >= items) return;
-    const Tile tile = g.tiles[item / ncols];
+    int nt;
+    const int tix = grouped_item(g.tiles, *g.tile_count, item, ncols, &nt);
+    const Tile tile = g.tiles[tix];
     const int e = tile.expert, r0 = tile.row0, r1 = tile.row1;
     const int nsub = (r1 - r0 + 15) / 16;
-    const int nt = item % ncols;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7
     const int wr = wave >> 2, wc = wave & 3;                      // 2 x 4 wavefronts
@@ -264,7 +265,7 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_bf16_kernel(GemmArgs g) {
     const bool apk = KIND == kDown && g.hid_packed;
     const int astep = apk ? 512 : 2;  // bytes per K element along the A stream
     const char* const a_s = static_cast<const char*>(g.a) +
-                            (apk ? size_t(item / ncols) * size_t(K / BKS) * 16384 : 0);
+                            (apk ? size_t(tix) * size_t(K / BKS) * 16384 : 0);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         if (apk) {
@@ -451,7 +452,7 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_bf16_kernel(GemmArgs g) {
         const int col = colbase + c8 * 8;
         if (KIND == kGateUp) {
             if (g.hid_packed) {  // tile row tr, stage col / 32, chunk (col / 8) % 4 in its slot
-                const size_t blk = size_t(item / ncols) * (g.F / BKS) + (col >> 5);
+                const size_t blk = size_t(tix) * (g.F / BKS) + (col >> 5);
                 *reinterpret_cast<uint4*>(&out[blk * 8192 + tr * 32 + ((((col >> 3) & 3) ^ ((tr >> 1) & 3)) << 3)]) = v;
             } else {
                 *reinterpret_cast<uint4*>(&out[size_t(row) * g.F + col]) = v;
@@ -504,6 +505,8 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_prefill_nvfp4_kernel(GemmArgs
     const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
     const int item = xcd * run + j;
     if (j >= run || item >= items) return;
+    // tile-major order: the grouped order of the bf16 kernel measured no faster here (NVFP4
+    // prefill forward 4.01-4.02 ms against 4.04-4.05 grouped, one process)
     const Tile tile = g.tiles[item / ncols];
     const int e = tile.expert, r0 = tile.row0, r1 = tile.row1;
     const int nsub = (r1 - r0 + 15) / 16;
