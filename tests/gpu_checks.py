@@ -32,6 +32,16 @@ def pick_experts(counts):
     return big, ragged, small
 
 
+def p99_err(got, ref):
+    """99th percentile over elements of |got - ref| / (|ref| + 1e-3 rms(ref)): the per-element
+    figure reported beside the infinity-norm relative error (the floor keeps elements near zero
+    from dominating)."""
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
+    d = np.abs(got - ref) / (np.abs(ref) + 1e-3 * rms + 1e-300)
+    return float(np.percentile(d, 99)) if d.size else 0.0
+
+
 def block_err(got, ref):
     """max |got - ref| / max |ref| over a block of rows."""
     return float(np.max(np.abs(got - ref)) / max(float(np.max(np.abs(ref))), 1e-30))

@@ -13,6 +13,7 @@ import torch
 
 from mixture_experts_layer_softmax_amd import lib, synth
 from mixture_experts_layer_softmax_amd.layer import MoELayer, bf16_bits_to_f64, to_device, to_host
+from gpu_checks import p99_err
 from oracle import oracle as O
 
 pytestmark = pytest.mark.gpu
@@ -75,8 +76,8 @@ def run_share(wl, sub, b, n, tokens=None, path=None):
     np.testing.assert_allclose(dbg["topk_w"].cpu().numpy(), ref["topk_w"], rtol=W_RTOL, atol=0)
     got = act_f64(to_host(y))[ref["tokens"]]
     e = rel_err(got, ref["y"])
-    note("  %s experts [%d, %d): %d of %d rows, y rel err %.3e" % (wl.name, b, b + n, a_local,
-                                                                 wl.assignments, e))
+    note("  %s experts [%d, %d): %d of %d rows, y rel err %.3e, per-element p99 %.3e"
+         % (wl.name, b, b + n, a_local, wl.assignments, e, p99_err(got, ref["y"])))
     assert e <= TOL
     return got, ref
 
@@ -182,8 +183,10 @@ def test_prefill6000_share_of_four_ranks_sampled():
         assert np.array_equal(dbg[key].cpu().numpy().reshape(ref[key].shape), ref[key]), key
     a_local = int(ref["offsets"][-1])
     assert np.array_equal(dbg["sorted_token"].cpu().numpy()[:a_local], ref["sorted_token"][:a_local])
-    e = rel_err(act_f64(to_host(y))[toks], ref["y"])
-    note("  %d of %d rows held; y rel err %.3e on %d tokens" % (a_local, wl.assignments, e, toks.size))
+    got = act_f64(to_host(y))[toks]
+    e = rel_err(got, ref["y"])
+    note("  %d of %d rows held; y rel err %.3e, per-element p99 %.3e, on %d tokens"
+         % (a_local, wl.assignments, e, p99_err(got, ref["y"]), toks.size))
     assert e <= TOL
 
 

@@ -12,7 +12,7 @@ import torch
 
 from mixture_experts_layer_softmax_amd import lib, synth
 from mixture_experts_layer_softmax_amd.layer import MoELayer, bf16_bits_to_f64, to_device, to_host
-from gpu_checks import check_experts_through_stages
+from gpu_checks import check_experts_through_stages, p99_err
 from oracle import oracle as O
 
 pytestmark = pytest.mark.gpu
@@ -478,7 +478,8 @@ def _check_forward(wl, inp, layer, tokens=None, path=None):
     np.testing.assert_allclose(dbg["topk_w"].cpu().numpy(), ref["topk_w"], rtol=W_RTOL, atol=0)
     got = act_f64(to_host(y))[ref["tokens"]]
     e = rel_err(got, ref["y"])
-    note("  %s y rel err %.3e over %d tokens" % (wl.name, e, len(ref["tokens"])))
+    note("  %s y rel err %.3e, per-element p99 %.3e, over %d tokens"
+         % (wl.name, e, p99_err(got, ref["y"]), len(ref["tokens"])))
     assert e <= TOL
     return y
 

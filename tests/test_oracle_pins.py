@@ -547,3 +547,21 @@ def test_hot_set_receives_half_of_the_assignments():
     share = np.isin(r["topk_ids"], synth.hot_set(wl)).mean()
     assert abs(share - synth.HOT_SHARE_TARGET) <= 0.005
     assert len(synth.hot_set(wl)) == 26
+
+
+def test_p99_error_metric_on_known_values():
+    """The per-element error figure the GPU tests report: 99th percentile of
+    |got - ref| / (|ref| + 1e-3 rms(ref)).  On 1000 elements of value 1 with the first 6 off by
+    0.25 and the last 5 off by 0.5, the 99th percentile falls between the two error levels."""
+    import sys, os
+    sys.path.insert(0, os.path.dirname(__file__))
+    from gpu_checks import p99_err
+    ref = np.ones(1000)
+    got = ref.copy()
+    got[-5:] += 0.5
+    got[:6] += 0.25
+    rms = 1.0
+    e = p99_err(got, ref)
+    # sorted errors: 989 zeros, 6 at 0.25/(1+1e-3), 5 at 0.5/(1+1e-3); rank 989.01 of 999
+    assert 0.25 / (1 + 1e-3 * rms) - 1e-12 <= e <= 0.5 / (1 + 1e-3 * rms) + 1e-12
+    assert p99_err(ref, ref) == 0.0
