@@ -524,6 +524,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_prefill_nvfp4_kernel(GemmArgs
     const char* pa[A_DMA];
     uint32_t va[A_DMA];
     const char* const a_s = static_cast<const char*>(g.a);
+    constexpr bool a_scalar_ = A32;  // activation loads in the scalar-base form
 #pragma unroll
     for (int i = 0; i < A_DMA; ++i) {
         const int row = (i * NW + wave) * 16 + (lane >> 2);
@@ -639,8 +640,11 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_prefill_nvfp4_kernel(GemmArgs
         }                                                                                       \
     } while (0)
     // NW = 8: the MFMAs of one stage with the decode of raw stage K0 (into SB) interleaved: after
-    // row group mi's MFMAs, output word mi of this thread's 8 (two chunks of four words)
-#define MOE_MFMA_DEC(AF, BF, SB, NIB, SW, K0, FULLC)                                            \
+    // row group mi's MFMAs, output word mi of this thread's 8 (two chunks of four words); the
+    // stage's loads (activation chunks after groups 1 and 3, raw weights after group 5) are
+    // issued between the groups too, so that a load that waits for the address unit does not
+    // hold back the MFMAs (NVFP4 prefill forward 4.02-4.04 -> 3.98 ms, one process)
+#define MOE_MFMA_DEC(AF, BF, SB, NIB, SW, K0, FULLC, SAW, SNW, SSW, KA, KW)                      \
     do {                                                                                        \
         typedef __attribute__((ext_vector_type(2))) float f2_;                                  \
         const int row_ = tid >> 1, h_ = tid & 1;                                                \
@@ -663,6 +667,12 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_prefill_nvfp4_kernel(GemmArgs
                 w_[mi] = __builtin_amdgcn_perm(__float_as_uint(v_.y * sc_), __float_as_uint(v_.x * sc_), 0x07060302u); \
             }                                                                                   \
             if (mi == 3) SB[lds_slot32(row_, 2 * h_)] = make_uint4(w_[0], w_[1], w_[2], w_[3]);  \
+            if (mi == 1 || mi == 3) {                                                           \
+                const int i_ = mi >> 1;                                                         \
+                if (a_scalar_) dma16s(a_s + size_t(KA) * 2, va[i_], &SAW[(i_ * NW + wave) * 64]); \
+                else dma16(pa[i_] + size_t(KA) * 2, &SAW[(i_ * NW + wave) * 64]);               \
+            }                                                                                   \
+            if (mi == 5) MOE_ISSUE_W(SNW, SSW, KW);                                             \
         }                                                                                       \
         SB[lds_slot32(row_, 2 * h_ + 1)] = make_uint4(w_[4], w_[5], w_[6], w_[7]);               \
     } while (0)
@@ -707,10 +717,12 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_prefill_nvfp4_kernel(GemmArgs
             swd_ = SSd[tid >> 1];                                            \
         }                                                                    \
         MOE_READ(SAr, SBr, GA, GB);                                          \
-        MOE_ISSUE_A(SAw, min((s + S + 4) * BKS, last));                      \
-        MOE_ISSUE_W(SNw, SSw, min((s + S + 5) * BKS, last));                 \
+        if constexpr (NW == 4) {                                             \
+            MOE_ISSUE_A(SAw, min((s + S + 4) * BKS, last));                  \
+            MOE_ISSUE_W(SNw, SSw, min((s + S + 5) * BKS, last));             \
+        }                                                                    \
         if constexpr (NW == 8) {                                             \
-            MOE_MFMA_DEC(FA, FB, SBd, nibd_, swd_, min((s + S + 2) * BKS, last), FULLC); \
+            MOE_MFMA_DEC(FA, FB, SBd, nibd_, swd_, min((s + S + 2) * BKS, last), FULLC, SAw, SNw, SSw, min((s + S + 4) * BKS, last), min((s + S + 5) * BKS, last)); \
             if (s + S + 1 >= nk) break;                                      \
         } else {                                                             \
             MOE_MFMA(FA, FB, FULLC);                                         \
