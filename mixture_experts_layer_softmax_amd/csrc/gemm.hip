@@ -466,7 +466,7 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_bf16_kernel(GemmArgs g) {
 // ---------------------------------------------------------------------------------------
 // Prefill kernel, NVFP4 weights: the bf16 kernel's 256 x 256 tile and activation DMA ring with
 // NW = 4 wavefronts (2 x 2, 128 x 128 each) or NW = 8 (2 x 4, 128 x 64 each; measured: 8 for
-// the down GEMM, 4 for gate/up); the weights are DMA'd raw (16 nibble bytes and one 4-byte
+// both kinds with packed weights, 4 for gate/up with row-major ones); the weights are DMA'd raw (16 nibble bytes and one 4-byte
 // scale word per weight row and stage, straight from the row-major NVFP4 arrays) and decoded
 // by the block into a bf16 LDS slot (e2m1 * e4m3 is exact in bf16) after the MFMAs of the
 // current stage are issued, so the decode overlaps the matrix core.  The per-expert fp32 scale
