@@ -3,8 +3,9 @@
  *
  * Microkernels that measure what the box actually sustains, so that a benchmark can state its
  * kernels' roofline fractions against measured peaks beside the data-sheet ones (bf16 dense
- * MFMA 2.5 PFLOP/s, HBM3E 8 TB/s), and what one grid barrier of the single-launch decode
- * kernel costs.  They compute nothing of the layer.
+ * MFMA 2.5 PFLOP/s, HBM3E 8 TB/s), what one grid barrier of the single-launch decode kernel
+ * costs, and how long the grouped GEMM kernel alone takes.  Apart from the last (which runs
+ * moe_grouped_gemm's own computation) they compute nothing of the layer.
  * Same conventions as moe.h: device pointers owned by the caller, work enqueued on `stream`
  * (a hipStream_t, NULL = default stream), return codes only, arguments validated on the host
  * before any HIP call.
@@ -44,6 +45,23 @@ moe_status moe_probe_read(const void* buf, size_t bytes, uint32_t* out, void* st
 #define MOE_PROBE_SYNC_BYTES 8256
 moe_status moe_probe_grid_barrier(int32_t blocks, int32_t barriers, void* sync, uint32_t spin_limit,
                                   void* stream);
+
+/* moe_grouped_gemm's GEMM timed on its own: the arguments of moe_grouped_gemm (same checks,
+ * same results in `out`) plus timing.  The tile list is built from `offsets` once; then the GEMM
+ * (for MX weights with its input quantization, which is part of every moe_grouped_gemm call) is
+ * launched `launches` times on `stream`, each launch bracketed by two HIP events, so the tile-list
+ * kernel stays outside the brackets.  With flush_bytes > 0, every launch is preceded (outside its
+ * bracket) by a moe_probe_read of flush_buf[0, flush_bytes) into flush_out, which evicts the
+ * layer's operands from the caches.  ms: host float[launches], receives each launch's duration in
+ * milliseconds; the call synchronizes `stream`.  launches in [1, 100000], ms not NULL, and a flush
+ * buffer as moe_probe_read requires when flush_bytes > 0, else MOE_ERR_INVALID_ARGUMENT.  With
+ * num_tokens == 0 nothing is launched and ms is filled with 0. */
+moe_status moe_probe_grouped_gemm_times(const moe_problem* p, moe_gemm_kind kind, const void* a,
+                                        const int32_t* a_rows, const int32_t* offsets,
+                                        const moe_expert_weights* w, void* out, void* workspace,
+                                        size_t workspace_bytes, const void* flush_buf,
+                                        size_t flush_bytes, uint32_t* flush_out, int32_t launches,
+                                        float* ms, void* stream);
 
 #ifdef __cplusplus
 }

@@ -11,8 +11,10 @@
 #include <cstdint>
 #include <cstdlib>
 #include <mutex>
+#include <vector>
 
 #include "../../include/moe.h"
+#include "../../include/moe_probe.h"
 #include "launch.h"
 
 using namespace moe;
@@ -424,6 +426,55 @@ moe_status moe_grouped_gemm(const moe_problem* p, moe_gemm_kind kind, const void
                            tcount, *w, out);
     MOE_TRY(mx_input(*p, g, workspace, L, s));
     return dev(launch_gemm(g, L.family, L.max_tiles, s));
+}
+
+moe_status moe_probe_grouped_gemm_times(const moe_problem* p, moe_gemm_kind kind, const void* a,
+                                        const int32_t* a_rows, const int32_t* offsets,
+                                        const moe_expert_weights* w, void* out, void* workspace,
+                                        size_t workspace_bytes, const void* flush_buf,
+                                        size_t flush_bytes, uint32_t* flush_out, int32_t launches,
+                                        float* ms, void* stream) {
+    MOE_TRY(check_problem(p));
+    if (kind != MOE_GEMM_GATE_UP_SWIGLU && kind != MOE_GEMM_DOWN) return MOE_ERR_INVALID_ARGUMENT;
+    if (launches < 1 || launches > 100000 || !ms) return MOE_ERR_INVALID_ARGUMENT;
+    if (flush_bytes && (!flush_buf || !flush_out || flush_bytes % 16 || !aligned(flush_buf)))
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (p->num_tokens == 0) {
+        for (int i = 0; i < launches; ++i) ms[i] = 0.0f;
+        return MOE_OK;
+    }
+    if (!a || !offsets || !out || !aligned(a) || !aligned(offsets) || !aligned(out) ||
+        (a_rows && !aligned(a_rows)))
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (kind == MOE_GEMM_DOWN && a_rows) return MOE_ERR_INVALID_ARGUMENT;
+    MOE_TRY(check_weights(*p, w));
+    MOE_TRY(check_ws(*p, workspace, workspace_bytes));
+    const Layout L = layout(*p);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    Tile* tiles = at<Tile>(workspace, L.tiles1);
+    int* tcount = at<int>(workspace, L.tcount);
+    MOE_TRY(dev(launch_tiles_from_offsets(offsets, p->num_experts, ebegin(*p), eend(*p),
+                                          p->num_tokens * p->top_k, L.bm, tiles, tcount,
+                                          L.max_tiles, s)));
+    GemmArgs g = gemm_args(*p, kind == MOE_GEMM_GATE_UP_SWIGLU ? kGateUp : kDown, a, a_rows, tiles,
+                           tcount, *w, out);
+    std::vector<hipEvent_t> ev(2 * size_t(launches), nullptr);
+    moe_status st = MOE_OK;
+    for (auto& e : ev)
+        if (st == MOE_OK && hipEventCreate(&e) != hipSuccess) st = MOE_ERR_DEVICE;
+    for (int i = 0; st == MOE_OK && i < launches; ++i) {
+        if (flush_bytes) st = moe_probe_read(flush_buf, flush_bytes, flush_out, stream);
+        if (st == MOE_OK) st = dev(hipEventRecord(ev[2 * i], s));
+        if (st == MOE_OK) st = mx_input(*p, g, workspace, L, s);
+        if (st == MOE_OK) st = dev(launch_gemm(g, L.family, L.max_tiles, s));
+        if (st == MOE_OK) st = dev(hipEventRecord(ev[2 * i + 1], s));
+    }
+    if (st == MOE_OK) st = dev(hipStreamSynchronize(s));
+    for (int i = 0; st == MOE_OK && i < launches; ++i)
+        st = dev(hipEventElapsedTime(&ms[i], ev[2 * i], ev[2 * i + 1]));
+    for (auto& e : ev)
+        if (e) (void)hipEventDestroy(e);
+    return st;
 }
 
 moe_status moe_combine(const moe_problem* p, const void* y_perm, const int32_t* inv_perm,

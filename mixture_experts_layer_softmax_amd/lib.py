@@ -27,7 +27,7 @@ PATHS = {"auto": PATH_AUTO, "prefill": PATH_PREFILL, "decode": PATH_DECODE, "fus
 EXPORTS = ("moe_status_string", "moe_workspace_size", "moe_packed_weights_size", "moe_pack_weights",
            "moe_pack_scales", "moe_route", "moe_permute", "moe_grouped_gemm", "moe_combine", "moe_forward",
            "moe_quantize_mxfp8", "moe_probe_mfma_bf16", "moe_probe_read", "moe_forward_static",
-           "moe_probe_grid_barrier")
+           "moe_probe_grid_barrier", "moe_probe_grouped_gemm_times")
 PROBE_SYNC_BYTES = 8256  # MOE_PROBE_SYNC_BYTES
 LAYOUT_ROW_MAJOR, LAYOUT_PACKED = 0, 1
 
@@ -92,6 +92,10 @@ def load() -> C.CDLL:
             L.moe_probe_read.argtypes = [vp, sz, vp, vp]
             L.moe_probe_grid_barrier.restype = i32
             L.moe_probe_grid_barrier.argtypes = [C.c_int32, C.c_int32, vp, C.c_uint32, vp]
+            L.moe_probe_grouped_gemm_times.restype = i32
+            L.moe_probe_grouped_gemm_times.argtypes = [P, i32, vp, vp, vp, C.POINTER(ExpertWeights), vp,
+                                                       vp, sz, vp, sz, vp, C.c_int32,
+                                                       C.POINTER(C.c_float), vp]
             L.moe_forward.restype = i32
             L.moe_forward.argtypes = [P, vp, vp, vp, C.POINTER(ExpertWeights), vp, vp, vp, vp, vp,
                                       vp, vp, vp, sz, vp]
@@ -221,6 +225,21 @@ def probe_read(buf, out, stream=None):
     n = buf.numel() * buf.element_size()
     _check(load().moe_probe_read(_ptr(buf), n, _ptr(out), _stream(stream)), "moe_probe_read")
     return float(n)
+
+
+def probe_grouped_gemm_times(p, kind, a, a_rows, offsets, w: ExpertWeights, out, ws, launches,
+                             flush=None, flush_out=None, stream=None):
+    """moe_probe_grouped_gemm_times: the GEMM of moe_grouped_gemm launched `launches` times, each
+    bracketed by events (the tile-list kernel and the optional cache flush over all of `flush`
+    outside the brackets); returns the per-launch times in ms (synchronizes the stream)."""
+    ms = (C.c_float * int(launches))()
+    nflush = 0 if flush is None else flush.numel() * flush.element_size()
+    _check(load().moe_probe_grouped_gemm_times(C.byref(p), int(kind), _ptr(a), _ptr(a_rows),
+                                               _ptr(offsets), C.byref(w), _ptr(out), _ptr(ws),
+                                               ws.numel() * ws.element_size(), _ptr(flush), nflush,
+                                               _ptr(flush_out), int(launches), ms, _stream(stream)),
+           "moe_probe_grouped_gemm_times")
+    return [float(v) for v in ms]
 
 
 def probe_grid_barrier(blocks, barriers, sync, spin_limit=1 << 20, stream=None):

@@ -217,3 +217,27 @@ def test_probe_validation(L):
     assert L.moe_probe_read(V(FAKE), 100, V(FAKE), None) == lib.MOE_ERR_INVALID_ARGUMENT
     assert L.moe_probe_read(V(FAKE + 8), 1024, V(FAKE), None) == lib.MOE_ERR_INVALID_ARGUMENT
     assert L.moe_probe_read(None, 1024, V(FAKE), None) == lib.MOE_ERR_INVALID_ARGUMENT
+
+
+def test_grouped_gemm_timing_probe_validation(L):
+    """moe_probe_grouped_gemm_times checks its own arguments (launches, the host time array, the
+    flush buffer) before any HIP call, and with no tokens fills the times with zeros."""
+    V = C.c_void_p
+    p = lib.problem(16, 256, 8, 2, 128)
+    w = lib.ExpertWeights(FAKE, FAKE, None, None, None, None, 1)
+    ms = (C.c_float * 4)(7.0, 7.0, 7.0, 7.0)
+    f = L.moe_probe_grouped_gemm_times
+    args = lambda kind=0, launches=4, times=ms, fb=None, fn=0, fo=None, prob=p: (
+        C.byref(prob), kind, V(FAKE), None, V(FAKE), C.byref(w), V(FAKE), V(FAKE), 1 << 40, fb, fn,
+        fo, launches, times, None)
+    assert f(*args(launches=0)) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert f(*args(launches=100001)) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert f(*args(times=None)) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert f(*args(kind=2)) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert f(*args(fb=None, fn=1024, fo=V(FAKE))) == lib.MOE_ERR_INVALID_ARGUMENT       # no buffer
+    assert f(*args(fb=V(FAKE), fn=100, fo=V(FAKE))) == lib.MOE_ERR_INVALID_ARGUMENT     # not x16
+    assert f(*args(fb=V(FAKE + 8), fn=1024, fo=V(FAKE))) == lib.MOE_ERR_INVALID_ARGUMENT
+    assert f(*args(fb=V(FAKE), fn=1024, fo=None)) == lib.MOE_ERR_INVALID_ARGUMENT
+    empty = lib.problem(0, 256, 8, 2, 128)
+    assert f(*args(prob=empty)) == lib.MOE_OK
+    assert list(ms) == [0.0] * 4

@@ -40,3 +40,33 @@ def test_read_probe_rate_is_plausible():
     r = _rate(lambda: lib.probe_read(buf, word))
     print("[gpu] read probe %.1f GB/s" % (r / 1e9), flush=True)
     assert 1e12 < r < 1.2e13
+
+
+@pytest.mark.parametrize("wdt", ["bf16", "nvfp4"])
+def test_grouped_gemm_timing_probe_runs_the_same_gemm(wdt):
+    """moe_probe_grouped_gemm_times writes what moe_grouped_gemm writes (bit for bit) and
+    returns one positive time per launch, no longer than a whole moe_grouped_gemm call."""
+    from mixture_experts_layer_softmax_amd import synth
+    from mixture_experts_layer_softmax_amd.layer import MoELayer
+
+    wl = synth.Workload("probe_" + wdt, 512, 512, 16, 4, 256, "bf16", wdt, 77, "none")
+    inp = synth.generate(wl)
+    layer = MoELayer.from_workload(wl, inp)
+    x = layer.act_tensor(inp["x"])
+    y, dbg = layer.forward(x, debug=True)
+    p = layer.problem_for(wl.tokens)
+    ws = layer.workspace(wl.tokens)
+    hid = layer.empty_act(wl.assignments, wl.ffn)
+    hid2 = layer.empty_act(wl.assignments, wl.ffn)
+    print("[gpu] timing probe, %s weights" % wdt, flush=True)
+    lib.grouped_gemm(p, lib.GATE_UP_SWIGLU, x, dbg["sorted_token"], dbg["offsets"], layer.weights, hid, ws)
+    flush = torch.ones(1 << 26, dtype=torch.uint8, device="cuda")
+    word = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for fb in (None, flush):
+        hid2.zero_()
+        ms = lib.probe_grouped_gemm_times(p, lib.GATE_UP_SWIGLU, x, dbg["sorted_token"], dbg["offsets"],
+                                          layer.weights, hid2, ws, 5, flush=fb, flush_out=word)
+        torch.cuda.synchronize()
+        assert torch.equal(hid.view(torch.int16), hid2.view(torch.int16))
+        assert len(ms) == 5 and all(0.0 < t < 1000.0 for t in ms)
+        print("[gpu]   flush=%s: %s ms" % (fb is not None, ", ".join("%.4f" % t for t in ms)), flush=True)
