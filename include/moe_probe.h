@@ -1,7 +1,7 @@
 /*
  * moe_probe.h -- measurement aids for the MoE layer library on MI355X (gfx950).
  *
- * Microkernels that measure what the box actually sustains, so that a benchmark can state its
+ * Microkernels that measure what the device actually sustains, so that a benchmark can state its
  * kernels' roofline fractions against measured peaks beside the data-sheet ones (bf16 dense
  * MFMA 2.5 PFLOP/s, HBM3E 8 TB/s), what one grid barrier of the single-launch decode kernel
  * costs, and how long the grouped GEMM kernel alone takes.  Apart from the last (which runs
