@@ -219,7 +219,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_fallback_kernel(GemmArgs g) 
 // wavefront waits for LDS data the other issues MFMAs.  K in 32-wide stages; a 4-slot LDS ring
 // (4 x 32 KiB) is filled by direct global->LDS loads (each wavefront moves two 1 KiB groups of
 // activation rows and two of weight rows per stage) and the operand fragments of the next
-// stage are read from LDS into registers while the MFMAs of the current stage run.  Rows are 64
+// stage are read from LDS into registers while the MFMAs of the current stage run: the weight
+// fragments first, each row group's activation fragment right after that group's MFMAs, into
+// the same registers (one activation set, 32 registers fewer; bf16 prefill gate/up 1.073 ->
+// 1.064 ms, forward 1.685 -> 1.670 ms, one process, bit-identical).  Rows are 64
 // bytes in LDS; the 16-byte chunk c of row r sits in slot c ^ ((r >> 1) & 3), which keeps the
 // fragment reads (8 consecutive rows, one chunk) on distinct banks.  Activation rows are
 // gathered through the dispatch map; weights come in the packed layout, where every stage of a
@@ -345,12 +348,20 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_bf16_kernel(GemmArgs g) {
         _Pragma("unroll") for (int mi = 0; mi < 8; ++mi) AF[mi] =                               \
             __builtin_bit_cast(bf16x8_t, SA[lds_slot32((mi * 2 + wr) * 16 + (lane & 15), ch_)]); \
     } while (0)
-#define MOE_MFMA8(AF, BF)                                                                       \
+#define MOE_READB8(SB, BF)                                                                      \
+    do {                                                                                        \
+        _Pragma("unroll") for (int ni = 0; ni < 4; ++ni) BF[ni] =                               \
+            __builtin_bit_cast(bf16x8_t, SB[lds_slot32(gb[ni] * 16 + (lane & 15), lane >> 4)]);  \
+    } while (0)
+    // the MFMAs of one stage; row group mi's activation fragment of the next stage (ring slot
+    // SAN) is read into AF[mi] right after the group's MFMAs, under the same row test
+#define MOE_MFMA8(AF, BF, SAN)                                                                  \
     do {                                                                                        \
         _Pragma("unroll") for (int mi = 0; mi < 8; ++mi) {                                      \
             if (__builtin_expect(mi < na_, 1)) {                                                \
                 _Pragma("unroll") for (int ni = 0; ni < 4; ++ni) acc[mi][ni] =                  \
                     __builtin_amdgcn_mfma_f32_16x16x32_bf16(AF[mi], BF[ni], acc[mi][ni], 0, 0, 0); \
+                AF[mi] = __builtin_bit_cast(bf16x8_t, SAN[lds_slot32((mi * 2 + wr) * 16 + (lane & 15), lane >> 4)]); \
             }                                                                                   \
         }                                                                                       \
     } while (0)
@@ -360,7 +371,7 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_bf16_kernel(GemmArgs g) {
     for (int mi = 0; mi < 8; ++mi)
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    bf16x8_t a0[8], b0[4], a1[8], b1[4];
+    bf16x8_t af[8], b0[4], b1[4];
     int na_;  // na, re-read each stage so that the group tests stay scalar compares
 
     const int nk = K / BKS;
@@ -370,45 +381,46 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_bf16_kernel(GemmArgs g) {
     MOE_ISSUE8(sA2, sB2, min(2 * BKS, last));
     wait_vm_lgkm0<8>();
     block_barrier();
-    MOE_READ8(sA0, sB0, a0, b0);
+    MOE_READ8(sA0, sB0, af, b0);
     MOE_ISSUE8(sA3, sB3, min(3 * BKS, last));
     for (int s = 0;; s += 4) {
         wait_vm_lgkm0<8>();
         block_barrier();
         na_ = na;
         asm volatile("" : "+s"(na_));
-        MOE_READ8(sA1, sB1, a1, b1);
+        MOE_READB8(sB1, b1);
         MOE_ISSUE8(sA0, sB0, min((s + 4) * BKS, last));
-        MOE_MFMA8(a0, b0);
+        MOE_MFMA8(af, b0, sA1);
         if (s + 1 >= nk) break;
         wait_vm_lgkm0<8>();
         block_barrier();
         na_ = na;
         asm volatile("" : "+s"(na_));
-        MOE_READ8(sA2, sB2, a0, b0);
+        MOE_READB8(sB2, b0);
         MOE_ISSUE8(sA1, sB1, min((s + 5) * BKS, last));
-        MOE_MFMA8(a1, b1);
+        MOE_MFMA8(af, b1, sA2);
         if (s + 2 >= nk) break;
         wait_vm_lgkm0<8>();
         block_barrier();
         na_ = na;
         asm volatile("" : "+s"(na_));
-        MOE_READ8(sA3, sB3, a1, b1);
+        MOE_READB8(sB3, b1);
         MOE_ISSUE8(sA2, sB2, min((s + 6) * BKS, last));
-        MOE_MFMA8(a0, b0);
+        MOE_MFMA8(af, b0, sA3);
         if (s + 3 >= nk) break;
         wait_vm_lgkm0<8>();
         block_barrier();
         na_ = na;
         asm volatile("" : "+s"(na_));
-        MOE_READ8(sA0, sB0, a0, b0);
+        MOE_READB8(sB0, b0);
         MOE_ISSUE8(sA3, sB3, min((s + 7) * BKS, last));
-        MOE_MFMA8(a1, b1);
+        MOE_MFMA8(af, b1, sA0);
         if (s + 4 >= nk) break;
     }
     wait_vm_lgkm0<0>();
 #undef MOE_ISSUE8
 #undef MOE_READ8
+#undef MOE_READB8
 #undef MOE_MFMA8
 
     // Epilogue through LDS: every wavefront is past its last fragment read once all have reached
@@ -474,12 +486,17 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_bf16_kernel(GemmArgs g) {
 //
 // Iteration i: activation stage i+1 and raw weight stage i+2 have landed (issued three
 // iterations earlier); read the raw words of stage i+2 this thread decodes (raw slot
-// (i+2)%4), then the fragments of stage i+1 (activations from ring slot (i+1)%4, decoded
-// weights from bf16 slot (i+1)%2); DMA activation stage i+4 (slot i%4) and raw weight stage
-// i+5 (raw slot (i+1)%4); run the MFMAs of stage i with the decode of raw stage i+2 into bf16
-// slot i%2 interleaved (NW = 8: one output word after each 16-row group's MFMAs, so that the
-// VALU work runs beside the matrix core instead of after it; measured: NVFP4 prefill gate/up
-// 2.79 -> 2.67 ms, down 1.40 -> 1.38 ms, forward 4.52 -> 4.35 ms, bit-identical).  Every wavefront issues the same number of DMA instructions
+// (i+2)%4) and the weight fragments of stage i+1 (bf16 slot (i+1)%2); DMA activation stage
+// i+4 (slot i%4) and raw weight stage i+5 (raw slot (i+1)%4); run the MFMAs of stage i with
+// the decode of raw stage i+2 into bf16 slot i%2 interleaved (NW = 8: one output word after
+// each 16-row group's MFMAs, so that the VALU work runs beside the matrix core instead of
+// after it; measured: NVFP4 prefill gate/up 2.79 -> 2.67 ms, down 1.40 -> 1.38 ms, forward
+// 4.52 -> 4.35 ms, bit-identical).  Each row group's activation fragment of stage i+1 (ring
+// slot (i+1)%4) is read right after that group's MFMAs of stage i, into the same registers
+// and under the same row test: groups past the tile's last row cost no LDS reads, and one
+// fragment set instead of two frees 24 registers (measured, one process: gate/up 2.45 ->
+// 2.39 ms with the real routing, 1.25 -> 1.07 ms with 32 rows per expert; down 1.226 ->
+// 1.216 ms; bit-identical).  Every wavefront issues the same number of DMA instructions
 // per iteration (NW = 4: four activation, one nibble, one scale; NW = 8: two activation and
 // one nibble or scale), so "landed" is a fixed load count; the barrier at the top of the
 // iteration also publishes each raw row to the thread that decodes it.
@@ -630,12 +647,23 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_prefill_nvfp4_kernel(GemmArgs
         _Pragma("unroll") for (int mi = 0; mi < 8; ++mi) AF[mi] =                               \
             __builtin_bit_cast(bf16x8_t, SA[lds_slot32((mi * 2 + wr) * 16 + (lane & 15), ch_)]); \
     } while (0)
-#define MOE_MFMA(AF, BF, FULLC)                                                                 \
+#define MOE_READ_B(SB, BF)                                                                      \
+    do {                                                                                        \
+        _Pragma("unroll") for (int ni = 0; ni < NB; ++ni) BF[ni] =                              \
+            __builtin_bit_cast(bf16x8_t, SB[lds_slot32(gb[ni] * 16 + (lane & 15), lane >> 4)]);  \
+    } while (0)
+    // row group mi's activation fragment of the next stage (ring slot SA) is read into AF[mi]
+    // right after the group's MFMAs, under the same test, so that a group without rows is
+    // neither multiplied nor read and one fragment set serves both stages
+#define MOE_READ_A1(SA, AF, mi)                                                                 \
+    AF[mi] = __builtin_bit_cast(bf16x8_t, SA[lds_slot32(((mi) * 2 + wr) * 16 + (lane & 15), lane >> 4)])
+#define MOE_MFMA(AF, BF, FULLC, SAR)                                                            \
     do {                                                                                        \
         _Pragma("unroll") for (int mi = 0; mi < 8; ++mi) {                                      \
             if (FULLC || __builtin_expect(mi < na_, 1)) {                                       \
                 _Pragma("unroll") for (int ni = 0; ni < NB; ++ni) acc[mi][ni] =                 \
                     __builtin_amdgcn_mfma_f32_16x16x32_bf16(AF[mi], BF[ni], acc[mi][ni], 0, 0, 0); \
+                MOE_READ_A1(SAR, AF, mi);                                                       \
             }                                                                                   \
         }                                                                                       \
     } while (0)
@@ -644,7 +672,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_prefill_nvfp4_kernel(GemmArgs
     // stage's loads (activation chunks after groups 1 and 3, raw weights after group 5) are
     // issued between the groups too, so that a load that waits for the address unit does not
     // hold back the MFMAs (NVFP4 prefill forward 4.02-4.04 -> 3.98 ms, one process)
-#define MOE_MFMA_DEC(AF, BF, SB, NIB, SW, K0, FULLC, SAW, SNW, SSW, KA, KW)                      \
+#define MOE_MFMA_DEC(AF, BF, SB, NIB, SW, K0, FULLC, SAW, SNW, SSW, KA, KW, SAR)                 \
     do {                                                                                        \
         typedef __attribute__((ext_vector_type(2))) float f2_;                                  \
         const int row_ = tid >> 1, h_ = tid & 1;                                                \
@@ -656,6 +684,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_prefill_nvfp4_kernel(GemmArgs
             if (FULLC || __builtin_expect(mi < na_, 1)) {                                       \
                 _Pragma("unroll") for (int ni = 0; ni < NB; ++ni) acc[mi][ni] =                 \
                     __builtin_amdgcn_mfma_f32_16x16x32_bf16(AF[mi], BF[ni], acc[mi][ni], 0, 0, 0); \
+                MOE_READ_A1(SAR, AF, mi);                                                       \
             }                                                                                   \
             {                                                                                   \
                 const uint32_t src_ = (mi < 4) ? nib_.x : nib_.y;                               \
@@ -682,7 +711,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_prefill_nvfp4_kernel(GemmArgs
     for (int mi = 0; mi < 8; ++mi)
 #pragma unroll
         for (int ni = 0; ni < NB; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    bf16x8_t a0[8], b0[NB], a1[8], b1[NB];
+    bf16x8_t af[8], b0[NB], b1[NB];
 
     const int nk = K / BKS;
     const int last = (nk - 1) * BKS;
@@ -697,7 +726,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_prefill_nvfp4_kernel(GemmArgs
     MOE_DECODE(sN1, sS1, sB1, min(1 * BKS, last));
     wait_vm_lgkm0<0>();
     block_barrier();
-    MOE_READ(sA0, sB0, a0, b0);
+    MOE_READ(sA0, sB0, af, b0);
     MOE_ISSUE_A(sA1, min(1 * BKS, last));
     MOE_ISSUE_W(sN2, sS2, min(2 * BKS, last));
     MOE_ISSUE_A(sA2, min(2 * BKS, last));
@@ -707,7 +736,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_prefill_nvfp4_kernel(GemmArgs
     uint2 nibd_ = make_uint2(0, 0);  // raw weight words this thread decodes in the next MFMA block
     uint32_t swd_ = 0;
     int na_;  // na, re-read each stage so that the group tests stay scalar compares
-#define MOE_IT(FULLC, S, FA, FB, GA, GB, SAr, SBr, SAw, SNw, SSw, SNd, SSd, SBd)      \
+#define MOE_IT(FULLC, S, FB, GB, SAr, SBr, SAw, SNw, SSw, SNd, SSd, SBd)      \
         wait_vm_lgkm0<2 * OPS>();                                            \
         block_barrier();                                                     \
         na_ = na;                                                            \
@@ -716,25 +745,25 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_prefill_nvfp4_kernel(GemmArgs
             nibd_ = reinterpret_cast<const uint2*>(SNd)[tid];                \
             swd_ = SSd[tid >> 1];                                            \
         }                                                                    \
-        MOE_READ(SAr, SBr, GA, GB);                                          \
+        MOE_READ_B(SBr, GB);                                                 \
         if constexpr (NW == 4) {                                             \
             MOE_ISSUE_A(SAw, min((s + S + 4) * BKS, last));                  \
             MOE_ISSUE_W(SNw, SSw, min((s + S + 5) * BKS, last));             \
         }                                                                    \
         if constexpr (NW == 8) {                                             \
-            MOE_MFMA_DEC(FA, FB, SBd, nibd_, swd_, min((s + S + 2) * BKS, last), FULLC, SAw, SNw, SSw, min((s + S + 4) * BKS, last), min((s + S + 5) * BKS, last)); \
+            MOE_MFMA_DEC(af, FB, SBd, nibd_, swd_, min((s + S + 2) * BKS, last), FULLC, SAw, SNw, SSw, min((s + S + 4) * BKS, last), min((s + S + 5) * BKS, last), SAr); \
             if (s + S + 1 >= nk) break;                                      \
         } else {                                                             \
-            MOE_MFMA(FA, FB, FULLC);                                         \
+            MOE_MFMA(af, FB, FULLC, SAr);                                    \
             if (s + S + 1 >= nk) break;                                      \
             MOE_DECODE(SNd, SSd, SBd, min((s + S + 2) * BKS, last));         \
         }
 #define MOE_LOOP(FULLC)                                                      \
     for (int s = 0;; s += 4) {                                           \
-        MOE_IT(FULLC, 0, a0, b0, a1, b1, sA1, sB1, sA0, sN1, sS1, sN2, sS2, sB0) \
-        MOE_IT(FULLC, 1, a1, b1, a0, b0, sA2, sB0, sA1, sN2, sS2, sN3, sS3, sB1) \
-        MOE_IT(FULLC, 2, a0, b0, a1, b1, sA3, sB1, sA2, sN3, sS3, sN0, sS0, sB0) \
-        MOE_IT(FULLC, 3, a1, b1, a0, b0, sA0, sB0, sA3, sN0, sS0, sN1, sS1, sB1) \
+        MOE_IT(FULLC, 0, b0, b1, sA1, sB1, sA0, sN1, sS1, sN2, sS2, sB0) \
+        MOE_IT(FULLC, 1, b1, b0, sA2, sB0, sA1, sN2, sS2, sN3, sS3, sB1) \
+        MOE_IT(FULLC, 2, b0, b1, sA3, sB1, sA2, sN3, sS3, sN0, sS0, sB0) \
+        MOE_IT(FULLC, 3, b1, b0, sA0, sB0, sA3, sN0, sS0, sN1, sS1, sB1) \
     }
     MOE_LOOP(false)
 #undef MOE_LOOP
@@ -746,6 +775,8 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_prefill_nvfp4_kernel(GemmArgs
 #undef MOE_READ
 #undef MOE_MFMA
 #undef MOE_MFMA_DEC
+#undef MOE_READ_B
+#undef MOE_READ_A1
 
     const float gs = g.gscale ? g.gscale[e] : 1.0f;
     // Epilogue through LDS, as in the bf16 kernel, in two rounds of 64 tile rows (the ring's
