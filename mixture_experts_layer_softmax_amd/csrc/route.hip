@@ -21,8 +21,11 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const void* __restri
                                                             const float* __restrict__ bias,
                                                             float* __restrict__ logits, int T,
                                                             int H, int E) {
+    // the wavefront index as a scalar, so that the row bases stay scalar too (8 x 8 form: 231
+    // -> 149 registers, 35 -> 16 64-bit address additions per chunk; NVFP4 prefill routing
+    // 305 -> 274 us, bit-identical)
     router_logits_wave<BF16, TM, TN>(x, wr, bias, logits, T, H, E,
-                                     blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave);
+                                     __builtin_amdgcn_readfirstlane(blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave));
 }
 
 // One wavefront per token.
