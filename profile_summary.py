@@ -72,8 +72,9 @@ def kernels(run_dir: str, tag: str, last: int, cmd: str) -> str:
     out = ["# Kernel trace: %s" % tag, "", "Command (run from the repository root on one MI355X):", "",
            "    " + cmd, "", "Then `python profile_summary.py kernels <run dir> %s --last %d`." % (tag, last), "",
            "Durations in microseconds.  *All*: every launch of the run (warm-up and untimed launches "
-           "included, as `rocprofv3 --stats` counts them).  *Timed*: the last %d launches of each kernel, "
-           "which are the launches of bench.py's timed region." % last, "",
+           "included, as `rocprofv3 --stats` counts them).  *Timed*: the last %d launches of each kernel: "
+           "for the gate/up GEMM the launches of bench.py's kernel timing (its roofline figure), which "
+           "follow the timed steps; for the other kernels the launches of the timed steps." % last, "",
            "| kernel | calls | all: average | timed: calls | timed: average | timed: median | timed: min | timed: max | share % |",
            "|---|---|---|---|---|---|---|---|---|"]
     for tot, name, d, tail in rows:
