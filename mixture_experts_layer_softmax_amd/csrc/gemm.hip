@@ -534,13 +534,18 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_prefill_nvfp4_kernel(GemmArgs
     __shared__ uint4 sB0[BN * 4], sB1[BN * 4];               // decoded bf16 stages
 
     const int ncols = (KIND == kGateUp) ? g.F / HALF : (g.N + BN - 1) / BN;
-    const int items = *g.tile_count * ncols;
-    const int run = (items + 7) >> 3;
+    // Work order: pairs of row tiles are dealt to the XCDs in turn (blocks b, b + 8, ... run on
+    // XCD b % 8), and an XCD runs each pair's 2 x ncols items tile-major, so that the blocks of
+    // one row tile share its activations, and an expert's consecutive row tiles its weight
+    // panels, in that XCD's L2.  Dealt in turn, costly and cheap tiles spread over the XCDs;
+    // contiguous ranges of items per XCD left some XCDs with more of the expensive full tiles
+    // (NVFP4 prefill gate/up 2.41-2.44 -> 2.36-2.38 ms, down 1.25-1.26 -> 1.20-1.21 ms, one
+    // process, bit-identical).  The grouped order of the bf16 kernel measured no faster here.
+    const int tcount = *g.tile_count;
     const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
-    const int item = xcd * run + j;
-    if (j >= run || item >= items) return;
-    // tile-major order: the grouped order of the bf16 kernel measured no faster here (NVFP4
-    // prefill forward 4.01-4.02 ms against 4.04-4.05 grouped, one process)
+    const int tl_ = 2 * (xcd + 8 * (j / (2 * ncols))) + (j % (2 * ncols)) / ncols;
+    if (tl_ >= tcount) return;
+    const int item = tl_ * ncols + j % ncols;
     const Tile tile = g.tiles[item / ncols];
     const int e = tile.expert, r0 = tile.row0, r1 = tile.row1;
     const int nsub = (r1 - r0 + 15) / 16;
@@ -1029,7 +1034,9 @@ hipError_t launch_gemm(const GemmArgs& g, int family, int max_tiles, hipStream_t
         else
             hipLaunchKernelGGL((gemm_prefill_bf16_kernel<kDown, false>), grid, dim3(512), 0, s, g);
     } else if (family == kFamPrefill && g.wfmt == kWNVFP4 && g.F % 128 == 0) {
-        const dim3 grid = prefill_grid(g, max_tiles, 256);
+        // pairs of row tiles dealt to the 8 XCDs in turn (see the kernel)
+        const int ncols_ = up ? g.F / 128 : (g.N + 255) / 256;
+        const dim3 grid = dim3(8 * ((max_tiles + 15) / 16) * 2 * ncols_);
         // packed weights: 8 wavefronts for both kinds (gate/up 2.97 -> 2.69 ms against 4 on
         // the NVFP4 prefill shape); row-major: 4 for gate/up, where 4 measured faster
         // the scalar-base activation loads need every row offset below 4 GiB
