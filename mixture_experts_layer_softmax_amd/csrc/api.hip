@@ -113,7 +113,7 @@ Layout layout(const moe_problem& p) {
     L.inv = take(A * 4);
     L.tiles1 = take(size_t(L.max_tiles) * sizeof(Tile));
     L.tiles2 = take(size_t(L.max_tiles) * sizeof(Tile));
-    L.tcount = take(4 * sizeof(int));
+    L.tcount = take(32 * sizeof(int));  // tile counts; [8..16]: the prefill list's XCD ranges
     // bf16 prefill forward: hid in the packed tile image (every tile a full 256 rows)
     L.hid = take(hid_packed(p) ? size_t(L.max_tiles) * 256 * F * 2 : A * F * act_bytes(p));
     L.yperm = take(A * H * act_bytes(p));

@@ -245,11 +245,12 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_bf16_kernel(GemmArgs g) {
     __shared__ uint4 sB0[BN * 4], sB1[BN * 4], sB2[BN * 4], sB3[BN * 4];
 
     const int ncols = (KIND == kGateUp) ? g.F / HALF : (g.N + BN - 1) / BN;
-    const int items = *g.tile_count * ncols;
-    const int run = (items + 7) >> 3;
+    // XCD x (blocks b with b % 8 == x) takes the items of row tiles tile_count[8 + x] ..
+    // tile_count[9 + x], ranges the dispatch cut by cost (bf16 prefill gate/up 1.053-1.059 ->
+    // 1.041-1.052 ms, down 0.542-0.545 -> 0.532-0.539 ms against equal item counts per XCD)
     const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
-    const int item = xcd * run + j;
-    if (j >= run || item >= items) return;
+    const int item = g.tile_count[8 + xcd] * ncols + j;
+    if (item >= g.tile_count[9 + xcd] * ncols) return;
     int nt;
     const int tix = grouped_item(g.tiles, *g.tile_count, item, ncols, &nt);
     const Tile tile = g.tiles[tix];
@@ -534,18 +535,19 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_prefill_nvfp4_kernel(GemmArgs
     __shared__ uint4 sB0[BN * 4], sB1[BN * 4];               // decoded bf16 stages
 
     const int ncols = (KIND == kGateUp) ? g.F / HALF : (g.N + BN - 1) / BN;
-    // Work order: pairs of row tiles are dealt to the XCDs in turn (blocks b, b + 8, ... run on
-    // XCD b % 8), and an XCD runs each pair's 2 x ncols items tile-major, so that the blocks of
-    // one row tile share its activations, and an expert's consecutive row tiles its weight
-    // panels, in that XCD's L2.  Dealt in turn, costly and cheap tiles spread over the XCDs;
-    // contiguous ranges of items per XCD left some XCDs with more of the expensive full tiles
-    // (NVFP4 prefill gate/up 2.41-2.44 -> 2.36-2.38 ms, down 1.25-1.26 -> 1.20-1.21 ms, one
-    // process, bit-identical).  The grouped order of the bf16 kernel measured no faster here.
-    const int tcount = *g.tile_count;
+    // Work order: blocks b, b + 8, ... run on XCD b % 8, and XCD x takes the row tiles
+    // tile_count[8 + x] .. tile_count[9 + x] of the list, ranges that the dispatch cut by cost
+    // (a fixed part per tile plus its rows), tile-major, so that the blocks of one row tile
+    // share its activations, and an expert's consecutive row tiles its weight panels, in that
+    // XCD's L2.  Equal numbers of items per XCD left some XCDs with more of the costly full
+    // tiles of the hot experts (NVFP4 prefill gate/up 2.41-2.44 ms; pairs of row tiles dealt
+    // to the XCDs in turn 2.36-2.38 ms in the same process).  The cut by cost measured the same
+    // as the pairs dealt in turn here (2.32-2.33 against 2.30-2.34 ms, down 1.18-1.20 against
+    // 1.19 ms) and serves the bf16 kernel too, where it is 1% faster.  The grouped order of the
+    // bf16 kernel measured no faster here.
     const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
-    const int tl_ = 2 * (xcd + 8 * (j / (2 * ncols))) + (j % (2 * ncols)) / ncols;
-    if (tl_ >= tcount) return;
-    const int item = tl_ * ncols + j % ncols;
+    const int item = g.tile_count[8 + xcd] * ncols + j;  // this XCD's range of row tiles
+    if (item >= g.tile_count[9 + xcd] * ncols) return;
     const Tile tile = g.tiles[item / ncols];
     const int e = tile.expert, r0 = tile.row0, r1 = tile.row1;
     const int nsub = (r1 - r0 + 15) / 16;
@@ -1001,11 +1003,12 @@ static void launch_mfma(const GemmArgs& g, int max_tiles, hipStream_t s) {
         hipLaunchKernelGGL((gemm_fallback_kernel<BM, BN, WM, WN, kDown, kWNVFP4>), grid, block, 0, s, g);
 }
 
-// Work items of the prefill kernels: (row tile, column tile) pairs, a multiple of 8 blocks so
-// that every XCD walks the same number of slots.
-static dim3 prefill_grid(const GemmArgs& g, int max_tiles, int bn) {
-    const int ncols = g.kind == kGateUp ? g.F / (bn / 2) : (g.N + bn - 1) / bn;
-    return dim3(((max_tiles * ncols + 7) / 8) * 8);
+// Blocks for the XCD ranges of a prefill tile list: a tile costs between half a full tile and a
+// full one, so a range cut at an eighth of the cost, rounded to a tile, holds fewer than
+// twice the mean number of tiles plus two
+static dim3 xcd_grid(const GemmArgs& g, int max_tiles) {
+    const int ncols = g.kind == kGateUp ? g.F / 128 : (g.N + 255) / 256;
+    return dim3(8 * (2 * ((max_tiles + 7) / 8) + 2) * ncols);
 }
 
 hipError_t launch_gemm(const GemmArgs& g, int family, int max_tiles, hipStream_t s) {
@@ -1022,7 +1025,7 @@ hipError_t launch_gemm(const GemmArgs& g, int family, int max_tiles, hipStream_t
         else
             hipLaunchKernelGGL((gemm_f32_kernel<kDown>), grid, block, 0, s, g);
     } else if (family == kFamPrefill && g.wfmt == kWBF16) {  // packed weights: F % 128 == 0, H % 256 == 0
-        const dim3 grid = prefill_grid(g, max_tiles, 256);
+        const dim3 grid = xcd_grid(g, max_tiles);
         // the scalar-base activation loads need every row offset below 4 GiB
         const bool a32 = size_t(g.a_rows_limit) * size_t(g.K) * 2 <= 0xffffffffull;
         if (up && a32)
@@ -1034,9 +1037,7 @@ hipError_t launch_gemm(const GemmArgs& g, int family, int max_tiles, hipStream_t
         else
             hipLaunchKernelGGL((gemm_prefill_bf16_kernel<kDown, false>), grid, dim3(512), 0, s, g);
     } else if (family == kFamPrefill && g.wfmt == kWNVFP4 && g.F % 128 == 0) {
-        // pairs of row tiles dealt to the 8 XCDs in turn (see the kernel)
-        const int ncols_ = up ? g.F / 128 : (g.N + 255) / 256;
-        const dim3 grid = dim3(8 * ((max_tiles + 15) / 16) * 2 * ncols_);
+        const dim3 grid = xcd_grid(g, max_tiles);
         // packed weights: 8 wavefronts for both kinds (gate/up 2.97 -> 2.69 ms against 4 on
         // the NVFP4 prefill shape); row-major: 4 for gate/up, where 4 measured faster
         // the scalar-base activation loads need every row offset below 4 GiB

@@ -124,7 +124,42 @@ __device__ __forceinline__ void emit_tiles(int e, int E, int count, int start, i
         t.pad = 0;
         tiles[first + i] = t;
     }
-    if (threadIdx.x == 0) *tile_count = min(total, cap);
+    const int ntiles = min(total, cap);
+    if (threadIdx.x == 0) *tile_count = ntiles;
+    if (bm >= 128) {
+        // prefill tile lists: the 8 XCDs' tile ranges, tile_count[8 + x] .. tile_count[9 + x],
+        // cut where the running cost of the list (bm / 16 + ceil(rows / 16) per tile: a fixed
+        // part per tile plus its rows) crosses x / 8 of the total
+        const int last_rows = nt ? count - (nt - 1) * bm : 0;
+        const int cost = nt ? (nt - 1) * (2 * bm / 16) + bm / 16 + (last_rows + 15) / 16 : 0;
+        int ctotal;
+        const int cstart = block_exclusive_scan<NT>(cost, &ctotal);
+        if (threadIdx.x == 0) {
+            tile_count[8] = 0;
+            tile_count[16] = ntiles;
+            // no rows: every range empty (nothing else writes them, and the area keeps the
+            // previous list's ranges)
+            if (ctotal == 0)
+                for (int x = 1; x < 8; ++x) tile_count[8 + x] = 0;
+        }
+        if (cost > 0) {
+            for (int x = 1; x < 8; ++x) {
+                const long long target = (long long)x * ctotal / 8;
+                if (target < cstart || target >= cstart + cost) continue;
+                int cum = cstart, b = first + nt;
+                for (int i = 0; i < nt; ++i) {
+                    const int rows = i + 1 < nt ? bm : last_rows;
+                    const int tc = bm / 16 + (rows + 15) / 16;
+                    if (target < cum + tc) {
+                        b = first + i + ((target - cum) * 2 >= tc ? 1 : 0);
+                        break;
+                    }
+                    cum += tc;
+                }
+                tile_count[8 + x] = min(b, ntiles);
+            }
+        }
+    }
 }
 
 // Small decode batches (any T <= 64): top-k selection and the whole dispatch (histogram, scan,

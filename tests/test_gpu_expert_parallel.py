@@ -217,3 +217,42 @@ def test_grouped_gemm_one_token_per_expert_full_size(ep):
     ey = rel_err(act_f64(to_host(yp)), ref_y)
     note("  hid rel err %.3e, y rel err %.3e" % (eh, ey))
     assert eh <= TOL and ey <= TOL
+
+
+@pytest.mark.parametrize("wdt", ["bf16", "nvfp4"])
+def test_grouped_gemm_with_no_held_rows_after_one_with_rows(wdt):
+    """Two standalone gate/up GEMMs in one workspace, of the same size: the first gives the held
+    experts rows, the second gives every row to experts not held.  The prefill kernels split the
+    tile list over the XCDs by ranges kept in the workspace; the second call's empty list must
+    empty every range, so it writes no row (the first call's ranges would name its stale tiles)."""
+    wl = W("gg0", 64, 512, 8, 2, 256, "bf16", wdt, 22, "none")
+    b, n = 2, 3
+    sub = share(synth.generate(wl), b, n)
+    layer = MoELayer.from_workload(wl, sub, expert_begin=b, local_experts=n)
+    A = 600
+    p = lib.problem(A, wl.hidden, wl.experts, 1, wl.ffn, "bf16", wdt, path="prefill",
+                    expert_begin=b, local_experts=n)
+    ws = torch.empty(lib.workspace_size(p), dtype=torch.uint8, device="cuda")
+    rng = np.random.default_rng(8)
+    a_host = synth.to_bf16_bits(rng.standard_normal((A, wl.hidden)).astype(np.float32))
+    a = to_device(a_host, "cuda")
+    first = np.array([10, 20, 300, 40, 200, 10, 10, 10], dtype=np.int32)  # held: 300, 40, 200
+    second = np.array([100, 100, 0, 0, 0, 200, 100, 100], dtype=np.int32)
+    for i, counts in enumerate((first, second)):
+        offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+        assert int(offsets[-1]) == A
+        expert_of_row = np.repeat(np.arange(wl.experts), counts)
+        held = (expert_of_row >= b) & (expert_of_row < b + n)
+        out = torch.full((A, wl.ffn), 7.0, dtype=torch.bfloat16, device="cuda")
+        note("grouped gemm %s call %d: %d held rows" % (wdt, i + 1, int(held.sum())))
+        lib.grouped_gemm(p, lib.GATE_UP_SWIGLU, a, None, torch.from_numpy(offsets).cuda(),
+                         layer.weights, out, ws)
+        torch.cuda.synchronize()
+        got = act_f64(to_host(out))
+        assert np.all(got[~held] == 7.0)
+        if held.any():
+            ref = O.gate_up_rows(dict(sub, x=a_host), wdt, wl.ffn, np.arange(A)[held],
+                                 expert_of_row[held] - b)
+            e = rel_err(got[held], ref)
+            note("  held rows rel err %.3e" % e)
+            assert e <= TOL
