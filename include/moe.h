@@ -223,7 +223,12 @@ moe_status moe_pack_scales(const moe_problem* p, const uint8_t* w13_scale, const
                            uint8_t* w13_scale_packed, uint8_t* w2_scale_packed, void* stream);
 
 /* Route.  x [T,H] and w_router [E,H] in act_dtype; router_bias fp32 [E] or NULL.
- * Writes topk_ids int32 [T,k] and topk_w fp32 [T,k] (routing contract above). */
+ * Writes topk_ids int32 [T,k] and topk_w fp32 [T,k] (routing contract above).  From 256 bf16
+ * tokens with renormalize = 1 the router screens first: approximate logits on the matrix cores
+ * and a bound on their distance to the canonical ones that holds for any summation order
+ * decide which experts can still be selected, and only those get canonical logits; the ids and
+ * weights are the ones the contract defines, bit for bit (tokens with non-finite or huge values
+ * get the canonical logits of every expert). */
 moe_status moe_route(const moe_problem* p, const void* x, const void* w_router,
                      const float* router_bias, int32_t* topk_ids, float* topk_w,
                      void* workspace, size_t workspace_bytes, void* stream);

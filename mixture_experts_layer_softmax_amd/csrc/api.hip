@@ -28,8 +28,8 @@ size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 struct Layout {
-    size_t sync, logits, ids, w, hist, base, counts, offsets, sorted, inv, tiles1, tiles2, tcount, hid,
-        yperm, xq, xs, hq, hs, total;
+    size_t sync, logits, mpart, wn2, ids, w, hist, base, counts, offsets, sorted, inv, tiles1, tiles2,
+        tcount, hid, yperm, xq, xs, hq, hs, total;
     int family, bm, max_tiles;
 };
 
@@ -91,6 +91,13 @@ moe_status check_problem(const moe_problem* p) {
 // 16 KiB, like its weights, instead of 256 rows of 64 bytes each
 bool hid_packed(const moe_problem& p) { return family_of(p) == kFamPrefill && p.w_dtype == MOE_BF16; }
 
+// Screened routing (route.hip) for large bf16 batches with renormalised weights: the same ids
+// and weights as the full canonical router.  Below 256 tokens the full router is as fast (it
+// is latency-bound there), and the full softmax (renormalize = 0) needs every canonical logit.
+bool screened_routing(const moe_problem& p) {
+    return p.act_dtype == MOE_BF16 && p.renormalize && p.num_tokens >= 256 && p.num_experts >= 16;
+}
+
 Layout layout(const moe_problem& p) {
     Layout L{};
     const size_t T = p.num_tokens, E = p.num_experts, k = p.top_k, H = p.hidden, F = p.ffn;
@@ -103,6 +110,10 @@ Layout layout(const moe_problem& p) {
     auto take = [&](size_t bytes) { size_t r = o; o += up(bytes > 0 ? bytes : 1); return r; };
     L.sync = take(sizeof(GridSync));  // grid-barrier words of the single-launch decode kernel
     L.logits = take(T * E * 4);
+    // screened routing: partial approximate logits and squared router-row norms per K slice
+    const size_t ks = screened_routing(p) ? size_t(screen_k_split(p.num_tokens, p.hidden, p.num_experts)) : 0;
+    L.mpart = take(ks * T * E * 4);
+    L.wn2 = take(ks * E * 4);
     L.ids = take(A * 4);
     L.w = take(A * 4);
     L.hist = take(nch * E * 4);
@@ -226,7 +237,10 @@ moe_status run_route(const moe_problem& p, const void* x, const void* wr, const 
                      int32_t* ids, float* w, const Layout& L, void* ws, hipStream_t s) {
     RouteArgs r{x, wr, bias, at<float>(ws, L.logits), p.num_tokens, p.hidden, p.num_experts,
                 p.act_dtype == MOE_BF16};
-    MOE_TRY(dev(launch_router_logits(r, s)));
+    if (screened_routing(p))
+        MOE_TRY(dev(launch_router_screened(r, at<float>(ws, L.mpart), at<float>(ws, L.wn2), p.top_k, s)));
+    else
+        MOE_TRY(dev(launch_router_logits(r, s)));
     return dev(launch_topk(r.logits, p.num_tokens, p.num_experts, p.top_k, p.renormalize, ids, w, s));
 }
 

@@ -105,6 +105,19 @@ int gemm_tile_rows(int family, int wfmt, int ffn);
 // layer; `blocks_per_cu` caps the persistent grid (0: as many as fit).
 hipError_t launch_decode_fused(const FusedArgs& a, bool nv4, int blocks_per_cu, hipStream_t s);
 hipError_t launch_router_logits(const RouteArgs& a, hipStream_t s);
+// Screened routing (bf16 activations, renormalised weights): approximate logits on the matrix
+// cores, canonical logits only for the experts that can be selected, -inf for the rest (route.hip
+// states why the selection equals the full canonical one).  logits [T,E]; scratch: mpart
+// [KS,T,E] (partial approximate logits over KS slices of K, KS = screen_k_split(T, H, E)) and wn2
+// [KS,E] (squared router-row norms).  topk follows as for launch_router_logits.
+struct ScreenConst {
+    float gamma;     // relative bound of the two dot products and the bias addition
+    float flush;     // 2^-126 H: terms flushed to zero
+    float norm_abs;  // sqrt(H) 2^-63: norm lost to squares that underflow
+};
+ScreenConst screen_const(int H);
+int screen_k_split(int T, int H, int E);
+hipError_t launch_router_screened(const RouteArgs& a, float* mpart, float* wn2, int k, hipStream_t s);
 hipError_t launch_topk(const float* logits, int T, int E, int k, int renorm, int32_t* ids,
                        float* w, hipStream_t s);
 hipError_t launch_dispatch(const DispatchArgs& d, hipStream_t s);

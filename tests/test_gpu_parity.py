@@ -166,6 +166,59 @@ def test_route_small_and_large_batch_kernels_agree():
         assert np.array_equal(out[400][1][:T], out[T][1]), T
 
 
+@pytest.mark.parametrize("E,k", [(128, 8), (256, 8), (200, 6), (512, 16)])
+def test_screened_route_equals_full_router_on_hard_rows(E, k):
+    """From 256 tokens, bf16 batches route through the screened router (approximate logits on
+    the matrix cores, canonical logits only for the experts that can be selected); below 256 the
+    full canonical router runs.  Routing the same rows as 256 tokens and as their first 255 must
+    give the same ids and weights bit for bit, on rows built to stress the screen: exact ties
+    (duplicated router rows, zero tokens whose logits are the bias), near ties (router rows one
+    bf16 step apart in one element), a token of norm 2^60 and non-finite tokens (both take the
+    full row), bf16 subnormal tokens, and ordinary ones.  Ids of the finite rows must also equal
+    the oracle's."""
+    rng = np.random.default_rng(E * 31 + k)
+    T, H = 256, 1024
+    wr = (rng.standard_normal((E, H)) * 0.02).astype(np.float32)
+    wr[1::7] = wr[0::7][: len(wr[1::7])]                       # exact duplicates
+    wr[3::11] = wr[2::11][: len(wr[3::11])]
+    bits = synth.to_bf16_bits(wr)
+    bits[5::13, 17] = bits[4::13, 17][: len(bits[5::13, 17])] + 1  # one bf16 step apart
+    bias = rng.choice(np.array([0.0, 0.25, 0.5], np.float32), size=E)
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    x[10:20] = 0.0                                              # logits = bias: ties everywhere
+    x[20:30] *= 1e-39                                           # bf16 subnormals
+    x[30] *= 2.0 ** 60                                          # norm above the screen's range
+    x[31, 5] = np.inf
+    x[32, 7] = np.nan
+    x[33] = x[34]                                               # identical tokens
+    xb = synth.to_bf16_bits(x)
+    note("screened route E=%d k=%d" % (E, k))
+    xd = to_device(xb, "cuda", "bf16")
+    wd = to_device(bits, "cuda", "bf16")
+    bd = to_device(bias, "cuda")
+    out = {}
+    for n in (T, T - 1):
+        p = lib.problem(n, H, E, k, 128)
+        ws = torch.empty(lib.workspace_size(p), dtype=torch.uint8, device="cuda")
+        ids = torch.empty(n, k, dtype=torch.int32, device="cuda")
+        w = torch.empty(n, k, dtype=torch.float32, device="cuda")
+        lib.route(p, xd[:n], wd, bd, ids, w, ws)
+        torch.cuda.synchronize()
+        out[n] = (ids.cpu().numpy(), w.cpu().numpy())
+    ids256, w256 = out[T]
+    ids255, w255 = out[T - 1]
+    assert np.array_equal(ids256[: T - 1], ids255)
+    assert np.array_equal(w256[: T - 1].view(np.uint32), w255.view(np.uint32))
+    for r in range(T):  # every token: k distinct valid experts
+        assert len(set(ids256[r].tolist())) == k and ids256[r].min() >= 0 and ids256[r].max() < E
+    finite = np.isfinite(x).all(axis=1)
+    ref = O.route({"x": xb[finite], "w_router": bits, "bias": bias}, k)
+    assert np.array_equal(ids256[finite], ref["topk_ids"])
+    keep = finite.copy()
+    keep[30] = False  # its weights are a softmax of logits near 2^54: the oracle's fp64 differs
+    np.testing.assert_allclose(w256[keep], ref["topk_w"][keep[finite]], rtol=W_RTOL, atol=0)
+
+
 # ---------------------------------------------------------------------------------------
 # dispatch
 # ---------------------------------------------------------------------------------------
