@@ -111,11 +111,11 @@ hipError_t launch_router_logits(const RouteArgs& a, hipStream_t s);
 // [KS,T,E] (partial approximate logits over KS slices of K, KS = screen_k_split(T, H, E)) and wn2
 // [KS,E] (squared router-row norms).  topk follows as for launch_router_logits.
 struct ScreenConst {
-    float gamma;     // relative bound of the two dot products and the bias addition
+    float gamma;     // relative bound of the two dot products, the slice sum and the bias addition
     float flush;     // 2^-126 H: terms flushed to zero
     float norm_abs;  // sqrt(H) 2^-63: norm lost to squares that underflow
 };
-ScreenConst screen_const(int H);
+ScreenConst screen_const(int H, int KS);
 int screen_k_split(int T, int H, int E);
 hipError_t launch_router_screened(const RouteArgs& a, float* mpart, float* wn2, int k, hipStream_t s);
 hipError_t launch_topk(const float* logits, int T, int E, int k, int renorm, int32_t* ids,

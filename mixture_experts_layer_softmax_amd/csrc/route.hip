@@ -58,15 +58,20 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
 // selected experts are candidates, with their canonical logits, so ids and weights are those of
 // the full canonical router bit for bit.
 //
-// The bound: each of the two dot products sums H exact bf16 x bf16 products (16 significant
-// bits fit fp32).  Any summation tree whose additions are accurate to a relative 2^-23 (round
-// to nearest, or truncation) is within ((1 + 2^-23)^n - 1) sum |x_i w_i| of the exact sum when
-// no term passes through more than n additions (the standard forward error bound of summation,
-// Higham, Accuracy and Stability of Numerical Algorithms, section 4.2); with n = H + 64 that
-// covers both dots and the bias addition.  sum |x_i w_i| <= |x| |w| (Cauchy-Schwarz).  Inputs,
-// products or partial sums flushed to zero below 2^-126 add at most 2^-126 (max|x| + max|w| + 2)
-// per term, a term in 2^-126 H (|x| + |w| + 2).  The norms are computed in fp32 from squares,
-// which can underflow: |x| <= (1 + 2^-10) sqrt(sum x^2) + sqrt(H) 2^-63.  |m| 2^-21 absorbs the
+// The bound: both dot products sum H exact bf16 x bf16 products (16 significant bits fit
+// fp32).  A sum whose additions are each accurate to a relative u is within
+// ((1 + u)^n - 1) sum |x_i w_i| of the exact sum when no term passes through more than n
+// additions (the forward error bound of summation, Higham, Accuracy and Stability of
+// Numerical Algorithms, section 4.2).  The canonical order is IEEE fused multiply-adds
+// (u = 2^-24): at most H / 64 + 8 per partial, a fold of 6 and the bias, n <= H / 64 + 16.  For the matrix
+// cores nothing is assumed about the order or the rounding inside an instruction beyond each
+// addition being accurate to u = 2^-23 (round to nearest, or truncation): an instruction adds
+// 32 products and the accumulator, so a term passes through at most 32 additions per
+// instruction of its K slice, H / KS in all, then the KS - 1 additions of the slices and the
+// bias: n = H / KS + KS + 1.  sum |x_i w_i| <= |x| |w| (Cauchy-Schwarz).  Inputs, products or
+// partial sums flushed to zero below 2^-126 add at most 2^-126 (max|x| + max|w| + 2) per term,
+// a term in 2^-126 H (|x| + |w| + 2).  The norms are computed in fp32 from squares, which can
+// underflow: |x| <= (1 + 2^-10) sqrt(sum x^2) + sqrt(H) 2^-63.  |m| 2^-21 absorbs the
 // rounding of m +- beta.  A token whose m or norms are not finite, or exceed 2^100 (|m|, |b|)
 // or 2^50 (norms, so that the bound stays finite), gets the canonical logits of all E experts.
 
@@ -85,7 +90,7 @@ __device__ __forceinline__ float sumsq_bf16x8(uint4 v, float acc) {
 
 // Block tile: 64 tokens x 128 experts x one of KS slices of K, 8 wavefronts (2 x 4) of 32 x 32,
 // K in stages of 64 through a two-buffer LDS ring; each thread's share of a stage (three 16-byte
-// chunks) is loaded into registers two stages ahead.  The K split multiplies the blocks, and so
+// chunks) is loaded into registers four stages ahead.  The K split multiplies the blocks, and so
 // the loads in flight, by KS (the kernel waits on memory latency, not on its MFMAs): slice ks
 // writes its partial sums to m + ks T E (the bias in slice 0) and the screen adds the KS
 // partials, an order the bound covers.  Blocks b, b + 8, ... run on one XCD, and the blocks of a
@@ -116,7 +121,7 @@ __global__ __launch_bounds__(512) void router_mfma_kernel(const uint16_t* __rest
     const uint4* const pw0 = reinterpret_cast<const uint4*>(wr + size_t(min(e0 + r, E - 1)) * H + k0) + c;
     const uint4* const pw1 = reinterpret_cast<const uint4*>(wr + size_t(min(e0 + r + 64, E - 1)) * H + k0) + c;
 
-    uint4 ra[3], rb[3];  // stages in flight
+    uint4 r0[3], r1[3], r2[3], r3[3];  // stages s with s % 4 = 0, 1, 2, 3 in flight
     float sw0 = 0.f, sw1 = 0.f;
     f32x4_t acc[2][2];
 #pragma unroll
@@ -158,22 +163,29 @@ __global__ __launch_bounds__(512) void router_mfma_kernel(const uint16_t* __rest
                     acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0); \
         }                                                                                     \
     } while (0)
-    // stage s sits in LDS buffer s % 2; ra holds the even stages in flight, rb the odd ones
-    MOE_RLOAD(ra, 0);
-    if (1 < nst) MOE_RLOAD(rb, 1);
-    MOE_RSTORE(ra, 0);
+    // stage s: registers r(s % 4), then LDS buffer s % 2; loaded four stages ahead of its MFMAs
+    MOE_RLOAD(r0, 0);
+    if (1 < nst) MOE_RLOAD(r1, 1);
+    if (2 < nst) MOE_RLOAD(r2, 2);
+    if (3 < nst) MOE_RLOAD(r3, 3);
+    MOE_RSTORE(r0, 0);
     __syncthreads();
-    for (int s = 0; s < nst; s += 2) {
-        if (s + 2 < nst) MOE_RLOAD(ra, s + 2);
-        MOE_RMFMA(0);
-        if (s + 1 < nst) MOE_RSTORE(rb, 1);
-        __syncthreads();
-        if (s + 1 >= nst) break;
-        if (s + 3 < nst) MOE_RLOAD(rb, s + 3);
-        MOE_RMFMA(1);
-        if (s + 2 < nst) MOE_RSTORE(ra, 0);
-        __syncthreads();
+#define MOE_RPHASE(J, RL, RS)                                  \
+    {                                                          \
+        const int cs = s + (J);                                \
+        if (cs >= nst) break;                                  \
+        if (cs + 4 < nst) MOE_RLOAD(RL, cs + 4);               \
+        MOE_RMFMA((J) & 1);                                    \
+        if (cs + 1 < nst) MOE_RSTORE(RS, ((J) + 1) & 1);       \
+        __syncthreads();                                       \
     }
+    for (int s = 0; s < nst; s += 4) {
+        MOE_RPHASE(0, r0, r1)
+        MOE_RPHASE(1, r1, r2)
+        MOE_RPHASE(2, r2, r3)
+        MOE_RPHASE(3, r3, r0)
+    }
+#undef MOE_RPHASE
 #undef MOE_RLOAD
 #undef MOE_RSTORE
 #undef MOE_RMFMA
@@ -366,10 +378,12 @@ __global__ __launch_bounds__(256) void router_screen_kernel(const uint16_t* __re
 
 // ---------------------------------------------------------------------------------------
 
-ScreenConst screen_const(int H) {
+ScreenConst screen_const(int H, int KS) {
     ScreenConst c;
-    const double n = double(H) + 64.0;
-    c.gamma = float(std::expm1(n * std::log1p(std::ldexp(1.0, -23))) * 2.0 * 1.001);
+    const double n_mfma = double(H) / KS + KS + 1, n_can = double(H) / 64 + 16;
+    const double g = std::expm1(n_mfma * std::log1p(std::ldexp(1.0, -23))) +
+                     std::expm1(n_can * std::log1p(std::ldexp(1.0, -24)));
+    c.gamma = float(g * 1.001);
     c.flush = float(std::ldexp(1.0, -126) * double(H) * 1.001);
     c.norm_abs = float(std::sqrt(double(H)) * std::ldexp(1.0, -63) * 1.001);
     return c;
@@ -408,7 +422,7 @@ hipError_t launch_router_screened(const RouteArgs& a, float* mpart, float* wn2, 
     const uint16_t* x = static_cast<const uint16_t*>(a.x);
     const uint16_t* wr = static_cast<const uint16_t*>(a.wr);
     hipLaunchKernelGGL(router_mfma_kernel, grid, dim3(512), 0, s, x, wr, a.bias, mpart, wn2, T, H, E, KS);
-    const ScreenConst sc = screen_const(H);
+    const ScreenConst sc = screen_const(H, KS);
     const dim3 g2((T + 3) / 4);
     // token row in registers for H = 1024, 2048, 4096
     const int cpl = (H == 4096) ? 8 : (H == 2048) ? 4 : (H == 1024) ? 2 : 0;
