@@ -238,9 +238,8 @@ moe_status run_route(const moe_problem& p, const void* x, const void* wr, const 
     RouteArgs r{x, wr, bias, at<float>(ws, L.logits), p.num_tokens, p.hidden, p.num_experts,
                 p.act_dtype == MOE_BF16};
     if (screened_routing(p))
-        MOE_TRY(dev(launch_router_screened(r, at<float>(ws, L.mpart), at<float>(ws, L.wn2), p.top_k, s)));
-    else
-        MOE_TRY(dev(launch_router_logits(r, s)));
+        return dev(launch_router_screened(r, at<float>(ws, L.mpart), at<float>(ws, L.wn2), p.top_k, ids, w, s));
+    MOE_TRY(dev(launch_router_logits(r, s)));
     return dev(launch_topk(r.logits, p.num_tokens, p.num_experts, p.top_k, p.renormalize, ids, w, s));
 }
 

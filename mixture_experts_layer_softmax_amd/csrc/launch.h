@@ -107,9 +107,9 @@ hipError_t launch_decode_fused(const FusedArgs& a, bool nv4, int blocks_per_cu, 
 hipError_t launch_router_logits(const RouteArgs& a, hipStream_t s);
 // Screened routing (bf16 activations, renormalised weights): approximate logits on the matrix
 // cores, canonical logits only for the experts that can be selected, -inf for the rest (route.hip
-// states why the selection equals the full canonical one).  logits [T,E]; scratch: mpart
-// [KS,T,E] (partial approximate logits over KS slices of K, KS = screen_k_split(T, H, E)) and wn2
-// [KS,E] (squared router-row norms).  topk follows as for launch_router_logits.
+// states why the selection equals the full canonical one), then the top-k selection into ids
+// [T,k] and tw [T,k].  Scratch: logits [T,E], mpart [KS,T,E] (partial approximate logits over
+// KS slices of K, KS = screen_k_split(T, H, E)) and wn2 [KS,E] (squared router-row norms).
 struct ScreenConst {
     float gamma;     // relative bound of the two dot products, the slice sum and the bias addition
     float flush;     // 2^-126 H: terms flushed to zero
@@ -117,7 +117,8 @@ struct ScreenConst {
 };
 ScreenConst screen_const(int H, int KS);
 int screen_k_split(int T, int H, int E);
-hipError_t launch_router_screened(const RouteArgs& a, float* mpart, float* wn2, int k, hipStream_t s);
+hipError_t launch_router_screened(const RouteArgs& a, float* mpart, float* wn2, int k, int32_t* ids,
+                                  float* tw, hipStream_t s);
 hipError_t launch_topk(const float* logits, int T, int E, int k, int renorm, int32_t* ids,
                        float* w, hipStream_t s);
 hipError_t launch_dispatch(const DispatchArgs& d, hipStream_t s);

@@ -52,7 +52,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
 //     holds for any summation order (below); tau = the k-th largest m_e - beta_e; experts with
 //     m_e + beta_e >= tau get their canonical logit (router_logits_wave, the code of the full
 //     router), the others -inf;
-//  3. topk_kernel, unchanged.
+//  3. the selection of topk_kernel on those values (in the same kernel).
 // An expert with m_e + beta_e < tau has l_e < tau <= l_f for at least k experts f (those whose
 // m_f - beta_f >= tau, themselves candidates), so it is not selected whatever the ties.  The k
 // selected experts are candidates, with their canonical logits, so ids and weights are those of
@@ -253,9 +253,12 @@ __device__ __forceinline__ void canonical_pair(const float (&xf)[CPL * 8], const
 }
 
 // One wavefront per token: m is the sum of the KS partials mpart + ks T E, the squared router
-// norms the sum of wn2 + ks E; logits receives the screened canonical logits.  CPL > 0:
-// H = 512 CPL, the token row is held in registers (as fp32) and candidates are taken two at a
-// time; CPL = 0: any H, each candidate through router_logits_wave.
+// norms the sum of wn2 + ks E; the selection (ids, weights) follows from the screened canonical
+// logits.  CPL > 0: H = 512 CPL, the token row is held in registers (as fp32), candidates are
+// taken two at a time and their logits stay in registers for the selection; CPL = 0: any H,
+// each candidate through router_logits_wave into the token's logits row (the others -inf), from
+// which the selection reads.  Either way the selection runs the code of topk_kernel on the same
+// values.
 template <int EPL, int CPL>
 __global__ __launch_bounds__(256) void router_screen_kernel(const uint16_t* __restrict__ x,
                                                             const uint16_t* __restrict__ wr,
@@ -263,7 +266,9 @@ __global__ __launch_bounds__(256) void router_screen_kernel(const uint16_t* __re
                                                             const float* __restrict__ mpart,
                                                             float* __restrict__ logits,
                                                             const float* __restrict__ wn2, int T,
-                                                            int H, int E, int k, int KS, ScreenConst sc) {
+                                                            int H, int E, int k, int KS, ScreenConst sc,
+                                                            int32_t* __restrict__ ids,
+                                                            float* __restrict__ tw) {
     const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
     if (t >= T) return;  // uniform per wave
     const int lane = lane_id();
@@ -316,6 +321,8 @@ __global__ __launch_bounds__(256) void router_screen_kernel(const uint16_t* __re
     }
     if (__builtin_amdgcn_ballot_w64(!ok) != 0) {  // non-finite or huge: the full canonical row
         for (int e = 0; e < E; ++e) router_logits_wave<true, 1, 1>(x, wr, bias, logits, T, H, E, t * E + e);
+        __threadfence_block();  // the row's stores (lane 0) before its loads (every lane)
+        topk_token<EPL>(row, E, k, 1, ids + size_t(t) * k, tw + size_t(t) * k, nullptr);
         return;
     }
     // tau: the k-th largest lower bound (k rounds, each removing one occurrence of the maximum)
@@ -342,10 +349,13 @@ __global__ __launch_bounds__(256) void router_screen_kernel(const uint16_t* __re
         tau = mx;
     }
     int pend = -1;  // CPL > 0: a candidate waiting for its pair
+    float cv[EPL];  // CPL > 0: canonical logits of the candidates, -inf elsewhere
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) cv[i] = -__builtin_inff();
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         const bool cand = live[i] && mv[i] + bnd[i] >= tau;
-        if (live[i] && !cand) row[lane + kWave * i] = -__builtin_inff();
+        if (CPL == 0 && live[i] && !cand) row[lane + kWave * i] = -__builtin_inff();
         uint64_t cm = __builtin_amdgcn_ballot_w64(cand);
         while (cm) {
             const int e = kWave * i + int(__builtin_ctzll(cm));
@@ -357,9 +367,14 @@ __global__ __launch_bounds__(256) void router_screen_kernel(const uint16_t* __re
                 }
                 float v0, v1;
                 canonical_pair<CPL>(xf, wr, H, pend, e, &v0, &v1);
-                if (lane == 0) {
-                    row[pend] = bias ? v0 + bias[pend] : v0;
-                    row[e] = bias ? v1 + bias[e] : v1;
+                if (bias) {
+                    v0 = v0 + bias[pend];
+                    v1 = v1 + bias[e];
+                }
+#pragma unroll
+                for (int q = 0; q < EPL; ++q) {
+                    if (pend == lane + kWave * q) cv[q] = v0;
+                    if (e == lane + kWave * q) cv[q] = v1;
                 }
                 pend = -1;
             } else {
@@ -371,8 +386,18 @@ __global__ __launch_bounds__(256) void router_screen_kernel(const uint16_t* __re
         if (pend >= 0) {  // an odd candidate: pair it with itself
             float v0, v1;
             canonical_pair<CPL>(xf, wr, H, pend, pend, &v0, &v1);
-            if (lane == 0) row[pend] = bias ? v0 + bias[pend] : v0;
+            if (bias) v0 = v0 + bias[pend];
+#pragma unroll
+            for (int q = 0; q < EPL; ++q)
+                if (pend == lane + kWave * q) cv[q] = v0;
         }
+        float sv, m0;
+        int se;
+        topk_rounds<EPL>(cv, live, k, &sv, &se, &m0);
+        topk_write_renormalised(sv, se, m0, k, ids + size_t(t) * k, tw + size_t(t) * k, nullptr);
+    } else {
+        __threadfence_block();  // the row's stores before its loads
+        topk_token<EPL>(row, E, k, 1, ids + size_t(t) * k, tw + size_t(t) * k, nullptr);
     }
 }
 
@@ -392,15 +417,15 @@ ScreenConst screen_const(int H, int KS) {
 template <int EPL>
 static void launch_screen(int cpl, dim3 g, const uint16_t* x, const uint16_t* wr, const float* bias,
                           const float* mpart, float* logits, const float* wn2, int T, int H, int E,
-                          int k, int KS, ScreenConst sc, hipStream_t s) {
+                          int k, int KS, ScreenConst sc, int32_t* ids, float* tw, hipStream_t s) {
     if (cpl == 8)
-        hipLaunchKernelGGL((router_screen_kernel<EPL, 8>), g, dim3(256), 0, s, x, wr, bias, mpart, logits, wn2, T, H, E, k, KS, sc);
+        hipLaunchKernelGGL((router_screen_kernel<EPL, 8>), g, dim3(256), 0, s, x, wr, bias, mpart, logits, wn2, T, H, E, k, KS, sc, ids, tw);
     else if (cpl == 4)
-        hipLaunchKernelGGL((router_screen_kernel<EPL, 4>), g, dim3(256), 0, s, x, wr, bias, mpart, logits, wn2, T, H, E, k, KS, sc);
+        hipLaunchKernelGGL((router_screen_kernel<EPL, 4>), g, dim3(256), 0, s, x, wr, bias, mpart, logits, wn2, T, H, E, k, KS, sc, ids, tw);
     else if (cpl == 2)
-        hipLaunchKernelGGL((router_screen_kernel<EPL, 2>), g, dim3(256), 0, s, x, wr, bias, mpart, logits, wn2, T, H, E, k, KS, sc);
+        hipLaunchKernelGGL((router_screen_kernel<EPL, 2>), g, dim3(256), 0, s, x, wr, bias, mpart, logits, wn2, T, H, E, k, KS, sc, ids, tw);
     else
-        hipLaunchKernelGGL((router_screen_kernel<EPL, 0>), g, dim3(256), 0, s, x, wr, bias, mpart, logits, wn2, T, H, E, k, KS, sc);
+        hipLaunchKernelGGL((router_screen_kernel<EPL, 0>), g, dim3(256), 0, s, x, wr, bias, mpart, logits, wn2, T, H, E, k, KS, sc, ids, tw);
 }
 
 // K slices of the screening GEMM: enough blocks for the loads in flight (measured, routing
@@ -414,7 +439,8 @@ int screen_k_split(int T, int H, int E) {
     return ks;
 }
 
-hipError_t launch_router_screened(const RouteArgs& a, float* mpart, float* wn2, int k, hipStream_t s) {
+hipError_t launch_router_screened(const RouteArgs& a, float* mpart, float* wn2, int k, int32_t* ids,
+                                  float* tw, hipStream_t s) {
     const int T = a.T, E = a.E, H = a.H;
     const int tilesT = (T + kRT - 1) / kRT, tilesE = (E + kRE - 1) / kRE;
     const int KS = screen_k_split(T, H, E);
@@ -428,13 +454,13 @@ hipError_t launch_router_screened(const RouteArgs& a, float* mpart, float* wn2, 
     const int cpl = (H == 4096) ? 8 : (H == 2048) ? 4 : (H == 1024) ? 2 : 0;
     const int epl = (E + kWave - 1) / kWave;
     if (epl <= 1)
-        launch_screen<1>(cpl, g2, x, wr, a.bias, mpart, a.logits, wn2, T, H, E, k, KS, sc, s);
+        launch_screen<1>(cpl, g2, x, wr, a.bias, mpart, a.logits, wn2, T, H, E, k, KS, sc, ids, tw, s);
     else if (epl <= 2)
-        launch_screen<2>(cpl, g2, x, wr, a.bias, mpart, a.logits, wn2, T, H, E, k, KS, sc, s);
+        launch_screen<2>(cpl, g2, x, wr, a.bias, mpart, a.logits, wn2, T, H, E, k, KS, sc, ids, tw, s);
     else if (epl <= 4)
-        launch_screen<4>(cpl, g2, x, wr, a.bias, mpart, a.logits, wn2, T, H, E, k, KS, sc, s);
+        launch_screen<4>(cpl, g2, x, wr, a.bias, mpart, a.logits, wn2, T, H, E, k, KS, sc, ids, tw, s);
     else
-        launch_screen<8>(cpl, g2, x, wr, a.bias, mpart, a.logits, wn2, T, H, E, k, KS, sc, s);
+        launch_screen<8>(cpl, g2, x, wr, a.bias, mpart, a.logits, wn2, T, H, E, k, KS, sc, ids, tw, s);
     return hipGetLastError();
 }
 

@@ -33,32 +33,17 @@ __device__ __forceinline__ int wave_min_i32(int v) {
     return __builtin_amdgcn_readlane(v, 63);
 }
 
-// Top-k of one token by one wavefront: k rounds of a wave-wide argmax over (logit desc,
-// expert asc), then the softmax weights in fp32.  A round takes the largest value (a DPP max;
-// fmaxf is exact), then the smallest expert index among the lanes whose candidate equals it
-// (+0 and -0 compare equal, as in a plain comparison).  `row` is the token's E logits; ids and w
-// receive k values each (and ids_lds too, when given).  NaN logits rank below every number, so
-// the comparison is a total order and every lane agrees on each winner: always k distinct valid
-// experts, also for non-finite logits (whose weights are then unspecified).
+// The k rounds of the selection over values v (lane l holds experts l, l + 64, ...; live marks
+// the experts that exist and are still unpicked).  Lane j < k receives the j-th pick in *sv /
+// *se; every lane receives the first (largest) value in *m0.
 template <int EPL>
-__device__ __forceinline__ void topk_token(const float* __restrict__ row, int E, int k, int renorm,
-                                           int32_t* __restrict__ ids, float* __restrict__ w,
-                                           int* ids_lds) {
+__device__ __forceinline__ void topk_rounds(const float (&v)[EPL], bool (&live)[EPL], int k,
+                                            float* sv, int* se, float* m0) {
     const int lane = lane_id();
     constexpr int NONE = 0x7fffffff;
-    float v[EPL];
-    bool live[EPL];
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-        const int e = lane + kWave * i;
-        live[i] = e < E;
-        v[i] = live[i] ? row[e] : 0.0f;
-        if (v[i] != v[i]) v[i] = -__builtin_inff();  // NaN ranks last: a total order for selection
-    }
-    // lane j < k keeps the j-th selection (value and expert); m0 is the first (largest) value
     float mysv = 0.0f;
     int myse = 0;
-    float m0 = 0.0f;
+    float first = 0.0f;
     for (int j = 0; j < k; ++j) {
         float bv = -__builtin_inff();
         int be = NONE;
@@ -72,7 +57,7 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ row, int E,
         const float m = wave_max_f32(bv);
         be = wave_min_i32((be != NONE && bv == m) ? be : NONE);
         bv = m;
-        if (j == 0) m0 = bv;
+        if (j == 0) first = bv;
 #pragma unroll
         for (int i = 0; i < EPL; ++i)
             if (be == lane + kWave * i) live[i] = false;
@@ -81,23 +66,66 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ row, int E,
             myse = be;
         }
     }
-    // weights: exp(l_j - l_0) / z; z sums the k terms in selection order (renormalised) or
-    // every logit's term (full softmax)
+    *sv = mysv;
+    *se = myse;
+    *m0 = first;
+}
+
+// Renormalised weights of the k picks: exp(l_j - l_0) / z, z summing the k terms in selection
+// order; lane j < k writes pick j.
+__device__ __forceinline__ void topk_write_renormalised(float sv, int se, float m0, int k,
+                                                        int32_t* __restrict__ ids, float* __restrict__ w,
+                                                        int* ids_lds) {
+    const int lane = lane_id();
     float z = 0.0f;
-    if (renorm) {
-        for (int j = 0; j < k; ++j)
-            z += expf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(mysv), j)) - m0);
-    } else {
-        float part = 0.0f;
-#pragma unroll
-        for (int i = 0; i < EPL; ++i) {
-            const int e = lane + kWave * i;
-            if (e < E) part += expf(row[e] - m0);
-        }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
-        z = part;
+    for (int j = 0; j < k; ++j)
+        z += expf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(sv), j)) - m0);
+    if (lane < k) {
+        ids[lane] = se;
+        w[lane] = expf(sv - m0) / z;
+        if (ids_lds) ids_lds[lane] = se;
     }
+}
+
+// Top-k of one token by one wavefront: k rounds of a wave-wide argmax over (logit desc,
+// expert asc), then the softmax weights in fp32.  A round takes the largest value (a DPP max;
+// fmaxf is exact), then the smallest expert index among the lanes whose candidate equals it
+// (+0 and -0 compare equal, as in a plain comparison).  `row` is the token's E logits; ids and w
+// receive k values each (and ids_lds too, when given).  NaN logits rank below every number, so
+// the comparison is a total order and every lane agrees on each winner: always k distinct valid
+// experts, also for non-finite logits (whose weights are then unspecified).
+template <int EPL>
+__device__ __forceinline__ void topk_token(const float* __restrict__ row, int E, int k, int renorm,
+                                           int32_t* __restrict__ ids, float* __restrict__ w,
+                                           int* ids_lds) {
+    const int lane = lane_id();
+    float v[EPL];
+    bool live[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const int e = lane + kWave * i;
+        live[i] = e < E;
+        v[i] = live[i] ? row[e] : 0.0f;
+        if (v[i] != v[i]) v[i] = -__builtin_inff();  // NaN ranks last: a total order for selection
+    }
+    // lane j < k keeps the j-th selection (value and expert); m0 is the first (largest) value
+    float mysv, m0;
+    int myse;
+    topk_rounds<EPL>(v, live, k, &mysv, &myse, &m0);
+    if (renorm) {
+        topk_write_renormalised(mysv, myse, m0, k, ids, w, ids_lds);
+        return;
+    }
+    // full softmax: z sums every logit's term
+    float part = 0.0f;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const int e = lane + kWave * i;
+        if (e < E) part += expf(row[e] - m0);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
+    const float z = part;
     if (lane < k) {
         ids[lane] = myse;
         w[lane] = expf(mysv - m0) / z;
