@@ -166,18 +166,20 @@ def test_route_small_and_large_batch_kernels_agree():
         assert np.array_equal(out[400][1][:T], out[T][1]), T
 
 
-@pytest.mark.parametrize("E,k", [(128, 8), (256, 8), (200, 6), (512, 16)])
-def test_screened_route_equals_full_router_on_hard_rows(E, k):
+# (T, H, E, k): the screen's K split is 4 for the 256-token cases and 1 at 8192 x 512; the token
+# row sits in registers for H = 1024 and 2048, and goes through the generic form for H = 512
+@pytest.mark.parametrize("T,H,E,k", [(256, 1024, 128, 8), (256, 1024, 256, 8), (256, 2048, 200, 6),
+                                     (256, 512, 512, 16), (8192, 1024, 512, 8)])
+def test_screened_route_equals_full_router_on_hard_rows(T, H, E, k):
     """From 256 tokens, bf16 batches route through the screened router (approximate logits on
     the matrix cores, canonical logits only for the experts that can be selected); below 256 the
-    full canonical router runs.  Routing the same rows as 256 tokens and as their first 255 must
-    give the same ids and weights bit for bit, on rows built to stress the screen: exact ties
+    full canonical router runs.  Routing T rows and their first 255 must give the same ids and
+    weights bit for bit on those 255, on rows built to stress the screen: exact ties
     (duplicated router rows, zero tokens whose logits are the bias), near ties (router rows one
     bf16 step apart in one element), a token of norm 2^60 and non-finite tokens (both take the
     full row), bf16 subnormal tokens, and ordinary ones.  Ids of the finite rows must also equal
     the oracle's."""
-    rng = np.random.default_rng(E * 31 + k)
-    T, H = 256, 1024
+    rng = np.random.default_rng(E * 31 + k + H)
     wr = (rng.standard_normal((E, H)) * 0.02).astype(np.float32)
     wr[1::7] = wr[0::7][: len(wr[1::7])]                       # exact duplicates
     wr[3::11] = wr[2::11][: len(wr[3::11])]
@@ -192,12 +194,12 @@ def test_screened_route_equals_full_router_on_hard_rows(E, k):
     x[32, 7] = np.nan
     x[33] = x[34]                                               # identical tokens
     xb = synth.to_bf16_bits(x)
-    note("screened route E=%d k=%d" % (E, k))
+    note("screened route T=%d H=%d E=%d k=%d" % (T, H, E, k))
     xd = to_device(xb, "cuda", "bf16")
     wd = to_device(bits, "cuda", "bf16")
     bd = to_device(bias, "cuda")
     out = {}
-    for n in (T, T - 1):
+    for n in (T, 255):
         p = lib.problem(n, H, E, k, 128)
         ws = torch.empty(lib.workspace_size(p), dtype=torch.uint8, device="cuda")
         ids = torch.empty(n, k, dtype=torch.int32, device="cuda")
@@ -206,9 +208,9 @@ def test_screened_route_equals_full_router_on_hard_rows(E, k):
         torch.cuda.synchronize()
         out[n] = (ids.cpu().numpy(), w.cpu().numpy())
     ids256, w256 = out[T]
-    ids255, w255 = out[T - 1]
-    assert np.array_equal(ids256[: T - 1], ids255)
-    assert np.array_equal(w256[: T - 1].view(np.uint32), w255.view(np.uint32))
+    ids255, w255 = out[255]
+    assert np.array_equal(ids256[:255], ids255)
+    assert np.array_equal(w256[:255].view(np.uint32), w255.view(np.uint32))
     for r in range(T):  # every token: k distinct valid experts
         assert len(set(ids256[r].tolist())) == k and ids256[r].min() >= 0 and ids256[r].max() < E
     finite = np.isfinite(x).all(axis=1)
