@@ -138,9 +138,24 @@ def cpu_baseline(wl, inputs, budget_s: float, held=None):
         if spent >= budget_s / 2 or n >= wl.tokens:  # a final sample of 10-20 s at the default
             break
         n = min(wl.tokens, int(n * max(2.0, budget_s / 2 / max(spent, 1e-3))))
-    return dict(value=n / spent, unit="tokens/s", cores=O.max_threads(), kind="oracle",
-                sample="first %d of the %d tokens, whole layer (route, dispatch, expert FFNs, "
-                       "combine) in fp64, %.1f s" % (n, wl.tokens, spent), seconds=spent)
+    out = dict(value=n / spent, unit="tokens/s", cores=O.max_threads(), kind="oracle",
+               sample="first %d of the %d tokens, whole layer (route, dispatch, expert FFNs, "
+                      "combine) in fp64, %.1f s" % (n, wl.tokens, spent), seconds=spent)
+    if wl.tokens <= 64:  # decode-sized batches: also one thread, median of three runs
+        threads = O.max_threads()
+        O.set_threads(1)
+        try:
+            runs = []
+            for _ in range(3):
+                t0 = time.perf_counter()
+                O.forward(sub, wl.top_k, wl.wdt, wl.ffn, wl.renormalize, held=held)
+                runs.append(time.perf_counter() - t0)
+        finally:
+            O.set_threads(threads)
+        one = sorted(runs)[1]
+        out["single_thread"] = dict(value=n / one, unit="tokens/s", cores=1, seconds=one,
+                                    sample="the same %d tokens, median of 3 runs" % n)
+    return out
 
 
 def measured_peaks(torch, lib):
