@@ -169,7 +169,7 @@ def test_route_small_and_large_batch_kernels_agree():
 # (T, H, E, k): the screen's K split is 4 for the 256-token cases and 1 at 8192 x 512; the token
 # row sits in registers for H = 1024 and 2048, and goes through the generic form for H = 512
 @pytest.mark.parametrize("T,H,E,k", [(256, 1024, 128, 8), (256, 1024, 256, 8), (256, 2048, 200, 6),
-                                     (256, 512, 512, 16), (8192, 1024, 512, 8)])
+                                     (256, 512, 512, 16), (8192, 1024, 512, 8), (300, 1024, 16, 4)])
 def test_screened_route_equals_full_router_on_hard_rows(T, H, E, k):
     """From 256 tokens, bf16 batches route through the screened router (approximate logits on
     the matrix cores, canonical logits only for the experts that can be selected); below 256 the
@@ -669,10 +669,13 @@ def test_small_batch_single_launch_dispatch(T, E, k):
     _check_forward(wl, inp, MoELayer.from_workload(wl, inp))
 
 
-def test_full_softmax_weights_option():
-    wl = W("nr", 50, 256, 8, 3, 128, "bf16", "bf16", 51, "normal", renormalize=False)
+@pytest.mark.parametrize("T,E", [(50, 8), (300, 32)])
+def test_full_softmax_weights_option(T, E):
+    """Full-softmax weights (renormalize = 0) need every canonical logit, so batches the screened
+    router would take (from 256 bf16 tokens) route through the full router instead."""
+    wl = W("nr", T, 256, E, 3, 128, "bf16", "bf16", 51, "normal", renormalize=False)
     inp = synth.generate(wl)
-    note("renormalize=0")
+    note("renormalize=0 T=%d E=%d" % (T, E))
     _check_forward(wl, inp, MoELayer.from_workload(wl, inp))
 
 
