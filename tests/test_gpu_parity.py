@@ -144,9 +144,9 @@ def test_route_with_exact_ties_matches_oracle(T, E, k):
 
 
 def test_route_small_and_large_batch_kernels_agree():
-    """The router's four wavefront shapes give the same logits: 8x8 (token, expert) blocks from
-    384 tokens, 4x4 for 64 to 383, one token and two experts for 17 and 63 tokens, one token and
-    one expert while T * E <= 2048 (16 tokens and 1 token at E = 128)."""
+    """The router's wavefront shapes give the same logits: the screened router from 256 tokens
+    (400), 4x4 (token, expert) blocks for 64 to 383, one token and two experts for 33 and 63
+    tokens, one token and one expert while T * E <= 4096 (32, 17, 16 and 1 tokens at E = 128)."""
     wl = synth.WORKLOADS["decode64"].with_tokens(400, x_sub=400)
     inp = synth.generate(wl, with_experts=False)
     p400 = lib.problem(400, wl.hidden, wl.experts, wl.top_k, wl.ffn)
@@ -154,14 +154,14 @@ def test_route_small_and_large_batch_kernels_agree():
     x = to_device(inp["x"], "cuda", "bf16")
     wr = to_device(inp["w_router"], "cuda", "bf16")
     out = {}
-    for T in (400, 383, 64, 63, 17, 16, 1):
+    for T in (400, 383, 64, 63, 33, 32, 17, 16, 1):
         p = lib.problem(T, wl.hidden, wl.experts, wl.top_k, wl.ffn)
         ids = torch.empty(T, wl.top_k, dtype=torch.int32, device="cuda")
         w = torch.empty(T, wl.top_k, dtype=torch.float32, device="cuda")
         note("route T=%d" % T)
         lib.route(p, x[:T], wr, None, ids, w, ws)
         out[T] = (ids.cpu().numpy(), w.cpu().numpy())
-    for T in (383, 64, 63, 17, 16, 1):
+    for T in (383, 64, 63, 33, 32, 17, 16, 1):
         assert np.array_equal(out[400][0][:T], out[T][0]), T
         assert np.array_equal(out[400][1][:T], out[T][1]), T
 
