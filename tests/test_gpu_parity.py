@@ -650,11 +650,13 @@ def test_all_tokens_on_the_same_experts(wdt):
     _check_forward(wl, inp, layer)
 
 
-@pytest.mark.parametrize("E,k", [(4, 4), (1, 1), (16, 16)])
-def test_k_equals_e(E, k):
-    wl = W("keqe", 40, 256, E, k, 128, "bf16", "bf16", 41 + E, "normal")
+@pytest.mark.parametrize("T,E,k", [(40, 4, 4), (40, 1, 1), (40, 16, 16), (300, 16, 16)])
+def test_k_equals_e(T, E, k):
+    """Every expert selected; at 300 tokens through the screened router, where every expert is a
+    candidate."""
+    wl = W("keqe", T, 256, E, k, 128, "bf16", "bf16", 41 + E, "normal")
     inp = synth.generate(wl)
-    note("k=E=%d" % E)
+    note("k=E=%d T=%d" % (E, T))
     _check_forward(wl, inp, MoELayer.from_workload(wl, inp))
 
 
