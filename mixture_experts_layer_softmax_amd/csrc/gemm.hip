@@ -625,19 +625,21 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_prefill_nvfp4_kernel(GemmArgs
             if constexpr (A32) dma16s(a_s + k0_ * 2, va[i], &SA[(i * NW + wave) * 64]);       \
             else dma16(pa[i] + k0_ * 2, &SA[(i * NW + wave) * 64]);                             \
     } while (0)
-    // nibbles of stage k0/32, and the scale word holding its two scales (stages 2m, 2m+1)
-#define MOE_ISSUE_W(SN, SS, K0)                                                                 \
+    // nibbles of stage k0/32, and the scale word holding its two scales (stages 2m, 2m+1); with
+    // NW = 8 the word is loaded with the pair's first stage only (SC: the stage is a pair's
+    // first), and the thread that decodes a row keeps it in a register for the second
+#define MOE_ISSUE_W(SN, SS, K0, SC)                                                             \
     do {                                                                                        \
         const int k0_ = (K0);                                                                   \
         if constexpr (PK) {                                                                     \
             if (NW == 4 || wave < 4)                                                            \
                 dma16s(wq_s + (k0_ >> 5) * 4096, mrow * 16, &SN[(wave & 3) * 64]);              \
-            if (NW == 4 || wave >= 4)                                                           \
+            if (NW == 4 || (wave >= 4 && (SC)))                                                 \
                 dma4s(ws_s + (k0_ >> 6) * 1024, mrow * 4, &SS[(wave & 3) * 64]);                \
         } else {                                                                                \
             if (NW == 4 || wave < 4)                                                            \
                 dma16((NW == 8 ? pw : pq) + k0_ / 2, &SN[(wave & 3) * 64]);                     \
-            if (NW == 4 || wave >= 4)                                                           \
+            if (NW == 4 || (wave >= 4 && (SC)))                                                 \
                 dma4((NW == 8 ? pw : ps) + ((k0_ >> 4) & ~3), &SS[(wave & 3) * 64]);            \
         }                                                                                       \
     } while (0)
@@ -696,7 +698,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_prefill_nvfp4_kernel(GemmArgs
     // stage's loads (activation chunks after groups 1 and 3, raw weights after group 5) are
     // issued between the groups too, so that a load that waits for the address unit does not
     // hold back the MFMAs (NVFP4 prefill forward 4.02-4.04 -> 3.98 ms, one process)
-#define MOE_MFMA_DEC(AF, BF, SB, NIB, SW, K0, FULLC, SAW, SNW, SSW, KA, KW, SAR)                 \
+#define MOE_MFMA_DEC(AF, BF, SB, NIB, SW, K0, FULLC, SAW, SNW, SSW, KA, KW, SCW, SAR)            \
     do {                                                                                        \
         typedef __attribute__((ext_vector_type(2))) float f2_;                                  \
         const int row_ = tid >> 1, h_ = tid & 1;                                                \
@@ -728,7 +730,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_prefill_nvfp4_kernel(GemmArgs
                 if (a_scalar_) dma16s(a_s + size_t(KA) * 2, va[i_], &SAW[(i_ * NW + wave) * 64]); \
                 else dma16(pa[i_] + size_t(KA) * 2, &SAW[(i_ * NW + wave) * 64]);               \
             }                                                                                   \
-            if (mi == 5) MOE_ISSUE_W(SNW, SSW, KW);                                             \
+            if (mi == 5) MOE_ISSUE_W(SNW, SSW, KW, SCW);                                        \
         }                                                                                       \
         SB[lds_slot32(row_, 2 * h_ + 1)] = make_uint4(w_[4], w_[5], w_[6], w_[7]);               \
     } while (0)
@@ -744,41 +746,43 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_prefill_nvfp4_kernel(GemmArgs
     const int last = (nk - 1) * BKS;
     // prologue: raw stages 0 and 1, activation stage 0; decode both; then activation stages
     // 1..3 and raw stages 2..4 in the steady-state issue order
-    MOE_ISSUE_W(sN0, sS0, 0);
-    MOE_ISSUE_W(sN1, sS1, min(1 * BKS, last));
+    MOE_ISSUE_W(sN0, sS0, 0, true);
+    MOE_ISSUE_W(sN1, sS1, min(1 * BKS, last), false);
     MOE_ISSUE_A(sA0, 0);
     wait_vm_lgkm0<0>();
     block_barrier();
     MOE_DECODE(sN0, sS0, sB0, 0);
-    MOE_DECODE(sN1, sS1, sB1, min(1 * BKS, last));
+    MOE_DECODE(sN1, (NW == 8 ? sS0 : sS1), sB1, min(1 * BKS, last));  // NW = 8: stage 0's word
     wait_vm_lgkm0<0>();
     block_barrier();
     MOE_READ(sA0, sB0, af, b0);
     MOE_ISSUE_A(sA1, min(1 * BKS, last));
-    MOE_ISSUE_W(sN2, sS2, min(2 * BKS, last));
+    MOE_ISSUE_W(sN2, sS2, min(2 * BKS, last), true);
     MOE_ISSUE_A(sA2, min(2 * BKS, last));
-    MOE_ISSUE_W(sN3, sS3, min(3 * BKS, last));
+    MOE_ISSUE_W(sN3, sS3, min(3 * BKS, last), false);
     MOE_ISSUE_A(sA3, min(3 * BKS, last));
-    MOE_ISSUE_W(sN0, sS0, min(4 * BKS, last));
+    MOE_ISSUE_W(sN0, sS0, min(4 * BKS, last), true);
     uint2 nibd_ = make_uint2(0, 0);  // raw weight words this thread decodes in the next MFMA block
     uint32_t swd_ = 0;
     int na_;  // na, re-read each stage so that the group tests stay scalar compares
 #define MOE_IT(FULLC, S, FB, GB, SAr, SBr, SAw, SNw, SSw, SNd, SSd, SBd)      \
-        wait_vm_lgkm0<2 * OPS>();                                            \
+        /* NW = 8: wavefronts 4-7 issue one load fewer per stage pair */      \
+        if (NW == 8 && wave >= 4) wait_vm_lgkm0<2 * OPS - 1>();              \
+        else wait_vm_lgkm0<2 * OPS>();                                       \
         block_barrier();                                                     \
         na_ = na;                                                            \
         asm volatile("" : "+s"(na_));                                        \
         if constexpr (NW == 8) {                                             \
             nibd_ = reinterpret_cast<const uint2*>(SNd)[tid];                \
-            swd_ = SSd[tid >> 1];                                            \
+            if ((S & 1) == 0) swd_ = SSd[tid >> 1]; /* odd stages: kept */   \
         }                                                                    \
         MOE_READ_B(SBr, GB);                                                 \
         if constexpr (NW == 4) {                                             \
             MOE_ISSUE_A(SAw, min((s + S + 4) * BKS, last));                  \
-            MOE_ISSUE_W(SNw, SSw, min((s + S + 5) * BKS, last));             \
+            MOE_ISSUE_W(SNw, SSw, min((s + S + 5) * BKS, last), true);       \
         }                                                                    \
         if constexpr (NW == 8) {                                             \
-            MOE_MFMA_DEC(af, FB, SBd, nibd_, swd_, min((s + S + 2) * BKS, last), FULLC, SAw, SNw, SSw, min((s + S + 4) * BKS, last), min((s + S + 5) * BKS, last), SAr); \
+            MOE_MFMA_DEC(af, FB, SBd, nibd_, swd_, min((s + S + 2) * BKS, last), FULLC, SAw, SNw, SSw, min((s + S + 4) * BKS, last), min((s + S + 5) * BKS, last), ((S) & 1) == 1, SAr); \
             if (s + S + 1 >= nk) break;                                      \
         } else {                                                             \
             MOE_MFMA(af, FB, FULLC, SAr);                                    \
