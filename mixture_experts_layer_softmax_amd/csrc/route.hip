@@ -48,8 +48,8 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
 //  1. router_mfma_kernel: approximate logits m[t,e] = x_t . w_e + b_e on the bf16 matrix cores
 //     (fp32 accumulation, in whatever order the matrix core adds, as partial sums over slices of
 //     K), and the squared norms |w_e|^2;
-//  2. router_screen_kernel, one wavefront per token: |x_t|^2, a bound beta_e >= |l[t,e] - m[t,e]| that
-//     holds for any summation order (below); tau = the k-th largest m_e - beta_e; experts with
+//  2. router_screen_kernel, one wavefront per token: |x_t|^2, a bound beta_e >= |l[t,e] - m[t,e]|
+//     that holds for any summation order (below); tau = the k-th largest m_e - beta_e; experts with
 //     m_e + beta_e >= tau get their canonical logit (router_logits_wave, the code of the full
 //     router), the others -inf;
 //  3. the selection of topk_kernel on those values (in the same kernel).
@@ -63,9 +63,10 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
 // ((1 + u)^n - 1) sum |x_i w_i| of the exact sum when no term passes through more than n
 // additions (the forward error bound of summation, Higham, Accuracy and Stability of
 // Numerical Algorithms, section 4.2).  The canonical order is IEEE fused multiply-adds
-// (u = 2^-24): at most H / 64 + 8 per partial, a fold of 6 and the bias, n <= H / 64 + 16.  For the matrix
-// cores nothing is assumed about the order or the rounding inside an instruction beyond each
-// addition being accurate to u = 2^-23 (round to nearest, or truncation): an instruction adds
+// (u = 2^-24): at most H / 64 + 8 per partial, a fold of 6 and the bias, n <= H / 64 + 16.
+// For the matrix cores nothing is assumed about the order or the rounding inside an
+// instruction beyond each addition being accurate to u = 2^-23 (round to nearest, or
+// truncation): an instruction adds
 // 32 products and the accumulator, so a term passes through at most 32 additions per
 // instruction of its K slice, H / KS in all, then the KS - 1 additions of the slices and the
 // bias: n = H / KS + KS + 1.  sum |x_i w_i| <= |x| |w| (Cauchy-Schwarz).  Inputs, products or
