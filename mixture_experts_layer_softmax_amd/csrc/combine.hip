@@ -4,7 +4,10 @@
 // kernel uses the positions dispatch assigned to gather a token's expert rows and accumulates
 // them in registers with vectorised accesses, then writes the final token.  Here: one block
 // per token, 16-byte loads of y_perm rows (all rows of a vector issued before the first FMA),
-// fp32 accumulation in ascending slot order, one rounding to the output type.  Slots with a
+// fp32 accumulation in ascending slot order, one rounding to the output type.  In bf16 the
+// y_perm loads and the output stores are non-temporal: every y_perm element is read once, and
+// caching it only evicts other lines (kernel trace, median us, 8192 tokens x 8 slots x 4096:
+// 113.5 -> 92.9; 4096 x 8 x 4096: 54.7 -> 47.8; bit-identical).  Slots with a
 // negative row were not dispatched here (their expert is held by another rank under expert
 // parallelism) and are skipped, so the result is the local part of the combine that the pages
 // follow with an all-reduce.
@@ -12,6 +15,8 @@
 #include "launch.h"
 
 namespace moe {
+
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;  // for the non-temporal builtins
 
 template <bool BF16>
 __global__ __launch_bounds__(512) void combine_kernel(const void* __restrict__ y_perm,
@@ -37,27 +42,28 @@ __global__ __launch_bounds__(512) void combine_kernel(const void* __restrict__ y
         }
     }
     if (BF16) {
-        const uint4* src = static_cast<const uint4*>(y_perm);
-        uint4* dst = static_cast<uint4*>(y);
+        const u32x4_t* src = static_cast<const u32x4_t*>(y_perm);
+        u32x4_t* dst = static_cast<u32x4_t*>(y);
         const int nv = H / 8;
         for (int v = threadIdx.x; v < nv; v += blockDim.x) {
-            uint4 q[kMaxTopK];  // all of this vector's row loads in flight before the first FMA
+            u32x4_t q[kMaxTopK];  // all of this vector's row loads in flight before the first FMA
 #pragma unroll
             for (int j = 0; j < kMaxTopK; ++j)
-                if (ok[j]) q[j] = src[size_t(rows[j]) * nv + v];
+                if (ok[j]) q[j] = __builtin_nontemporal_load(src + size_t(rows[j]) * nv + v);
             float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int j = 0; j < kMaxTopK; ++j) {
                 if (!ok[j]) continue;
-                const uint32_t u[4] = {q[j].x, q[j].y, q[j].z, q[j].w};
+                const uint32_t u[4] = {q[j][0], q[j][1], q[j][2], q[j][3]};
 #pragma unroll
                 for (int p = 0; p < 4; ++p) {
                     acc[2 * p] = __builtin_fmaf(ws[j], bf16_lo(u[p]), acc[2 * p]);
                     acc[2 * p + 1] = __builtin_fmaf(ws[j], bf16_hi(u[p]), acc[2 * p + 1]);
                 }
             }
-            dst[size_t(t) * nv + v] = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
-                                                 pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
+            const u32x4_t o = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                               pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
+            __builtin_nontemporal_store(o, dst + size_t(t) * nv + v);
         }
     } else {
         const float4* src = static_cast<const float4*>(y_perm);

@@ -308,11 +308,21 @@ __global__ __launch_bounds__(256) void router_screen_kernel(const uint16_t* __re
         mv[i] = 0.0f;
         bnd[i] = 0.0f;
         if (live[i]) {
+            // all slices' loads in flight before the first sum (KS <= 4), summed in slice order
+            float mp[4], wp[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (q < KS) {
+                    mp[q] = mpart[(size_t(q) * T + t) * E + e];
+                    wp[q] = wn2[q * E + e];
+                }
             float w2 = 0.0f;
-            for (int q = 0; q < KS; ++q) {
-                mv[i] += mpart[(size_t(q) * T + t) * E + e];
-                w2 += wn2[q * E + e];
-            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (q < KS) {
+                    mv[i] += mp[q];
+                    w2 += wp[q];
+                }
             const float ws = __builtin_sqrtf(w2) * (1.0f + 0x1p-10f) + sc.norm_abs;
             const float ab = bias ? __builtin_fabsf(bias[e]) : 0.0f;
             ok = ok && ws <= 0x1p50f && ab <= 0x1p100f && __builtin_fabsf(mv[i]) <= 0x1p100f;
@@ -432,6 +442,7 @@ static void launch_screen(int cpl, dim3 g, const uint16_t* x, const uint16_t* wr
 // K slices of the screening GEMM: enough blocks for the loads in flight (measured, routing
 // alone, median us: 8192 tokens x 256 experts, slices 1 / 2 / 4 / 8: 119 / 107 / 117 / 135;
 // 4096 x 128: 86 / 68 / 61 / 63), so four slices below 256 blocks, two below 512, else one.
+// At most four: the screen kernel sums up to four slices.
 int screen_k_split(int T, int H, int E) {
     const int nst = H / kRK;
     const long blocks = long((T + kRT - 1) / kRT + 7) / 8 * 8 * ((E + kRE - 1) / kRE);
