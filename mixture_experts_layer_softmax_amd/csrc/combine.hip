@@ -16,8 +16,6 @@
 
 namespace moe {
 
-typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;  // for the non-temporal builtins
-
 template <bool BF16>
 __global__ __launch_bounds__(512) void combine_kernel(const void* __restrict__ y_perm,
                                                       const int32_t* __restrict__ inv_perm,
@@ -42,28 +40,28 @@ __global__ __launch_bounds__(512) void combine_kernel(const void* __restrict__ y
         }
     }
     if (BF16) {
-        const u32x4_t* src = static_cast<const u32x4_t*>(y_perm);
-        u32x4_t* dst = static_cast<u32x4_t*>(y);
+        const uint4* src = static_cast<const uint4*>(y_perm);
+        uint4* dst = static_cast<uint4*>(y);
         const int nv = H / 8;
         for (int v = threadIdx.x; v < nv; v += blockDim.x) {
-            u32x4_t q[kMaxTopK];  // all of this vector's row loads in flight before the first FMA
+            uint4 q[kMaxTopK];  // all of this vector's row loads in flight before the first FMA
 #pragma unroll
             for (int j = 0; j < kMaxTopK; ++j)
-                if (ok[j]) q[j] = __builtin_nontemporal_load(src + size_t(rows[j]) * nv + v);
+                if (ok[j]) q[j] = load_nt16(src + size_t(rows[j]) * nv + v);
             float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int j = 0; j < kMaxTopK; ++j) {
                 if (!ok[j]) continue;
-                const uint32_t u[4] = {q[j][0], q[j][1], q[j][2], q[j][3]};
+                const uint32_t u[4] = {q[j].x, q[j].y, q[j].z, q[j].w};
 #pragma unroll
                 for (int p = 0; p < 4; ++p) {
                     acc[2 * p] = __builtin_fmaf(ws[j], bf16_lo(u[p]), acc[2 * p]);
                     acc[2 * p + 1] = __builtin_fmaf(ws[j], bf16_hi(u[p]), acc[2 * p + 1]);
                 }
             }
-            const u32x4_t o = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
-                               pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
-            __builtin_nontemporal_store(o, dst + size_t(t) * nv + v);
+            store_nt16(dst + size_t(t) * nv + v,
+                       make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                                  pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])));
         }
     } else {
         const float4* src = static_cast<const float4*>(y_perm);
