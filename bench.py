@@ -183,7 +183,7 @@ def measured_peaks(torch, lib):
     del buf
     return dict(mfma_bf16_tflops=flops / 1e12, hbm_read_gbs=rate / 1e9,
                 probes="bf16 MFMA loop, %d blocks x 4 wavefronts x 20000 x 8 v_mfma_f32_16x16x32_bf16; "
-                       "read stream over 4 GiB" % (8 * cus))
+                       "non-temporal read stream over 4 GiB" % (8 * cus))
 
 
 def percentile(v, q):
