@@ -179,7 +179,7 @@ def measured_peaks(torch, lib):
     flops = best(lambda: lib.probe_mfma_bf16(8 * cus, 20000, sink))
     buf = torch.empty(4 * 2 ** 30, dtype=torch.uint8, device="cuda:0")
     word = torch.empty(1, dtype=torch.int32, device="cuda:0")
-    rate = best(lambda: lib.probe_read(buf, word))
+    rate = best(lambda: lib.probe_read(buf, word, nontemporal=True))
     del buf
     return dict(mfma_bf16_tflops=flops / 1e12, hbm_read_gbs=rate / 1e9,
                 probes="bf16 MFMA loop, %d blocks x 4 wavefronts x 20000 x 8 v_mfma_f32_16x16x32_bf16; "

@@ -36,6 +36,11 @@ moe_status moe_probe_mfma_bf16(int32_t blocks, int32_t iters, float* out, void* 
  * else MOE_ERR_INVALID_ARGUMENT. */
 moe_status moe_probe_read(const void* buf, size_t bytes, uint32_t* out, void* stream);
 
+/* The same read stream with non-temporal loads (no cache lines allocated for reuse): the rate
+ * of a stream like the decode GEMMs' weight loads.  Unlike moe_probe_read it does not evict
+ * the caches.  Arguments and errors as moe_probe_read. */
+moe_status moe_probe_read_nt(const void* buf, size_t bytes, uint32_t* out, void* stream);
+
 /* Grid barriers alone: one cooperative launch of `blocks` blocks of 256 threads (they must fit
  * on the device at once, else MOE_ERR_DEVICE) that pass `barriers` grid barriers of the
  * single-launch decode kernel (MOE_PATH_DECODE_FUSED) in a row and do nothing else.  sync:

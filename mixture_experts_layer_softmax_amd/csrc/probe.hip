@@ -36,9 +36,12 @@ __global__ __launch_bounds__(256) void mfma_probe_kernel(int iters, float* __res
 }
 
 // Each block step reads one contiguous 32 KiB chunk, eight 16-byte loads per thread issued
-// before any is used, with the non-temporal hint like the decode GEMMs' weight streams (the
-// same loop with default loads measured about 6.44 TB/s, below those GEMMs); the words past
-// the last whole chunk are read grid-stride.
+// before any is used; the words past the last whole chunk are read grid-stride.  NT: the
+// whole-chunk loads carry the non-temporal hint, like the decode GEMMs' weight streams (the
+// stream then measured about 7.1 TB/s against 6.44 with default loads, which the decode GEMMs
+// exceed); without it the loads allocate cache lines, so a read of a large buffer evicts
+// whatever the caches held.
+template <bool NT>
 __global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict__ p, long n16,
                                                          uint32_t* __restrict__ out) {
     constexpr int U = 8;
@@ -49,7 +52,7 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict
         const uint4* q = p + c * kChunk + threadIdx.x;
         uint4 v[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) v[u] = load_nt16(q + u * 256);
+        for (int u = 0; u < U; ++u) v[u] = NT ? load_nt16(q + u * 256) : q[u * 256];
 #pragma unroll
         for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].w;
     }
@@ -97,12 +100,21 @@ extern "C" moe_status moe_probe_mfma_bf16(int32_t blocks, int32_t iters, float* 
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
 }
 
-extern "C" moe_status moe_probe_read(const void* buf, size_t bytes, uint32_t* out, void* stream) {
+template <bool NT>
+static moe_status probe_read(const void* buf, size_t bytes, uint32_t* out, void* stream) {
     if (!buf || !out || bytes == 0 || (bytes & 15u) || (reinterpret_cast<uintptr_t>(buf) & 15u) ||
         (reinterpret_cast<uintptr_t>(out) & 3u))
         return MOE_ERR_INVALID_ARGUMENT;
-    hipLaunchKernelGGL(moe::read_probe_kernel, dim3(16384), dim3(256), 0,
+    hipLaunchKernelGGL(moe::read_probe_kernel<NT>, dim3(16384), dim3(256), 0,
                        static_cast<hipStream_t>(stream), static_cast<const uint4*>(buf),
                        long(bytes / 16), out);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
+}
+
+extern "C" moe_status moe_probe_read(const void* buf, size_t bytes, uint32_t* out, void* stream) {
+    return probe_read<false>(buf, bytes, out, stream);
+}
+
+extern "C" moe_status moe_probe_read_nt(const void* buf, size_t bytes, uint32_t* out, void* stream) {
+    return probe_read<true>(buf, bytes, out, stream);
 }

@@ -26,7 +26,7 @@ PATHS = {"auto": PATH_AUTO, "prefill": PATH_PREFILL, "decode": PATH_DECODE, "fus
 #: every symbol the header declares
 EXPORTS = ("moe_status_string", "moe_workspace_size", "moe_packed_weights_size", "moe_pack_weights",
            "moe_pack_scales", "moe_route", "moe_permute", "moe_grouped_gemm", "moe_combine", "moe_forward",
-           "moe_quantize_mxfp8", "moe_probe_mfma_bf16", "moe_probe_read", "moe_forward_static",
+           "moe_quantize_mxfp8", "moe_probe_mfma_bf16", "moe_probe_read", "moe_probe_read_nt", "moe_forward_static",
            "moe_probe_grid_barrier", "moe_probe_grouped_gemm_times")
 PROBE_SYNC_BYTES = 8256  # MOE_PROBE_SYNC_BYTES
 LAYOUT_ROW_MAJOR, LAYOUT_PACKED = 0, 1
@@ -90,6 +90,8 @@ def load() -> C.CDLL:
             L.moe_probe_mfma_bf16.argtypes = [C.c_int32, C.c_int32, vp, vp]
             L.moe_probe_read.restype = i32
             L.moe_probe_read.argtypes = [vp, sz, vp, vp]
+            L.moe_probe_read_nt.restype = i32
+            L.moe_probe_read_nt.argtypes = [vp, sz, vp, vp]
             L.moe_probe_grid_barrier.restype = i32
             L.moe_probe_grid_barrier.argtypes = [C.c_int32, C.c_int32, vp, C.c_uint32, vp]
             L.moe_probe_grouped_gemm_times.restype = i32
@@ -220,10 +222,12 @@ def probe_mfma_bf16(blocks, iters, out, stream=None):
     return float(blocks) * 4 * iters * 8 * 16384
 
 
-def probe_read(buf, out, stream=None):
-    """Launch the HBM read-stream probe over all of ``buf``; returns the bytes read."""
+def probe_read(buf, out, stream=None, nontemporal=False):
+    """Launch the HBM read-stream probe over all of ``buf`` (moe_probe_read, which evicts the
+    caches, or with ``nontemporal`` moe_probe_read_nt); returns the bytes read."""
     n = buf.numel() * buf.element_size()
-    _check(load().moe_probe_read(_ptr(buf), n, _ptr(out), _stream(stream)), "moe_probe_read")
+    name = "moe_probe_read_nt" if nontemporal else "moe_probe_read"
+    _check(getattr(load(), name)(_ptr(buf), n, _ptr(out), _stream(stream)), name)
     return float(n)
 
 

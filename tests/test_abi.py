@@ -217,6 +217,9 @@ def test_probe_validation(L):
     assert L.moe_probe_read(V(FAKE), 100, V(FAKE), None) == lib.MOE_ERR_INVALID_ARGUMENT
     assert L.moe_probe_read(V(FAKE + 8), 1024, V(FAKE), None) == lib.MOE_ERR_INVALID_ARGUMENT
     assert L.moe_probe_read(None, 1024, V(FAKE), None) == lib.MOE_ERR_INVALID_ARGUMENT
+    for bad in ((V(FAKE), 0, V(FAKE)), (V(FAKE), 100, V(FAKE)), (V(FAKE + 8), 1024, V(FAKE)),
+                (None, 1024, V(FAKE))):
+        assert L.moe_probe_read_nt(*bad, None) == lib.MOE_ERR_INVALID_ARGUMENT
 
 
 def test_grouped_gemm_timing_probe_validation(L):

@@ -34,11 +34,12 @@ def test_mfma_probe_rate_is_plausible():
     assert 2e14 < r < 3.0e15  # between 8 % and 120 % of the 2.5 PFLOP/s data-sheet peak
 
 
-def test_read_probe_rate_is_plausible():
+@pytest.mark.parametrize("nontemporal", [False, True])
+def test_read_probe_rate_is_plausible(nontemporal):
     buf = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
     word = torch.zeros(1, dtype=torch.int32, device="cuda")
-    r = _rate(lambda: lib.probe_read(buf, word))
-    print("[gpu] read probe %.1f GB/s" % (r / 1e9), flush=True)
+    r = _rate(lambda: lib.probe_read(buf, word, nontemporal=nontemporal))
+    print("[gpu] read probe (nontemporal=%s) %.1f GB/s" % (nontemporal, r / 1e9), flush=True)
     assert 1e12 < r < 1.2e13
 
 
