@@ -43,11 +43,6 @@ __device__ __forceinline__ uint4 load_nt16(const void* p) {
     const u32x4 v = __builtin_nontemporal_load(static_cast<const u32x4*>(p));
     return make_uint4(v.x, v.y, v.z, v.w);
 }
-__device__ __forceinline__ void store_nt16(void* p, uint4 v) {
-    typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
-    const u32x4 w = {v.x, v.y, v.z, v.w};
-    __builtin_nontemporal_store(w, static_cast<u32x4*>(p));
-}
 
 __device__ __forceinline__ uint64_t lanemask_lt() {
     return (uint64_t(1) << lane_id()) - 1;
